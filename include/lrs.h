@@ -1,0 +1,222 @@
+/*
+ * lrs.h -- C ABI of the MI355X (gfx950) linear-recurrence-scan library for
+ * reinforcement-learning credit assignment.
+ *
+ * What is computed.  Each call evaluates one estimator over a batch of
+ * rollouts of shape [num_envs, seq_len].  All seven are the same first-order
+ * linear recurrence A_t = alpha_t + beta_t * A_{t+1} (its forward-time mirror
+ * for the two forward estimators), solved as an associative scan with the
+ * operator (a_B, b_B) (+) (a_A, b_A) = (a_B + b_B a_A, b_A b_B); each call
+ * builds its alpha/beta on chip from the raw inputs and makes one pass over
+ * HBM (rl-triton paper, gist.science technical summary, Methodology 1 and 2;
+ * rl-triton README, Kernels table).
+ *
+ * Episode boundaries (same summary, Methodology 3).  Per element (n, t):
+ *   end_t   = terminated_t || truncated_t || t == seq_len-1
+ *   Vnext_t = terminated_t ? 0
+ *           : truncated_t  ? trunc_values[t]       (supplied bootstrap)
+ *           : t == seq_len-1 ? bootstrap_value[n]  (0 if NULL)
+ *           : values[t+1]
+ * A terminated step has successor value 0; a truncated step uses the
+ * supplied value; if both flags are set, termination wins.  The rollout-
+ * window bootstrap enters the local term of step seq_len-1 only (never also
+ * as a carry), and is ignored when that step is itself a cut.  The recursion
+ * never continues past end_t, so no value leaks between episodes (exact for
+ * finite inputs).
+ *
+ * Conventions shared by every call
+ *   - num_envs (N) >= 1, 1 <= seq_len (T) < 2^31, N*T < 2^34.
+ *   - Every array pointer is DEVICE memory owned by the caller.  Arrays of
+ *     shape [N, T] are row-major and contiguous (row stride T); per-env
+ *     arrays have N elements.  Float inputs/outputs are fp32; masks are
+ *     uint8 with 0 = false, nonzero = true.  Any alignment of at least the
+ *     element size is accepted; 16-byte aligned floats and 8-byte aligned
+ *     masks take the vectorised fast path.
+ *   - Outputs must not overlap any input or each other.
+ *   - All float inputs must be finite.
+ *   - gamma and lambda must lie in [0, 1].  Clip thresholds must be > 0;
+ *     +INFINITY means "no clip".
+ *   - workspace: caller-owned device memory of at least
+ *     lrs_workspace_bytes(...) bytes, ZERO-FILLED before its first use; the
+ *     library keeps it consistent from call to call afterwards, so it must
+ *     not be modified between calls.  Calls that share one workspace must be
+ *     ordered on one stream (concurrent use of one workspace races).  May be
+ *     NULL with workspace_bytes 0 when lrs_workspace_bytes returns 0.
+ *   - stream: the HIP stream to enqueue on (NULL = the null stream).  Calls
+ *     are asynchronous; the library never allocates, frees or synchronises.
+ *   - Errors: argument checks run on the host before anything is enqueued
+ *     and return LRS_ERR_INVALID_ARG / LRS_ERR_WORKSPACE with nothing
+ *     enqueued; a failed launch returns LRS_ERR_HIP.  lrs_last_error() then
+ *     holds a message (per thread).  Faults inside a kernel surface at the
+ *     caller's next synchronisation, as for any HIP kernel.
+ */
+#ifndef LRS_H
+#define LRS_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lrs_status {
+    LRS_OK = 0,
+    LRS_ERR_INVALID_ARG = 1, /* bad size, null pointer, scalar out of range */
+    LRS_ERR_WORKSPACE = 2,   /* workspace missing or smaller than required */
+    LRS_ERR_HIP = 3          /* a HIP runtime call failed (kernel launch)    */
+} lrs_status;
+
+typedef enum lrs_estimator {
+    LRS_GAE = 0,
+    LRS_VTRACE = 1,
+    LRS_RETRACE = 2,
+    LRS_LAMBDA_RETURNS = 3,
+    LRS_DISCOUNTED_RETURNS = 4,
+    LRS_ELIGIBILITY_TRACES = 5,
+    LRS_PREFIX_SUM_I32 = 6,
+    LRS_PREFIX_SUM_F32 = 7
+} lrs_estimator;
+
+/* Library version, encoded as major*10000 + minor*100 + patch. */
+int lrs_version(void);
+
+/* Static description of a status code (never NULL). */
+const char* lrs_status_string(lrs_status s);
+
+/* Message of the last failed call on the calling thread ("" if none). */
+const char* lrs_last_error(void);
+
+/* Bytes of workspace a call of `est` at [num_envs, seq_len] may need: 64
+ * bytes plus 16 bytes per 256 elements (about 6% of one fp32 input).  The
+ * same workspace serves every estimator at this or any smaller size.
+ * Returns 0 for invalid sizes. */
+size_t lrs_workspace_bytes(lrs_estimator est, int64_t num_envs, int64_t seq_len);
+
+/* Generalized Advantage Estimation (README Kernels table, compute_gae:
+ * backward scan over delta + gamma*lambda*A; Schulman et al. 2016 eq. 16):
+ *   delta_t = r_t + gamma*Vnext_t - V_t
+ *   A_t     = delta_t + (end_t ? 0 : gamma*lambda*A_{t+1})
+ * In:  rewards, values [N,T] f32; terminateds [N,T] u8 (required);
+ *      truncateds [N,T] u8 (nullable) and trunc_values [N,T] f32 (required
+ *      iff truncateds); bootstrap_value [N] f32 (nullable = 0).
+ * Out: advantages [N,T] f32.                                               */
+lrs_status lrs_gae_f32(int64_t num_envs, int64_t seq_len,
+                       const float* rewards, const float* values,
+                       const uint8_t* terminateds, const uint8_t* truncateds,
+                       const float* trunc_values, const float* bootstrap_value,
+                       float gamma, float lambda,
+                       float* advantages,
+                       void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/* V-trace (README Kernels table, compute_vtrace: importance-weighted targets
+ * and advantages; Espeholt et al. 2018 sec. 4.1 eq. 1 with the lambda-trace of
+ * sec. 4.2).  w_t = exp(log_rhos_t) = pi/mu of the taken action:
+ *   rho_t = min(rho_bar, w_t), c_t = lambda*min(c_bar, w_t)
+ *   A_t   = rho_t*(r_t + gamma*Vnext_t - V_t) + (end_t ? 0 : gamma*c_t*A_{t+1})
+ *   vs_t  = V_t + A_t
+ *   pg_t  = min(pg_rho_bar, w_t)*(r_t + gamma*(end_t ? Vnext_t : vs_{t+1}) - V_t)
+ * In:  log_rhos, rewards, values [N,T] f32; masks / trunc_values / bootstrap
+ *      as for GAE.  Out: vs, pg_advantages [N,T] f32 (both required).       */
+lrs_status lrs_vtrace_f32(int64_t num_envs, int64_t seq_len,
+                          const float* log_rhos, const float* rewards,
+                          const float* values,
+                          const uint8_t* terminateds, const uint8_t* truncateds,
+                          const float* trunc_values, const float* bootstrap_value,
+                          float gamma, float lambda,
+                          float rho_bar, float c_bar, float pg_rho_bar,
+                          float* vs, float* pg_advantages,
+                          void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/* Retrace(lambda) (README Kernels table, compute_retrace: off-policy return
+ * with truncated importance ratios; Munos et al. 2016).  q_values = Q(s_t,a_t),
+ * values = E_pi Q(s_t,.) (trunc_values and bootstrap_value are expected
+ * values too); c_{t+1} = lambda*min(c_bar, exp(log_rhos_{t+1})):
+ *   G_t = r_t + gamma*(end_t ? Vnext_t : V_{t+1} + c_{t+1}*(G_{t+1} - Q_{t+1}))
+ * Out: q_ret [N,T] f32.                                                     */
+lrs_status lrs_retrace_f32(int64_t num_envs, int64_t seq_len,
+                           const float* log_rhos, const float* rewards,
+                           const float* q_values, const float* values,
+                           const uint8_t* terminateds, const uint8_t* truncateds,
+                           const float* trunc_values, const float* bootstrap_value,
+                           float gamma, float lambda, float c_bar,
+                           float* q_ret,
+                           void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* TD(lambda) returns (README Kernels table, compute_lambda_returns: mixes
+ * one-step TD and Monte-Carlo targets; Sutton & Barto sec. 12.1, recursive):
+ *   G_t = r_t + gamma*(end_t ? Vnext_t : (1-lambda)*V_{t+1} + lambda*G_{t+1})
+ * Out: returns [N,T] f32.                                                   */
+lrs_status lrs_lambda_returns_f32(int64_t num_envs, int64_t seq_len,
+                                  const float* rewards, const float* values,
+                                  const uint8_t* terminateds, const uint8_t* truncateds,
+                                  const float* trunc_values, const float* bootstrap_value,
+                                  float gamma, float lambda,
+                                  float* returns,
+                                  void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
+/* Discounted returns (README Kernels table, compute_discounted_returns:
+ * discounted reward-to-go):
+ *   G_t = r_t + gamma*(end_t ? Vnext_t : G_{t+1})
+ * values are never read (Vnext is 0, trunc_values or bootstrap_value).
+ * Out: returns [N,T] f32.                                                   */
+lrs_status lrs_discounted_returns_f32(int64_t num_envs, int64_t seq_len,
+                                      const float* rewards,
+                                      const uint8_t* terminateds, const uint8_t* truncateds,
+                                      const float* trunc_values, const float* bootstrap_value,
+                                      float gamma,
+                                      float* returns,
+                                      void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
+
+/* Accumulating eligibility traces, forward in time (README Kernels table,
+ * compute_eligibility_traces formula):
+ *   e_t = x_t + (t == 0 || dones_{t-1} ? 0 : gamma*lambda*e_{t-1})
+ * In:  x [N,T] f32, dones [N,T] u8 (required).  Out: traces [N,T] f32.      */
+lrs_status lrs_eligibility_traces_f32(int64_t num_envs, int64_t seq_len,
+                                      const float* x, const uint8_t* dones,
+                                      float gamma, float lambda,
+                                      float* traces,
+                                      void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
+
+/* Episodic inclusive prefix sum (README Kernels table,
+ * compute_episodic_prefix_sum: cumulative sum with done-mask resets; same
+ * reset rule as the traces):
+ *   S_t = x_t + (t == 0 || dones_{t-1} ? 0 : S_{t-1})
+ * The int32 variant is exact in two's-complement arithmetic (sums outside
+ * the int32 range wrap modulo 2^32).                                         */
+lrs_status lrs_episodic_prefix_sum_i32(int64_t num_envs, int64_t seq_len,
+                                       const int32_t* x, const uint8_t* dones,
+                                       int32_t* sums,
+                                       void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+
+lrs_status lrs_episodic_prefix_sum_f32(int64_t num_envs, int64_t seq_len,
+                                       const float* x, const uint8_t* dones,
+                                       float* sums,
+                                       void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+
+/* Diagnostics and tuning (process-wide; not for concurrent use).
+ * force_lookback != 0: every later call takes the multi-block carry-
+ *   propagation path, even where whole rows fit in one tile.
+ * elems_per_lane (4 or 8) and waves_per_block (1, 4 or 16): fix the tile
+ *   (elems_per_lane * 64 * waves_per_block elements) instead of choosing it
+ *   from the shape; 0 restores the automatic choice.
+ * Returns LRS_ERR_INVALID_ARG for an unsupported combination.  Results stay
+ * within fp32 rounding of each other across schedules (the int32 prefix sum
+ * is identical). */
+lrs_status lrs_debug_set_schedule(int force_lookback, int elems_per_lane,
+                                  int waves_per_block);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LRS_H */
