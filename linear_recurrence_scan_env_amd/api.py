@@ -1,0 +1,326 @@
+"""Python binding of liblrs.so: the seven estimators on torch tensors.
+
+Argument marshalling only: every step of every estimator runs in the gfx950
+kernels behind the C ABI (include/lrs.h).  torch supplies device memory and
+the current stream.  There is no CPU path: calling any compute_* function
+without the built library, or on tensors that are not on a GPU, raises.
+
+Names and keyword arguments follow the rl-triton README (Kernels table and
+Usage section): compute_gae(rewards, values, terminateds, gamma, lambda_).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+import torch
+
+from . import build as _build
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+_SIGS = {
+    "lrs_gae_f32": [_I64, _I64, _P, _P, _P, _P, _P, _P, _F, _F, _P, _P, _SZ, _P],
+    "lrs_vtrace_f32": [_I64, _I64, _P, _P, _P, _P, _P, _P, _P, _F, _F, _F, _F, _F, _P, _P, _P, _SZ,
+                       _P],
+    "lrs_retrace_f32": [_I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _F, _F, _F, _P, _P, _SZ, _P],
+    "lrs_lambda_returns_f32": [_I64, _I64, _P, _P, _P, _P, _P, _P, _F, _F, _P, _P, _SZ, _P],
+    "lrs_discounted_returns_f32": [_I64, _I64, _P, _P, _P, _P, _P, _F, _P, _P, _SZ, _P],
+    "lrs_eligibility_traces_f32": [_I64, _I64, _P, _P, _F, _F, _P, _P, _SZ, _P],
+    "lrs_episodic_prefix_sum_i32": [_I64, _I64, _P, _P, _P, _P, _SZ, _P],
+    "lrs_episodic_prefix_sum_f32": [_I64, _I64, _P, _P, _P, _P, _SZ, _P],
+}
+
+ESTIMATOR_ID = {"gae": 0, "vtrace": 1, "retrace": 2, "lambda_returns": 3,
+                "discounted_returns": 4, "eligibility_traces": 5, "prefix_sum_i32": 6,
+                "prefix_sum_f32": 7}
+
+_lib = None
+_lock = threading.Lock()
+
+
+class LrsError(RuntimeError):
+    pass
+
+
+def lib_path() -> str:
+    return _build.LIB
+
+
+def load():
+    """Load liblrs.so (after torch, so both share torch's HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = _build.LIB
+        if not os.path.exists(path):
+            raise LrsError(f"{path} is not built: run `python -m linear_recurrence_scan_env_amd.build`"
+                           " (there is no CPU fallback)")
+        lib = ctypes.CDLL(path)
+        for name, args in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        lib.lrs_version.restype = ctypes.c_int
+        lib.lrs_status_string.restype = ctypes.c_char_p
+        lib.lrs_status_string.argtypes = [ctypes.c_int]
+        lib.lrs_last_error.restype = ctypes.c_char_p
+        lib.lrs_workspace_bytes.restype = _SZ
+        lib.lrs_workspace_bytes.argtypes = [ctypes.c_int, _I64, _I64]
+        lib.lrs_debug_set_schedule.restype = ctypes.c_int
+        lib.lrs_debug_set_schedule.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        _check_single_hip_runtime()
+        _lib = lib
+    return _lib
+
+
+def _check_single_hip_runtime():
+    """Two different libamdhip64 images in one process would make torch's
+    stream handles meaningless to the library: refuse to run then."""
+    try:
+        with open("/proc/self/maps") as f:
+            paths = {line.split()[-1] for line in f if "libamdhip64" in line}
+    except OSError:
+        return
+    real = {os.path.realpath(p) for p in paths}
+    if len(real) > 1:
+        raise LrsError(f"more than one HIP runtime is loaded: {sorted(real)}")
+
+
+def _check(status: int, name: str):
+    if status != 0:
+        lib = load()
+        msg = lib.lrs_last_error().decode()
+        kind = lib.lrs_status_string(status).decode()
+        if status in (1, 2):
+            raise ValueError(f"{name}: {kind}: {msg}")
+        raise LrsError(f"{name}: {kind}: {msg}")
+
+
+def set_schedule(force_lookback: bool = False, elems_per_lane: int = 0, waves_per_block: int = 0):
+    """Diagnostics: force the carry-propagation path and/or a fixed tile."""
+    _check(load().lrs_debug_set_schedule(int(force_lookback), int(elems_per_lane),
+                                         int(waves_per_block)), "set_schedule")
+
+
+# ------------------------------------------------------------ marshalling
+
+_workspaces = {}
+
+
+def workspace(device: torch.device, stream: torch.cuda.Stream, est: str, n: int, t: int):
+    """Zero-filled workspace cached per (device, stream), grown on demand."""
+    need = int(load().lrs_workspace_bytes(ESTIMATOR_ID[est], n, t))
+    key = (device.index, stream.cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(max(need, 4096), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def _dev_tensor(x, name, dtype, shape, device):
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if x.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (there is no CPU path)")
+    if device is not None and x.device != device:
+        raise ValueError(f"{name} is on {x.device}, expected {device}")
+    if x.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {x.dtype}")
+    if shape is not None and tuple(x.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(x.shape)}")
+    return x.contiguous()
+
+
+def _mask(x, name, shape, device):
+    """bool/uint8 masks pass through; other dtypes become (x != 0) first."""
+    if x is None:
+        return None
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if x.dtype == torch.bool:
+        x = x.view(torch.uint8)
+    elif x.dtype != torch.uint8:
+        x = (x != 0).view(torch.uint8)
+    return _dev_tensor(x, name, torch.uint8, shape, device)
+
+
+def _ptr(x):
+    return None if x is None else x.data_ptr()
+
+
+def _rows(x, name):
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D [num_envs, seq_len] tensor")
+    return x.shape[0], x.shape[1]
+
+
+def _prep_boundary(shape, device, terminateds, truncateds, trunc_values, bootstrap_value):
+    term = _mask(terminateds, "terminateds", shape, device)
+    if term is None:
+        raise ValueError("terminateds is required")
+    trunc = _mask(truncateds, "truncateds", shape, device)
+    tv = None
+    if trunc is not None:
+        if trunc_values is None:
+            raise ValueError("truncateds given without trunc_values")
+        tv = _dev_tensor(trunc_values, "trunc_values", torch.float32, shape, device)
+    boot = None
+    if bootstrap_value is not None:
+        boot = _dev_tensor(bootstrap_value, "bootstrap_value", torch.float32, (shape[0],), device)
+    return term, trunc, tv, boot
+
+
+def _out(out, like, name):
+    if out is None:
+        return torch.empty_like(like)
+    o = _dev_tensor(out, name, like.dtype, like.shape, like.device)
+    if o.data_ptr() != out.data_ptr():
+        raise ValueError(f"{name} must be contiguous")
+    return o
+
+
+def _launch_ctx(device, est, n, t):
+    stream = torch.cuda.current_stream(device)
+    ws = workspace(device, stream, est, n, t)
+    return ws, ws.numel(), stream.cuda_stream
+
+
+def compute_gae(rewards, values, terminateds, gamma=0.99, lambda_=0.95, *, truncateds=None,
+                trunc_values=None, bootstrap_value=None, out=None):
+    """Generalized advantage estimates, [num_envs, seq_len] float32."""
+    n, t = _rows(rewards, "rewards")
+    dev = rewards.device
+    r = _dev_tensor(rewards, "rewards", torch.float32, (n, t), None)
+    v = _dev_tensor(values, "values", torch.float32, (n, t), dev)
+    term, trunc, tv, boot = _prep_boundary((n, t), dev, terminateds, truncateds, trunc_values,
+                                           bootstrap_value)
+    adv = _out(out, r, "out")
+    ws, wsb, st = _launch_ctx(dev, "gae", n, t)
+    _check(load().lrs_gae_f32(n, t, _ptr(r), _ptr(v), _ptr(term), _ptr(trunc), _ptr(tv),
+                              _ptr(boot), gamma, lambda_, _ptr(adv), _ptr(ws), wsb, st),
+           "compute_gae")
+    return adv
+
+
+def compute_vtrace(log_rhos, rewards, values, terminateds, gamma=0.99, lambda_=1.0, *,
+                   rho_bar=1.0, c_bar=1.0, pg_rho_bar=None, truncateds=None, trunc_values=None,
+                   bootstrap_value=None, out=None):
+    """V-trace targets and policy-gradient advantages: returns (vs, pg_advantages)."""
+    n, t = _rows(rewards, "rewards")
+    dev = rewards.device
+    r = _dev_tensor(rewards, "rewards", torch.float32, (n, t), None)
+    lr = _dev_tensor(log_rhos, "log_rhos", torch.float32, (n, t), dev)
+    v = _dev_tensor(values, "values", torch.float32, (n, t), dev)
+    term, trunc, tv, boot = _prep_boundary((n, t), dev, terminateds, truncateds, trunc_values,
+                                           bootstrap_value)
+    vs = _out(None if out is None else out[0], r, "out[0]")
+    pg = _out(None if out is None else out[1], r, "out[1]")
+    if pg_rho_bar is None:
+        pg_rho_bar = rho_bar
+    ws, wsb, st = _launch_ctx(dev, "vtrace", n, t)
+    _check(load().lrs_vtrace_f32(n, t, _ptr(lr), _ptr(r), _ptr(v), _ptr(term), _ptr(trunc),
+                                 _ptr(tv), _ptr(boot), gamma, lambda_, _inf(rho_bar), _inf(c_bar),
+                                 _inf(pg_rho_bar), _ptr(vs), _ptr(pg), _ptr(ws), wsb, st),
+           "compute_vtrace")
+    return vs, pg
+
+
+def compute_retrace(log_rhos, rewards, q_values, values, terminateds, gamma=0.99, lambda_=0.95, *,
+                    c_bar=1.0, truncateds=None, trunc_values=None, bootstrap_value=None, out=None):
+    """Retrace(lambda) targets for Q(s_t, a_t); values = E_pi Q(s_t, .)."""
+    n, t = _rows(rewards, "rewards")
+    dev = rewards.device
+    r = _dev_tensor(rewards, "rewards", torch.float32, (n, t), None)
+    lr = _dev_tensor(log_rhos, "log_rhos", torch.float32, (n, t), dev)
+    q = _dev_tensor(q_values, "q_values", torch.float32, (n, t), dev)
+    v = _dev_tensor(values, "values", torch.float32, (n, t), dev)
+    term, trunc, tv, boot = _prep_boundary((n, t), dev, terminateds, truncateds, trunc_values,
+                                           bootstrap_value)
+    g = _out(out, r, "out")
+    ws, wsb, st = _launch_ctx(dev, "retrace", n, t)
+    _check(load().lrs_retrace_f32(n, t, _ptr(lr), _ptr(r), _ptr(q), _ptr(v), _ptr(term),
+                                  _ptr(trunc), _ptr(tv), _ptr(boot), gamma, lambda_, _inf(c_bar),
+                                  _ptr(g), _ptr(ws), wsb, st), "compute_retrace")
+    return g
+
+
+def compute_lambda_returns(rewards, values, terminateds, gamma=0.99, lambda_=0.95, *,
+                           truncateds=None, trunc_values=None, bootstrap_value=None, out=None):
+    """TD(lambda) returns."""
+    n, t = _rows(rewards, "rewards")
+    dev = rewards.device
+    r = _dev_tensor(rewards, "rewards", torch.float32, (n, t), None)
+    v = _dev_tensor(values, "values", torch.float32, (n, t), dev)
+    term, trunc, tv, boot = _prep_boundary((n, t), dev, terminateds, truncateds, trunc_values,
+                                           bootstrap_value)
+    g = _out(out, r, "out")
+    ws, wsb, st = _launch_ctx(dev, "lambda_returns", n, t)
+    _check(load().lrs_lambda_returns_f32(n, t, _ptr(r), _ptr(v), _ptr(term), _ptr(trunc),
+                                         _ptr(tv), _ptr(boot), gamma, lambda_, _ptr(g), _ptr(ws),
+                                         wsb, st), "compute_lambda_returns")
+    return g
+
+
+def compute_discounted_returns(rewards, terminateds, gamma=0.99, *, truncateds=None,
+                               trunc_values=None, bootstrap_value=None, out=None):
+    """Discounted reward-to-go."""
+    n, t = _rows(rewards, "rewards")
+    dev = rewards.device
+    r = _dev_tensor(rewards, "rewards", torch.float32, (n, t), None)
+    term, trunc, tv, boot = _prep_boundary((n, t), dev, terminateds, truncateds, trunc_values,
+                                           bootstrap_value)
+    g = _out(out, r, "out")
+    ws, wsb, st = _launch_ctx(dev, "discounted_returns", n, t)
+    _check(load().lrs_discounted_returns_f32(n, t, _ptr(r), _ptr(term), _ptr(trunc), _ptr(tv),
+                                             _ptr(boot), gamma, _ptr(g), _ptr(ws), wsb, st),
+           "compute_discounted_returns")
+    return g
+
+
+def compute_eligibility_traces(x, dones, gamma=0.99, lambda_=0.95, *, out=None):
+    """Accumulating eligibility traces, forward in time."""
+    n, t = _rows(x, "x")
+    dev = x.device
+    xs = _dev_tensor(x, "x", torch.float32, (n, t), None)
+    d = _mask(dones, "dones", (n, t), dev)
+    if d is None:
+        raise ValueError("dones is required")
+    e = _out(out, xs, "out")
+    ws, wsb, st = _launch_ctx(dev, "eligibility_traces", n, t)
+    _check(load().lrs_eligibility_traces_f32(n, t, _ptr(xs), _ptr(d), gamma, lambda_, _ptr(e),
+                                             _ptr(ws), wsb, st), "compute_eligibility_traces")
+    return e
+
+
+def compute_episodic_prefix_sum(x, dones, *, out=None):
+    """Inclusive prefix sum with done resets; int32 (exact) or float32 input."""
+    n, t = _rows(x, "x")
+    dev = x.device
+    if x.dtype == torch.int32:
+        xs = _dev_tensor(x, "x", torch.int32, (n, t), None)
+        fn, est = load().lrs_episodic_prefix_sum_i32, "prefix_sum_i32"
+    else:
+        xs = _dev_tensor(x, "x", torch.float32, (n, t), None)
+        fn, est = load().lrs_episodic_prefix_sum_f32, "prefix_sum_f32"
+    d = _mask(dones, "dones", (n, t), dev)
+    if d is None:
+        raise ValueError("dones is required")
+    s = _out(out, xs, "out")
+    ws, wsb, st = _launch_ctx(dev, est, n, t)
+    _check(fn(n, t, _ptr(xs), _ptr(d), _ptr(s), _ptr(ws), wsb, st), "compute_episodic_prefix_sum")
+    return s
+
+
+def _inf(x):
+    x = float(x)
+    return math.inf if math.isinf(x) and x > 0 else x

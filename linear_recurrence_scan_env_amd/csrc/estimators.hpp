@@ -1,0 +1,530 @@
+// estimators.hpp -- per-estimator coefficient construction and epilogues.
+//
+// Each functor Op<E> handles the E consecutive elements a lane owns:
+//   prepare(): load the raw streams once (vector loads), build alpha_j and
+//              beta_j in registers, keep what the epilogue needs;
+//   far_open(): whether the lane's far boundary element takes a value from
+//              beyond the lane (backward: not an episode end; forward: not a
+//              reset), used to skip the cross-tile carry when a tile ends on
+//              a boundary;
+//   finish():  given the value entering from the far side, run the lane's
+//              serial recursion, apply the epilogue, store once.
+// The [N, T] arrays are treated as one flat stream of N*T elements in which
+// row ends are ordinary segment boundaries; `Pos` gives each element's place
+// in its row.
+//
+// Definitions follow the rl-triton README Kernels table (one row per
+// estimator) and the boundary rules of the gist.science technical summary,
+// Methodology 3 (terminated: successor value 0; truncated: supplied value;
+// rollout-window end: bootstrap value in the local term only).
+#pragma once
+
+#include "scan_core.hpp"
+
+namespace lrs {
+
+struct Ctx {
+    uint64_t total;  // N*T
+    uint32_t T;      // seq_len
+    int lane;
+    bool vec;        // vector loads allowed
+};
+
+template <int E>
+struct Pos {
+    uint64_t i0;     // flat index of element 0
+    uint64_t n0;     // row of element 0
+    int count;       // valid elements (E except at the end of the array)
+    uint32_t last;   // bit j: element j is the last step of its row
+    uint32_t first;  // bit j: element j is the first step of its row
+};
+
+// Value of stream p at flat index i0+E (element 0 of the next lane), taken
+// from the neighbouring lane; the last lane of a wave reads it from memory,
+// and only when it is used.
+template <int E>
+__device__ __forceinline__ float next_elem(float my0, const float* __restrict__ p,
+                                           const Pos<E>& P, const Ctx& c, bool used)
+{
+    float v = shfl_down(my0, 1);
+    if (c.lane == kWave - 1) v = (used && P.i0 + E < c.total) ? p[P.i0 + E] : 0.0f;
+    return v;
+}
+
+// ------------------------------------------------ backward episode ends
+// end_j  = terminated_j | truncated_j | last-in-row_j
+// vend_j = successor value at an end: 0 if terminated, else trunc_values if
+//          truncated, else the row's bootstrap value (0 if none).
+// trunc_values is read only at truncated steps, bootstrap only at row ends.
+template <int E>
+struct Ends {
+    uint32_t end;
+    float vend[E];
+};
+
+struct BoundaryArgs {
+    const uint8_t* term;
+    const uint8_t* trunc;   // nullable
+    const float* tv;        // read only where trunc
+    const float* boot;      // nullable
+};
+
+template <int E>
+__device__ __forceinline__ Ends<E> load_ends(const BoundaryArgs& b, const Pos<E>& P, const Ctx& c)
+{
+    const uint32_t tau = load_mask<E>(b.term, P.i0, P.count, c.vec);
+    const uint32_t kap = b.trunc ? load_mask<E>(b.trunc, P.i0, P.count, c.vec) : 0u;
+    Ends<E> r;
+    r.end = tau | kap | P.last;
+    uint64_t n = P.n0;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+        float v = 0.0f;
+        if (!((tau >> j) & 1u)) {
+            if ((kap >> j) & 1u)
+                v = b.tv[P.i0 + j];
+            else if (((P.last >> j) & 1u) && b.boot)
+                v = b.boot[n];
+        }
+        r.vend[j] = v;
+        if ((P.last >> j) & 1u) ++n;
+    }
+    return r;
+}
+
+// Elements past the end of the array are identities.
+template <int E, class T>
+__device__ __forceinline__ void clear_tail(T (&alpha)[E], T (&beta)[E], int count)
+{
+#pragma unroll
+    for (int j = 0; j < E; ++j)
+        if (j >= count) {
+            alpha[j] = T(0);
+            beta[j] = T(1);
+        }
+}
+
+template <int E>
+__device__ __forceinline__ void backward_pass(float (&out)[E], const float (&alpha)[E],
+                                              const float (&beta)[E], float carry)
+{
+    float a = carry;
+#pragma unroll
+    for (int j = E - 1; j >= 0; --j) {
+        a = fmaf(beta[j], a, alpha[j]);
+        out[j] = a;
+    }
+}
+
+// --------------------------------------------------------------- GAE
+// README Kernels table (compute_gae): delta_t = r_t + gamma*Vnext_t - V_t,
+// A_t = delta_t + gamma*lambda*A_{t+1} inside an episode.
+struct GaeArgs {
+    BoundaryArgs b;
+    const float* rewards;
+    const float* values;
+    float gamma, gl;  // gl = fp32(gamma*lambda)
+    float* adv;
+};
+
+template <int E>
+struct GaeOp {
+    using T = float;
+    using Args = GaeArgs;
+    static constexpr bool kBackward = true;
+    struct State {
+        uint32_t end;
+    };
+
+    __device__ static void prepare(const Args& a, const Pos<E>& P, const Ctx& c, float (&alpha)[E],
+                                   float (&beta)[E], State& s)
+    {
+        float r[E], v[E];
+        load_f32<E>(r, a.rewards, P.i0, P.count, c.vec);
+        load_f32<E>(v, a.values, P.i0, P.count, c.vec);
+        const Ends<E> e = load_ends<E>(a.b, P, c);
+        const float vnx = next_elem<E>(v[0], a.values, P, c, !((e.end >> (E - 1)) & 1u));
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            const bool end = (e.end >> j) & 1u;
+            const float v1 = (j + 1 < E) ? v[(j + 1) % E] : vnx;
+            const float vn = end ? e.vend[j] : v1;
+            alpha[j] = fmaf(a.gamma, vn, r[j]) - v[j];
+            beta[j] = end ? 0.0f : a.gl;
+        }
+        clear_tail<E>(alpha, beta, P.count);
+        s.end = e.end;
+    }
+    __device__ static bool far_open(const State& s) { return !((s.end >> (E - 1)) & 1u); }
+    __device__ static void finish(const Args& a, const Pos<E>& P, const Ctx& c,
+                                  const float (&alpha)[E], const float (&beta)[E], const State&,
+                                  float carry)
+    {
+        float out[E];
+        backward_pass<E>(out, alpha, beta, carry);
+        store_f32<E>(a.adv, out, P.i0, P.count, c.vec);
+    }
+};
+
+// -------------------------------------------------------- TD(lambda) returns
+// README Kernels table (compute_lambda_returns):
+// G_t = r_t + gamma*((1-lambda)*V_{t+1} + lambda*G_{t+1}) inside an episode,
+// G_t = r_t + gamma*Vnext_t at its end.
+struct LambdaArgs {
+    BoundaryArgs b;
+    const float* rewards;
+    const float* values;
+    float gamma, gl, g1l;  // gl = fp32(gamma*lambda), g1l = fp32(gamma*(1-lambda))
+    float* out;
+};
+
+template <int E>
+struct LambdaOp {
+    using T = float;
+    using Args = LambdaArgs;
+    static constexpr bool kBackward = true;
+    struct State {
+        uint32_t end;
+    };
+
+    __device__ static void prepare(const Args& a, const Pos<E>& P, const Ctx& c, float (&alpha)[E],
+                                   float (&beta)[E], State& s)
+    {
+        float r[E], v[E];
+        load_f32<E>(r, a.rewards, P.i0, P.count, c.vec);
+        load_f32<E>(v, a.values, P.i0, P.count, c.vec);
+        const Ends<E> e = load_ends<E>(a.b, P, c);
+        const float vnx = next_elem<E>(v[0], a.values, P, c, !((e.end >> (E - 1)) & 1u));
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            const bool end = (e.end >> j) & 1u;
+            const float v1 = (j + 1 < E) ? v[(j + 1) % E] : vnx;
+            alpha[j] = end ? fmaf(a.gamma, e.vend[j], r[j]) : fmaf(a.g1l, v1, r[j]);
+            beta[j] = end ? 0.0f : a.gl;
+        }
+        clear_tail<E>(alpha, beta, P.count);
+        s.end = e.end;
+    }
+    __device__ static bool far_open(const State& s) { return !((s.end >> (E - 1)) & 1u); }
+    __device__ static void finish(const Args& a, const Pos<E>& P, const Ctx& c,
+                                  const float (&alpha)[E], const float (&beta)[E], const State&,
+                                  float carry)
+    {
+        float out[E];
+        backward_pass<E>(out, alpha, beta, carry);
+        store_f32<E>(a.out, out, P.i0, P.count, c.vec);
+    }
+};
+
+// --------------------------------------------------------- discounted returns
+// README Kernels table (compute_discounted_returns): G_t = r_t + gamma*G_{t+1}
+// inside an episode, r_t + gamma*Vnext_t at its end (values never read).
+struct DiscArgs {
+    BoundaryArgs b;
+    const float* rewards;
+    float gamma;
+    float* out;
+};
+
+template <int E>
+struct DiscOp {
+    using T = float;
+    using Args = DiscArgs;
+    static constexpr bool kBackward = true;
+    struct State {
+        uint32_t end;
+    };
+
+    __device__ static void prepare(const Args& a, const Pos<E>& P, const Ctx& c, float (&alpha)[E],
+                                   float (&beta)[E], State& s)
+    {
+        float r[E];
+        load_f32<E>(r, a.rewards, P.i0, P.count, c.vec);
+        const Ends<E> e = load_ends<E>(a.b, P, c);
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            const bool end = (e.end >> j) & 1u;
+            alpha[j] = end ? fmaf(a.gamma, e.vend[j], r[j]) : r[j];
+            beta[j] = end ? 0.0f : a.gamma;
+        }
+        clear_tail<E>(alpha, beta, P.count);
+        s.end = e.end;
+    }
+    __device__ static bool far_open(const State& s) { return !((s.end >> (E - 1)) & 1u); }
+    __device__ static void finish(const Args& a, const Pos<E>& P, const Ctx& c,
+                                  const float (&alpha)[E], const float (&beta)[E], const State&,
+                                  float carry)
+    {
+        float out[E];
+        backward_pass<E>(out, alpha, beta, carry);
+        store_f32<E>(a.out, out, P.i0, P.count, c.vec);
+    }
+};
+
+// ------------------------------------------------------------------ V-trace
+// README Kernels table (compute_vtrace: importance-weighted targets and
+// advantages); Espeholt et al. 2018 eq. 1 with c_t = lambda*min(c_bar, w_t):
+// A_t = rho_t*(r_t + gamma*Vnext_t - V_t) + gamma*c_t*A_{t+1}, vs_t = V_t + A_t,
+// pg_t = min(pg_rho_bar, w_t)*(r_t + gamma*(end_t ? Vnext_t : vs_{t+1}) - V_t).
+struct VtraceArgs {
+    BoundaryArgs b;
+    const float* log_rhos;
+    const float* rewards;
+    const float* values;
+    float gamma, lambda, rho_bar, c_bar, pg_rho_bar;
+    float* vs;
+    float* pg;
+};
+
+template <int E>
+struct VtraceOp {
+    using T = float;
+    using Args = VtraceArgs;
+    static constexpr bool kBackward = true;
+    struct State {
+        uint32_t end;
+        float r[E], v[E], tgt[E], rho_pg[E];  // tgt: Vnext at ends, V_{t+1} elsewhere
+    };
+
+    __device__ static void prepare(const Args& a, const Pos<E>& P, const Ctx& c, float (&alpha)[E],
+                                   float (&beta)[E], State& s)
+    {
+        float lr[E];
+        load_f32<E>(lr, a.log_rhos, P.i0, P.count, c.vec);
+        load_f32<E>(s.r, a.rewards, P.i0, P.count, c.vec);
+        load_f32<E>(s.v, a.values, P.i0, P.count, c.vec);
+        const Ends<E> e = load_ends<E>(a.b, P, c);
+        const float vnx = next_elem<E>(s.v[0], a.values, P, c, !((e.end >> (E - 1)) & 1u));
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            const bool end = (e.end >> j) & 1u;
+            const float w = expf(lr[j]);
+            const float rho = fminf(a.rho_bar, w);
+            const float cc = a.lambda * fminf(a.c_bar, w);
+            const float v1 = (j + 1 < E) ? s.v[(j + 1) % E] : vnx;
+            const float vn = end ? e.vend[j] : v1;
+            s.tgt[j] = vn;
+            s.rho_pg[j] = fminf(a.pg_rho_bar, w);
+            alpha[j] = rho * (fmaf(a.gamma, vn, s.r[j]) - s.v[j]);
+            beta[j] = end ? 0.0f : a.gamma * cc;
+        }
+        clear_tail<E>(alpha, beta, P.count);
+        s.end = e.end;
+    }
+    __device__ static bool far_open(const State& s) { return !((s.end >> (E - 1)) & 1u); }
+    __device__ static void finish(const Args& a, const Pos<E>& P, const Ctx& c,
+                                  const float (&alpha)[E], const float (&beta)[E], const State& s,
+                                  float carry)
+    {
+        float vs[E], pg[E];
+        float a_next = carry;  // A at the element after j
+#pragma unroll
+        for (int j = E - 1; j >= 0; --j) {
+            const float A = fmaf(beta[j], a_next, alpha[j]);
+            const bool end = (s.end >> j) & 1u;
+            const float target = end ? s.tgt[j] : s.tgt[j] + a_next;  // Vnext or vs_{t+1}
+            vs[j] = s.v[j] + A;
+            pg[j] = s.rho_pg[j] * (fmaf(a.gamma, target, s.r[j]) - s.v[j]);
+            a_next = A;
+        }
+        store_f32<E>(a.vs, vs, P.i0, P.count, c.vec);
+        store_f32<E>(a.pg, pg, P.i0, P.count, c.vec);
+    }
+};
+
+// ------------------------------------------------------------------ Retrace
+// README Kernels table (compute_retrace: off-policy return with truncated
+// importance ratios); Munos et al. 2016 with c_{t+1} = lambda*min(c_bar, w_{t+1}):
+// G_t = r_t + gamma*(V_{t+1} - c_{t+1}*Q_{t+1}) + gamma*c_{t+1}*G_{t+1} inside
+// an episode, r_t + gamma*Vnext_t at its end.
+struct RetraceArgs {
+    BoundaryArgs b;
+    const float* log_rhos;
+    const float* rewards;
+    const float* q_values;
+    const float* values;
+    float gamma, lambda, c_bar;
+    float* out;
+};
+
+template <int E>
+struct RetraceOp {
+    using T = float;
+    using Args = RetraceArgs;
+    static constexpr bool kBackward = true;
+    struct State {
+        uint32_t end;
+    };
+
+    __device__ static float trace(const Args& a, float lr)
+    {
+        return a.lambda * fminf(a.c_bar, expf(lr));
+    }
+
+    __device__ static void prepare(const Args& a, const Pos<E>& P, const Ctx& c, float (&alpha)[E],
+                                   float (&beta)[E], State& s)
+    {
+        float lr[E], r[E], q[E], v[E], cc[E];
+        load_f32<E>(lr, a.log_rhos, P.i0, P.count, c.vec);
+        load_f32<E>(r, a.rewards, P.i0, P.count, c.vec);
+        load_f32<E>(q, a.q_values, P.i0, P.count, c.vec);
+        load_f32<E>(v, a.values, P.i0, P.count, c.vec);
+        const Ends<E> e = load_ends<E>(a.b, P, c);
+#pragma unroll
+        for (int j = 0; j < E; ++j) cc[j] = trace(a, lr[j]);
+        const bool used = !((e.end >> (E - 1)) & 1u);
+        // successor (t+1) quantities of the lane's last element
+        float cnx = shfl_down(cc[0], 1);
+        const float qnx = next_elem<E>(q[0], a.q_values, P, c, used);
+        const float vnx = next_elem<E>(v[0], a.values, P, c, used);
+        if (c.lane == kWave - 1)
+            cnx = (used && P.i0 + E < c.total) ? trace(a, a.log_rhos[P.i0 + E]) : 0.0f;
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            const bool end = (e.end >> j) & 1u;
+            const float c1 = (j + 1 < E) ? cc[(j + 1) % E] : cnx;
+            const float q1 = (j + 1 < E) ? q[(j + 1) % E] : qnx;
+            const float v1 = (j + 1 < E) ? v[(j + 1) % E] : vnx;
+            alpha[j] = end ? fmaf(a.gamma, e.vend[j], r[j]) : fmaf(a.gamma, fmaf(-c1, q1, v1), r[j]);
+            beta[j] = end ? 0.0f : a.gamma * c1;
+        }
+        clear_tail<E>(alpha, beta, P.count);
+        s.end = e.end;
+    }
+    __device__ static bool far_open(const State& s) { return !((s.end >> (E - 1)) & 1u); }
+    __device__ static void finish(const Args& a, const Pos<E>& P, const Ctx& c,
+                                  const float (&alpha)[E], const float (&beta)[E], const State&,
+                                  float carry)
+    {
+        float out[E];
+        backward_pass<E>(out, alpha, beta, carry);
+        store_f32<E>(a.out, out, P.i0, P.count, c.vec);
+    }
+};
+
+// --------------------------------------------------- forward estimators
+// reset_j = first-in-row_j | dones_{j-1}.  dones of the element before the
+// lane comes from the neighbouring lane (lane 0 of a wave reads it).
+template <int E>
+__device__ __forceinline__ uint32_t load_resets(const uint8_t* __restrict__ dones, const Pos<E>& P,
+                                                const Ctx& c)
+{
+    const uint32_t d = load_mask<E>(dones, P.i0, P.count, c.vec);
+    uint32_t dprev = (uint32_t)__shfl_up((int)((d >> (E - 1)) & 1u), 1, kWave);
+    if (c.lane == 0)
+        dprev = (!(P.first & 1u) && P.i0 > 0 && P.i0 - 1 < c.total) ? (dones[P.i0 - 1] != 0) : 0u;
+    return P.first | (d << 1) | dprev;  // bit j: reset at element j
+}
+
+struct ForwardArgs {
+    const void* x;
+    const uint8_t* dones;
+    float gl;  // eligibility traces: fp32(gamma*lambda)
+    void* out;
+};
+
+// README Kernels table (compute_eligibility_traces):
+// e_t = x_t + gamma*lambda*(1 - d_{t-1})*e_{t-1}.
+template <int E>
+struct EligOp {
+    using T = float;
+    using Args = ForwardArgs;
+    static constexpr bool kBackward = false;
+    struct State {
+        uint32_t reset;
+    };
+    __device__ static void prepare(const Args& a, const Pos<E>& P, const Ctx& c, float (&alpha)[E],
+                                   float (&beta)[E], State& s)
+    {
+        load_f32<E>(alpha, (const float*)a.x, P.i0, P.count, c.vec);
+        s.reset = load_resets<E>(a.dones, P, c);
+#pragma unroll
+        for (int j = 0; j < E; ++j) beta[j] = ((s.reset >> j) & 1u) ? 0.0f : a.gl;
+        clear_tail<E>(alpha, beta, P.count);
+    }
+    __device__ static bool far_open(const State& s) { return !(s.reset & 1u); }
+    __device__ static void finish(const Args& a, const Pos<E>& P, const Ctx& c,
+                                  const float (&alpha)[E], const float (&beta)[E], const State&,
+                                  float carry)
+    {
+        float out[E];
+        float e = carry;
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            e = fmaf(beta[j], e, alpha[j]);
+            out[j] = e;
+        }
+        store_f32<E>((float*)a.out, out, P.i0, P.count, c.vec);
+    }
+};
+
+// README Kernels table (compute_episodic_prefix_sum): S_t = x_t + (1 - d_{t-1})*S_{t-1}.
+template <int E>
+struct PrefixF32Op {
+    using T = float;
+    using Args = ForwardArgs;
+    static constexpr bool kBackward = false;
+    struct State {
+        uint32_t reset;
+    };
+    __device__ static void prepare(const Args& a, const Pos<E>& P, const Ctx& c, float (&alpha)[E],
+                                   float (&beta)[E], State& s)
+    {
+        load_f32<E>(alpha, (const float*)a.x, P.i0, P.count, c.vec);
+        s.reset = load_resets<E>(a.dones, P, c);
+#pragma unroll
+        for (int j = 0; j < E; ++j) beta[j] = ((s.reset >> j) & 1u) ? 0.0f : 1.0f;
+        clear_tail<E>(alpha, beta, P.count);
+    }
+    __device__ static bool far_open(const State& s) { return !(s.reset & 1u); }
+    __device__ static void finish(const Args& a, const Pos<E>& P, const Ctx& c,
+                                  const float (&alpha)[E], const float (&beta)[E], const State& s,
+                                  float carry)
+    {
+        float out[E];
+        float e = carry;
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            e = ((s.reset >> j) & 1u) ? alpha[j] : e + alpha[j];
+            out[j] = e;
+        }
+        (void)beta;
+        store_f32<E>((float*)a.out, out, P.i0, P.count, c.vec);
+    }
+};
+
+template <int E>
+struct PrefixI32Op {
+    using T = uint32_t;
+    using Args = ForwardArgs;
+    static constexpr bool kBackward = false;
+    struct State {
+        uint32_t reset;
+    };
+    __device__ static void prepare(const Args& a, const Pos<E>& P, const Ctx& c,
+                                   uint32_t (&alpha)[E], uint32_t (&beta)[E], State& s)
+    {
+        load_u32<E>(alpha, (const int32_t*)a.x, P.i0, P.count, c.vec);
+        s.reset = load_resets<E>(a.dones, P, c);
+#pragma unroll
+        for (int j = 0; j < E; ++j) beta[j] = ((s.reset >> j) & 1u) ? 0u : 1u;
+        clear_tail<E>(alpha, beta, P.count);
+    }
+    __device__ static bool far_open(const State& s) { return !(s.reset & 1u); }
+    __device__ static void finish(const Args& a, const Pos<E>& P, const Ctx& c,
+                                  const uint32_t (&alpha)[E], const uint32_t (&beta)[E],
+                                  const State& s, uint32_t carry)
+    {
+        uint32_t out[E];
+        uint32_t e = carry;
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            e = ((s.reset >> j) & 1u) ? alpha[j] : e + alpha[j];
+            out[j] = e;
+        }
+        (void)beta;
+        store_u32<E>((int32_t*)a.out, out, P.i0, P.count, c.vec);
+    }
+};
+
+}  // namespace lrs

@@ -1,0 +1,523 @@
+// lrs.hip -- gfx950 kernels and the C ABI declared in include/lrs.h.
+//
+// One kernel template serves all seven estimators.  The [N, T] input is one
+// flat stream of N*T elements; row ends are segment boundaries like episode
+// ends, so rows never need separate handling.  A block owns a tile of
+// E*64*W consecutive elements; each lane owns E of them:
+//   1. vector-load the raw streams once, build (alpha, beta) in registers;
+//   2. compose the lane's E maps serially, then a 6-step wave64 scan;
+//   3. combine the W wave aggregates through LDS;
+//   4. if rows straddle tiles, obtain the value entering the tile from the
+//      neighbouring tiles' published aggregates (decoupled look-back over
+//      aggregates only, in ticket order);
+//   5. apply the carry, run each lane's recursion, store once.
+// Nothing but the final outputs (and 16 bytes of aggregate per tile on the
+// look-back path) is written to HBM: one read of each input, one write of
+// each output, as the rl-triton paper's fused kernels do (gist.science
+// technical summary, Methodology 2).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/lrs.h"
+#include "estimators.hpp"
+
+namespace lrs {
+
+struct Sched {
+    uint64_t total;      // N*T
+    uint8_t* ws;         // workspace (look-back only)
+    uint32_t T;
+    uint32_t num_tiles;
+    int lookback;
+    int vec;
+};
+
+// Called once per block after its last look-back read.  The block that
+// completes the launch resets the ticket counters and moves the epoch on;
+// every other block has read the epoch before counting itself out.
+__device__ __forceinline__ void finish_launch(WsHeader* hdr, uint32_t num_tiles, uint32_t tag)
+{
+    const uint32_t done =
+        __hip_atomic_fetch_add(&hdr->exited, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == num_tiles - 1u) {
+        uint32_t next = tag;                 // = epoch + 1
+        if (next == 0xffffffffu) next = 0u;  // keep tags (epoch + 1) nonzero
+        __hip_atomic_store(&hdr->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&hdr->exited, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&hdr->epoch, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+template <class Op, int E, int W>
+__global__ __launch_bounds__(W * kWave) void scan_kernel(const typename Op::Args args, const Sched s)
+{
+    using T = typename Op::T;
+    constexpr bool kB = Op::kBackward;
+    constexpr uint32_t kTile = (uint32_t)E * kWave * W;
+
+    __shared__ T sh_a[W];
+    __shared__ T sh_b[W];
+    __shared__ T sh_carry;
+    __shared__ uint32_t sh_tile, sh_tag, sh_open;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    WsHeader* hdr = reinterpret_cast<WsHeader*>(s.ws);
+    uint64_t* rec = reinterpret_cast<uint64_t*>(s.ws + sizeof(WsHeader));
+
+    uint32_t tile = blockIdx.x, tag = 0;
+    if (s.lookback) {
+        if (tid == 0) {
+            const uint32_t ticket =
+                __hip_atomic_fetch_add(&hdr->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t epoch =
+                __hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (ticket >= s.num_tiles) {  // header not in its reset state
+                __hip_atomic_fetch_or(&hdr->error, kErrTicket, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+                sh_tile = 0xffffffffu;
+            } else {
+                sh_tile = kB ? s.num_tiles - 1u - ticket : ticket;
+            }
+            sh_tag = epoch + 1u;
+        }
+        __syncthreads();
+        tile = sh_tile;
+        tag = sh_tag;
+        if (tile == 0xffffffffu) {
+            if (tid == 0) finish_launch(hdr, s.num_tiles, tag);
+            return;
+        }
+    }
+
+    // Where this lane's elements sit in their rows.
+    const uint64_t tile_start = (uint64_t)tile * kTile;
+    const uint64_t tile_row = tile_start / s.T;
+    const uint32_t tile_t = (uint32_t)(tile_start - tile_row * s.T);
+    const uint32_t off = (uint32_t)tid * E;
+    Pos<E> P;
+    P.i0 = tile_start + off;
+    P.count = P.i0 >= s.total ? 0 : (int)((s.total - P.i0) < (uint64_t)E ? (s.total - P.i0) : E);
+    {
+        const uint32_t u = tile_t + off;
+        P.n0 = tile_row + u / s.T;
+        uint32_t t = u % s.T;
+        P.last = 0;
+        P.first = 0;
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            if (t == s.T - 1) P.last |= 1u << j;
+            if (t == 0) P.first |= 1u << j;
+            t = (t == s.T - 1) ? 0u : t + 1u;
+        }
+        const uint32_t valid = (P.count >= 32) ? ~0u : ((1u << P.count) - 1u);
+        P.last &= valid;
+        P.first &= valid;
+    }
+    const Ctx c{s.total, s.T, lane, s.vec != 0};
+
+    T alpha[E], beta[E];
+    typename Op::State st;
+    Op::prepare(args, P, c, alpha, beta, st);
+
+    // Lane aggregate, then the wave scan.
+    Aff<T> agg = identity<T>();
+    if (kB) {
+#pragma unroll
+        for (int j = E - 1; j >= 0; --j) agg = combine(Aff<T>{alpha[j], beta[j]}, agg);
+    } else {
+#pragma unroll
+        for (int j = 0; j < E; ++j) agg = combine(Aff<T>{alpha[j], beta[j]}, agg);
+    }
+    const Aff<T> inc = wave_scan<kB>(agg, lane);
+    const Aff<T> exc = wave_exclusive<kB>(inc, lane);
+    if (lane == (kB ? 0 : kWave - 1)) {
+        sh_a[wave] = inc.a;
+        sh_b[wave] = inc.b;
+    }
+    if (kB ? (tid == W * kWave - 1) : (tid == 0)) sh_open = Op::far_open(st) ? 1u : 0u;
+    __syncthreads();
+
+    // Compose the wave aggregates: the whole tile, and the waves beyond mine.
+    Aff<T> tile_agg = identity<T>(), beyond = identity<T>();
+    if (kB) {
+#pragma unroll
+        for (int v = W - 1; v >= 0; --v) {
+            const Aff<T> x{sh_a[v], sh_b[v]};
+            tile_agg = combine(x, tile_agg);
+            if (v > wave) beyond = combine(x, beyond);
+        }
+    } else {
+#pragma unroll
+        for (int v = 0; v < W; ++v) {
+            const Aff<T> x{sh_a[v], sh_b[v]};
+            tile_agg = combine(x, tile_agg);
+            if (v < wave) beyond = combine(x, beyond);
+        }
+    }
+
+    T carry = T(0);
+    if (s.lookback) {
+        if (wave == 0) {
+            if (lane == 0) publish_aggregate<T>(rec, tile, tag, tile_agg);
+            const bool far_most = kB ? (tile == s.num_tiles - 1u) : (tile == 0u);
+            T cin = T(0);
+            if (!far_most && sh_open)
+                cin = lookback_carry<kB, T>(rec, tile, s.num_tiles, tag, lane, &hdr->error);
+            if (lane == 0) {
+                sh_carry = cin;
+                finish_launch(hdr, s.num_tiles, tag);
+            }
+        }
+        __syncthreads();
+        carry = sh_carry;
+    }
+
+    const T wave_in = apply(beyond, carry);
+    const T lane_in = apply(exc, wave_in);
+    Op::finish(args, P, c, alpha, beta, st, lane_in);
+}
+
+// ------------------------------------------------------------ host side
+
+struct Cfg {
+    int E, W;
+    uint32_t tile() const { return (uint32_t)(E * kWave * W); }
+};
+constexpr int kNumCfg = 4;
+constexpr Cfg kCfgs[kNumCfg] = {{4, 1}, {4, 4}, {8, 4}, {8, 16}};
+constexpr uint32_t kMinTile = 256;
+constexpr int kLookbackCfg = 2;  // 2048-element tiles
+
+std::atomic<int> g_force_lookback{0};
+std::atomic<int> g_forced_cfg{-1};
+
+thread_local char g_err[512];
+
+lrs_status fail(lrs_status st, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+bool valid_sizes(int64_t N, int64_t T)
+{
+    if (N < 1 || T < 1 || T >= (int64_t(1) << 31)) return false;
+    if (N > (int64_t(1) << 34) / T) return false;
+    return N * T < (int64_t(1) << 34);
+}
+
+size_t workspace_bytes_for(uint64_t total)
+{
+    return sizeof(WsHeader) + 16 * ((total + kMinTile - 1) / kMinTile);
+}
+
+// Pick the tile: prefer a tile holding whole rows (no cross-tile carry) with
+// enough blocks to spread over the 256 CUs; otherwise the look-back path.
+int choose_cfg(uint64_t total, uint64_t T, bool* lookback)
+{
+    const int forced = g_forced_cfg.load();
+    const bool force_lb = g_force_lookback.load() != 0;
+    if (forced >= 0 || force_lb) {
+        const int c = forced >= 0 ? forced : 0;
+        const uint64_t tiles = (total + kCfgs[c].tile() - 1) / kCfgs[c].tile();
+        *lookback = force_lb || (tiles > 1 && kCfgs[c].tile() % T != 0);
+        return c;
+    }
+    const int pref[kNumCfg] = {2, 3, 1, 0};
+    int best = -1;
+    uint64_t best_tiles = 0;
+    for (int p : pref) {
+        const Cfg& k = kCfgs[p];
+        const uint64_t tiles = (total + k.tile() - 1) / k.tile();
+        if (k.tile() % T != 0 && tiles > 1) continue;  // rows would straddle tiles
+        if (tiles >= 512) {
+            best = p;
+            break;
+        }
+        if (tiles > best_tiles) {
+            best = p;
+            best_tiles = tiles;
+        }
+    }
+    if (best >= 0) {
+        *lookback = false;
+        return best;
+    }
+    *lookback = true;
+    return kLookbackCfg;
+}
+
+bool aligned(const void* p, uintptr_t a) { return p == nullptr || ((uintptr_t)p % a) == 0; }
+
+template <class Op, int E, int W>
+hipError_t launch_cfg(const typename Op::Args& a, const Sched& s, hipStream_t stream)
+{
+    void* kargs[] = {(void*)&a, (void*)&s};
+    return hipLaunchKernel((const void*)&scan_kernel<Op, E, W>, dim3(s.num_tiles), dim3(W * kWave),
+                           kargs, 0, stream);
+}
+
+template <template <int> class Op>
+hipError_t launch_any(int cfg, const typename Op<4>::Args& a, const Sched& s, hipStream_t stream)
+{
+    switch (cfg) {
+        case 0: return launch_cfg<Op<4>, 4, 1>(a, s, stream);
+        case 1: return launch_cfg<Op<4>, 4, 4>(a, s, stream);
+        case 2: return launch_cfg<Op<8>, 8, 4>(a, s, stream);
+        default: return launch_cfg<Op<8>, 8, 16>(a, s, stream);
+    }
+}
+
+// Shared checks and launch.  floats/masks: every array the kernel may
+// vector-load, for the alignment decision.
+template <template <int> class Op>
+lrs_status run(const char* name, int64_t N, int64_t T, const typename Op<4>::Args& a,
+               const void* const* floats, int nfloats, const void* const* masks, int nmasks,
+               void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    const uint64_t total = (uint64_t)N * (uint64_t)T;
+    bool lookback = false;
+    const int cfg = choose_cfg(total, (uint64_t)T, &lookback);
+    const Cfg& k = kCfgs[cfg];
+    Sched s{};
+    s.total = total;
+    s.T = (uint32_t)T;
+    s.num_tiles = (uint32_t)((total + k.tile() - 1) / k.tile());
+    s.lookback = lookback ? 1 : 0;
+    s.ws = static_cast<uint8_t*>(ws);
+    if (lookback) {
+        const size_t need = sizeof(WsHeader) + 16 * (size_t)s.num_tiles;
+        if (ws == nullptr || ws_bytes < need)
+            return fail(LRS_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", name,
+                        need, ws == nullptr ? (size_t)0 : ws_bytes);
+        if (!aligned(ws, 16)) return fail(LRS_ERR_WORKSPACE, "%s: workspace not 16-byte aligned", name);
+    }
+    bool vec = true;
+    for (int i = 0; i < nfloats; ++i) vec = vec && aligned(floats[i], 16);
+    for (int i = 0; i < nmasks; ++i) vec = vec && aligned(masks[i], (uintptr_t)k.E);
+    s.vec = vec ? 1 : 0;
+    const hipError_t e = launch_any<Op>(cfg, a, s, stream);
+    if (e != hipSuccess)
+        return fail(LRS_ERR_HIP, "%s: kernel launch failed: %s", name, hipGetErrorString(e));
+    g_err[0] = '\0';
+    return LRS_OK;
+}
+
+bool unit_interval(float x) { return x >= 0.0f && x <= 1.0f; }  // false for NaN
+bool positive(float x) { return x > 0.0f; }                       // +inf allowed, NaN not
+
+lrs_status check_common(const char* name, int64_t N, int64_t T)
+{
+    if (!valid_sizes(N, T))
+        return fail(LRS_ERR_INVALID_ARG,
+                    "%s: need num_envs >= 1, 1 <= seq_len < 2^31, num_envs*seq_len < 2^34 "
+                    "(got %lld x %lld)",
+                    name, (long long)N, (long long)T);
+    return LRS_OK;
+}
+
+lrs_status check_boundary(const char* name, const uint8_t* term, const uint8_t* trunc,
+                          const float* tv)
+{
+    if (term == nullptr) return fail(LRS_ERR_INVALID_ARG, "%s: terminateds is required", name);
+    if (trunc != nullptr && tv == nullptr)
+        return fail(LRS_ERR_INVALID_ARG, "%s: truncateds given without trunc_values", name);
+    return LRS_OK;
+}
+
+#define LRS_REQUIRE(cond, ...)                                   \
+    do {                                                         \
+        if (!(cond)) return fail(LRS_ERR_INVALID_ARG, __VA_ARGS__); \
+    } while (0)
+
+#define LRS_TRY(expr)                      \
+    do {                                   \
+        const lrs_status st_ = (expr);     \
+        if (st_ != LRS_OK) return st_;     \
+    } while (0)
+
+}  // namespace lrs
+
+using namespace lrs;
+
+extern "C" {
+
+int lrs_version(void) { return 100; }
+
+const char* lrs_status_string(lrs_status s)
+{
+    switch (s) {
+        case LRS_OK: return "success";
+        case LRS_ERR_INVALID_ARG: return "invalid argument";
+        case LRS_ERR_WORKSPACE: return "workspace missing or too small";
+        case LRS_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* lrs_last_error(void) { return g_err; }
+
+size_t lrs_workspace_bytes(lrs_estimator est, int64_t num_envs, int64_t seq_len)
+{
+    if ((int)est < 0 || (int)est > (int)LRS_PREFIX_SUM_F32) return 0;
+    if (!valid_sizes(num_envs, seq_len)) return 0;
+    return workspace_bytes_for((uint64_t)num_envs * (uint64_t)seq_len);
+}
+
+lrs_status lrs_debug_set_schedule(int force_lookback, int elems_per_lane, int waves_per_block)
+{
+    int cfg = -1;
+    if (elems_per_lane != 0 || waves_per_block != 0) {
+        for (int i = 0; i < kNumCfg; ++i)
+            if (kCfgs[i].E == elems_per_lane && kCfgs[i].W == waves_per_block) cfg = i;
+        if (cfg < 0)
+            return fail(LRS_ERR_INVALID_ARG, "lrs_debug_set_schedule: unsupported tile %d x %d",
+                        elems_per_lane, waves_per_block);
+    }
+    g_force_lookback.store(force_lookback != 0);
+    g_forced_cfg.store(cfg);
+    return LRS_OK;
+}
+
+lrs_status lrs_gae_f32(int64_t N, int64_t T, const float* rewards, const float* values,
+                       const uint8_t* term, const uint8_t* trunc, const float* tv,
+                       const float* boot, float gamma, float lambda, float* adv, void* ws,
+                       size_t ws_bytes, hipStream_t stream)
+{
+    const char* nm = "lrs_gae_f32";
+    LRS_TRY(check_common(nm, N, T));
+    LRS_REQUIRE(rewards && values && adv, "%s: rewards, values and advantages are required", nm);
+    LRS_TRY(check_boundary(nm, term, trunc, tv));
+    LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda), "%s: gamma and lambda must be in [0, 1]", nm);
+    GaeArgs a{{term, trunc, tv, boot}, rewards, values, gamma,
+              (float)((double)gamma * (double)lambda), adv};
+    const void* f[] = {rewards, values, adv};
+    const void* m[] = {term, trunc};
+    return run<GaeOp>(nm, N, T, a, f, 3, m, 2, ws, ws_bytes, stream);
+}
+
+lrs_status lrs_vtrace_f32(int64_t N, int64_t T, const float* log_rhos, const float* rewards,
+                          const float* values, const uint8_t* term, const uint8_t* trunc,
+                          const float* tv, const float* boot, float gamma, float lambda,
+                          float rho_bar, float c_bar, float pg_rho_bar, float* vs,
+                          float* pg_adv, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    const char* nm = "lrs_vtrace_f32";
+    LRS_TRY(check_common(nm, N, T));
+    LRS_REQUIRE(log_rhos && rewards && values && vs && pg_adv,
+                "%s: log_rhos, rewards, values, vs and pg_advantages are required", nm);
+    LRS_TRY(check_boundary(nm, term, trunc, tv));
+    LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda), "%s: gamma and lambda must be in [0, 1]", nm);
+    LRS_REQUIRE(positive(rho_bar) && positive(c_bar) && positive(pg_rho_bar),
+                "%s: rho_bar, c_bar and pg_rho_bar must be > 0", nm);
+    VtraceArgs a{{term, trunc, tv, boot}, log_rhos, rewards, values, gamma, lambda,
+                 rho_bar, c_bar, pg_rho_bar, vs, pg_adv};
+    const void* f[] = {log_rhos, rewards, values, vs, pg_adv};
+    const void* m[] = {term, trunc};
+    return run<VtraceOp>(nm, N, T, a, f, 5, m, 2, ws, ws_bytes, stream);
+}
+
+lrs_status lrs_retrace_f32(int64_t N, int64_t T, const float* log_rhos, const float* rewards,
+                           const float* q_values, const float* values, const uint8_t* term,
+                           const uint8_t* trunc, const float* tv, const float* boot, float gamma,
+                           float lambda, float c_bar, float* q_ret, void* ws, size_t ws_bytes,
+                           hipStream_t stream)
+{
+    const char* nm = "lrs_retrace_f32";
+    LRS_TRY(check_common(nm, N, T));
+    LRS_REQUIRE(log_rhos && rewards && q_values && values && q_ret,
+                "%s: log_rhos, rewards, q_values, values and q_ret are required", nm);
+    LRS_TRY(check_boundary(nm, term, trunc, tv));
+    LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda), "%s: gamma and lambda must be in [0, 1]", nm);
+    LRS_REQUIRE(positive(c_bar), "%s: c_bar must be > 0", nm);
+    RetraceArgs a{{term, trunc, tv, boot}, log_rhos, rewards, q_values, values,
+                  gamma, lambda, c_bar, q_ret};
+    const void* f[] = {log_rhos, rewards, q_values, values, q_ret};
+    const void* m[] = {term, trunc};
+    return run<RetraceOp>(nm, N, T, a, f, 5, m, 2, ws, ws_bytes, stream);
+}
+
+lrs_status lrs_lambda_returns_f32(int64_t N, int64_t T, const float* rewards, const float* values,
+                                  const uint8_t* term, const uint8_t* trunc, const float* tv,
+                                  const float* boot, float gamma, float lambda, float* out,
+                                  void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    const char* nm = "lrs_lambda_returns_f32";
+    LRS_TRY(check_common(nm, N, T));
+    LRS_REQUIRE(rewards && values && out, "%s: rewards, values and returns are required", nm);
+    LRS_TRY(check_boundary(nm, term, trunc, tv));
+    LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda), "%s: gamma and lambda must be in [0, 1]", nm);
+    LambdaArgs a{{term, trunc, tv, boot}, rewards, values, gamma,
+                 (float)((double)gamma * (double)lambda),
+                 (float)((double)gamma * (1.0 - (double)lambda)), out};
+    const void* f[] = {rewards, values, out};
+    const void* m[] = {term, trunc};
+    return run<LambdaOp>(nm, N, T, a, f, 3, m, 2, ws, ws_bytes, stream);
+}
+
+lrs_status lrs_discounted_returns_f32(int64_t N, int64_t T, const float* rewards,
+                                      const uint8_t* term, const uint8_t* trunc, const float* tv,
+                                      const float* boot, float gamma, float* out, void* ws,
+                                      size_t ws_bytes, hipStream_t stream)
+{
+    const char* nm = "lrs_discounted_returns_f32";
+    LRS_TRY(check_common(nm, N, T));
+    LRS_REQUIRE(rewards && out, "%s: rewards and returns are required", nm);
+    LRS_TRY(check_boundary(nm, term, trunc, tv));
+    LRS_REQUIRE(unit_interval(gamma), "%s: gamma must be in [0, 1]", nm);
+    DiscArgs a{{term, trunc, tv, boot}, rewards, gamma, out};
+    const void* f[] = {rewards, out};
+    const void* m[] = {term, trunc};
+    return run<DiscOp>(nm, N, T, a, f, 2, m, 2, ws, ws_bytes, stream);
+}
+
+lrs_status lrs_eligibility_traces_f32(int64_t N, int64_t T, const float* x, const uint8_t* dones,
+                                      float gamma, float lambda, float* out, void* ws,
+                                      size_t ws_bytes, hipStream_t stream)
+{
+    const char* nm = "lrs_eligibility_traces_f32";
+    LRS_TRY(check_common(nm, N, T));
+    LRS_REQUIRE(x && dones && out, "%s: x, dones and traces are required", nm);
+    LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda), "%s: gamma and lambda must be in [0, 1]", nm);
+    ForwardArgs a{x, dones, (float)((double)gamma * (double)lambda), out};
+    const void* f[] = {x, out};
+    const void* m[] = {dones};
+    return run<EligOp>(nm, N, T, a, f, 2, m, 1, ws, ws_bytes, stream);
+}
+
+lrs_status lrs_episodic_prefix_sum_i32(int64_t N, int64_t T, const int32_t* x,
+                                       const uint8_t* dones, int32_t* out, void* ws,
+                                       size_t ws_bytes, hipStream_t stream)
+{
+    const char* nm = "lrs_episodic_prefix_sum_i32";
+    LRS_TRY(check_common(nm, N, T));
+    LRS_REQUIRE(x && dones && out, "%s: x, dones and sums are required", nm);
+    ForwardArgs a{x, dones, 1.0f, out};
+    const void* f[] = {x, out};
+    const void* m[] = {dones};
+    return run<PrefixI32Op>(nm, N, T, a, f, 2, m, 1, ws, ws_bytes, stream);
+}
+
+lrs_status lrs_episodic_prefix_sum_f32(int64_t N, int64_t T, const float* x, const uint8_t* dones,
+                                       float* out, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    const char* nm = "lrs_episodic_prefix_sum_f32";
+    LRS_TRY(check_common(nm, N, T));
+    LRS_REQUIRE(x && dones && out, "%s: x, dones and sums are required", nm);
+    ForwardArgs a{x, dones, 1.0f, out};
+    const void* f[] = {x, out};
+    const void* m[] = {dones};
+    return run<PrefixF32Op>(nm, N, T, a, f, 2, m, 1, ws, ws_bytes, stream);
+}
+
+}  // extern "C"

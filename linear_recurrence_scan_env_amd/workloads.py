@@ -2,7 +2,7 @@
 
 This module holds no arithmetic of the estimators: it only draws random
 arrays with the shapes and distributions of the benchmark workloads, so the
-same bytes can be fed to the HIP library and to the fp64 oracle.
+same bytes can be fed to the HIP library and to any CPU reference.
 
 Every named stream comes from its own generator,
 ``numpy.random.default_rng([seed, STREAM_KEY[name]])``, so a stream's values
