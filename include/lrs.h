@@ -88,8 +88,8 @@ const char* lrs_status_string(lrs_status s);
 /* Message of the last failed call on the calling thread ("" if none). */
 const char* lrs_last_error(void);
 
-/* Bytes of workspace a call of `est` at [num_envs, seq_len] may need: 64
- * bytes plus 16 bytes per 256 elements (about 6% of one fp32 input).  The
+/* Bytes of workspace a call of `est` at [num_envs, seq_len] may need:
+ * 4224 bytes plus 16 bytes per 256 elements (about 6% of one fp32 input).  The
  * same workspace serves every estimator at this or any smaller size.
  * Returns 0 for invalid sizes. */
 size_t lrs_workspace_bytes(lrs_estimator est, int64_t num_envs, int64_t seq_len);

@@ -55,7 +55,8 @@ __device__ __forceinline__ float next_elem(float my0, const float* __restrict__ 
 // end_j  = terminated_j | truncated_j | last-in-row_j
 // vend_j = successor value at an end: 0 if terminated, else trunc_values if
 //          truncated, else the row's bootstrap value (0 if none).
-// trunc_values is read only at truncated steps, bootstrap only at row ends.
+// Every load here depends on the element's position only, never on another
+// loaded value, so all of a lane's loads are in flight together.
 template <int E>
 struct Ends {
     uint32_t end;
@@ -65,7 +66,7 @@ struct Ends {
 struct BoundaryArgs {
     const uint8_t* term;
     const uint8_t* trunc;   // nullable
-    const float* tv;        // read only where trunc
+    const float* tv;        // required iff trunc
     const float* boot;      // nullable
 };
 
@@ -73,23 +74,37 @@ template <int E>
 __device__ __forceinline__ Ends<E> load_ends(const BoundaryArgs& b, const Pos<E>& P, const Ctx& c)
 {
     const uint32_t tau = load_mask<E>(b.term, P.i0, P.count, c.vec);
-    const uint32_t kap = b.trunc ? load_mask<E>(b.trunc, P.i0, P.count, c.vec) : 0u;
-    Ends<E> r;
-    r.end = tau | kap | P.last;
+    uint32_t kap = 0u;
+    float tv[E];
+    if (b.trunc) {
+        kap = load_mask<E>(b.trunc, P.i0, P.count, c.vec);
+        load_f32<E>(tv, b.tv, P.i0, P.count, c.vec);
+    } else {
+#pragma unroll
+        for (int j = 0; j < E; ++j) tv[j] = 0.0f;
+    }
+    float bv[E];
     uint64_t n = P.n0;
 #pragma unroll
     for (int j = 0; j < E; ++j) {
-        float v = 0.0f;
-        if (!((tau >> j) & 1u)) {
-            if ((kap >> j) & 1u)
-                v = b.tv[P.i0 + j];
-            else if (((P.last >> j) & 1u) && b.boot)
-                v = b.boot[n];
-        }
-        r.vend[j] = v;
-        if ((P.last >> j) & 1u) ++n;
+        const bool last = (P.last >> j) & 1u;
+        bv[j] = (last && b.boot) ? b.boot[n] : 0.0f;
+        if (last) ++n;
     }
+    Ends<E> r;
+    r.end = tau | kap | P.last;
+#pragma unroll
+    for (int j = 0; j < E; ++j)
+        r.vend[j] = ((tau >> j) & 1u) ? 0.0f : (((kap >> j) & 1u) ? tv[j] : bv[j]);
     return r;
+}
+
+// The successor of the lane's last element is read only when that element
+// is not the last of its row (position only, so no load waits on another).
+template <int E>
+__device__ __forceinline__ bool successor_used(const Pos<E>& P)
+{
+    return !((P.last >> (E - 1)) & 1u);
 }
 
 // Elements past the end of the array are identities.
@@ -143,7 +158,7 @@ struct GaeOp {
         load_f32<E>(r, a.rewards, P.i0, P.count, c.vec);
         load_f32<E>(v, a.values, P.i0, P.count, c.vec);
         const Ends<E> e = load_ends<E>(a.b, P, c);
-        const float vnx = next_elem<E>(v[0], a.values, P, c, !((e.end >> (E - 1)) & 1u));
+        const float vnx = next_elem<E>(v[0], a.values, P, c, successor_used<E>(P));
 #pragma unroll
         for (int j = 0; j < E; ++j) {
             const bool end = (e.end >> j) & 1u;
@@ -194,7 +209,7 @@ struct LambdaOp {
         load_f32<E>(r, a.rewards, P.i0, P.count, c.vec);
         load_f32<E>(v, a.values, P.i0, P.count, c.vec);
         const Ends<E> e = load_ends<E>(a.b, P, c);
-        const float vnx = next_elem<E>(v[0], a.values, P, c, !((e.end >> (E - 1)) & 1u));
+        const float vnx = next_elem<E>(v[0], a.values, P, c, successor_used<E>(P));
 #pragma unroll
         for (int j = 0; j < E; ++j) {
             const bool end = (e.end >> j) & 1u;
@@ -294,7 +309,7 @@ struct VtraceOp {
         load_f32<E>(s.r, a.rewards, P.i0, P.count, c.vec);
         load_f32<E>(s.v, a.values, P.i0, P.count, c.vec);
         const Ends<E> e = load_ends<E>(a.b, P, c);
-        const float vnx = next_elem<E>(s.v[0], a.values, P, c, !((e.end >> (E - 1)) & 1u));
+        const float vnx = next_elem<E>(s.v[0], a.values, P, c, successor_used<E>(P));
 #pragma unroll
         for (int j = 0; j < E; ++j) {
             const bool end = (e.end >> j) & 1u;
@@ -372,7 +387,7 @@ struct RetraceOp {
         const Ends<E> e = load_ends<E>(a.b, P, c);
 #pragma unroll
         for (int j = 0; j < E; ++j) cc[j] = trace(a, lr[j]);
-        const bool used = !((e.end >> (E - 1)) & 1u);
+        const bool used = successor_used<E>(P);
         // successor (t+1) quantities of the lane's last element
         float cnx = shfl_down(cc[0], 1);
         const float qnx = next_elem<E>(q[0], a.q_values, P, c, used);

@@ -37,20 +37,26 @@ struct Sched {
     int vec;
 };
 
-// Called once per block after its last look-back read.  The block that
-// completes the launch resets the ticket counters and moves the epoch on;
-// every other block has read the epoch before counting itself out.
-__device__ __forceinline__ void finish_launch(WsHeader* hdr, uint32_t num_tiles, uint32_t tag)
+// Called once per block (one thread) after its last look-back read.
+__device__ __forceinline__ void finish_launch(WsHeader* hdr, uint32_t num_blocks, uint32_t block,
+                                              uint32_t tag)
 {
+    const uint32_t g = block % kGroups;
+    const uint32_t members = (num_blocks - g + kGroups - 1) / kGroups;  // blocks in group g
+    const uint32_t groups = num_blocks < kGroups ? num_blocks : kGroups;
+    const uint32_t seen =
+        __hip_atomic_fetch_add(&hdr->group[g].count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (seen != members - 1u) return;
     const uint32_t done =
-        __hip_atomic_fetch_add(&hdr->exited, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (done == num_tiles - 1u) {
-        uint32_t next = tag;                 // = epoch + 1
-        if (next == 0xffffffffu) next = 0u;  // keep tags (epoch + 1) nonzero
-        __hip_atomic_store(&hdr->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&hdr->exited, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&hdr->epoch, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+        __hip_atomic_fetch_add(&hdr->top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done != groups - 1u) return;
+    // Last block of the launch: every block has read the epoch by now.
+    for (uint32_t i = 0; i < groups; ++i)
+        __hip_atomic_store(&hdr->group[i].count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&hdr->top, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t next = tag;                 // = epoch + 1
+    if (next == 0xffffffffu) next = 0u;  // keep tags (epoch + 1) nonzero
+    __hip_atomic_store(&hdr->epoch, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <class Op, int E, int W>
@@ -63,7 +69,7 @@ __global__ __launch_bounds__(W * kWave) void scan_kernel(const typename Op::Args
     __shared__ T sh_a[W];
     __shared__ T sh_b[W];
     __shared__ T sh_carry;
-    __shared__ uint32_t sh_tile, sh_tag, sh_open;
+    __shared__ uint32_t sh_tag, sh_open;
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -71,29 +77,13 @@ __global__ __launch_bounds__(W * kWave) void scan_kernel(const typename Op::Args
     WsHeader* hdr = reinterpret_cast<WsHeader*>(s.ws);
     uint64_t* rec = reinterpret_cast<uint64_t*>(s.ws + sizeof(WsHeader));
 
-    uint32_t tile = blockIdx.x, tag = 0;
+    // Backward scans take tiles from the end of the array, so the tile a
+    // block depends on always has a lower block index.
+    const uint32_t tile = (s.lookback && kB) ? s.num_tiles - 1u - blockIdx.x : blockIdx.x;
+    uint32_t tag = 0;
     if (s.lookback) {
-        if (tid == 0) {
-            const uint32_t ticket =
-                __hip_atomic_fetch_add(&hdr->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const uint32_t epoch =
-                __hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (ticket >= s.num_tiles) {  // header not in its reset state
-                __hip_atomic_fetch_or(&hdr->error, kErrTicket, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
-                sh_tile = 0xffffffffu;
-            } else {
-                sh_tile = kB ? s.num_tiles - 1u - ticket : ticket;
-            }
-            sh_tag = epoch + 1u;
-        }
-        __syncthreads();
-        tile = sh_tile;
-        tag = sh_tag;
-        if (tile == 0xffffffffu) {
-            if (tid == 0) finish_launch(hdr, s.num_tiles, tag);
-            return;
-        }
+        if (tid == 0) sh_tag = __hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+        // published to the block by the __syncthreads below
     }
 
     // Where this lane's elements sit in their rows.
@@ -164,6 +154,7 @@ __global__ __launch_bounds__(W * kWave) void scan_kernel(const typename Op::Args
 
     T carry = T(0);
     if (s.lookback) {
+        tag = sh_tag;
         if (wave == 0) {
             if (lane == 0) publish_aggregate<T>(rec, tile, tag, tile_agg);
             const bool far_most = kB ? (tile == s.num_tiles - 1u) : (tile == 0u);
@@ -172,7 +163,7 @@ __global__ __launch_bounds__(W * kWave) void scan_kernel(const typename Op::Args
                 cin = lookback_carry<kB, T>(rec, tile, s.num_tiles, tag, lane, &hdr->error);
             if (lane == 0) {
                 sh_carry = cin;
-                finish_launch(hdr, s.num_tiles, tag);
+                finish_launch(hdr, s.num_tiles, blockIdx.x, tag);
             }
         }
         __syncthreads();
@@ -192,7 +183,7 @@ struct Cfg {
 };
 constexpr int kNumCfg = 4;
 constexpr Cfg kCfgs[kNumCfg] = {{4, 1}, {4, 4}, {8, 4}, {8, 16}};
-constexpr uint32_t kMinTile = 256;
+constexpr uint32_t kMinTile = 256;  // smallest tile the look-back path may use
 constexpr int kLookbackCfg = 2;  // 2048-element tiles
 
 std::atomic<int> g_force_lookback{0};
@@ -401,9 +392,9 @@ lrs_status lrs_gae_f32(int64_t N, int64_t T, const float* rewards, const float* 
     LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda), "%s: gamma and lambda must be in [0, 1]", nm);
     GaeArgs a{{term, trunc, tv, boot}, rewards, values, gamma,
               (float)((double)gamma * (double)lambda), adv};
-    const void* f[] = {rewards, values, adv};
+    const void* f[] = {rewards, values, adv, tv};
     const void* m[] = {term, trunc};
-    return run<GaeOp>(nm, N, T, a, f, 3, m, 2, ws, ws_bytes, stream);
+    return run<GaeOp>(nm, N, T, a, f, 4, m, 2, ws, ws_bytes, stream);
 }
 
 lrs_status lrs_vtrace_f32(int64_t N, int64_t T, const float* log_rhos, const float* rewards,
@@ -422,9 +413,9 @@ lrs_status lrs_vtrace_f32(int64_t N, int64_t T, const float* log_rhos, const flo
                 "%s: rho_bar, c_bar and pg_rho_bar must be > 0", nm);
     VtraceArgs a{{term, trunc, tv, boot}, log_rhos, rewards, values, gamma, lambda,
                  rho_bar, c_bar, pg_rho_bar, vs, pg_adv};
-    const void* f[] = {log_rhos, rewards, values, vs, pg_adv};
+    const void* f[] = {log_rhos, rewards, values, vs, pg_adv, tv};
     const void* m[] = {term, trunc};
-    return run<VtraceOp>(nm, N, T, a, f, 5, m, 2, ws, ws_bytes, stream);
+    return run<VtraceOp>(nm, N, T, a, f, 6, m, 2, ws, ws_bytes, stream);
 }
 
 lrs_status lrs_retrace_f32(int64_t N, int64_t T, const float* log_rhos, const float* rewards,
@@ -442,9 +433,9 @@ lrs_status lrs_retrace_f32(int64_t N, int64_t T, const float* log_rhos, const fl
     LRS_REQUIRE(positive(c_bar), "%s: c_bar must be > 0", nm);
     RetraceArgs a{{term, trunc, tv, boot}, log_rhos, rewards, q_values, values,
                   gamma, lambda, c_bar, q_ret};
-    const void* f[] = {log_rhos, rewards, q_values, values, q_ret};
+    const void* f[] = {log_rhos, rewards, q_values, values, q_ret, tv};
     const void* m[] = {term, trunc};
-    return run<RetraceOp>(nm, N, T, a, f, 5, m, 2, ws, ws_bytes, stream);
+    return run<RetraceOp>(nm, N, T, a, f, 6, m, 2, ws, ws_bytes, stream);
 }
 
 lrs_status lrs_lambda_returns_f32(int64_t N, int64_t T, const float* rewards, const float* values,
@@ -460,9 +451,9 @@ lrs_status lrs_lambda_returns_f32(int64_t N, int64_t T, const float* rewards, co
     LambdaArgs a{{term, trunc, tv, boot}, rewards, values, gamma,
                  (float)((double)gamma * (double)lambda),
                  (float)((double)gamma * (1.0 - (double)lambda)), out};
-    const void* f[] = {rewards, values, out};
+    const void* f[] = {rewards, values, out, tv};
     const void* m[] = {term, trunc};
-    return run<LambdaOp>(nm, N, T, a, f, 3, m, 2, ws, ws_bytes, stream);
+    return run<LambdaOp>(nm, N, T, a, f, 4, m, 2, ws, ws_bytes, stream);
 }
 
 lrs_status lrs_discounted_returns_f32(int64_t N, int64_t T, const float* rewards,
@@ -476,9 +467,9 @@ lrs_status lrs_discounted_returns_f32(int64_t N, int64_t T, const float* rewards
     LRS_TRY(check_boundary(nm, term, trunc, tv));
     LRS_REQUIRE(unit_interval(gamma), "%s: gamma must be in [0, 1]", nm);
     DiscArgs a{{term, trunc, tv, boot}, rewards, gamma, out};
-    const void* f[] = {rewards, out};
+    const void* f[] = {rewards, out, tv};
     const void* m[] = {term, trunc};
-    return run<DiscOp>(nm, N, T, a, f, 2, m, 2, ws, ws_bytes, stream);
+    return run<DiscOp>(nm, N, T, a, f, 3, m, 2, ws, ws_bytes, stream);
 }
 
 lrs_status lrs_eligibility_traces_f32(int64_t N, int64_t T, const float* x, const uint8_t* dones,

@@ -197,38 +197,47 @@ __device__ __forceinline__ void store_u32(int32_t* __restrict__ p, const uint32_
 
 // ------------------------------------------------ cross-tile carry protocol
 //
-// Workspace: a 64-byte header {ticket, exited, epoch} followed by one
-// 16-byte record per tile: two 64-bit words, each (tag << 32 | payload), the
-// payloads being the bit patterns of the tile aggregate's a and b.  Every
-// word is written and read with single-copy-atomic 64-bit accesses at agent
-// scope, and each word carries its own tag, so a reader that sees both tags
-// equal to this launch's tag holds a consistent aggregate without any fence.
+// Workspace: a header followed by one 16-byte record per tile: two 64-bit
+// words, each (tag << 32 | payload), the payloads being the bit patterns of
+// the tile aggregate's a and b.  Every word is written and read with
+// single-copy-atomic 64-bit accesses at agent scope, and each word carries
+// its own tag, so a reader that sees both tags equal to this launch's tag
+// holds a consistent aggregate without any fence.
 //
-// tag = epoch + 1, where epoch is read from the header by each block; the
-// last block of a launch to finish advances the epoch and resets the ticket
-// counters, so the next launch on the same stream starts clean and stale
-// records (older tags, or the zero fill) are never mistaken for fresh ones.
+// Header: the launch epoch, an error word, and block-completion counters
+// spread over kGroups cache lines (block b counts itself in group b % kGroups;
+// the block completing a group counts the group in `top`).  tag = epoch + 1.
+// Every block reads the epoch before counting itself out; the block that
+// completes the last group zeroes the counters and advances the epoch, so
+// the next launch on the same stream starts clean and stale records (older
+// tags, or the zero fill) are never mistaken for fresh ones.  Spreading the
+// counters keeps same-address atomics, which serialize, to a few per line.
 //
-// Tiles are processed in ticket order (dynamic tile ids), so a tile only
-// ever waits for tiles that hold smaller tickets, i.e. blocks that are
-// already running or done: every wait ends.
+// Tiles are taken in dispatch order (backward scans from the end of the
+// array), so a tile only waits for tiles of lower block index.  Workgroups
+// of a dispatch are started in index order, so those blocks are running or
+// finished and every wait ends; each wait is also bounded (kMaxPolls), so a
+// violated assumption or a corrupted workspace yields a flagged error in the
+// header instead of a hang.
+
+constexpr uint32_t kGroups = 32;
+constexpr uint32_t kLine = 128;  // bytes between counters
 
 struct WsHeader {
-    uint32_t ticket;
-    uint32_t exited;
     uint32_t epoch;
-    uint32_t error;  // nonzero: a ticket out of range or a wait gave up
-    uint32_t pad[12];
+    uint32_t error;  // nonzero: a wait gave up (kErrTimeout)
+    uint32_t top;    // number of completed groups
+    uint32_t pad0[kLine / 4 - 3];
+    struct {
+        uint32_t count;
+        uint32_t pad[kLine / 4 - 1];
+    } group[kGroups];
 };
+static_assert(sizeof(WsHeader) == kLine * (kGroups + 1), "header layout");
 
-// Upper bound on the polls of one look-back wait (about a second).  A wait
-// only runs out if the workspace was not zero-filled before first use or was
-// modified between calls; the block then takes a zero carry and flags the
-// header, instead of spinning forever.
+// Upper bound on the polls of one look-back wait (about a second).
 constexpr uint32_t kMaxPolls = 1u << 20;
-constexpr uint32_t kErrTicket = 1u;
 constexpr uint32_t kErrTimeout = 2u;
-static_assert(sizeof(WsHeader) == 64, "header is 64 bytes");
 
 __device__ __forceinline__ uint64_t ld_agent(const uint64_t* p)
 {
