@@ -15,9 +15,9 @@ K graph replays and host launch overhead stays off the critical path.
 
 Prints one JSON line.  value = 12 * num_envs * seq_len / step time (Gelem/s).
 roofline: the call with the longest average duration, its algorithmic bytes
-(one read of every input element the definition uses, one write of every
-output) over its average duration, measured with HIP events around a graph
-of R back-to-back launches of that call on the launch stream.
+(one read of every input stream, one write of every output) over its
+average duration, measured with HIP events around a graph of R back-to-back
+launches of that call on the launch stream.
 cpu_baseline: the fp64 oracle on the host cores, full steps on the same batch.
 """
 from __future__ import annotations
@@ -50,13 +50,13 @@ def key(est, trunc):
     return est + ("+trunc" if trunc else "")
 
 
-def alg_bytes(est, trunc, n, t, n_trunc):
-    """Dense streams at DENSE_BYTES per element; with truncations add the
-    truncation mask (1 B/elem) and trunc_values at the truncated steps only
-    (the only places the definition reads them); 4 B of bootstrap per env."""
+def alg_bytes(est, trunc, n, t):
+    """One read of each input stream and one write of each output:
+    DENSE_BYTES per element, plus 5 B per element with truncations (the
+    uint8 mask and the fp32 trunc_values), plus 4 B of bootstrap per env."""
     b = DENSE_BYTES[est] * n * t
     if trunc:
-        b += n * t + 4 * n_trunc
+        b += 5 * n * t
     if est in BACKWARD:
         b += 4 * n
     return b
@@ -124,6 +124,122 @@ def cpu_baseline(ro, seconds):
                       f"{el:.1f} s, fp64 sequential recursion, OpenMP over envs"}
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_all7_4096x128.md")
+CALIBRATION_BYTES = 64 << 20  # one --calibrate-copy dispatch reads and writes this much
+
+
+def source_hash():
+    """sha256 of the kernel sources: counters taken on other sources are stale."""
+    import hashlib
+    h = hashlib.sha256()
+    pkg = os.path.join(ROOT, "linear_recurrence_scan_env_amd", "csrc")
+    for f in sorted(os.listdir(pkg)) + ["../../include/lrs.h"]:
+        with open(os.path.join(pkg, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def call_of_kernel(name):
+    """Map a demangled kernel name to a bench call key."""
+    ops = {"GaeOp": "gae", "VtraceOp": "vtrace", "RetraceOp": "retrace",
+           "LambdaOp": "lambda_returns", "DiscOp": "discounted_returns",
+           "EligOp": "eligibility_traces", "PrefixF32Op": "prefix_sum_f32",
+           "PrefixI32Op": "prefix_sum_i32"}
+    for op, est in ops.items():
+        if f"lrs::{op}<" in name:
+            return key(est, ", true>" in name.split(op, 1)[1][:12])
+    return None
+
+
+def summarize_stats(csv_path, command):
+    import csv
+    rows = list(csv.DictReader(open(csv_path)))
+    out = ["# rocprofv3 kernel statistics: seven estimators at 4096 x 128", "",
+           "Command:", "", "```", command, "```", "",
+           "| kernel | call | dispatches | avg us | min us | max us |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| `{r['Name'].split('(')[0]}` | {call_of_kernel(r['Name']) or '-'} | "
+                   f"{r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
+                   f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} |")
+    print("\n".join(out))
+
+
+def summarize_counters(fetch_csv, write_csv, command_fetch, command_write):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by what the same
+    counters read for the calibration copy of CALIBRATION_BYTES."""
+    import csv
+    import collections
+
+    def load(path):
+        per = collections.defaultdict(list)
+        calib = []
+        for r in csv.DictReader(open(path)):
+            v = float(r["Counter_Value"]) * 1024.0
+            k = call_of_kernel(r["Kernel_Name"])
+            if k:
+                per[k].append(v)
+            elif "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) == CALIBRATION_BYTES // 512:
+                calib.append(v)
+        return per, calib
+
+    fetch, fcal = load(fetch_csv)
+    write, wcal = load(write_csv)
+    ff = CALIBRATION_BYTES / (sum(fcal) / len(fcal))
+    wf = CALIBRATION_BYTES / (sum(wcal) / len(wcal))
+    n, t = 4096, 128
+    out = ["# HBM traffic per launch: seven estimators at 4096 x 128 (cold inputs)", "",
+           "Commands (one counter per pass):", "", "```", command_fetch, command_write, "```", "",
+           f"Calibration: a device copy of {CALIBRATION_BYTES >> 20} MiB reads FETCH_SIZE "
+           f"{sum(fcal) / len(fcal) / 1024:.1f} KiB and WRITE_SIZE {sum(wcal) / len(wcal) / 1024:.1f} KiB "
+           f"per dispatch, so the scale factors are fetch x{ff:.4f}, write x{wf:.4f}.", "",
+           "| call | FETCH KiB (raw) | WRITE KiB (raw) | traffic bytes (scaled) | algorithmic bytes | traffic / algorithmic |",
+           "|---|---|---|---|---|---|"]
+    data = {}
+    for k in fetch:
+        fr = sum(fetch[k]) / len(fetch[k])
+        wr = sum(write[k]) / len(write[k])
+        traffic = int(round(fr * ff + wr * wf))
+        est, tr = k.split("+")[0], k.endswith("+trunc")
+        ab = alg_bytes(est, tr, n, t)
+        data[k] = traffic
+        out.append(f"| {k} | {fr / 1024:.1f} | {wr / 1024:.1f} | {traffic} | {ab} | {traffic / ab:.3f} |")
+    out += ["", "Machine-readable (read by bench.py; valid only for these kernel sources):", "",
+            f"source_sha256: {source_hash()}",
+            "traffic_bytes: " + json.dumps(data, sort_keys=True)]
+    print("\n".join(out))
+
+
+def committed_traffic(call):
+    """Scaled HBM bytes per launch of `call` from the committed counter
+    summary, or None when it is missing or was taken on other sources."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    sha = traffic = None
+    for line in text.splitlines():
+        if line.startswith("source_sha256:"):
+            sha = line.split(":", 1)[1].strip()
+        if line.startswith("traffic_bytes:"):
+            traffic = json.loads(line.split(":", 1)[1])
+    if sha != source_hash() or not traffic:
+        return None
+    return traffic.get(call)
+
+
+def run_eager(args, lrs, reps, R, N, T, g, lam, stream, dev):
+    """Counter-collection mode: the same calls, launched one by one."""
+    import torch
+    calls = [[make_call(lrs, e, tr, D, O, g, lam) for e, tr in CALLS] for D, O in reps]
+    with torch.cuda.stream(stream):
+        for k in range(args.warmup + args.steps):
+            for f in calls[k % R]:
+                f()
+        torch.cuda.synchronize()
+    print(json.dumps({"mode": "eager", "steps": args.steps, "warmup": args.warmup,
+                      "workload": WORKLOAD, "replicas": R}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -134,7 +250,23 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--roofline-reps", type=int, default=20)
+    ap.add_argument("--eager", action="store_true",
+                    help="launch calls one by one instead of replaying HIP graphs "
+                         "(for counter collection)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run 5 device copies of a 64 MiB tensor: a kernel of known "
+                         "HBM traffic for scaling FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--summarize-stats", nargs=2, metavar=("CSV", "COMMAND"),
+                    help="print a markdown summary of a rocprofv3 kernel_stats.csv")
+    ap.add_argument("--summarize-counters", nargs=4,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "FETCH_COMMAND", "WRITE_COMMAND"),
+                    help="print the HBM-traffic summary of two rocprofv3 --pmc runs")
     args = ap.parse_args()
+
+    if args.summarize_stats:
+        return summarize_stats(*args.summarize_stats)
+    if args.summarize_counters:
+        return summarize_counters(*args.summarize_counters)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -158,7 +290,6 @@ def main():
                            streams=["rewards", "values", "q_values", "log_rhos", "terminateds",
                                     "truncateds", "trunc_values", "bootstrap_value", "x", "dones"])
     g, lam = ro.gamma, ro.lambda_
-    n_trunc = int(ro.arrays["truncateds"].sum())
 
     host = {k: torch.from_numpy(v) for k, v in ro.arrays.items()}
     per_rep = sum(v.numel() * v.element_size() for v in host.values()) + 13 * N * T * 4
@@ -174,6 +305,16 @@ def main():
         reps.append((D, O))
 
     stream = torch.cuda.Stream(dev)
+    if args.calibrate_copy:
+        src = torch.ones(16 << 20, device=dev)
+        dst = torch.empty_like(src)
+        with torch.cuda.stream(stream):
+            for _ in range(5):
+                dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if args.eager:
+        return run_eager(args, lrs, reps, R, N, T, g, lam, stream, dev)
     with torch.cuda.stream(stream):
         # Eager warm-up on the capture stream (allocates its workspace outside capture).
         for D, O in reps[:2]:
@@ -220,7 +361,7 @@ def main():
             ev1.record(stream)
             torch.cuda.synchronize()
             us = ev0.elapsed_time(ev1) * 1e3 / (args.roofline_reps * R)
-            b = alg_bytes(e, tr, N, T, n_trunc)
+            b = alg_bytes(e, tr, N, T)
             per_call[k_] = {"us": round(us, 3), "alg_bytes": b, "GBps": round(b / us / 1e3, 1)}
 
     elems_per_step = len(CALLS) * N * T
@@ -244,7 +385,9 @@ def main():
                    "cache": "warm" if args.warm else "cold", "replicas": R,
                    "launch": "hip graph per step"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": committed_traffic(dom),
+                     "alg_bytes": per_call[dom]["alg_bytes"]},
         "per_call": per_call,
     }
     if not args.no_cpu_baseline:

@@ -10,8 +10,9 @@
 //   finish():  given the value entering from the far side, run the lane's
 //              serial recursion, apply the epilogue, store once.
 // The [N, T] arrays are treated as one flat stream of N*T elements in which
-// row ends are ordinary segment boundaries; `Pos` gives each element's place
-// in its row.
+// row ends are ordinary segment boundaries; Pos gives each element's place
+// in its row.  Every load depends on positions only, never on another loaded
+// value, so all of a lane's loads are in flight together.
 //
 // Definitions follow the rl-triton README Kernels table (one row per
 // estimator) and the boundary rules of the gist.science technical summary,
@@ -27,36 +28,44 @@ struct Ctx {
     uint64_t total;  // N*T
     uint32_t T;      // seq_len
     int lane;
-    bool vec;        // vector loads allowed
+    bool vec;        // base pointers allow vector access
 };
 
-template <int E>
-struct Pos {
-    uint64_t i0;     // flat index of element 0
-    uint64_t n0;     // row of element 0
-    int count;       // valid elements (E except at the end of the array)
-    uint32_t last;   // bit j: element j is the last step of its row
-    uint32_t first;  // bit j: element j is the first step of its row
-};
-
-// Value of stream p at flat index i0+E (element 0 of the next lane), taken
-// from the neighbouring lane; the last lane of a wave reads it from memory,
-// and only when it is used.
-template <int E>
+// Value of stream p at flat index i0+E (element 0 of the next lane).  Full
+// tiles load it in every lane (same cache line as the neighbouring lane's
+// vector load), unconditionally, so it is in flight with the lane's other
+// loads; it is discarded where unused.  The
+// guarded path takes it from the neighbouring lane and reads memory only in
+// the wave's last lane, where it is used.  `used` (the lane's last element is
+// not a row end) guarantees i0+E < N*T.
+template <int E, bool F>
 __device__ __forceinline__ float next_elem(float my0, const float* __restrict__ p,
-                                           const Pos<E>& P, const Ctx& c, bool used)
+                                           const Pos<E, F>& P, const Ctx& c, bool used)
 {
-    float v = shfl_down(my0, 1);
-    if (c.lane == kWave - 1) v = (used && P.i0 + E < c.total) ? p[P.i0 + E] : 0.0f;
-    return v;
+    if constexpr (F) {
+        // unused: re-read the lane's own first element (a line already
+        // fetched) rather than touch the next tile
+        const float v = p[used ? P.i0 + E : P.i0];
+        return used ? v : 0.0f;
+    } else {
+        float v = lane_next(my0, c.lane, 0.0f);
+        if (c.lane == kWave - 1 && used) v = p[P.i0 + E];
+        return v;
+    }
+}
+
+// The successor of the lane's last element is read only when that element
+// is not the last of its row.
+template <int E, bool F>
+__device__ __forceinline__ bool successor_used(const Pos<E, F>& P)
+{
+    return P.count == E && !((P.last >> (E - 1)) & 1u);
 }
 
 // ------------------------------------------------ backward episode ends
 // end_j  = terminated_j | truncated_j | last-in-row_j
 // vend_j = successor value at an end: 0 if terminated, else trunc_values if
 //          truncated, else the row's bootstrap value (0 if none).
-// Every load here depends on the element's position only, never on another
-// loaded value, so all of a lane's loads are in flight together.
 template <int E>
 struct Ends {
     uint32_t end;
@@ -65,31 +74,42 @@ struct Ends {
 
 struct BoundaryArgs {
     const uint8_t* term;
-    const uint8_t* trunc;   // nullable
-    const float* tv;        // required iff trunc
-    const float* boot;      // nullable
+    const uint8_t* trunc;   // used iff the kernel is the truncating variant
+    const float* tv;        // idem
+    const float* boot;      // never null: without bootstrap values the host
+    int has_boot;           // passes another input array and has_boot = 0
 };
 
-template <int E>
-__device__ __forceinline__ Ends<E> load_ends(const BoundaryArgs& b, const Pos<E>& P, const Ctx& c)
+template <int E, bool F, bool kTrunc>
+__device__ __forceinline__ Ends<E> load_ends(const BoundaryArgs& b, const Pos<E, F>& P,
+                                             const Ctx& c)
 {
-    const uint32_t tau = load_mask<E>(b.term, P.i0, P.count, c.vec);
+    const uint32_t tau = load_mask<E>(b.term, P, c.vec);
     uint32_t kap = 0u;
     float tv[E];
-    if (b.trunc) {
-        kap = load_mask<E>(b.trunc, P.i0, P.count, c.vec);
-        load_f32<E>(tv, b.tv, P.i0, P.count, c.vec);
+    if constexpr (kTrunc) {
+        kap = load_mask<E>(b.trunc, P, c.vec);
+        load_f32<E>(tv, b.tv, P, c.vec);
     } else {
 #pragma unroll
         for (int j = 0; j < E; ++j) tv[j] = 0.0f;
     }
+    // Bootstrap of each row end in the lane.  Full tiles have seq_len >= E,
+    // so a lane holds at most one row end, which belongs to its first row:
+    // one unconditional load.  The guarded path loads per row end.
     float bv[E];
-    uint64_t n = P.n0;
+    if constexpr (F) {
+        const float b0 = b.boot[b.has_boot ? P.n0 : 0];
 #pragma unroll
-    for (int j = 0; j < E; ++j) {
-        const bool last = (P.last >> j) & 1u;
-        bv[j] = (last && b.boot) ? b.boot[n] : 0.0f;
-        if (last) ++n;
+        for (int j = 0; j < E; ++j) bv[j] = b.has_boot ? b0 : 0.0f;
+    } else {
+        uint64_t n = P.n0;
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            const bool last = (P.last >> j) & 1u;
+            bv[j] = (last && b.has_boot) ? b.boot[n] : 0.0f;
+            if (last) ++n;
+        }
     }
     Ends<E> r;
     r.end = tau | kap | P.last;
@@ -99,21 +119,14 @@ __device__ __forceinline__ Ends<E> load_ends(const BoundaryArgs& b, const Pos<E>
     return r;
 }
 
-// The successor of the lane's last element is read only when that element
-// is not the last of its row (position only, so no load waits on another).
-template <int E>
-__device__ __forceinline__ bool successor_used(const Pos<E>& P)
-{
-    return !((P.last >> (E - 1)) & 1u);
-}
-
 // Elements past the end of the array are identities.
-template <int E, class T>
-__device__ __forceinline__ void clear_tail(T (&alpha)[E], T (&beta)[E], int count)
+template <int E, bool F, class T>
+__device__ __forceinline__ void clear_tail(T (&alpha)[E], T (&beta)[E], const Pos<E, F>& P)
 {
+    if (F) return;
 #pragma unroll
     for (int j = 0; j < E; ++j)
-        if (j >= count) {
+        if (j >= P.count) {
             alpha[j] = T(0);
             beta[j] = T(1);
         }
@@ -142,7 +155,7 @@ struct GaeArgs {
     float* adv;
 };
 
-template <int E>
+template <int E, bool kTrunc>
 struct GaeOp {
     using T = float;
     using Args = GaeArgs;
@@ -151,14 +164,15 @@ struct GaeOp {
         uint32_t end;
     };
 
-    __device__ static void prepare(const Args& a, const Pos<E>& P, const Ctx& c, float (&alpha)[E],
-                                   float (&beta)[E], State& s)
+    template <bool F>
+    __device__ static void prepare(const Args& a, const Pos<E, F>& P, const Ctx& c,
+                                   float (&alpha)[E], float (&beta)[E], State& s)
     {
         float r[E], v[E];
-        load_f32<E>(r, a.rewards, P.i0, P.count, c.vec);
-        load_f32<E>(v, a.values, P.i0, P.count, c.vec);
-        const Ends<E> e = load_ends<E>(a.b, P, c);
-        const float vnx = next_elem<E>(v[0], a.values, P, c, successor_used<E>(P));
+        load_f32<E>(r, a.rewards, P, c.vec);
+        load_f32<E>(v, a.values, P, c.vec);
+        const Ends<E> e = load_ends<E, F, kTrunc>(a.b, P, c);
+        const float vnx = next_elem<E>(v[0], a.values, P, c, successor_used(P));
 #pragma unroll
         for (int j = 0; j < E; ++j) {
             const bool end = (e.end >> j) & 1u;
@@ -167,17 +181,18 @@ struct GaeOp {
             alpha[j] = fmaf(a.gamma, vn, r[j]) - v[j];
             beta[j] = end ? 0.0f : a.gl;
         }
-        clear_tail<E>(alpha, beta, P.count);
+        clear_tail(alpha, beta, P);
         s.end = e.end;
     }
     __device__ static bool far_open(const State& s) { return !((s.end >> (E - 1)) & 1u); }
-    __device__ static void finish(const Args& a, const Pos<E>& P, const Ctx& c,
+    template <bool F>
+    __device__ static void finish(const Args& a, const Pos<E, F>& P, const Ctx& c,
                                   const float (&alpha)[E], const float (&beta)[E], const State&,
                                   float carry)
     {
         float out[E];
         backward_pass<E>(out, alpha, beta, carry);
-        store_f32<E>(a.adv, out, P.i0, P.count, c.vec);
+        store_f32<E>(a.adv, out, P, c.vec);
     }
 };
 
@@ -193,7 +208,7 @@ struct LambdaArgs {
     float* out;
 };
 
-template <int E>
+template <int E, bool kTrunc>
 struct LambdaOp {
     using T = float;
     using Args = LambdaArgs;
@@ -202,14 +217,15 @@ struct LambdaOp {
         uint32_t end;
     };
 
-    __device__ static void prepare(const Args& a, const Pos<E>& P, const Ctx& c, float (&alpha)[E],
-                                   float (&beta)[E], State& s)
+    template <bool F>
+    __device__ static void prepare(const Args& a, const Pos<E, F>& P, const Ctx& c,
+                                   float (&alpha)[E], float (&beta)[E], State& s)
     {
         float r[E], v[E];
-        load_f32<E>(r, a.rewards, P.i0, P.count, c.vec);
-        load_f32<E>(v, a.values, P.i0, P.count, c.vec);
-        const Ends<E> e = load_ends<E>(a.b, P, c);
-        const float vnx = next_elem<E>(v[0], a.values, P, c, successor_used<E>(P));
+        load_f32<E>(r, a.rewards, P, c.vec);
+        load_f32<E>(v, a.values, P, c.vec);
+        const Ends<E> e = load_ends<E, F, kTrunc>(a.b, P, c);
+        const float vnx = next_elem<E>(v[0], a.values, P, c, successor_used(P));
 #pragma unroll
         for (int j = 0; j < E; ++j) {
             const bool end = (e.end >> j) & 1u;
@@ -217,17 +233,18 @@ struct LambdaOp {
             alpha[j] = end ? fmaf(a.gamma, e.vend[j], r[j]) : fmaf(a.g1l, v1, r[j]);
             beta[j] = end ? 0.0f : a.gl;
         }
-        clear_tail<E>(alpha, beta, P.count);
+        clear_tail(alpha, beta, P);
         s.end = e.end;
     }
     __device__ static bool far_open(const State& s) { return !((s.end >> (E - 1)) & 1u); }
-    __device__ static void finish(const Args& a, const Pos<E>& P, const Ctx& c,
+    template <bool F>
+    __device__ static void finish(const Args& a, const Pos<E, F>& P, const Ctx& c,
                                   const float (&alpha)[E], const float (&beta)[E], const State&,
                                   float carry)
     {
         float out[E];
         backward_pass<E>(out, alpha, beta, carry);
-        store_f32<E>(a.out, out, P.i0, P.count, c.vec);
+        store_f32<E>(a.out, out, P, c.vec);
     }
 };
 
@@ -241,7 +258,7 @@ struct DiscArgs {
     float* out;
 };
 
-template <int E>
+template <int E, bool kTrunc>
 struct DiscOp {
     using T = float;
     using Args = DiscArgs;
@@ -250,29 +267,31 @@ struct DiscOp {
         uint32_t end;
     };
 
-    __device__ static void prepare(const Args& a, const Pos<E>& P, const Ctx& c, float (&alpha)[E],
-                                   float (&beta)[E], State& s)
+    template <bool F>
+    __device__ static void prepare(const Args& a, const Pos<E, F>& P, const Ctx& c,
+                                   float (&alpha)[E], float (&beta)[E], State& s)
     {
         float r[E];
-        load_f32<E>(r, a.rewards, P.i0, P.count, c.vec);
-        const Ends<E> e = load_ends<E>(a.b, P, c);
+        load_f32<E>(r, a.rewards, P, c.vec);
+        const Ends<E> e = load_ends<E, F, kTrunc>(a.b, P, c);
 #pragma unroll
         for (int j = 0; j < E; ++j) {
             const bool end = (e.end >> j) & 1u;
             alpha[j] = end ? fmaf(a.gamma, e.vend[j], r[j]) : r[j];
             beta[j] = end ? 0.0f : a.gamma;
         }
-        clear_tail<E>(alpha, beta, P.count);
+        clear_tail(alpha, beta, P);
         s.end = e.end;
     }
     __device__ static bool far_open(const State& s) { return !((s.end >> (E - 1)) & 1u); }
-    __device__ static void finish(const Args& a, const Pos<E>& P, const Ctx& c,
+    template <bool F>
+    __device__ static void finish(const Args& a, const Pos<E, F>& P, const Ctx& c,
                                   const float (&alpha)[E], const float (&beta)[E], const State&,
                                   float carry)
     {
         float out[E];
         backward_pass<E>(out, alpha, beta, carry);
-        store_f32<E>(a.out, out, P.i0, P.count, c.vec);
+        store_f32<E>(a.out, out, P, c.vec);
     }
 };
 
@@ -291,7 +310,7 @@ struct VtraceArgs {
     float* pg;
 };
 
-template <int E>
+template <int E, bool kTrunc>
 struct VtraceOp {
     using T = float;
     using Args = VtraceArgs;
@@ -301,15 +320,16 @@ struct VtraceOp {
         float r[E], v[E], tgt[E], rho_pg[E];  // tgt: Vnext at ends, V_{t+1} elsewhere
     };
 
-    __device__ static void prepare(const Args& a, const Pos<E>& P, const Ctx& c, float (&alpha)[E],
-                                   float (&beta)[E], State& s)
+    template <bool F>
+    __device__ static void prepare(const Args& a, const Pos<E, F>& P, const Ctx& c,
+                                   float (&alpha)[E], float (&beta)[E], State& s)
     {
         float lr[E];
-        load_f32<E>(lr, a.log_rhos, P.i0, P.count, c.vec);
-        load_f32<E>(s.r, a.rewards, P.i0, P.count, c.vec);
-        load_f32<E>(s.v, a.values, P.i0, P.count, c.vec);
-        const Ends<E> e = load_ends<E>(a.b, P, c);
-        const float vnx = next_elem<E>(s.v[0], a.values, P, c, successor_used<E>(P));
+        load_f32<E>(lr, a.log_rhos, P, c.vec);
+        load_f32<E>(s.r, a.rewards, P, c.vec);
+        load_f32<E>(s.v, a.values, P, c.vec);
+        const Ends<E> e = load_ends<E, F, kTrunc>(a.b, P, c);
+        const float vnx = next_elem<E>(s.v[0], a.values, P, c, successor_used(P));
 #pragma unroll
         for (int j = 0; j < E; ++j) {
             const bool end = (e.end >> j) & 1u;
@@ -323,11 +343,12 @@ struct VtraceOp {
             alpha[j] = rho * (fmaf(a.gamma, vn, s.r[j]) - s.v[j]);
             beta[j] = end ? 0.0f : a.gamma * cc;
         }
-        clear_tail<E>(alpha, beta, P.count);
+        clear_tail(alpha, beta, P);
         s.end = e.end;
     }
     __device__ static bool far_open(const State& s) { return !((s.end >> (E - 1)) & 1u); }
-    __device__ static void finish(const Args& a, const Pos<E>& P, const Ctx& c,
+    template <bool F>
+    __device__ static void finish(const Args& a, const Pos<E, F>& P, const Ctx& c,
                                   const float (&alpha)[E], const float (&beta)[E], const State& s,
                                   float carry)
     {
@@ -342,8 +363,8 @@ struct VtraceOp {
             pg[j] = s.rho_pg[j] * (fmaf(a.gamma, target, s.r[j]) - s.v[j]);
             a_next = A;
         }
-        store_f32<E>(a.vs, vs, P.i0, P.count, c.vec);
-        store_f32<E>(a.pg, pg, P.i0, P.count, c.vec);
+        store_f32<E>(a.vs, vs, P, c.vec);
+        store_f32<E>(a.pg, pg, P, c.vec);
     }
 };
 
@@ -362,7 +383,7 @@ struct RetraceArgs {
     float* out;
 };
 
-template <int E>
+template <int E, bool kTrunc>
 struct RetraceOp {
     using T = float;
     using Args = RetraceArgs;
@@ -376,24 +397,24 @@ struct RetraceOp {
         return a.lambda * fminf(a.c_bar, expf(lr));
     }
 
-    __device__ static void prepare(const Args& a, const Pos<E>& P, const Ctx& c, float (&alpha)[E],
-                                   float (&beta)[E], State& s)
+    template <bool F>
+    __device__ static void prepare(const Args& a, const Pos<E, F>& P, const Ctx& c,
+                                   float (&alpha)[E], float (&beta)[E], State& s)
     {
         float lr[E], r[E], q[E], v[E], cc[E];
-        load_f32<E>(lr, a.log_rhos, P.i0, P.count, c.vec);
-        load_f32<E>(r, a.rewards, P.i0, P.count, c.vec);
-        load_f32<E>(q, a.q_values, P.i0, P.count, c.vec);
-        load_f32<E>(v, a.values, P.i0, P.count, c.vec);
-        const Ends<E> e = load_ends<E>(a.b, P, c);
-#pragma unroll
-        for (int j = 0; j < E; ++j) cc[j] = trace(a, lr[j]);
-        const bool used = successor_used<E>(P);
+        load_f32<E>(lr, a.log_rhos, P, c.vec);
+        load_f32<E>(r, a.rewards, P, c.vec);
+        load_f32<E>(q, a.q_values, P, c.vec);
+        load_f32<E>(v, a.values, P, c.vec);
+        const Ends<E> e = load_ends<E, F, kTrunc>(a.b, P, c);
+        const bool used = successor_used(P);
         // successor (t+1) quantities of the lane's last element
-        float cnx = shfl_down(cc[0], 1);
+        const float lrnx = next_elem<E>(lr[0], a.log_rhos, P, c, used);
         const float qnx = next_elem<E>(q[0], a.q_values, P, c, used);
         const float vnx = next_elem<E>(v[0], a.values, P, c, used);
-        if (c.lane == kWave - 1)
-            cnx = (used && P.i0 + E < c.total) ? trace(a, a.log_rhos[P.i0 + E]) : 0.0f;
+#pragma unroll
+        for (int j = 0; j < E; ++j) cc[j] = trace(a, lr[j]);
+        const float cnx = trace(a, lrnx);
 #pragma unroll
         for (int j = 0; j < E; ++j) {
             const bool end = (e.end >> j) & 1u;
@@ -403,31 +424,42 @@ struct RetraceOp {
             alpha[j] = end ? fmaf(a.gamma, e.vend[j], r[j]) : fmaf(a.gamma, fmaf(-c1, q1, v1), r[j]);
             beta[j] = end ? 0.0f : a.gamma * c1;
         }
-        clear_tail<E>(alpha, beta, P.count);
+        clear_tail(alpha, beta, P);
         s.end = e.end;
     }
     __device__ static bool far_open(const State& s) { return !((s.end >> (E - 1)) & 1u); }
-    __device__ static void finish(const Args& a, const Pos<E>& P, const Ctx& c,
+    template <bool F>
+    __device__ static void finish(const Args& a, const Pos<E, F>& P, const Ctx& c,
                                   const float (&alpha)[E], const float (&beta)[E], const State&,
                                   float carry)
     {
         float out[E];
         backward_pass<E>(out, alpha, beta, carry);
-        store_f32<E>(a.out, out, P.i0, P.count, c.vec);
+        store_f32<E>(a.out, out, P, c.vec);
     }
 };
 
 // --------------------------------------------------- forward estimators
 // reset_j = first-in-row_j | dones_{j-1}.  dones of the element before the
-// lane comes from the neighbouring lane (lane 0 of a wave reads it).
-template <int E>
-__device__ __forceinline__ uint32_t load_resets(const uint8_t* __restrict__ dones, const Pos<E>& P,
-                                                const Ctx& c)
+// lane comes from the neighbouring lane (lane 0 of a wave reads it, except
+// at a row start where it is not needed).
+template <int E, bool F>
+__device__ __forceinline__ uint32_t load_resets(const uint8_t* __restrict__ dones,
+                                                const Pos<E, F>& P, const Ctx& c)
 {
-    const uint32_t d = load_mask<E>(dones, P.i0, P.count, c.vec);
-    uint32_t dprev = (uint32_t)__shfl_up((int)((d >> (E - 1)) & 1u), 1, kWave);
-    if (c.lane == 0)
-        dprev = (!(P.first & 1u) && P.i0 > 0 && P.i0 - 1 < c.total) ? (dones[P.i0 - 1] != 0) : 0u;
+    const uint32_t d = load_mask<E>(dones, P, c.vec);
+    uint32_t dprev;
+    if constexpr (F) {
+        // every lane loads its predecessor's flag unconditionally, in flight
+        // with the other loads (its own first flag where none is needed)
+        const bool used = P.i0 > 0 && !(P.first & 1u);
+        const uint32_t w = dones[used ? P.i0 - 1 : P.i0] != 0 ? 1u : 0u;
+        dprev = used ? w : 0u;
+    } else {
+        dprev = lane_prev((d >> (E - 1)) & 1u, c.lane, 0u);
+        if (c.lane == 0 && !(P.first & 1u) && P.count > 0 && P.i0 > 0)
+            dprev = dones[P.i0 - 1] != 0 ? 1u : 0u;
+    }
     return P.first | (d << 1) | dprev;  // bit j: reset at element j
 }
 
@@ -448,17 +480,19 @@ struct EligOp {
     struct State {
         uint32_t reset;
     };
-    __device__ static void prepare(const Args& a, const Pos<E>& P, const Ctx& c, float (&alpha)[E],
-                                   float (&beta)[E], State& s)
+    template <bool F>
+    __device__ static void prepare(const Args& a, const Pos<E, F>& P, const Ctx& c,
+                                   float (&alpha)[E], float (&beta)[E], State& s)
     {
-        load_f32<E>(alpha, (const float*)a.x, P.i0, P.count, c.vec);
+        load_f32<E>(alpha, (const float*)a.x, P, c.vec);
         s.reset = load_resets<E>(a.dones, P, c);
 #pragma unroll
         for (int j = 0; j < E; ++j) beta[j] = ((s.reset >> j) & 1u) ? 0.0f : a.gl;
-        clear_tail<E>(alpha, beta, P.count);
+        clear_tail(alpha, beta, P);
     }
     __device__ static bool far_open(const State& s) { return !(s.reset & 1u); }
-    __device__ static void finish(const Args& a, const Pos<E>& P, const Ctx& c,
+    template <bool F>
+    __device__ static void finish(const Args& a, const Pos<E, F>& P, const Ctx& c,
                                   const float (&alpha)[E], const float (&beta)[E], const State&,
                                   float carry)
     {
@@ -469,7 +503,7 @@ struct EligOp {
             e = fmaf(beta[j], e, alpha[j]);
             out[j] = e;
         }
-        store_f32<E>((float*)a.out, out, P.i0, P.count, c.vec);
+        store_f32<E>((float*)a.out, out, P, c.vec);
     }
 };
 
@@ -482,17 +516,19 @@ struct PrefixF32Op {
     struct State {
         uint32_t reset;
     };
-    __device__ static void prepare(const Args& a, const Pos<E>& P, const Ctx& c, float (&alpha)[E],
-                                   float (&beta)[E], State& s)
+    template <bool F>
+    __device__ static void prepare(const Args& a, const Pos<E, F>& P, const Ctx& c,
+                                   float (&alpha)[E], float (&beta)[E], State& s)
     {
-        load_f32<E>(alpha, (const float*)a.x, P.i0, P.count, c.vec);
+        load_f32<E>(alpha, (const float*)a.x, P, c.vec);
         s.reset = load_resets<E>(a.dones, P, c);
 #pragma unroll
         for (int j = 0; j < E; ++j) beta[j] = ((s.reset >> j) & 1u) ? 0.0f : 1.0f;
-        clear_tail<E>(alpha, beta, P.count);
+        clear_tail(alpha, beta, P);
     }
     __device__ static bool far_open(const State& s) { return !(s.reset & 1u); }
-    __device__ static void finish(const Args& a, const Pos<E>& P, const Ctx& c,
+    template <bool F>
+    __device__ static void finish(const Args& a, const Pos<E, F>& P, const Ctx& c,
                                   const float (&alpha)[E], const float (&beta)[E], const State& s,
                                   float carry)
     {
@@ -504,7 +540,7 @@ struct PrefixF32Op {
             out[j] = e;
         }
         (void)beta;
-        store_f32<E>((float*)a.out, out, P.i0, P.count, c.vec);
+        store_f32<E>((float*)a.out, out, P, c.vec);
     }
 };
 
@@ -516,17 +552,19 @@ struct PrefixI32Op {
     struct State {
         uint32_t reset;
     };
-    __device__ static void prepare(const Args& a, const Pos<E>& P, const Ctx& c,
+    template <bool F>
+    __device__ static void prepare(const Args& a, const Pos<E, F>& P, const Ctx& c,
                                    uint32_t (&alpha)[E], uint32_t (&beta)[E], State& s)
     {
-        load_u32<E>(alpha, (const int32_t*)a.x, P.i0, P.count, c.vec);
+        load_u32<E>(alpha, (const int32_t*)a.x, P, c.vec);
         s.reset = load_resets<E>(a.dones, P, c);
 #pragma unroll
         for (int j = 0; j < E; ++j) beta[j] = ((s.reset >> j) & 1u) ? 0u : 1u;
-        clear_tail<E>(alpha, beta, P.count);
+        clear_tail(alpha, beta, P);
     }
     __device__ static bool far_open(const State& s) { return !(s.reset & 1u); }
-    __device__ static void finish(const Args& a, const Pos<E>& P, const Ctx& c,
+    template <bool F>
+    __device__ static void finish(const Args& a, const Pos<E, F>& P, const Ctx& c,
                                   const uint32_t (&alpha)[E], const uint32_t (&beta)[E],
                                   const State& s, uint32_t carry)
     {
@@ -538,7 +576,7 @@ struct PrefixI32Op {
             out[j] = e;
         }
         (void)beta;
-        store_u32<E>((int32_t*)a.out, out, P.i0, P.count, c.vec);
+        store_u32<E>((int32_t*)a.out, out, P, c.vec);
     }
 };
 

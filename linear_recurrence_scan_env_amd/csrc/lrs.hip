@@ -59,58 +59,30 @@ __device__ __forceinline__ void finish_launch(WsHeader* hdr, uint32_t num_blocks
     __hip_atomic_store(&hdr->epoch, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <class Op, int E, int W>
-__global__ __launch_bounds__(W * kWave) void scan_kernel(const typename Op::Args args, const Sched s)
+template <class T, int W>
+struct BlockShared {
+    T a[W];
+    T b[W];
+    T carry;
+    uint32_t tag;
+    uint32_t open;
+};
+
+// Everything after the positions are known.  F: the tile lies wholly inside
+// the array and the base pointers are vector aligned (straight-line vector
+// loads and stores); otherwise every access is guarded by the lane's count.
+template <class Op, int E, int W, bool F>
+__device__ __forceinline__ void tile_body(const typename Op::Args& args, const Sched& s,
+                                          uint32_t tile, const Pos<E, F>& P, const Ctx& c,
+                                          BlockShared<typename Op::T, W>& sh)
 {
     using T = typename Op::T;
     constexpr bool kB = Op::kBackward;
-    constexpr uint32_t kTile = (uint32_t)E * kWave * W;
-
-    __shared__ T sh_a[W];
-    __shared__ T sh_b[W];
-    __shared__ T sh_carry;
-    __shared__ uint32_t sh_tag, sh_open;
-
     const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
+    const int lane = c.lane;
     const int wave = tid / kWave;
     WsHeader* hdr = reinterpret_cast<WsHeader*>(s.ws);
     uint64_t* rec = reinterpret_cast<uint64_t*>(s.ws + sizeof(WsHeader));
-
-    // Backward scans take tiles from the end of the array, so the tile a
-    // block depends on always has a lower block index.
-    const uint32_t tile = (s.lookback && kB) ? s.num_tiles - 1u - blockIdx.x : blockIdx.x;
-    uint32_t tag = 0;
-    if (s.lookback) {
-        if (tid == 0) sh_tag = __hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-        // published to the block by the __syncthreads below
-    }
-
-    // Where this lane's elements sit in their rows.
-    const uint64_t tile_start = (uint64_t)tile * kTile;
-    const uint64_t tile_row = tile_start / s.T;
-    const uint32_t tile_t = (uint32_t)(tile_start - tile_row * s.T);
-    const uint32_t off = (uint32_t)tid * E;
-    Pos<E> P;
-    P.i0 = tile_start + off;
-    P.count = P.i0 >= s.total ? 0 : (int)((s.total - P.i0) < (uint64_t)E ? (s.total - P.i0) : E);
-    {
-        const uint32_t u = tile_t + off;
-        P.n0 = tile_row + u / s.T;
-        uint32_t t = u % s.T;
-        P.last = 0;
-        P.first = 0;
-#pragma unroll
-        for (int j = 0; j < E; ++j) {
-            if (t == s.T - 1) P.last |= 1u << j;
-            if (t == 0) P.first |= 1u << j;
-            t = (t == s.T - 1) ? 0u : t + 1u;
-        }
-        const uint32_t valid = (P.count >= 32) ? ~0u : ((1u << P.count) - 1u);
-        P.last &= valid;
-        P.first &= valid;
-    }
-    const Ctx c{s.total, s.T, lane, s.vec != 0};
 
     T alpha[E], beta[E];
     typename Op::State st;
@@ -127,47 +99,66 @@ __global__ __launch_bounds__(W * kWave) void scan_kernel(const typename Op::Args
     }
     const Aff<T> inc = wave_scan<kB>(agg, lane);
     const Aff<T> exc = wave_exclusive<kB>(inc, lane);
-    if (lane == (kB ? 0 : kWave - 1)) {
-        sh_a[wave] = inc.a;
-        sh_b[wave] = inc.b;
-    }
-    if (kB ? (tid == W * kWave - 1) : (tid == 0)) sh_open = Op::far_open(st) ? 1u : 0u;
-    __syncthreads();
 
-    // Compose the wave aggregates: the whole tile, and the waves beyond mine.
     Aff<T> tile_agg = identity<T>(), beyond = identity<T>();
-    if (kB) {
-#pragma unroll
-        for (int v = W - 1; v >= 0; --v) {
-            const Aff<T> x{sh_a[v], sh_b[v]};
-            tile_agg = combine(x, tile_agg);
-            if (v > wave) beyond = combine(x, beyond);
-        }
-    } else {
-#pragma unroll
-        for (int v = 0; v < W; ++v) {
-            const Aff<T> x{sh_a[v], sh_b[v]};
-            tile_agg = combine(x, tile_agg);
-            if (v < wave) beyond = combine(x, beyond);
-        }
-    }
-
     T carry = T(0);
-    if (s.lookback) {
-        tag = sh_tag;
-        if (wave == 0) {
+    if constexpr (W == 1) {
+        // One wave per block: everything stays in registers, no barrier.
+        const int near_lane = kB ? 0 : kWave - 1;
+        tile_agg = {readlane(inc.a, near_lane), readlane(inc.b, near_lane)};
+        if (s.lookback) {
+            const uint32_t tag = __builtin_amdgcn_readfirstlane(__hip_atomic_load(
+                                     &hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) + 1u;
+            const uint32_t open = readlane(Op::far_open(st) ? 1u : 0u, kB ? kWave - 1 : 0);
             if (lane == 0) publish_aggregate<T>(rec, tile, tag, tile_agg);
             const bool far_most = kB ? (tile == s.num_tiles - 1u) : (tile == 0u);
-            T cin = T(0);
-            if (!far_most && sh_open)
-                cin = lookback_carry<kB, T>(rec, tile, s.num_tiles, tag, lane, &hdr->error);
-            if (lane == 0) {
-                sh_carry = cin;
-                finish_launch(hdr, s.num_tiles, blockIdx.x, tag);
+            if (!far_most && open)
+                carry = lookback_carry<kB, T>(rec, tile, s.num_tiles, tag, lane, &hdr->error);
+            if (lane == 0) finish_launch(hdr, s.num_tiles, blockIdx.x, tag);
+        }
+    } else {
+        if (s.lookback && tid == 0)
+            sh.tag = __hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+        if (lane == (kB ? 0 : kWave - 1)) {
+            sh.a[wave] = inc.a;
+            sh.b[wave] = inc.b;
+        }
+        if (kB ? (tid == W * kWave - 1) : (tid == 0)) sh.open = Op::far_open(st) ? 1u : 0u;
+        __syncthreads();
+
+        // Compose the wave aggregates: the whole tile, and the waves beyond mine.
+        if (kB) {
+#pragma unroll
+            for (int v = W - 1; v >= 0; --v) {
+                const Aff<T> x{sh.a[v], sh.b[v]};
+                tile_agg = combine(x, tile_agg);
+                if (v > wave) beyond = combine(x, beyond);
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < W; ++v) {
+                const Aff<T> x{sh.a[v], sh.b[v]};
+                tile_agg = combine(x, tile_agg);
+                if (v < wave) beyond = combine(x, beyond);
             }
         }
-        __syncthreads();
-        carry = sh_carry;
+
+        if (s.lookback) {
+            const uint32_t tag = sh.tag;
+            if (wave == 0) {
+                if (lane == 0) publish_aggregate<T>(rec, tile, tag, tile_agg);
+                const bool far_most = kB ? (tile == s.num_tiles - 1u) : (tile == 0u);
+                T cin = T(0);
+                if (!far_most && sh.open)
+                    cin = lookback_carry<kB, T>(rec, tile, s.num_tiles, tag, lane, &hdr->error);
+                if (lane == 0) {
+                    sh.carry = cin;
+                    finish_launch(hdr, s.num_tiles, blockIdx.x, tag);
+                }
+            }
+            __syncthreads();
+            carry = sh.carry;
+        }
     }
 
     const T wave_in = apply(beyond, carry);
@@ -175,7 +166,58 @@ __global__ __launch_bounds__(W * kWave) void scan_kernel(const typename Op::Args
     Op::finish(args, P, c, alpha, beta, st, lane_in);
 }
 
+template <class Op, int E, int W>
+__global__ __launch_bounds__(W * kWave) void scan_kernel(const typename Op::Args args, const Sched s)
+{
+    constexpr bool kB = Op::kBackward;
+    constexpr uint32_t kTile = (uint32_t)E * kWave * W;
+    __shared__ BlockShared<typename Op::T, W> sh;
+
+    const int tid = threadIdx.x;
+    // Backward scans on the look-back path take tiles from the end of the
+    // array, so the tile a block depends on always has a lower block index.
+    const uint32_t tile = (s.lookback && kB) ? s.num_tiles - 1u - blockIdx.x : blockIdx.x;
+
+    // Where this lane's elements sit in their rows.
+    const uint64_t tile_start = (uint64_t)tile * kTile;
+    const uint64_t tile_row = tile_start / s.T;
+    const uint32_t tile_t = (uint32_t)(tile_start - tile_row * s.T);
+    const uint32_t off = (uint32_t)tid * E;
+    const uint64_t i0 = tile_start + off;
+    const int count = i0 >= s.total ? 0 : (int)((s.total - i0) < (uint64_t)E ? (s.total - i0) : E);
+    const uint32_t u = tile_t + off;
+    const uint64_t n0 = tile_row + u / s.T;
+    uint32_t t = u % s.T, last = 0, first = 0;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+        if (t == s.T - 1) last |= 1u << j;
+        if (t == 0) first |= 1u << j;
+        t = (t == s.T - 1) ? 0u : t + 1u;
+    }
+    const Ctx c{s.total, s.T, tid & (kWave - 1), s.vec != 0};
+
+    if (s.vec && tile_start + kTile <= s.total && s.T >= (uint32_t)E) {
+        const Pos<E, true> P{i0, n0, E, last, first};
+        tile_body<Op, E, W, true>(args, s, tile, P, c, sh);
+    } else {
+        const uint32_t valid = (count >= 32) ? ~0u : ((1u << count) - 1u);
+        const Pos<E, false> P{i0, n0, count, last & valid, first & valid};
+        tile_body<Op, E, W, false>(args, s, tile, P, c, sh);
+    }
+}
+
 // ------------------------------------------------------------ host side
+
+template <int E> using GaeT = GaeOp<E, true>;
+template <int E> using GaeN = GaeOp<E, false>;
+template <int E> using LambdaT = LambdaOp<E, true>;
+template <int E> using LambdaN = LambdaOp<E, false>;
+template <int E> using DiscT = DiscOp<E, true>;
+template <int E> using DiscN = DiscOp<E, false>;
+template <int E> using VtraceT = VtraceOp<E, true>;
+template <int E> using VtraceN = VtraceOp<E, false>;
+template <int E> using RetraceT = RetraceOp<E, true>;
+template <int E> using RetraceN = RetraceOp<E, false>;
 
 struct Cfg {
     int E, W;
@@ -212,8 +254,9 @@ size_t workspace_bytes_for(uint64_t total)
     return sizeof(WsHeader) + 16 * ((total + kMinTile - 1) / kMinTile);
 }
 
-// Pick the tile: prefer a tile holding whole rows (no cross-tile carry) with
-// enough blocks to spread over the 256 CUs; otherwise the look-back path.
+// Pick the tile: the smallest tile holding whole rows (no cross-tile carry,
+// most blocks in flight); rows longer than every tile, or not dividing one,
+// take the look-back path.
 int choose_cfg(uint64_t total, uint64_t T, bool* lookback)
 {
     const int forced = g_forced_cfg.load();
@@ -224,25 +267,12 @@ int choose_cfg(uint64_t total, uint64_t T, bool* lookback)
         *lookback = force_lb || (tiles > 1 && kCfgs[c].tile() % T != 0);
         return c;
     }
-    const int pref[kNumCfg] = {2, 3, 1, 0};
-    int best = -1;
-    uint64_t best_tiles = 0;
-    for (int p : pref) {
-        const Cfg& k = kCfgs[p];
-        const uint64_t tiles = (total + k.tile() - 1) / k.tile();
-        if (k.tile() % T != 0 && tiles > 1) continue;  // rows would straddle tiles
-        if (tiles >= 512) {
-            best = p;
-            break;
+    for (int c = 0; c < kNumCfg; ++c) {
+        const uint64_t tiles = (total + kCfgs[c].tile() - 1) / kCfgs[c].tile();
+        if (kCfgs[c].tile() % T == 0 || tiles == 1) {
+            *lookback = false;
+            return c;
         }
-        if (tiles > best_tiles) {
-            best = p;
-            best_tiles = tiles;
-        }
-    }
-    if (best >= 0) {
-        *lookback = false;
-        return best;
     }
     *lookback = true;
     return kLookbackCfg;
@@ -390,11 +420,11 @@ lrs_status lrs_gae_f32(int64_t N, int64_t T, const float* rewards, const float* 
     LRS_REQUIRE(rewards && values && adv, "%s: rewards, values and advantages are required", nm);
     LRS_TRY(check_boundary(nm, term, trunc, tv));
     LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda), "%s: gamma and lambda must be in [0, 1]", nm);
-    GaeArgs a{{term, trunc, tv, boot}, rewards, values, gamma,
+    GaeArgs a{{term, trunc, tv, boot ? boot : rewards, boot != nullptr}, rewards, values, gamma,
               (float)((double)gamma * (double)lambda), adv};
     const void* f[] = {rewards, values, adv, tv};
     const void* m[] = {term, trunc};
-    return run<GaeOp>(nm, N, T, a, f, 4, m, 2, ws, ws_bytes, stream);
+    return trunc ? run<GaeT>(nm, N, T, a, f, 4, m, 2, ws, ws_bytes, stream) : run<GaeN>(nm, N, T, a, f, 4, m, 2, ws, ws_bytes, stream);
 }
 
 lrs_status lrs_vtrace_f32(int64_t N, int64_t T, const float* log_rhos, const float* rewards,
@@ -411,11 +441,11 @@ lrs_status lrs_vtrace_f32(int64_t N, int64_t T, const float* log_rhos, const flo
     LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda), "%s: gamma and lambda must be in [0, 1]", nm);
     LRS_REQUIRE(positive(rho_bar) && positive(c_bar) && positive(pg_rho_bar),
                 "%s: rho_bar, c_bar and pg_rho_bar must be > 0", nm);
-    VtraceArgs a{{term, trunc, tv, boot}, log_rhos, rewards, values, gamma, lambda,
+    VtraceArgs a{{term, trunc, tv, boot ? boot : rewards, boot != nullptr}, log_rhos, rewards, values, gamma, lambda,
                  rho_bar, c_bar, pg_rho_bar, vs, pg_adv};
     const void* f[] = {log_rhos, rewards, values, vs, pg_adv, tv};
     const void* m[] = {term, trunc};
-    return run<VtraceOp>(nm, N, T, a, f, 6, m, 2, ws, ws_bytes, stream);
+    return trunc ? run<VtraceT>(nm, N, T, a, f, 6, m, 2, ws, ws_bytes, stream) : run<VtraceN>(nm, N, T, a, f, 6, m, 2, ws, ws_bytes, stream);
 }
 
 lrs_status lrs_retrace_f32(int64_t N, int64_t T, const float* log_rhos, const float* rewards,
@@ -431,11 +461,11 @@ lrs_status lrs_retrace_f32(int64_t N, int64_t T, const float* log_rhos, const fl
     LRS_TRY(check_boundary(nm, term, trunc, tv));
     LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda), "%s: gamma and lambda must be in [0, 1]", nm);
     LRS_REQUIRE(positive(c_bar), "%s: c_bar must be > 0", nm);
-    RetraceArgs a{{term, trunc, tv, boot}, log_rhos, rewards, q_values, values,
+    RetraceArgs a{{term, trunc, tv, boot ? boot : rewards, boot != nullptr}, log_rhos, rewards, q_values, values,
                   gamma, lambda, c_bar, q_ret};
     const void* f[] = {log_rhos, rewards, q_values, values, q_ret, tv};
     const void* m[] = {term, trunc};
-    return run<RetraceOp>(nm, N, T, a, f, 6, m, 2, ws, ws_bytes, stream);
+    return trunc ? run<RetraceT>(nm, N, T, a, f, 6, m, 2, ws, ws_bytes, stream) : run<RetraceN>(nm, N, T, a, f, 6, m, 2, ws, ws_bytes, stream);
 }
 
 lrs_status lrs_lambda_returns_f32(int64_t N, int64_t T, const float* rewards, const float* values,
@@ -448,12 +478,12 @@ lrs_status lrs_lambda_returns_f32(int64_t N, int64_t T, const float* rewards, co
     LRS_REQUIRE(rewards && values && out, "%s: rewards, values and returns are required", nm);
     LRS_TRY(check_boundary(nm, term, trunc, tv));
     LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda), "%s: gamma and lambda must be in [0, 1]", nm);
-    LambdaArgs a{{term, trunc, tv, boot}, rewards, values, gamma,
+    LambdaArgs a{{term, trunc, tv, boot ? boot : rewards, boot != nullptr}, rewards, values, gamma,
                  (float)((double)gamma * (double)lambda),
                  (float)((double)gamma * (1.0 - (double)lambda)), out};
     const void* f[] = {rewards, values, out, tv};
     const void* m[] = {term, trunc};
-    return run<LambdaOp>(nm, N, T, a, f, 4, m, 2, ws, ws_bytes, stream);
+    return trunc ? run<LambdaT>(nm, N, T, a, f, 4, m, 2, ws, ws_bytes, stream) : run<LambdaN>(nm, N, T, a, f, 4, m, 2, ws, ws_bytes, stream);
 }
 
 lrs_status lrs_discounted_returns_f32(int64_t N, int64_t T, const float* rewards,
@@ -466,10 +496,10 @@ lrs_status lrs_discounted_returns_f32(int64_t N, int64_t T, const float* rewards
     LRS_REQUIRE(rewards && out, "%s: rewards and returns are required", nm);
     LRS_TRY(check_boundary(nm, term, trunc, tv));
     LRS_REQUIRE(unit_interval(gamma), "%s: gamma must be in [0, 1]", nm);
-    DiscArgs a{{term, trunc, tv, boot}, rewards, gamma, out};
+    DiscArgs a{{term, trunc, tv, boot ? boot : rewards, boot != nullptr}, rewards, gamma, out};
     const void* f[] = {rewards, out, tv};
     const void* m[] = {term, trunc};
-    return run<DiscOp>(nm, N, T, a, f, 3, m, 2, ws, ws_bytes, stream);
+    return trunc ? run<DiscT>(nm, N, T, a, f, 3, m, 2, ws, ws_bytes, stream) : run<DiscN>(nm, N, T, a, f, 3, m, 2, ws, ws_bytes, stream);
 }
 
 lrs_status lrs_eligibility_traces_f32(int64_t N, int64_t T, const float* x, const uint8_t* dones,

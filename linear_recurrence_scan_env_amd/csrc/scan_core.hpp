@@ -39,39 +39,99 @@ __device__ __forceinline__ uint32_t apply(Aff<uint32_t> f, uint32_t x) { return 
 template <class T>
 __device__ __forceinline__ Aff<T> identity() { return {T(0), T(1)}; }
 
-__device__ __forceinline__ float shfl_down(float v, int d) { return __shfl_down(v, d, kWave); }
-__device__ __forceinline__ uint32_t shfl_down(uint32_t v, int d)
+// ------------------------------------------------------- lane exchange
+// DPP row shifts move data between lanes of a 16-lane row inside one VALU
+// instruction (row_shl:n -- lane i reads lane i+n; row_shr:n -- lane i reads
+// lane i-n; a lane whose source is outside its row keeps `old`).  The three
+// row boundaries of a wave64 are bridged with v_readlane.
+constexpr int kDppRowShl = 0x100;
+constexpr int kDppRowShr = 0x110;
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float old, float src)
 {
-    return (uint32_t)__shfl_down((int)v, d, kWave);
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src),
+                                                      kCtrl, 0xf, 0xf, false));
 }
-__device__ __forceinline__ float shfl_up(float v, int d) { return __shfl_up(v, d, kWave); }
-__device__ __forceinline__ uint32_t shfl_up(uint32_t v, int d)
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t src)
 {
-    return (uint32_t)__shfl_up((int)v, d, kWave);
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, kCtrl, 0xf, 0xf, false);
 }
-__device__ __forceinline__ float shfl(float v, int src) { return __shfl(v, src, kWave); }
-__device__ __forceinline__ uint32_t shfl(uint32_t v, int src)
+
+__device__ __forceinline__ float readlane(float v, int l)
 {
-    return (uint32_t)__shfl((int)v, src, kWave);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ uint32_t readlane(uint32_t v, int l)
+{
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+
+// Value held by lane+1 (lane 63 gets `edge`).
+template <class T>
+__device__ __forceinline__ T lane_next(T v, int lane, T edge)
+{
+    T r = dpp<kDppRowShl + 1>(edge, v);
+    const T r16 = readlane(v, 16), r32 = readlane(v, 32), r48 = readlane(v, 48);
+    if (lane == 15) r = r16;
+    if (lane == 31) r = r32;
+    if (lane == 47) r = r48;
+    return r;
+}
+
+// Value held by lane-1 (lane 0 gets `edge`).
+template <class T>
+__device__ __forceinline__ T lane_prev(T v, int lane, T edge)
+{
+    T r = dpp<kDppRowShr + 1>(edge, v);
+    const T r15 = readlane(v, 15), r31 = readlane(v, 31), r47 = readlane(v, 47);
+    if (lane == 16) r = r15;
+    if (lane == 32) r = r31;
+    if (lane == 48) r = r47;
+    return r;
 }
 
 // Inclusive scan over the 64 lanes of a wave.  Backward: lane L ends up with
 // the composition of lanes L..63 (far = higher lanes).  Forward: lanes 0..L.
+// Four DPP steps scan each 16-lane row; the row totals are then combined
+// through v_readlane and folded into each row.
 template <bool kBackward, class T>
 __device__ __forceinline__ Aff<T> wave_scan(Aff<T> x, int lane)
 {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        Aff<T> f;
-        if (kBackward) {
-            f.a = shfl_down(x.a, d);
-            f.b = shfl_down(x.b, d);
-            if (lane + d < kWave) x = combine(x, f);
-        } else {
-            f.a = shfl_up(x.a, d);
-            f.b = shfl_up(x.b, d);
-            if (lane >= d) x = combine(x, f);
-        }
+    const Aff<T> id = identity<T>();
+#define LRS_ROW_STEP(n)                                                          \
+    {                                                                            \
+        Aff<T> f;                                                                \
+        if (kBackward) {                                                         \
+            f.a = dpp<kDppRowShl + (n)>(id.a, x.a);                              \
+            f.b = dpp<kDppRowShl + (n)>(id.b, x.b);                              \
+        } else {                                                                 \
+            f.a = dpp<kDppRowShr + (n)>(id.a, x.a);                              \
+            f.b = dpp<kDppRowShr + (n)>(id.b, x.b);                              \
+        }                                                                        \
+        x = combine(x, f);                                                       \
+    }
+    LRS_ROW_STEP(1)
+    LRS_ROW_STEP(2)
+    LRS_ROW_STEP(4)
+    LRS_ROW_STEP(8)
+#undef LRS_ROW_STEP
+    const int row = lane >> 4;
+    if (kBackward) {
+        // row totals sit in lanes 16r; suffix over rows 3..1
+        const Aff<T> s3{readlane(x.a, 48), readlane(x.b, 48)};
+        const Aff<T> s2 = combine(Aff<T>{readlane(x.a, 32), readlane(x.b, 32)}, s3);
+        const Aff<T> s1 = combine(Aff<T>{readlane(x.a, 16), readlane(x.b, 16)}, s2);
+        const Aff<T> far = row == 0 ? s1 : (row == 1 ? s2 : (row == 2 ? s3 : id));
+        x = combine(x, far);
+    } else {
+        // row totals sit in lanes 16r+15; prefix over rows 0..2
+        const Aff<T> p0{readlane(x.a, 15), readlane(x.b, 15)};
+        const Aff<T> p1 = combine(Aff<T>{readlane(x.a, 31), readlane(x.b, 31)}, p0);
+        const Aff<T> p2 = combine(Aff<T>{readlane(x.a, 47), readlane(x.b, 47)}, p1);
+        const Aff<T> far = row == 3 ? p2 : (row == 2 ? p1 : (row == 1 ? p0 : id));
+        x = combine(x, far);
     }
     return x;
 }
@@ -80,32 +140,41 @@ __device__ __forceinline__ Aff<T> wave_scan(Aff<T> x, int lane)
 template <bool kBackward, class T>
 __device__ __forceinline__ Aff<T> wave_exclusive(Aff<T> inc, int lane)
 {
-    Aff<T> e;
-    if (kBackward) {
-        e.a = shfl_down(inc.a, 1);
-        e.b = shfl_down(inc.b, 1);
-        if (lane == kWave - 1) e = identity<T>();
-    } else {
-        e.a = shfl_up(inc.a, 1);
-        e.b = shfl_up(inc.b, 1);
-        if (lane == 0) e = identity<T>();
-    }
-    return e;
+    const Aff<T> id = identity<T>();
+    if (kBackward) return {lane_next(inc.a, lane, id.a), lane_next(inc.b, lane, id.b)};
+    return {lane_prev(inc.a, lane, id.a), lane_prev(inc.b, lane, id.b)};
 }
 
 // ----------------------------------------------------------------- loads
-// E consecutive elements starting at flat index i0 (a multiple of E).  The
-// vector form needs `vec` (base pointer alignment checked on the host) and a
-// full chunk; the ragged tail and misaligned bases take scalar loads.
+// A lane owns E consecutive elements starting at flat index i0 (a multiple
+// of E).  Pos<E, kFull> says where they are; kFull marks a tile that lies
+// wholly inside the array with vector-aligned base pointers, in which case
+// every access below is an unconditional vector load or store.  Otherwise
+// (the last tile, misaligned views) each access checks the lane's count.
 
-template <int E>
-__device__ __forceinline__ void load_f32(float (&v)[E], const float* __restrict__ p, uint64_t i0,
-                                         int count, bool vec)
+template <int E, bool kFull>
+struct Pos {
+    uint64_t i0;     // flat index of element 0
+    uint64_t n0;     // row of element 0
+    int count;       // valid elements (E except at the end of the array)
+    uint32_t last;   // bit j: element j is the last step of its row
+    uint32_t first;  // bit j: element j is the first step of its row
+};
+
+template <int E, bool kFull>
+__device__ __forceinline__ bool vector_ok(const Pos<E, kFull>& P, bool vec)
 {
-    if (vec && count == E) {
+    return kFull || (vec && P.count == E);
+}
+
+template <int E, bool kFull>
+__device__ __forceinline__ void load_f32(float (&v)[E], const float* __restrict__ p,
+                                         const Pos<E, kFull>& P, bool vec)
+{
+    if (vector_ok(P, vec)) {
 #pragma unroll
         for (int k = 0; k < E / 4; ++k) {
-            float4 q = *reinterpret_cast<const float4*>(p + i0 + 4 * k);
+            const float4 q = *reinterpret_cast<const float4*>(p + P.i0 + 4 * k);
             v[4 * k + 0] = q.x;
             v[4 * k + 1] = q.y;
             v[4 * k + 2] = q.z;
@@ -113,18 +182,18 @@ __device__ __forceinline__ void load_f32(float (&v)[E], const float* __restrict_
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < E; ++j) v[j] = (j < count) ? p[i0 + j] : 0.0f;
+        for (int j = 0; j < E; ++j) v[j] = (j < P.count) ? p[P.i0 + j] : 0.0f;
     }
 }
 
-template <int E>
+template <int E, bool kFull>
 __device__ __forceinline__ void load_u32(uint32_t (&v)[E], const int32_t* __restrict__ p,
-                                         uint64_t i0, int count, bool vec)
+                                         const Pos<E, kFull>& P, bool vec)
 {
-    if (vec && count == E) {
+    if (vector_ok(P, vec)) {
 #pragma unroll
         for (int k = 0; k < E / 4; ++k) {
-            int4 q = *reinterpret_cast<const int4*>(p + i0 + 4 * k);
+            const int4 q = *reinterpret_cast<const int4*>(p + P.i0 + 4 * k);
             v[4 * k + 0] = (uint32_t)q.x;
             v[4 * k + 1] = (uint32_t)q.y;
             v[4 * k + 2] = (uint32_t)q.z;
@@ -132,11 +201,11 @@ __device__ __forceinline__ void load_u32(uint32_t (&v)[E], const int32_t* __rest
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < E; ++j) v[j] = (j < count) ? (uint32_t)p[i0 + j] : 0u;
+        for (int j = 0; j < E; ++j) v[j] = (j < P.count) ? (uint32_t)p[P.i0 + j] : 0u;
     }
 }
 
-// Bit j of the result is (mask[i0 + j] != 0).
+// Bit k of the result is (byte k of w != 0).
 __device__ __forceinline__ uint32_t nonzero_bytes(uint32_t w)
 {
     uint32_t bits = 0;
@@ -145,53 +214,53 @@ __device__ __forceinline__ uint32_t nonzero_bytes(uint32_t w)
     return bits;
 }
 
-template <int E>
-__device__ __forceinline__ uint32_t load_mask(const uint8_t* __restrict__ p, uint64_t i0,
-                                              int count, bool vec)
+// Bit j of the result is (mask[i0 + j] != 0); a null mask reads as all zero.
+template <int E, bool kFull>
+__device__ __forceinline__ uint32_t load_mask(const uint8_t* __restrict__ p, const Pos<E, kFull>& P,
+                                              bool vec)
 {
     static_assert(E == 4 || E == 8, "mask loads are 4 or 8 bytes");
-    if (p == nullptr) return 0u;
-    if (vec && count == E) {
-        if (E == 4) return nonzero_bytes(*reinterpret_cast<const uint32_t*>(p + i0));
-        uint2 w = *reinterpret_cast<const uint2*>(p + i0);
+    if (vector_ok(P, vec)) {
+        if (E == 4) return nonzero_bytes(*reinterpret_cast<const uint32_t*>(p + P.i0));
+        const uint2 w = *reinterpret_cast<const uint2*>(p + P.i0);
         return nonzero_bytes(w.x) | (nonzero_bytes(w.y) << 4);
     }
     uint32_t bits = 0;
 #pragma unroll
     for (int j = 0; j < E; ++j)
-        if (j < count && p[i0 + j] != 0) bits |= 1u << j;
+        if (j < P.count && p[P.i0 + j] != 0) bits |= 1u << j;
     return bits;
 }
 
-template <int E>
-__device__ __forceinline__ void store_f32(float* __restrict__ p, const float (&v)[E], uint64_t i0,
-                                          int count, bool vec)
+template <int E, bool kFull>
+__device__ __forceinline__ void store_f32(float* __restrict__ p, const float (&v)[E],
+                                          const Pos<E, kFull>& P, bool vec)
 {
-    if (vec && count == E) {
+    if (vector_ok(P, vec)) {
 #pragma unroll
         for (int k = 0; k < E / 4; ++k)
-            *reinterpret_cast<float4*>(p + i0 + 4 * k) =
+            *reinterpret_cast<float4*>(p + P.i0 + 4 * k) =
                 make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
     } else {
 #pragma unroll
         for (int j = 0; j < E; ++j)
-            if (j < count) p[i0 + j] = v[j];
+            if (j < P.count) p[P.i0 + j] = v[j];
     }
 }
 
-template <int E>
+template <int E, bool kFull>
 __device__ __forceinline__ void store_u32(int32_t* __restrict__ p, const uint32_t (&v)[E],
-                                          uint64_t i0, int count, bool vec)
+                                          const Pos<E, kFull>& P, bool vec)
 {
-    if (vec && count == E) {
+    if (vector_ok(P, vec)) {
 #pragma unroll
         for (int k = 0; k < E / 4; ++k)
-            *reinterpret_cast<int4*>(p + i0 + 4 * k) =
+            *reinterpret_cast<int4*>(p + P.i0 + 4 * k) =
                 make_int4((int)v[4 * k], (int)v[4 * k + 1], (int)v[4 * k + 2], (int)v[4 * k + 3]);
     } else {
 #pragma unroll
         for (int j = 0; j < E; ++j)
-            if (j < count) p[i0 + j] = (int32_t)v[j];
+            if (j < P.count) p[P.i0 + j] = (int32_t)v[j];
     }
 }
 
@@ -302,8 +371,8 @@ __device__ T lookback_carry(const uint64_t* rec, uint32_t tile, uint32_t num_til
             if ((missing & needed) == 0) {
                 if (lane > k) v = identity<T>();
                 Aff<T> tot = wave_scan<true>(v, lane);  // lane 0 = composition of 0..k
-                tot.a = shfl(tot.a, 0);
-                tot.b = shfl(tot.b, 0);
+                tot.a = readlane(tot.a, 0);
+                tot.b = readlane(tot.b, 0);
                 acc = combine(acc, tot);
                 if (zero_b) return acc.a;
                 break;  // all 64 neighbours continue the segment: next window
