@@ -1,24 +1,26 @@
 #!/usr/bin/env python3
-"""Throughput of the seven-estimator scan path on one MI355X.
+"""Throughput of the scan path on one MI355X.
 
-Workload: num_envs = 4096, seq_len = 128, fp32 (the pages' headline shape).
-One step = every estimator once without truncations (prefix sum in fp32) and
-the five truncating estimators once more with truncations: 12 library calls,
-each one pass over its [4096, 128] inputs.
+Default workload (the pages' headline shape): num_envs = 4096, seq_len = 128,
+fp32.  One step = every estimator once without truncations (prefix sum in
+fp32) and the five truncating estimators once more with truncations: 12
+library calls, each one pass over its [4096, 128] inputs.  --workload picks
+one of the other benchmark workloads (their steps are listed in WORKLOADS).
 
-Inputs sit in HBM before timing starts.  The batch is replicated R times
-(>= 1 GiB in all, four times the 256 MB Infinity Cache) and step k uses
-replica k mod R, so every call reads its inputs from HBM rather than from a
-cache ("cold"); --warm reuses one replica.  Each replica's 12 calls are
+Inputs sit in HBM before timing starts.  Each workload's batch is replicated
+R times (>= 1 GiB in all, four times the 256 MB Infinity Cache) and step k
+uses replica k mod R, so every call reads its inputs from HBM rather than
+from a cache ("cold"); --warm reuses one replica.  Each replica's calls are
 captured once into a HIP graph (torch.cuda.CUDAGraph), so the timed loop is
 K graph replays and host launch overhead stays off the critical path.
 
-Prints one JSON line.  value = 12 * num_envs * seq_len / step time (Gelem/s).
-roofline: the call with the longest average duration, its algorithmic bytes
-(one read of every input stream, one write of every output) over its
-average duration, measured with HIP events around a graph of R back-to-back
-launches of that call on the launch stream.
-cpu_baseline: the fp64 oracle on the host cores, full steps on the same batch.
+Prints one JSON line.  value = elements processed per step / step time
+(Gelem/s).  roofline: the call with the longest average duration, its
+algorithmic bytes (one read of every input stream, one write of every
+output) over its average duration, measured with HIP events around a graph
+of >= 64 back-to-back launches of that call (cycling over its replicas) on
+the launch stream.  cpu_baseline:
+the fp64 oracle on the host cores, whole steps on the same batch.
 """
 from __future__ import annotations
 
@@ -35,19 +37,42 @@ sys.path.insert(0, ROOT)
 
 METRIC = "Gelem/s + HBM GB/s (% peak), 7 estimators, 4096 envs×T=128..131072"
 HBM_PEAK_GBPS = 8000.0
-WORKLOAD = "all7_4096x128"
 BACKWARD = ("gae", "vtrace", "retrace", "lambda_returns", "discounted_returns")
-CALLS = [("gae", False), ("vtrace", False), ("retrace", False), ("lambda_returns", False),
-         ("discounted_returns", False), ("eligibility_traces", False), ("prefix_sum_f32", False),
-         ("gae", True), ("vtrace", True), ("retrace", True), ("lambda_returns", True),
-         ("discounted_returns", True)]
+ALL7 = [("gae", False), ("vtrace", False), ("retrace", False), ("lambda_returns", False),
+        ("discounted_returns", False), ("eligibility_traces", False), ("prefix_sum_f32", False),
+        ("gae", True), ("vtrace", True), ("retrace", True), ("lambda_returns", True),
+        ("discounted_returns", True)]
+# workload -> the calls of one step: (estimator, with truncations, num_envs, seq_len)
+WORKLOADS = {
+    "all7_4096x128": [(e, tr, 4096, 128) for e, tr in ALL7],
+    "gae_64x512": [("gae", False, 64, 512)],
+    "long_64x131072": [(e, True, 64, 131072) for e in ("gae", "vtrace", "retrace")],
+    "sweep_4096xT": [(e, False, 4096, t) for t in (32, 128, 512, 2048, 8192)
+                     for e in ("discounted_returns", "lambda_returns", "eligibility_traces")],
+    "prefix_16384x1024": [("prefix_sum_i32", False, 16384, 1024),
+                          ("prefix_sum_f32", False, 16384, 1024)],
+}
+DEFAULT_WORKLOAD = "all7_4096x128"
+# input streams each estimator reads
+NEEDS = {
+    "gae": ("rewards", "values", "terminateds", "bootstrap_value"),
+    "vtrace": ("log_rhos", "rewards", "values", "terminateds", "bootstrap_value"),
+    "retrace": ("log_rhos", "rewards", "q_values", "values", "terminateds", "bootstrap_value"),
+    "lambda_returns": ("rewards", "values", "terminateds", "bootstrap_value"),
+    "discounted_returns": ("rewards", "terminateds", "bootstrap_value"),
+    "eligibility_traces": ("x", "dones"),
+    "prefix_sum_f32": ("x", "dones"),
+    "prefix_sum_i32": ("x_int", "dones"),
+}
 # bytes per element: one read of each dense input, one write of each output
 DENSE_BYTES = {"gae": 13, "vtrace": 21, "retrace": 21, "lambda_returns": 13,
-               "discounted_returns": 9, "eligibility_traces": 9, "prefix_sum_f32": 9}
+               "discounted_returns": 9, "eligibility_traces": 9, "prefix_sum_f32": 9,
+               "prefix_sum_i32": 9}
 
 
-def key(est, trunc):
-    return est + ("+trunc" if trunc else "")
+def key(est, trunc, n=None, t=None):
+    k = est + ("+trunc" if trunc else "")
+    return k if n is None else f"{k}@{n}x{t}"
 
 
 def alg_bytes(est, trunc, n, t):
@@ -65,7 +90,7 @@ def alg_bytes(est, trunc, n, t):
 def make_call(lrs, est, trunc, D, O, g, lam):
     kg = dict(truncateds=D["truncateds"] if trunc else None,
               trunc_values=D["trunc_values"] if trunc else None,
-              bootstrap_value=D["bootstrap_value"])
+              bootstrap_value=D.get("bootstrap_value"))
     k = key(est, trunc)
     if est == "gae":
         return lambda: lrs.compute_gae(D["rewards"], D["values"], D["terminateds"], g, lam,
@@ -87,41 +112,62 @@ def make_call(lrs, est, trunc, D, O, g, lam):
         return lambda: lrs.compute_eligibility_traces(D["x"], D["dones"], g, lam, out=O[k])
     if est == "prefix_sum_f32":
         return lambda: lrs.compute_episodic_prefix_sum(D["x"], D["dones"], out=O[k])
+    if est == "prefix_sum_i32":
+        return lambda: lrs.compute_episodic_prefix_sum(D["x_int"], D["dones"], out=O[k])
     raise KeyError(est)
 
 
-def cpu_baseline(ro, seconds):
-    import oracle
+def oracle_call(oracle, est, trunc, ro):
     a = ro.arrays
     g, lam = ro.gamma, ro.lambda_
-    kt = dict(truncateds=a["truncateds"], trunc_values=a["trunc_values"],
-              bootstrap_value=a["bootstrap_value"])
-    kn = dict(bootstrap_value=a["bootstrap_value"])
+    kk = dict(bootstrap_value=a.get("bootstrap_value"))
+    if trunc:
+        kk.update(truncateds=a["truncateds"], trunc_values=a["trunc_values"])
+    if est == "gae":
+        return lambda: oracle.gae(a["rewards"], a["values"], a["terminateds"], g, lam, **kk)
+    if est == "vtrace":
+        return lambda: oracle.vtrace(a["log_rhos"], a["rewards"], a["values"], a["terminateds"],
+                                     g, lam, **kk)
+    if est == "retrace":
+        return lambda: oracle.retrace(a["log_rhos"], a["rewards"], a["q_values"], a["values"],
+                                      a["terminateds"], g, lam, **kk)
+    if est == "lambda_returns":
+        return lambda: oracle.lambda_returns(a["rewards"], a["values"], a["terminateds"], g, lam,
+                                             **kk)
+    if est == "discounted_returns":
+        return lambda: oracle.discounted_returns(a["rewards"], a["terminateds"], g, **kk)
+    if est == "eligibility_traces":
+        return lambda: oracle.eligibility_traces(a["x"], a["dones"], g, lam)
+    if est == "prefix_sum_f32":
+        return lambda: oracle.prefix_sum(a["x"], a["dones"])
+    if est == "prefix_sum_i32":
+        return lambda: oracle.prefix_sum(a["x_int"], a["dones"])
+    raise KeyError(est)
+
+
+def cpu_baseline(name, batches, seconds):
+    """The oracle, untuned, timed on whole steps of the same batch until
+    `seconds` have passed (at least one step after a warm-up step)."""
+    import oracle
+    calls = [oracle_call(oracle, e, tr, batches[(n, t)]) for e, tr, n, t in WORKLOADS[name]]
 
     def step():
-        for kk in (kn, kt):
-            oracle.gae(a["rewards"], a["values"], a["terminateds"], g, lam, **kk)
-            oracle.vtrace(a["log_rhos"], a["rewards"], a["values"], a["terminateds"], g, lam, **kk)
-            oracle.retrace(a["log_rhos"], a["rewards"], a["q_values"], a["values"],
-                           a["terminateds"], g, lam, **kk)
-            oracle.lambda_returns(a["rewards"], a["values"], a["terminateds"], g, lam, **kk)
-            oracle.discounted_returns(a["rewards"], a["terminateds"], g, **kk)
-        oracle.eligibility_traces(a["x"], a["dones"], g, lam)
-        oracle.prefix_sum(a["x"], a["dones"])
+        for f in calls:
+            f()
 
     step()  # warm-up (also builds/loads the library)
-    n, t0 = 0, time.perf_counter()
+    k, t0 = 0, time.perf_counter()
     while True:
         step()
-        n += 1
+        k += 1
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    elems = n * len(CALLS) * ro.num_envs * ro.seq_len
+    elems = k * sum(n * t for _, _, n, t in WORKLOADS[name])
     return {"value": round(elems / el / 1e9, 4), "unit": "Gelem/s", "cores": oracle.threads(),
             "kind": "oracle",
-            "sample": f"{n} full steps (12 calls each) of the {ro.num_envs}x{ro.seq_len} batch, "
-                      f"{el:.1f} s, fp64 sequential recursion, OpenMP over envs"}
+            "sample": f"{k} whole steps ({len(calls)} calls each) of the {name} batch, {el:.1f} s, "
+                      f"fp64 sequential recursion, OpenMP over envs"}
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_all7_4096x128.md")
@@ -227,22 +273,23 @@ def committed_traffic(call):
     return traffic.get(call)
 
 
-def run_eager(args, lrs, reps, R, N, T, g, lam, stream, dev):
+def run_eager(args, steps_fns, stream):
     """Counter-collection mode: the same calls, launched one by one."""
     import torch
-    calls = [[make_call(lrs, e, tr, D, O, g, lam) for e, tr in CALLS] for D, O in reps]
+    R = len(steps_fns)
     with torch.cuda.stream(stream):
         for k in range(args.warmup + args.steps):
-            for f in calls[k % R]:
+            for f in steps_fns[k % R]:
                 f()
         torch.cuda.synchronize()
     print(json.dumps({"mode": "eager", "steps": args.steps, "warmup": args.warmup,
-                      "workload": WORKLOAD, "replicas": R}), flush=True)
+                      "workload": args.workload, "step_graphs": R}), flush=True)
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--replicas", type=int, default=0, help="0: enough for >= 1 GiB")
@@ -283,30 +330,61 @@ def main():
     torch.cuda.set_device(dev)
     lrs.load()
 
-    p = workloads.WORKLOADS[WORKLOAD]
-    N, T = p["num_envs"], p["seq_len"]
-    ro = workloads.rollout(N, T, seed=0, term_p=p["term_p"], trunc_p=p["trunc_p"],
-                           gamma=p["gamma"], lambda_=p["lambda_"], done_p=p["term_p"],
-                           streams=["rewards", "values", "q_values", "log_rhos", "terminateds",
-                                    "truncateds", "trunc_values", "bootstrap_value", "x", "dones"])
-    g, lam = ro.gamma, ro.lambda_
+    name = args.workload
+    calls = WORKLOADS[name]
+    p = workloads.WORKLOADS[name]
+    shapes = sorted({(n, t) for _, _, n, t in calls})
+    batches = {}
+    for n, t in shapes:
+        streams = {s_ for e, tr, n_, t_ in calls if (n_, t_) == (n, t) for s_ in NEEDS[e]}
+        if any(tr for e, tr, n_, t_ in calls if (n_, t_) == (n, t)):
+            streams.add("truncateds")
+        batches[(n, t)] = workloads.rollout(
+            n, t, seed=0, term_p=p["term_p"], trunc_p=p["trunc_p"], gamma=p["gamma"],
+            lambda_=p["lambda_"], done_p=p["term_p"], streams=sorted(streams))
+    ro0 = batches[shapes[0]]
+    g, lam = ro0.gamma, ro0.lambda_
 
-    host = {k: torch.from_numpy(v) for k, v in ro.arrays.items()}
-    per_rep = sum(v.numel() * v.element_size() for v in host.values()) + 13 * N * T * 4
-    R = 1 if args.warm else (args.replicas or max(8, -(-(1 << 30) // per_rep)))
-    reps = []
-    for _ in range(R):
-        D = {k: v.to(dev) for k, v in host.items()}
-        O = {}
-        for est, tr in CALLS:
-            O[key(est, tr)] = torch.empty(N, T, device=dev)
-            if est == "vtrace":
-                O[key(est, tr) + "/pg"] = torch.empty(N, T, device=dev)
-        reps.append((D, O))
+    hosts = {s_: {k: torch.from_numpy(v) for k, v in b.arrays.items()} for s_, b in batches.items()}
+
+    # Replicas per shape: enough copies of that shape's inputs and outputs
+    # for >= 1 GiB, so that each call reads cold data however small it is.
+    def shape_bytes(s_):
+        b = sum(v.numel() * v.element_size() for v in hosts[s_].values())
+        return b + sum((2 if e == "vtrace" else 1) * n * t * 4 for e, _, n, t in calls
+                       if (n, t) == s_)
+
+    if args.warm:
+        nrep = {s_: 1 for s_ in shapes}
+    elif args.replicas:
+        nrep = {s_: args.replicas for s_ in shapes}
+    else:
+        nrep = {s_: max(2, -(-(1 << 30) // shape_bytes(s_))) for s_ in shapes}
+    R = max(nrep.values())
+    store = {}  # (shape, replica) -> (inputs, outputs)
+    for s_ in shapes:
+        for i in range(nrep[s_]):
+            D = {k: v.to(dev) for k, v in hosts[s_].items()}
+            O = {}
+            for e, tr, n, t in calls:
+                if (n, t) != s_:
+                    continue
+                dt = torch.int32 if e == "prefix_sum_i32" else torch.float32
+                O[key(e, tr)] = torch.empty(n, t, device=dev, dtype=dt)
+                if e == "vtrace":
+                    O[key(e, tr) + "/pg"] = torch.empty(n, t, device=dev)
+            store[(s_, i)] = (D, O)
+
+    def fn(e, tr, n, t, i):
+        D, O = store[((n, t), i % nrep[(n, t)])]
+        return make_call(lrs, e, tr, D, O, g, lam)
+
+    def step_fns(i):
+        return [fn(e, tr, n, t, i) for e, tr, n, t in calls]
 
     stream = torch.cuda.Stream(dev)
     if args.calibrate_copy:
-        src = torch.ones(16 << 20, device=dev)
+        src = torch.ones(CALIBRATION_BYTES // 4, device=dev)
         dst = torch.empty_like(src)
         with torch.cuda.stream(stream):
             for _ in range(5):
@@ -314,12 +392,13 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     if args.eager:
-        return run_eager(args, lrs, reps, R, N, T, g, lam, stream, dev)
+        return run_eager(args, [step_fns(i) for i in range(R)], stream)
+
     with torch.cuda.stream(stream):
         # Eager warm-up on the capture stream (allocates its workspace outside capture).
-        for D, O in reps[:2]:
-            for est, tr in CALLS:
-                make_call(lrs, est, tr, D, O, g, lam)()
+        for i in range(min(R, 2)):
+            for f in step_fns(i):
+                f()
         stream.synchronize()
 
         def capture(fns):
@@ -329,10 +408,12 @@ def main():
                     f()
             return gr
 
-        step_graphs = [capture([make_call(lrs, e, tr, D, O, g, lam) for e, tr in CALLS])
-                       for D, O in reps]
-        call_graphs = {key(e, tr): capture([make_call(lrs, e, tr, D, O, g, lam) for D, O in reps])
-                       for e, tr in CALLS}
+        step_graphs = [capture(step_fns(i)) for i in range(R)]
+        call_keys = [key(e, tr, n, t) for e, tr, n, t in calls]
+        # per call: a graph of >= 64 launches cycling over that call's replicas
+        launches = {k_: max(64, nrep[(n, t)]) for k_, (e, tr, n, t) in zip(call_keys, calls)}
+        call_graphs = {k_: capture([fn(e, tr, n, t, i) for i in range(launches[k_])])
+                       for k_, (e, tr, n, t) in zip(call_keys, calls)}
         torch.cuda.synchronize()
 
         # ---- timed steps
@@ -350,8 +431,7 @@ def main():
 
         # ---- per-call average launch duration (graph of R launches, events around it)
         per_call = {}
-        for e, tr in CALLS:
-            k_ = key(e, tr)
+        for (e, tr, n, t), k_ in zip(calls, call_keys):
             call_graphs[k_].replay()
             ev0 = torch.cuda.Event(enable_timing=True)
             ev1 = torch.cuda.Event(enable_timing=True)
@@ -360,14 +440,24 @@ def main():
                 call_graphs[k_].replay()
             ev1.record(stream)
             torch.cuda.synchronize()
-            us = ev0.elapsed_time(ev1) * 1e3 / (args.roofline_reps * R)
-            b = alg_bytes(e, tr, N, T)
-            per_call[k_] = {"us": round(us, 3), "alg_bytes": b, "GBps": round(b / us / 1e3, 1)}
+            us = ev0.elapsed_time(ev1) * 1e3 / (args.roofline_reps * launches[k_])
+            b = alg_bytes(e, tr, n, t)
+            per_call[k_ if len(shapes) > 1 else key(e, tr)] = {
+                "us": round(us, 3), "alg_bytes": b, "GBps": round(b / us / 1e3, 1),
+                "Gelem/s": round(n * t / us / 1e3, 2)}
 
-    elems_per_step = len(CALLS) * N * T
+    elems_per_step = sum(n * t for _, _, n, t in calls)
     value = elems_per_step / (ms_per_step * 1e-3) / 1e9
     dom = max(per_call, key=lambda k_: per_call[k_]["us"])
     achieved = per_call[dom]["GBps"]
+    cfg = {"workload": name, "calls_per_step": len(calls),
+           "cache": "warm" if args.warm else "cold",
+           "replicas": {f"{n}x{t}": nrep[(n, t)] for n, t in shapes},
+           "launch": "hip graph per step"}
+    if len(shapes) == 1:
+        cfg.update(num_envs=shapes[0][0], seq_len=shapes[0][1])
+    else:
+        cfg.update(shapes=[f"{n}x{t}" for n, t in shapes])
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -379,19 +469,17 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "i32" if all(e == "prefix_sum_i32" for e, *_ in calls) else "f32",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD, "num_envs": N, "seq_len": T, "calls_per_step": len(CALLS),
-                   "cache": "warm" if args.warm else "cold", "replicas": R,
-                   "launch": "hip graph per step"},
+        "config": cfg,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": committed_traffic(dom),
+                     "traffic": committed_traffic(dom) if name == DEFAULT_WORKLOAD else None,
                      "alg_bytes": per_call[dom]["alg_bytes"]},
         "per_call": per_call,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(ro, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(name, batches, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

@@ -223,8 +223,8 @@ struct Cfg {
     int E, W;
     uint32_t tile() const { return (uint32_t)(E * kWave * W); }
 };
-constexpr int kNumCfg = 4;
-constexpr Cfg kCfgs[kNumCfg] = {{4, 1}, {4, 4}, {8, 4}, {8, 16}};
+constexpr int kNumCfg = 5;  // ordered by tile size
+constexpr Cfg kCfgs[kNumCfg] = {{4, 1}, {4, 4}, {8, 4}, {16, 4}, {8, 16}};
 constexpr uint32_t kMinTile = 256;  // smallest tile the look-back path may use
 constexpr int kLookbackCfg = 2;  // 2048-element tiles
 
@@ -295,6 +295,7 @@ hipError_t launch_any(int cfg, const typename Op<4>::Args& a, const Sched& s, hi
         case 0: return launch_cfg<Op<4>, 4, 1>(a, s, stream);
         case 1: return launch_cfg<Op<4>, 4, 4>(a, s, stream);
         case 2: return launch_cfg<Op<8>, 8, 4>(a, s, stream);
+        case 3: return launch_cfg<Op<16>, 16, 4>(a, s, stream);
         default: return launch_cfg<Op<8>, 8, 16>(a, s, stream);
     }
 }

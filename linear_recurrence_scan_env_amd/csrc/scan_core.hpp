@@ -219,11 +219,16 @@ template <int E, bool kFull>
 __device__ __forceinline__ uint32_t load_mask(const uint8_t* __restrict__ p, const Pos<E, kFull>& P,
                                               bool vec)
 {
-    static_assert(E == 4 || E == 8, "mask loads are 4 or 8 bytes");
+    static_assert(E == 4 || E == 8 || E == 16, "mask loads are 4, 8 or 16 bytes");
     if (vector_ok(P, vec)) {
         if (E == 4) return nonzero_bytes(*reinterpret_cast<const uint32_t*>(p + P.i0));
-        const uint2 w = *reinterpret_cast<const uint2*>(p + P.i0);
-        return nonzero_bytes(w.x) | (nonzero_bytes(w.y) << 4);
+        if (E == 8) {
+            const uint2 w = *reinterpret_cast<const uint2*>(p + P.i0);
+            return nonzero_bytes(w.x) | (nonzero_bytes(w.y) << 4);
+        }
+        const uint4 w = *reinterpret_cast<const uint4*>(p + P.i0);
+        return nonzero_bytes(w.x) | (nonzero_bytes(w.y) << 4) | (nonzero_bytes(w.z) << 8) |
+               (nonzero_bytes(w.w) << 12);
     }
     uint32_t bits = 0;
 #pragma unroll
@@ -232,6 +237,11 @@ __device__ __forceinline__ uint32_t load_mask(const uint8_t* __restrict__ p, con
     return bits;
 }
 
+// Outputs are written once and not read again by this launch: full-tile
+// stores are non-temporal (streamed past the caches).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 template <int E, bool kFull>
 __device__ __forceinline__ void store_f32(float* __restrict__ p, const float (&v)[E],
                                           const Pos<E, kFull>& P, bool vec)
@@ -239,8 +249,8 @@ __device__ __forceinline__ void store_f32(float* __restrict__ p, const float (&v
     if (vector_ok(P, vec)) {
 #pragma unroll
         for (int k = 0; k < E / 4; ++k)
-            *reinterpret_cast<float4*>(p + P.i0 + 4 * k) =
-                make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+            __builtin_nontemporal_store(f32x4{v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]},
+                                        reinterpret_cast<f32x4*>(p + P.i0 + 4 * k));
     } else {
 #pragma unroll
         for (int j = 0; j < E; ++j)
@@ -255,8 +265,8 @@ __device__ __forceinline__ void store_u32(int32_t* __restrict__ p, const uint32_
     if (vector_ok(P, vec)) {
 #pragma unroll
         for (int k = 0; k < E / 4; ++k)
-            *reinterpret_cast<int4*>(p + P.i0 + 4 * k) =
-                make_int4((int)v[4 * k], (int)v[4 * k + 1], (int)v[4 * k + 2], (int)v[4 * k + 3]);
+            __builtin_nontemporal_store(u32x4{v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]},
+                                        reinterpret_cast<u32x4*>(p + P.i0 + 4 * k));
     } else {
 #pragma unroll
         for (int j = 0; j < E; ++j)
@@ -346,8 +356,29 @@ template <bool kBackward, class T>
 __device__ T lookback_carry(const uint64_t* rec, uint32_t tile, uint32_t num_tiles, uint32_t tag,
                             int lane, uint32_t* error)
 {
-    Aff<T> acc = identity<T>();
     uint32_t polls = 0;
+    // Common case first: the adjacent tile's aggregate alone settles the
+    // carry when its b is zero (a cut inside it, or gamma*lambda products
+    // that underflow across a tile).  Poll just that record, one load pair.
+    {
+        const uint64_t j = kBackward ? (uint64_t)tile + 1 : (uint64_t)tile - 1;
+        for (;;) {
+            const uint64_t wa = ld_agent(rec + 2 * j);
+            const uint64_t wb = ld_agent(rec + 2 * j + 1);
+            if ((uint32_t)(wa >> 32) == tag && (uint32_t)(wb >> 32) == tag) {
+                if (from_bits<T>((uint32_t)wb) == T(0)) return from_bits<T>((uint32_t)wa);
+                break;  // the segment continues past it: full look-back below
+            }
+            if (++polls > kMaxPolls) {
+                if (lane == 0)
+                    __hip_atomic_fetch_or(error, kErrTimeout, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+                return T(0);
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    }
+    Aff<T> acc = identity<T>();
     for (uint32_t base = 0;; base += kWave) {
         const int64_t j = kBackward ? (int64_t)tile + 1 + base + lane
                                     : (int64_t)tile - 1 - (int64_t)base - lane;
