@@ -206,7 +206,7 @@ lrs_status lrs_episodic_prefix_sum_f32(int64_t num_envs, int64_t seq_len,
 /* Diagnostics and tuning (process-wide; not for concurrent use).
  * force_lookback != 0: every later call takes the multi-block carry-
  *   propagation path, even where whole rows fit in one tile.
- * elems_per_lane x waves_per_block in {4x1, 4x4, 8x4, 16x4, 8x16}: fix the
+ * elems_per_lane x waves_per_block in {4x1, 4x4, 8x4, 4x8, 16x4, 4x16, 8x16}: fix the
  *   tile (elems_per_lane * 64 * waves_per_block elements) instead of
  *   choosing it from the shape; 0 x 0 restores the automatic choice.
  * Returns LRS_ERR_INVALID_ARG for an unsupported combination.  Results stay

@@ -223,10 +223,11 @@ struct Cfg {
     int E, W;
     uint32_t tile() const { return (uint32_t)(E * kWave * W); }
 };
-constexpr int kNumCfg = 5;  // ordered by tile size
-constexpr Cfg kCfgs[kNumCfg] = {{4, 1}, {4, 4}, {8, 4}, {16, 4}, {8, 16}};
+constexpr int kNumCfg = 7;  // ordered by tile size
+constexpr Cfg kCfgs[kNumCfg] = {{4, 1}, {4, 4}, {8, 4}, {4, 8}, {16, 4}, {4, 16}, {8, 16}};
 constexpr uint32_t kMinTile = 256;  // smallest tile the look-back path may use
-constexpr int kLookbackCfg = 2;  // 2048-element tiles
+constexpr int kAlignedCfgs[3] = {0, 1, 3};  // 4x1, 4x4, 4x8
+constexpr int kLookbackCfg = 3;             // 4x8: 2048-element tiles
 
 std::atomic<int> g_force_lookback{0};
 std::atomic<int> g_forced_cfg{-1};
@@ -254,9 +255,11 @@ size_t workspace_bytes_for(uint64_t total)
     return sizeof(WsHeader) + 16 * ((total + kMinTile - 1) / kMinTile);
 }
 
-// Pick the tile: the smallest tile holding whole rows (no cross-tile carry,
-// most blocks in flight); rows longer than every tile, or not dividing one,
-// take the look-back path.
+// Pick the tile.  Measured on MI355X: four elements per lane stream best,
+// and the look-back costs little once most tiles are settled by their
+// neighbour, so: the smallest of the 4-per-lane tiles (256, 1024, 2048
+// elements) that holds whole rows; otherwise the look-back path on
+// 2048-element tiles of eight waves.
 int choose_cfg(uint64_t total, uint64_t T, bool* lookback)
 {
     const int forced = g_forced_cfg.load();
@@ -267,7 +270,7 @@ int choose_cfg(uint64_t total, uint64_t T, bool* lookback)
         *lookback = force_lb || (tiles > 1 && kCfgs[c].tile() % T != 0);
         return c;
     }
-    for (int c = 0; c < kNumCfg; ++c) {
+    for (int c : kAlignedCfgs) {
         const uint64_t tiles = (total + kCfgs[c].tile() - 1) / kCfgs[c].tile();
         if (kCfgs[c].tile() % T == 0 || tiles == 1) {
             *lookback = false;
@@ -295,7 +298,9 @@ hipError_t launch_any(int cfg, const typename Op<4>::Args& a, const Sched& s, hi
         case 0: return launch_cfg<Op<4>, 4, 1>(a, s, stream);
         case 1: return launch_cfg<Op<4>, 4, 4>(a, s, stream);
         case 2: return launch_cfg<Op<8>, 8, 4>(a, s, stream);
-        case 3: return launch_cfg<Op<16>, 16, 4>(a, s, stream);
+        case 3: return launch_cfg<Op<4>, 4, 8>(a, s, stream);
+        case 4: return launch_cfg<Op<16>, 16, 4>(a, s, stream);
+        case 5: return launch_cfg<Op<4>, 4, 16>(a, s, stream);
         default: return launch_cfg<Op<8>, 8, 16>(a, s, stream);
     }
 }

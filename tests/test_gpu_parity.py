@@ -118,7 +118,8 @@ def test_small_shapes(est, shape):
 
 
 @pytest.mark.parametrize("est", ESTIMATORS)
-@pytest.mark.parametrize("tile", [(4, 1), (4, 4), (8, 4), (16, 4), (8, 16)], ids=lambda t: f"E{t[0]}W{t[1]}")
+@pytest.mark.parametrize("tile", [(4, 1), (4, 4), (8, 4), (4, 8), (16, 4), (4, 16), (8, 16)],
+                         ids=lambda t: f"E{t[0]}W{t[1]}")
 @pytest.mark.parametrize("shape", [(3, 1000), (2, 5000), (64, 128), (1, 20000)],
                          ids=lambda s: f"{s[0]}x{s[1]}")
 def test_forced_lookback(est, tile, shape):
