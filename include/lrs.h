@@ -89,7 +89,7 @@ const char* lrs_status_string(lrs_status s);
 const char* lrs_last_error(void);
 
 /* Bytes of workspace a call of `est` at [num_envs, seq_len] may need:
- * 4224 bytes plus 16 bytes per 256 elements (about 6% of one fp32 input).  The
+ * 4224 bytes plus 32 bytes per 256 elements (about 3% of one fp32 array).  The
  * same workspace serves every estimator at this or any smaller size.
  * Returns 0 for invalid sizes. */
 size_t lrs_workspace_bytes(lrs_estimator est, int64_t num_envs, int64_t seq_len);

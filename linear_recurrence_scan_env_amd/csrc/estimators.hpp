@@ -31,13 +31,14 @@ struct Ctx {
     bool vec;        // base pointers allow vector access
 };
 
-// Value of stream p at flat index i0+E (element 0 of the next lane).  Full
-// tiles load it in every lane (same cache line as the neighbouring lane's
+// Value of stream p at flat index i0+E (element 0 of the next chunk).  Full
+// tiles load it in every lane (same cache line as the neighbouring chunk's
 // vector load), unconditionally, so it is in flight with the lane's other
-// loads; it is discarded where unused.  The
-// guarded path takes it from the neighbouring lane and reads memory only in
-// the wave's last lane, where it is used.  `used` (the lane's last element is
-// not a row end) guarantees i0+E < N*T.
+// loads; it is discarded where unused.  The guarded path takes it from the
+// lane holding the next chunk (backward estimators hold chunks in reversed
+// lane order: lane L-1) and reads memory only in lane 0, which holds the
+// wave's last chunk.  `used` (the lane's last element is not a row end)
+// guarantees i0+E < N*T.
 template <int E, bool F>
 __device__ __forceinline__ float next_elem(float my0, const float* __restrict__ p,
                                            const Pos<E, F>& P, const Ctx& c, bool used)
@@ -48,8 +49,8 @@ __device__ __forceinline__ float next_elem(float my0, const float* __restrict__ 
         const float v = p[used ? P.i0 + E : P.i0];
         return used ? v : 0.0f;
     } else {
-        float v = lane_next(my0, c.lane, 0.0f);
-        if (c.lane == kWave - 1 && used) v = p[P.i0 + E];
+        float v = lane_prev(my0, 0.0f);
+        if (c.lane == 0) v = used ? p[P.i0 + E] : 0.0f;
         return v;
     }
 }
@@ -456,7 +457,7 @@ __device__ __forceinline__ uint32_t load_resets(const uint8_t* __restrict__ done
         const uint32_t w = dones[used ? P.i0 - 1 : P.i0] != 0 ? 1u : 0u;
         dprev = used ? w : 0u;
     } else {
-        dprev = lane_prev((d >> (E - 1)) & 1u, c.lane, 0u);
+        dprev = lane_prev((d >> (E - 1)) & 1u, 0u);
         if (c.lane == 0 && !(P.first & 1u) && P.count > 0 && P.i0 > 0)
             dprev = dones[P.i0 - 1] != 0 ? 1u : 0u;
     }

@@ -33,6 +33,15 @@ struct Sched {
     uint8_t* ws;         // workspace (look-back only)
     uint32_t T;
     uint32_t num_tiles;
+    // Look-back only.  When every row spans a whole number of tiles and
+    // there are many rows, tiles_per_row > 1 and block b takes position
+    // b / rows (counted from the end of the row for backward scans) of row
+    // b % rows: all rows' outermost tiles first, so a tile's neighbour ran
+    // `rows` blocks earlier and its aggregate is usually published before
+    // this block needs it.  Otherwise tiles_per_row = 0 and tiles are taken
+    // in flat order.
+    uint32_t tiles_per_row;
+    uint32_t rows;
     int lookback;
     int vec;
 };
@@ -59,11 +68,11 @@ __device__ __forceinline__ void finish_launch(WsHeader* hdr, uint32_t num_blocks
     __hip_atomic_store(&hdr->epoch, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <class T, int W>
+template <class A, int W>
 struct BlockShared {
-    T a[W];
-    T b[W];
-    T carry;
+    A a[W];
+    A b[W];
+    A carry;
     uint32_t tag;
     uint32_t open;
 };
@@ -74,9 +83,10 @@ struct BlockShared {
 template <class Op, int E, int W, bool F>
 __device__ __forceinline__ void tile_body(const typename Op::Args& args, const Sched& s,
                                           uint32_t tile, const Pos<E, F>& P, const Ctx& c,
-                                          BlockShared<typename Op::T, W>& sh)
+                                          BlockShared<typename AccOf<typename Op::T>::type, W>& sh)
 {
     using T = typename Op::T;
+    using A = typename AccOf<T>::type;  // composition type
     constexpr bool kB = Op::kBackward;
     const int tid = threadIdx.x;
     const int lane = c.lane;
@@ -84,73 +94,71 @@ __device__ __forceinline__ void tile_body(const typename Op::Args& args, const S
     WsHeader* hdr = reinterpret_cast<WsHeader*>(s.ws);
     uint64_t* rec = reinterpret_cast<uint64_t*>(s.ws + sizeof(WsHeader));
 
+    // The neighbour's record is read first, in flight with the tile's loads.
+    const bool far_most = kB ? (tile == s.num_tiles - 1u) : (tile == 0u);
+    Record early{{0, 0, 0, 0}};
+    if (s.lookback && !far_most && wave == 0) early = read_adjacent<kB>(rec, tile);
+
     T alpha[E], beta[E];
     typename Op::State st;
     Op::prepare(args, P, c, alpha, beta, st);
 
     // Lane aggregate, then the wave scan.
-    Aff<T> agg = identity<T>();
+    Aff<A> agg = identity<A>();
     if (kB) {
 #pragma unroll
-        for (int j = E - 1; j >= 0; --j) agg = combine(Aff<T>{alpha[j], beta[j]}, agg);
+        for (int j = E - 1; j >= 0; --j) agg = combine(Aff<A>{A(alpha[j]), A(beta[j])}, agg);
     } else {
 #pragma unroll
-        for (int j = 0; j < E; ++j) agg = combine(Aff<T>{alpha[j], beta[j]}, agg);
+        for (int j = 0; j < E; ++j) agg = combine(Aff<A>{A(alpha[j]), A(beta[j])}, agg);
     }
-    const Aff<T> inc = wave_scan<kB>(agg, lane);
-    const Aff<T> exc = wave_exclusive<kB>(inc, lane);
+    const Aff<A> inc = lane_scan(agg);  // lane 63 holds the wave total
+    const Aff<A> exc = lane_exclusive(inc);
 
-    Aff<T> tile_agg = identity<T>(), beyond = identity<T>();
-    T carry = T(0);
+    // The tile's far boundary element (backward: its last; forward: its
+    // first) sits in lane 0 of wave W-1 (backward) or of wave 0 (forward).
+    Aff<A> tile_agg = identity<A>(), beyond = identity<A>();
+    A carry = A(0);
     if constexpr (W == 1) {
         // One wave per block: everything stays in registers, no barrier.
-        const int near_lane = kB ? 0 : kWave - 1;
-        tile_agg = {readlane(inc.a, near_lane), readlane(inc.b, near_lane)};
+        tile_agg = readlane(inc, kWave - 1);
         if (s.lookback) {
             const uint32_t tag = __builtin_amdgcn_readfirstlane(__hip_atomic_load(
                                      &hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) + 1u;
-            const uint32_t open = readlane(Op::far_open(st) ? 1u : 0u, kB ? kWave - 1 : 0);
-            if (lane == 0) publish_aggregate<T>(rec, tile, tag, tile_agg);
-            const bool far_most = kB ? (tile == s.num_tiles - 1u) : (tile == 0u);
+            const uint32_t open = readlane(Op::far_open(st) ? 1u : 0u, 0);
+            if (lane == 0) publish_aggregate<A>(rec, tile, tag, tile_agg);
             if (!far_most && open)
-                carry = lookback_carry<kB, T>(rec, tile, s.num_tiles, tag, lane, &hdr->error);
+                carry = lookback_carry<kB, A>(rec, tile, s.num_tiles, tag, lane, &hdr->error, early);
             if (lane == 0) finish_launch(hdr, s.num_tiles, blockIdx.x, tag);
         }
     } else {
         if (s.lookback && tid == 0)
             sh.tag = __hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-        if (lane == (kB ? 0 : kWave - 1)) {
+        if (lane == kWave - 1) {
             sh.a[wave] = inc.a;
             sh.b[wave] = inc.b;
         }
-        if (kB ? (tid == W * kWave - 1) : (tid == 0)) sh.open = Op::far_open(st) ? 1u : 0u;
+        if (lane == 0 && wave == (kB ? W - 1 : 0)) sh.open = Op::far_open(st) ? 1u : 0u;
         __syncthreads();
 
-        // Compose the wave aggregates: the whole tile, and the waves beyond mine.
-        if (kB) {
-#pragma unroll
-            for (int v = W - 1; v >= 0; --v) {
-                const Aff<T> x{sh.a[v], sh.b[v]};
-                tile_agg = combine(x, tile_agg);
-                if (v > wave) beyond = combine(x, beyond);
-            }
-        } else {
-#pragma unroll
-            for (int v = 0; v < W; ++v) {
-                const Aff<T> x{sh.a[v], sh.b[v]};
-                tile_agg = combine(x, tile_agg);
-                if (v < wave) beyond = combine(x, beyond);
-            }
-        }
+        // Compose the wave totals: lane v holds wave v's; a row scan gives
+        // the whole tile and, for each wave, the waves beyond it (backward:
+        // the later waves; forward: the earlier ones).
+        Aff<A> x = identity<A>();
+        if (lane < W) x = {sh.a[lane], sh.b[lane]};
+        x = row_scan<kB, W>(x);
+        const int w = __builtin_amdgcn_readfirstlane(wave);
+        tile_agg = readlane(x, kB ? 0 : W - 1);
+        if (kB ? (w < W - 1) : (w > 0)) beyond = readlane(x, kB ? w + 1 : w - 1);
 
         if (s.lookback) {
             const uint32_t tag = sh.tag;
             if (wave == 0) {
-                if (lane == 0) publish_aggregate<T>(rec, tile, tag, tile_agg);
-                const bool far_most = kB ? (tile == s.num_tiles - 1u) : (tile == 0u);
-                T cin = T(0);
+                if (lane == 0) publish_aggregate<A>(rec, tile, tag, tile_agg);
+                A cin = A(0);
                 if (!far_most && sh.open)
-                    cin = lookback_carry<kB, T>(rec, tile, s.num_tiles, tag, lane, &hdr->error);
+                    cin = lookback_carry<kB, A>(rec, tile, s.num_tiles, tag, lane, &hdr->error,
+                                                early);
                 if (lane == 0) {
                     sh.carry = cin;
                     finish_launch(hdr, s.num_tiles, blockIdx.x, tag);
@@ -161,8 +169,8 @@ __device__ __forceinline__ void tile_body(const typename Op::Args& args, const S
         }
     }
 
-    const T wave_in = apply(beyond, carry);
-    const T lane_in = apply(exc, wave_in);
+    const A wave_in = apply(beyond, carry);
+    const T lane_in = T(apply(exc, wave_in));
     Op::finish(args, P, c, alpha, beta, st, lane_in);
 }
 
@@ -171,18 +179,30 @@ __global__ __launch_bounds__(W * kWave) void scan_kernel(const typename Op::Args
 {
     constexpr bool kB = Op::kBackward;
     constexpr uint32_t kTile = (uint32_t)E * kWave * W;
-    __shared__ BlockShared<typename Op::T, W> sh;
+    __shared__ BlockShared<typename AccOf<typename Op::T>::type, W> sh;
 
     const int tid = threadIdx.x;
-    // Backward scans on the look-back path take tiles from the end of the
-    // array, so the tile a block depends on always has a lower block index.
-    const uint32_t tile = (s.lookback && kB) ? s.num_tiles - 1u - blockIdx.x : blockIdx.x;
+    // On the look-back path the tile a block depends on always belongs to a
+    // block of lower index: backward scans take tiles from the end of their
+    // row (or of the array), forward scans from the start.
+    uint32_t tile = blockIdx.x;
+    if (s.lookback) {
+        if (s.tiles_per_row > 1) {
+            const uint32_t pos = blockIdx.x / s.rows, row = blockIdx.x % s.rows;
+            tile = row * s.tiles_per_row + (kB ? s.tiles_per_row - 1u - pos : pos);
+        } else if (kB) {
+            tile = s.num_tiles - 1u - blockIdx.x;
+        }
+    }
 
     // Where this lane's elements sit in their rows.
     const uint64_t tile_start = (uint64_t)tile * kTile;
     const uint64_t tile_row = tile_start / s.T;
     const uint32_t tile_t = (uint32_t)(tile_start - tile_row * s.T);
-    const uint32_t off = (uint32_t)tid * E;
+    // Backward estimators give lane L chunk 63-L of its wave (see scan_core.hpp).
+    const uint32_t lane = tid & (kWave - 1);
+    const uint32_t chunk = (tid - lane) + (kB ? kWave - 1 - lane : lane);
+    const uint32_t off = chunk * E;
     const uint64_t i0 = tile_start + off;
     const int count = i0 >= s.total ? 0 : (int)((s.total - i0) < (uint64_t)E ? (s.total - i0) : E);
     const uint32_t u = tile_t + off;
@@ -228,6 +248,7 @@ constexpr Cfg kCfgs[kNumCfg] = {{4, 1}, {4, 4}, {8, 4}, {4, 8}, {16, 4}, {4, 16}
 constexpr uint32_t kMinTile = 256;  // smallest tile the look-back path may use
 constexpr int kAlignedCfgs[3] = {0, 1, 3};  // 4x1, 4x4, 4x8
 constexpr int kLookbackCfg = 3;             // 4x8: 2048-element tiles
+constexpr int64_t kPositionMajorRows = 1024;
 
 std::atomic<int> g_force_lookback{0};
 std::atomic<int> g_forced_cfg{-1};
@@ -252,7 +273,7 @@ bool valid_sizes(int64_t N, int64_t T)
 
 size_t workspace_bytes_for(uint64_t total)
 {
-    return sizeof(WsHeader) + 16 * ((total + kMinTile - 1) / kMinTile);
+    return sizeof(WsHeader) + 8 * kRecordWords * ((total + kMinTile - 1) / kMinTile);
 }
 
 // Pick the tile.  Measured on MI355X: four elements per lane stream best,
@@ -321,9 +342,19 @@ lrs_status run(const char* name, int64_t N, int64_t T, const typename Op<4>::Arg
     s.T = (uint32_t)T;
     s.num_tiles = (uint32_t)((total + k.tile() - 1) / k.tile());
     s.lookback = lookback ? 1 : 0;
+    // Position-major order pays when rows outnumber the blocks resident at
+    // once (about 1000 here), so that a tile's neighbour has finished; with
+    // fewer rows, flat order keeps concurrent blocks on contiguous memory.
+    if ((uint64_t)T % k.tile() == 0 && N >= kPositionMajorRows) {
+        s.tiles_per_row = (uint32_t)((uint64_t)T / k.tile());
+        s.rows = (uint32_t)N;
+    } else {
+        s.tiles_per_row = 0;
+        s.rows = 0;
+    }
     s.ws = static_cast<uint8_t*>(ws);
     if (lookback) {
-        const size_t need = sizeof(WsHeader) + 16 * (size_t)s.num_tiles;
+        const size_t need = sizeof(WsHeader) + 8 * kRecordWords * (size_t)s.num_tiles;
         if (ws == nullptr || ws_bytes < need)
             return fail(LRS_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", name,
                         need, ws == nullptr ? (size_t)0 : ws_bytes);

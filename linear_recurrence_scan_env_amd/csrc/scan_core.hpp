@@ -33,30 +33,74 @@ __device__ __forceinline__ Aff<uint32_t> combine(Aff<uint32_t> near, Aff<uint32_
     return {near.b ? near.a + far.a : near.a, near.b & far.b};
 }
 
+__device__ __forceinline__ Aff<double> combine(Aff<double> near, Aff<double> far)
+{
+    return {fma(near.b, far.a, near.a), near.b * far.b};
+}
+
 __device__ __forceinline__ float apply(Aff<float> f, float x) { return fmaf(f.b, x, f.a); }
+__device__ __forceinline__ double apply(Aff<double> f, double x) { return fma(f.b, x, f.a); }
 __device__ __forceinline__ uint32_t apply(Aff<uint32_t> f, uint32_t x) { return f.b ? f.a + x : f.a; }
 
 template <class T>
 __device__ __forceinline__ Aff<T> identity() { return {T(0), T(1)}; }
 
+// Maps are composed in AccOf<T>: fp32 coefficients are composed in fp64, so
+// the products of many beta values across lanes, waves and tiles carry no
+// accumulated fp32 rounding; integer maps stay exact in uint32.
+template <class T>
+struct AccOf {
+    using type = T;
+};
+template <>
+struct AccOf<float> {
+    using type = double;
+};
+
 // ------------------------------------------------------- lane exchange
-// DPP row shifts move data between lanes of a 16-lane row inside one VALU
-// instruction (row_shl:n -- lane i reads lane i+n; row_shr:n -- lane i reads
-// lane i-n; a lane whose source is outside its row keeps `old`).  The three
-// row boundaries of a wave64 are bridged with v_readlane.
+//
+// Lane order.  Every scan runs forward in lane order: lane L's inclusive
+// value composes lanes 0..L with lane L nearest the output.  Forward
+// estimators give lane L the L-th chunk of the wave; backward estimators
+// give it chunk 63-L, so that "nearer the output" (earlier in time) is again
+// the higher lane.  Either way the wave total sits in lane 63 and a lane's
+// exclusive value comes from lane L-1.
+//
+// DPP (GFX9 encodings): row_shr:n -- lane i reads lane i-n of its 16-lane
+// row; row_shl:n -- lane i+n; row_bcast:15 / row_bcast:31 -- lane 15 of a
+// row / lane 31 feed the following row(s) selected by the row mask;
+// wave_shr:1 -- lane i reads lane i-1 across the wave.  A lane whose source
+// is invalid or whose row is masked off keeps `old`.
 constexpr int kDppRowShl = 0x100;
 constexpr int kDppRowShr = 0x110;
+constexpr int kDppWaveShr1 = 0x138;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
 
-template <int kCtrl>
+template <int kCtrl, int kRowMask = 0xf>
 __device__ __forceinline__ float dpp(float old, float src)
 {
     return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src),
-                                                      kCtrl, 0xf, 0xf, false));
+                                                      kCtrl, kRowMask, 0xf, false));
 }
-template <int kCtrl>
+template <int kCtrl, int kRowMask = 0xf>
 __device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t src)
 {
-    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, kCtrl, 0xf, 0xf, false);
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, kCtrl, kRowMask, 0xf, false);
+}
+template <int kCtrl, int kRowMask = 0xf>
+__device__ __forceinline__ double dpp(double old, double src)
+{
+    const int2 o = __builtin_bit_cast(int2, old), x = __builtin_bit_cast(int2, src);
+    const int2 r = make_int2(__builtin_amdgcn_update_dpp(o.x, x.x, kCtrl, kRowMask, 0xf, false),
+                             __builtin_amdgcn_update_dpp(o.y, x.y, kCtrl, kRowMask, 0xf, false));
+    return __builtin_bit_cast(double, r);
+}
+
+template <int kCtrl, int kRowMask = 0xf, class T>
+__device__ __forceinline__ Aff<T> dpp(Aff<T> old, Aff<T> src)
+{
+    return {dpp<kCtrl, kRowMask>(old.a, src.a), dpp<kCtrl, kRowMask>(old.b, src.b)};
 }
 
 __device__ __forceinline__ float readlane(float v, int l)
@@ -67,82 +111,60 @@ __device__ __forceinline__ uint32_t readlane(uint32_t v, int l)
 {
     return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
 }
-
-// Value held by lane+1 (lane 63 gets `edge`).
-template <class T>
-__device__ __forceinline__ T lane_next(T v, int lane, T edge)
+__device__ __forceinline__ double readlane(double v, int l)
 {
-    T r = dpp<kDppRowShl + 1>(edge, v);
-    const T r16 = readlane(v, 16), r32 = readlane(v, 32), r48 = readlane(v, 48);
-    if (lane == 15) r = r16;
-    if (lane == 31) r = r32;
-    if (lane == 47) r = r48;
-    return r;
+    const int2 x = __builtin_bit_cast(int2, v);
+    return __builtin_bit_cast(double, make_int2(__builtin_amdgcn_readlane(x.x, l),
+                                                __builtin_amdgcn_readlane(x.y, l)));
+}
+template <class T>
+__device__ __forceinline__ Aff<T> readlane(Aff<T> v, int l)
+{
+    return {readlane(v.a, l), readlane(v.b, l)};
 }
 
 // Value held by lane-1 (lane 0 gets `edge`).
 template <class T>
-__device__ __forceinline__ T lane_prev(T v, int lane, T edge)
+__device__ __forceinline__ T lane_prev(T v, T edge)
 {
-    T r = dpp<kDppRowShr + 1>(edge, v);
-    const T r15 = readlane(v, 15), r31 = readlane(v, 31), r47 = readlane(v, 47);
-    if (lane == 16) r = r15;
-    if (lane == 32) r = r31;
-    if (lane == 48) r = r47;
-    return r;
+    return dpp<kDppWaveShr1>(edge, v);
 }
 
-// Inclusive scan over the 64 lanes of a wave.  Backward: lane L ends up with
-// the composition of lanes L..63 (far = higher lanes).  Forward: lanes 0..L.
-// Four DPP steps scan each 16-lane row; the row totals are then combined
-// through v_readlane and folded into each row.
-template <bool kBackward, class T>
-__device__ __forceinline__ Aff<T> wave_scan(Aff<T> x, int lane)
+// Inclusive forward scan over the 64 lanes: four row_shr steps inside each
+// 16-lane row, then row_bcast:15 and row_bcast:31 carry row totals into the
+// rows above.
+template <class T>
+__device__ __forceinline__ Aff<T> lane_scan(Aff<T> x)
 {
     const Aff<T> id = identity<T>();
-#define LRS_ROW_STEP(n)                                                          \
-    {                                                                            \
-        Aff<T> f;                                                                \
-        if (kBackward) {                                                         \
-            f.a = dpp<kDppRowShl + (n)>(id.a, x.a);                              \
-            f.b = dpp<kDppRowShl + (n)>(id.b, x.b);                              \
-        } else {                                                                 \
-            f.a = dpp<kDppRowShr + (n)>(id.a, x.a);                              \
-            f.b = dpp<kDppRowShr + (n)>(id.b, x.b);                              \
-        }                                                                        \
-        x = combine(x, f);                                                       \
-    }
-    LRS_ROW_STEP(1)
-    LRS_ROW_STEP(2)
-    LRS_ROW_STEP(4)
-    LRS_ROW_STEP(8)
-#undef LRS_ROW_STEP
-    const int row = lane >> 4;
-    if (kBackward) {
-        // row totals sit in lanes 16r; suffix over rows 3..1
-        const Aff<T> s3{readlane(x.a, 48), readlane(x.b, 48)};
-        const Aff<T> s2 = combine(Aff<T>{readlane(x.a, 32), readlane(x.b, 32)}, s3);
-        const Aff<T> s1 = combine(Aff<T>{readlane(x.a, 16), readlane(x.b, 16)}, s2);
-        const Aff<T> far = row == 0 ? s1 : (row == 1 ? s2 : (row == 2 ? s3 : id));
-        x = combine(x, far);
-    } else {
-        // row totals sit in lanes 16r+15; prefix over rows 0..2
-        const Aff<T> p0{readlane(x.a, 15), readlane(x.b, 15)};
-        const Aff<T> p1 = combine(Aff<T>{readlane(x.a, 31), readlane(x.b, 31)}, p0);
-        const Aff<T> p2 = combine(Aff<T>{readlane(x.a, 47), readlane(x.b, 47)}, p1);
-        const Aff<T> far = row == 3 ? p2 : (row == 2 ? p1 : (row == 1 ? p0 : id));
-        x = combine(x, far);
-    }
+    x = combine(x, dpp<kDppRowShr + 1>(id, x));
+    x = combine(x, dpp<kDppRowShr + 2>(id, x));
+    x = combine(x, dpp<kDppRowShr + 4>(id, x));
+    x = combine(x, dpp<kDppRowShr + 8>(id, x));
+    x = combine(x, dpp<kDppRowBcast15, 0xa>(id, x));
+    x = combine(x, dpp<kDppRowBcast31, 0xc>(id, x));
     return x;
 }
 
-// Exclusive value of a lane: the inclusive scan of its far neighbour.
-template <bool kBackward, class T>
-__device__ __forceinline__ Aff<T> wave_exclusive(Aff<T> inc, int lane)
+// Exclusive value of a lane: the inclusive value of lane-1.
+template <class T>
+__device__ __forceinline__ Aff<T> lane_exclusive(Aff<T> inc)
 {
+    return dpp<kDppWaveShr1>(identity<T>(), inc);
+}
+
+// Inclusive scan of lanes 0..W-1 (W <= 16, all in row 0).  kSuffix: lane v
+// composes lanes v..W-1 (far = higher lanes); otherwise lanes 0..v.
+template <bool kSuffix, int W, class T>
+__device__ __forceinline__ Aff<T> row_scan(Aff<T> x)
+{
+    static_assert(W >= 1 && W <= 16, "one 16-lane row");
     const Aff<T> id = identity<T>();
-    if (kBackward) return {lane_next(inc.a, lane, id.a), lane_next(inc.b, lane, id.b)};
-    return {lane_prev(inc.a, lane, id.a), lane_prev(inc.b, lane, id.b)};
+    if (W > 1) x = combine(x, kSuffix ? dpp<kDppRowShl + 1>(id, x) : dpp<kDppRowShr + 1>(id, x));
+    if (W > 2) x = combine(x, kSuffix ? dpp<kDppRowShl + 2>(id, x) : dpp<kDppRowShr + 2>(id, x));
+    if (W > 4) x = combine(x, kSuffix ? dpp<kDppRowShl + 4>(id, x) : dpp<kDppRowShr + 4>(id, x));
+    if (W > 8) x = combine(x, kSuffix ? dpp<kDppRowShl + 8>(id, x) : dpp<kDppRowShr + 8>(id, x));
+    return x;
 }
 
 // ----------------------------------------------------------------- loads
@@ -276,12 +298,13 @@ __device__ __forceinline__ void store_u32(int32_t* __restrict__ p, const uint32_
 
 // ------------------------------------------------ cross-tile carry protocol
 //
-// Workspace: a header followed by one 16-byte record per tile: two 64-bit
-// words, each (tag << 32 | payload), the payloads being the bit patterns of
-// the tile aggregate's a and b.  Every word is written and read with
-// single-copy-atomic 64-bit accesses at agent scope, and each word carries
-// its own tag, so a reader that sees both tags equal to this launch's tag
-// holds a consistent aggregate without any fence.
+// Workspace: a header followed by one 32-byte record per tile: four 64-bit
+// words, each (tag << 32 | payload), the payloads being the low and high
+// halves of the tile aggregate's a and b (64-bit composition values; the
+// integer prefix sum leaves the high halves zero).  Every word is written
+// and read with single-copy-atomic 64-bit accesses at agent scope, and each
+// word carries its own tag, so a reader that sees all four tags equal to this
+// launch's tag holds a consistent aggregate without any fence.
 //
 // Header: the launch epoch, an error word, and block-completion counters
 // spread over kGroups cache lines (block b counts itself in group b % kGroups;
@@ -292,12 +315,11 @@ __device__ __forceinline__ void store_u32(int32_t* __restrict__ p, const uint32_
 // tags, or the zero fill) are never mistaken for fresh ones.  Spreading the
 // counters keeps same-address atomics, which serialize, to a few per line.
 //
-// Tiles are taken in dispatch order (backward scans from the end of the
-// array), so a tile only waits for tiles of lower block index.  Workgroups
-// of a dispatch are started in index order, so those blocks are running or
-// finished and every wait ends; each wait is also bounded (kMaxPolls), so a
-// violated assumption or a corrupted workspace yields a flagged error in the
-// header instead of a hang.
+// A tile only ever waits for tiles of lower block index (the host maps
+// blocks to tiles so).  Workgroups of a dispatch are started in index order,
+// so those blocks are running or finished and every wait ends; each wait is
+// also bounded (kMaxPolls), so a violated assumption or a corrupted
+// workspace yields a flagged error in the header instead of a hang.
 
 constexpr uint32_t kGroups = 32;
 constexpr uint32_t kLine = 128;  // bytes between counters
@@ -327,22 +349,66 @@ __device__ __forceinline__ void st_agent(uint64_t* p, uint64_t v)
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ uint32_t bits_of(float x) { return __float_as_uint(x); }
-__device__ __forceinline__ uint32_t bits_of(uint32_t x) { return x; }
-template <class T>
-__device__ __forceinline__ T from_bits(uint32_t x);
-template <>
-__device__ __forceinline__ float from_bits<float>(uint32_t x) { return __uint_as_float(x); }
-template <>
-__device__ __forceinline__ uint32_t from_bits<uint32_t>(uint32_t x) { return x; }
+constexpr uint32_t kRecordWords = 4;
 
-template <class T>
-__device__ __forceinline__ void publish_aggregate(uint64_t* rec, uint32_t tile, uint32_t tag,
-                                                  Aff<T> agg)
+__device__ __forceinline__ uint64_t payload_bits(double x) { return __builtin_bit_cast(uint64_t, x); }
+__device__ __forceinline__ uint64_t payload_bits(uint32_t x) { return x; }
+template <class A>
+__device__ __forceinline__ A from_payload(uint32_t lo, uint32_t hi);
+template <>
+__device__ __forceinline__ double from_payload<double>(uint32_t lo, uint32_t hi)
 {
-    const uint64_t hi = (uint64_t)tag << 32;
-    st_agent(rec + 2 * (uint64_t)tile, hi | bits_of(agg.a));
-    st_agent(rec + 2 * (uint64_t)tile + 1, hi | bits_of(agg.b));
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+template <>
+__device__ __forceinline__ uint32_t from_payload<uint32_t>(uint32_t lo, uint32_t)
+{
+    return lo;
+}
+
+template <class A>
+__device__ __forceinline__ void publish_aggregate(uint64_t* rec, uint32_t tile, uint32_t tag,
+                                                  Aff<A> agg)
+{
+    const uint64_t t = (uint64_t)tag << 32;
+    const uint64_t a = payload_bits(agg.a), b = payload_bits(agg.b);
+    uint64_t* r = rec + kRecordWords * (uint64_t)tile;
+    st_agent(r + 0, t | (a & 0xffffffffu));
+    st_agent(r + 1, t | (a >> 32));
+    st_agent(r + 2, t | (b & 0xffffffffu));
+    st_agent(r + 3, t | (b >> 32));
+}
+
+// One tile's record as read (possibly stale).
+struct Record {
+    uint64_t w[kRecordWords];
+};
+
+__device__ __forceinline__ Record read_record(const uint64_t* rec, uint64_t tile)
+{
+    const uint64_t* r = rec + kRecordWords * tile;
+    return {{ld_agent(r + 0), ld_agent(r + 1), ld_agent(r + 2), ld_agent(r + 3)}};
+}
+
+__device__ __forceinline__ bool record_current(const Record& x, uint32_t tag)
+{
+    return (uint32_t)(x.w[0] >> 32) == tag && (uint32_t)(x.w[1] >> 32) == tag &&
+           (uint32_t)(x.w[2] >> 32) == tag && (uint32_t)(x.w[3] >> 32) == tag;
+}
+
+template <class A>
+__device__ __forceinline__ Aff<A> record_value(const Record& x)
+{
+    return {from_payload<A>((uint32_t)x.w[0], (uint32_t)x.w[1]),
+            from_payload<A>((uint32_t)x.w[2], (uint32_t)x.w[3])};
+}
+
+// The adjacent tile's record, read as early as possible (issued with the
+// tile's own loads); lookback_carry() re-polls it only if this copy is stale.
+template <bool kBackward>
+__device__ __forceinline__ Record read_adjacent(const uint64_t* rec, uint32_t tile)
+{
+    return read_record(rec, kBackward ? (uint64_t)tile + 1 : (uint64_t)tile - 1);
 }
 
 // Executed by one full wave.  Returns the value entering `tile` from its far
@@ -352,58 +418,59 @@ __device__ __forceinline__ void publish_aggregate(uint64_t* rec, uint32_t tile, 
 // b is zero (a segment boundary) or the end of the array.  Only aggregates
 // are used, combined in a fixed order, so the result does not depend on
 // timing (deterministic run to run).
-template <bool kBackward, class T>
-__device__ T lookback_carry(const uint64_t* rec, uint32_t tile, uint32_t num_tiles, uint32_t tag,
-                            int lane, uint32_t* error)
+template <bool kBackward, class A>
+__device__ A lookback_carry(const uint64_t* rec, uint32_t tile, uint32_t num_tiles, uint32_t tag,
+                            int lane, uint32_t* error, const Record& early)
 {
     uint32_t polls = 0;
     // Common case first: the adjacent tile's aggregate alone settles the
     // carry when its b is zero (a cut inside it, or gamma*lambda products
-    // that underflow across a tile).  Poll just that record, one load pair.
+    // that underflow across a tile).  Check the early copy, then poll just
+    // that record.
     {
         const uint64_t j = kBackward ? (uint64_t)tile + 1 : (uint64_t)tile - 1;
-        for (;;) {
-            const uint64_t wa = ld_agent(rec + 2 * j);
-            const uint64_t wb = ld_agent(rec + 2 * j + 1);
-            if ((uint32_t)(wa >> 32) == tag && (uint32_t)(wb >> 32) == tag) {
-                if (from_bits<T>((uint32_t)wb) == T(0)) return from_bits<T>((uint32_t)wa);
+        for (bool first = true;; first = false) {
+            const Record x = first ? early : read_record(rec, j);
+            if (record_current(x, tag)) {
+                const Aff<A> v = record_value<A>(x);
+                if (v.b == A(0)) return v.a;
                 break;  // the segment continues past it: full look-back below
             }
             if (++polls > kMaxPolls) {
                 if (lane == 0)
                     __hip_atomic_fetch_or(error, kErrTimeout, __ATOMIC_RELAXED,
                                           __HIP_MEMORY_SCOPE_AGENT);
-                return T(0);
+                return A(0);
             }
             __builtin_amdgcn_s_sleep(1);
         }
     }
-    Aff<T> acc = identity<T>();
+    // Window of 64 neighbours: lane l holds the one at distance 63 - l (lane
+    // 63 the adjacent tile), so that the forward lane scan composes them
+    // nearest-first and lane 63 ends with the whole composition.
+    Aff<A> acc = identity<A>();
     for (uint32_t base = 0;; base += kWave) {
-        const int64_t j = kBackward ? (int64_t)tile + 1 + base + lane
-                                    : (int64_t)tile - 1 - (int64_t)base - lane;
+        const int64_t d = (int64_t)base + (kWave - 1 - lane);
+        const int64_t j = kBackward ? (int64_t)tile + 1 + d : (int64_t)tile - 1 - d;
         const bool exists = j >= 0 && j < (int64_t)num_tiles;
-        Aff<T> v = {T(0), T(0)};  // beyond the array: nothing flows in
+        Aff<A> v = {A(0), A(0)};  // beyond the array: nothing flows in
         bool have = !exists;
         for (;;) {
             if (!have) {
-                const uint64_t wa = ld_agent(rec + 2 * (uint64_t)j);
-                const uint64_t wb = ld_agent(rec + 2 * (uint64_t)j + 1);
-                if ((uint32_t)(wa >> 32) == tag && (uint32_t)(wb >> 32) == tag) {
+                const Record x = read_record(rec, (uint64_t)j);
+                if (record_current(x, tag)) {
                     have = true;
-                    v.a = from_bits<T>((uint32_t)wa);
-                    v.b = from_bits<T>((uint32_t)wb);
+                    v = record_value<A>(x);
                 }
             }
-            const uint64_t zero_b = __ballot(have && v.b == T(0));
+            const uint64_t zero_b = __ballot(have && v.b == A(0));
             const uint64_t missing = __ballot(!have);
-            const int k = zero_b ? __ffsll((unsigned long long)zero_b) - 1 : kWave - 1;
-            const uint64_t needed = (k == kWave - 1) ? ~0ull : ((2ull << k) - 1ull);
+            // nearest neighbour with b == 0 = the highest such lane
+            const int l0 = zero_b ? 63 - __clzll((long long)zero_b) : 0;
+            const uint64_t needed = ~0ull << l0;  // lanes l0..63
             if ((missing & needed) == 0) {
-                if (lane > k) v = identity<T>();
-                Aff<T> tot = wave_scan<true>(v, lane);  // lane 0 = composition of 0..k
-                tot.a = readlane(tot.a, 0);
-                tot.b = readlane(tot.b, 0);
+                if (lane < l0) v = identity<A>();
+                const Aff<A> tot = readlane(lane_scan(v), kWave - 1);
                 acc = combine(acc, tot);
                 if (zero_b) return acc.a;
                 break;  // all 64 neighbours continue the segment: next window
@@ -412,7 +479,7 @@ __device__ T lookback_carry(const uint64_t* rec, uint32_t tile, uint32_t num_til
                 if (lane == 0)
                     __hip_atomic_fetch_or(error, kErrTimeout, __ATOMIC_RELAXED,
                                           __HIP_MEMORY_SCOPE_AGENT);
-                return T(0);
+                return A(0);
             }
             __builtin_amdgcn_s_sleep(1);
         }

@@ -61,8 +61,8 @@ def test_version_and_strings(lib):
 
 
 def test_workspace_bytes(lib):
-    assert lib.lrs_workspace_bytes(0, 4096, 128) == 4224 + 16 * (4096 * 128 // 256)
-    assert lib.lrs_workspace_bytes(1, 1, 1) == 4224 + 16
+    assert lib.lrs_workspace_bytes(0, 4096, 128) == 4224 + 32 * (4096 * 128 // 256)
+    assert lib.lrs_workspace_bytes(1, 1, 1) == 4224 + 32
     assert lib.lrs_workspace_bytes(0, 0, 128) == 0
     assert lib.lrs_workspace_bytes(0, 5, 0) == 0
     assert lib.lrs_workspace_bytes(0, 1 << 20, 1 << 20) == 0  # 2^40 elements: over the limit

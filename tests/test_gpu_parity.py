@@ -120,10 +120,11 @@ def test_small_shapes(est, shape):
 @pytest.mark.parametrize("est", ESTIMATORS)
 @pytest.mark.parametrize("tile", [(4, 1), (4, 4), (8, 4), (4, 8), (16, 4), (4, 16), (8, 16)],
                          ids=lambda t: f"E{t[0]}W{t[1]}")
-@pytest.mark.parametrize("shape", [(3, 1000), (2, 5000), (64, 128), (1, 20000)],
+@pytest.mark.parametrize("shape", [(3, 1000), (2, 5000), (64, 128), (1, 20000), (1024, 2048)],
                          ids=lambda s: f"{s[0]}x{s[1]}")
 def test_forced_lookback(est, tile, shape):
-    """Carry propagation across tiles, for every tile shape."""
+    """Carry propagation across tiles, for every tile shape (1024 x 2048 also
+    takes the position-major tile order)."""
     N, T = shape
     ro = workloads.rollout(N, T, seed=11 + T, term_p=0.002, trunc_p=0.002, gamma=0.99,
                            lambda_=0.97)
