@@ -44,7 +44,50 @@ struct Sched {
     uint32_t rows;
     int lookback;
     int vec;
+    // Division by T without a divide: shifts when T is a power of two
+    // (log2T), else a multiply by magic = floor(2^64 / T) + 1.
+    uint64_t magic;
+    uint32_t log2T;
+    int pow2;
+    // T is a multiple of the elements per lane: a lane's elements never
+    // cross a row end, so their row-start and row-end bits take two compares.
+    int lane_in_row;
 };
+
+// Row and step of a flat index below 2^35.  The multiply-high estimate
+// floor(n * magic / 2^64) exceeds n / T by less than n / 2^64, so it is the
+// quotient or one above it; one correction makes it exact.
+__device__ __forceinline__ void split_index(uint64_t n, const Sched& s, uint64_t& row, uint32_t& t)
+{
+    if (s.pow2) {
+        row = n >> s.log2T;
+        t = (uint32_t)n & (s.T - 1u);
+        return;
+    }
+    uint64_t q = __umul64hi(n, s.magic);
+    int64_t r = (int64_t)(n - q * s.T);
+    if (r < 0) {
+        --q;
+        r += s.T;
+    }
+    row = q;
+    t = (uint32_t)r;
+}
+
+// Same for a 32-bit index u: the overshoot u / 2^64 * (magic - 2^64 / T) is
+// below 2^-32 < 1 / T, so the estimate is already the quotient.  Only the
+// high 64 bits of the 96-bit product u * magic are formed.
+__device__ __forceinline__ void split_index32(uint32_t u, const Sched& s, uint32_t& q, uint32_t& t)
+{
+    if (s.pow2) {
+        q = u >> s.log2T;
+        t = u & (s.T - 1u);
+        return;
+    }
+    const uint32_t mlo = (uint32_t)s.magic, mhi = (uint32_t)(s.magic >> 32);
+    q = (uint32_t)(((uint64_t)u * mhi + __umulhi(u, mlo)) >> 32);
+    t = u - q * s.T;
+}
 
 // Called once per block (one thread) after its last look-back read.
 __device__ __forceinline__ void finish_launch(WsHeader* hdr, uint32_t num_blocks, uint32_t block,
@@ -186,33 +229,41 @@ __global__ __launch_bounds__(W * kWave) void scan_kernel(const typename Op::Args
     // block of lower index: backward scans take tiles from the end of their
     // row (or of the array), forward scans from the start.
     uint32_t tile = blockIdx.x;
-    if (s.lookback) {
-        if (s.tiles_per_row > 1) {
-            const uint32_t pos = blockIdx.x / s.rows, row = blockIdx.x % s.rows;
-            tile = row * s.tiles_per_row + (kB ? s.tiles_per_row - 1u - pos : pos);
-        } else if (kB) {
-            tile = s.num_tiles - 1u - blockIdx.x;
-        }
+    uint64_t tile_row;
+    uint32_t tile_t;
+    if (s.lookback && s.tiles_per_row > 1) {
+        const uint32_t pos = blockIdx.x / s.rows, row = blockIdx.x % s.rows;
+        const uint32_t p = kB ? s.tiles_per_row - 1u - pos : pos;
+        tile = row * s.tiles_per_row + p;
+        tile_row = row;
+        tile_t = p * kTile;
+    } else {
+        if (s.lookback && kB) tile = s.num_tiles - 1u - blockIdx.x;
+        split_index((uint64_t)tile * kTile, s, tile_row, tile_t);
     }
+    const uint64_t tile_start = (uint64_t)tile * kTile;
 
     // Where this lane's elements sit in their rows.
-    const uint64_t tile_start = (uint64_t)tile * kTile;
-    const uint64_t tile_row = tile_start / s.T;
-    const uint32_t tile_t = (uint32_t)(tile_start - tile_row * s.T);
     // Backward estimators give lane L chunk 63-L of its wave (see scan_core.hpp).
     const uint32_t lane = tid & (kWave - 1);
     const uint32_t chunk = (tid - lane) + (kB ? kWave - 1 - lane : lane);
     const uint32_t off = chunk * E;
     const uint64_t i0 = tile_start + off;
     const int count = i0 >= s.total ? 0 : (int)((s.total - i0) < (uint64_t)E ? (s.total - i0) : E);
-    const uint32_t u = tile_t + off;
-    const uint64_t n0 = tile_row + u / s.T;
-    uint32_t t = u % s.T, last = 0, first = 0;
+    uint32_t q, t;
+    split_index32(tile_t + off, s, q, t);  // tile_t + off < 2^31 + 2^14
+    const uint64_t n0 = tile_row + q;
+    uint32_t last = 0, first = 0;
+    if (s.lane_in_row) {
+        if (t + (uint32_t)E == s.T) last = 1u << (E - 1);
+        if (t == 0) first = 1u;
+    } else {
 #pragma unroll
-    for (int j = 0; j < E; ++j) {
-        if (t == s.T - 1) last |= 1u << j;
-        if (t == 0) first |= 1u << j;
-        t = (t == s.T - 1) ? 0u : t + 1u;
+        for (int j = 0; j < E; ++j) {
+            if (t == s.T - 1) last |= 1u << j;
+            if (t == 0) first |= 1u << j;
+            t = (t == s.T - 1) ? 0u : t + 1u;
+        }
     }
     const Ctx c{s.total, s.T, tid & (kWave - 1), s.vec != 0};
 
@@ -352,6 +403,11 @@ lrs_status run(const char* name, int64_t N, int64_t T, const typename Op<4>::Arg
         s.tiles_per_row = 0;
         s.rows = 0;
     }
+    s.pow2 = (T & (T - 1)) == 0 ? 1 : 0;
+    s.log2T = 0;
+    while ((1ull << s.log2T) < (uint64_t)T) ++s.log2T;
+    s.magic = s.pow2 ? 0 : ~0ull / (uint64_t)T + 1ull;  // T >= 3 here: no overflow
+    s.lane_in_row = (uint64_t)T % (uint64_t)k.E == 0 ? 1 : 0;
     s.ws = static_cast<uint8_t*>(ws);
     if (lookback) {
         const size_t need = sizeof(WsHeader) + 8 * kRecordWords * (size_t)s.num_tiles;

@@ -230,10 +230,12 @@ __device__ __forceinline__ void load_u32(uint32_t (&v)[E], const int32_t* __rest
 // Bit k of the result is (byte k of w != 0).
 __device__ __forceinline__ uint32_t nonzero_bytes(uint32_t w)
 {
-    uint32_t bits = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) bits |= (((w >> (8 * k)) & 0xffu) != 0u ? 1u : 0u) << k;
-    return bits;
+    // Bit 7 of each byte of h is set iff that byte of w is nonzero (the low
+    // seven bits plus 0x7f carry into bit 7 without leaving the byte).
+    const uint32_t h = (((w & 0x7f7f7f7fu) + 0x7f7f7f7fu) | w) & 0x80808080u;
+    // Multiplying by 2^21 + 2^14 + 2^7 + 1 moves bits 7, 15, 23, 31 to bits
+    // 28..31; no two partial products share a bit, so nothing carries.
+    return (h * 0x00204081u) >> 28;
 }
 
 // Bit j of the result is (mask[i0 + j] != 0); a null mask reads as all zero.

@@ -120,7 +120,8 @@ def test_small_shapes(est, shape):
 @pytest.mark.parametrize("est", ESTIMATORS)
 @pytest.mark.parametrize("tile", [(4, 1), (4, 4), (8, 4), (4, 8), (16, 4), (4, 16), (8, 16)],
                          ids=lambda t: f"E{t[0]}W{t[1]}")
-@pytest.mark.parametrize("shape", [(3, 1000), (2, 5000), (64, 128), (1, 20000), (1024, 2048)],
+@pytest.mark.parametrize("shape", [(3, 1000), (2, 5000), (64, 128), (1, 20000), (1024, 2048),
+                                   (5, 3001)],
                          ids=lambda s: f"{s[0]}x{s[1]}")
 def test_forced_lookback(est, tile, shape):
     """Carry propagation across tiles, for every tile shape (1024 x 2048 also
@@ -133,6 +134,17 @@ def test_forced_lookback(est, tile, shape):
         check(run_pair(est, ro), T)
     finally:
         lrs.set_schedule(False, 0, 0)
+
+
+@pytest.mark.parametrize("est", ["gae", "discounted_returns", "prefix_sum_i32", "prefix_sum_f32"])
+def test_long_odd_rows(est):
+    """Rows of odd length far beyond a 32-bit tile offset's reach of a row
+    start: row and step of every element come from the multiply-high
+    division, and a lane's elements straddle row ends."""
+    N, T = 3, 7_000_003
+    ro = workloads.rollout(N, T, seed=17, term_p=1e-4, trunc_p=1e-4, gamma=0.99, lambda_=0.97,
+                           done_p=1e-4)
+    check(run_pair(est, ro, trunc=est == "gae"), T)
 
 
 @pytest.mark.parametrize("est", ESTIMATORS)
