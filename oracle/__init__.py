@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for the seven RL credit-assignment estimators.
+"""fp64 CPU oracle for the seven RL credit-assignment estimators and the
+generic segmented affine scan they reduce to.
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
 CPU-baseline leg of the benchmark may import this package.  The product
@@ -90,6 +91,7 @@ def _open(path):
         "lrs_oracle_eligibility_traces": [I, I, P, P, D, D, P],
         "lrs_oracle_prefix_sum_f32": [I, I, P, P, P],
         "lrs_oracle_prefix_sum_i32": [I, I, P, P, P],
+        "lrs_oracle_affine_scan": [I, I, P, P, P, P, ctypes.c_int, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -225,4 +227,18 @@ def prefix_sum(x, dones):
     d = _mask(dones, xs.shape)
     out = np.empty(xs.shape, np.float64)
     _load().lrs_oracle_prefix_sum_f32(xs.shape[0], xs.shape[1], _ptr(xs), _ptr(d), _ptr(out))
+    return out
+
+
+def affine_scan(alpha, beta, *, reset=None, carry_in=None, reverse=False):
+    """y_t = alpha_t + beta_t * y_prev along each row (prev = t-1, or t+1 when
+    reverse); y_prev of the first step in scan order is carry_in[n] (0 if
+    None); a nonzero reset[t] drops the beta_t * y_prev term.  float64 out."""
+    a = _f32(alpha)
+    b = _f32(beta, a.shape)
+    rs = _mask(reset, a.shape)
+    c = None if carry_in is None else _f32(carry_in, (a.shape[0],))
+    out = np.empty(a.shape, np.float64)
+    _load().lrs_oracle_affine_scan(a.shape[0], a.shape[1], _ptr(a), _ptr(b), _ptr(rs), _ptr(c),
+                                   1 if reverse else 0, _ptr(out))
     return out

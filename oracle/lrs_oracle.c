@@ -7,6 +7,8 @@
  * leg of the benchmark do.  It shares no code, header, table or helper with
  * the HIP path.
  *
+ * Also the generic segmented affine scan those estimators reduce to.
+ *
  * Sources (cited by title and section; no other text is relied on):
  *   [P1] "rl-triton: High-Performance Triton GPU Kernels for Reinforcement
  *        Learning Credit Assignment", gist.science summary page, Technical
@@ -280,6 +282,35 @@ void lrs_oracle_prefix_sum_i32(int64_t N, int64_t T, const int32_t* x,
             if (t == 0 || done[i - 1]) s = 0;
             s += (int64_t)x[i];
             out[i] = (int32_t)(uint32_t)(uint64_t)s;
+        }
+    }
+}
+
+/* Generic segmented first-order linear recurrence, the operator all seven
+ * estimators reduce to ([P1] Methodology 1, Unified Algebraic Framework; the
+ * same page's Significance and Claims section names other segmented affine
+ * recurrences as further users).  Scan order runs along t (reverse = 0) or
+ * against it (reverse = 1); "previous" means the neighbour earlier in scan
+ * order:
+ *   reverse = 0:  y_t = alpha_t + beta_t * y_{t-1}
+ *   reverse = 1:  y_t = alpha_t + beta_t * y_{t+1}
+ * The step before the first one in scan order is carry[n] (0 if carry is
+ * NULL).  Where reset[t] is nonzero (reset may be NULL), y_t = alpha_t: the
+ * recursion does not read the previous step, as if beta_t were 0.           */
+void lrs_oracle_affine_scan(int64_t N, int64_t T, const float* alpha,
+                            const float* beta, const uint8_t* reset,
+                            const float* carry, int reverse, double* out)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        double y = carry ? (double)carry[n] : 0.0;
+        for (int64_t k = 0; k < T; ++k) {
+            int64_t t = reverse ? T - 1 - k : k;
+            size_t i = IDX(n, t);
+            double next = (double)alpha[i];
+            if (!(reset && reset[i])) next += (double)beta[i] * y;
+            out[i] = next;
+            y = next;
         }
     }
 }

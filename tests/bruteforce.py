@@ -196,3 +196,34 @@ def prefix(x, done):
             s = _seg_start(d, n, t)
             out[n, t] = float(sum(xf[n, s:t + 1]))
     return out
+
+
+def affine(alpha, beta, reset=None, carry=None, reverse=False):
+    """Generic segmented affine scan from its sum form:
+        y_t = sum_{k in chain(t)} (prod of beta over the steps from t up to,
+              not including, k) * alpha_k  [+ the same product over the whole
+              chain times carry[n], when the chain reaches the row's start]
+    where chain(t) walks from t against the scan order (t, t-1, ... forward;
+    t, t+1, ... reverse) and stops after the first step whose reset is set.
+    """
+    a = np.asarray(alpha, dtype=np.float64)
+    b = np.asarray(beta, dtype=np.float64)
+    rs = np.zeros(a.shape, bool) if reset is None else (np.asarray(reset) != 0)
+    c = np.zeros(a.shape[0]) if carry is None else np.asarray(carry, dtype=np.float64)
+    N, T = a.shape
+    step = 1 if reverse else -1
+    out = np.zeros((N, T))
+    for n in range(N):
+        for t in range(T):
+            total, w, k = 0.0, 1.0, t
+            while True:
+                total += w * a[n, k]
+                if rs[n, k]:
+                    break
+                w *= b[n, k]
+                k += step
+                if k < 0 or k >= T:
+                    total += w * c[n]
+                    break
+            out[n, t] = total
+    return out

@@ -67,6 +67,20 @@ MUTANTS = [
      "if (t == 0 || done[i]) s = 0;"),
     ("prefix i32 exclusive", "s += (int64_t)x[i];\n            out[i] = (int32_t)(uint32_t)(uint64_t)s;",
      "out[i] = (int32_t)(uint32_t)(uint64_t)s;\n            s += (int64_t)x[i];"),
+    # generic affine scan
+    ("affine: reset ignored", "if (!(reset && reset[i])) next += (double)beta[i] * y;",
+     "next += (double)beta[i] * y;"),
+    ("affine: carry dropped", "double y = carry ? (double)carry[n] : 0.0;", "double y = 0.0;"),
+    ("affine: carry of the wrong row", "double y = carry ? (double)carry[n] : 0.0;",
+     "double y = carry ? (double)carry[0] : 0.0;"),
+    ("affine: direction flipped", "int64_t t = reverse ? T - 1 - k : k;",
+     "int64_t t = reverse ? k : T - 1 - k;"),
+    ("affine: alpha and beta transposed",
+     "double next = (double)alpha[i];\n            if (!(reset && reset[i])) next += (double)beta[i] * y;",
+     "double next = (double)beta[i];\n            if (!(reset && reset[i])) next += (double)alpha[i] * y;"),
+    ("affine: reset also drops alpha",
+     "if (!(reset && reset[i])) next += (double)beta[i] * y;",
+     "if (!(reset && reset[i])) next += (double)beta[i] * y; else next = y;"),
 ]
 
 
@@ -116,6 +130,11 @@ def battery_passes() -> bool:
                                c_bar=0.9, pg_rho_bar=1.3, **k)
         vs_b, pg_b = bf.vtrace(c["lr"], c["r"], c["V"], c["term"], g, lam, 1.1, 0.9, 1.3, **t)
         pairs += [(vs, vs_b), (pg, pg_b)]
+        beta = (0.6 * c["V"]).astype(np.float32)
+        for reverse in (False, True):
+            pairs.append((oracle.affine_scan(c["x"], beta, reset=c["term"], carry_in=c["boot"],
+                                             reverse=reverse),
+                          bf.affine(c["x"], beta, c["term"], c["boot"], reverse)))
         for got, want in pairs:
             if not np.allclose(got, want, rtol=1e-10, atol=1e-10):
                 return False

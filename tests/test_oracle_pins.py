@@ -468,3 +468,111 @@ def test_tree_scan_reproduces_recursion(seed):
             s = [combine(s[t], s[t + d]) if t + d < 97 else s[t] for t in range(97)]
             d *= 2
         close([v[0] for v in s], A[n], 1e-12)
+
+
+# ------------------------------------------------ generic segmented affine scan
+def affine_case(seed, N, T, p_reset):
+    rng = np.random.default_rng(seed)
+    return dict(alpha=rng.standard_normal((N, T)).astype(np.float32),
+                beta=rng.uniform(-1.2, 1.2, (N, T)).astype(np.float32),
+                reset=(rng.random((N, T)) < p_reset).astype(np.uint8),
+                carry=rng.standard_normal(N).astype(np.float32))
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+@pytest.mark.parametrize("seed,N,T,pr", [(40, 3, 17, 0.15), (41, 2, 1, 0.5), (42, 4, 9, 0.0),
+                                         (43, 2, 23, 0.4)])
+def test_affine_bruteforce(seed, N, T, pr, reverse):
+    c = affine_case(seed, N, T, pr)
+    for reset in (c["reset"], None):
+        for carry in (c["carry"], None):
+            got = oracle.affine_scan(c["alpha"], c["beta"], reset=reset, carry_in=carry,
+                                     reverse=reverse)
+            want = bf.affine(c["alpha"], c["beta"], reset, carry, reverse)
+            close(got, want, 1e-12)
+
+
+def test_affine_hand_worked():
+    # one row, T = 4, beta = 0.5 everywhere, reset at t = 2, carry 8:
+    # forward  y0 = 1 + 0.5*8 = 5, y1 = 2 + 2.5 = 4.5, y2 = 3 (reset), y3 = 4 + 1.5 = 5.5
+    # reverse  y3 = 4 + 4 = 8, y2 = 3 (reset), y1 = 2 + 1.5 = 3.5, y0 = 1 + 1.75 = 2.75
+    a = np.array([[1, 2, 3, 4]], np.float32)
+    b = np.full((1, 4), 0.5, np.float32)
+    r = np.array([[0, 0, 1, 0]], np.uint8)
+    cin = np.array([8.0], np.float32)
+    assert oracle.affine_scan(a, b, reset=r, carry_in=cin).tolist() == [[5.0, 4.5, 3.0, 5.5]]
+    assert oracle.affine_scan(a, b, reset=r, carry_in=cin, reverse=True).tolist() == \
+        [[2.75, 3.5, 3.0, 8.0]]
+
+
+@pytest.mark.parametrize("seed", [44, 45])
+def test_affine_mirror_exact(seed):
+    """Reversing every row turns a reverse scan into a forward one, bit for bit."""
+    c = affine_case(seed, 5, 31, 0.1)
+    back = oracle.affine_scan(c["alpha"], c["beta"], reset=c["reset"], carry_in=c["carry"],
+                              reverse=True)
+    fwd = oracle.affine_scan(c["alpha"][:, ::-1], c["beta"][:, ::-1], reset=c["reset"][:, ::-1],
+                             carry_in=c["carry"])
+    assert np.array_equal(back, fwd[:, ::-1])
+
+
+def test_affine_geometric_closed_form():
+    """Constant alpha = a, beta = b, no resets, carry c (reverse):
+    y_t = a (1 - b^L) / (1 - b) + b^L c with L = T - t."""
+    T, a, b, cin = 40, 0.75, 0.875, -2.5
+    y = oracle.affine_scan(np.full((1, T), a, np.float32), np.full((1, T), b, np.float32),
+                           carry_in=np.array([cin], np.float32), reverse=True)[0]
+    L = T - np.arange(T)
+    close(y, a * (1 - b ** L) / (1 - b) + b ** L * cin, 1e-13)
+
+
+@pytest.mark.parametrize("seed", [46, 47])
+def test_affine_lfilter(seed):
+    """Forward, constant beta, no resets: a first-order IIR filter whose
+    initial state is beta * carry."""
+    rng = np.random.default_rng(seed)
+    N, T, b = 3, 50, 0.93
+    a = rng.standard_normal((N, T)).astype(np.float32)
+    cin = rng.standard_normal(N).astype(np.float32)
+    y = oracle.affine_scan(a, np.full((N, T), b, np.float32), carry_in=cin)
+    bb = float(np.float32(b))
+    for n in range(N):
+        want, _ = lfilter([1.0], [1.0, -bb], a[n].astype(np.float64),
+                                       zi=[bb * float(cin[n])])
+        close(y[n], want, 1e-12)
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_affine_integer_segmented_cumsum(reverse):
+    """beta = 1 with resets is a segmented cumulative sum (numpy.cumsum per
+    segment), exact on integers."""
+    rng = np.random.default_rng(48)
+    N, T = 3, 60
+    a = rng.integers(-9, 10, (N, T)).astype(np.float32)
+    r = (rng.random((N, T)) < 0.1).astype(np.uint8)
+    y = oracle.affine_scan(a, np.ones((N, T), np.float32), reset=r, reverse=reverse)
+    for n in range(N):
+        row, rr = (a[n, ::-1], r[n, ::-1]) if reverse else (a[n], r[n])
+        want = np.empty(T)
+        starts = [0] + [t for t in range(1, T) if rr[t]]
+        for s, e in zip(starts, starts[1:] + [T]):
+            want[s:e] = np.cumsum(row[s:e])
+        assert np.array_equal(y[n], want[::-1] if reverse else want)
+
+
+def test_affine_reduces_to_gae():
+    """GAE is the reverse affine scan with alpha = delta and beta = gamma*lambda
+    cut at episode ends (Methodology 1).  Dyadic inputs keep both sides exact."""
+    rng = np.random.default_rng(49)
+    N, T, g, lam = 3, 40, 0.5, 0.75
+    r = rng.integers(-8, 9, (N, T)).astype(np.float32)
+    v = rng.integers(-8, 9, (N, T)).astype(np.float32)
+    term = (rng.random((N, T)) < 0.1).astype(np.uint8)
+    boot = rng.integers(-8, 9, N).astype(np.float32)
+    vn = np.concatenate([v[:, 1:], boot[:, None]], axis=1).astype(np.float64)
+    vn[term != 0] = 0.0
+    delta = r + g * vn - v
+    beta = np.where(term != 0, 0.0, g * lam)
+    beta[:, -1] = 0.0
+    got = oracle.affine_scan(delta.astype(np.float32), beta.astype(np.float32), reverse=True)
+    assert np.array_equal(got, oracle.gae(r, v, term, g, lam, bootstrap_value=boot))
