@@ -51,6 +51,7 @@ WORKLOADS = {
                      for e in ("discounted_returns", "lambda_returns", "eligibility_traces")],
     "prefix_16384x1024": [("prefix_sum_i32", False, 16384, 1024),
                           ("prefix_sum_f32", False, 16384, 1024)],
+    "affine_4096x8192": [("affine_fwd", False, 4096, 8192), ("affine_rev", False, 4096, 8192)],
 }
 DEFAULT_WORKLOAD = "all7_4096x128"
 # input streams each estimator reads
@@ -63,11 +64,13 @@ NEEDS = {
     "eligibility_traces": ("x", "dones"),
     "prefix_sum_f32": ("x", "dones"),
     "prefix_sum_i32": ("x_int", "dones"),
+    "affine_fwd": ("alpha", "beta", "reset", "carry_in"),
+    "affine_rev": ("alpha", "beta", "reset", "carry_in"),
 }
 # bytes per element: one read of each dense input, one write of each output
 DENSE_BYTES = {"gae": 13, "vtrace": 21, "retrace": 21, "lambda_returns": 13,
                "discounted_returns": 9, "eligibility_traces": 9, "prefix_sum_f32": 9,
-               "prefix_sum_i32": 9}
+               "prefix_sum_i32": 9, "affine_fwd": 13, "affine_rev": 13}
 
 
 def key(est, trunc, n=None, t=None):
@@ -78,11 +81,12 @@ def key(est, trunc, n=None, t=None):
 def alg_bytes(est, trunc, n, t):
     """One read of each input stream and one write of each output:
     DENSE_BYTES per element, plus 5 B per element with truncations (the
-    uint8 mask and the fp32 trunc_values), plus 4 B of bootstrap per env."""
+    uint8 mask and the fp32 trunc_values), plus 4 B of bootstrap (or carry)
+    per env."""
     b = DENSE_BYTES[est] * n * t
     if trunc:
         b += 5 * n * t
-    if est in BACKWARD:
+    if est in BACKWARD or est.startswith("affine"):
         b += 4 * n
     return b
 
@@ -114,6 +118,10 @@ def make_call(lrs, est, trunc, D, O, g, lam):
         return lambda: lrs.compute_episodic_prefix_sum(D["x"], D["dones"], out=O[k])
     if est == "prefix_sum_i32":
         return lambda: lrs.compute_episodic_prefix_sum(D["x_int"], D["dones"], out=O[k])
+    if est in ("affine_fwd", "affine_rev"):
+        return lambda: lrs.compute_affine_scan(D["alpha"], D["beta"], reset=D.get("reset"),
+                                               carry_in=D.get("carry_in"),
+                                               reverse=est == "affine_rev", out=O[k])
     raise KeyError(est)
 
 
@@ -142,6 +150,9 @@ def oracle_call(oracle, est, trunc, ro):
         return lambda: oracle.prefix_sum(a["x"], a["dones"])
     if est == "prefix_sum_i32":
         return lambda: oracle.prefix_sum(a["x_int"], a["dones"])
+    if est in ("affine_fwd", "affine_rev"):
+        return lambda: oracle.affine_scan(a["alpha"], a["beta"], reset=a.get("reset"),
+                                          carry_in=a.get("carry_in"), reverse=est == "affine_rev")
     raise KeyError(est)
 
 
@@ -194,13 +205,16 @@ def call_of_kernel(name):
     for op, est in ops.items():
         if f"lrs::{op}<" in name:
             return key(est, ", true>" in name.split(op, 1)[1][:12])
+    if "lrs::AffineOp<" in name:
+        rev = name.split("AffineOp<", 1)[1].split(",")[1].strip()
+        return "affine_rev" if rev == "true" else "affine_fwd"
     return None
 
 
-def summarize_stats(csv_path, command):
+def summarize_stats(csv_path, command, title="seven estimators at 4096 x 128"):
     import csv
     rows = list(csv.DictReader(open(csv_path)))
-    out = ["# rocprofv3 kernel statistics: seven estimators at 4096 x 128", "",
+    out = [f"# rocprofv3 kernel statistics: {title}", "",
            "Command:", "", "```", command, "```", "",
            "| kernel | call | dispatches | avg us | min us | max us |", "|---|---|---|---|---|---|"]
     for r in rows:
@@ -303,7 +317,7 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run 5 device copies of a 64 MiB tensor: a kernel of known "
                          "HBM traffic for scaling FETCH_SIZE / WRITE_SIZE counters")
-    ap.add_argument("--summarize-stats", nargs=2, metavar=("CSV", "COMMAND"),
+    ap.add_argument("--summarize-stats", nargs="+", metavar="CSV COMMAND [TITLE]",
                     help="print a markdown summary of a rocprofv3 kernel_stats.csv")
     ap.add_argument("--summarize-counters", nargs=4,
                     metavar=("FETCH_CSV", "WRITE_CSV", "FETCH_COMMAND", "WRITE_COMMAND"),
@@ -336,6 +350,11 @@ def main():
     shapes = sorted({(n, t) for _, _, n, t in calls})
     batches = {}
     for n, t in shapes:
+        if name.startswith("affine"):
+            arrs = workloads.affine_inputs(n, t, seed=0, reset_p=p["reset_p"],
+                                           beta_range=p["beta_range"])
+            batches[(n, t)] = workloads.Rollout(n, t, 1.0, 1.0, arrs)
+            continue
         streams = {s_ for e, tr, n_, t_ in calls if (n_, t_) == (n, t) for s_ in NEEDS[e]}
         if any(tr for e, tr, n_, t_ in calls if (n_, t_) == (n, t)):
             streams.add("truncateds")
@@ -345,7 +364,8 @@ def main():
     ro0 = batches[shapes[0]]
     g, lam = ro0.gamma, ro0.lambda_
 
-    hosts = {s_: {k: torch.from_numpy(v) for k, v in b.arrays.items()} for s_, b in batches.items()}
+    hosts = {s_: {k: torch.from_numpy(v) for k, v in b.arrays.items() if v is not None}
+             for s_, b in batches.items()}
 
     # Replicas per shape: enough copies of that shape's inputs and outputs
     # for >= 1 GiB, so that each call reads cold data however small it is.

@@ -9,7 +9,8 @@
  * operator (a_B, b_B) (+) (a_A, b_A) = (a_B + b_B a_A, b_A b_B); each call
  * builds its alpha/beta on chip from the raw inputs and makes one pass over
  * HBM (rl-triton paper, gist.science technical summary, Methodology 1 and 2;
- * rl-triton README, Kernels table).
+ * rl-triton README, Kernels table).  lrs_affine_scan_f32 exposes the bare
+ * recurrence over caller-supplied alpha/beta.
  *
  * Episode boundaries (same summary, Methodology 3).  Per element (n, t):
  *   end_t   = terminated_t || truncated_t || t == seq_len-1
@@ -76,7 +77,8 @@ typedef enum lrs_estimator {
     LRS_DISCOUNTED_RETURNS = 4,
     LRS_ELIGIBILITY_TRACES = 5,
     LRS_PREFIX_SUM_I32 = 6,
-    LRS_PREFIX_SUM_F32 = 7
+    LRS_PREFIX_SUM_F32 = 7,
+    LRS_AFFINE_SCAN = 8
 } lrs_estimator;
 
 /* Library version, encoded as major*10000 + minor*100 + patch. */
@@ -88,7 +90,8 @@ const char* lrs_status_string(lrs_status s);
 /* Message of the last failed call on the calling thread ("" if none). */
 const char* lrs_last_error(void);
 
-/* Bytes of workspace a call of `est` at [num_envs, seq_len] may need:
+/* Bytes of workspace a call of `est` (an estimator, or LRS_AFFINE_SCAN) at
+ * [num_envs, seq_len] may need:
  * 4224 bytes plus 32 bytes per 256 elements (about 3% of one fp32 array).  The
  * same workspace serves every estimator at this or any smaller size.
  * Returns 0 for invalid sizes. */
@@ -202,6 +205,31 @@ lrs_status lrs_episodic_prefix_sum_f32(int64_t num_envs, int64_t seq_len,
                                        float* sums,
                                        void* workspace, size_t workspace_bytes,
                                        hipStream_t stream);
+
+/* Generic segmented affine scan over caller-supplied coefficients: the one
+ * recurrence every estimator above reduces to (gist.science technical
+ * summary, Methodology 1; its Significance and Claims section names other
+ * segmented affine recurrences as users), here with alpha and beta read from
+ * memory instead of built on chip.  Per row n, in scan order:
+ *   reverse = 0:  y_t = alpha_t + beta_t * y_{t-1}   (t = 0 .. T-1)
+ *   reverse = 1:  y_t = alpha_t + beta_t * y_{t+1}   (t = T-1 .. 0)
+ * The y before the row's first step in scan order is carry_in[n] (0 if
+ * carry_in is NULL).  Where reset[t] is nonzero (reset may be NULL),
+ * y_t = alpha_t: the beta_t * y_prev term is dropped, exactly as if
+ * beta_t were 0, so nothing from before the reset reaches y_t or later.
+ * Streaming a long row in windows: scan the window nearest the scan's end
+ * first, then pass its outputs at the shared edge (column 0 for reverse,
+ * column T-1 forward, made contiguous) as carry_in of the next window.
+ * In:  alpha, beta [N,T] f32 (any finite values; |beta| > 1 may overflow);
+ *      reset [N,T] u8 (nullable); carry_in [N] f32 (nullable).
+ * Out: y [N,T] f32.  reverse must be 0 or 1 (else LRS_ERR_INVALID_ARG).   */
+lrs_status lrs_affine_scan_f32(int64_t num_envs, int64_t seq_len,
+                               const float* alpha, const float* beta,
+                               const uint8_t* reset, const float* carry_in,
+                               int reverse,
+                               float* y,
+                               void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
 
 /* Diagnostics and tuning (process-wide; not for concurrent use).
  * force_lookback != 0: every later call takes the multi-block carry-

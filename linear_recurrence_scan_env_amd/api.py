@@ -1,4 +1,5 @@
-"""Python binding of liblrs.so: the seven estimators on torch tensors.
+"""Python binding of liblrs.so: the seven estimators and the generic
+segmented affine scan on torch tensors.
 
 Argument marshalling only: every step of every estimator runs in the gfx950
 kernels behind the C ABI (include/lrs.h).  torch supplies device memory and
@@ -34,11 +35,12 @@ _SIGS = {
     "lrs_eligibility_traces_f32": [_I64, _I64, _P, _P, _F, _F, _P, _P, _SZ, _P],
     "lrs_episodic_prefix_sum_i32": [_I64, _I64, _P, _P, _P, _P, _SZ, _P],
     "lrs_episodic_prefix_sum_f32": [_I64, _I64, _P, _P, _P, _P, _SZ, _P],
+    "lrs_affine_scan_f32": [_I64, _I64, _P, _P, _P, _P, ctypes.c_int, _P, _P, _SZ, _P],
 }
 
 ESTIMATOR_ID = {"gae": 0, "vtrace": 1, "retrace": 2, "lambda_returns": 3,
                 "discounted_returns": 4, "eligibility_traces": 5, "prefix_sum_i32": 6,
-                "prefix_sum_f32": 7}
+                "prefix_sum_f32": 7, "affine_scan": 8}
 
 _lib = None
 _lock = threading.Lock()
@@ -319,6 +321,25 @@ def compute_episodic_prefix_sum(x, dones, *, out=None):
     ws, wsb, st = _launch_ctx(dev, est, n, t)
     _check(fn(n, t, _ptr(xs), _ptr(d), _ptr(s), _ptr(ws), wsb, st), "compute_episodic_prefix_sum")
     return s
+
+
+def compute_affine_scan(alpha, beta, *, reset=None, carry_in=None, reverse=False, out=None):
+    """Segmented first-order linear recurrence over given coefficients, per row:
+    y_t = alpha_t + beta_t * y_{t-1} (forward) or y_t = alpha_t + beta_t * y_{t+1}
+    (reverse=True).  carry_in [num_envs] is the y before each row's first step
+    in scan order (0 if None); where reset is set, y_t = alpha_t."""
+    n, t = _rows(alpha, "alpha")
+    dev = alpha.device
+    a = _dev_tensor(alpha, "alpha", torch.float32, (n, t), None)
+    b = _dev_tensor(beta, "beta", torch.float32, (n, t), dev)
+    rs = _mask(reset, "reset", (n, t), dev)
+    c = None if carry_in is None else _dev_tensor(carry_in, "carry_in", torch.float32, (n,), dev)
+    y = _out(out, a, "out")
+    ws, wsb, st = _launch_ctx(dev, "affine_scan", n, t)
+    _check(load().lrs_affine_scan_f32(n, t, _ptr(a), _ptr(b), _ptr(rs), _ptr(c),
+                                      1 if reverse else 0, _ptr(y), _ptr(ws), wsb, st),
+           "compute_affine_scan")
+    return y
 
 
 def _inf(x):

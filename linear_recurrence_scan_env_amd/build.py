@@ -14,10 +14,15 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "lrs.hip")
-DEPS = [SRC, os.path.join(PKG, "csrc", "scan_core.hpp"), os.path.join(PKG, "csrc", "estimators.hpp"),
-        os.path.join(ROOT, "include", "lrs.h")]
+CSRC = os.path.join(PKG, "csrc")
+# One translation unit per group of entry points, compiled in parallel.
+SOURCES = [os.path.join(CSRC, f) for f in
+           ("abi.hip", "returns.hip", "offpolicy.hip", "forward.hip", "affine.hip")]
+HEADERS = [os.path.join(CSRC, f) for f in ("launch.hpp", "scan_core.hpp", "estimators.hpp")] + \
+    [os.path.join(ROOT, "include", "lrs.h")]
+DEPS = SOURCES + HEADERS
 LIB = os.path.join(PKG, "liblrs.so")
+OBJ_DIR = os.path.join(PKG, "_build")
 ARCH = "gfx950"
 
 
@@ -29,7 +34,7 @@ def hipcc() -> str:
 
 
 def flags(resource_usage: bool = False):
-    f = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-command-line-argument",
          "-I", os.path.join(ROOT, "include")]
@@ -39,15 +44,31 @@ def flags(resource_usage: bool = False):
 
 
 def build(resource_usage: bool = False, quiet: bool = True) -> str:
-    """Always recompiles; writes liblrs.so atomically."""
+    """Always recompiles every source (in parallel), links liblrs.so atomically."""
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    cc = hipcc()
+    procs = []
+    for src in SOURCES:
+        obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
+        cmd = [cc] + flags(resource_usage) + ["-c", src, "-o", obj]
+        procs.append((src, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                                 stderr=subprocess.PIPE, text=True)))
+    failed = []
+    for src, obj, p in procs:
+        out, err = p.communicate()
+        if p.returncode != 0:
+            failed.append(src)
+            sys.stderr.write(out + err)
+        elif not quiet or resource_usage:
+            sys.stderr.write(err)
+    if failed:
+        raise RuntimeError(f"hipcc failed on {', '.join(map(os.path.basename, failed))}")
     tmp = LIB + ".tmp"
-    cmd = [hipcc()] + flags(resource_usage) + [SRC, "-o", tmp]
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC"] + [o for _, o, _ in procs] + ["-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed ({res.returncode}) building {LIB}")
-    if not quiet or resource_usage:
-        sys.stderr.write(res.stderr)
+        raise RuntimeError(f"hipcc failed ({res.returncode}) linking {LIB}")
     os.replace(tmp, LIB)
     return LIB
 

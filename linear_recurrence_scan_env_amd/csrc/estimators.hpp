@@ -161,6 +161,7 @@ struct GaeOp {
     using T = float;
     using Args = GaeArgs;
     static constexpr bool kBackward = true;
+    static constexpr bool kWideTiles = true;
     struct State {
         uint32_t end;
     };
@@ -214,6 +215,7 @@ struct LambdaOp {
     using T = float;
     using Args = LambdaArgs;
     static constexpr bool kBackward = true;
+    static constexpr bool kWideTiles = true;
     struct State {
         uint32_t end;
     };
@@ -264,6 +266,7 @@ struct DiscOp {
     using T = float;
     using Args = DiscArgs;
     static constexpr bool kBackward = true;
+    static constexpr bool kWideTiles = true;
     struct State {
         uint32_t end;
     };
@@ -316,6 +319,9 @@ struct VtraceOp {
     using T = float;
     using Args = VtraceArgs;
     static constexpr bool kBackward = true;
+    // Whole rows of 4096 or 8192 in one block (E = 8 or 16 waves) cost
+    // this op occupancy: its per-element state needs more registers.
+    static constexpr bool kWideTiles = false;
     struct State {
         uint32_t end;
         float r[E], v[E], tgt[E], rho_pg[E];  // tgt: Vnext at ends, V_{t+1} elsewhere
@@ -389,6 +395,9 @@ struct RetraceOp {
     using T = float;
     using Args = RetraceArgs;
     static constexpr bool kBackward = true;
+    // Whole rows of 4096 or 8192 in one block (E = 8 or 16 waves) cost
+    // this op occupancy: its per-element state needs more registers.
+    static constexpr bool kWideTiles = false;
     struct State {
         uint32_t end;
     };
@@ -478,6 +487,7 @@ struct EligOp {
     using T = float;
     using Args = ForwardArgs;
     static constexpr bool kBackward = false;
+    static constexpr bool kWideTiles = true;
     struct State {
         uint32_t reset;
     };
@@ -514,6 +524,7 @@ struct PrefixF32Op {
     using T = float;
     using Args = ForwardArgs;
     static constexpr bool kBackward = false;
+    static constexpr bool kWideTiles = true;
     struct State {
         uint32_t reset;
     };
@@ -550,6 +561,7 @@ struct PrefixI32Op {
     using T = uint32_t;
     using Args = ForwardArgs;
     static constexpr bool kBackward = false;
+    static constexpr bool kWideTiles = true;
     struct State {
         uint32_t reset;
     };
@@ -578,6 +590,93 @@ struct PrefixI32Op {
         }
         (void)beta;
         store_u32<E>((int32_t*)a.out, out, P, c.vec);
+    }
+};
+
+// ---------------------------------------------- generic segmented affine scan
+// Summary page, Methodology 1 (Unified Algebraic Framework): every estimator
+// above is the recurrence y_t = alpha_t + beta_t * y_prev over per-step pairs;
+// here the pairs come from memory.  y_prev is y_{t+1} when kRev (scan from
+// the row end), else y_{t-1}.  Before the row's first step in scan order it
+// is carry[n] (0 without carries).  A set reset[t] drops beta_t * y_prev.
+struct AffineArgs {
+    const float* alpha;
+    const float* beta;
+    const uint8_t* reset;  // used iff the kernel is the resetting variant
+    const float* carry;    // never null: without carries the host passes
+    int has_carry;         // alpha and has_carry = 0
+    float* out;
+};
+
+template <int E, bool kRev, bool kReset>
+struct AffineOp {
+    using T = float;
+    using Args = AffineArgs;
+    static constexpr bool kBackward = kRev;
+    static constexpr bool kWideTiles = true;
+    struct State {
+        uint32_t cut;
+    };
+
+    template <bool F>
+    __device__ static void prepare(const Args& a, const Pos<E, F>& P, const Ctx& c,
+                                   float (&alpha)[E], float (&beta)[E], State& s)
+    {
+        load_f32<E>(alpha, a.alpha, P, c.vec);
+        load_f32<E>(beta, a.beta, P, c.vec);
+        uint32_t reset = 0u;
+        if constexpr (kReset) reset = load_mask<E>(a.reset, P, c.vec);
+        // Steps whose predecessor in scan order lies outside the row.
+        const uint32_t edge = kRev ? P.last : P.first;
+        float cv[E];
+        if constexpr (F) {
+            // seq_len >= E: at most one such step per lane.  Reverse, it ends
+            // the lane's first row.  Forward, it starts the lane's first row
+            // if it is the lane's first element, else the next row.
+            const bool next_row = !kRev && edge != 0u && !(edge & 1u);
+            const float c0 = a.carry[a.has_carry ? P.n0 + (next_row ? 1 : 0) : 0];
+#pragma unroll
+            for (int j = 0; j < E; ++j) cv[j] = a.has_carry ? c0 : 0.0f;
+        } else {
+            uint64_t n = P.n0;
+#pragma unroll
+            for (int j = 0; j < E; ++j) {
+                const bool e = (edge >> j) & 1u;
+                if (!kRev && e && j > 0) ++n;
+                cv[j] = (e && a.has_carry) ? a.carry[n] : 0.0f;
+                if (kRev && e) ++n;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            const bool r = (reset >> j) & 1u, e = (edge >> j) & 1u;
+            if (e && !r) alpha[j] = fmaf(beta[j], cv[j], alpha[j]);
+            if (r || e) beta[j] = 0.0f;
+        }
+        clear_tail(alpha, beta, P);
+        s.cut = reset | edge;
+    }
+    __device__ static bool far_open(const State& s)
+    {
+        return kRev ? !((s.cut >> (E - 1)) & 1u) : !(s.cut & 1u);
+    }
+    template <bool F>
+    __device__ static void finish(const Args& a, const Pos<E, F>& P, const Ctx& c,
+                                  const float (&alpha)[E], const float (&beta)[E], const State&,
+                                  float carry)
+    {
+        float out[E];
+        if constexpr (kRev) {
+            backward_pass<E>(out, alpha, beta, carry);
+        } else {
+            float y = carry;
+#pragma unroll
+            for (int j = 0; j < E; ++j) {
+                y = fmaf(beta[j], y, alpha[j]);
+                out[j] = y;
+            }
+        }
+        store_f32<E>(a.out, out, P, c.vec);
     }
 };
 

@@ -1,6 +1,7 @@
-// lrs.hip -- gfx950 kernels and the C ABI declared in include/lrs.h.
+// launch.hpp -- the scan kernel template and its host-side launch logic,
+// shared by the translation units that define the C ABI of include/lrs.h.
 //
-// One kernel template serves all seven estimators.  The [N, T] input is one
+// One kernel template serves all seven estimators and the generic scan.  The [N, T] input is one
 // flat stream of N*T elements; row ends are segment boundaries like episode
 // ends, so rows never need separate handling.  A block owns a tile of
 // E*64*W consecutive elements; each lane owns E of them:
@@ -15,6 +16,7 @@
 // look-back path) is written to HBM: one read of each input, one write of
 // each output, as the rl-triton paper's fused kernels do (gist.science
 // technical summary, Methodology 2).
+#pragma once
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -279,16 +281,6 @@ __global__ __launch_bounds__(W * kWave) void scan_kernel(const typename Op::Args
 
 // ------------------------------------------------------------ host side
 
-template <int E> using GaeT = GaeOp<E, true>;
-template <int E> using GaeN = GaeOp<E, false>;
-template <int E> using LambdaT = LambdaOp<E, true>;
-template <int E> using LambdaN = LambdaOp<E, false>;
-template <int E> using DiscT = DiscOp<E, true>;
-template <int E> using DiscN = DiscOp<E, false>;
-template <int E> using VtraceT = VtraceOp<E, true>;
-template <int E> using VtraceN = VtraceOp<E, false>;
-template <int E> using RetraceT = RetraceOp<E, true>;
-template <int E> using RetraceN = RetraceOp<E, false>;
 
 struct Cfg {
     int E, W;
@@ -297,16 +289,18 @@ struct Cfg {
 constexpr int kNumCfg = 7;  // ordered by tile size
 constexpr Cfg kCfgs[kNumCfg] = {{4, 1}, {4, 4}, {8, 4}, {4, 8}, {16, 4}, {4, 16}, {8, 16}};
 constexpr uint32_t kMinTile = 256;  // smallest tile the look-back path may use
-constexpr int kAlignedCfgs[3] = {0, 1, 3};  // 4x1, 4x4, 4x8
-constexpr int kLookbackCfg = 3;             // 4x8: 2048-element tiles
+constexpr int kAlignedCfgs[5] = {0, 1, 3, 5, 6};  // 4x1, 4x4, 4x8, 4x16, 8x16
+constexpr uint32_t kNarrowMaxTile = 2048;  // ops without kWideTiles stop at 4x8
+constexpr uint64_t kWideMinTiles = 1024;   // whole-row tiles above 2048 need this many
+constexpr int kLookbackCfg = 3;            // 4x8: 2048-element tiles
 constexpr int64_t kPositionMajorRows = 1024;
 
-std::atomic<int> g_force_lookback{0};
-std::atomic<int> g_forced_cfg{-1};
+// Defined in abi.hip.
+extern std::atomic<int> g_force_lookback;
+extern std::atomic<int> g_forced_cfg;
+extern thread_local char g_err[512];
 
-thread_local char g_err[512];
-
-lrs_status fail(lrs_status st, const char* fmt, ...)
+inline lrs_status fail(lrs_status st, const char* fmt, ...)
 {
     va_list ap;
     va_start(ap, fmt);
@@ -315,24 +309,26 @@ lrs_status fail(lrs_status st, const char* fmt, ...)
     return st;
 }
 
-bool valid_sizes(int64_t N, int64_t T)
+inline bool valid_sizes(int64_t N, int64_t T)
 {
     if (N < 1 || T < 1 || T >= (int64_t(1) << 31)) return false;
     if (N > (int64_t(1) << 34) / T) return false;
     return N * T < (int64_t(1) << 34);
 }
 
-size_t workspace_bytes_for(uint64_t total)
+inline size_t workspace_bytes_for(uint64_t total)
 {
     return sizeof(WsHeader) + 8 * kRecordWords * ((total + kMinTile - 1) / kMinTile);
 }
 
-// Pick the tile.  Measured on MI355X: four elements per lane stream best,
-// and the look-back costs little once most tiles are settled by their
-// neighbour, so: the smallest of the 4-per-lane tiles (256, 1024, 2048
-// elements) that holds whole rows; otherwise the look-back path on
-// 2048-element tiles of eight waves.
-int choose_cfg(uint64_t total, uint64_t T, bool* lookback)
+// Pick the tile.  Measured on MI355X: four elements per lane stream best
+// for tiles up to 2048 elements, and a tile that holds whole rows needs no
+// look-back, so: the smallest tile that holds whole rows, among 256, 1024
+// and 2048 elements (4 per lane) and, for ops whose registers allow it and
+// when at least kWideMinTiles such tiles fill the chip, 4096 (4 per lane,
+// 16 waves) and 8192 (8 per lane, 16 waves); otherwise the look-back path
+// on 2048-element tiles of eight waves.
+inline int choose_cfg(uint64_t total, uint64_t T, bool wide_ok, bool* lookback)
 {
     const int forced = g_forced_cfg.load();
     const bool force_lb = g_force_lookback.load() != 0;
@@ -344,6 +340,7 @@ int choose_cfg(uint64_t total, uint64_t T, bool* lookback)
     }
     for (int c : kAlignedCfgs) {
         const uint64_t tiles = (total + kCfgs[c].tile() - 1) / kCfgs[c].tile();
+        if (kCfgs[c].tile() > kNarrowMaxTile && (!wide_ok || tiles < kWideMinTiles)) break;
         if (kCfgs[c].tile() % T == 0 || tiles == 1) {
             *lookback = false;
             return c;
@@ -353,7 +350,7 @@ int choose_cfg(uint64_t total, uint64_t T, bool* lookback)
     return kLookbackCfg;
 }
 
-bool aligned(const void* p, uintptr_t a) { return p == nullptr || ((uintptr_t)p % a) == 0; }
+inline bool aligned(const void* p, uintptr_t a) { return p == nullptr || ((uintptr_t)p % a) == 0; }
 
 template <class Op, int E, int W>
 hipError_t launch_cfg(const typename Op::Args& a, const Sched& s, hipStream_t stream)
@@ -386,7 +383,7 @@ lrs_status run(const char* name, int64_t N, int64_t T, const typename Op<4>::Arg
 {
     const uint64_t total = (uint64_t)N * (uint64_t)T;
     bool lookback = false;
-    const int cfg = choose_cfg(total, (uint64_t)T, &lookback);
+    const int cfg = choose_cfg(total, (uint64_t)T, Op<4>::kWideTiles, &lookback);
     const Cfg& k = kCfgs[cfg];
     Sched s{};
     s.total = total;
@@ -427,10 +424,10 @@ lrs_status run(const char* name, int64_t N, int64_t T, const typename Op<4>::Arg
     return LRS_OK;
 }
 
-bool unit_interval(float x) { return x >= 0.0f && x <= 1.0f; }  // false for NaN
-bool positive(float x) { return x > 0.0f; }                       // +inf allowed, NaN not
+inline bool unit_interval(float x) { return x >= 0.0f && x <= 1.0f; }  // false for NaN
+inline bool positive(float x) { return x > 0.0f; }                       // +inf allowed, NaN not
 
-lrs_status check_common(const char* name, int64_t N, int64_t T)
+inline lrs_status check_common(const char* name, int64_t N, int64_t T)
 {
     if (!valid_sizes(N, T))
         return fail(LRS_ERR_INVALID_ARG,
@@ -440,7 +437,7 @@ lrs_status check_common(const char* name, int64_t N, int64_t T)
     return LRS_OK;
 }
 
-lrs_status check_boundary(const char* name, const uint8_t* term, const uint8_t* trunc,
+inline lrs_status check_boundary(const char* name, const uint8_t* term, const uint8_t* trunc,
                           const float* tv)
 {
     if (term == nullptr) return fail(LRS_ERR_INVALID_ARG, "%s: terminateds is required", name);
@@ -461,177 +458,3 @@ lrs_status check_boundary(const char* name, const uint8_t* term, const uint8_t* 
     } while (0)
 
 }  // namespace lrs
-
-using namespace lrs;
-
-extern "C" {
-
-int lrs_version(void) { return 100; }
-
-const char* lrs_status_string(lrs_status s)
-{
-    switch (s) {
-        case LRS_OK: return "success";
-        case LRS_ERR_INVALID_ARG: return "invalid argument";
-        case LRS_ERR_WORKSPACE: return "workspace missing or too small";
-        case LRS_ERR_HIP: return "HIP runtime error";
-    }
-    return "unknown status";
-}
-
-const char* lrs_last_error(void) { return g_err; }
-
-size_t lrs_workspace_bytes(lrs_estimator est, int64_t num_envs, int64_t seq_len)
-{
-    if ((int)est < 0 || (int)est > (int)LRS_PREFIX_SUM_F32) return 0;
-    if (!valid_sizes(num_envs, seq_len)) return 0;
-    return workspace_bytes_for((uint64_t)num_envs * (uint64_t)seq_len);
-}
-
-lrs_status lrs_debug_set_schedule(int force_lookback, int elems_per_lane, int waves_per_block)
-{
-    int cfg = -1;
-    if (elems_per_lane != 0 || waves_per_block != 0) {
-        for (int i = 0; i < kNumCfg; ++i)
-            if (kCfgs[i].E == elems_per_lane && kCfgs[i].W == waves_per_block) cfg = i;
-        if (cfg < 0)
-            return fail(LRS_ERR_INVALID_ARG, "lrs_debug_set_schedule: unsupported tile %d x %d",
-                        elems_per_lane, waves_per_block);
-    }
-    g_force_lookback.store(force_lookback != 0);
-    g_forced_cfg.store(cfg);
-    return LRS_OK;
-}
-
-lrs_status lrs_gae_f32(int64_t N, int64_t T, const float* rewards, const float* values,
-                       const uint8_t* term, const uint8_t* trunc, const float* tv,
-                       const float* boot, float gamma, float lambda, float* adv, void* ws,
-                       size_t ws_bytes, hipStream_t stream)
-{
-    const char* nm = "lrs_gae_f32";
-    LRS_TRY(check_common(nm, N, T));
-    LRS_REQUIRE(rewards && values && adv, "%s: rewards, values and advantages are required", nm);
-    LRS_TRY(check_boundary(nm, term, trunc, tv));
-    LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda), "%s: gamma and lambda must be in [0, 1]", nm);
-    GaeArgs a{{term, trunc, tv, boot ? boot : rewards, boot != nullptr}, rewards, values, gamma,
-              (float)((double)gamma * (double)lambda), adv};
-    const void* f[] = {rewards, values, adv, tv};
-    const void* m[] = {term, trunc};
-    return trunc ? run<GaeT>(nm, N, T, a, f, 4, m, 2, ws, ws_bytes, stream) : run<GaeN>(nm, N, T, a, f, 4, m, 2, ws, ws_bytes, stream);
-}
-
-lrs_status lrs_vtrace_f32(int64_t N, int64_t T, const float* log_rhos, const float* rewards,
-                          const float* values, const uint8_t* term, const uint8_t* trunc,
-                          const float* tv, const float* boot, float gamma, float lambda,
-                          float rho_bar, float c_bar, float pg_rho_bar, float* vs,
-                          float* pg_adv, void* ws, size_t ws_bytes, hipStream_t stream)
-{
-    const char* nm = "lrs_vtrace_f32";
-    LRS_TRY(check_common(nm, N, T));
-    LRS_REQUIRE(log_rhos && rewards && values && vs && pg_adv,
-                "%s: log_rhos, rewards, values, vs and pg_advantages are required", nm);
-    LRS_TRY(check_boundary(nm, term, trunc, tv));
-    LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda), "%s: gamma and lambda must be in [0, 1]", nm);
-    LRS_REQUIRE(positive(rho_bar) && positive(c_bar) && positive(pg_rho_bar),
-                "%s: rho_bar, c_bar and pg_rho_bar must be > 0", nm);
-    VtraceArgs a{{term, trunc, tv, boot ? boot : rewards, boot != nullptr}, log_rhos, rewards, values, gamma, lambda,
-                 rho_bar, c_bar, pg_rho_bar, vs, pg_adv};
-    const void* f[] = {log_rhos, rewards, values, vs, pg_adv, tv};
-    const void* m[] = {term, trunc};
-    return trunc ? run<VtraceT>(nm, N, T, a, f, 6, m, 2, ws, ws_bytes, stream) : run<VtraceN>(nm, N, T, a, f, 6, m, 2, ws, ws_bytes, stream);
-}
-
-lrs_status lrs_retrace_f32(int64_t N, int64_t T, const float* log_rhos, const float* rewards,
-                           const float* q_values, const float* values, const uint8_t* term,
-                           const uint8_t* trunc, const float* tv, const float* boot, float gamma,
-                           float lambda, float c_bar, float* q_ret, void* ws, size_t ws_bytes,
-                           hipStream_t stream)
-{
-    const char* nm = "lrs_retrace_f32";
-    LRS_TRY(check_common(nm, N, T));
-    LRS_REQUIRE(log_rhos && rewards && q_values && values && q_ret,
-                "%s: log_rhos, rewards, q_values, values and q_ret are required", nm);
-    LRS_TRY(check_boundary(nm, term, trunc, tv));
-    LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda), "%s: gamma and lambda must be in [0, 1]", nm);
-    LRS_REQUIRE(positive(c_bar), "%s: c_bar must be > 0", nm);
-    RetraceArgs a{{term, trunc, tv, boot ? boot : rewards, boot != nullptr}, log_rhos, rewards, q_values, values,
-                  gamma, lambda, c_bar, q_ret};
-    const void* f[] = {log_rhos, rewards, q_values, values, q_ret, tv};
-    const void* m[] = {term, trunc};
-    return trunc ? run<RetraceT>(nm, N, T, a, f, 6, m, 2, ws, ws_bytes, stream) : run<RetraceN>(nm, N, T, a, f, 6, m, 2, ws, ws_bytes, stream);
-}
-
-lrs_status lrs_lambda_returns_f32(int64_t N, int64_t T, const float* rewards, const float* values,
-                                  const uint8_t* term, const uint8_t* trunc, const float* tv,
-                                  const float* boot, float gamma, float lambda, float* out,
-                                  void* ws, size_t ws_bytes, hipStream_t stream)
-{
-    const char* nm = "lrs_lambda_returns_f32";
-    LRS_TRY(check_common(nm, N, T));
-    LRS_REQUIRE(rewards && values && out, "%s: rewards, values and returns are required", nm);
-    LRS_TRY(check_boundary(nm, term, trunc, tv));
-    LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda), "%s: gamma and lambda must be in [0, 1]", nm);
-    LambdaArgs a{{term, trunc, tv, boot ? boot : rewards, boot != nullptr}, rewards, values, gamma,
-                 (float)((double)gamma * (double)lambda),
-                 (float)((double)gamma * (1.0 - (double)lambda)), out};
-    const void* f[] = {rewards, values, out, tv};
-    const void* m[] = {term, trunc};
-    return trunc ? run<LambdaT>(nm, N, T, a, f, 4, m, 2, ws, ws_bytes, stream) : run<LambdaN>(nm, N, T, a, f, 4, m, 2, ws, ws_bytes, stream);
-}
-
-lrs_status lrs_discounted_returns_f32(int64_t N, int64_t T, const float* rewards,
-                                      const uint8_t* term, const uint8_t* trunc, const float* tv,
-                                      const float* boot, float gamma, float* out, void* ws,
-                                      size_t ws_bytes, hipStream_t stream)
-{
-    const char* nm = "lrs_discounted_returns_f32";
-    LRS_TRY(check_common(nm, N, T));
-    LRS_REQUIRE(rewards && out, "%s: rewards and returns are required", nm);
-    LRS_TRY(check_boundary(nm, term, trunc, tv));
-    LRS_REQUIRE(unit_interval(gamma), "%s: gamma must be in [0, 1]", nm);
-    DiscArgs a{{term, trunc, tv, boot ? boot : rewards, boot != nullptr}, rewards, gamma, out};
-    const void* f[] = {rewards, out, tv};
-    const void* m[] = {term, trunc};
-    return trunc ? run<DiscT>(nm, N, T, a, f, 3, m, 2, ws, ws_bytes, stream) : run<DiscN>(nm, N, T, a, f, 3, m, 2, ws, ws_bytes, stream);
-}
-
-lrs_status lrs_eligibility_traces_f32(int64_t N, int64_t T, const float* x, const uint8_t* dones,
-                                      float gamma, float lambda, float* out, void* ws,
-                                      size_t ws_bytes, hipStream_t stream)
-{
-    const char* nm = "lrs_eligibility_traces_f32";
-    LRS_TRY(check_common(nm, N, T));
-    LRS_REQUIRE(x && dones && out, "%s: x, dones and traces are required", nm);
-    LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda), "%s: gamma and lambda must be in [0, 1]", nm);
-    ForwardArgs a{x, dones, (float)((double)gamma * (double)lambda), out};
-    const void* f[] = {x, out};
-    const void* m[] = {dones};
-    return run<EligOp>(nm, N, T, a, f, 2, m, 1, ws, ws_bytes, stream);
-}
-
-lrs_status lrs_episodic_prefix_sum_i32(int64_t N, int64_t T, const int32_t* x,
-                                       const uint8_t* dones, int32_t* out, void* ws,
-                                       size_t ws_bytes, hipStream_t stream)
-{
-    const char* nm = "lrs_episodic_prefix_sum_i32";
-    LRS_TRY(check_common(nm, N, T));
-    LRS_REQUIRE(x && dones && out, "%s: x, dones and sums are required", nm);
-    ForwardArgs a{x, dones, 1.0f, out};
-    const void* f[] = {x, out};
-    const void* m[] = {dones};
-    return run<PrefixI32Op>(nm, N, T, a, f, 2, m, 1, ws, ws_bytes, stream);
-}
-
-lrs_status lrs_episodic_prefix_sum_f32(int64_t N, int64_t T, const float* x, const uint8_t* dones,
-                                       float* out, void* ws, size_t ws_bytes, hipStream_t stream)
-{
-    const char* nm = "lrs_episodic_prefix_sum_f32";
-    LRS_TRY(check_common(nm, N, T));
-    LRS_REQUIRE(x && dones && out, "%s: x, dones and sums are required", nm);
-    ForwardArgs a{x, dones, 1.0f, out};
-    const void* f[] = {x, out};
-    const void* m[] = {dones};
-    return run<PrefixF32Op>(nm, N, T, a, f, 2, m, 1, ws, ws_bytes, stream);
-}
-
-}  // extern "C"

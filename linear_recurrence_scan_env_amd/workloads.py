@@ -22,6 +22,7 @@ STREAM_KEY = {
     "rewards": 1, "values": 2, "q_values": 3, "log_rhos": 4,
     "terminateds": 5, "truncateds": 6, "trunc_values": 7,
     "bootstrap_value": 8, "x": 9, "x_int": 10, "dones": 11,
+    "alpha": 12, "beta": 13, "reset": 14, "carry_in": 15,
 }
 
 
@@ -38,6 +39,11 @@ def normal(seed, name, shape, sigma=1.0):
 
 def bernoulli(seed, name, shape, p):
     return (_rng(seed, name).random(shape, dtype=np.float64) < p).astype(np.uint8)
+
+
+def uniform(seed, name, shape, lo, hi):
+    """Floats uniform on [lo, hi), float32."""
+    return _rng(seed, name).uniform(lo, hi, size=shape).astype(np.float32)
 
 
 def uniform_int(seed, name, shape, lo, hi):
@@ -90,7 +96,21 @@ def rollout(num_envs, seq_len, *, seed=0, term_p=0.01, trunc_p=0.0, logrho_sigma
     return Rollout(shape[0], shape[1], float(np.float32(gamma)), float(np.float32(lambda_)), a)
 
 
-# The five benchmark workloads, as (name, sizes, drawing parameters).
+def affine_inputs(num_envs, seq_len, *, seed=0, reset_p=0.02, beta_range=(0.9, 1.0),
+                  carry=True):
+    """Coefficients for the generic affine scan: alpha ~ N(0,1), beta ~
+    U[beta_range), reset ~ Bern(reset_p) (None when reset_p == 0), carry_in ~
+    N(0,1) per env (None unless carry)."""
+    shape = (int(num_envs), int(seq_len))
+    return {
+        "alpha": normal(seed, "alpha", shape),
+        "beta": uniform(seed, "beta", shape, *beta_range),
+        "reset": bernoulli(seed, "reset", shape, reset_p) if reset_p > 0 else None,
+        "carry_in": normal(seed, "carry_in", (shape[0],)) if carry else None,
+    }
+
+
+# The benchmark workloads, as (name, sizes, drawing parameters).
 WORKLOADS = {
     # GAE, 64 x 512, terminations Bern(0.01), no truncations.
     "gae_64x512": dict(num_envs=64, seq_len=512, term_p=0.01, trunc_p=0.0,
@@ -108,4 +128,7 @@ WORKLOADS = {
     # Episodic prefix sum, 16384 x 1024, done Bern(0.02), int32 in [-1000, 1000].
     "prefix_16384x1024": dict(num_envs=16384, seq_len=1024, term_p=0.02, trunc_p=0.0,
                               gamma=1.0, lambda_=1.0),
+    # Generic affine scan over stored coefficients, both directions, 4096 x
+    # 8192: beta ~ U[0.9, 1), resets Bern(0.02), a carry per env.
+    "affine_4096x8192": dict(num_envs=4096, seq_len=8192, reset_p=0.02, beta_range=(0.9, 1.0)),
 }

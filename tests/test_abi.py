@@ -41,7 +41,7 @@ def test_header_declares_every_estimator():
               "lrs_discounted_returns_f32", "lrs_eligibility_traces_f32",
               "lrs_episodic_prefix_sum_i32", "lrs_episodic_prefix_sum_f32",
               "lrs_workspace_bytes", "lrs_status_string", "lrs_last_error", "lrs_version",
-              "lrs_debug_set_schedule"]:
+              "lrs_debug_set_schedule", "lrs_affine_scan_f32"]:
         assert n in names
 
 
@@ -67,6 +67,8 @@ def test_workspace_bytes(lib):
     assert lib.lrs_workspace_bytes(0, 5, 0) == 0
     assert lib.lrs_workspace_bytes(0, 1 << 20, 1 << 20) == 0  # 2^40 elements: over the limit
     assert lib.lrs_workspace_bytes(42, 4, 4) == 0
+    assert lib.lrs_workspace_bytes(8, 4096, 128) == lib.lrs_workspace_bytes(0, 4096, 128)
+    assert lib.lrs_workspace_bytes(9, 4, 4) == 0
 
 
 FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation
@@ -112,6 +114,15 @@ def test_other_estimators_reject(lib):
     assert lib.lrs_episodic_prefix_sum_f32(4, 8, FAKE, FAKE, None, None, 0, None) == 1
 
 
+def test_affine_scan_rejects(lib):
+    def call(N=4, T=8, a=FAKE, b=FAKE, reverse=0, y=FAKE):
+        return lib.lrs_affine_scan_f32(N, T, a, b, None, None, reverse, y, None, 0, None)
+    for kw in [dict(N=0), dict(T=-1), dict(a=None), dict(b=None), dict(y=None), dict(reverse=2),
+               dict(reverse=-1)]:
+        assert call(**kw) == 1
+        assert lib.lrs_last_error().startswith(b"lrs_affine_scan_f32")
+
+
 def test_debug_schedule_validation(lib):
     assert lib.lrs_debug_set_schedule(0, 3, 4) == 1
     assert lib.lrs_debug_set_schedule(0, 8, 2) == 1
@@ -126,6 +137,8 @@ def test_python_api_has_no_cpu_path():
         lrs.compute_gae(x, x, x)
     with pytest.raises(ValueError, match="GPU"):
         lrs.compute_episodic_prefix_sum(x.int(), x)
+    with pytest.raises(ValueError, match="GPU"):
+        lrs.compute_affine_scan(x, x)
 
 
 def test_product_does_not_reference_the_oracle():
