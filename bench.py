@@ -52,7 +52,13 @@ WORKLOADS = {
     "prefix_16384x1024": [("prefix_sum_i32", False, 16384, 1024),
                           ("prefix_sum_f32", False, 16384, 1024)],
     "affine_4096x8192": [("affine_fwd", False, 4096, 8192), ("affine_rev", False, 4096, 8192)],
+    # the same calls with bfloat16 storage of every floating-point stream
+    "all7_4096x128_bf16": [(e, tr, 4096, 128) for e, tr in ALL7],
+    "long_64x131072_bf16": [(e, True, 64, 131072) for e in ("gae", "vtrace", "retrace")],
 }
+# storage type of the floating-point streams (fp32 unless listed); arithmetic is fp32 throughout
+STORAGE = {"all7_4096x128_bf16": "bf16", "long_64x131072_bf16": "bf16"}
+BASE_WORKLOAD = {"all7_4096x128_bf16": "all7_4096x128", "long_64x131072_bf16": "long_64x131072"}
 DEFAULT_WORKLOAD = "all7_4096x128"
 # input streams each estimator reads
 NEEDS = {
@@ -67,10 +73,12 @@ NEEDS = {
     "affine_fwd": ("alpha", "beta", "reset", "carry_in"),
     "affine_rev": ("alpha", "beta", "reset", "carry_in"),
 }
-# bytes per element: one read of each dense input, one write of each output
-DENSE_BYTES = {"gae": 13, "vtrace": 21, "retrace": 21, "lambda_returns": 13,
-               "discounted_returns": 9, "eligibility_traces": 9, "prefix_sum_f32": 9,
-               "prefix_sum_i32": 9, "affine_fwd": 13, "affine_rev": 13}
+# dense per-element streams of each call: (data streams read or written, uint8 masks read).
+# With 4-byte data: GAE and TD(lambda) 13 B/elem, V-trace and Retrace 21, the others 9,
+# the affine scan 13.
+STREAMS = {"gae": (3, 1), "vtrace": (5, 1), "retrace": (5, 1), "lambda_returns": (3, 1),
+           "discounted_returns": (2, 1), "eligibility_traces": (2, 1), "prefix_sum_f32": (2, 1),
+           "prefix_sum_i32": (2, 1), "affine_fwd": (3, 1), "affine_rev": (3, 1)}
 
 
 def key(est, trunc, n=None, t=None):
@@ -78,16 +86,17 @@ def key(est, trunc, n=None, t=None):
     return k if n is None else f"{k}@{n}x{t}"
 
 
-def alg_bytes(est, trunc, n, t):
-    """One read of each input stream and one write of each output:
-    DENSE_BYTES per element, plus 5 B per element with truncations (the
-    uint8 mask and the fp32 trunc_values), plus 4 B of bootstrap (or carry)
-    per env."""
-    b = DENSE_BYTES[est] * n * t
+def alg_bytes(est, trunc, n, t, width=4):
+    """One read of each input stream and one write of each output, with
+    `width`-byte data: STREAMS per element, plus one mask byte and one datum
+    (trunc_values) per element with truncations, plus one datum of bootstrap
+    (or carry) per env."""
+    data, masks = STREAMS[est]
+    b = (data * width + masks) * n * t
     if trunc:
-        b += 5 * n * t
+        b += (width + 1) * n * t
     if est in BACKWARD or est.startswith("affine"):
-        b += 4 * n
+        b += width * n
     return b
 
 
@@ -346,7 +355,10 @@ def main():
 
     name = args.workload
     calls = WORKLOADS[name]
-    p = workloads.WORKLOADS[name]
+    p = workloads.WORKLOADS[BASE_WORKLOAD.get(name, name)]
+    storage = STORAGE.get(name, "f32")
+    width = 2 if storage in ("bf16", "f16") else 4
+    store_dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[storage]
     shapes = sorted({(n, t) for _, _, n, t in calls})
     batches = {}
     for n, t in shapes:
@@ -366,12 +378,17 @@ def main():
 
     hosts = {s_: {k: torch.from_numpy(v) for k, v in b.arrays.items() if v is not None}
              for s_, b in batches.items()}
+    if storage != "f32":
+        for h in hosts.values():
+            for k, v in h.items():
+                if v.dtype == torch.float32:
+                    h[k] = v.to(store_dt)
 
     # Replicas per shape: enough copies of that shape's inputs and outputs
     # for >= 1 GiB, so that each call reads cold data however small it is.
     def shape_bytes(s_):
         b = sum(v.numel() * v.element_size() for v in hosts[s_].values())
-        return b + sum((2 if e == "vtrace" else 1) * n * t * 4 for e, _, n, t in calls
+        return b + sum((2 if e == "vtrace" else 1) * n * t * width for e, _, n, t in calls
                        if (n, t) == s_)
 
     if args.warm:
@@ -389,10 +406,10 @@ def main():
             for e, tr, n, t in calls:
                 if (n, t) != s_:
                     continue
-                dt = torch.int32 if e == "prefix_sum_i32" else torch.float32
+                dt = torch.int32 if e == "prefix_sum_i32" else store_dt
                 O[key(e, tr)] = torch.empty(n, t, device=dev, dtype=dt)
                 if e == "vtrace":
-                    O[key(e, tr) + "/pg"] = torch.empty(n, t, device=dev)
+                    O[key(e, tr) + "/pg"] = torch.empty(n, t, device=dev, dtype=dt)
             store[(s_, i)] = (D, O)
 
     def fn(e, tr, n, t, i):
@@ -461,7 +478,7 @@ def main():
             ev1.record(stream)
             torch.cuda.synchronize()
             us = ev0.elapsed_time(ev1) * 1e3 / (args.roofline_reps * launches[k_])
-            b = alg_bytes(e, tr, n, t)
+            b = alg_bytes(e, tr, n, t, width)
             per_call[k_ if len(shapes) > 1 else key(e, tr)] = {
                 "us": round(us, 3), "alg_bytes": b, "GBps": round(b / us / 1e3, 1),
                 "Gelem/s": round(n * t / us / 1e3, 2)}
@@ -473,7 +490,7 @@ def main():
     cfg = {"workload": name, "calls_per_step": len(calls),
            "cache": "warm" if args.warm else "cold",
            "replicas": {f"{n}x{t}": nrep[(n, t)] for n, t in shapes},
-           "launch": "hip graph per step"}
+           "launch": "hip graph per step", "storage": storage}
     if len(shapes) == 1:
         cfg.update(num_envs=shapes[0][0], seq_len=shapes[0][1])
     else:

@@ -62,6 +62,11 @@
 extern "C" {
 #endif
 
+/* Bit containers for the 16-bit variants: bfloat16 (1-8-7) and IEEE 754
+ * binary16 (1-5-10) values, stored as their bit patterns. */
+typedef uint16_t lrs_bf16;
+typedef uint16_t lrs_f16;
+
 typedef enum lrs_status {
     LRS_OK = 0,
     LRS_ERR_INVALID_ARG = 1, /* bad size, null pointer, scalar out of range */
@@ -230,6 +235,117 @@ lrs_status lrs_affine_scan_f32(int64_t num_envs, int64_t seq_len,
                                float* y,
                                void* workspace, size_t workspace_bytes,
                                hipStream_t stream);
+
+/* 16-bit storage variants of every call above (bfloat16: _bf16, IEEE half:
+ * _f16).  Same operation, arguments, limits and errors as the _f32 call of
+ * the same name; every floating-point stream -- the per-step inputs,
+ * trunc_values, bootstrap_value, carry_in and every output -- is 16-bit,
+ * while masks stay uint8 and the scalars (gamma, lambda, clips) stay float.
+ * Arithmetic is fp32 (and the cross-tile composition fp64) exactly as in
+ * the _f32 calls: inputs widen exactly, each output is rounded once to
+ * nearest even, so it lies within half a 16-bit ulp of the fp32 result.
+ * Halving the bytes per element halves the time of these HBM-bound calls.
+ * The pages serve standard formats only (gist.science summary, closing
+ * limitations paragraph of its plain-language part); this storage option is
+ * this library's extension of the same recurrences.  The vector fast path
+ * needs 8-byte aligned data streams (2-byte alignment is accepted).       */
+lrs_status lrs_gae_bf16(int64_t num_envs, int64_t seq_len,
+                        const lrs_bf16* rewards, const lrs_bf16* values,
+                        const uint8_t* terminateds, const uint8_t* truncateds,
+                        const lrs_bf16* trunc_values, const lrs_bf16* bootstrap_value,
+                        float gamma, float lambda, lrs_bf16* advantages,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+lrs_status lrs_vtrace_bf16(int64_t num_envs, int64_t seq_len,
+                           const lrs_bf16* log_rhos, const lrs_bf16* rewards, const lrs_bf16* values,
+                           const uint8_t* terminateds, const uint8_t* truncateds,
+                           const lrs_bf16* trunc_values, const lrs_bf16* bootstrap_value,
+                           float gamma, float lambda,
+                           float rho_bar, float c_bar, float pg_rho_bar,
+                           lrs_bf16* vs, lrs_bf16* pg_advantages,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+lrs_status lrs_retrace_bf16(int64_t num_envs, int64_t seq_len,
+                            const lrs_bf16* log_rhos, const lrs_bf16* rewards,
+                            const lrs_bf16* q_values, const lrs_bf16* values,
+                            const uint8_t* terminateds, const uint8_t* truncateds,
+                            const lrs_bf16* trunc_values, const lrs_bf16* bootstrap_value,
+                            float gamma, float lambda, float c_bar, lrs_bf16* q_ret,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+lrs_status lrs_lambda_returns_bf16(int64_t num_envs, int64_t seq_len,
+                                   const lrs_bf16* rewards, const lrs_bf16* values,
+                                   const uint8_t* terminateds, const uint8_t* truncateds,
+                                   const lrs_bf16* trunc_values, const lrs_bf16* bootstrap_value,
+                                   float gamma, float lambda, lrs_bf16* returns,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+lrs_status lrs_discounted_returns_bf16(int64_t num_envs, int64_t seq_len,
+                                       const lrs_bf16* rewards,
+                                       const uint8_t* terminateds, const uint8_t* truncateds,
+                                       const lrs_bf16* trunc_values, const lrs_bf16* bootstrap_value,
+                                       float gamma, lrs_bf16* returns,
+                                       void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+lrs_status lrs_eligibility_traces_bf16(int64_t num_envs, int64_t seq_len,
+                                       const lrs_bf16* x, const uint8_t* dones,
+                                       float gamma, float lambda, lrs_bf16* traces,
+                                       void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+lrs_status lrs_episodic_prefix_sum_bf16(int64_t num_envs, int64_t seq_len,
+                                        const lrs_bf16* x, const uint8_t* dones, lrs_bf16* sums,
+                                        void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream);
+lrs_status lrs_affine_scan_bf16(int64_t num_envs, int64_t seq_len,
+                                const lrs_bf16* alpha, const lrs_bf16* beta,
+                                const uint8_t* reset, const lrs_bf16* carry_in, int reverse,
+                                lrs_bf16* y,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+lrs_status lrs_gae_f16(int64_t num_envs, int64_t seq_len,
+                        const lrs_f16* rewards, const lrs_f16* values,
+                        const uint8_t* terminateds, const uint8_t* truncateds,
+                        const lrs_f16* trunc_values, const lrs_f16* bootstrap_value,
+                        float gamma, float lambda, lrs_f16* advantages,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+lrs_status lrs_vtrace_f16(int64_t num_envs, int64_t seq_len,
+                           const lrs_f16* log_rhos, const lrs_f16* rewards, const lrs_f16* values,
+                           const uint8_t* terminateds, const uint8_t* truncateds,
+                           const lrs_f16* trunc_values, const lrs_f16* bootstrap_value,
+                           float gamma, float lambda,
+                           float rho_bar, float c_bar, float pg_rho_bar,
+                           lrs_f16* vs, lrs_f16* pg_advantages,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+lrs_status lrs_retrace_f16(int64_t num_envs, int64_t seq_len,
+                            const lrs_f16* log_rhos, const lrs_f16* rewards,
+                            const lrs_f16* q_values, const lrs_f16* values,
+                            const uint8_t* terminateds, const uint8_t* truncateds,
+                            const lrs_f16* trunc_values, const lrs_f16* bootstrap_value,
+                            float gamma, float lambda, float c_bar, lrs_f16* q_ret,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+lrs_status lrs_lambda_returns_f16(int64_t num_envs, int64_t seq_len,
+                                   const lrs_f16* rewards, const lrs_f16* values,
+                                   const uint8_t* terminateds, const uint8_t* truncateds,
+                                   const lrs_f16* trunc_values, const lrs_f16* bootstrap_value,
+                                   float gamma, float lambda, lrs_f16* returns,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+lrs_status lrs_discounted_returns_f16(int64_t num_envs, int64_t seq_len,
+                                       const lrs_f16* rewards,
+                                       const uint8_t* terminateds, const uint8_t* truncateds,
+                                       const lrs_f16* trunc_values, const lrs_f16* bootstrap_value,
+                                       float gamma, lrs_f16* returns,
+                                       void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+lrs_status lrs_eligibility_traces_f16(int64_t num_envs, int64_t seq_len,
+                                       const lrs_f16* x, const uint8_t* dones,
+                                       float gamma, float lambda, lrs_f16* traces,
+                                       void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+lrs_status lrs_episodic_prefix_sum_f16(int64_t num_envs, int64_t seq_len,
+                                        const lrs_f16* x, const uint8_t* dones, lrs_f16* sums,
+                                        void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream);
+lrs_status lrs_affine_scan_f16(int64_t num_envs, int64_t seq_len,
+                                const lrs_f16* alpha, const lrs_f16* beta,
+                                const uint8_t* reset, const lrs_f16* carry_in, int reverse,
+                                lrs_f16* y,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Diagnostics and tuning (process-wide; not for concurrent use).
  * force_lookback != 0: every later call takes the multi-block carry-

@@ -1,5 +1,6 @@
 """Python binding of liblrs.so: the seven estimators and the generic
-segmented affine scan on torch tensors.
+segmented affine scan on torch tensors (float32, bfloat16 or float16 data;
+the dtype of the first data tensor picks the _f32 / _bf16 / _f16 entry).
 
 Argument marshalling only: every step of every estimator runs in the gfx950
 kernels behind the C ABI (include/lrs.h).  torch supplies device memory and
@@ -25,7 +26,7 @@ _I64 = ctypes.c_int64
 _F = ctypes.c_float
 _SZ = ctypes.c_size_t
 
-_SIGS = {
+_BASE_SIGS = {
     "lrs_gae_f32": [_I64, _I64, _P, _P, _P, _P, _P, _P, _F, _F, _P, _P, _SZ, _P],
     "lrs_vtrace_f32": [_I64, _I64, _P, _P, _P, _P, _P, _P, _P, _F, _F, _F, _F, _F, _P, _P, _P, _SZ,
                        _P],
@@ -37,6 +38,24 @@ _SIGS = {
     "lrs_episodic_prefix_sum_f32": [_I64, _I64, _P, _P, _P, _P, _SZ, _P],
     "lrs_affine_scan_f32": [_I64, _I64, _P, _P, _P, _P, ctypes.c_int, _P, _P, _SZ, _P],
 }
+# the 16-bit variants take the same arguments (pointers to 16-bit data)
+_SIGS = dict(_BASE_SIGS)
+for _name, _args in _BASE_SIGS.items():
+    if _name.endswith("_f32"):
+        for _sfx in ("bf16", "f16"):
+            _SIGS[_name[:-3] + _sfx] = _args
+
+# storage dtype of the floating-point streams -> entry-point suffix
+_SUFFIX = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}
+
+
+def _suffix(x, name):
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    try:
+        return _SUFFIX[x.dtype]
+    except KeyError:
+        raise TypeError(f"{name} must be float32, bfloat16 or float16, got {x.dtype}") from None
 
 ESTIMATOR_ID = {"gae": 0, "vtrace": 1, "retrace": 2, "lambda_returns": 3,
                 "discounted_returns": 4, "eligibility_traces": 5, "prefix_sum_i32": 6,
@@ -166,7 +185,7 @@ def _rows(x, name):
     return x.shape[0], x.shape[1]
 
 
-def _prep_boundary(shape, device, terminateds, truncateds, trunc_values, bootstrap_value):
+def _prep_boundary(shape, device, dtype, terminateds, truncateds, trunc_values, bootstrap_value):
     term = _mask(terminateds, "terminateds", shape, device)
     if term is None:
         raise ValueError("terminateds is required")
@@ -175,10 +194,10 @@ def _prep_boundary(shape, device, terminateds, truncateds, trunc_values, bootstr
     if trunc is not None:
         if trunc_values is None:
             raise ValueError("truncateds given without trunc_values")
-        tv = _dev_tensor(trunc_values, "trunc_values", torch.float32, shape, device)
+        tv = _dev_tensor(trunc_values, "trunc_values", dtype, shape, device)
     boot = None
     if bootstrap_value is not None:
-        boot = _dev_tensor(bootstrap_value, "bootstrap_value", torch.float32, (shape[0],), device)
+        boot = _dev_tensor(bootstrap_value, "bootstrap_value", dtype, (shape[0],), device)
     return term, trunc, tv, boot
 
 
@@ -199,16 +218,17 @@ def _launch_ctx(device, est, n, t):
 
 def compute_gae(rewards, values, terminateds, gamma=0.99, lambda_=0.95, *, truncateds=None,
                 trunc_values=None, bootstrap_value=None, out=None):
-    """Generalized advantage estimates, [num_envs, seq_len] float32."""
+    """Generalized advantage estimates, [num_envs, seq_len], in the dtype of
+    rewards (float32, bfloat16 or float16; every float input must match)."""
     n, t = _rows(rewards, "rewards")
-    dev = rewards.device
-    r = _dev_tensor(rewards, "rewards", torch.float32, (n, t), None)
-    v = _dev_tensor(values, "values", torch.float32, (n, t), dev)
-    term, trunc, tv, boot = _prep_boundary((n, t), dev, terminateds, truncateds, trunc_values,
+    dev, sfx, dt = rewards.device, _suffix(rewards, "rewards"), rewards.dtype
+    r = _dev_tensor(rewards, "rewards", dt, (n, t), None)
+    v = _dev_tensor(values, "values", dt, (n, t), dev)
+    term, trunc, tv, boot = _prep_boundary((n, t), dev, dt, terminateds, truncateds, trunc_values,
                                            bootstrap_value)
     adv = _out(out, r, "out")
     ws, wsb, st = _launch_ctx(dev, "gae", n, t)
-    _check(load().lrs_gae_f32(n, t, _ptr(r), _ptr(v), _ptr(term), _ptr(trunc), _ptr(tv),
+    _check(getattr(load(), f"lrs_gae_{sfx}")(n, t, _ptr(r), _ptr(v), _ptr(term), _ptr(trunc), _ptr(tv),
                               _ptr(boot), gamma, lambda_, _ptr(adv), _ptr(ws), wsb, st),
            "compute_gae")
     return adv
@@ -219,18 +239,18 @@ def compute_vtrace(log_rhos, rewards, values, terminateds, gamma=0.99, lambda_=1
                    bootstrap_value=None, out=None):
     """V-trace targets and policy-gradient advantages: returns (vs, pg_advantages)."""
     n, t = _rows(rewards, "rewards")
-    dev = rewards.device
-    r = _dev_tensor(rewards, "rewards", torch.float32, (n, t), None)
-    lr = _dev_tensor(log_rhos, "log_rhos", torch.float32, (n, t), dev)
-    v = _dev_tensor(values, "values", torch.float32, (n, t), dev)
-    term, trunc, tv, boot = _prep_boundary((n, t), dev, terminateds, truncateds, trunc_values,
+    dev, sfx, dt = rewards.device, _suffix(rewards, "rewards"), rewards.dtype
+    r = _dev_tensor(rewards, "rewards", dt, (n, t), None)
+    lr = _dev_tensor(log_rhos, "log_rhos", dt, (n, t), dev)
+    v = _dev_tensor(values, "values", dt, (n, t), dev)
+    term, trunc, tv, boot = _prep_boundary((n, t), dev, dt, terminateds, truncateds, trunc_values,
                                            bootstrap_value)
     vs = _out(None if out is None else out[0], r, "out[0]")
     pg = _out(None if out is None else out[1], r, "out[1]")
     if pg_rho_bar is None:
         pg_rho_bar = rho_bar
     ws, wsb, st = _launch_ctx(dev, "vtrace", n, t)
-    _check(load().lrs_vtrace_f32(n, t, _ptr(lr), _ptr(r), _ptr(v), _ptr(term), _ptr(trunc),
+    _check(getattr(load(), f"lrs_vtrace_{sfx}")(n, t, _ptr(lr), _ptr(r), _ptr(v), _ptr(term), _ptr(trunc),
                                  _ptr(tv), _ptr(boot), gamma, lambda_, _inf(rho_bar), _inf(c_bar),
                                  _inf(pg_rho_bar), _ptr(vs), _ptr(pg), _ptr(ws), wsb, st),
            "compute_vtrace")
@@ -241,16 +261,16 @@ def compute_retrace(log_rhos, rewards, q_values, values, terminateds, gamma=0.99
                     c_bar=1.0, truncateds=None, trunc_values=None, bootstrap_value=None, out=None):
     """Retrace(lambda) targets for Q(s_t, a_t); values = E_pi Q(s_t, .)."""
     n, t = _rows(rewards, "rewards")
-    dev = rewards.device
-    r = _dev_tensor(rewards, "rewards", torch.float32, (n, t), None)
-    lr = _dev_tensor(log_rhos, "log_rhos", torch.float32, (n, t), dev)
-    q = _dev_tensor(q_values, "q_values", torch.float32, (n, t), dev)
-    v = _dev_tensor(values, "values", torch.float32, (n, t), dev)
-    term, trunc, tv, boot = _prep_boundary((n, t), dev, terminateds, truncateds, trunc_values,
+    dev, sfx, dt = rewards.device, _suffix(rewards, "rewards"), rewards.dtype
+    r = _dev_tensor(rewards, "rewards", dt, (n, t), None)
+    lr = _dev_tensor(log_rhos, "log_rhos", dt, (n, t), dev)
+    q = _dev_tensor(q_values, "q_values", dt, (n, t), dev)
+    v = _dev_tensor(values, "values", dt, (n, t), dev)
+    term, trunc, tv, boot = _prep_boundary((n, t), dev, dt, terminateds, truncateds, trunc_values,
                                            bootstrap_value)
     g = _out(out, r, "out")
     ws, wsb, st = _launch_ctx(dev, "retrace", n, t)
-    _check(load().lrs_retrace_f32(n, t, _ptr(lr), _ptr(r), _ptr(q), _ptr(v), _ptr(term),
+    _check(getattr(load(), f"lrs_retrace_{sfx}")(n, t, _ptr(lr), _ptr(r), _ptr(q), _ptr(v), _ptr(term),
                                   _ptr(trunc), _ptr(tv), _ptr(boot), gamma, lambda_, _inf(c_bar),
                                   _ptr(g), _ptr(ws), wsb, st), "compute_retrace")
     return g
@@ -260,14 +280,14 @@ def compute_lambda_returns(rewards, values, terminateds, gamma=0.99, lambda_=0.9
                            truncateds=None, trunc_values=None, bootstrap_value=None, out=None):
     """TD(lambda) returns."""
     n, t = _rows(rewards, "rewards")
-    dev = rewards.device
-    r = _dev_tensor(rewards, "rewards", torch.float32, (n, t), None)
-    v = _dev_tensor(values, "values", torch.float32, (n, t), dev)
-    term, trunc, tv, boot = _prep_boundary((n, t), dev, terminateds, truncateds, trunc_values,
+    dev, sfx, dt = rewards.device, _suffix(rewards, "rewards"), rewards.dtype
+    r = _dev_tensor(rewards, "rewards", dt, (n, t), None)
+    v = _dev_tensor(values, "values", dt, (n, t), dev)
+    term, trunc, tv, boot = _prep_boundary((n, t), dev, dt, terminateds, truncateds, trunc_values,
                                            bootstrap_value)
     g = _out(out, r, "out")
     ws, wsb, st = _launch_ctx(dev, "lambda_returns", n, t)
-    _check(load().lrs_lambda_returns_f32(n, t, _ptr(r), _ptr(v), _ptr(term), _ptr(trunc),
+    _check(getattr(load(), f"lrs_lambda_returns_{sfx}")(n, t, _ptr(r), _ptr(v), _ptr(term), _ptr(trunc),
                                          _ptr(tv), _ptr(boot), gamma, lambda_, _ptr(g), _ptr(ws),
                                          wsb, st), "compute_lambda_returns")
     return g
@@ -277,43 +297,45 @@ def compute_discounted_returns(rewards, terminateds, gamma=0.99, *, truncateds=N
                                trunc_values=None, bootstrap_value=None, out=None):
     """Discounted reward-to-go."""
     n, t = _rows(rewards, "rewards")
-    dev = rewards.device
-    r = _dev_tensor(rewards, "rewards", torch.float32, (n, t), None)
-    term, trunc, tv, boot = _prep_boundary((n, t), dev, terminateds, truncateds, trunc_values,
+    dev, sfx, dt = rewards.device, _suffix(rewards, "rewards"), rewards.dtype
+    r = _dev_tensor(rewards, "rewards", dt, (n, t), None)
+    term, trunc, tv, boot = _prep_boundary((n, t), dev, dt, terminateds, truncateds, trunc_values,
                                            bootstrap_value)
     g = _out(out, r, "out")
     ws, wsb, st = _launch_ctx(dev, "discounted_returns", n, t)
-    _check(load().lrs_discounted_returns_f32(n, t, _ptr(r), _ptr(term), _ptr(trunc), _ptr(tv),
+    _check(getattr(load(), f"lrs_discounted_returns_{sfx}")(n, t, _ptr(r), _ptr(term), _ptr(trunc), _ptr(tv),
                                              _ptr(boot), gamma, _ptr(g), _ptr(ws), wsb, st),
            "compute_discounted_returns")
     return g
 
 
 def compute_eligibility_traces(x, dones, gamma=0.99, lambda_=0.95, *, out=None):
-    """Accumulating eligibility traces, forward in time."""
+    """Accumulating eligibility traces, forward in time (dtype of x)."""
     n, t = _rows(x, "x")
-    dev = x.device
-    xs = _dev_tensor(x, "x", torch.float32, (n, t), None)
+    dev, sfx = x.device, _suffix(x, "x")
+    xs = _dev_tensor(x, "x", x.dtype, (n, t), None)
     d = _mask(dones, "dones", (n, t), dev)
     if d is None:
         raise ValueError("dones is required")
     e = _out(out, xs, "out")
     ws, wsb, st = _launch_ctx(dev, "eligibility_traces", n, t)
-    _check(load().lrs_eligibility_traces_f32(n, t, _ptr(xs), _ptr(d), gamma, lambda_, _ptr(e),
+    _check(getattr(load(), f"lrs_eligibility_traces_{sfx}")(n, t, _ptr(xs), _ptr(d), gamma, lambda_, _ptr(e),
                                              _ptr(ws), wsb, st), "compute_eligibility_traces")
     return e
 
 
 def compute_episodic_prefix_sum(x, dones, *, out=None):
-    """Inclusive prefix sum with done resets; int32 (exact) or float32 input."""
+    """Inclusive prefix sum with done resets; int32 (exact), float32, bfloat16
+    or float16 input, output of the same dtype."""
     n, t = _rows(x, "x")
     dev = x.device
-    if x.dtype == torch.int32:
+    if isinstance(x, torch.Tensor) and x.dtype == torch.int32:
         xs = _dev_tensor(x, "x", torch.int32, (n, t), None)
         fn, est = load().lrs_episodic_prefix_sum_i32, "prefix_sum_i32"
     else:
-        xs = _dev_tensor(x, "x", torch.float32, (n, t), None)
-        fn, est = load().lrs_episodic_prefix_sum_f32, "prefix_sum_f32"
+        sfx = _suffix(x, "x")
+        xs = _dev_tensor(x, "x", x.dtype, (n, t), None)
+        fn, est = getattr(load(), f"lrs_episodic_prefix_sum_{sfx}"), "prefix_sum_f32"
     d = _mask(dones, "dones", (n, t), dev)
     if d is None:
         raise ValueError("dones is required")
@@ -329,14 +351,14 @@ def compute_affine_scan(alpha, beta, *, reset=None, carry_in=None, reverse=False
     (reverse=True).  carry_in [num_envs] is the y before each row's first step
     in scan order (0 if None); where reset is set, y_t = alpha_t."""
     n, t = _rows(alpha, "alpha")
-    dev = alpha.device
-    a = _dev_tensor(alpha, "alpha", torch.float32, (n, t), None)
-    b = _dev_tensor(beta, "beta", torch.float32, (n, t), dev)
+    dev, sfx, dt = alpha.device, _suffix(alpha, "alpha"), alpha.dtype
+    a = _dev_tensor(alpha, "alpha", dt, (n, t), None)
+    b = _dev_tensor(beta, "beta", dt, (n, t), dev)
     rs = _mask(reset, "reset", (n, t), dev)
-    c = None if carry_in is None else _dev_tensor(carry_in, "carry_in", torch.float32, (n,), dev)
+    c = None if carry_in is None else _dev_tensor(carry_in, "carry_in", dt, (n,), dev)
     y = _out(out, a, "out")
     ws, wsb, st = _launch_ctx(dev, "affine_scan", n, t)
-    _check(load().lrs_affine_scan_f32(n, t, _ptr(a), _ptr(b), _ptr(rs), _ptr(c),
+    _check(getattr(load(), f"lrs_affine_scan_{sfx}")(n, t, _ptr(a), _ptr(b), _ptr(rs), _ptr(c),
                                       1 if reverse else 0, _ptr(y), _ptr(ws), wsb, st),
            "compute_affine_scan")
     return y

@@ -16,9 +16,11 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 # One translation unit per group of entry points, compiled in parallel.
-SOURCES = [os.path.join(CSRC, f) for f in
-           ("abi.hip", "returns.hip", "offpolicy.hip", "forward.hip", "affine.hip")]
-HEADERS = [os.path.join(CSRC, f) for f in ("launch.hpp", "scan_core.hpp", "estimators.hpp")] + \
+SOURCES = [os.path.join(CSRC, "abi.hip")] + [
+    os.path.join(CSRC, f"{group}{sfx}.hip")
+    for group in ("returns", "offpolicy", "forward", "affine") for sfx in ("", "_bf16", "_f16")]
+HEADERS = [os.path.join(CSRC, f)
+           for f in ("launch.hpp", "scan_core.hpp", "estimators.hpp", "entries.hpp")] + \
     [os.path.join(ROOT, "include", "lrs.h")]
 DEPS = SOURCES + HEADERS
 LIB = os.path.join(PKG, "liblrs.so")
@@ -47,20 +49,29 @@ def build(resource_usage: bool = False, quiet: bool = True) -> str:
     """Always recompiles every source (in parallel), links liblrs.so atomically."""
     os.makedirs(OBJ_DIR, exist_ok=True)
     cc = hipcc()
-    procs = []
-    for src in SOURCES:
-        obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
-        cmd = [cc] + flags(resource_usage) + ["-c", src, "-o", obj]
-        procs.append((src, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE,
-                                                 stderr=subprocess.PIPE, text=True)))
-    failed = []
-    for src, obj, p in procs:
+    jobs = max(1, min(16, os.cpu_count() or 1))
+    procs, failed, pending = [], [], list(SOURCES)
+
+    def reap(entry):
+        src, obj, p = entry
         out, err = p.communicate()
         if p.returncode != 0:
             failed.append(src)
             sys.stderr.write(out + err)
         elif not quiet or resource_usage:
             sys.stderr.write(err)
+
+    running = []
+    while pending or running:
+        while pending and len(running) < jobs:
+            src = pending.pop(0)
+            obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
+            cmd = [cc] + flags(resource_usage) + ["-c", src, "-o", obj]
+            entry = (src, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                                stderr=subprocess.PIPE, text=True))
+            running.append(entry)
+            procs.append(entry)
+        reap(running.pop(0))
     if failed:
         raise RuntimeError(f"hipcc failed on {', '.join(map(os.path.basename, failed))}")
     tmp = LIB + ".tmp"

@@ -1,0 +1,201 @@
+// entries.hpp -- argument checks and launch of every estimator and of the
+// generic affine scan, for any element type D of the data streams (float,
+// bf16_t, f16_t).  The extern "C" functions of include/lrs.h are thin
+// wrappers over these templates, one translation unit per group and type.
+#pragma once
+
+#include "launch.hpp"
+
+namespace lrs {
+
+template <class D> struct GaeSel {
+    template <int E> using T = GaeOp<E, true, D>;
+    template <int E> using N = GaeOp<E, false, D>;
+};
+template <class D> struct LambdaSel {
+    template <int E> using T = LambdaOp<E, true, D>;
+    template <int E> using N = LambdaOp<E, false, D>;
+};
+template <class D> struct DiscSel {
+    template <int E> using T = DiscOp<E, true, D>;
+    template <int E> using N = DiscOp<E, false, D>;
+};
+template <class D> struct VtraceSel {
+    template <int E> using T = VtraceOp<E, true, D>;
+    template <int E> using N = VtraceOp<E, false, D>;
+};
+template <class D> struct RetraceSel {
+    template <int E> using T = RetraceOp<E, true, D>;
+    template <int E> using N = RetraceOp<E, false, D>;
+};
+template <class D> struct ForwardSel {
+    template <int E> using Elig = EligOp<E, D>;
+    template <int E> using Prefix = PrefixF32Op<E, D>;
+};
+template <class D> struct AffineSel {
+    template <int E> using FwdR = AffineOp<E, false, true, D>;
+    template <int E> using FwdN = AffineOp<E, false, false, D>;
+    template <int E> using RevR = AffineOp<E, true, true, D>;
+    template <int E> using RevN = AffineOp<E, true, false, D>;
+};
+
+template <class D>
+lrs_status gae_entry(const char* nm, int64_t N, int64_t T, const D* rewards, const D* values,
+                     const uint8_t* term, const uint8_t* trunc, const D* tv, const D* boot,
+                     float gamma, float lambda, D* adv, void* ws, size_t ws_bytes,
+                     hipStream_t stream)
+{
+    LRS_TRY(check_common(nm, N, T));
+    LRS_REQUIRE(rewards && values && adv, "%s: rewards, values and advantages are required", nm);
+    LRS_TRY(check_boundary(nm, term, trunc, tv));
+    LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda), "%s: gamma and lambda must be in [0, 1]", nm);
+    GaeArgs<D> a{{term, trunc, tv, boot ? boot : rewards, boot != nullptr}, rewards, values, gamma,
+                 (float)((double)gamma * (double)lambda), adv};
+    const void* f[] = {rewards, values, adv, tv};
+    const void* m[] = {term, trunc};
+    using S = GaeSel<D>;
+    return trunc ? run<S::template T>(nm, N, T, a, f, 4, m, 2, ws, ws_bytes, stream)
+                 : run<S::template N>(nm, N, T, a, f, 4, m, 2, ws, ws_bytes, stream);
+}
+
+template <class D>
+lrs_status vtrace_entry(const char* nm, int64_t N, int64_t T, const D* log_rhos, const D* rewards,
+                        const D* values, const uint8_t* term, const uint8_t* trunc, const D* tv,
+                        const D* boot, float gamma, float lambda, float rho_bar, float c_bar,
+                        float pg_rho_bar, D* vs, D* pg_adv, void* ws, size_t ws_bytes,
+                        hipStream_t stream)
+{
+    LRS_TRY(check_common(nm, N, T));
+    LRS_REQUIRE(log_rhos && rewards && values && vs && pg_adv,
+                "%s: log_rhos, rewards, values, vs and pg_advantages are required", nm);
+    LRS_TRY(check_boundary(nm, term, trunc, tv));
+    LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda), "%s: gamma and lambda must be in [0, 1]", nm);
+    LRS_REQUIRE(positive(rho_bar) && positive(c_bar) && positive(pg_rho_bar),
+                "%s: rho_bar, c_bar and pg_rho_bar must be > 0", nm);
+    VtraceArgs<D> a{{term, trunc, tv, boot ? boot : rewards, boot != nullptr}, log_rhos, rewards,
+                    values, gamma, lambda, rho_bar, c_bar, pg_rho_bar, vs, pg_adv};
+    const void* f[] = {log_rhos, rewards, values, vs, pg_adv, tv};
+    const void* m[] = {term, trunc};
+    using S = VtraceSel<D>;
+    return trunc ? run<S::template T>(nm, N, T, a, f, 6, m, 2, ws, ws_bytes, stream)
+                 : run<S::template N>(nm, N, T, a, f, 6, m, 2, ws, ws_bytes, stream);
+}
+
+template <class D>
+lrs_status retrace_entry(const char* nm, int64_t N, int64_t T, const D* log_rhos,
+                         const D* rewards, const D* q_values, const D* values, const uint8_t* term,
+                         const uint8_t* trunc, const D* tv, const D* boot, float gamma,
+                         float lambda, float c_bar, D* q_ret, void* ws, size_t ws_bytes,
+                         hipStream_t stream)
+{
+    LRS_TRY(check_common(nm, N, T));
+    LRS_REQUIRE(log_rhos && rewards && q_values && values && q_ret,
+                "%s: log_rhos, rewards, q_values, values and q_ret are required", nm);
+    LRS_TRY(check_boundary(nm, term, trunc, tv));
+    LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda), "%s: gamma and lambda must be in [0, 1]", nm);
+    LRS_REQUIRE(positive(c_bar), "%s: c_bar must be > 0", nm);
+    RetraceArgs<D> a{{term, trunc, tv, boot ? boot : rewards, boot != nullptr}, log_rhos, rewards,
+                     q_values, values, gamma, lambda, c_bar, q_ret};
+    const void* f[] = {log_rhos, rewards, q_values, values, q_ret, tv};
+    const void* m[] = {term, trunc};
+    using S = RetraceSel<D>;
+    return trunc ? run<S::template T>(nm, N, T, a, f, 6, m, 2, ws, ws_bytes, stream)
+                 : run<S::template N>(nm, N, T, a, f, 6, m, 2, ws, ws_bytes, stream);
+}
+
+template <class D>
+lrs_status lambda_returns_entry(const char* nm, int64_t N, int64_t T, const D* rewards,
+                                const D* values, const uint8_t* term, const uint8_t* trunc,
+                                const D* tv, const D* boot, float gamma, float lambda, D* out,
+                                void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    LRS_TRY(check_common(nm, N, T));
+    LRS_REQUIRE(rewards && values && out, "%s: rewards, values and returns are required", nm);
+    LRS_TRY(check_boundary(nm, term, trunc, tv));
+    LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda), "%s: gamma and lambda must be in [0, 1]", nm);
+    LambdaArgs<D> a{{term, trunc, tv, boot ? boot : rewards, boot != nullptr}, rewards, values, gamma,
+                    (float)((double)gamma * (double)lambda),
+                    (float)((double)gamma * (1.0 - (double)lambda)), out};
+    const void* f[] = {rewards, values, out, tv};
+    const void* m[] = {term, trunc};
+    using S = LambdaSel<D>;
+    return trunc ? run<S::template T>(nm, N, T, a, f, 4, m, 2, ws, ws_bytes, stream)
+                 : run<S::template N>(nm, N, T, a, f, 4, m, 2, ws, ws_bytes, stream);
+}
+
+template <class D>
+lrs_status discounted_returns_entry(const char* nm, int64_t N, int64_t T, const D* rewards,
+                                    const uint8_t* term, const uint8_t* trunc, const D* tv,
+                                    const D* boot, float gamma, D* out, void* ws, size_t ws_bytes,
+                                    hipStream_t stream)
+{
+    LRS_TRY(check_common(nm, N, T));
+    LRS_REQUIRE(rewards && out, "%s: rewards and returns are required", nm);
+    LRS_TRY(check_boundary(nm, term, trunc, tv));
+    LRS_REQUIRE(unit_interval(gamma), "%s: gamma must be in [0, 1]", nm);
+    DiscArgs<D> a{{term, trunc, tv, boot ? boot : rewards, boot != nullptr}, rewards, gamma, out};
+    const void* f[] = {rewards, out, tv};
+    const void* m[] = {term, trunc};
+    using S = DiscSel<D>;
+    return trunc ? run<S::template T>(nm, N, T, a, f, 3, m, 2, ws, ws_bytes, stream)
+                 : run<S::template N>(nm, N, T, a, f, 3, m, 2, ws, ws_bytes, stream);
+}
+
+template <class D>
+lrs_status eligibility_traces_entry(const char* nm, int64_t N, int64_t T, const D* x,
+                                    const uint8_t* dones, float gamma, float lambda, D* out,
+                                    void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    LRS_TRY(check_common(nm, N, T));
+    LRS_REQUIRE(x && dones && out, "%s: x, dones and traces are required", nm);
+    LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda), "%s: gamma and lambda must be in [0, 1]", nm);
+    ForwardArgs a{x, dones, (float)((double)gamma * (double)lambda), out};
+    const void* f[] = {x, out};
+    const void* m[] = {dones};
+    return run<ForwardSel<D>::template Elig>(nm, N, T, a, f, 2, m, 1, ws, ws_bytes, stream);
+}
+
+template <class D>
+lrs_status prefix_sum_entry(const char* nm, int64_t N, int64_t T, const D* x, const uint8_t* dones,
+                            D* out, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    LRS_TRY(check_common(nm, N, T));
+    LRS_REQUIRE(x && dones && out, "%s: x, dones and sums are required", nm);
+    ForwardArgs a{x, dones, 1.0f, out};
+    const void* f[] = {x, out};
+    const void* m[] = {dones};
+    return run<ForwardSel<D>::template Prefix>(nm, N, T, a, f, 2, m, 1, ws, ws_bytes, stream);
+}
+
+inline lrs_status prefix_sum_i32_entry(const char* nm, int64_t N, int64_t T, const int32_t* x,
+                                       const uint8_t* dones, int32_t* out, void* ws,
+                                       size_t ws_bytes, hipStream_t stream)
+{
+    LRS_TRY(check_common(nm, N, T));
+    LRS_REQUIRE(x && dones && out, "%s: x, dones and sums are required", nm);
+    ForwardArgs a{x, dones, 1.0f, out};
+    const void* f[] = {x, out};
+    const void* m[] = {dones};
+    return run<PrefixI32Op>(nm, N, T, a, f, 2, m, 1, ws, ws_bytes, stream);
+}
+
+template <class D>
+lrs_status affine_scan_entry(const char* nm, int64_t N, int64_t T, const D* alpha, const D* beta,
+                             const uint8_t* reset, const D* carry_in, int reverse, D* out,
+                             void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    LRS_TRY(check_common(nm, N, T));
+    LRS_REQUIRE(alpha && beta && out, "%s: alpha, beta and out are required", nm);
+    LRS_REQUIRE(reverse == 0 || reverse == 1, "%s: reverse must be 0 or 1", nm);
+    AffineArgs<D> a{alpha, beta, reset, carry_in ? carry_in : alpha, carry_in != nullptr, out};
+    const void* f[] = {alpha, beta, out};
+    const void* m[] = {reset};
+    using S = AffineSel<D>;
+    if (reverse)
+        return reset ? run<S::template RevR>(nm, N, T, a, f, 3, m, 1, ws, ws_bytes, stream)
+                     : run<S::template RevN>(nm, N, T, a, f, 3, m, 1, ws, ws_bytes, stream);
+    return reset ? run<S::template FwdR>(nm, N, T, a, f, 3, m, 1, ws, ws_bytes, stream)
+                 : run<S::template FwdN>(nm, N, T, a, f, 3, m, 1, ws, ws_bytes, stream);
+}
+
+}  // namespace lrs

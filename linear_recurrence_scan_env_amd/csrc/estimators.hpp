@@ -39,18 +39,18 @@ struct Ctx {
 // lane order: lane L-1) and reads memory only in lane 0, which holds the
 // wave's last chunk.  `used` (the lane's last element is not a row end)
 // guarantees i0+E < N*T.
-template <int E, bool F>
-__device__ __forceinline__ float next_elem(float my0, const float* __restrict__ p,
+template <int E, bool F, class D>
+__device__ __forceinline__ float next_elem(float my0, const D* __restrict__ p,
                                            const Pos<E, F>& P, const Ctx& c, bool used)
 {
     if constexpr (F) {
         // unused: re-read the lane's own first element (a line already
         // fetched) rather than touch the next tile
-        const float v = p[used ? P.i0 + E : P.i0];
+        const float v = to_f32(p[used ? P.i0 + E : P.i0]);
         return used ? v : 0.0f;
     } else {
         float v = lane_prev(my0, 0.0f);
-        if (c.lane == 0) v = used ? p[P.i0 + E] : 0.0f;
+        if (c.lane == 0) v = used ? to_f32(p[P.i0 + E]) : 0.0f;
         return v;
     }
 }
@@ -73,16 +73,17 @@ struct Ends {
     float vend[E];
 };
 
+template <class D>
 struct BoundaryArgs {
     const uint8_t* term;
     const uint8_t* trunc;   // used iff the kernel is the truncating variant
-    const float* tv;        // idem
-    const float* boot;      // never null: without bootstrap values the host
+    const D* tv;            // idem
+    const D* boot;          // never null: without bootstrap values the host
     int has_boot;           // passes another input array and has_boot = 0
 };
 
-template <int E, bool F, bool kTrunc>
-__device__ __forceinline__ Ends<E> load_ends(const BoundaryArgs& b, const Pos<E, F>& P,
+template <int E, bool F, bool kTrunc, class D>
+__device__ __forceinline__ Ends<E> load_ends(const BoundaryArgs<D>& b, const Pos<E, F>& P,
                                              const Ctx& c)
 {
     const uint32_t tau = load_mask<E>(b.term, P, c.vec);
@@ -100,7 +101,7 @@ __device__ __forceinline__ Ends<E> load_ends(const BoundaryArgs& b, const Pos<E,
     // one unconditional load.  The guarded path loads per row end.
     float bv[E];
     if constexpr (F) {
-        const float b0 = b.boot[b.has_boot ? P.n0 : 0];
+        const float b0 = to_f32(b.boot[b.has_boot ? P.n0 : 0]);
 #pragma unroll
         for (int j = 0; j < E; ++j) bv[j] = b.has_boot ? b0 : 0.0f;
     } else {
@@ -108,7 +109,7 @@ __device__ __forceinline__ Ends<E> load_ends(const BoundaryArgs& b, const Pos<E,
 #pragma unroll
         for (int j = 0; j < E; ++j) {
             const bool last = (P.last >> j) & 1u;
-            bv[j] = (last && b.has_boot) ? b.boot[n] : 0.0f;
+            bv[j] = (last && b.has_boot) ? to_f32(b.boot[n]) : 0.0f;
             if (last) ++n;
         }
     }
@@ -148,18 +149,20 @@ __device__ __forceinline__ void backward_pass(float (&out)[E], const float (&alp
 // --------------------------------------------------------------- GAE
 // README Kernels table (compute_gae): delta_t = r_t + gamma*Vnext_t - V_t,
 // A_t = delta_t + gamma*lambda*A_{t+1} inside an episode.
+template <class D>
 struct GaeArgs {
-    BoundaryArgs b;
-    const float* rewards;
-    const float* values;
+    BoundaryArgs<D> b;
+    const D* rewards;
+    const D* values;
     float gamma, gl;  // gl = fp32(gamma*lambda)
-    float* adv;
+    D* adv;
 };
 
-template <int E, bool kTrunc>
+template <int E, bool kTrunc, class D = float>
 struct GaeOp {
     using T = float;
-    using Args = GaeArgs;
+    using Args = GaeArgs<D>;
+    static constexpr int kElemBytes = sizeof(D);
     static constexpr bool kBackward = true;
     static constexpr bool kWideTiles = true;
     struct State {
@@ -202,18 +205,20 @@ struct GaeOp {
 // README Kernels table (compute_lambda_returns):
 // G_t = r_t + gamma*((1-lambda)*V_{t+1} + lambda*G_{t+1}) inside an episode,
 // G_t = r_t + gamma*Vnext_t at its end.
+template <class D>
 struct LambdaArgs {
-    BoundaryArgs b;
-    const float* rewards;
-    const float* values;
+    BoundaryArgs<D> b;
+    const D* rewards;
+    const D* values;
     float gamma, gl, g1l;  // gl = fp32(gamma*lambda), g1l = fp32(gamma*(1-lambda))
-    float* out;
+    D* out;
 };
 
-template <int E, bool kTrunc>
+template <int E, bool kTrunc, class D = float>
 struct LambdaOp {
     using T = float;
-    using Args = LambdaArgs;
+    using Args = LambdaArgs<D>;
+    static constexpr int kElemBytes = sizeof(D);
     static constexpr bool kBackward = true;
     static constexpr bool kWideTiles = true;
     struct State {
@@ -254,17 +259,19 @@ struct LambdaOp {
 // --------------------------------------------------------- discounted returns
 // README Kernels table (compute_discounted_returns): G_t = r_t + gamma*G_{t+1}
 // inside an episode, r_t + gamma*Vnext_t at its end (values never read).
+template <class D>
 struct DiscArgs {
-    BoundaryArgs b;
-    const float* rewards;
+    BoundaryArgs<D> b;
+    const D* rewards;
     float gamma;
-    float* out;
+    D* out;
 };
 
-template <int E, bool kTrunc>
+template <int E, bool kTrunc, class D = float>
 struct DiscOp {
     using T = float;
-    using Args = DiscArgs;
+    using Args = DiscArgs<D>;
+    static constexpr int kElemBytes = sizeof(D);
     static constexpr bool kBackward = true;
     static constexpr bool kWideTiles = true;
     struct State {
@@ -304,20 +311,22 @@ struct DiscOp {
 // advantages); Espeholt et al. 2018 eq. 1 with c_t = lambda*min(c_bar, w_t):
 // A_t = rho_t*(r_t + gamma*Vnext_t - V_t) + gamma*c_t*A_{t+1}, vs_t = V_t + A_t,
 // pg_t = min(pg_rho_bar, w_t)*(r_t + gamma*(end_t ? Vnext_t : vs_{t+1}) - V_t).
+template <class D>
 struct VtraceArgs {
-    BoundaryArgs b;
-    const float* log_rhos;
-    const float* rewards;
-    const float* values;
+    BoundaryArgs<D> b;
+    const D* log_rhos;
+    const D* rewards;
+    const D* values;
     float gamma, lambda, rho_bar, c_bar, pg_rho_bar;
-    float* vs;
-    float* pg;
+    D* vs;
+    D* pg;
 };
 
-template <int E, bool kTrunc>
+template <int E, bool kTrunc, class D = float>
 struct VtraceOp {
     using T = float;
-    using Args = VtraceArgs;
+    using Args = VtraceArgs<D>;
+    static constexpr int kElemBytes = sizeof(D);
     static constexpr bool kBackward = true;
     // Whole rows of 4096 or 8192 in one block (E = 8 or 16 waves) cost
     // this op occupancy: its per-element state needs more registers.
@@ -380,20 +389,22 @@ struct VtraceOp {
 // importance ratios); Munos et al. 2016 with c_{t+1} = lambda*min(c_bar, w_{t+1}):
 // G_t = r_t + gamma*(V_{t+1} - c_{t+1}*Q_{t+1}) + gamma*c_{t+1}*G_{t+1} inside
 // an episode, r_t + gamma*Vnext_t at its end.
+template <class D>
 struct RetraceArgs {
-    BoundaryArgs b;
-    const float* log_rhos;
-    const float* rewards;
-    const float* q_values;
-    const float* values;
+    BoundaryArgs<D> b;
+    const D* log_rhos;
+    const D* rewards;
+    const D* q_values;
+    const D* values;
     float gamma, lambda, c_bar;
-    float* out;
+    D* out;
 };
 
-template <int E, bool kTrunc>
+template <int E, bool kTrunc, class D = float>
 struct RetraceOp {
     using T = float;
-    using Args = RetraceArgs;
+    using Args = RetraceArgs<D>;
+    static constexpr int kElemBytes = sizeof(D);
     static constexpr bool kBackward = true;
     // Whole rows of 4096 or 8192 in one block (E = 8 or 16 waves) cost
     // this op occupancy: its per-element state needs more registers.
@@ -482,10 +493,11 @@ struct ForwardArgs {
 
 // README Kernels table (compute_eligibility_traces):
 // e_t = x_t + gamma*lambda*(1 - d_{t-1})*e_{t-1}.
-template <int E>
+template <int E, class D = float>
 struct EligOp {
     using T = float;
     using Args = ForwardArgs;
+    static constexpr int kElemBytes = sizeof(D);
     static constexpr bool kBackward = false;
     static constexpr bool kWideTiles = true;
     struct State {
@@ -495,7 +507,7 @@ struct EligOp {
     __device__ static void prepare(const Args& a, const Pos<E, F>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
-        load_f32<E>(alpha, (const float*)a.x, P, c.vec);
+        load_f32<E>(alpha, (const D*)a.x, P, c.vec);
         s.reset = load_resets<E>(a.dones, P, c);
 #pragma unroll
         for (int j = 0; j < E; ++j) beta[j] = ((s.reset >> j) & 1u) ? 0.0f : a.gl;
@@ -514,15 +526,16 @@ struct EligOp {
             e = fmaf(beta[j], e, alpha[j]);
             out[j] = e;
         }
-        store_f32<E>((float*)a.out, out, P, c.vec);
+        store_f32<E>((D*)a.out, out, P, c.vec);
     }
 };
 
 // README Kernels table (compute_episodic_prefix_sum): S_t = x_t + (1 - d_{t-1})*S_{t-1}.
-template <int E>
+template <int E, class D = float>
 struct PrefixF32Op {
     using T = float;
     using Args = ForwardArgs;
+    static constexpr int kElemBytes = sizeof(D);
     static constexpr bool kBackward = false;
     static constexpr bool kWideTiles = true;
     struct State {
@@ -532,7 +545,7 @@ struct PrefixF32Op {
     __device__ static void prepare(const Args& a, const Pos<E, F>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
-        load_f32<E>(alpha, (const float*)a.x, P, c.vec);
+        load_f32<E>(alpha, (const D*)a.x, P, c.vec);
         s.reset = load_resets<E>(a.dones, P, c);
 #pragma unroll
         for (int j = 0; j < E; ++j) beta[j] = ((s.reset >> j) & 1u) ? 0.0f : 1.0f;
@@ -552,7 +565,7 @@ struct PrefixF32Op {
             out[j] = e;
         }
         (void)beta;
-        store_f32<E>((float*)a.out, out, P, c.vec);
+        store_f32<E>((D*)a.out, out, P, c.vec);
     }
 };
 
@@ -560,6 +573,7 @@ template <int E>
 struct PrefixI32Op {
     using T = uint32_t;
     using Args = ForwardArgs;
+    static constexpr int kElemBytes = 4;
     static constexpr bool kBackward = false;
     static constexpr bool kWideTiles = true;
     struct State {
@@ -599,19 +613,21 @@ struct PrefixI32Op {
 // here the pairs come from memory.  y_prev is y_{t+1} when kRev (scan from
 // the row end), else y_{t-1}.  Before the row's first step in scan order it
 // is carry[n] (0 without carries).  A set reset[t] drops beta_t * y_prev.
+template <class D>
 struct AffineArgs {
-    const float* alpha;
-    const float* beta;
+    const D* alpha;
+    const D* beta;
     const uint8_t* reset;  // used iff the kernel is the resetting variant
-    const float* carry;    // never null: without carries the host passes
+    const D* carry;        // never null: without carries the host passes
     int has_carry;         // alpha and has_carry = 0
-    float* out;
+    D* out;
 };
 
-template <int E, bool kRev, bool kReset>
+template <int E, bool kRev, bool kReset, class D = float>
 struct AffineOp {
     using T = float;
-    using Args = AffineArgs;
+    using Args = AffineArgs<D>;
+    static constexpr int kElemBytes = sizeof(D);
     static constexpr bool kBackward = kRev;
     static constexpr bool kWideTiles = true;
     struct State {
@@ -634,7 +650,7 @@ struct AffineOp {
             // the lane's first row.  Forward, it starts the lane's first row
             // if it is the lane's first element, else the next row.
             const bool next_row = !kRev && edge != 0u && !(edge & 1u);
-            const float c0 = a.carry[a.has_carry ? P.n0 + (next_row ? 1 : 0) : 0];
+            const float c0 = to_f32(a.carry[a.has_carry ? P.n0 + (next_row ? 1 : 0) : 0]);
 #pragma unroll
             for (int j = 0; j < E; ++j) cv[j] = a.has_carry ? c0 : 0.0f;
         } else {
@@ -643,7 +659,7 @@ struct AffineOp {
             for (int j = 0; j < E; ++j) {
                 const bool e = (edge >> j) & 1u;
                 if (!kRev && e && j > 0) ++n;
-                cv[j] = (e && a.has_carry) ? a.carry[n] : 0.0f;
+                cv[j] = (e && a.has_carry) ? to_f32(a.carry[n]) : 0.0f;
                 if (kRev && e) ++n;
             }
         }

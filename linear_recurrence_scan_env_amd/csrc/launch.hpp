@@ -414,7 +414,9 @@ lrs_status run(const char* name, int64_t N, int64_t T, const typename Op<4>::Arg
         if (!aligned(ws, 16)) return fail(LRS_ERR_WORKSPACE, "%s: workspace not 16-byte aligned", name);
     }
     bool vec = true;
-    for (int i = 0; i < nfloats; ++i) vec = vec && aligned(floats[i], 16);
+    // data streams: one vector access per lane covers E elements, at most 16 bytes
+    const uintptr_t data_align = (uintptr_t)(k.E * Op<4>::kElemBytes < 16 ? k.E * Op<4>::kElemBytes : 16);
+    for (int i = 0; i < nfloats; ++i) vec = vec && aligned(floats[i], data_align);
     for (int i = 0; i < nmasks; ++i) vec = vec && aligned(masks[i], (uintptr_t)k.E);
     s.vec = vec ? 1 : 0;
     const hipError_t e = launch_any<Op>(cfg, a, s, stream);
@@ -438,7 +440,7 @@ inline lrs_status check_common(const char* name, int64_t N, int64_t T)
 }
 
 inline lrs_status check_boundary(const char* name, const uint8_t* term, const uint8_t* trunc,
-                          const float* tv)
+                                 const void* tv)
 {
     if (term == nullptr) return fail(LRS_ERR_INVALID_ARG, "%s: terminateds is required", name);
     if (trunc != nullptr && tv == nullptr)

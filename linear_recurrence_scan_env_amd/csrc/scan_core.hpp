@@ -10,6 +10,8 @@
 // beyond it irrelevant (exactly, for finite values).
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -189,22 +191,90 @@ __device__ __forceinline__ bool vector_ok(const Pos<E, kFull>& P, bool vec)
     return kFull || (vec && P.count == E);
 }
 
-template <int E, bool kFull>
-__device__ __forceinline__ void load_f32(float (&v)[E], const float* __restrict__ p,
+// ------------------------------------------------------- element storage
+// Data streams are fp32, or 16-bit (bfloat16 or IEEE half) with fp32
+// arithmetic: loads widen exactly, stores round to nearest even (gfx950
+// converts a pair of floats in one instruction).  The 16-bit types are bit
+// containers; their values only ever exist as floats in registers.
+struct bf16_t {
+    uint16_t bits;
+};
+struct f16_t {
+    uint16_t bits;
+};
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+template <class D>
+constexpr bool kHalfWidth = sizeof(D) == 2;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float((uint32_t)x.bits << 16); }
+__device__ __forceinline__ float to_f32(f16_t x) { return (float)__builtin_bit_cast(_Float16, x.bits); }
+
+template <class D>
+__device__ __forceinline__ D from_f32(float x)
+{
+    if constexpr (std::is_same<D, float>::value) return x;
+    else if constexpr (std::is_same<D, bf16_t>::value) return D{__builtin_bit_cast(uint16_t, (__bf16)x)};
+    else return D{__builtin_bit_cast(uint16_t, (_Float16)x)};
+}
+
+// Two 16-bit values packed in a word (element 2k in the low half).
+template <class D>
+__device__ __forceinline__ void unpack2(uint32_t w, float& lo, float& hi)
+{
+    if constexpr (std::is_same<D, bf16_t>::value) {
+        lo = __uint_as_float(w << 16);
+        hi = __uint_as_float(w & 0xffff0000u);
+    } else {
+        const f16x2 h = __builtin_bit_cast(f16x2, w);
+        lo = (float)h.x;
+        hi = (float)h.y;
+    }
+}
+
+template <class D>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi)
+{
+    if constexpr (std::is_same<D, bf16_t>::value)
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
+}
+
+template <int E, bool kFull, class D>
+__device__ __forceinline__ void load_f32(float (&v)[E], const D* __restrict__ p,
                                          const Pos<E, kFull>& P, bool vec)
 {
     if (vector_ok(P, vec)) {
+        if constexpr (std::is_same<D, float>::value) {
 #pragma unroll
-        for (int k = 0; k < E / 4; ++k) {
-            const float4 q = *reinterpret_cast<const float4*>(p + P.i0 + 4 * k);
-            v[4 * k + 0] = q.x;
-            v[4 * k + 1] = q.y;
-            v[4 * k + 2] = q.z;
-            v[4 * k + 3] = q.w;
+            for (int k = 0; k < E / 4; ++k) {
+                const float4 q = *reinterpret_cast<const float4*>(p + P.i0 + 4 * k);
+                v[4 * k + 0] = q.x;
+                v[4 * k + 1] = q.y;
+                v[4 * k + 2] = q.z;
+                v[4 * k + 3] = q.w;
+            }
+        } else if constexpr (E == 4) {
+            const uint2 q = *reinterpret_cast<const uint2*>(p + P.i0);
+            unpack2<D>(q.x, v[0], v[1]);
+            unpack2<D>(q.y, v[2], v[3]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < E / 8; ++k) {
+                const uint4 q = *reinterpret_cast<const uint4*>(p + P.i0 + 8 * k);
+                unpack2<D>(q.x, v[8 * k + 0], v[8 * k + 1]);
+                unpack2<D>(q.y, v[8 * k + 2], v[8 * k + 3]);
+                unpack2<D>(q.z, v[8 * k + 4], v[8 * k + 5]);
+                unpack2<D>(q.w, v[8 * k + 6], v[8 * k + 7]);
+            }
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < E; ++j) v[j] = (j < P.count) ? p[P.i0 + j] : 0.0f;
+        for (int j = 0; j < E; ++j) v[j] = (j < P.count) ? to_f32(p[P.i0 + j]) : 0.0f;
     }
 }
 
@@ -266,19 +336,33 @@ __device__ __forceinline__ uint32_t load_mask(const uint8_t* __restrict__ p, con
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-template <int E, bool kFull>
-__device__ __forceinline__ void store_f32(float* __restrict__ p, const float (&v)[E],
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int E, bool kFull, class D>
+__device__ __forceinline__ void store_f32(D* __restrict__ p, const float (&v)[E],
                                           const Pos<E, kFull>& P, bool vec)
 {
     if (vector_ok(P, vec)) {
+        if constexpr (std::is_same<D, float>::value) {
 #pragma unroll
-        for (int k = 0; k < E / 4; ++k)
-            __builtin_nontemporal_store(f32x4{v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]},
-                                        reinterpret_cast<f32x4*>(p + P.i0 + 4 * k));
+            for (int k = 0; k < E / 4; ++k)
+                __builtin_nontemporal_store(f32x4{v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]},
+                                            reinterpret_cast<f32x4*>(p + P.i0 + 4 * k));
+        } else if constexpr (E == 4) {
+            __builtin_nontemporal_store(u32x2{pack2<D>(v[0], v[1]), pack2<D>(v[2], v[3])},
+                                        reinterpret_cast<u32x2*>(p + P.i0));
+        } else {
+#pragma unroll
+            for (int k = 0; k < E / 8; ++k)
+                __builtin_nontemporal_store(
+                    u32x4{pack2<D>(v[8 * k + 0], v[8 * k + 1]), pack2<D>(v[8 * k + 2], v[8 * k + 3]),
+                          pack2<D>(v[8 * k + 4], v[8 * k + 5]), pack2<D>(v[8 * k + 6], v[8 * k + 7])},
+                    reinterpret_cast<u32x4*>(p + P.i0 + 8 * k));
+        }
     } else {
 #pragma unroll
         for (int j = 0; j < E; ++j)
-            if (j < P.count) p[P.i0 + j] = v[j];
+            if (j < P.count) p[P.i0 + j] = from_f32<D>(v[j]);
     }
 }
 
