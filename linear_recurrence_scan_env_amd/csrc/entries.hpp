@@ -1,6 +1,8 @@
 // entries.hpp -- argument checks and launch of every estimator and of the
 // generic affine scan, for any element type D of the data streams (float,
-// bf16_t, f16_t).  The extern "C" functions of include/lrs.h are thin
+// bf16_t, f16_t).  Each call also states the largest beta its maps can hold
+// (gamma*lambda, gamma, gamma*lambda*c_bar, 1 for sums, unbounded for caller
+// coefficients), which sets the composition precision.  The extern "C" functions of include/lrs.h are thin
 // wrappers over these templates, one translation unit per group and type.
 #pragma once
 
@@ -54,8 +56,8 @@ lrs_status gae_entry(const char* nm, int64_t N, int64_t T, const D* rewards, con
     const void* f[] = {rewards, values, adv, tv};
     const void* m[] = {term, trunc};
     using S = GaeSel<D>;
-    return trunc ? run<S::template T>(nm, N, T, a, f, 4, m, 2, ws, ws_bytes, stream)
-                 : run<S::template N>(nm, N, T, a, f, 4, m, 2, ws, ws_bytes, stream);
+    return trunc ? run<S::template T>(nm, N, T, a.gl, a, f, 4, m, 2, ws, ws_bytes, stream)
+                 : run<S::template N>(nm, N, T, a.gl, a, f, 4, m, 2, ws, ws_bytes, stream);
 }
 
 template <class D>
@@ -77,8 +79,9 @@ lrs_status vtrace_entry(const char* nm, int64_t N, int64_t T, const D* log_rhos,
     const void* f[] = {log_rhos, rewards, values, vs, pg_adv, tv};
     const void* m[] = {term, trunc};
     using S = VtraceSel<D>;
-    return trunc ? run<S::template T>(nm, N, T, a, f, 6, m, 2, ws, ws_bytes, stream)
-                 : run<S::template N>(nm, N, T, a, f, 6, m, 2, ws, ws_bytes, stream);
+    const float beta_max = gamma * lambda * c_bar;  // beta_t = gamma * c_t <= this
+    return trunc ? run<S::template T>(nm, N, T, beta_max, a, f, 6, m, 2, ws, ws_bytes, stream)
+                 : run<S::template N>(nm, N, T, beta_max, a, f, 6, m, 2, ws, ws_bytes, stream);
 }
 
 template <class D>
@@ -99,8 +102,9 @@ lrs_status retrace_entry(const char* nm, int64_t N, int64_t T, const D* log_rhos
     const void* f[] = {log_rhos, rewards, q_values, values, q_ret, tv};
     const void* m[] = {term, trunc};
     using S = RetraceSel<D>;
-    return trunc ? run<S::template T>(nm, N, T, a, f, 6, m, 2, ws, ws_bytes, stream)
-                 : run<S::template N>(nm, N, T, a, f, 6, m, 2, ws, ws_bytes, stream);
+    const float beta_max = gamma * lambda * c_bar;  // beta_t = gamma * c_t <= this
+    return trunc ? run<S::template T>(nm, N, T, beta_max, a, f, 6, m, 2, ws, ws_bytes, stream)
+                 : run<S::template N>(nm, N, T, beta_max, a, f, 6, m, 2, ws, ws_bytes, stream);
 }
 
 template <class D>
@@ -119,8 +123,8 @@ lrs_status lambda_returns_entry(const char* nm, int64_t N, int64_t T, const D* r
     const void* f[] = {rewards, values, out, tv};
     const void* m[] = {term, trunc};
     using S = LambdaSel<D>;
-    return trunc ? run<S::template T>(nm, N, T, a, f, 4, m, 2, ws, ws_bytes, stream)
-                 : run<S::template N>(nm, N, T, a, f, 4, m, 2, ws, ws_bytes, stream);
+    return trunc ? run<S::template T>(nm, N, T, a.gl, a, f, 4, m, 2, ws, ws_bytes, stream)
+                 : run<S::template N>(nm, N, T, a.gl, a, f, 4, m, 2, ws, ws_bytes, stream);
 }
 
 template <class D>
@@ -137,8 +141,8 @@ lrs_status discounted_returns_entry(const char* nm, int64_t N, int64_t T, const 
     const void* f[] = {rewards, out, tv};
     const void* m[] = {term, trunc};
     using S = DiscSel<D>;
-    return trunc ? run<S::template T>(nm, N, T, a, f, 3, m, 2, ws, ws_bytes, stream)
-                 : run<S::template N>(nm, N, T, a, f, 3, m, 2, ws, ws_bytes, stream);
+    return trunc ? run<S::template T>(nm, N, T, gamma, a, f, 3, m, 2, ws, ws_bytes, stream)
+                 : run<S::template N>(nm, N, T, gamma, a, f, 3, m, 2, ws, ws_bytes, stream);
 }
 
 template <class D>
@@ -152,7 +156,7 @@ lrs_status eligibility_traces_entry(const char* nm, int64_t N, int64_t T, const 
     ForwardArgs a{x, dones, (float)((double)gamma * (double)lambda), out};
     const void* f[] = {x, out};
     const void* m[] = {dones};
-    return run<ForwardSel<D>::template Elig>(nm, N, T, a, f, 2, m, 1, ws, ws_bytes, stream);
+    return run<ForwardSel<D>::template Elig>(nm, N, T, a.gl, a, f, 2, m, 1, ws, ws_bytes, stream);
 }
 
 template <class D>
@@ -164,7 +168,7 @@ lrs_status prefix_sum_entry(const char* nm, int64_t N, int64_t T, const D* x, co
     ForwardArgs a{x, dones, 1.0f, out};
     const void* f[] = {x, out};
     const void* m[] = {dones};
-    return run<ForwardSel<D>::template Prefix>(nm, N, T, a, f, 2, m, 1, ws, ws_bytes, stream);
+    return run<ForwardSel<D>::template Prefix>(nm, N, T, 1.0f, a, f, 2, m, 1, ws, ws_bytes, stream);
 }
 
 inline lrs_status prefix_sum_i32_entry(const char* nm, int64_t N, int64_t T, const int32_t* x,
@@ -176,7 +180,7 @@ inline lrs_status prefix_sum_i32_entry(const char* nm, int64_t N, int64_t T, con
     ForwardArgs a{x, dones, 1.0f, out};
     const void* f[] = {x, out};
     const void* m[] = {dones};
-    return run<PrefixI32Op>(nm, N, T, a, f, 2, m, 1, ws, ws_bytes, stream);
+    return run<PrefixI32Op>(nm, N, T, 1.0f, a, f, 2, m, 1, ws, ws_bytes, stream);
 }
 
 template <class D>
@@ -191,11 +195,12 @@ lrs_status affine_scan_entry(const char* nm, int64_t N, int64_t T, const D* alph
     const void* f[] = {alpha, beta, out};
     const void* m[] = {reset};
     using S = AffineSel<D>;
+    const float beta_max = INFINITY;  // caller coefficients: no bound known
     if (reverse)
-        return reset ? run<S::template RevR>(nm, N, T, a, f, 3, m, 1, ws, ws_bytes, stream)
-                     : run<S::template RevN>(nm, N, T, a, f, 3, m, 1, ws, ws_bytes, stream);
-    return reset ? run<S::template FwdR>(nm, N, T, a, f, 3, m, 1, ws, ws_bytes, stream)
-                 : run<S::template FwdN>(nm, N, T, a, f, 3, m, 1, ws, ws_bytes, stream);
+        return reset ? run<S::template RevR>(nm, N, T, beta_max, a, f, 3, m, 1, ws, ws_bytes, stream)
+                     : run<S::template RevN>(nm, N, T, beta_max, a, f, 3, m, 1, ws, ws_bytes, stream);
+    return reset ? run<S::template FwdR>(nm, N, T, beta_max, a, f, 3, m, 1, ws, ws_bytes, stream)
+                 : run<S::template FwdN>(nm, N, T, beta_max, a, f, 3, m, 1, ws, ws_bytes, stream);
 }
 
 }  // namespace lrs

@@ -125,13 +125,12 @@ struct BlockShared {
 // Everything after the positions are known.  F: the tile lies wholly inside
 // the array and the base pointers are vector aligned (straight-line vector
 // loads and stores); otherwise every access is guarded by the lane's count.
-template <class Op, int E, int W, bool F>
+template <class Op, int E, int W, class A, bool F>
 __device__ __forceinline__ void tile_body(const typename Op::Args& args, const Sched& s,
                                           uint32_t tile, const Pos<E, F>& P, const Ctx& c,
-                                          BlockShared<typename AccOf<typename Op::T>::type, W>& sh)
+                                          BlockShared<A, W>& sh)
 {
-    using T = typename Op::T;
-    using A = typename AccOf<T>::type;  // composition type
+    using T = typename Op::T;  // A: the composition type (fp32 or fp64 for fp32 maps)
     constexpr bool kB = Op::kBackward;
     const int tid = threadIdx.x;
     const int lane = c.lane;
@@ -142,15 +141,29 @@ __device__ __forceinline__ void tile_body(const typename Op::Args& args, const S
     // The neighbour's record is read first, in flight with the tile's loads.
     const bool far_most = kB ? (tile == s.num_tiles - 1u) : (tile == 0u);
     Record early{{0, 0, 0, 0}};
-    if (s.lookback && !far_most && wave == 0) early = read_adjacent<kB>(rec, tile);
+    if (s.lookback && !far_most && wave == 0) early = read_adjacent<kB, A>(rec, tile);
 
     T alpha[E], beta[E];
     typename Op::State st;
     Op::prepare(args, P, c, alpha, beta, st);
 
-    // Lane aggregate, then the wave scan.
+    // Lane aggregate, then the wave scan.  fp32 maps keep a in fp32 but form
+    // the product of the lane's betas in fp64 and round it once: with a
+    // constant beta every lane would otherwise hold the same rounded beta^E,
+    // and the scan would multiply that one relative error once per lane of
+    // distance.
     Aff<A> agg = identity<A>();
-    if (kB) {
+    if constexpr (std::is_same<A, float>::value) {
+        float a = 0.0f;
+        double b = 1.0;
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+            const int j = kB ? E - 1 - k : k;
+            a = fmaf(beta[j], a, alpha[j]);
+            b *= (double)beta[j];
+        }
+        agg = {a, (float)b};
+    } else if (kB) {
 #pragma unroll
         for (int j = E - 1; j >= 0; --j) agg = combine(Aff<A>{A(alpha[j]), A(beta[j])}, agg);
     } else {
@@ -219,12 +232,12 @@ __device__ __forceinline__ void tile_body(const typename Op::Args& args, const S
     Op::finish(args, P, c, alpha, beta, st, lane_in);
 }
 
-template <class Op, int E, int W>
+template <class Op, int E, int W, class A>
 __global__ __launch_bounds__(W * kWave) void scan_kernel(const typename Op::Args args, const Sched s)
 {
     constexpr bool kB = Op::kBackward;
     constexpr uint32_t kTile = (uint32_t)E * kWave * W;
-    __shared__ BlockShared<typename AccOf<typename Op::T>::type, W> sh;
+    __shared__ BlockShared<A, W> sh;
 
     const int tid = threadIdx.x;
     // On the look-back path the tile a block depends on always belongs to a
@@ -271,11 +284,11 @@ __global__ __launch_bounds__(W * kWave) void scan_kernel(const typename Op::Args
 
     if (s.vec && tile_start + kTile <= s.total && s.T >= (uint32_t)E) {
         const Pos<E, true> P{i0, n0, E, last, first};
-        tile_body<Op, E, W, true>(args, s, tile, P, c, sh);
+        tile_body<Op, E, W, A, true>(args, s, tile, P, c, sh);
     } else {
         const uint32_t valid = (count >= 32) ? ~0u : ((1u << count) - 1u);
         const Pos<E, false> P{i0, n0, count, last & valid, first & valid};
-        tile_body<Op, E, W, false>(args, s, tile, P, c, sh);
+        tile_body<Op, E, W, A, false>(args, s, tile, P, c, sh);
     }
 }
 
@@ -294,6 +307,8 @@ constexpr uint32_t kNarrowMaxTile = 2048;  // ops without kWideTiles stop at 4x8
 constexpr uint64_t kWideMinTiles = 1024;   // whole-row tiles above 2048 need this many
 constexpr int kLookbackCfg = 3;            // 4x8: 2048-element tiles
 constexpr int64_t kPositionMajorRows = 1024;
+// Largest beta for which fp32 maps compose in fp32 (see run()).
+constexpr float kFp32BetaMax = 0.99f;
 
 // Defined in abi.hip.
 extern std::atomic<int> g_force_lookback;
@@ -352,32 +367,32 @@ inline int choose_cfg(uint64_t total, uint64_t T, bool wide_ok, bool* lookback)
 
 inline bool aligned(const void* p, uintptr_t a) { return p == nullptr || ((uintptr_t)p % a) == 0; }
 
-template <class Op, int E, int W>
+template <class Op, int E, int W, class A>
 hipError_t launch_cfg(const typename Op::Args& a, const Sched& s, hipStream_t stream)
 {
     void* kargs[] = {(void*)&a, (void*)&s};
-    return hipLaunchKernel((const void*)&scan_kernel<Op, E, W>, dim3(s.num_tiles), dim3(W * kWave),
+    return hipLaunchKernel((const void*)&scan_kernel<Op, E, W, A>, dim3(s.num_tiles), dim3(W * kWave),
                            kargs, 0, stream);
 }
 
-template <template <int> class Op>
+template <template <int> class Op, class A>
 hipError_t launch_any(int cfg, const typename Op<4>::Args& a, const Sched& s, hipStream_t stream)
 {
     switch (cfg) {
-        case 0: return launch_cfg<Op<4>, 4, 1>(a, s, stream);
-        case 1: return launch_cfg<Op<4>, 4, 4>(a, s, stream);
-        case 2: return launch_cfg<Op<8>, 8, 4>(a, s, stream);
-        case 3: return launch_cfg<Op<4>, 4, 8>(a, s, stream);
-        case 4: return launch_cfg<Op<16>, 16, 4>(a, s, stream);
-        case 5: return launch_cfg<Op<4>, 4, 16>(a, s, stream);
-        default: return launch_cfg<Op<8>, 8, 16>(a, s, stream);
+        case 0: return launch_cfg<Op<4>, 4, 1, A>(a, s, stream);
+        case 1: return launch_cfg<Op<4>, 4, 4, A>(a, s, stream);
+        case 2: return launch_cfg<Op<8>, 8, 4, A>(a, s, stream);
+        case 3: return launch_cfg<Op<4>, 4, 8, A>(a, s, stream);
+        case 4: return launch_cfg<Op<16>, 16, 4, A>(a, s, stream);
+        case 5: return launch_cfg<Op<4>, 4, 16, A>(a, s, stream);
+        default: return launch_cfg<Op<8>, 8, 16, A>(a, s, stream);
     }
 }
 
 // Shared checks and launch.  floats/masks: every array the kernel may
 // vector-load, for the alignment decision.
 template <template <int> class Op>
-lrs_status run(const char* name, int64_t N, int64_t T, const typename Op<4>::Args& a,
+lrs_status run(const char* name, int64_t N, int64_t T, float beta_max, const typename Op<4>::Args& a,
                const void* const* floats, int nfloats, const void* const* masks, int nmasks,
                void* ws, size_t ws_bytes, hipStream_t stream)
 {
@@ -419,7 +434,16 @@ lrs_status run(const char* name, int64_t N, int64_t T, const typename Op<4>::Arg
     for (int i = 0; i < nfloats; ++i) vec = vec && aligned(floats[i], data_align);
     for (int i = 0; i < nmasks; ++i) vec = vec && aligned(masks[i], (uintptr_t)k.E);
     s.vec = vec ? 1 : 0;
-    const hipError_t e = launch_any<Op>(cfg, a, s, stream);
+    // fp32 maps compose in fp64 when the call's betas may come close to 1:
+    // long near-undamped chains (sums) accumulate fp32 rounding beyond the
+    // parity bound, while damped chains forget it within ~1/(1 - beta) steps.
+    using Val = typename Op<4>::T;
+    hipError_t e;
+    if constexpr (std::is_same<Val, float>::value)
+        e = beta_max > kFp32BetaMax ? launch_any<Op, double>(cfg, a, s, stream)
+                                    : launch_any<Op, float>(cfg, a, s, stream);
+    else
+        e = launch_any<Op, Val>(cfg, a, s, stream);
     if (e != hipSuccess)
         return fail(LRS_ERR_HIP, "%s: kernel launch failed: %s", name, hipGetErrorString(e));
     g_err[0] = '\0';

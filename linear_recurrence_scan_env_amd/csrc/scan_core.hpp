@@ -47,16 +47,14 @@ __device__ __forceinline__ uint32_t apply(Aff<uint32_t> f, uint32_t x) { return 
 template <class T>
 __device__ __forceinline__ Aff<T> identity() { return {T(0), T(1)}; }
 
-// Maps are composed in AccOf<T>: fp32 coefficients are composed in fp64, so
-// the products of many beta values across lanes, waves and tiles carry no
-// accumulated fp32 rounding; integer maps stay exact in uint32.
+// Maps are composed in AccOf<T>: fp32 maps in fp32 and integer maps exactly
+// in uint32.  The one fp32 composition that needs more precision is a lane's
+// own product of betas (see lane_aggregate in the kernel): a constant beta
+// makes that product, and its rounding, the same in every lane, and the
+// scan would multiply the same relative error once per lane of distance.
 template <class T>
 struct AccOf {
     using type = T;
-};
-template <>
-struct AccOf<float> {
-    using type = double;
 };
 
 // ------------------------------------------------------- lane exchange
@@ -437,7 +435,12 @@ __device__ __forceinline__ void st_agent(uint64_t* p, uint64_t v)
 
 constexpr uint32_t kRecordWords = 4;
 
+// 32-bit aggregates fill two words of a record, 64-bit ones all four.
+template <class A>
+constexpr uint32_t kWordsOf = sizeof(A) == 8 ? 4u : 2u;
+
 __device__ __forceinline__ uint64_t payload_bits(double x) { return __builtin_bit_cast(uint64_t, x); }
+__device__ __forceinline__ uint64_t payload_bits(float x) { return __builtin_bit_cast(uint32_t, x); }
 __device__ __forceinline__ uint64_t payload_bits(uint32_t x) { return x; }
 template <class A>
 __device__ __forceinline__ A from_payload(uint32_t lo, uint32_t hi);
@@ -445,6 +448,11 @@ template <>
 __device__ __forceinline__ double from_payload<double>(uint32_t lo, uint32_t hi)
 {
     return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+template <>
+__device__ __forceinline__ float from_payload<float>(uint32_t lo, uint32_t)
+{
+    return __builtin_bit_cast(float, lo);
 }
 template <>
 __device__ __forceinline__ uint32_t from_payload<uint32_t>(uint32_t lo, uint32_t)
@@ -459,10 +467,15 @@ __device__ __forceinline__ void publish_aggregate(uint64_t* rec, uint32_t tile, 
     const uint64_t t = (uint64_t)tag << 32;
     const uint64_t a = payload_bits(agg.a), b = payload_bits(agg.b);
     uint64_t* r = rec + kRecordWords * (uint64_t)tile;
-    st_agent(r + 0, t | (a & 0xffffffffu));
-    st_agent(r + 1, t | (a >> 32));
-    st_agent(r + 2, t | (b & 0xffffffffu));
-    st_agent(r + 3, t | (b >> 32));
+    if constexpr (kWordsOf<A> == 4) {
+        st_agent(r + 0, t | (a & 0xffffffffu));
+        st_agent(r + 1, t | (a >> 32));
+        st_agent(r + 2, t | (b & 0xffffffffu));
+        st_agent(r + 3, t | (b >> 32));
+    } else {
+        st_agent(r + 0, t | a);
+        st_agent(r + 1, t | b);
+    }
 }
 
 // One tile's record as read (possibly stale).
@@ -470,31 +483,41 @@ struct Record {
     uint64_t w[kRecordWords];
 };
 
+template <class A>
 __device__ __forceinline__ Record read_record(const uint64_t* rec, uint64_t tile)
 {
     const uint64_t* r = rec + kRecordWords * tile;
-    return {{ld_agent(r + 0), ld_agent(r + 1), ld_agent(r + 2), ld_agent(r + 3)}};
+    if constexpr (kWordsOf<A> == 4)
+        return {{ld_agent(r + 0), ld_agent(r + 1), ld_agent(r + 2), ld_agent(r + 3)}};
+    else
+        return {{ld_agent(r + 0), ld_agent(r + 1), 0, 0}};
 }
 
+template <class A>
 __device__ __forceinline__ bool record_current(const Record& x, uint32_t tag)
 {
-    return (uint32_t)(x.w[0] >> 32) == tag && (uint32_t)(x.w[1] >> 32) == tag &&
-           (uint32_t)(x.w[2] >> 32) == tag && (uint32_t)(x.w[3] >> 32) == tag;
+    bool ok = (uint32_t)(x.w[0] >> 32) == tag && (uint32_t)(x.w[1] >> 32) == tag;
+    if constexpr (kWordsOf<A> == 4)
+        ok = ok && (uint32_t)(x.w[2] >> 32) == tag && (uint32_t)(x.w[3] >> 32) == tag;
+    return ok;
 }
 
 template <class A>
 __device__ __forceinline__ Aff<A> record_value(const Record& x)
 {
-    return {from_payload<A>((uint32_t)x.w[0], (uint32_t)x.w[1]),
-            from_payload<A>((uint32_t)x.w[2], (uint32_t)x.w[3])};
+    if constexpr (kWordsOf<A> == 4)
+        return {from_payload<A>((uint32_t)x.w[0], (uint32_t)x.w[1]),
+                from_payload<A>((uint32_t)x.w[2], (uint32_t)x.w[3])};
+    else
+        return {from_payload<A>((uint32_t)x.w[0], 0u), from_payload<A>((uint32_t)x.w[1], 0u)};
 }
 
 // The adjacent tile's record, read as early as possible (issued with the
 // tile's own loads); lookback_carry() re-polls it only if this copy is stale.
-template <bool kBackward>
+template <bool kBackward, class A>
 __device__ __forceinline__ Record read_adjacent(const uint64_t* rec, uint32_t tile)
 {
-    return read_record(rec, kBackward ? (uint64_t)tile + 1 : (uint64_t)tile - 1);
+    return read_record<A>(rec, kBackward ? (uint64_t)tile + 1 : (uint64_t)tile - 1);
 }
 
 // Executed by one full wave.  Returns the value entering `tile` from its far
@@ -516,8 +539,8 @@ __device__ A lookback_carry(const uint64_t* rec, uint32_t tile, uint32_t num_til
     {
         const uint64_t j = kBackward ? (uint64_t)tile + 1 : (uint64_t)tile - 1;
         for (bool first = true;; first = false) {
-            const Record x = first ? early : read_record(rec, j);
-            if (record_current(x, tag)) {
+            const Record x = first ? early : read_record<A>(rec, j);
+            if (record_current<A>(x, tag)) {
                 const Aff<A> v = record_value<A>(x);
                 if (v.b == A(0)) return v.a;
                 break;  // the segment continues past it: full look-back below
@@ -543,8 +566,8 @@ __device__ A lookback_carry(const uint64_t* rec, uint32_t tile, uint32_t num_til
         bool have = !exists;
         for (;;) {
             if (!have) {
-                const Record x = read_record(rec, (uint64_t)j);
-                if (record_current(x, tag)) {
+                const Record x = read_record<A>(rec, (uint64_t)j);
+                if (record_current<A>(x, tag)) {
                     have = true;
                     v = record_value<A>(x);
                 }

@@ -147,6 +147,29 @@ def test_long_odd_rows(est):
     check(run_pair(est, ro, trunc=est == "gae"), T)
 
 
+@pytest.mark.parametrize("g,lam", [(0.99, 1.0), (1.0, 0.99), (1.0, 0.995), (0.995, 1.0)],
+                         ids=["beta0.99-fp32", "beta0.99b-fp32", "beta0.995-fp64",
+                              "beta0.995b-fp64"])
+@pytest.mark.parametrize("est", ["gae", "lambda_returns", "discounted_returns",
+                                 "eligibility_traces", "vtrace", "retrace"])
+def test_composition_precision_edges(est, g, lam):
+    """Rows of 4096 with rare cuts and real-valued inputs, for betas just at
+    the largest that composes in fp32 (0.99) and just above it (fp64
+    composition), under forced look-back on small tiles so that every carry
+    crosses many tiles.  One of gamma, lambda is 1, so gamma*lambda is exact
+    in fp32 and only the scan's own rounding is measured: a gamma*lambda
+    that fp32 cannot hold shifts every step's beta by the same rounding,
+    which grows like eps / (1 - beta) in any fp32 evaluation."""
+    N, T = 16, 4096
+    ro = workloads.rollout(N, T, seed=61, term_p=2e-4, trunc_p=2e-4, gamma=g, lambda_=lam,
+                           done_p=2e-4)
+    lrs.set_schedule(True, 4, 1)
+    try:
+        check(run_pair(est, ro), T)
+    finally:
+        lrs.set_schedule(False, 0, 0)
+
+
 @pytest.mark.parametrize("est", ESTIMATORS)
 def test_long_chains_gamma_lambda_one(est):
     """gamma = lambda = 1, no cuts: carries cross every tile of a row."""
