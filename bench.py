@@ -55,10 +55,13 @@ WORKLOADS = {
     # the same calls with bfloat16 storage of every floating-point stream
     "all7_4096x128_bf16": [(e, tr, 4096, 128) for e, tr in ALL7],
     "long_64x131072_bf16": [(e, True, 64, 131072) for e in ("gae", "vtrace", "retrace")],
+    "sweep_4096xT_bf16": [(e, False, 4096, t) for t in (32, 128, 512, 2048, 8192)
+                          for e in ("discounted_returns", "lambda_returns", "eligibility_traces")],
 }
 # storage type of the floating-point streams (fp32 unless listed); arithmetic is fp32 throughout
-STORAGE = {"all7_4096x128_bf16": "bf16", "long_64x131072_bf16": "bf16"}
-BASE_WORKLOAD = {"all7_4096x128_bf16": "all7_4096x128", "long_64x131072_bf16": "long_64x131072"}
+STORAGE = {"all7_4096x128_bf16": "bf16", "long_64x131072_bf16": "bf16", "sweep_4096xT_bf16": "bf16"}
+BASE_WORKLOAD = {"all7_4096x128_bf16": "all7_4096x128", "long_64x131072_bf16": "long_64x131072",
+                 "sweep_4096xT_bf16": "sweep_4096xT"}
 DEFAULT_WORKLOAD = "all7_4096x128"
 # input streams each estimator reads
 NEEDS = {
@@ -195,28 +198,33 @@ CALIBRATION_BYTES = 64 << 20  # one --calibrate-copy dispatch reads and writes t
 
 
 def source_hash():
-    """sha256 of the kernel sources: counters taken on other sources are stale."""
+    """sha256 of the kernel sources (csrc/): counters taken on other sources are stale."""
     import hashlib
     h = hashlib.sha256()
     pkg = os.path.join(ROOT, "linear_recurrence_scan_env_amd", "csrc")
-    for f in sorted(os.listdir(pkg)) + ["../../include/lrs.h"]:
-        with open(os.path.join(pkg, f), "rb") as fh:
-            h.update(fh.read())
+    for f in sorted(os.listdir(pkg)):
+        if f.endswith((".hip", ".hpp")):
+            with open(os.path.join(pkg, f), "rb") as fh:
+                h.update(fh.read())
     return h.hexdigest()
 
 
 def call_of_kernel(name):
-    """Map a demangled kernel name to a bench call key."""
+    """Map a demangled kernel name (scan_kernel<Op<E, ...>, E, W, Acc>) to a bench call key."""
+    import re
     ops = {"GaeOp": "gae", "VtraceOp": "vtrace", "RetraceOp": "retrace",
            "LambdaOp": "lambda_returns", "DiscOp": "discounted_returns",
            "EligOp": "eligibility_traces", "PrefixF32Op": "prefix_sum_f32",
            "PrefixI32Op": "prefix_sum_i32"}
-    for op, est in ops.items():
-        if f"lrs::{op}<" in name:
-            return key(est, ", true>" in name.split(op, 1)[1][:12])
-    if "lrs::AffineOp<" in name:
-        rev = name.split("AffineOp<", 1)[1].split(",")[1].strip()
-        return "affine_rev" if rev == "true" else "affine_fwd"
+    m = re.search(r"lrs::(\w+Op)<([^<>]*)>", name)
+    if not m:
+        return None
+    op, args = m.group(1), [a.strip() for a in m.group(2).split(",")]
+    if op in ops:
+        trunc = op in ("GaeOp", "VtraceOp", "RetraceOp", "LambdaOp", "DiscOp") and args[1] == "true"
+        return key(ops[op], trunc)
+    if op == "AffineOp":
+        return "affine_rev" if args[1] == "true" else "affine_fwd"
     return None
 
 

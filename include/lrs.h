@@ -35,6 +35,13 @@
  *     masks take the vectorised fast path.
  *   - Outputs must not overlap any input or each other.
  *   - All float inputs must be finite.
+ *   - Precision: coefficients and each lane's recursion are fp32; maps are
+ *     composed across lanes, waves and tiles in fp32 with every lane's own
+ *     product of betas formed in fp64, or wholly in fp64 when the call's
+ *     betas may exceed 0.99 (sums, gamma or lambda of 1, large c_bar, and
+ *     caller coefficients of lrs_affine_scan_*), where long undamped chains
+ *     would accumulate fp32 rounding.  gamma*lambda (and similar products of
+ *     scalars) are rounded to fp32 once, as fp32 coefficients.
  *   - gamma and lambda must lie in [0, 1].  Clip thresholds must be > 0;
  *     +INFINITY means "no clip".
  *   - workspace: caller-owned device memory of at least
@@ -241,10 +248,11 @@ lrs_status lrs_affine_scan_f32(int64_t num_envs, int64_t seq_len,
  * the same name; every floating-point stream -- the per-step inputs,
  * trunc_values, bootstrap_value, carry_in and every output -- is 16-bit,
  * while masks stay uint8 and the scalars (gamma, lambda, clips) stay float.
- * Arithmetic is fp32 (and the cross-tile composition fp64) exactly as in
- * the _f32 calls: inputs widen exactly, each output is rounded once to
- * nearest even, so it lies within half a 16-bit ulp of the fp32 result.
- * Halving the bytes per element halves the time of these HBM-bound calls.
+ * Arithmetic is exactly that of the _f32 calls: inputs widen exactly and
+ * each output is rounded once to nearest even, so on the same tile schedule
+ * it is the fp32 result rounded (the schedule, chosen from the shape and the
+ * storage type, may differ from the _f32 call's and move the last fp32 bits).
+ * Fewer bytes per element make these HBM-bound calls faster.
  * The pages serve standard formats only (gist.science summary, closing
  * limitations paragraph of its plain-language part); this storage option is
  * this library's extension of the same recurrences.  The vector fast path

@@ -306,6 +306,9 @@ constexpr int kAlignedCfgs[5] = {0, 1, 3, 5, 6};  // 4x1, 4x4, 4x8, 4x16, 8x16
 constexpr uint32_t kNarrowMaxTile = 2048;  // ops without kWideTiles stop at 4x8
 constexpr uint64_t kWideMinTiles = 1024;   // whole-row tiles above 2048 need this many
 constexpr int kLookbackCfg = 3;            // 4x8: 2048-element tiles
+// 16-bit data: eight elements per lane make each data load 16 bytes
+constexpr int kLookbackCfgHalfWide = 6;    // 8x16: 8192-element tiles (ops with kWideTiles)
+constexpr int kLookbackCfgHalf = 2;        // 8x4: 2048-element tiles
 constexpr int64_t kPositionMajorRows = 1024;
 // Largest beta for which fp32 maps compose in fp32 (see run()).
 constexpr float kFp32BetaMax = 0.99f;
@@ -341,9 +344,13 @@ inline size_t workspace_bytes_for(uint64_t total)
 // look-back, so: the smallest tile that holds whole rows, among 256, 1024
 // and 2048 elements (4 per lane) and, for ops whose registers allow it and
 // when at least kWideMinTiles such tiles fill the chip, 4096 (4 per lane,
-// 16 waves) and 8192 (8 per lane, 16 waves); otherwise the look-back path
-// on 2048-element tiles of eight waves.
-inline int choose_cfg(uint64_t total, uint64_t T, bool wide_ok, bool* lookback)
+// 16 waves) and 8192 (8 per lane, 16 waves).  Otherwise the look-back path:
+// fp32 data on 2048-element tiles of eight waves; 16-bit data on eight
+// elements per lane (16-byte loads), in 8192-element tiles for ops with
+// kWideTiles when at least kWideMinTiles of them fill the chip, else in
+// 2048-element tiles of four waves.  16-bit rows that divide 2048 also take
+// those 2048-element tiles when at least kWideMinTiles of them fill the chip.
+inline int choose_cfg(uint64_t total, uint64_t T, bool wide_ok, int elem_bytes, bool* lookback)
 {
     const int forced = g_forced_cfg.load();
     const bool force_lb = g_force_lookback.load() != 0;
@@ -352,6 +359,15 @@ inline int choose_cfg(uint64_t total, uint64_t T, bool wide_ok, bool* lookback)
         const uint64_t tiles = (total + kCfgs[c].tile() - 1) / kCfgs[c].tile();
         *lookback = force_lb || (tiles > 1 && kCfgs[c].tile() % T != 0);
         return c;
+    }
+    if (elem_bytes == 2) {
+        // 16-bit rows that fit 2048-element tiles: eight elements per lane
+        // (16-byte loads) when enough such tiles fill the chip
+        const Cfg& h = kCfgs[kLookbackCfgHalf];
+        if (h.tile() % T == 0 && (total + h.tile() - 1) / h.tile() >= kWideMinTiles) {
+            *lookback = false;
+            return kLookbackCfgHalf;
+        }
     }
     for (int c : kAlignedCfgs) {
         const uint64_t tiles = (total + kCfgs[c].tile() - 1) / kCfgs[c].tile();
@@ -362,6 +378,11 @@ inline int choose_cfg(uint64_t total, uint64_t T, bool wide_ok, bool* lookback)
         }
     }
     *lookback = true;
+    if (elem_bytes == 2) {
+        const uint64_t wide_tiles = (total + kCfgs[kLookbackCfgHalfWide].tile() - 1) /
+                                    kCfgs[kLookbackCfgHalfWide].tile();
+        return wide_ok && wide_tiles >= kWideMinTiles ? kLookbackCfgHalfWide : kLookbackCfgHalf;
+    }
     return kLookbackCfg;
 }
 
@@ -398,7 +419,7 @@ lrs_status run(const char* name, int64_t N, int64_t T, float beta_max, const typ
 {
     const uint64_t total = (uint64_t)N * (uint64_t)T;
     bool lookback = false;
-    const int cfg = choose_cfg(total, (uint64_t)T, Op<4>::kWideTiles, &lookback);
+    const int cfg = choose_cfg(total, (uint64_t)T, Op<4>::kWideTiles, Op<4>::kElemBytes, &lookback);
     const Cfg& k = kCfgs[cfg];
     Sched s{};
     s.total = total;

@@ -13,9 +13,11 @@ the other parity tests (1e-5 for seq_len <= 4096, else 1e-4).  The fp32 result
 is within tol32 * (1 + |ref|) of ref, and rounding it to 16 bits adds at most
 u times its magnitude.
 
-The kernels run the same fp32 arithmetic for every storage type, so each
-16-bit output must also equal the fp32 entry point's output (on the same
-widened inputs) rounded to nearest even -- checked bit for bit.
+The kernels run the same fp32 arithmetic for every storage type, so on one
+tile schedule each 16-bit output must also equal the fp32 entry point's
+output (on the same widened inputs) rounded to nearest even -- checked bit
+for bit.  (The automatic schedule may pick different tiles for 16-bit data,
+which changes the association order and so the last bits.)
 """
 import numpy as np
 import pytest
@@ -111,15 +113,27 @@ def check(got16, ref, u, T):
     assert worst <= 0.0, f"bound exceeded by {worst:.3e} at {np.unravel_index(excess.argmax(), excess.shape)}"
 
 
-def run_case(est, ro, dtname, trunc=True):
+def run_case(est, ro, dtname, trunc=True, same_tile=(4, 8)):
+    """Oracle bound on the automatic schedule (which may pick a different tile
+    for 16-bit data than for fp32); the bit-exact comparison with the fp32
+    entry point runs both on one tile, `same_tile` (None: the schedule the
+    caller has already forced)."""
     dt, u = DTYPES[dtname]
     host, d16, d32 = rounded(ro, dt)
     outs16 = call(est, d16, ro.gamma, ro.lambda_, trunc)
-    outs32 = call(est, d32, ro.gamma, ro.lambda_, trunc)
     refs = reference(est, host, ro.gamma, ro.lambda_, trunc)
-    for o16, o32, ref in zip(outs16, outs32, refs):
+    for o16, ref in zip(outs16, refs):
         assert o16.dtype == dt
         check(o16, ref, u, ro.seq_len)
+    if same_tile is not None:
+        lrs.set_schedule(False, *same_tile)
+    try:
+        pair16 = call(est, d16, ro.gamma, ro.lambda_, trunc)
+        pair32 = call(est, d32, ro.gamma, ro.lambda_, trunc)
+    finally:
+        if same_tile is not None:
+            lrs.set_schedule(False, 0, 0)
+    for o16, o32 in zip(pair16, pair32):
         assert torch.equal(o16, o32.to(dt)), "16-bit output is not the fp32 result rounded once"
 
 
@@ -145,7 +159,7 @@ def test_forced_lookback(tile, est, dtname):
     ro = workloads.rollout(N, T, seed=31, term_p=0.002, trunc_p=0.002, gamma=0.99, lambda_=0.97)
     lrs.set_schedule(True, *tile)
     try:
-        run_case(est, ro, dtname)
+        run_case(est, ro, dtname, same_tile=None)
     finally:
         lrs.set_schedule(False, 0, 0)
 
@@ -159,13 +173,19 @@ def test_affine_scan(reverse, dtname):
     t16 = {k: torch.from_numpy(inp[k]).to(dt) for k in ("alpha", "beta", "carry_in")}
     host = {k: v.float().numpy() for k, v in t16.items()}
     R = torch.from_numpy(inp["reset"]).cuda()
-    y16 = lrs.compute_affine_scan(t16["alpha"].cuda(), t16["beta"].cuda(), reset=R,
-                                  carry_in=t16["carry_in"].cuda(), reverse=reverse)
-    y32 = lrs.compute_affine_scan(t16["alpha"].float().cuda(), t16["beta"].float().cuda(),
-                                  reset=R, carry_in=t16["carry_in"].float().cuda(), reverse=reverse)
+    def scan(x):
+        return lrs.compute_affine_scan(x["alpha"], x["beta"], reset=R, carry_in=x["carry_in"],
+                                       reverse=reverse)
+    d16 = {k: v.cuda() for k, v in t16.items()}
+    d32 = {k: v.float().cuda() for k, v in t16.items()}
     ref = oracle.affine_scan(host["alpha"], host["beta"], reset=inp["reset"],
                              carry_in=host["carry_in"], reverse=reverse)
-    check(y16, ref, u, T)
+    check(scan(d16), ref, u, T)
+    lrs.set_schedule(False, 4, 8)
+    try:
+        y16, y32 = scan(d16), scan(d32)
+    finally:
+        lrs.set_schedule(False, 0, 0)
     assert torch.equal(y16, y32.to(dt))
 
 
