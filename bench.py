@@ -57,11 +57,18 @@ WORKLOADS = {
     "long_64x131072_bf16": [(e, True, 64, 131072) for e in ("gae", "vtrace", "retrace")],
     "sweep_4096xT_bf16": [(e, False, 4096, t) for t in (32, 128, 512, 2048, 8192)
                           for e in ("discounted_returns", "lambda_returns", "eligibility_traces")],
+    # the same calls on time-major [seq_len, num_envs] arrays
+    "all7_4096x128_tm": [(e, tr, 4096, 128) for e, tr in ALL7],
+    "sweep_4096xT_tm": [(e, False, 4096, t) for t in (32, 128, 512, 2048, 8192)
+                        for e in ("discounted_returns", "lambda_returns", "eligibility_traces")],
 }
+# workloads on time-major arrays
+TIME_MAJOR = {"all7_4096x128_tm", "sweep_4096xT_tm"}
 # storage type of the floating-point streams (fp32 unless listed); arithmetic is fp32 throughout
 STORAGE = {"all7_4096x128_bf16": "bf16", "long_64x131072_bf16": "bf16", "sweep_4096xT_bf16": "bf16"}
 BASE_WORKLOAD = {"all7_4096x128_bf16": "all7_4096x128", "long_64x131072_bf16": "long_64x131072",
-                 "sweep_4096xT_bf16": "sweep_4096xT"}
+                 "sweep_4096xT_bf16": "sweep_4096xT", "all7_4096x128_tm": "all7_4096x128",
+                 "sweep_4096xT_tm": "sweep_4096xT"}
 DEFAULT_WORKLOAD = "all7_4096x128"
 # input streams each estimator reads
 NEEDS = {
@@ -103,10 +110,10 @@ def alg_bytes(est, trunc, n, t, width=4):
     return b
 
 
-def make_call(lrs, est, trunc, D, O, g, lam):
+def make_call(lrs, est, trunc, D, O, g, lam, tm=False):
     kg = dict(truncateds=D["truncateds"] if trunc else None,
               trunc_values=D["trunc_values"] if trunc else None,
-              bootstrap_value=D.get("bootstrap_value"))
+              bootstrap_value=D.get("bootstrap_value"), time_major=tm)
     k = key(est, trunc)
     if est == "gae":
         return lambda: lrs.compute_gae(D["rewards"], D["values"], D["terminateds"], g, lam,
@@ -125,15 +132,18 @@ def make_call(lrs, est, trunc, D, O, g, lam):
         return lambda: lrs.compute_discounted_returns(D["rewards"], D["terminateds"], g, out=O[k],
                                                       **kg)
     if est == "eligibility_traces":
-        return lambda: lrs.compute_eligibility_traces(D["x"], D["dones"], g, lam, out=O[k])
+        return lambda: lrs.compute_eligibility_traces(D["x"], D["dones"], g, lam, out=O[k],
+                                                      time_major=tm)
     if est == "prefix_sum_f32":
-        return lambda: lrs.compute_episodic_prefix_sum(D["x"], D["dones"], out=O[k])
+        return lambda: lrs.compute_episodic_prefix_sum(D["x"], D["dones"], out=O[k], time_major=tm)
     if est == "prefix_sum_i32":
-        return lambda: lrs.compute_episodic_prefix_sum(D["x_int"], D["dones"], out=O[k])
+        return lambda: lrs.compute_episodic_prefix_sum(D["x_int"], D["dones"], out=O[k],
+                                                       time_major=tm)
     if est in ("affine_fwd", "affine_rev"):
         return lambda: lrs.compute_affine_scan(D["alpha"], D["beta"], reset=D.get("reset"),
                                                carry_in=D.get("carry_in"),
-                                               reverse=est == "affine_rev", out=O[k])
+                                               reverse=est == "affine_rev", out=O[k],
+                                               time_major=tm)
     raise KeyError(est)
 
 
@@ -391,6 +401,12 @@ def main():
             for k, v in h.items():
                 if v.dtype == torch.float32:
                     h[k] = v.to(store_dt)
+    tm = name in TIME_MAJOR
+    if tm:  # per-step arrays as [seq_len, num_envs]
+        for h in hosts.values():
+            for k, v in h.items():
+                if v.dim() == 2:
+                    h[k] = v.t().contiguous()
 
     # Replicas per shape: enough copies of that shape's inputs and outputs
     # for >= 1 GiB, so that each call reads cold data however small it is.
@@ -415,14 +431,15 @@ def main():
                 if (n, t) != s_:
                     continue
                 dt = torch.int32 if e == "prefix_sum_i32" else store_dt
-                O[key(e, tr)] = torch.empty(n, t, device=dev, dtype=dt)
+                oshape = (t, n) if tm else (n, t)
+                O[key(e, tr)] = torch.empty(oshape, device=dev, dtype=dt)
                 if e == "vtrace":
-                    O[key(e, tr) + "/pg"] = torch.empty(n, t, device=dev, dtype=dt)
+                    O[key(e, tr) + "/pg"] = torch.empty(oshape, device=dev, dtype=dt)
             store[(s_, i)] = (D, O)
 
     def fn(e, tr, n, t, i):
         D, O = store[((n, t), i % nrep[(n, t)])]
-        return make_call(lrs, e, tr, D, O, g, lam)
+        return make_call(lrs, e, tr, D, O, g, lam, tm)
 
     def step_fns(i):
         return [fn(e, tr, n, t, i) for e, tr, n, t in calls]
@@ -498,7 +515,8 @@ def main():
     cfg = {"workload": name, "calls_per_step": len(calls),
            "cache": "warm" if args.warm else "cold",
            "replicas": {f"{n}x{t}": nrep[(n, t)] for n, t in shapes},
-           "launch": "hip graph per step", "storage": storage}
+           "launch": "hip graph per step", "storage": storage,
+           "layout": "time-major [seq_len, num_envs]" if tm else "row-major [num_envs, seq_len]"}
     if len(shapes) == 1:
         cfg.update(num_envs=shapes[0][0], seq_len=shapes[0][1])
     else:

@@ -103,9 +103,10 @@ const char* lrs_status_string(lrs_status s);
 const char* lrs_last_error(void);
 
 /* Bytes of workspace a call of `est` (an estimator, or LRS_AFFINE_SCAN) at
- * [num_envs, seq_len] may need:
- * 4224 bytes plus 32 bytes per 256 elements (about 3% of one fp32 array).  The
- * same workspace serves every estimator at this or any smaller size.
+ * [num_envs, seq_len] may need, in either layout:
+ * 4224 bytes plus the larger of 32 bytes per 256 elements (about 3% of one
+ * fp32 array) and 16 bytes per env per 128 steps.  The same workspace serves
+ * every estimator and layout at this or any smaller size.
  * Returns 0 for invalid sizes. */
 size_t lrs_workspace_bytes(lrs_estimator est, int64_t num_envs, int64_t seq_len);
 
@@ -354,6 +355,171 @@ lrs_status lrs_affine_scan_f16(int64_t num_envs, int64_t seq_len,
                                 const uint8_t* reset, const lrs_f16* carry_in, int reverse,
                                 lrs_f16* y,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Time-major variants (_tm_): every call above, for each storage type, with
+ * the per-step arrays laid out [seq_len, num_envs] -- row = time step,
+ * element (n, t) at t * num_envs + n, rows contiguous -- the layout of
+ * rollout buffers filled one step at a time.  Per-env arrays
+ * (bootstrap_value, carry_in) stay [num_envs].  Same operation, arguments,
+ * limits, precision and errors as the call of the same name (num_envs must
+ * also be below 2^32); results equal that call's on the transposed arrays
+ * up to fp32 re-association, bit for bit for the int32 prefix sum.  The
+ * pages fix the [num_envs, seq_len] layout (README Usage); this layout is
+ * this library's extension.  A lane owns one environment (loads coalesce
+ * across environments) and tiles of 128 steps pass carries along time; no
+ * alignment beyond the element size is needed.  The workspace from
+ * lrs_workspace_bytes covers both layouts.                               */
+lrs_status lrs_gae_tm_f32(int64_t num_envs, int64_t seq_len,
+                           const float* rewards, const float* values,
+                           const uint8_t* terminateds, const uint8_t* truncateds,
+                           const float* trunc_values, const float* bootstrap_value,
+                           float gamma, float lambda, float* advantages,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+lrs_status lrs_vtrace_tm_f32(int64_t num_envs, int64_t seq_len,
+                              const float* log_rhos, const float* rewards, const float* values,
+                              const uint8_t* terminateds, const uint8_t* truncateds,
+                              const float* trunc_values, const float* bootstrap_value,
+                              float gamma, float lambda,
+                              float rho_bar, float c_bar, float pg_rho_bar,
+                              float* vs, float* pg_advantages,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+lrs_status lrs_retrace_tm_f32(int64_t num_envs, int64_t seq_len,
+                               const float* log_rhos, const float* rewards,
+                               const float* q_values, const float* values,
+                               const uint8_t* terminateds, const uint8_t* truncateds,
+                               const float* trunc_values, const float* bootstrap_value,
+                               float gamma, float lambda, float c_bar, float* q_ret,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+lrs_status lrs_lambda_returns_tm_f32(int64_t num_envs, int64_t seq_len,
+                                      const float* rewards, const float* values,
+                                      const uint8_t* terminateds, const uint8_t* truncateds,
+                                      const float* trunc_values, const float* bootstrap_value,
+                                      float gamma, float lambda, float* returns,
+                                      void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
+lrs_status lrs_discounted_returns_tm_f32(int64_t num_envs, int64_t seq_len,
+                                          const float* rewards,
+                                          const uint8_t* terminateds, const uint8_t* truncateds,
+                                          const float* trunc_values, const float* bootstrap_value,
+                                          float gamma, float* returns,
+                                          void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream);
+lrs_status lrs_eligibility_traces_tm_f32(int64_t num_envs, int64_t seq_len,
+                                          const float* x, const uint8_t* dones,
+                                          float gamma, float lambda, float* traces,
+                                          void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream);
+lrs_status lrs_episodic_prefix_sum_tm_f32(int64_t num_envs, int64_t seq_len,
+                                           const float* x, const uint8_t* dones, float* sums,
+                                           void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream);
+lrs_status lrs_affine_scan_tm_f32(int64_t num_envs, int64_t seq_len,
+                                   const float* alpha, const float* beta,
+                                   const uint8_t* reset, const float* carry_in, int reverse,
+                                   float* y,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+lrs_status lrs_episodic_prefix_sum_tm_i32(int64_t num_envs, int64_t seq_len,
+                                          const int32_t* x, const uint8_t* dones, int32_t* sums,
+                                          void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream);
+lrs_status lrs_gae_tm_bf16(int64_t num_envs, int64_t seq_len,
+                           const lrs_bf16* rewards, const lrs_bf16* values,
+                           const uint8_t* terminateds, const uint8_t* truncateds,
+                           const lrs_bf16* trunc_values, const lrs_bf16* bootstrap_value,
+                           float gamma, float lambda, lrs_bf16* advantages,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+lrs_status lrs_vtrace_tm_bf16(int64_t num_envs, int64_t seq_len,
+                              const lrs_bf16* log_rhos, const lrs_bf16* rewards, const lrs_bf16* values,
+                              const uint8_t* terminateds, const uint8_t* truncateds,
+                              const lrs_bf16* trunc_values, const lrs_bf16* bootstrap_value,
+                              float gamma, float lambda,
+                              float rho_bar, float c_bar, float pg_rho_bar,
+                              lrs_bf16* vs, lrs_bf16* pg_advantages,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+lrs_status lrs_retrace_tm_bf16(int64_t num_envs, int64_t seq_len,
+                               const lrs_bf16* log_rhos, const lrs_bf16* rewards,
+                               const lrs_bf16* q_values, const lrs_bf16* values,
+                               const uint8_t* terminateds, const uint8_t* truncateds,
+                               const lrs_bf16* trunc_values, const lrs_bf16* bootstrap_value,
+                               float gamma, float lambda, float c_bar, lrs_bf16* q_ret,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+lrs_status lrs_lambda_returns_tm_bf16(int64_t num_envs, int64_t seq_len,
+                                      const lrs_bf16* rewards, const lrs_bf16* values,
+                                      const uint8_t* terminateds, const uint8_t* truncateds,
+                                      const lrs_bf16* trunc_values, const lrs_bf16* bootstrap_value,
+                                      float gamma, float lambda, lrs_bf16* returns,
+                                      void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
+lrs_status lrs_discounted_returns_tm_bf16(int64_t num_envs, int64_t seq_len,
+                                          const lrs_bf16* rewards,
+                                          const uint8_t* terminateds, const uint8_t* truncateds,
+                                          const lrs_bf16* trunc_values, const lrs_bf16* bootstrap_value,
+                                          float gamma, lrs_bf16* returns,
+                                          void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream);
+lrs_status lrs_eligibility_traces_tm_bf16(int64_t num_envs, int64_t seq_len,
+                                          const lrs_bf16* x, const uint8_t* dones,
+                                          float gamma, float lambda, lrs_bf16* traces,
+                                          void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream);
+lrs_status lrs_episodic_prefix_sum_tm_bf16(int64_t num_envs, int64_t seq_len,
+                                           const lrs_bf16* x, const uint8_t* dones, lrs_bf16* sums,
+                                           void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream);
+lrs_status lrs_affine_scan_tm_bf16(int64_t num_envs, int64_t seq_len,
+                                   const lrs_bf16* alpha, const lrs_bf16* beta,
+                                   const uint8_t* reset, const lrs_bf16* carry_in, int reverse,
+                                   lrs_bf16* y,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+lrs_status lrs_gae_tm_f16(int64_t num_envs, int64_t seq_len,
+                           const lrs_f16* rewards, const lrs_f16* values,
+                           const uint8_t* terminateds, const uint8_t* truncateds,
+                           const lrs_f16* trunc_values, const lrs_f16* bootstrap_value,
+                           float gamma, float lambda, lrs_f16* advantages,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+lrs_status lrs_vtrace_tm_f16(int64_t num_envs, int64_t seq_len,
+                              const lrs_f16* log_rhos, const lrs_f16* rewards, const lrs_f16* values,
+                              const uint8_t* terminateds, const uint8_t* truncateds,
+                              const lrs_f16* trunc_values, const lrs_f16* bootstrap_value,
+                              float gamma, float lambda,
+                              float rho_bar, float c_bar, float pg_rho_bar,
+                              lrs_f16* vs, lrs_f16* pg_advantages,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+lrs_status lrs_retrace_tm_f16(int64_t num_envs, int64_t seq_len,
+                               const lrs_f16* log_rhos, const lrs_f16* rewards,
+                               const lrs_f16* q_values, const lrs_f16* values,
+                               const uint8_t* terminateds, const uint8_t* truncateds,
+                               const lrs_f16* trunc_values, const lrs_f16* bootstrap_value,
+                               float gamma, float lambda, float c_bar, lrs_f16* q_ret,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+lrs_status lrs_lambda_returns_tm_f16(int64_t num_envs, int64_t seq_len,
+                                      const lrs_f16* rewards, const lrs_f16* values,
+                                      const uint8_t* terminateds, const uint8_t* truncateds,
+                                      const lrs_f16* trunc_values, const lrs_f16* bootstrap_value,
+                                      float gamma, float lambda, lrs_f16* returns,
+                                      void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
+lrs_status lrs_discounted_returns_tm_f16(int64_t num_envs, int64_t seq_len,
+                                          const lrs_f16* rewards,
+                                          const uint8_t* terminateds, const uint8_t* truncateds,
+                                          const lrs_f16* trunc_values, const lrs_f16* bootstrap_value,
+                                          float gamma, lrs_f16* returns,
+                                          void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream);
+lrs_status lrs_eligibility_traces_tm_f16(int64_t num_envs, int64_t seq_len,
+                                          const lrs_f16* x, const uint8_t* dones,
+                                          float gamma, float lambda, lrs_f16* traces,
+                                          void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream);
+lrs_status lrs_episodic_prefix_sum_tm_f16(int64_t num_envs, int64_t seq_len,
+                                           const lrs_f16* x, const uint8_t* dones, lrs_f16* sums,
+                                           void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream);
+lrs_status lrs_affine_scan_tm_f16(int64_t num_envs, int64_t seq_len,
+                                   const lrs_f16* alpha, const lrs_f16* beta,
+                                   const uint8_t* reset, const lrs_f16* carry_in, int reverse,
+                                   lrs_f16* y,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Diagnostics and tuning (process-wide; not for concurrent use).
  * force_lookback != 0: every later call takes the multi-block carry-

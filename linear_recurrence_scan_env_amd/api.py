@@ -1,6 +1,9 @@
 """Python binding of liblrs.so: the seven estimators and the generic
 segmented affine scan on torch tensors (float32, bfloat16 or float16 data;
 the dtype of the first data tensor picks the _f32 / _bf16 / _f16 entry).
+Per-step tensors are [num_envs, seq_len]; with time_major=True they are
+[seq_len, num_envs] and the _tm_ entry points run (outputs in the same
+layout); per-env tensors are [num_envs] either way.
 
 Argument marshalling only: every step of every estimator runs in the gfx950
 kernels behind the C ABI (include/lrs.h).  torch supplies device memory and
@@ -38,12 +41,16 @@ _BASE_SIGS = {
     "lrs_episodic_prefix_sum_f32": [_I64, _I64, _P, _P, _P, _P, _SZ, _P],
     "lrs_affine_scan_f32": [_I64, _I64, _P, _P, _P, _P, ctypes.c_int, _P, _P, _SZ, _P],
 }
-# the 16-bit variants take the same arguments (pointers to 16-bit data)
+# the 16-bit variants take the same arguments (pointers to 16-bit data), and
+# so do the time-major (_tm_) variants of every call
 _SIGS = dict(_BASE_SIGS)
 for _name, _args in _BASE_SIGS.items():
     if _name.endswith("_f32"):
         for _sfx in ("bf16", "f16"):
             _SIGS[_name[:-3] + _sfx] = _args
+for _name, _args in list(_SIGS.items()):
+    _stem, _sfx = _name.rsplit("_", 1)
+    _SIGS[f"{_stem}_tm_{_sfx}"] = _args
 
 # storage dtype of the floating-point streams -> entry-point suffix
 _SUFFIX = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}
@@ -179,13 +186,22 @@ def _ptr(x):
     return None if x is None else x.data_ptr()
 
 
-def _rows(x, name):
+def _rows(x, name, time_major=False):
+    """(num_envs, seq_len, shape of the per-step arrays)."""
     if not isinstance(x, torch.Tensor) or x.dim() != 2:
-        raise ValueError(f"{name} must be a 2-D [num_envs, seq_len] tensor")
-    return x.shape[0], x.shape[1]
+        layout = "[seq_len, num_envs]" if time_major else "[num_envs, seq_len]"
+        raise ValueError(f"{name} must be a 2-D {layout} tensor")
+    if time_major:
+        return x.shape[1], x.shape[0], (x.shape[0], x.shape[1])
+    return x.shape[0], x.shape[1], (x.shape[0], x.shape[1])
 
 
-def _prep_boundary(shape, device, dtype, terminateds, truncateds, trunc_values, bootstrap_value):
+def _entry(stem, sfx, time_major):
+    return getattr(load(), f"{stem}_tm_{sfx}" if time_major else f"{stem}_{sfx}")
+
+
+def _prep_boundary(shape, n, device, dtype, terminateds, truncateds, trunc_values,
+                   bootstrap_value):
     term = _mask(terminateds, "terminateds", shape, device)
     if term is None:
         raise ValueError("terminateds is required")
@@ -197,7 +213,7 @@ def _prep_boundary(shape, device, dtype, terminateds, truncateds, trunc_values, 
         tv = _dev_tensor(trunc_values, "trunc_values", dtype, shape, device)
     boot = None
     if bootstrap_value is not None:
-        boot = _dev_tensor(bootstrap_value, "bootstrap_value", dtype, (shape[0],), device)
+        boot = _dev_tensor(bootstrap_value, "bootstrap_value", dtype, (n,), device)
     return term, trunc, tv, boot
 
 
@@ -217,126 +233,137 @@ def _launch_ctx(device, est, n, t):
 
 
 def compute_gae(rewards, values, terminateds, gamma=0.99, lambda_=0.95, *, truncateds=None,
-                trunc_values=None, bootstrap_value=None, out=None):
+                trunc_values=None, bootstrap_value=None, out=None,
+                time_major=False):
     """Generalized advantage estimates, [num_envs, seq_len], in the dtype of
     rewards (float32, bfloat16 or float16; every float input must match)."""
-    n, t = _rows(rewards, "rewards")
+    n, t, shape = _rows(rewards, "rewards", time_major)
     dev, sfx, dt = rewards.device, _suffix(rewards, "rewards"), rewards.dtype
-    r = _dev_tensor(rewards, "rewards", dt, (n, t), None)
-    v = _dev_tensor(values, "values", dt, (n, t), dev)
-    term, trunc, tv, boot = _prep_boundary((n, t), dev, dt, terminateds, truncateds, trunc_values,
-                                           bootstrap_value)
+    r = _dev_tensor(rewards, "rewards", dt, shape, None)
+    v = _dev_tensor(values, "values", dt, shape, dev)
+    term, trunc, tv, boot = _prep_boundary(shape, n, dev, dt, terminateds, truncateds,
+                                           trunc_values, bootstrap_value)
     adv = _out(out, r, "out")
     ws, wsb, st = _launch_ctx(dev, "gae", n, t)
-    _check(getattr(load(), f"lrs_gae_{sfx}")(n, t, _ptr(r), _ptr(v), _ptr(term), _ptr(trunc), _ptr(tv),
-                              _ptr(boot), gamma, lambda_, _ptr(adv), _ptr(ws), wsb, st),
+    fn = _entry("lrs_gae", sfx, time_major)
+    _check(fn(n, t, _ptr(r), _ptr(v), _ptr(term), _ptr(trunc), _ptr(tv),
+              _ptr(boot), gamma, lambda_, _ptr(adv), _ptr(ws), wsb, st),
            "compute_gae")
     return adv
 
 
 def compute_vtrace(log_rhos, rewards, values, terminateds, gamma=0.99, lambda_=1.0, *,
                    rho_bar=1.0, c_bar=1.0, pg_rho_bar=None, truncateds=None, trunc_values=None,
-                   bootstrap_value=None, out=None):
+                   bootstrap_value=None, out=None, time_major=False):
     """V-trace targets and policy-gradient advantages: returns (vs, pg_advantages)."""
-    n, t = _rows(rewards, "rewards")
+    n, t, shape = _rows(rewards, "rewards", time_major)
     dev, sfx, dt = rewards.device, _suffix(rewards, "rewards"), rewards.dtype
-    r = _dev_tensor(rewards, "rewards", dt, (n, t), None)
-    lr = _dev_tensor(log_rhos, "log_rhos", dt, (n, t), dev)
-    v = _dev_tensor(values, "values", dt, (n, t), dev)
-    term, trunc, tv, boot = _prep_boundary((n, t), dev, dt, terminateds, truncateds, trunc_values,
-                                           bootstrap_value)
+    r = _dev_tensor(rewards, "rewards", dt, shape, None)
+    lr = _dev_tensor(log_rhos, "log_rhos", dt, shape, dev)
+    v = _dev_tensor(values, "values", dt, shape, dev)
+    term, trunc, tv, boot = _prep_boundary(shape, n, dev, dt, terminateds, truncateds,
+                                           trunc_values, bootstrap_value)
     vs = _out(None if out is None else out[0], r, "out[0]")
     pg = _out(None if out is None else out[1], r, "out[1]")
     if pg_rho_bar is None:
         pg_rho_bar = rho_bar
     ws, wsb, st = _launch_ctx(dev, "vtrace", n, t)
-    _check(getattr(load(), f"lrs_vtrace_{sfx}")(n, t, _ptr(lr), _ptr(r), _ptr(v), _ptr(term), _ptr(trunc),
-                                 _ptr(tv), _ptr(boot), gamma, lambda_, _inf(rho_bar), _inf(c_bar),
-                                 _inf(pg_rho_bar), _ptr(vs), _ptr(pg), _ptr(ws), wsb, st),
+    fn = _entry("lrs_vtrace", sfx, time_major)
+    _check(fn(n, t, _ptr(lr), _ptr(r), _ptr(v), _ptr(term), _ptr(trunc),
+              _ptr(tv), _ptr(boot), gamma, lambda_, _inf(rho_bar), _inf(c_bar),
+              _inf(pg_rho_bar), _ptr(vs), _ptr(pg), _ptr(ws), wsb, st),
            "compute_vtrace")
     return vs, pg
 
 
 def compute_retrace(log_rhos, rewards, q_values, values, terminateds, gamma=0.99, lambda_=0.95, *,
-                    c_bar=1.0, truncateds=None, trunc_values=None, bootstrap_value=None, out=None):
+                    c_bar=1.0, truncateds=None, trunc_values=None, bootstrap_value=None, out=None,
+                time_major=False):
     """Retrace(lambda) targets for Q(s_t, a_t); values = E_pi Q(s_t, .)."""
-    n, t = _rows(rewards, "rewards")
+    n, t, shape = _rows(rewards, "rewards", time_major)
     dev, sfx, dt = rewards.device, _suffix(rewards, "rewards"), rewards.dtype
-    r = _dev_tensor(rewards, "rewards", dt, (n, t), None)
-    lr = _dev_tensor(log_rhos, "log_rhos", dt, (n, t), dev)
-    q = _dev_tensor(q_values, "q_values", dt, (n, t), dev)
-    v = _dev_tensor(values, "values", dt, (n, t), dev)
-    term, trunc, tv, boot = _prep_boundary((n, t), dev, dt, terminateds, truncateds, trunc_values,
-                                           bootstrap_value)
+    r = _dev_tensor(rewards, "rewards", dt, shape, None)
+    lr = _dev_tensor(log_rhos, "log_rhos", dt, shape, dev)
+    q = _dev_tensor(q_values, "q_values", dt, shape, dev)
+    v = _dev_tensor(values, "values", dt, shape, dev)
+    term, trunc, tv, boot = _prep_boundary(shape, n, dev, dt, terminateds, truncateds,
+                                           trunc_values, bootstrap_value)
     g = _out(out, r, "out")
     ws, wsb, st = _launch_ctx(dev, "retrace", n, t)
-    _check(getattr(load(), f"lrs_retrace_{sfx}")(n, t, _ptr(lr), _ptr(r), _ptr(q), _ptr(v), _ptr(term),
-                                  _ptr(trunc), _ptr(tv), _ptr(boot), gamma, lambda_, _inf(c_bar),
-                                  _ptr(g), _ptr(ws), wsb, st), "compute_retrace")
+    fn = _entry("lrs_retrace", sfx, time_major)
+    _check(fn(n, t, _ptr(lr), _ptr(r), _ptr(q), _ptr(v), _ptr(term),
+              _ptr(trunc), _ptr(tv), _ptr(boot), gamma, lambda_, _inf(c_bar),
+              _ptr(g), _ptr(ws), wsb, st), "compute_retrace")
     return g
 
 
 def compute_lambda_returns(rewards, values, terminateds, gamma=0.99, lambda_=0.95, *,
-                           truncateds=None, trunc_values=None, bootstrap_value=None, out=None):
+                           truncateds=None, trunc_values=None, bootstrap_value=None, out=None,
+                time_major=False):
     """TD(lambda) returns."""
-    n, t = _rows(rewards, "rewards")
+    n, t, shape = _rows(rewards, "rewards", time_major)
     dev, sfx, dt = rewards.device, _suffix(rewards, "rewards"), rewards.dtype
-    r = _dev_tensor(rewards, "rewards", dt, (n, t), None)
-    v = _dev_tensor(values, "values", dt, (n, t), dev)
-    term, trunc, tv, boot = _prep_boundary((n, t), dev, dt, terminateds, truncateds, trunc_values,
-                                           bootstrap_value)
+    r = _dev_tensor(rewards, "rewards", dt, shape, None)
+    v = _dev_tensor(values, "values", dt, shape, dev)
+    term, trunc, tv, boot = _prep_boundary(shape, n, dev, dt, terminateds, truncateds,
+                                           trunc_values, bootstrap_value)
     g = _out(out, r, "out")
     ws, wsb, st = _launch_ctx(dev, "lambda_returns", n, t)
-    _check(getattr(load(), f"lrs_lambda_returns_{sfx}")(n, t, _ptr(r), _ptr(v), _ptr(term), _ptr(trunc),
-                                         _ptr(tv), _ptr(boot), gamma, lambda_, _ptr(g), _ptr(ws),
-                                         wsb, st), "compute_lambda_returns")
+    fn = _entry("lrs_lambda_returns", sfx, time_major)
+    _check(fn(n, t, _ptr(r), _ptr(v), _ptr(term), _ptr(trunc),
+              _ptr(tv), _ptr(boot), gamma, lambda_, _ptr(g), _ptr(ws),
+              wsb, st), "compute_lambda_returns")
     return g
 
 
 def compute_discounted_returns(rewards, terminateds, gamma=0.99, *, truncateds=None,
-                               trunc_values=None, bootstrap_value=None, out=None):
+                               trunc_values=None, bootstrap_value=None, out=None,
+                time_major=False):
     """Discounted reward-to-go."""
-    n, t = _rows(rewards, "rewards")
+    n, t, shape = _rows(rewards, "rewards", time_major)
     dev, sfx, dt = rewards.device, _suffix(rewards, "rewards"), rewards.dtype
-    r = _dev_tensor(rewards, "rewards", dt, (n, t), None)
-    term, trunc, tv, boot = _prep_boundary((n, t), dev, dt, terminateds, truncateds, trunc_values,
-                                           bootstrap_value)
+    r = _dev_tensor(rewards, "rewards", dt, shape, None)
+    term, trunc, tv, boot = _prep_boundary(shape, n, dev, dt, terminateds, truncateds,
+                                           trunc_values, bootstrap_value)
     g = _out(out, r, "out")
     ws, wsb, st = _launch_ctx(dev, "discounted_returns", n, t)
-    _check(getattr(load(), f"lrs_discounted_returns_{sfx}")(n, t, _ptr(r), _ptr(term), _ptr(trunc), _ptr(tv),
-                                             _ptr(boot), gamma, _ptr(g), _ptr(ws), wsb, st),
+    fn = _entry("lrs_discounted_returns", sfx, time_major)
+    _check(fn(n, t, _ptr(r), _ptr(term), _ptr(trunc), _ptr(tv),
+              _ptr(boot), gamma, _ptr(g), _ptr(ws), wsb, st),
            "compute_discounted_returns")
     return g
 
 
-def compute_eligibility_traces(x, dones, gamma=0.99, lambda_=0.95, *, out=None):
+def compute_eligibility_traces(x, dones, gamma=0.99, lambda_=0.95, *, out=None,
+                               time_major=False):
     """Accumulating eligibility traces, forward in time (dtype of x)."""
-    n, t = _rows(x, "x")
+    n, t, shape = _rows(x, "x", time_major)
     dev, sfx = x.device, _suffix(x, "x")
-    xs = _dev_tensor(x, "x", x.dtype, (n, t), None)
-    d = _mask(dones, "dones", (n, t), dev)
+    xs = _dev_tensor(x, "x", x.dtype, shape, None)
+    d = _mask(dones, "dones", shape, dev)
     if d is None:
         raise ValueError("dones is required")
     e = _out(out, xs, "out")
     ws, wsb, st = _launch_ctx(dev, "eligibility_traces", n, t)
-    _check(getattr(load(), f"lrs_eligibility_traces_{sfx}")(n, t, _ptr(xs), _ptr(d), gamma, lambda_, _ptr(e),
-                                             _ptr(ws), wsb, st), "compute_eligibility_traces")
+    fn = _entry("lrs_eligibility_traces", sfx, time_major)
+    _check(fn(n, t, _ptr(xs), _ptr(d), gamma, lambda_, _ptr(e),
+              _ptr(ws), wsb, st), "compute_eligibility_traces")
     return e
 
 
-def compute_episodic_prefix_sum(x, dones, *, out=None):
+def compute_episodic_prefix_sum(x, dones, *, out=None, time_major=False):
     """Inclusive prefix sum with done resets; int32 (exact), float32, bfloat16
     or float16 input, output of the same dtype."""
-    n, t = _rows(x, "x")
+    n, t, shape = _rows(x, "x", time_major)
     dev = x.device
     if isinstance(x, torch.Tensor) and x.dtype == torch.int32:
-        xs = _dev_tensor(x, "x", torch.int32, (n, t), None)
-        fn, est = load().lrs_episodic_prefix_sum_i32, "prefix_sum_i32"
+        xs = _dev_tensor(x, "x", torch.int32, shape, None)
+        fn, est = _entry("lrs_episodic_prefix_sum", "i32", time_major), "prefix_sum_i32"
     else:
         sfx = _suffix(x, "x")
-        xs = _dev_tensor(x, "x", x.dtype, (n, t), None)
-        fn, est = getattr(load(), f"lrs_episodic_prefix_sum_{sfx}"), "prefix_sum_f32"
-    d = _mask(dones, "dones", (n, t), dev)
+        xs = _dev_tensor(x, "x", x.dtype, shape, None)
+        fn, est = _entry("lrs_episodic_prefix_sum", sfx, time_major), "prefix_sum_f32"
+    d = _mask(dones, "dones", shape, dev)
     if d is None:
         raise ValueError("dones is required")
     s = _out(out, xs, "out")
@@ -345,20 +372,21 @@ def compute_episodic_prefix_sum(x, dones, *, out=None):
     return s
 
 
-def compute_affine_scan(alpha, beta, *, reset=None, carry_in=None, reverse=False, out=None):
+def compute_affine_scan(alpha, beta, *, reset=None, carry_in=None, reverse=False, out=None,
+                        time_major=False):
     """Segmented first-order linear recurrence over given coefficients, per row:
     y_t = alpha_t + beta_t * y_{t-1} (forward) or y_t = alpha_t + beta_t * y_{t+1}
     (reverse=True).  carry_in [num_envs] is the y before each row's first step
     in scan order (0 if None); where reset is set, y_t = alpha_t."""
-    n, t = _rows(alpha, "alpha")
+    n, t, shape = _rows(alpha, "alpha", time_major)
     dev, sfx, dt = alpha.device, _suffix(alpha, "alpha"), alpha.dtype
-    a = _dev_tensor(alpha, "alpha", dt, (n, t), None)
-    b = _dev_tensor(beta, "beta", dt, (n, t), dev)
-    rs = _mask(reset, "reset", (n, t), dev)
+    a = _dev_tensor(alpha, "alpha", dt, shape, None)
+    b = _dev_tensor(beta, "beta", dt, shape, dev)
+    rs = _mask(reset, "reset", shape, dev)
     c = None if carry_in is None else _dev_tensor(carry_in, "carry_in", dt, (n,), dev)
     y = _out(out, a, "out")
     ws, wsb, st = _launch_ctx(dev, "affine_scan", n, t)
-    _check(getattr(load(), f"lrs_affine_scan_{sfx}")(n, t, _ptr(a), _ptr(b), _ptr(rs), _ptr(c),
+    _check(_entry("lrs_affine_scan", sfx, time_major)(n, t, _ptr(a), _ptr(b), _ptr(rs), _ptr(c),
                                       1 if reverse else 0, _ptr(y), _ptr(ws), wsb, st),
            "compute_affine_scan")
     return y

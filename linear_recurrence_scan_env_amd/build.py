@@ -20,7 +20,8 @@ SOURCES = [os.path.join(CSRC, "abi.hip")] + [
     os.path.join(CSRC, f"{group}{sfx}.hip")
     for group in ("returns", "offpolicy", "forward", "affine") for sfx in ("", "_bf16", "_f16")]
 HEADERS = [os.path.join(CSRC, f)
-           for f in ("launch.hpp", "scan_core.hpp", "estimators.hpp", "entries.hpp")] + \
+           for f in ("launch.hpp", "scan_core.hpp", "estimators.hpp", "entries.hpp",
+                     "timemajor.hpp")] + \
     [os.path.join(ROOT, "include", "lrs.h")]
 DEPS = SOURCES + HEADERS
 LIB = os.path.join(PKG, "liblrs.so")

@@ -1,7 +1,7 @@
 // abi.hip -- library-wide entry points of include/lrs.h (no kernels): version,
 // status strings, the last-error buffer, workspace sizing and the debug
 // schedule override.
-#include "launch.hpp"
+#include "timemajor.hpp"
 
 namespace lrs {
 
@@ -34,7 +34,9 @@ size_t lrs_workspace_bytes(lrs_estimator est, int64_t num_envs, int64_t seq_len)
 {
     if ((int)est < 0 || (int)est > (int)LRS_AFFINE_SCAN) return 0;
     if (!valid_sizes(num_envs, seq_len)) return 0;
-    return workspace_bytes_for((uint64_t)num_envs * (uint64_t)seq_len);
+    const size_t row_major = workspace_bytes_for((uint64_t)num_envs * (uint64_t)seq_len);
+    const size_t time_major = workspace_bytes_tm((uint64_t)num_envs, (uint64_t)seq_len);
+    return row_major > time_major ? row_major : time_major;
 }
 
 lrs_status lrs_debug_set_schedule(int force_lookback, int elems_per_lane, int waves_per_block)

@@ -2,13 +2,28 @@
 // generic affine scan, for any element type D of the data streams (float,
 // bf16_t, f16_t).  Each call also states the largest beta its maps can hold
 // (gamma*lambda, gamma, gamma*lambda*c_bar, 1 for sums, unbounded for caller
-// coefficients), which sets the composition precision.  The extern "C" functions of include/lrs.h are thin
-// wrappers over these templates, one translation unit per group and type.
+// coefficients), which sets the composition precision, and the layout of its
+// arrays (row-major [N, T] or time-major [T, N]).  The extern "C" functions
+// of include/lrs.h are thin wrappers over these templates, one translation
+// unit per group and storage type.
 #pragma once
 
 #include "launch.hpp"
+#include "timemajor.hpp"
 
 namespace lrs {
+
+// Row-major [N, T] (one flat segmented scan) or time-major [T, N] (chained
+// per-environment carries along time) launch of one functor.
+template <template <int> class Op>
+lrs_status run_layout(bool tm, const char* nm, int64_t N, int64_t T, float beta_max,
+                      const typename Op<4>::Args& a, const void* const* floats, int nfloats,
+                      const void* const* masks, int nmasks, void* ws, size_t ws_bytes,
+                      hipStream_t stream)
+{
+    if (tm) return run_tm<Op>(nm, N, T, beta_max, a, ws, ws_bytes, stream);
+    return run<Op>(nm, N, T, beta_max, a, floats, nfloats, masks, nmasks, ws, ws_bytes, stream);
+}
 
 template <class D> struct GaeSel {
     template <int E> using T = GaeOp<E, true, D>;
@@ -42,7 +57,8 @@ template <class D> struct AffineSel {
 };
 
 template <class D>
-lrs_status gae_entry(const char* nm, int64_t N, int64_t T, const D* rewards, const D* values,
+lrs_status gae_entry(const char* nm, bool tm, int64_t N, int64_t T, const D* rewards,
+                     const D* values,
                      const uint8_t* term, const uint8_t* trunc, const D* tv, const D* boot,
                      float gamma, float lambda, D* adv, void* ws, size_t ws_bytes,
                      hipStream_t stream)
@@ -50,18 +66,22 @@ lrs_status gae_entry(const char* nm, int64_t N, int64_t T, const D* rewards, con
     LRS_TRY(check_common(nm, N, T));
     LRS_REQUIRE(rewards && values && adv, "%s: rewards, values and advantages are required", nm);
     LRS_TRY(check_boundary(nm, term, trunc, tv));
-    LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda), "%s: gamma and lambda must be in [0, 1]", nm);
+    LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda),
+                "%s: gamma and lambda must be in [0, 1]", nm);
     GaeArgs<D> a{{term, trunc, tv, boot ? boot : rewards, boot != nullptr}, rewards, values, gamma,
                  (float)((double)gamma * (double)lambda), adv};
     const void* f[] = {rewards, values, adv, tv};
     const void* m[] = {term, trunc};
     using S = GaeSel<D>;
-    return trunc ? run<S::template T>(nm, N, T, a.gl, a, f, 4, m, 2, ws, ws_bytes, stream)
-                 : run<S::template N>(nm, N, T, a.gl, a, f, 4, m, 2, ws, ws_bytes, stream);
+    return trunc ? run_layout<S::template T>(tm, nm, N, T, a.gl, a, f, 4, m, 2, ws, ws_bytes,
+                                             stream)
+                 : run_layout<S::template N>(tm, nm, N, T, a.gl, a, f, 4, m, 2, ws, ws_bytes,
+                                             stream);
 }
 
 template <class D>
-lrs_status vtrace_entry(const char* nm, int64_t N, int64_t T, const D* log_rhos, const D* rewards,
+lrs_status vtrace_entry(const char* nm, bool tm, int64_t N, int64_t T, const D* log_rhos,
+                        const D* rewards,
                         const D* values, const uint8_t* term, const uint8_t* trunc, const D* tv,
                         const D* boot, float gamma, float lambda, float rho_bar, float c_bar,
                         float pg_rho_bar, D* vs, D* pg_adv, void* ws, size_t ws_bytes,
@@ -71,7 +91,8 @@ lrs_status vtrace_entry(const char* nm, int64_t N, int64_t T, const D* log_rhos,
     LRS_REQUIRE(log_rhos && rewards && values && vs && pg_adv,
                 "%s: log_rhos, rewards, values, vs and pg_advantages are required", nm);
     LRS_TRY(check_boundary(nm, term, trunc, tv));
-    LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda), "%s: gamma and lambda must be in [0, 1]", nm);
+    LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda),
+                "%s: gamma and lambda must be in [0, 1]", nm);
     LRS_REQUIRE(positive(rho_bar) && positive(c_bar) && positive(pg_rho_bar),
                 "%s: rho_bar, c_bar and pg_rho_bar must be > 0", nm);
     VtraceArgs<D> a{{term, trunc, tv, boot ? boot : rewards, boot != nullptr}, log_rhos, rewards,
@@ -80,12 +101,14 @@ lrs_status vtrace_entry(const char* nm, int64_t N, int64_t T, const D* log_rhos,
     const void* m[] = {term, trunc};
     using S = VtraceSel<D>;
     const float beta_max = gamma * lambda * c_bar;  // beta_t = gamma * c_t <= this
-    return trunc ? run<S::template T>(nm, N, T, beta_max, a, f, 6, m, 2, ws, ws_bytes, stream)
-                 : run<S::template N>(nm, N, T, beta_max, a, f, 6, m, 2, ws, ws_bytes, stream);
+    return trunc ? run_layout<S::template T>(tm, nm, N, T, beta_max, a, f, 6, m, 2, ws, ws_bytes,
+                                             stream)
+                 : run_layout<S::template N>(tm, nm, N, T, beta_max, a, f, 6, m, 2, ws, ws_bytes,
+                                             stream);
 }
 
 template <class D>
-lrs_status retrace_entry(const char* nm, int64_t N, int64_t T, const D* log_rhos,
+lrs_status retrace_entry(const char* nm, bool tm, int64_t N, int64_t T, const D* log_rhos,
                          const D* rewards, const D* q_values, const D* values, const uint8_t* term,
                          const uint8_t* trunc, const D* tv, const D* boot, float gamma,
                          float lambda, float c_bar, D* q_ret, void* ws, size_t ws_bytes,
@@ -95,7 +118,8 @@ lrs_status retrace_entry(const char* nm, int64_t N, int64_t T, const D* log_rhos
     LRS_REQUIRE(log_rhos && rewards && q_values && values && q_ret,
                 "%s: log_rhos, rewards, q_values, values and q_ret are required", nm);
     LRS_TRY(check_boundary(nm, term, trunc, tv));
-    LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda), "%s: gamma and lambda must be in [0, 1]", nm);
+    LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda),
+                "%s: gamma and lambda must be in [0, 1]", nm);
     LRS_REQUIRE(positive(c_bar), "%s: c_bar must be > 0", nm);
     RetraceArgs<D> a{{term, trunc, tv, boot ? boot : rewards, boot != nullptr}, log_rhos, rewards,
                      q_values, values, gamma, lambda, c_bar, q_ret};
@@ -103,12 +127,14 @@ lrs_status retrace_entry(const char* nm, int64_t N, int64_t T, const D* log_rhos
     const void* m[] = {term, trunc};
     using S = RetraceSel<D>;
     const float beta_max = gamma * lambda * c_bar;  // beta_t = gamma * c_t <= this
-    return trunc ? run<S::template T>(nm, N, T, beta_max, a, f, 6, m, 2, ws, ws_bytes, stream)
-                 : run<S::template N>(nm, N, T, beta_max, a, f, 6, m, 2, ws, ws_bytes, stream);
+    return trunc ? run_layout<S::template T>(tm, nm, N, T, beta_max, a, f, 6, m, 2, ws, ws_bytes,
+                                             stream)
+                 : run_layout<S::template N>(tm, nm, N, T, beta_max, a, f, 6, m, 2, ws, ws_bytes,
+                                             stream);
 }
 
 template <class D>
-lrs_status lambda_returns_entry(const char* nm, int64_t N, int64_t T, const D* rewards,
+lrs_status lambda_returns_entry(const char* nm, bool tm, int64_t N, int64_t T, const D* rewards,
                                 const D* values, const uint8_t* term, const uint8_t* trunc,
                                 const D* tv, const D* boot, float gamma, float lambda, D* out,
                                 void* ws, size_t ws_bytes, hipStream_t stream)
@@ -116,19 +142,23 @@ lrs_status lambda_returns_entry(const char* nm, int64_t N, int64_t T, const D* r
     LRS_TRY(check_common(nm, N, T));
     LRS_REQUIRE(rewards && values && out, "%s: rewards, values and returns are required", nm);
     LRS_TRY(check_boundary(nm, term, trunc, tv));
-    LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda), "%s: gamma and lambda must be in [0, 1]", nm);
-    LambdaArgs<D> a{{term, trunc, tv, boot ? boot : rewards, boot != nullptr}, rewards, values, gamma,
+    LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda),
+                "%s: gamma and lambda must be in [0, 1]", nm);
+    LambdaArgs<D> a{{term, trunc, tv, boot ? boot : rewards, boot != nullptr}, rewards, values,
+                    gamma,
                     (float)((double)gamma * (double)lambda),
                     (float)((double)gamma * (1.0 - (double)lambda)), out};
     const void* f[] = {rewards, values, out, tv};
     const void* m[] = {term, trunc};
     using S = LambdaSel<D>;
-    return trunc ? run<S::template T>(nm, N, T, a.gl, a, f, 4, m, 2, ws, ws_bytes, stream)
-                 : run<S::template N>(nm, N, T, a.gl, a, f, 4, m, 2, ws, ws_bytes, stream);
+    return trunc ? run_layout<S::template T>(tm, nm, N, T, a.gl, a, f, 4, m, 2, ws, ws_bytes,
+                                             stream)
+                 : run_layout<S::template N>(tm, nm, N, T, a.gl, a, f, 4, m, 2, ws, ws_bytes,
+                                             stream);
 }
 
 template <class D>
-lrs_status discounted_returns_entry(const char* nm, int64_t N, int64_t T, const D* rewards,
+lrs_status discounted_returns_entry(const char* nm, bool tm, int64_t N, int64_t T, const D* rewards,
                                     const uint8_t* term, const uint8_t* trunc, const D* tv,
                                     const D* boot, float gamma, D* out, void* ws, size_t ws_bytes,
                                     hipStream_t stream)
@@ -141,26 +171,31 @@ lrs_status discounted_returns_entry(const char* nm, int64_t N, int64_t T, const 
     const void* f[] = {rewards, out, tv};
     const void* m[] = {term, trunc};
     using S = DiscSel<D>;
-    return trunc ? run<S::template T>(nm, N, T, gamma, a, f, 3, m, 2, ws, ws_bytes, stream)
-                 : run<S::template N>(nm, N, T, gamma, a, f, 3, m, 2, ws, ws_bytes, stream);
+    return trunc ? run_layout<S::template T>(tm, nm, N, T, gamma, a, f, 3, m, 2, ws, ws_bytes,
+                                             stream)
+                 : run_layout<S::template N>(tm, nm, N, T, gamma, a, f, 3, m, 2, ws, ws_bytes,
+                                             stream);
 }
 
 template <class D>
-lrs_status eligibility_traces_entry(const char* nm, int64_t N, int64_t T, const D* x,
+lrs_status eligibility_traces_entry(const char* nm, bool tm, int64_t N, int64_t T, const D* x,
                                     const uint8_t* dones, float gamma, float lambda, D* out,
                                     void* ws, size_t ws_bytes, hipStream_t stream)
 {
     LRS_TRY(check_common(nm, N, T));
     LRS_REQUIRE(x && dones && out, "%s: x, dones and traces are required", nm);
-    LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda), "%s: gamma and lambda must be in [0, 1]", nm);
+    LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda),
+                "%s: gamma and lambda must be in [0, 1]", nm);
     ForwardArgs a{x, dones, (float)((double)gamma * (double)lambda), out};
     const void* f[] = {x, out};
     const void* m[] = {dones};
-    return run<ForwardSel<D>::template Elig>(nm, N, T, a.gl, a, f, 2, m, 1, ws, ws_bytes, stream);
+    return run_layout<ForwardSel<D>::template Elig>(tm, nm, N, T, a.gl, a, f, 2, m, 1, ws, ws_bytes,
+                                                    stream);
 }
 
 template <class D>
-lrs_status prefix_sum_entry(const char* nm, int64_t N, int64_t T, const D* x, const uint8_t* dones,
+lrs_status prefix_sum_entry(const char* nm, bool tm, int64_t N, int64_t T, const D* x,
+                            const uint8_t* dones,
                             D* out, void* ws, size_t ws_bytes, hipStream_t stream)
 {
     LRS_TRY(check_common(nm, N, T));
@@ -168,10 +203,12 @@ lrs_status prefix_sum_entry(const char* nm, int64_t N, int64_t T, const D* x, co
     ForwardArgs a{x, dones, 1.0f, out};
     const void* f[] = {x, out};
     const void* m[] = {dones};
-    return run<ForwardSel<D>::template Prefix>(nm, N, T, 1.0f, a, f, 2, m, 1, ws, ws_bytes, stream);
+    return run_layout<ForwardSel<D>::template Prefix>(tm, nm, N, T, 1.0f, a, f, 2, m, 1, ws,
+                                                      ws_bytes, stream);
 }
 
-inline lrs_status prefix_sum_i32_entry(const char* nm, int64_t N, int64_t T, const int32_t* x,
+inline lrs_status prefix_sum_i32_entry(const char* nm, bool tm, int64_t N, int64_t T,
+                                       const int32_t* x,
                                        const uint8_t* dones, int32_t* out, void* ws,
                                        size_t ws_bytes, hipStream_t stream)
 {
@@ -180,11 +217,12 @@ inline lrs_status prefix_sum_i32_entry(const char* nm, int64_t N, int64_t T, con
     ForwardArgs a{x, dones, 1.0f, out};
     const void* f[] = {x, out};
     const void* m[] = {dones};
-    return run<PrefixI32Op>(nm, N, T, 1.0f, a, f, 2, m, 1, ws, ws_bytes, stream);
+    return run_layout<PrefixI32Op>(tm, nm, N, T, 1.0f, a, f, 2, m, 1, ws, ws_bytes, stream);
 }
 
 template <class D>
-lrs_status affine_scan_entry(const char* nm, int64_t N, int64_t T, const D* alpha, const D* beta,
+lrs_status affine_scan_entry(const char* nm, bool tm, int64_t N, int64_t T, const D* alpha,
+                             const D* beta,
                              const uint8_t* reset, const D* carry_in, int reverse, D* out,
                              void* ws, size_t ws_bytes, hipStream_t stream)
 {
@@ -197,10 +235,14 @@ lrs_status affine_scan_entry(const char* nm, int64_t N, int64_t T, const D* alph
     using S = AffineSel<D>;
     const float beta_max = INFINITY;  // caller coefficients: no bound known
     if (reverse)
-        return reset ? run<S::template RevR>(nm, N, T, beta_max, a, f, 3, m, 1, ws, ws_bytes, stream)
-                     : run<S::template RevN>(nm, N, T, beta_max, a, f, 3, m, 1, ws, ws_bytes, stream);
-    return reset ? run<S::template FwdR>(nm, N, T, beta_max, a, f, 3, m, 1, ws, ws_bytes, stream)
-                 : run<S::template FwdN>(nm, N, T, beta_max, a, f, 3, m, 1, ws, ws_bytes, stream);
+        return reset ? run_layout<S::template RevR>(tm, nm, N, T, beta_max, a, f, 3, m, 1, ws,
+                                                    ws_bytes, stream)
+                     : run_layout<S::template RevN>(tm, nm, N, T, beta_max, a, f, 3, m, 1, ws,
+                                                    ws_bytes, stream);
+    return reset ? run_layout<S::template FwdR>(tm, nm, N, T, beta_max, a, f, 3, m, 1, ws, ws_bytes,
+                                                stream)
+                 : run_layout<S::template FwdN>(tm, nm, N, T, beta_max, a, f, 3, m, 1, ws, ws_bytes,
+                                                stream);
 }
 
 }  // namespace lrs

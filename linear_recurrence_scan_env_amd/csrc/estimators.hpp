@@ -39,11 +39,15 @@ struct Ctx {
 // lane order: lane L-1) and reads memory only in lane 0, which holds the
 // wave's last chunk.  `used` (the lane's last element is not a row end)
 // guarantees i0+E < N*T.
-template <int E, bool F, class D>
+template <int E, bool F, bool TM, class D>
 __device__ __forceinline__ float next_elem(float my0, const D* __restrict__ p,
-                                           const Pos<E, F>& P, const Ctx& c, bool used)
+                                           const Pos<E, F, TM>& P, const Ctx& c, bool used)
 {
-    if constexpr (F) {
+    if constexpr (TM) {
+        // time-major: the successor is the same row's next step, E rows on
+        // (it exists whenever `used`)
+        return used ? to_f32(p[P.i0 + (uint64_t)E * P.stride]) : 0.0f;
+    } else if constexpr (F) {
         // unused: re-read the lane's own first element (a line already
         // fetched) rather than touch the next tile
         const float v = to_f32(p[used ? P.i0 + E : P.i0]);
@@ -57,8 +61,8 @@ __device__ __forceinline__ float next_elem(float my0, const D* __restrict__ p,
 
 // The successor of the lane's last element is read only when that element
 // is not the last of its row.
-template <int E, bool F>
-__device__ __forceinline__ bool successor_used(const Pos<E, F>& P)
+template <int E, bool F, bool TM>
+__device__ __forceinline__ bool successor_used(const Pos<E, F, TM>& P)
 {
     return P.count == E && !((P.last >> (E - 1)) & 1u);
 }
@@ -82,8 +86,8 @@ struct BoundaryArgs {
     int has_boot;           // passes another input array and has_boot = 0
 };
 
-template <int E, bool F, bool kTrunc, class D>
-__device__ __forceinline__ Ends<E> load_ends(const BoundaryArgs<D>& b, const Pos<E, F>& P,
+template <int E, bool F, bool TM, bool kTrunc, class D>
+__device__ __forceinline__ Ends<E> load_ends(const BoundaryArgs<D>& b, const Pos<E, F, TM>& P,
                                              const Ctx& c)
 {
     const uint32_t tau = load_mask<E>(b.term, P, c.vec);
@@ -122,8 +126,8 @@ __device__ __forceinline__ Ends<E> load_ends(const BoundaryArgs<D>& b, const Pos
 }
 
 // Elements past the end of the array are identities.
-template <int E, bool F, class T>
-__device__ __forceinline__ void clear_tail(T (&alpha)[E], T (&beta)[E], const Pos<E, F>& P)
+template <int E, bool F, bool TM, class T>
+__device__ __forceinline__ void clear_tail(T (&alpha)[E], T (&beta)[E], const Pos<E, F, TM>& P)
 {
     if (F) return;
 #pragma unroll
@@ -169,14 +173,14 @@ struct GaeOp {
         uint32_t end;
     };
 
-    template <bool F>
-    __device__ static void prepare(const Args& a, const Pos<E, F>& P, const Ctx& c,
+    template <bool F, bool TM>
+    __device__ static void prepare(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
         float r[E], v[E];
         load_f32<E>(r, a.rewards, P, c.vec);
         load_f32<E>(v, a.values, P, c.vec);
-        const Ends<E> e = load_ends<E, F, kTrunc>(a.b, P, c);
+        const Ends<E> e = load_ends<E, F, TM, kTrunc>(a.b, P, c);
         const float vnx = next_elem<E>(v[0], a.values, P, c, successor_used(P));
 #pragma unroll
         for (int j = 0; j < E; ++j) {
@@ -190,8 +194,8 @@ struct GaeOp {
         s.end = e.end;
     }
     __device__ static bool far_open(const State& s) { return !((s.end >> (E - 1)) & 1u); }
-    template <bool F>
-    __device__ static void finish(const Args& a, const Pos<E, F>& P, const Ctx& c,
+    template <bool F, bool TM>
+    __device__ static void finish(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
                                   const float (&alpha)[E], const float (&beta)[E], const State&,
                                   float carry)
     {
@@ -225,14 +229,14 @@ struct LambdaOp {
         uint32_t end;
     };
 
-    template <bool F>
-    __device__ static void prepare(const Args& a, const Pos<E, F>& P, const Ctx& c,
+    template <bool F, bool TM>
+    __device__ static void prepare(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
         float r[E], v[E];
         load_f32<E>(r, a.rewards, P, c.vec);
         load_f32<E>(v, a.values, P, c.vec);
-        const Ends<E> e = load_ends<E, F, kTrunc>(a.b, P, c);
+        const Ends<E> e = load_ends<E, F, TM, kTrunc>(a.b, P, c);
         const float vnx = next_elem<E>(v[0], a.values, P, c, successor_used(P));
 #pragma unroll
         for (int j = 0; j < E; ++j) {
@@ -245,8 +249,8 @@ struct LambdaOp {
         s.end = e.end;
     }
     __device__ static bool far_open(const State& s) { return !((s.end >> (E - 1)) & 1u); }
-    template <bool F>
-    __device__ static void finish(const Args& a, const Pos<E, F>& P, const Ctx& c,
+    template <bool F, bool TM>
+    __device__ static void finish(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
                                   const float (&alpha)[E], const float (&beta)[E], const State&,
                                   float carry)
     {
@@ -278,13 +282,13 @@ struct DiscOp {
         uint32_t end;
     };
 
-    template <bool F>
-    __device__ static void prepare(const Args& a, const Pos<E, F>& P, const Ctx& c,
+    template <bool F, bool TM>
+    __device__ static void prepare(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
         float r[E];
         load_f32<E>(r, a.rewards, P, c.vec);
-        const Ends<E> e = load_ends<E, F, kTrunc>(a.b, P, c);
+        const Ends<E> e = load_ends<E, F, TM, kTrunc>(a.b, P, c);
 #pragma unroll
         for (int j = 0; j < E; ++j) {
             const bool end = (e.end >> j) & 1u;
@@ -295,8 +299,8 @@ struct DiscOp {
         s.end = e.end;
     }
     __device__ static bool far_open(const State& s) { return !((s.end >> (E - 1)) & 1u); }
-    template <bool F>
-    __device__ static void finish(const Args& a, const Pos<E, F>& P, const Ctx& c,
+    template <bool F, bool TM>
+    __device__ static void finish(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
                                   const float (&alpha)[E], const float (&beta)[E], const State&,
                                   float carry)
     {
@@ -336,15 +340,15 @@ struct VtraceOp {
         float r[E], v[E], tgt[E], rho_pg[E];  // tgt: Vnext at ends, V_{t+1} elsewhere
     };
 
-    template <bool F>
-    __device__ static void prepare(const Args& a, const Pos<E, F>& P, const Ctx& c,
+    template <bool F, bool TM>
+    __device__ static void prepare(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
         float lr[E];
         load_f32<E>(lr, a.log_rhos, P, c.vec);
         load_f32<E>(s.r, a.rewards, P, c.vec);
         load_f32<E>(s.v, a.values, P, c.vec);
-        const Ends<E> e = load_ends<E, F, kTrunc>(a.b, P, c);
+        const Ends<E> e = load_ends<E, F, TM, kTrunc>(a.b, P, c);
         const float vnx = next_elem<E>(s.v[0], a.values, P, c, successor_used(P));
 #pragma unroll
         for (int j = 0; j < E; ++j) {
@@ -363,8 +367,8 @@ struct VtraceOp {
         s.end = e.end;
     }
     __device__ static bool far_open(const State& s) { return !((s.end >> (E - 1)) & 1u); }
-    template <bool F>
-    __device__ static void finish(const Args& a, const Pos<E, F>& P, const Ctx& c,
+    template <bool F, bool TM>
+    __device__ static void finish(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
                                   const float (&alpha)[E], const float (&beta)[E], const State& s,
                                   float carry)
     {
@@ -418,8 +422,8 @@ struct RetraceOp {
         return a.lambda * fminf(a.c_bar, expf(lr));
     }
 
-    template <bool F>
-    __device__ static void prepare(const Args& a, const Pos<E, F>& P, const Ctx& c,
+    template <bool F, bool TM>
+    __device__ static void prepare(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
         float lr[E], r[E], q[E], v[E], cc[E];
@@ -427,7 +431,7 @@ struct RetraceOp {
         load_f32<E>(r, a.rewards, P, c.vec);
         load_f32<E>(q, a.q_values, P, c.vec);
         load_f32<E>(v, a.values, P, c.vec);
-        const Ends<E> e = load_ends<E, F, kTrunc>(a.b, P, c);
+        const Ends<E> e = load_ends<E, F, TM, kTrunc>(a.b, P, c);
         const bool used = successor_used(P);
         // successor (t+1) quantities of the lane's last element
         const float lrnx = next_elem<E>(lr[0], a.log_rhos, P, c, used);
@@ -449,8 +453,8 @@ struct RetraceOp {
         s.end = e.end;
     }
     __device__ static bool far_open(const State& s) { return !((s.end >> (E - 1)) & 1u); }
-    template <bool F>
-    __device__ static void finish(const Args& a, const Pos<E, F>& P, const Ctx& c,
+    template <bool F, bool TM>
+    __device__ static void finish(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
                                   const float (&alpha)[E], const float (&beta)[E], const State&,
                                   float carry)
     {
@@ -464,13 +468,16 @@ struct RetraceOp {
 // reset_j = first-in-row_j | dones_{j-1}.  dones of the element before the
 // lane comes from the neighbouring lane (lane 0 of a wave reads it, except
 // at a row start where it is not needed).
-template <int E, bool F>
+template <int E, bool F, bool TM>
 __device__ __forceinline__ uint32_t load_resets(const uint8_t* __restrict__ dones,
-                                                const Pos<E, F>& P, const Ctx& c)
+                                                const Pos<E, F, TM>& P, const Ctx& c)
 {
     const uint32_t d = load_mask<E>(dones, P, c.vec);
     uint32_t dprev;
-    if constexpr (F) {
+    if constexpr (TM) {
+        // time-major: the predecessor is the same row's previous step
+        dprev = (P.count > 0 && !(P.first & 1u)) ? (dones[P.i0 - P.stride] != 0 ? 1u : 0u) : 0u;
+    } else if constexpr (F) {
         // every lane loads its predecessor's flag unconditionally, in flight
         // with the other loads (its own first flag where none is needed)
         const bool used = P.i0 > 0 && !(P.first & 1u);
@@ -503,8 +510,8 @@ struct EligOp {
     struct State {
         uint32_t reset;
     };
-    template <bool F>
-    __device__ static void prepare(const Args& a, const Pos<E, F>& P, const Ctx& c,
+    template <bool F, bool TM>
+    __device__ static void prepare(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
         load_f32<E>(alpha, (const D*)a.x, P, c.vec);
@@ -514,8 +521,8 @@ struct EligOp {
         clear_tail(alpha, beta, P);
     }
     __device__ static bool far_open(const State& s) { return !(s.reset & 1u); }
-    template <bool F>
-    __device__ static void finish(const Args& a, const Pos<E, F>& P, const Ctx& c,
+    template <bool F, bool TM>
+    __device__ static void finish(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
                                   const float (&alpha)[E], const float (&beta)[E], const State&,
                                   float carry)
     {
@@ -541,8 +548,8 @@ struct PrefixF32Op {
     struct State {
         uint32_t reset;
     };
-    template <bool F>
-    __device__ static void prepare(const Args& a, const Pos<E, F>& P, const Ctx& c,
+    template <bool F, bool TM>
+    __device__ static void prepare(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
         load_f32<E>(alpha, (const D*)a.x, P, c.vec);
@@ -552,8 +559,8 @@ struct PrefixF32Op {
         clear_tail(alpha, beta, P);
     }
     __device__ static bool far_open(const State& s) { return !(s.reset & 1u); }
-    template <bool F>
-    __device__ static void finish(const Args& a, const Pos<E, F>& P, const Ctx& c,
+    template <bool F, bool TM>
+    __device__ static void finish(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
                                   const float (&alpha)[E], const float (&beta)[E], const State& s,
                                   float carry)
     {
@@ -579,8 +586,8 @@ struct PrefixI32Op {
     struct State {
         uint32_t reset;
     };
-    template <bool F>
-    __device__ static void prepare(const Args& a, const Pos<E, F>& P, const Ctx& c,
+    template <bool F, bool TM>
+    __device__ static void prepare(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
                                    uint32_t (&alpha)[E], uint32_t (&beta)[E], State& s)
     {
         load_u32<E>(alpha, (const int32_t*)a.x, P, c.vec);
@@ -590,8 +597,8 @@ struct PrefixI32Op {
         clear_tail(alpha, beta, P);
     }
     __device__ static bool far_open(const State& s) { return !(s.reset & 1u); }
-    template <bool F>
-    __device__ static void finish(const Args& a, const Pos<E, F>& P, const Ctx& c,
+    template <bool F, bool TM>
+    __device__ static void finish(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
                                   const uint32_t (&alpha)[E], const uint32_t (&beta)[E],
                                   const State& s, uint32_t carry)
     {
@@ -634,8 +641,8 @@ struct AffineOp {
         uint32_t cut;
     };
 
-    template <bool F>
-    __device__ static void prepare(const Args& a, const Pos<E, F>& P, const Ctx& c,
+    template <bool F, bool TM>
+    __device__ static void prepare(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
         load_f32<E>(alpha, a.alpha, P, c.vec);
@@ -676,8 +683,8 @@ struct AffineOp {
     {
         return kRev ? !((s.cut >> (E - 1)) & 1u) : !(s.cut & 1u);
     }
-    template <bool F>
-    __device__ static void finish(const Args& a, const Pos<E, F>& P, const Ctx& c,
+    template <bool F, bool TM>
+    __device__ static void finish(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
                                   const float (&alpha)[E], const float (&beta)[E], const State&,
                                   float carry)
     {

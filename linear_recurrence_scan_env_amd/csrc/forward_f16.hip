@@ -10,7 +10,17 @@ lrs_status lrs_eligibility_traces_f16(int64_t N, int64_t T, const lrs_f16* x, co
                                       float gamma, float lambda, lrs_f16* out, void* ws,
                                       size_t ws_bytes, hipStream_t stream)
 {
-    return eligibility_traces_entry<f16_t>("lrs_eligibility_traces_f16", N, T,
+    return eligibility_traces_entry<f16_t>("lrs_eligibility_traces_f16", false, N, T,
+        reinterpret_cast<const f16_t*>(x), dones, gamma, lambda, reinterpret_cast<f16_t*>(out), ws,
+        ws_bytes, stream);
+}
+
+lrs_status lrs_eligibility_traces_tm_f16(int64_t N, int64_t T, const lrs_f16* x,
+                                         const uint8_t* dones, float gamma, float lambda,
+                                         lrs_f16* out, void* ws, size_t ws_bytes,
+                                         hipStream_t stream)
+{
+    return eligibility_traces_entry<f16_t>("lrs_eligibility_traces_tm_f16", true, N, T,
         reinterpret_cast<const f16_t*>(x), dones, gamma, lambda, reinterpret_cast<f16_t*>(out), ws,
         ws_bytes, stream);
 }
@@ -19,7 +29,16 @@ lrs_status lrs_episodic_prefix_sum_f16(int64_t N, int64_t T, const lrs_f16* x,
                                        const uint8_t* dones, lrs_f16* out, void* ws,
                                        size_t ws_bytes, hipStream_t stream)
 {
-    return prefix_sum_entry<f16_t>("lrs_episodic_prefix_sum_f16", N, T,
+    return prefix_sum_entry<f16_t>("lrs_episodic_prefix_sum_f16", false, N, T,
+        reinterpret_cast<const f16_t*>(x), dones, reinterpret_cast<f16_t*>(out), ws, ws_bytes,
+        stream);
+}
+
+lrs_status lrs_episodic_prefix_sum_tm_f16(int64_t N, int64_t T, const lrs_f16* x,
+                                          const uint8_t* dones, lrs_f16* out, void* ws,
+                                          size_t ws_bytes, hipStream_t stream)
+{
+    return prefix_sum_entry<f16_t>("lrs_episodic_prefix_sum_tm_f16", true, N, T,
         reinterpret_cast<const f16_t*>(x), dones, reinterpret_cast<f16_t*>(out), ws, ws_bytes,
         stream);
 }

@@ -11,8 +11,20 @@ lrs_status lrs_vtrace_f32(int64_t N, int64_t T, const float* log_rhos, const flo
                           float rho_bar, float c_bar, float pg_rho_bar, float* vs, float* pg_adv,
                           void* ws, size_t ws_bytes, hipStream_t stream)
 {
-    return vtrace_entry<float>("lrs_vtrace_f32", N, T, log_rhos, rewards, values, term, trunc, tv,
-        boot, gamma, lambda, rho_bar, c_bar, pg_rho_bar, vs, pg_adv, ws, ws_bytes, stream);
+    return vtrace_entry<float>("lrs_vtrace_f32", false, N, T, log_rhos, rewards, values, term,
+        trunc, tv, boot, gamma, lambda, rho_bar, c_bar, pg_rho_bar, vs, pg_adv, ws, ws_bytes,
+        stream);
+}
+
+lrs_status lrs_vtrace_tm_f32(int64_t N, int64_t T, const float* log_rhos, const float* rewards,
+                             const float* values, const uint8_t* term, const uint8_t* trunc,
+                             const float* tv, const float* boot, float gamma, float lambda,
+                             float rho_bar, float c_bar, float pg_rho_bar, float* vs,
+                             float* pg_adv, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    return vtrace_entry<float>("lrs_vtrace_tm_f32", true, N, T, log_rhos, rewards, values, term,
+        trunc, tv, boot, gamma, lambda, rho_bar, c_bar, pg_rho_bar, vs, pg_adv, ws, ws_bytes,
+        stream);
 }
 
 lrs_status lrs_retrace_f32(int64_t N, int64_t T, const float* log_rhos, const float* rewards,
@@ -21,8 +33,18 @@ lrs_status lrs_retrace_f32(int64_t N, int64_t T, const float* log_rhos, const fl
                            float lambda, float c_bar, float* q_ret, void* ws, size_t ws_bytes,
                            hipStream_t stream)
 {
-    return retrace_entry<float>("lrs_retrace_f32", N, T, log_rhos, rewards, q_values, values, term,
-        trunc, tv, boot, gamma, lambda, c_bar, q_ret, ws, ws_bytes, stream);
+    return retrace_entry<float>("lrs_retrace_f32", false, N, T, log_rhos, rewards, q_values,
+        values, term, trunc, tv, boot, gamma, lambda, c_bar, q_ret, ws, ws_bytes, stream);
+}
+
+lrs_status lrs_retrace_tm_f32(int64_t N, int64_t T, const float* log_rhos, const float* rewards,
+                              const float* q_values, const float* values, const uint8_t* term,
+                              const uint8_t* trunc, const float* tv, const float* boot,
+                              float gamma, float lambda, float c_bar, float* q_ret, void* ws,
+                              size_t ws_bytes, hipStream_t stream)
+{
+    return retrace_entry<float>("lrs_retrace_tm_f32", true, N, T, log_rhos, rewards, q_values,
+        values, term, trunc, tv, boot, gamma, lambda, c_bar, q_ret, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -11,10 +11,21 @@ lrs_status lrs_gae_bf16(int64_t N, int64_t T, const lrs_bf16* rewards, const lrs
                         const lrs_bf16* boot, float gamma, float lambda, lrs_bf16* adv, void* ws,
                         size_t ws_bytes, hipStream_t stream)
 {
-    return gae_entry<bf16_t>("lrs_gae_bf16", N, T, reinterpret_cast<const bf16_t*>(rewards),
+    return gae_entry<bf16_t>("lrs_gae_bf16", false, N, T, reinterpret_cast<const bf16_t*>(rewards),
         reinterpret_cast<const bf16_t*>(values), term, trunc, reinterpret_cast<const bf16_t*>(tv),
         reinterpret_cast<const bf16_t*>(boot), gamma, lambda, reinterpret_cast<bf16_t*>(adv), ws,
         ws_bytes, stream);
+}
+
+lrs_status lrs_gae_tm_bf16(int64_t N, int64_t T, const lrs_bf16* rewards, const lrs_bf16* values,
+                           const uint8_t* term, const uint8_t* trunc, const lrs_bf16* tv,
+                           const lrs_bf16* boot, float gamma, float lambda, lrs_bf16* adv,
+                           void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    return gae_entry<bf16_t>("lrs_gae_tm_bf16", true, N, T,
+        reinterpret_cast<const bf16_t*>(rewards), reinterpret_cast<const bf16_t*>(values), term,
+        trunc, reinterpret_cast<const bf16_t*>(tv), reinterpret_cast<const bf16_t*>(boot), gamma,
+        lambda, reinterpret_cast<bf16_t*>(adv), ws, ws_bytes, stream);
 }
 
 lrs_status lrs_lambda_returns_bf16(int64_t N, int64_t T, const lrs_bf16* rewards,
@@ -23,7 +34,19 @@ lrs_status lrs_lambda_returns_bf16(int64_t N, int64_t T, const lrs_bf16* rewards
                                    float gamma, float lambda, lrs_bf16* out, void* ws,
                                    size_t ws_bytes, hipStream_t stream)
 {
-    return lambda_returns_entry<bf16_t>("lrs_lambda_returns_bf16", N, T,
+    return lambda_returns_entry<bf16_t>("lrs_lambda_returns_bf16", false, N, T,
+        reinterpret_cast<const bf16_t*>(rewards), reinterpret_cast<const bf16_t*>(values), term,
+        trunc, reinterpret_cast<const bf16_t*>(tv), reinterpret_cast<const bf16_t*>(boot), gamma,
+        lambda, reinterpret_cast<bf16_t*>(out), ws, ws_bytes, stream);
+}
+
+lrs_status lrs_lambda_returns_tm_bf16(int64_t N, int64_t T, const lrs_bf16* rewards,
+                                      const lrs_bf16* values, const uint8_t* term,
+                                      const uint8_t* trunc, const lrs_bf16* tv,
+                                      const lrs_bf16* boot, float gamma, float lambda,
+                                      lrs_bf16* out, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    return lambda_returns_entry<bf16_t>("lrs_lambda_returns_tm_bf16", true, N, T,
         reinterpret_cast<const bf16_t*>(rewards), reinterpret_cast<const bf16_t*>(values), term,
         trunc, reinterpret_cast<const bf16_t*>(tv), reinterpret_cast<const bf16_t*>(boot), gamma,
         lambda, reinterpret_cast<bf16_t*>(out), ws, ws_bytes, stream);
@@ -35,7 +58,19 @@ lrs_status lrs_discounted_returns_bf16(int64_t N, int64_t T, const lrs_bf16* rew
                                        lrs_bf16* out, void* ws, size_t ws_bytes,
                                        hipStream_t stream)
 {
-    return discounted_returns_entry<bf16_t>("lrs_discounted_returns_bf16", N, T,
+    return discounted_returns_entry<bf16_t>("lrs_discounted_returns_bf16", false, N, T,
+        reinterpret_cast<const bf16_t*>(rewards), term, trunc, reinterpret_cast<const bf16_t*>(tv),
+        reinterpret_cast<const bf16_t*>(boot), gamma, reinterpret_cast<bf16_t*>(out), ws, ws_bytes,
+        stream);
+}
+
+lrs_status lrs_discounted_returns_tm_bf16(int64_t N, int64_t T, const lrs_bf16* rewards,
+                                          const uint8_t* term, const uint8_t* trunc,
+                                          const lrs_bf16* tv, const lrs_bf16* boot, float gamma,
+                                          lrs_bf16* out, void* ws, size_t ws_bytes,
+                                          hipStream_t stream)
+{
+    return discounted_returns_entry<bf16_t>("lrs_discounted_returns_tm_bf16", true, N, T,
         reinterpret_cast<const bf16_t*>(rewards), term, trunc, reinterpret_cast<const bf16_t*>(tv),
         reinterpret_cast<const bf16_t*>(boot), gamma, reinterpret_cast<bf16_t*>(out), ws, ws_bytes,
         stream);

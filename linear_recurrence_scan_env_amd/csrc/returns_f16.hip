@@ -11,7 +11,18 @@ lrs_status lrs_gae_f16(int64_t N, int64_t T, const lrs_f16* rewards, const lrs_f
                        const lrs_f16* boot, float gamma, float lambda, lrs_f16* adv, void* ws,
                        size_t ws_bytes, hipStream_t stream)
 {
-    return gae_entry<f16_t>("lrs_gae_f16", N, T, reinterpret_cast<const f16_t*>(rewards),
+    return gae_entry<f16_t>("lrs_gae_f16", false, N, T, reinterpret_cast<const f16_t*>(rewards),
+        reinterpret_cast<const f16_t*>(values), term, trunc, reinterpret_cast<const f16_t*>(tv),
+        reinterpret_cast<const f16_t*>(boot), gamma, lambda, reinterpret_cast<f16_t*>(adv), ws,
+        ws_bytes, stream);
+}
+
+lrs_status lrs_gae_tm_f16(int64_t N, int64_t T, const lrs_f16* rewards, const lrs_f16* values,
+                          const uint8_t* term, const uint8_t* trunc, const lrs_f16* tv,
+                          const lrs_f16* boot, float gamma, float lambda, lrs_f16* adv, void* ws,
+                          size_t ws_bytes, hipStream_t stream)
+{
+    return gae_entry<f16_t>("lrs_gae_tm_f16", true, N, T, reinterpret_cast<const f16_t*>(rewards),
         reinterpret_cast<const f16_t*>(values), term, trunc, reinterpret_cast<const f16_t*>(tv),
         reinterpret_cast<const f16_t*>(boot), gamma, lambda, reinterpret_cast<f16_t*>(adv), ws,
         ws_bytes, stream);
@@ -23,7 +34,19 @@ lrs_status lrs_lambda_returns_f16(int64_t N, int64_t T, const lrs_f16* rewards,
                                   float lambda, lrs_f16* out, void* ws, size_t ws_bytes,
                                   hipStream_t stream)
 {
-    return lambda_returns_entry<f16_t>("lrs_lambda_returns_f16", N, T,
+    return lambda_returns_entry<f16_t>("lrs_lambda_returns_f16", false, N, T,
+        reinterpret_cast<const f16_t*>(rewards), reinterpret_cast<const f16_t*>(values), term,
+        trunc, reinterpret_cast<const f16_t*>(tv), reinterpret_cast<const f16_t*>(boot), gamma,
+        lambda, reinterpret_cast<f16_t*>(out), ws, ws_bytes, stream);
+}
+
+lrs_status lrs_lambda_returns_tm_f16(int64_t N, int64_t T, const lrs_f16* rewards,
+                                     const lrs_f16* values, const uint8_t* term,
+                                     const uint8_t* trunc, const lrs_f16* tv, const lrs_f16* boot,
+                                     float gamma, float lambda, lrs_f16* out, void* ws,
+                                     size_t ws_bytes, hipStream_t stream)
+{
+    return lambda_returns_entry<f16_t>("lrs_lambda_returns_tm_f16", true, N, T,
         reinterpret_cast<const f16_t*>(rewards), reinterpret_cast<const f16_t*>(values), term,
         trunc, reinterpret_cast<const f16_t*>(tv), reinterpret_cast<const f16_t*>(boot), gamma,
         lambda, reinterpret_cast<f16_t*>(out), ws, ws_bytes, stream);
@@ -34,7 +57,19 @@ lrs_status lrs_discounted_returns_f16(int64_t N, int64_t T, const lrs_f16* rewar
                                       const lrs_f16* boot, float gamma, lrs_f16* out, void* ws,
                                       size_t ws_bytes, hipStream_t stream)
 {
-    return discounted_returns_entry<f16_t>("lrs_discounted_returns_f16", N, T,
+    return discounted_returns_entry<f16_t>("lrs_discounted_returns_f16", false, N, T,
+        reinterpret_cast<const f16_t*>(rewards), term, trunc, reinterpret_cast<const f16_t*>(tv),
+        reinterpret_cast<const f16_t*>(boot), gamma, reinterpret_cast<f16_t*>(out), ws, ws_bytes,
+        stream);
+}
+
+lrs_status lrs_discounted_returns_tm_f16(int64_t N, int64_t T, const lrs_f16* rewards,
+                                         const uint8_t* term, const uint8_t* trunc,
+                                         const lrs_f16* tv, const lrs_f16* boot, float gamma,
+                                         lrs_f16* out, void* ws, size_t ws_bytes,
+                                         hipStream_t stream)
+{
+    return discounted_returns_entry<f16_t>("lrs_discounted_returns_tm_f16", true, N, T,
         reinterpret_cast<const f16_t*>(rewards), term, trunc, reinterpret_cast<const f16_t*>(tv),
         reinterpret_cast<const f16_t*>(boot), gamma, reinterpret_cast<f16_t*>(out), ws, ws_bytes,
         stream);

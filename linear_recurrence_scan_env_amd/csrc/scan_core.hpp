@@ -174,19 +174,30 @@ __device__ __forceinline__ Aff<T> row_scan(Aff<T> x)
 // every access below is an unconditional vector load or store.  Otherwise
 // (the last tile, misaligned views) each access checks the lane's count.
 
-template <int E, bool kFull>
+template <int E, bool kFull, bool kTM = false>
 struct Pos {
     uint64_t i0;     // flat index of element 0
     uint64_t n0;     // row of element 0
     int count;       // valid elements (E except at the end of the array)
     uint32_t last;   // bit j: element j is the last step of its row
     uint32_t first;  // bit j: element j is the first step of its row
+    // Time-major ([T, N]) lanes: element j sits at i0 + j * stride (stride =
+    // N) and all E elements are steps of row n0; every access is a guarded
+    // scalar access, coalesced across the lanes of a wave.
+    uint64_t stride;
 };
 
-template <int E, bool kFull>
-__device__ __forceinline__ bool vector_ok(const Pos<E, kFull>& P, bool vec)
+template <int E, bool kFull, bool TM>
+__device__ __forceinline__ bool vector_ok(const Pos<E, kFull, TM>& P, bool vec)
 {
-    return kFull || (vec && P.count == E);
+    return !TM && (kFull || (vec && P.count == E));
+}
+
+// Flat index of a lane's element j.
+template <int E, bool kFull, bool TM>
+__device__ __forceinline__ uint64_t elem_index(const Pos<E, kFull, TM>& P, int j)
+{
+    return TM ? P.i0 + (uint64_t)j * P.stride : P.i0 + (uint64_t)j;
 }
 
 // ------------------------------------------------------- element storage
@@ -242,9 +253,9 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi)
         return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
 }
 
-template <int E, bool kFull, class D>
+template <int E, bool kFull, bool TM, class D>
 __device__ __forceinline__ void load_f32(float (&v)[E], const D* __restrict__ p,
-                                         const Pos<E, kFull>& P, bool vec)
+                                         const Pos<E, kFull, TM>& P, bool vec)
 {
     if (vector_ok(P, vec)) {
         if constexpr (std::is_same<D, float>::value) {
@@ -272,13 +283,13 @@ __device__ __forceinline__ void load_f32(float (&v)[E], const D* __restrict__ p,
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < E; ++j) v[j] = (j < P.count) ? to_f32(p[P.i0 + j]) : 0.0f;
+        for (int j = 0; j < E; ++j) v[j] = (j < P.count) ? to_f32(p[elem_index(P, j)]) : 0.0f;
     }
 }
 
-template <int E, bool kFull>
+template <int E, bool kFull, bool TM>
 __device__ __forceinline__ void load_u32(uint32_t (&v)[E], const int32_t* __restrict__ p,
-                                         const Pos<E, kFull>& P, bool vec)
+                                         const Pos<E, kFull, TM>& P, bool vec)
 {
     if (vector_ok(P, vec)) {
 #pragma unroll
@@ -291,7 +302,7 @@ __device__ __forceinline__ void load_u32(uint32_t (&v)[E], const int32_t* __rest
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < E; ++j) v[j] = (j < P.count) ? (uint32_t)p[P.i0 + j] : 0u;
+        for (int j = 0; j < E; ++j) v[j] = (j < P.count) ? (uint32_t)p[elem_index(P, j)] : 0u;
     }
 }
 
@@ -307,8 +318,8 @@ __device__ __forceinline__ uint32_t nonzero_bytes(uint32_t w)
 }
 
 // Bit j of the result is (mask[i0 + j] != 0); a null mask reads as all zero.
-template <int E, bool kFull>
-__device__ __forceinline__ uint32_t load_mask(const uint8_t* __restrict__ p, const Pos<E, kFull>& P,
+template <int E, bool kFull, bool TM>
+__device__ __forceinline__ uint32_t load_mask(const uint8_t* __restrict__ p, const Pos<E, kFull, TM>& P,
                                               bool vec)
 {
     static_assert(E == 4 || E == 8 || E == 16, "mask loads are 4, 8 or 16 bytes");
@@ -325,7 +336,7 @@ __device__ __forceinline__ uint32_t load_mask(const uint8_t* __restrict__ p, con
     uint32_t bits = 0;
 #pragma unroll
     for (int j = 0; j < E; ++j)
-        if (j < P.count && p[P.i0 + j] != 0) bits |= 1u << j;
+        if (j < P.count && p[elem_index(P, j)] != 0) bits |= 1u << j;
     return bits;
 }
 
@@ -336,9 +347,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-template <int E, bool kFull, class D>
+template <int E, bool kFull, bool TM, class D>
 __device__ __forceinline__ void store_f32(D* __restrict__ p, const float (&v)[E],
-                                          const Pos<E, kFull>& P, bool vec)
+                                          const Pos<E, kFull, TM>& P, bool vec)
 {
     if (vector_ok(P, vec)) {
         if constexpr (std::is_same<D, float>::value) {
@@ -360,13 +371,13 @@ __device__ __forceinline__ void store_f32(D* __restrict__ p, const float (&v)[E]
     } else {
 #pragma unroll
         for (int j = 0; j < E; ++j)
-            if (j < P.count) p[P.i0 + j] = from_f32<D>(v[j]);
+            if (j < P.count) p[elem_index(P, j)] = from_f32<D>(v[j]);
     }
 }
 
-template <int E, bool kFull>
+template <int E, bool kFull, bool TM>
 __device__ __forceinline__ void store_u32(int32_t* __restrict__ p, const uint32_t (&v)[E],
-                                          const Pos<E, kFull>& P, bool vec)
+                                          const Pos<E, kFull, TM>& P, bool vec)
 {
     if (vector_ok(P, vec)) {
 #pragma unroll
@@ -376,7 +387,7 @@ __device__ __forceinline__ void store_u32(int32_t* __restrict__ p, const uint32_
     } else {
 #pragma unroll
         for (int j = 0; j < E; ++j)
-            if (j < P.count) p[P.i0 + j] = (int32_t)v[j];
+            if (j < P.count) p[elem_index(P, j)] = (int32_t)v[j];
     }
 }
 
