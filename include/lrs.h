@@ -105,7 +105,7 @@ const char* lrs_last_error(void);
 /* Bytes of workspace a call of `est` (an estimator, or LRS_AFFINE_SCAN) at
  * [num_envs, seq_len] may need, in either layout:
  * 4224 bytes plus the larger of 32 bytes per 256 elements (about 3% of one
- * fp32 array) and 16 bytes per env per 128 steps.  The same workspace serves
+ * fp32 array) and 24 bytes per env per 64 steps.  The same workspace serves
  * every estimator and layout at this or any smaller size.
  * Returns 0 for invalid sizes. */
 size_t lrs_workspace_bytes(lrs_estimator est, int64_t num_envs, int64_t seq_len);
@@ -366,9 +366,10 @@ lrs_status lrs_affine_scan_f16(int64_t num_envs, int64_t seq_len,
  * up to fp32 re-association, bit for bit for the int32 prefix sum.  The
  * pages fix the [num_envs, seq_len] layout (README Usage); this layout is
  * this library's extension.  A lane owns one environment (loads coalesce
- * across environments) and tiles of 128 steps pass carries along time; no
+ * across environments) and tiles of 64 or 128 steps pass carries along time; no
  * alignment beyond the element size is needed.  The workspace from
- * lrs_workspace_bytes covers both layouts.                               */
+ * lrs_workspace_bytes covers both layouts.  Results are deterministic run
+ * to run, as for the row-major calls.                                    */
 lrs_status lrs_gae_tm_f32(int64_t num_envs, int64_t seq_len,
                            const float* rewards, const float* values,
                            const uint8_t* terminateds, const uint8_t* truncateds,
@@ -532,6 +533,11 @@ lrs_status lrs_affine_scan_tm_f16(int64_t num_envs, int64_t seq_len,
  * is identical). */
 lrs_status lrs_debug_set_schedule(int force_lookback, int elems_per_lane,
                                   int waves_per_block);
+
+/* Time-major calls: fix the waves per block (8: tiles of 64 steps, 16:
+ * tiles of 128 steps; 8 steps per lane either way), or 0 for the automatic
+ * choice.  Returns LRS_ERR_INVALID_ARG for any other value. */
+lrs_status lrs_debug_set_time_major_waves(int waves_per_block);
 
 #ifdef __cplusplus
 }

@@ -17,11 +17,12 @@ from .api import (  # noqa: F401
     lib_path,
     load,
     set_schedule,
+    set_time_major_waves,
 )
 
 __all__ = [
     "compute_gae", "compute_vtrace", "compute_retrace", "compute_lambda_returns",
     "compute_discounted_returns", "compute_eligibility_traces", "compute_episodic_prefix_sum",
     "compute_affine_scan",
-    "LrsError", "load", "lib_path", "set_schedule",
+    "LrsError", "load", "lib_path", "set_schedule", "set_time_major_waves",
 ]

@@ -105,6 +105,7 @@ def load():
         lib.lrs_workspace_bytes.argtypes = [ctypes.c_int, _I64, _I64]
         lib.lrs_debug_set_schedule.restype = ctypes.c_int
         lib.lrs_debug_set_schedule.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        lib.lrs_debug_set_time_major_waves.argtypes = [ctypes.c_int]
         _check_single_hip_runtime()
         _lib = lib
     return _lib
@@ -137,6 +138,11 @@ def set_schedule(force_lookback: bool = False, elems_per_lane: int = 0, waves_pe
     """Diagnostics: force the carry-propagation path and/or a fixed tile."""
     _check(load().lrs_debug_set_schedule(int(force_lookback), int(elems_per_lane),
                                          int(waves_per_block)), "set_schedule")
+
+
+def set_time_major_waves(waves_per_block: int = 0):
+    """Diagnostics: waves per block of the time-major calls (8, 16; 0 = automatic)."""
+    _check(load().lrs_debug_set_time_major_waves(int(waves_per_block)), "set_time_major_waves")
 
 
 # ------------------------------------------------------------ marshalling

@@ -7,6 +7,7 @@ namespace lrs {
 
 std::atomic<int> g_force_lookback{0};
 std::atomic<int> g_forced_cfg{-1};
+std::atomic<int> g_forced_tm_waves{0};
 thread_local char g_err[512];
 
 }  // namespace lrs
@@ -51,6 +52,15 @@ lrs_status lrs_debug_set_schedule(int force_lookback, int elems_per_lane, int wa
     }
     g_force_lookback.store(force_lookback != 0);
     g_forced_cfg.store(cfg);
+    return LRS_OK;
+}
+
+lrs_status lrs_debug_set_time_major_waves(int waves_per_block)
+{
+    if (waves_per_block != 0 && waves_per_block != kTmWSmall && waves_per_block != kTmWLarge)
+        return fail(LRS_ERR_INVALID_ARG, "lrs_debug_set_time_major_waves: %d is not 0, %d or %d",
+                    waves_per_block, kTmWSmall, kTmWLarge);
+    g_forced_tm_waves.store(waves_per_block);
     return LRS_OK;
 }
 

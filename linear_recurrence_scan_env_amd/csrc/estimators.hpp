@@ -45,7 +45,12 @@ __device__ __forceinline__ float next_elem(float my0, const D* __restrict__ p,
 {
     if constexpr (TM) {
         // time-major: the successor is the same row's next step, E rows on
-        // (it exists whenever `used`)
+        // (it exists whenever `used`); full lanes load unconditionally (their
+        // own first element when unused)
+        if constexpr (F) {
+            const float v = to_f32(p[used ? P.i0 + (uint64_t)E * P.stride : P.i0]);
+            return used ? v : 0.0f;
+        }
         return used ? to_f32(p[P.i0 + (uint64_t)E * P.stride]) : 0.0f;
     } else if constexpr (F) {
         // unused: re-read the lane's own first element (a line already
@@ -476,7 +481,13 @@ __device__ __forceinline__ uint32_t load_resets(const uint8_t* __restrict__ done
     uint32_t dprev;
     if constexpr (TM) {
         // time-major: the predecessor is the same row's previous step
-        dprev = (P.count > 0 && !(P.first & 1u)) ? (dones[P.i0 - P.stride] != 0 ? 1u : 0u) : 0u;
+        const bool used = P.count > 0 && !(P.first & 1u);
+        if constexpr (F) {
+            const uint32_t w = dones[used ? P.i0 - P.stride : P.i0] != 0 ? 1u : 0u;
+            dprev = used ? w : 0u;
+        } else {
+            dprev = used ? (dones[P.i0 - P.stride] != 0 ? 1u : 0u) : 0u;
+        }
     } else if constexpr (F) {
         // every lane loads its predecessor's flag unconditionally, in flight
         // with the other loads (its own first flag where none is needed)

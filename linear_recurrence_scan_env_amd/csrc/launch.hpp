@@ -316,6 +316,7 @@ constexpr float kFp32BetaMax = 0.99f;
 // Defined in abi.hip.
 extern std::atomic<int> g_force_lookback;
 extern std::atomic<int> g_forced_cfg;
+extern std::atomic<int> g_forced_tm_waves;  // 0: automatic
 extern thread_local char g_err[512];
 
 inline lrs_status fail(lrs_status st, const char* fmt, ...)

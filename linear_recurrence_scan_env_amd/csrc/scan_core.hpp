@@ -182,8 +182,9 @@ struct Pos {
     uint32_t last;   // bit j: element j is the last step of its row
     uint32_t first;  // bit j: element j is the first step of its row
     // Time-major ([T, N]) lanes: element j sits at i0 + j * stride (stride =
-    // N) and all E elements are steps of row n0; every access is a guarded
-    // scalar access, coalesced across the lanes of a wave.
+    // N) and all E elements are steps of row n0; every access is a scalar
+    // access, coalesced across the lanes of a wave, and unconditional when
+    // kFull (the lane's E steps all exist).
     uint64_t stride;
 };
 
@@ -283,7 +284,7 @@ __device__ __forceinline__ void load_f32(float (&v)[E], const D* __restrict__ p,
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < E; ++j) v[j] = (j < P.count) ? to_f32(p[elem_index(P, j)]) : 0.0f;
+        for (int j = 0; j < E; ++j) v[j] = (kFull || j < P.count) ? to_f32(p[elem_index(P, j)]) : 0.0f;
     }
 }
 
@@ -302,7 +303,7 @@ __device__ __forceinline__ void load_u32(uint32_t (&v)[E], const int32_t* __rest
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < E; ++j) v[j] = (j < P.count) ? (uint32_t)p[elem_index(P, j)] : 0u;
+        for (int j = 0; j < E; ++j) v[j] = (kFull || j < P.count) ? (uint32_t)p[elem_index(P, j)] : 0u;
     }
 }
 
@@ -336,7 +337,7 @@ __device__ __forceinline__ uint32_t load_mask(const uint8_t* __restrict__ p, con
     uint32_t bits = 0;
 #pragma unroll
     for (int j = 0; j < E; ++j)
-        if (j < P.count && p[elem_index(P, j)] != 0) bits |= 1u << j;
+        if ((kFull || j < P.count) && p[elem_index(P, j)] != 0) bits |= 1u << j;
     return bits;
 }
 
@@ -371,7 +372,7 @@ __device__ __forceinline__ void store_f32(D* __restrict__ p, const float (&v)[E]
     } else {
 #pragma unroll
         for (int j = 0; j < E; ++j)
-            if (j < P.count) p[elem_index(P, j)] = from_f32<D>(v[j]);
+            if (kFull || j < P.count) p[elem_index(P, j)] = from_f32<D>(v[j]);
     }
 }
 
@@ -387,7 +388,7 @@ __device__ __forceinline__ void store_u32(int32_t* __restrict__ p, const uint32_
     } else {
 #pragma unroll
         for (int j = 0; j < E; ++j)
-            if (j < P.count) p[elem_index(P, j)] = (int32_t)v[j];
+            if (kFull || j < P.count) p[elem_index(P, j)] = (int32_t)v[j];
     }
 }
 

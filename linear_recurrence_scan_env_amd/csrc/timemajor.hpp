@@ -9,14 +9,16 @@
 // the row-major ones, fed a time-major Pos (strided, guarded accesses; all
 // of a lane's steps belong to one environment).
 //
-// Carries between tiles run along time, per environment: tile k publishes,
-// for each of its environments, the value at its near edge (the inclusive
-// result that the next tile in scan order needs), tagged with the launch
-// epoch, and the next tile waits for exactly that value: a chained scan,
-// deterministic, with no look-back.  Blocks take tiles time-tile-major from
-// the scan's far end, so a tile's predecessor belongs to the block
-// `groups` lower, which is running or done.  A lane whose tile holds a cut
-// publishes before it waits.  Every wait is bounded (kMaxPolls).
+// Carries between tiles run along time, per environment: each tile publishes
+// its aggregate as soon as its own maps are composed, and its inclusive value
+// (the value at its near edge) once it has its carry.  A tile looks back over
+// up to kWindowTM earlier-in-scan tiles, to the first published inclusive
+// value or cut, and applies the aggregates in between from the far one to the
+// near one.  That is exactly the arithmetic by which those tiles form their
+// own inclusive values, so the result is the same bits however far a tile
+// had to look: deterministic.  Blocks take tiles time-tile-major from the
+// scan's far end, so every tile a block reads belongs to a block of lower
+// index, which is running or done.  Every wait is bounded (kMaxPolls).
 #pragma once
 
 #include "launch.hpp"
@@ -24,44 +26,38 @@
 namespace lrs {
 
 struct SchedTM {
-    uint8_t* ws;          // header + per-(tile, environment) values
+    uint8_t* ws;          // header + per-(tile, environment) records
     uint32_t N, T;
     uint32_t groups;      // ceil(N / 64): environment groups
     uint32_t time_tiles;  // ceil(T / (E * W))
     uint32_t num_blocks;  // groups * time_tiles
 };
 
-// Words per published value: one 64-bit word (tag << 32 | bits) for 32-bit
-// values, two (low and high halves, each tagged) for fp64.
-template <class A>
-constexpr uint32_t kWordsTM = sizeof(A) == 8 ? 2u : 1u;
+// Records: three planes of time_tiles * N tagged 64-bit words (tag << 32 |
+// 32 payload bits): the tile's aggregate a and b per environment, and its
+// inclusive value y (the value at its near edge, which the next tile in
+// scan order needs).  Planar, so a wave's 64 environments read 512
+// contiguous bytes.  The payload is fp32 for fp32 maps whatever their
+// composition type (uint32 for the integer prefix sum): a tile defines y as
+// apply(published aggregate, carry) in that type, so any reader that
+// rebuilds y from published aggregates gets the same bits.
+constexpr uint32_t kPlanesTM = 3;
+constexpr int kWindowTM = 16;  // aggregates a waiting tile may compose
 
+// Record payload type of a composition type: uint32 stays, fp32/fp64 -> fp32.
 template <class A>
-__device__ __forceinline__ void publish_tm(uint64_t* rec, uint64_t slot, uint32_t tag, A v)
+using RecOf = typename std::conditional<std::is_same<A, uint32_t>::value, uint32_t, float>::type;
+
+template <class R>
+__device__ __forceinline__ uint64_t tagged(uint32_t tag, R v)
 {
-    const uint64_t t = (uint64_t)tag << 32;
-    const uint64_t bits = payload_bits(v);
-    if constexpr (kWordsTM<A> == 2) {
-        st_agent(rec + 2 * slot, t | (bits & 0xffffffffu));
-        st_agent(rec + 2 * slot + 1, t | (bits >> 32));
-    } else {
-        st_agent(rec + slot, t | bits);
-    }
+    return ((uint64_t)tag << 32) | __builtin_bit_cast(uint32_t, v);
 }
-
-// true and the value once both halves carry `tag`
-template <class A>
-__device__ __forceinline__ bool read_tm(const uint64_t* rec, uint64_t slot, uint32_t tag, A& v)
+template <class R>
+__device__ __forceinline__ bool untag(uint64_t w, uint32_t tag, R& v)
 {
-    if constexpr (kWordsTM<A> == 2) {
-        const uint64_t lo = ld_agent(rec + 2 * slot), hi = ld_agent(rec + 2 * slot + 1);
-        if ((uint32_t)(lo >> 32) != tag || (uint32_t)(hi >> 32) != tag) return false;
-        v = from_payload<A>((uint32_t)lo, (uint32_t)hi);
-    } else {
-        const uint64_t w = ld_agent(rec + slot);
-        if ((uint32_t)(w >> 32) != tag) return false;
-        v = from_payload<A>((uint32_t)w, 0u);
-    }
+    if ((uint32_t)(w >> 32) != tag) return false;
+    v = __builtin_bit_cast(R, (uint32_t)w);
     return true;
 }
 
@@ -69,24 +65,26 @@ template <class A, int W>
 struct BlockSharedTM {
     A a[W][kWave];
     A b[W][kWave];
-    A carry[kWave];
+    RecOf<A> win_a[kWindowTM][kWave];  // aggregates gathered by the look-back
+    RecOf<A> win_b[kWindowTM][kWave];
+    RecOf<A> carry[kWave];
 };
 
-template <class Op, int E, int W, class A>
-__global__ __launch_bounds__(W * kWave) void scan_kernel_tm(const typename Op::Args args,
-                                                            const SchedTM s)
+// One tile.  F: every lane of the block is an environment and every one of
+// its steps exists (unconditional accesses); otherwise accesses are guarded.
+template <class Op, int E, int W, class A, bool F>
+__device__ __forceinline__ void tile_body_tm(const typename Op::Args& args, const SchedTM& s,
+                                             uint32_t k, uint32_t g, BlockSharedTM<A, W>& sh)
 {
     using T = typename Op::T;
+    using R = RecOf<A>;
     constexpr bool kB = Op::kBackward;
     constexpr uint32_t kSteps = (uint32_t)E * W;
     constexpr int kNear = kB ? 0 : W - 1;  // the wave holding the tile's near edge
-    __shared__ BlockSharedTM<A, W> sh;
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    const uint32_t pos = blockIdx.x / s.groups, g = blockIdx.x % s.groups;
-    const uint32_t k = kB ? s.time_tiles - 1u - pos : pos;  // time tile
     const uint32_t n = g * kWave + lane;
     const bool active = n < s.N;
     const uint32_t t0 = k * kSteps + (uint32_t)wave * E;
@@ -99,7 +97,7 @@ __global__ __launch_bounds__(W * kWave) void scan_kernel_tm(const typename Op::A
         if (t0 == 0) first = 1u;
     }
     const uint32_t col = active ? n : 0u;  // inactive lanes touch nothing (count = 0)
-    const Pos<E, false, true> P{(uint64_t)t0 * s.N + col, col, count, last, first, s.N};
+    const Pos<E, F, true> P{(uint64_t)t0 * s.N + col, col, count, last, first, s.N};
     const Ctx c{(uint64_t)s.N * s.T, s.T, lane, false};
 
     T alpha[E], beta[E];
@@ -126,9 +124,11 @@ __global__ __launch_bounds__(W * kWave) void scan_kernel_tm(const typename Op::A
 #pragma unroll
         for (int j = 0; j < E; ++j) x = combine(Aff<A>{A(alpha[j]), A(beta[j])}, x);
     }
-    sh.a[wave][lane] = x.a;
-    sh.b[wave][lane] = x.b;
-    __syncthreads();
+    if constexpr (W > 1) {
+        sh.a[wave][lane] = x.a;
+        sh.b[wave][lane] = x.b;
+        __syncthreads();
+    }
 
     // Waves between this one and the tile's far edge, nearest first.
     Aff<A> beyond = identity<A>();
@@ -138,100 +138,168 @@ __global__ __launch_bounds__(W * kWave) void scan_kernel_tm(const typename Op::A
         if (w >= 0 && w < W) beyond = combine(beyond, Aff<A>{sh.a[w][lane], sh.b[w][lane]});
     }
 
-    if (wave == kNear) {
+    R carry = R(0);
+    if (wave == kNear && s.time_tiles > 1) {
         WsHeader* hdr = reinterpret_cast<WsHeader*>(s.ws);
         uint64_t* rec = reinterpret_cast<uint64_t*>(s.ws + sizeof(WsHeader));
-        A carry = A(0);
-        if (s.time_tiles > 1) {
-            const uint32_t tag = __builtin_amdgcn_readfirstlane(__hip_atomic_load(
-                                     &hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) + 1u;
-            const Aff<A> tile = combine(x, beyond);
-            const bool far_most = kB ? (k == s.time_tiles - 1u) : (k == 0u);
-            const bool near_most = kB ? (k == 0u) : (k == s.time_tiles - 1u);
-            const uint64_t own = (uint64_t)k * s.N + n;
-            // a cut inside the tile (or nothing beyond it): publish now
-            bool published = !active || near_most;
-            if (!published && (far_most || tile.b == A(0))) {
-                publish_tm<A>(rec, own, tag, tile.a);
-                published = true;
-            }
-            if (active && !far_most) {
-                const uint64_t pred = (uint64_t)(kB ? k + 1u : k - 1u) * s.N + n;
-                uint32_t polls = 0;
-                bool have = false;
-                for (;;) {
-                    if (!have) have = read_tm<A>(rec, pred, tag, carry);
-                    if (__ballot(!have) == 0) break;  // the active lanes poll together
-                    if (++polls > kMaxPolls) {
-                        if (lane == 0)
-                            __hip_atomic_fetch_or(&hdr->error, kErrTimeout, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
-                        if (!have) carry = A(0);
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
-                }
-            }
-            if (!published) publish_tm<A>(rec, own, tag, apply(tile, carry));
-            if (lane == 0) finish_launch(hdr, s.num_blocks, blockIdx.x, tag);
+        const uint64_t plane = (uint64_t)s.time_tiles * s.N;
+        uint64_t* rec_a = rec;
+        uint64_t* rec_b = rec + plane;
+        uint64_t* rec_y = rec + 2 * plane;
+        const uint32_t tag = __builtin_amdgcn_readfirstlane(__hip_atomic_load(
+                                 &hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) + 1u;
+        const Aff<A> tile_map = combine(x, beyond);
+        const Aff<R> tile = {(R)tile_map.a, (R)tile_map.b};  // as published
+        const bool far_most = kB ? (k == s.time_tiles - 1u) : (k == 0u);
+        const bool near_most = kB ? (k == 0u) : (k == s.time_tiles - 1u);
+        const uint64_t own = (uint64_t)k * s.N + n;
+        if (active && !near_most) {
+            // the aggregate first, so that later tiles can look past this one
+            st_agent(rec_a + own, tagged(tag, tile.a));
+            st_agent(rec_b + own, tagged(tag, tile.b));
+            if (far_most || tile.b == R(0)) st_agent(rec_y + own, tagged(tag, tile.a));
         }
-        sh.carry[lane] = carry;
+        if (!far_most) {
+            // Look back along time, per environment, up to the first tile
+            // whose inclusive value is published or whose aggregate has a cut
+            // (b = 0: its value is its a), keeping the open aggregates in
+            // between; then apply them from the far one to the near one.
+            const int step = kB ? 1 : -1;
+            const int64_t last_tile = kB ? (int64_t)s.time_tiles - 1 : 0;  // the far-most one
+            int64_t j = (int64_t)k + step;
+            int depth = 0;
+            bool done = !active;
+            R base = R(0);
+            uint32_t polls = 0;
+            while (__ballot(!done) != 0) {
+                if (!done) {
+                    const uint64_t slot = (uint64_t)j * s.N + n;
+                    R y, a, b;
+                    if (untag(ld_agent(rec_y + slot), tag, y)) {
+                        base = y;
+                        done = true;
+                    } else if (j != last_tile && depth < kWindowTM &&
+                               untag(ld_agent(rec_a + slot), tag, a) &&
+                               untag(ld_agent(rec_b + slot), tag, b)) {
+                        // (at the far-most tile only its y is awaited, so j
+                        // never leaves the array)
+                        if (b == R(0)) {
+                            base = a;
+                            done = true;
+                        } else {
+                            sh.win_a[depth][lane] = a;
+                            sh.win_b[depth][lane] = b;
+                            ++depth;
+                            j += step;
+                        }
+                    }
+                }
+                if (++polls > kMaxPolls) {
+                    if (lane == 0)
+                        __hip_atomic_fetch_or(&hdr->error, kErrTimeout, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+                if (__ballot(!done) != 0) __builtin_amdgcn_s_sleep(1);
+            }
+            carry = base;
+            for (int d = depth - 1; d >= 0; --d)
+                carry = apply(Aff<R>{sh.win_a[d][lane], sh.win_b[d][lane]}, carry);
+            if (active && !near_most && tile.b != R(0))
+                st_agent(rec_y + own, tagged(tag, apply(tile, carry)));
+        }
+        if (lane == 0) finish_launch(hdr, s.num_blocks, blockIdx.x, tag);
     }
-    __syncthreads();
+    if constexpr (W > 1) {
+        if (wave == kNear) sh.carry[lane] = carry;
+        __syncthreads();
+        carry = sh.carry[lane];
+    }
 
-    const T lane_in = T(apply(beyond, sh.carry[lane]));
+    const T lane_in = T(apply(beyond, A(carry)));
     Op::finish(args, P, c, alpha, beta, st, lane_in);
 }
 
-// ------------------------------------------------------------- host side
-constexpr int kTmE = 8;   // steps per lane
-constexpr int kTmW = 16;  // waves per block: 128-step tiles
-
-inline uint64_t tm_time_tiles(uint64_t T) { return (T + kTmE * kTmW - 1) / (kTmE * kTmW); }
-
-// Workspace of a time-major call: the header and up to two words per
-// (tile, environment).  At most the row-major need (32 bytes per 256
-// elements) plus 16 bytes per environment.
-inline size_t workspace_bytes_tm(uint64_t N, uint64_t T)
+template <class Op, int E, int W, class A>
+__global__ __launch_bounds__(W * kWave) void scan_kernel_tm(const typename Op::Args args,
+                                                            const SchedTM s)
 {
-    return sizeof(WsHeader) + 16 * N * tm_time_tiles(T);
+    constexpr uint32_t kSteps = (uint32_t)E * W;
+    __shared__ BlockSharedTM<A, W> sh;
+    // Tiles are taken time-tile-major from the scan's far end.
+    const uint32_t pos = blockIdx.x / s.groups, g = blockIdx.x % s.groups;
+    const uint32_t k = Op::kBackward ? s.time_tiles - 1u - pos : pos;
+    const bool full = (uint64_t)(k + 1u) * kSteps <= s.T && (uint64_t)(g + 1u) * kWave <= s.N;
+    if (full)
+        tile_body_tm<Op, E, W, A, true>(args, s, k, g, sh);
+    else
+        tile_body_tm<Op, E, W, A, false>(args, s, k, g, sh);
 }
 
-template <template <int> class Op, class A>
+// ------------------------------------------------------------- host side
+constexpr int kTmE = 8;        // steps per lane
+constexpr int kTmWSmall = 8;   // waves per block: 64-step tiles, for rows of <= 64 steps
+constexpr int kTmWLarge = 16;  // 128-step tiles otherwise (measured faster from T = 128 up)
+
+inline uint64_t tm_tiles(uint64_t T, int W) { return (T + (uint64_t)kTmE * W - 1) / ((uint64_t)kTmE * W); }
+
+inline int tm_waves(uint64_t T)
+{
+    const int forced = g_forced_tm_waves.load();
+    if (forced > 0) return forced;
+    return T <= (uint64_t)kTmE * kTmWSmall ? kTmWSmall : kTmWLarge;
+}
+
+// Workspace of a time-major call: the header and three words per
+// (64-step tile, environment).
+inline size_t workspace_bytes_tm(uint64_t N, uint64_t T)
+{
+    return sizeof(WsHeader) + 8 * kPlanesTM * N * tm_tiles(T, kTmWSmall);
+}
+
+template <template <int> class Op, int W, class A>
 hipError_t launch_tm(const typename Op<kTmE>::Args& a, const SchedTM& s, hipStream_t stream)
 {
     void* params[] = {(void*)&a, (void*)&s};
-    return hipLaunchKernel((const void*)&scan_kernel_tm<Op<kTmE>, kTmE, kTmW, A>,
-                           dim3(s.num_blocks), dim3(kTmW * kWave), params, 0, stream);
+    return hipLaunchKernel((const void*)&scan_kernel_tm<Op<kTmE>, kTmE, W, A>,
+                           dim3(s.num_blocks), dim3(W * kWave), params, 0, stream);
+}
+
+template <template <int> class Op, int W>
+hipError_t launch_tm_acc(float beta_max, const typename Op<kTmE>::Args& a, const SchedTM& s,
+                         hipStream_t stream)
+{
+    using Val = typename Op<kTmE>::T;
+    if constexpr (std::is_same<Val, float>::value)
+        return beta_max > kFp32BetaMax ? launch_tm<Op, W, double>(a, s, stream)
+                                       : launch_tm<Op, W, float>(a, s, stream);
+    else
+        return launch_tm<Op, W, Val>(a, s, stream);
 }
 
 template <template <int> class Op>
 lrs_status run_tm(const char* name, int64_t N, int64_t T, float beta_max,
                   const typename Op<kTmE>::Args& a, void* ws, size_t ws_bytes, hipStream_t stream)
 {
+    if (N >= (int64_t(1) << 32))
+        return fail(LRS_ERR_INVALID_ARG, "%s: time-major calls need num_envs < 2^32", name);
+    const int W = tm_waves((uint64_t)T);
     SchedTM s{};
     s.N = (uint32_t)N;
     s.T = (uint32_t)T;
     s.groups = (uint32_t)((N + kWave - 1) / kWave);
-    s.time_tiles = (uint32_t)tm_time_tiles((uint64_t)T);
+    s.time_tiles = (uint32_t)tm_tiles((uint64_t)T, W);
     s.num_blocks = s.groups * s.time_tiles;
     s.ws = static_cast<uint8_t*>(ws);
-    if (N >= (int64_t(1) << 32))
-        return fail(LRS_ERR_INVALID_ARG, "%s: time-major calls need num_envs < 2^32", name);
     if (s.time_tiles > 1) {
-        const size_t need = workspace_bytes_tm((uint64_t)N, (uint64_t)T);
+        const size_t need = sizeof(WsHeader) + 8 * kPlanesTM * (size_t)N * s.time_tiles;
         if (ws == nullptr || ws_bytes < need)
             return fail(LRS_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", name,
                         need, ws == nullptr ? (size_t)0 : ws_bytes);
         if (!aligned(ws, 16)) return fail(LRS_ERR_WORKSPACE, "%s: workspace not 16-byte aligned", name);
     }
-    using Val = typename Op<kTmE>::T;
-    hipError_t e;
-    if constexpr (std::is_same<Val, float>::value)
-        e = beta_max > kFp32BetaMax ? launch_tm<Op, double>(a, s, stream)
-                                    : launch_tm<Op, float>(a, s, stream);
-    else
-        e = launch_tm<Op, Val>(a, s, stream);
+    const hipError_t e = W == kTmWLarge ? launch_tm_acc<Op, kTmWLarge>(beta_max, a, s, stream)
+                                        : launch_tm_acc<Op, kTmWSmall>(beta_max, a, s, stream);
     if (e != hipSuccess)
         return fail(LRS_ERR_HIP, "%s: kernel launch failed: %s", name, hipGetErrorString(e));
     g_err[0] = '\0';

@@ -60,8 +60,15 @@ def test_version_and_strings(lib):
     assert lib.lrs_status_string(99) == b"unknown status"
 
 
+def documented_workspace(n, t):
+    """lrs.h: 4224 bytes plus the larger of 32 bytes per 256 elements and
+    24 bytes per env per 64 steps."""
+    return 4224 + max(32 * -(-(n * t) // 256), 24 * n * -(-t // 64))
+
+
 def test_workspace_bytes(lib):
-    assert lib.lrs_workspace_bytes(0, 4096, 128) == 4224 + 32 * (4096 * 128 // 256)
+    for n, t in [(4096, 128), (1, 1), (64, 131072), (3, 1000), (16384, 1024), (1, 65)]:
+        assert lib.lrs_workspace_bytes(0, n, t) == documented_workspace(n, t)
     assert lib.lrs_workspace_bytes(1, 1, 1) == 4224 + 32
     assert lib.lrs_workspace_bytes(0, 0, 128) == 0
     assert lib.lrs_workspace_bytes(0, 5, 0) == 0

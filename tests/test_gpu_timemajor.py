@@ -29,6 +29,15 @@ def _gpu():
         pytest.skip("no GPU")
     lrs.load()
     yield
+    lrs.set_time_major_waves(0)
+
+
+@pytest.fixture(params=[8, 16], ids=["W8", "W16"])
+def waves(request):
+    """Both time-major tile shapes (64- and 128-step tiles)."""
+    lrs.set_time_major_waves(request.param)
+    yield request.param
+    lrs.set_time_major_waves(0)
 
 
 def dev_tm(a, k):
@@ -107,7 +116,7 @@ SHAPES = [(1, 1), (3, 5), (64, 128), (65, 129), (63, 127), (130, 300), (7, 1000)
 
 @pytest.mark.parametrize("est", ESTIMATORS)
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
-def test_small_shapes(shape, est):
+def test_small_shapes(shape, est, waves):
     N, T = shape
     ro = workloads.rollout(N, T, seed=N * 7 + T, term_p=0.05, trunc_p=0.03, gamma=0.97,
                            lambda_=0.9)
@@ -115,7 +124,7 @@ def test_small_shapes(shape, est):
 
 
 @pytest.mark.parametrize("est", ESTIMATORS)
-def test_long_rows_rare_cuts(est):
+def test_long_rows_rare_cuts(est, waves):
     """Carries cross many 128-step tiles (rare episode ends)."""
     N, T = 96, 6000
     ro = workloads.rollout(N, T, seed=71, term_p=2e-4, trunc_p=2e-4, gamma=0.99, lambda_=0.95,
@@ -124,7 +133,7 @@ def test_long_rows_rare_cuts(est):
 
 
 @pytest.mark.parametrize("est", ["discounted_returns", "eligibility_traces", "prefix_sum_f32"])
-def test_undamped_chains(est):
+def test_undamped_chains(est, waves):
     """gamma = lambda = 1 (fp64 composition) over 5000 steps without cuts,
     integer-valued inputs: exact."""
     N, T = 70, 5000
@@ -166,7 +175,7 @@ def test_no_leakage_exact(est):
             assert np.array_equal(x[:, :cut + 1], y[:, :cut + 1])
 
 
-def test_deterministic():
+def test_deterministic(waves):
     ro = workloads.rollout(100, 5000, seed=75, term_p=1e-4, trunc_p=1e-4)
     outs = [[g for g, _ in run_tm("vtrace", ro)] for _ in range(3)]
     for rep in outs[1:]:
@@ -189,7 +198,7 @@ def test_matches_row_major_call():
 
 @pytest.mark.parametrize("reverse", [False, True], ids=["fwd", "rev"])
 @pytest.mark.parametrize("shape", [(65, 129), (200, 3001)], ids=lambda s: f"{s[0]}x{s[1]}")
-def test_affine_scan(shape, reverse):
+def test_affine_scan(shape, reverse, waves):
     N, T = shape
     inp = workloads.affine_inputs(N, T, seed=77, reset_p=0.01, beta_range=(-1.0, 1.0))
     y = lrs.compute_affine_scan(dev_tm(inp["alpha"], "alpha"), dev_tm(inp["beta"], "beta"),
@@ -243,3 +252,9 @@ def test_python_validation_tm():
         lrs.compute_gae(x, torch.zeros(4, 8, device="cuda"), x, time_major=True)
     with pytest.raises(ValueError):  # bootstrap is per env: [num_envs] = [4]
         lrs.compute_gae(x, x, x, bootstrap_value=torch.zeros(8, device="cuda"), time_major=True)
+
+
+def test_time_major_waves_validation():
+    with pytest.raises(Exception):
+        lrs.set_time_major_waves(4)
+    lrs.set_time_major_waves(0)
