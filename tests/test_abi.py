@@ -130,6 +130,27 @@ def test_affine_scan_rejects(lib):
         assert lib.lrs_last_error().startswith(b"lrs_affine_scan_f32")
 
 
+def test_time_major_and_16bit_entry_points_reject(lib):
+    for name in ["lrs_gae_tm_f32", "lrs_gae_bf16", "lrs_gae_tm_f16"]:
+        fn = getattr(lib, name)
+        assert fn(0, 8, FAKE, FAKE, FAKE, None, None, None, 0.9, 0.9, FAKE, None, 0, None) == 1
+        assert fn(4, 8, FAKE, FAKE, None, None, None, None, 0.9, 0.9, FAKE, None, 0, None) == 1
+        assert lib.lrs_last_error().startswith(name.encode())
+    assert lib.lrs_episodic_prefix_sum_tm_i32(4, 8, FAKE, None, FAKE, None, 0, None) == 1
+    assert lib.lrs_affine_scan_tm_bf16(4, 8, FAKE, FAKE, None, None, 3, FAKE, None, 0, None) == 1
+    # time-major calls with more than one tile need the workspace
+    st = lib.lrs_discounted_returns_tm_f32(4, 1000, FAKE, FAKE, None, None, None, 0.9, FAKE, None,
+                                           0, None)
+    assert st == 2 and b"workspace" in lib.lrs_last_error()
+
+
+def test_time_major_waves_validation(lib):
+    for w in (1, 4, 12, 32, -1):
+        assert lib.lrs_debug_set_time_major_waves(w) == 1
+    for w in (8, 16, 0):
+        assert lib.lrs_debug_set_time_major_waves(w) == 0
+
+
 def test_debug_schedule_validation(lib):
     assert lib.lrs_debug_set_schedule(0, 3, 4) == 1
     assert lib.lrs_debug_set_schedule(0, 8, 2) == 1
@@ -146,6 +167,10 @@ def test_python_api_has_no_cpu_path():
         lrs.compute_episodic_prefix_sum(x.int(), x)
     with pytest.raises(ValueError, match="GPU"):
         lrs.compute_affine_scan(x, x)
+    with pytest.raises(ValueError, match="GPU"):
+        lrs.compute_gae(x, x, x, time_major=True)
+    with pytest.raises(ValueError, match="GPU"):
+        lrs.compute_vtrace(x.bfloat16(), x.bfloat16(), x.bfloat16(), x)
 
 
 def test_product_does_not_reference_the_oracle():
