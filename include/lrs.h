@@ -50,6 +50,11 @@
  *     not be modified between calls.  Calls that share one workspace must be
  *     ordered on one stream (concurrent use of one workspace races).  May be
  *     NULL with workspace_bytes 0 when lrs_workspace_bytes returns 0.
+ *     Its first 4224 bytes are a header the calls maintain; the 32-bit word at
+ *     byte offset 4 is an error word that a call sets (bit 1, value 2) if one
+ *     of its carry waits gave up after its bounded number of polls (results
+ *     of that call are then wrong); it stays set until the caller clears it.
+ *     Reading it after synchronising is a cheap health check.
  *   - stream: the HIP stream to enqueue on (NULL = the null stream).  Calls
  *     are asynchronous; the library never allocates, frees or synchronises.
  *   - Errors: argument checks run on the host before anything is enqueued

@@ -18,11 +18,12 @@ from .api import (  # noqa: F401
     load,
     set_schedule,
     set_time_major_waves,
+    workspace_state,
 )
 
 __all__ = [
     "compute_gae", "compute_vtrace", "compute_retrace", "compute_lambda_returns",
     "compute_discounted_returns", "compute_eligibility_traces", "compute_episodic_prefix_sum",
     "compute_affine_scan",
-    "LrsError", "load", "lib_path", "set_schedule", "set_time_major_waves",
+    "LrsError", "load", "lib_path", "set_schedule", "set_time_major_waves", "workspace_state",
 ]

@@ -161,6 +161,22 @@ def workspace(device: torch.device, stream: torch.cuda.Stream, est: str, n: int,
     return ws
 
 
+def workspace_state():
+    """Diagnostics: synchronize, then read the header of every cached workspace.
+    Returns a list of dicts: epoch (launches that used the carry protocol),
+    error (nonzero: a carry wait gave up, bit 2 = timeout), top and
+    counters_nonzero (both 0 between launches: every launch resets them)."""
+    import numpy as np
+    torch.cuda.synchronize()
+    out = []
+    for ws in _workspaces.values():
+        h = ws[:4224].cpu().numpy().view(np.uint32)
+        counts = h[32::32][:32]  # one counter per 128-byte line after the first
+        out.append({"epoch": int(h[0]), "error": int(h[1]), "top": int(h[2]),
+                    "counters_nonzero": int(np.count_nonzero(counts))})
+    return out
+
+
 def _dev_tensor(x, name, dtype, shape, device):
     if not isinstance(x, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")

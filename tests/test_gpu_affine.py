@@ -188,3 +188,11 @@ def test_python_validation_on_gpu():
         lrs.compute_affine_scan(x, x, carry_in=torch.zeros(5, device="cuda"))
     with pytest.raises(TypeError):
         lrs.compute_affine_scan(x, x.double())
+
+
+def test_zz_workspace_headers_clean():
+    """No carry wait of any launch above gave up, and every launch left the
+    completion counters reset."""
+    for h in lrs.workspace_state():
+        assert h["error"] == 0, h
+        assert h["top"] == 0 and h["counters_nonzero"] == 0, h

@@ -237,3 +237,11 @@ def test_full_long_64x131072_bf16(est):
     ro = workloads.rollout(p["num_envs"], p["seq_len"], seed=0, term_p=p["term_p"],
                            trunc_p=p["trunc_p"], gamma=p["gamma"], lambda_=p["lambda_"])
     run_case(est, ro, "bf16")
+
+
+def test_zz_workspace_headers_clean():
+    """No carry wait of any launch above gave up, and every launch left the
+    completion counters reset."""
+    for h in lrs.workspace_state():
+        assert h["error"] == 0, h
+        assert h["top"] == 0 and h["counters_nonzero"] == 0, h

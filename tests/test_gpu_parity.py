@@ -368,3 +368,11 @@ def test_python_validation_on_gpu():
         lrs.compute_gae(x, x, x, truncateds=x)
     with pytest.raises(TypeError):
         lrs.compute_gae(x.double(), x, x)
+
+
+def test_zz_workspace_headers_clean():
+    """No carry wait of any launch above gave up, and every launch left the
+    completion counters reset."""
+    for h in lrs.workspace_state():
+        assert h["error"] == 0, h
+        assert h["top"] == 0 and h["counters_nonzero"] == 0, h

@@ -258,3 +258,11 @@ def test_time_major_waves_validation():
     with pytest.raises(Exception):
         lrs.set_time_major_waves(4)
     lrs.set_time_major_waves(0)
+
+
+def test_zz_workspace_headers_clean():
+    """No carry wait of any launch above gave up, and every launch left the
+    completion counters reset."""
+    for h in lrs.workspace_state():
+        assert h["error"] == 0, h
+        assert h["top"] == 0 and h["counters_nonzero"] == 0, h
