@@ -19,7 +19,8 @@ Prints one JSON line.  value = elements processed per step / step time
 algorithmic bytes (one read of every input stream, one write of every
 output) over its average duration, measured with HIP events around a graph
 of >= 64 back-to-back launches of that call (cycling over its replicas) on
-the launch stream.  cpu_baseline:
+the launch stream; copy_same_bytes times a plain device copy of the same
+bytes the same way, for context.  cpu_baseline:
 the fp64 oracle on the host cores, whole steps on the same batch.
 """
 from __future__ import annotations
@@ -314,6 +315,40 @@ def committed_traffic(call):
     return traffic.get(call)
 
 
+def copy_reference(alg_bytes, stream, reps):
+    """A plain device copy moving the dominant call's algorithmic bytes (half
+    read, half written), timed like the calls: cold buffers (>= 1 GiB of
+    them, cycled), a HIP graph of >= 64 back-to-back launches, events around
+    it.  The per-launch time no kernel of this size can beat by much, for
+    context beside the roofline fraction."""
+    import torch
+    half = max(4, alg_bytes // 2) // 4  # fp32 elements per side
+    pairs = max(8, -(-(1 << 30) // (8 * half)))
+    bufs = [(torch.empty(half, device=stream.device), torch.empty(half, device=stream.device))
+            for _ in range(pairs)]
+    launches = max(64, pairs)
+    with torch.cuda.stream(stream):
+        for src, dst in bufs[:2]:
+            dst.copy_(src)
+        stream.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=stream):
+            for i in range(launches):
+                src, dst = bufs[i % pairs]
+                dst.copy_(src)
+        gr.replay()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(reps):
+            gr.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / (reps * launches)
+    del bufs
+    return {"us": round(us, 3), "GBps": round(8 * half / us / 1e3, 1)}
+
+
 def run_eager(args, steps_fns, stream):
     """Counter-collection mode: the same calls, launched one by one."""
     import torch
@@ -512,6 +547,7 @@ def main():
     value = elems_per_step / (ms_per_step * 1e-3) / 1e9
     dom = max(per_call, key=lambda k_: per_call[k_]["us"])
     achieved = per_call[dom]["GBps"]
+    copy_ref = copy_reference(per_call[dom]["alg_bytes"], stream, args.roofline_reps)
     cfg = {"workload": name, "calls_per_step": len(calls),
            "cache": "warm" if args.warm else "cold",
            "replicas": {f"{n}x{t}": nrep[(n, t)] for n, t in shapes},
@@ -538,7 +574,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": committed_traffic(dom) if name == DEFAULT_WORKLOAD else None,
-                     "alg_bytes": per_call[dom]["alg_bytes"]},
+                     "alg_bytes": per_call[dom]["alg_bytes"],
+                     "copy_same_bytes": copy_ref},
         "per_call": per_call,
     }
     if not args.no_cpu_baseline:
