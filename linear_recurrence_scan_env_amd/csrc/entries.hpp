@@ -58,9 +58,8 @@ template <class D> struct AffineSel {
 
 template <class D>
 lrs_status gae_entry(const char* nm, bool tm, int64_t N, int64_t T, const D* rewards,
-                     const D* values,
-                     const uint8_t* term, const uint8_t* trunc, const D* tv, const D* boot,
-                     float gamma, float lambda, D* adv, void* ws, size_t ws_bytes,
+                     const D* values, const uint8_t* term, const uint8_t* trunc, const D* tv,
+                     const D* boot, float gamma, float lambda, D* adv, void* ws, size_t ws_bytes,
                      hipStream_t stream)
 {
     LRS_TRY(check_common(nm, N, T));
@@ -73,19 +72,17 @@ lrs_status gae_entry(const char* nm, bool tm, int64_t N, int64_t T, const D* rew
     const void* f[] = {rewards, values, adv, tv};
     const void* m[] = {term, trunc};
     using S = GaeSel<D>;
-    return trunc ? run_layout<S::template T>(tm, nm, N, T, a.gl, a, f, 4, m, 2, ws, ws_bytes,
-                                             stream)
-                 : run_layout<S::template N>(tm, nm, N, T, a.gl, a, f, 4, m, 2, ws, ws_bytes,
-                                             stream);
+    return trunc
+        ? run_layout<S::template T>(tm, nm, N, T, a.gl, a, f, 4, m, 2, ws, ws_bytes, stream)
+        : run_layout<S::template N>(tm, nm, N, T, a.gl, a, f, 4, m, 2, ws, ws_bytes, stream);
 }
 
 template <class D>
 lrs_status vtrace_entry(const char* nm, bool tm, int64_t N, int64_t T, const D* log_rhos,
-                        const D* rewards,
-                        const D* values, const uint8_t* term, const uint8_t* trunc, const D* tv,
-                        const D* boot, float gamma, float lambda, float rho_bar, float c_bar,
-                        float pg_rho_bar, D* vs, D* pg_adv, void* ws, size_t ws_bytes,
-                        hipStream_t stream)
+                        const D* rewards, const D* values, const uint8_t* term,
+                        const uint8_t* trunc, const D* tv, const D* boot, float gamma, float lambda,
+                        float rho_bar, float c_bar, float pg_rho_bar, D* vs, D* pg_adv, void* ws,
+                        size_t ws_bytes, hipStream_t stream)
 {
     LRS_TRY(check_common(nm, N, T));
     LRS_REQUIRE(log_rhos && rewards && values && vs && pg_adv,
@@ -101,10 +98,9 @@ lrs_status vtrace_entry(const char* nm, bool tm, int64_t N, int64_t T, const D* 
     const void* m[] = {term, trunc};
     using S = VtraceSel<D>;
     const float beta_max = gamma * lambda * c_bar;  // beta_t = gamma * c_t <= this
-    return trunc ? run_layout<S::template T>(tm, nm, N, T, beta_max, a, f, 6, m, 2, ws, ws_bytes,
-                                             stream)
-                 : run_layout<S::template N>(tm, nm, N, T, beta_max, a, f, 6, m, 2, ws, ws_bytes,
-                                             stream);
+    return trunc
+        ? run_layout<S::template T>(tm, nm, N, T, beta_max, a, f, 6, m, 2, ws, ws_bytes, stream)
+        : run_layout<S::template N>(tm, nm, N, T, beta_max, a, f, 6, m, 2, ws, ws_bytes, stream);
 }
 
 template <class D>
@@ -127,10 +123,9 @@ lrs_status retrace_entry(const char* nm, bool tm, int64_t N, int64_t T, const D*
     const void* m[] = {term, trunc};
     using S = RetraceSel<D>;
     const float beta_max = gamma * lambda * c_bar;  // beta_t = gamma * c_t <= this
-    return trunc ? run_layout<S::template T>(tm, nm, N, T, beta_max, a, f, 6, m, 2, ws, ws_bytes,
-                                             stream)
-                 : run_layout<S::template N>(tm, nm, N, T, beta_max, a, f, 6, m, 2, ws, ws_bytes,
-                                             stream);
+    return trunc
+        ? run_layout<S::template T>(tm, nm, N, T, beta_max, a, f, 6, m, 2, ws, ws_bytes, stream)
+        : run_layout<S::template N>(tm, nm, N, T, beta_max, a, f, 6, m, 2, ws, ws_bytes, stream);
 }
 
 template <class D>
@@ -151,10 +146,9 @@ lrs_status lambda_returns_entry(const char* nm, bool tm, int64_t N, int64_t T, c
     const void* f[] = {rewards, values, out, tv};
     const void* m[] = {term, trunc};
     using S = LambdaSel<D>;
-    return trunc ? run_layout<S::template T>(tm, nm, N, T, a.gl, a, f, 4, m, 2, ws, ws_bytes,
-                                             stream)
-                 : run_layout<S::template N>(tm, nm, N, T, a.gl, a, f, 4, m, 2, ws, ws_bytes,
-                                             stream);
+    return trunc
+        ? run_layout<S::template T>(tm, nm, N, T, a.gl, a, f, 4, m, 2, ws, ws_bytes, stream)
+        : run_layout<S::template N>(tm, nm, N, T, a.gl, a, f, 4, m, 2, ws, ws_bytes, stream);
 }
 
 template <class D>
@@ -171,10 +165,9 @@ lrs_status discounted_returns_entry(const char* nm, bool tm, int64_t N, int64_t 
     const void* f[] = {rewards, out, tv};
     const void* m[] = {term, trunc};
     using S = DiscSel<D>;
-    return trunc ? run_layout<S::template T>(tm, nm, N, T, gamma, a, f, 3, m, 2, ws, ws_bytes,
-                                             stream)
-                 : run_layout<S::template N>(tm, nm, N, T, gamma, a, f, 3, m, 2, ws, ws_bytes,
-                                             stream);
+    return trunc
+        ? run_layout<S::template T>(tm, nm, N, T, gamma, a, f, 3, m, 2, ws, ws_bytes, stream)
+        : run_layout<S::template N>(tm, nm, N, T, gamma, a, f, 3, m, 2, ws, ws_bytes, stream);
 }
 
 template <class D>
@@ -195,8 +188,8 @@ lrs_status eligibility_traces_entry(const char* nm, bool tm, int64_t N, int64_t 
 
 template <class D>
 lrs_status prefix_sum_entry(const char* nm, bool tm, int64_t N, int64_t T, const D* x,
-                            const uint8_t* dones,
-                            D* out, void* ws, size_t ws_bytes, hipStream_t stream)
+                            const uint8_t* dones, D* out, void* ws, size_t ws_bytes,
+                            hipStream_t stream)
 {
     LRS_TRY(check_common(nm, N, T));
     LRS_REQUIRE(x && dones && out, "%s: x, dones and sums are required", nm);
@@ -208,9 +201,8 @@ lrs_status prefix_sum_entry(const char* nm, bool tm, int64_t N, int64_t T, const
 }
 
 inline lrs_status prefix_sum_i32_entry(const char* nm, bool tm, int64_t N, int64_t T,
-                                       const int32_t* x,
-                                       const uint8_t* dones, int32_t* out, void* ws,
-                                       size_t ws_bytes, hipStream_t stream)
+                                       const int32_t* x, const uint8_t* dones, int32_t* out,
+                                       void* ws, size_t ws_bytes, hipStream_t stream)
 {
     LRS_TRY(check_common(nm, N, T));
     LRS_REQUIRE(x && dones && out, "%s: x, dones and sums are required", nm);
@@ -222,9 +214,8 @@ inline lrs_status prefix_sum_i32_entry(const char* nm, bool tm, int64_t N, int64
 
 template <class D>
 lrs_status affine_scan_entry(const char* nm, bool tm, int64_t N, int64_t T, const D* alpha,
-                             const D* beta,
-                             const uint8_t* reset, const D* carry_in, int reverse, D* out,
-                             void* ws, size_t ws_bytes, hipStream_t stream)
+                             const D* beta, const uint8_t* reset, const D* carry_in, int reverse,
+                             D* out, void* ws, size_t ws_bytes, hipStream_t stream)
 {
     LRS_TRY(check_common(nm, N, T));
     LRS_REQUIRE(alpha && beta && out, "%s: alpha, beta and out are required", nm);
@@ -233,16 +224,15 @@ lrs_status affine_scan_entry(const char* nm, bool tm, int64_t N, int64_t T, cons
     const void* f[] = {alpha, beta, out};
     const void* m[] = {reset};
     using S = AffineSel<D>;
-    const float beta_max = INFINITY;  // caller coefficients: no bound known
+    const float bm = INFINITY;  // caller coefficients: no bound on beta is known
     if (reverse)
-        return reset ? run_layout<S::template RevR>(tm, nm, N, T, beta_max, a, f, 3, m, 1, ws,
-                                                    ws_bytes, stream)
-                     : run_layout<S::template RevN>(tm, nm, N, T, beta_max, a, f, 3, m, 1, ws,
-                                                    ws_bytes, stream);
-    return reset ? run_layout<S::template FwdR>(tm, nm, N, T, beta_max, a, f, 3, m, 1, ws, ws_bytes,
-                                                stream)
-                 : run_layout<S::template FwdN>(tm, nm, N, T, beta_max, a, f, 3, m, 1, ws, ws_bytes,
-                                                stream);
+        return reset ? run_layout<S::template RevR>(tm, nm, N, T, bm, a, f, 3, m, 1, ws, ws_bytes,
+                                                    stream)
+                     : run_layout<S::template RevN>(tm, nm, N, T, bm, a, f, 3, m, 1, ws, ws_bytes,
+                                                    stream);
+    return reset
+        ? run_layout<S::template FwdR>(tm, nm, N, T, bm, a, f, 3, m, 1, ws, ws_bytes, stream)
+        : run_layout<S::template FwdN>(tm, nm, N, T, bm, a, f, 3, m, 1, ws, ws_bytes, stream);
 }
 
 }  // namespace lrs
