@@ -39,9 +39,9 @@ struct Ctx {
 // lane order: lane L-1) and reads memory only in lane 0, which holds the
 // wave's last chunk.  `used` (the lane's last element is not a row end)
 // guarantees i0+E < N*T.
-template <int E, bool F, bool TM, class D>
+template <int E, bool F, bool TM, bool NT, class D>
 __device__ __forceinline__ float next_elem(float my0, const D* __restrict__ p,
-                                           const Pos<E, F, TM>& P, const Ctx& c, bool used)
+                                           const Pos<E, F, TM, NT>& P, const Ctx& c, bool used)
 {
     if constexpr (TM) {
         // time-major: the successor is the same row's next step, E rows on
@@ -66,8 +66,8 @@ __device__ __forceinline__ float next_elem(float my0, const D* __restrict__ p,
 
 // The successor of the lane's last element is read only when that element
 // is not the last of its row.
-template <int E, bool F, bool TM>
-__device__ __forceinline__ bool successor_used(const Pos<E, F, TM>& P)
+template <int E, bool F, bool TM, bool NT>
+__device__ __forceinline__ bool successor_used(const Pos<E, F, TM, NT>& P)
 {
     return P.count == E && !((P.last >> (E - 1)) & 1u);
 }
@@ -91,8 +91,8 @@ struct BoundaryArgs {
     int has_boot;           // passes another input array and has_boot = 0
 };
 
-template <int E, bool F, bool TM, bool kTrunc, class D>
-__device__ __forceinline__ Ends<E> load_ends(const BoundaryArgs<D>& b, const Pos<E, F, TM>& P,
+template <int E, bool F, bool TM, bool NT, bool kTrunc, class D>
+__device__ __forceinline__ Ends<E> load_ends(const BoundaryArgs<D>& b, const Pos<E, F, TM, NT>& P,
                                              const Ctx& c)
 {
     const uint32_t tau = load_mask<E>(b.term, P, c.vec);
@@ -131,8 +131,8 @@ __device__ __forceinline__ Ends<E> load_ends(const BoundaryArgs<D>& b, const Pos
 }
 
 // Elements past the end of the array are identities.
-template <int E, bool F, bool TM, class T>
-__device__ __forceinline__ void clear_tail(T (&alpha)[E], T (&beta)[E], const Pos<E, F, TM>& P)
+template <int E, bool F, bool TM, bool NT, class T>
+__device__ __forceinline__ void clear_tail(T (&alpha)[E], T (&beta)[E], const Pos<E, F, TM, NT>& P)
 {
     if (F) return;
 #pragma unroll
@@ -174,18 +174,19 @@ struct GaeOp {
     static constexpr int kElemBytes = sizeof(D);
     static constexpr bool kBackward = true;
     static constexpr bool kWideTiles = true;
+    static constexpr bool kStreamLoads = true;
     struct State {
         uint32_t end;
     };
 
-    template <bool F, bool TM>
-    __device__ static void prepare(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT>
+    __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
         float r[E], v[E];
         load_f32<E>(r, a.rewards, P, c.vec);
         load_f32<E>(v, a.values, P, c.vec);
-        const Ends<E> e = load_ends<E, F, TM, kTrunc>(a.b, P, c);
+        const Ends<E> e = load_ends<E, F, TM, NT, kTrunc>(a.b, P, c);
         const float vnx = next_elem<E>(v[0], a.values, P, c, successor_used(P));
 #pragma unroll
         for (int j = 0; j < E; ++j) {
@@ -199,8 +200,8 @@ struct GaeOp {
         s.end = e.end;
     }
     __device__ static bool far_open(const State& s) { return !((s.end >> (E - 1)) & 1u); }
-    template <bool F, bool TM>
-    __device__ static void finish(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT>
+    __device__ static void finish(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
                                   const float (&alpha)[E], const float (&beta)[E], const State&,
                                   float carry)
     {
@@ -230,18 +231,20 @@ struct LambdaOp {
     static constexpr int kElemBytes = sizeof(D);
     static constexpr bool kBackward = true;
     static constexpr bool kWideTiles = true;
+    // non-temporal input loads measure slower for this op on long rows
+    static constexpr bool kStreamLoads = false;
     struct State {
         uint32_t end;
     };
 
-    template <bool F, bool TM>
-    __device__ static void prepare(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT>
+    __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
         float r[E], v[E];
         load_f32<E>(r, a.rewards, P, c.vec);
         load_f32<E>(v, a.values, P, c.vec);
-        const Ends<E> e = load_ends<E, F, TM, kTrunc>(a.b, P, c);
+        const Ends<E> e = load_ends<E, F, TM, NT, kTrunc>(a.b, P, c);
         const float vnx = next_elem<E>(v[0], a.values, P, c, successor_used(P));
 #pragma unroll
         for (int j = 0; j < E; ++j) {
@@ -254,8 +257,8 @@ struct LambdaOp {
         s.end = e.end;
     }
     __device__ static bool far_open(const State& s) { return !((s.end >> (E - 1)) & 1u); }
-    template <bool F, bool TM>
-    __device__ static void finish(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT>
+    __device__ static void finish(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
                                   const float (&alpha)[E], const float (&beta)[E], const State&,
                                   float carry)
     {
@@ -283,17 +286,18 @@ struct DiscOp {
     static constexpr int kElemBytes = sizeof(D);
     static constexpr bool kBackward = true;
     static constexpr bool kWideTiles = true;
+    static constexpr bool kStreamLoads = true;
     struct State {
         uint32_t end;
     };
 
-    template <bool F, bool TM>
-    __device__ static void prepare(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT>
+    __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
         float r[E];
         load_f32<E>(r, a.rewards, P, c.vec);
-        const Ends<E> e = load_ends<E, F, TM, kTrunc>(a.b, P, c);
+        const Ends<E> e = load_ends<E, F, TM, NT, kTrunc>(a.b, P, c);
 #pragma unroll
         for (int j = 0; j < E; ++j) {
             const bool end = (e.end >> j) & 1u;
@@ -304,8 +308,8 @@ struct DiscOp {
         s.end = e.end;
     }
     __device__ static bool far_open(const State& s) { return !((s.end >> (E - 1)) & 1u); }
-    template <bool F, bool TM>
-    __device__ static void finish(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT>
+    __device__ static void finish(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
                                   const float (&alpha)[E], const float (&beta)[E], const State&,
                                   float carry)
     {
@@ -340,20 +344,21 @@ struct VtraceOp {
     // Whole rows of 4096 or 8192 in one block (E = 8 or 16 waves) cost
     // this op occupancy: its per-element state needs more registers.
     static constexpr bool kWideTiles = false;
+    static constexpr bool kStreamLoads = true;
     struct State {
         uint32_t end;
         float r[E], v[E], tgt[E], rho_pg[E];  // tgt: Vnext at ends, V_{t+1} elsewhere
     };
 
-    template <bool F, bool TM>
-    __device__ static void prepare(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT>
+    __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
         float lr[E];
         load_f32<E>(lr, a.log_rhos, P, c.vec);
         load_f32<E>(s.r, a.rewards, P, c.vec);
         load_f32<E>(s.v, a.values, P, c.vec);
-        const Ends<E> e = load_ends<E, F, TM, kTrunc>(a.b, P, c);
+        const Ends<E> e = load_ends<E, F, TM, NT, kTrunc>(a.b, P, c);
         const float vnx = next_elem<E>(s.v[0], a.values, P, c, successor_used(P));
 #pragma unroll
         for (int j = 0; j < E; ++j) {
@@ -372,8 +377,8 @@ struct VtraceOp {
         s.end = e.end;
     }
     __device__ static bool far_open(const State& s) { return !((s.end >> (E - 1)) & 1u); }
-    template <bool F, bool TM>
-    __device__ static void finish(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT>
+    __device__ static void finish(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
                                   const float (&alpha)[E], const float (&beta)[E], const State& s,
                                   float carry)
     {
@@ -418,6 +423,7 @@ struct RetraceOp {
     // Whole rows of 4096 or 8192 in one block (E = 8 or 16 waves) cost
     // this op occupancy: its per-element state needs more registers.
     static constexpr bool kWideTiles = false;
+    static constexpr bool kStreamLoads = true;
     struct State {
         uint32_t end;
     };
@@ -427,8 +433,8 @@ struct RetraceOp {
         return a.lambda * fminf(a.c_bar, expf(lr));
     }
 
-    template <bool F, bool TM>
-    __device__ static void prepare(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT>
+    __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
         float lr[E], r[E], q[E], v[E], cc[E];
@@ -436,7 +442,7 @@ struct RetraceOp {
         load_f32<E>(r, a.rewards, P, c.vec);
         load_f32<E>(q, a.q_values, P, c.vec);
         load_f32<E>(v, a.values, P, c.vec);
-        const Ends<E> e = load_ends<E, F, TM, kTrunc>(a.b, P, c);
+        const Ends<E> e = load_ends<E, F, TM, NT, kTrunc>(a.b, P, c);
         const bool used = successor_used(P);
         // successor (t+1) quantities of the lane's last element
         const float lrnx = next_elem<E>(lr[0], a.log_rhos, P, c, used);
@@ -458,8 +464,8 @@ struct RetraceOp {
         s.end = e.end;
     }
     __device__ static bool far_open(const State& s) { return !((s.end >> (E - 1)) & 1u); }
-    template <bool F, bool TM>
-    __device__ static void finish(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT>
+    __device__ static void finish(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
                                   const float (&alpha)[E], const float (&beta)[E], const State&,
                                   float carry)
     {
@@ -473,9 +479,9 @@ struct RetraceOp {
 // reset_j = first-in-row_j | dones_{j-1}.  dones of the element before the
 // lane comes from the neighbouring lane (lane 0 of a wave reads it, except
 // at a row start where it is not needed).
-template <int E, bool F, bool TM>
+template <int E, bool F, bool TM, bool NT>
 __device__ __forceinline__ uint32_t load_resets(const uint8_t* __restrict__ dones,
-                                                const Pos<E, F, TM>& P, const Ctx& c)
+                                                const Pos<E, F, TM, NT>& P, const Ctx& c)
 {
     const uint32_t d = load_mask<E>(dones, P, c.vec);
     uint32_t dprev;
@@ -518,11 +524,12 @@ struct EligOp {
     static constexpr int kElemBytes = sizeof(D);
     static constexpr bool kBackward = false;
     static constexpr bool kWideTiles = true;
+    static constexpr bool kStreamLoads = true;
     struct State {
         uint32_t reset;
     };
-    template <bool F, bool TM>
-    __device__ static void prepare(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT>
+    __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
         load_f32<E>(alpha, (const D*)a.x, P, c.vec);
@@ -532,8 +539,8 @@ struct EligOp {
         clear_tail(alpha, beta, P);
     }
     __device__ static bool far_open(const State& s) { return !(s.reset & 1u); }
-    template <bool F, bool TM>
-    __device__ static void finish(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT>
+    __device__ static void finish(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
                                   const float (&alpha)[E], const float (&beta)[E], const State&,
                                   float carry)
     {
@@ -556,11 +563,12 @@ struct PrefixF32Op {
     static constexpr int kElemBytes = sizeof(D);
     static constexpr bool kBackward = false;
     static constexpr bool kWideTiles = true;
+    static constexpr bool kStreamLoads = true;
     struct State {
         uint32_t reset;
     };
-    template <bool F, bool TM>
-    __device__ static void prepare(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT>
+    __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
         load_f32<E>(alpha, (const D*)a.x, P, c.vec);
@@ -570,8 +578,8 @@ struct PrefixF32Op {
         clear_tail(alpha, beta, P);
     }
     __device__ static bool far_open(const State& s) { return !(s.reset & 1u); }
-    template <bool F, bool TM>
-    __device__ static void finish(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT>
+    __device__ static void finish(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
                                   const float (&alpha)[E], const float (&beta)[E], const State& s,
                                   float carry)
     {
@@ -594,11 +602,12 @@ struct PrefixI32Op {
     static constexpr int kElemBytes = 4;
     static constexpr bool kBackward = false;
     static constexpr bool kWideTiles = true;
+    static constexpr bool kStreamLoads = true;
     struct State {
         uint32_t reset;
     };
-    template <bool F, bool TM>
-    __device__ static void prepare(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT>
+    __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
                                    uint32_t (&alpha)[E], uint32_t (&beta)[E], State& s)
     {
         load_u32<E>(alpha, (const int32_t*)a.x, P, c.vec);
@@ -608,8 +617,8 @@ struct PrefixI32Op {
         clear_tail(alpha, beta, P);
     }
     __device__ static bool far_open(const State& s) { return !(s.reset & 1u); }
-    template <bool F, bool TM>
-    __device__ static void finish(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT>
+    __device__ static void finish(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
                                   const uint32_t (&alpha)[E], const uint32_t (&beta)[E],
                                   const State& s, uint32_t carry)
     {
@@ -648,12 +657,13 @@ struct AffineOp {
     static constexpr int kElemBytes = sizeof(D);
     static constexpr bool kBackward = kRev;
     static constexpr bool kWideTiles = true;
+    static constexpr bool kStreamLoads = true;
     struct State {
         uint32_t cut;
     };
 
-    template <bool F, bool TM>
-    __device__ static void prepare(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT>
+    __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
         load_f32<E>(alpha, a.alpha, P, c.vec);
@@ -694,8 +704,8 @@ struct AffineOp {
     {
         return kRev ? !((s.cut >> (E - 1)) & 1u) : !(s.cut & 1u);
     }
-    template <bool F, bool TM>
-    __device__ static void finish(const Args& a, const Pos<E, F, TM>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT>
+    __device__ static void finish(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
                                   const float (&alpha)[E], const float (&beta)[E], const State&,
                                   float carry)
     {

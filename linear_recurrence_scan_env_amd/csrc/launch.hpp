@@ -125,9 +125,9 @@ struct BlockShared {
 // Everything after the positions are known.  F: the tile lies wholly inside
 // the array and the base pointers are vector aligned (straight-line vector
 // loads and stores); otherwise every access is guarded by the lane's count.
-template <class Op, int E, int W, class A, bool F>
+template <class Op, int E, int W, class A, bool F, bool NT>
 __device__ __forceinline__ void tile_body(const typename Op::Args& args, const Sched& s,
-                                          uint32_t tile, const Pos<E, F>& P, const Ctx& c,
+                                          uint32_t tile, const Pos<E, F, false, NT>& P, const Ctx& c,
                                           BlockShared<A, W>& sh)
 {
     using T = typename Op::T;  // A: the composition type (fp32 or fp64 for fp32 maps)
@@ -232,7 +232,7 @@ __device__ __forceinline__ void tile_body(const typename Op::Args& args, const S
     Op::finish(args, P, c, alpha, beta, st, lane_in);
 }
 
-template <class Op, int E, int W, class A>
+template <class Op, int E, int W, class A, bool NT>
 __global__ __launch_bounds__(W * kWave) void scan_kernel(const typename Op::Args args, const Sched s)
 {
     constexpr bool kB = Op::kBackward;
@@ -283,12 +283,12 @@ __global__ __launch_bounds__(W * kWave) void scan_kernel(const typename Op::Args
     const Ctx c{s.total, s.T, tid & (kWave - 1), s.vec != 0};
 
     if (s.vec && tile_start + kTile <= s.total && s.T >= (uint32_t)E) {
-        const Pos<E, true> P{i0, n0, E, last, first};
-        tile_body<Op, E, W, A, true>(args, s, tile, P, c, sh);
+        const Pos<E, true, false, NT> P{i0, n0, E, last, first};
+        tile_body<Op, E, W, A, true, NT>(args, s, tile, P, c, sh);
     } else {
         const uint32_t valid = (count >= 32) ? ~0u : ((1u << count) - 1u);
-        const Pos<E, false> P{i0, n0, count, last & valid, first & valid};
-        tile_body<Op, E, W, A, false>(args, s, tile, P, c, sh);
+        const Pos<E, false, false, NT> P{i0, n0, count, last & valid, first & valid};
+        tile_body<Op, E, W, A, false, NT>(args, s, tile, P, c, sh);
     }
 }
 
@@ -389,25 +389,32 @@ inline int choose_cfg(uint64_t total, uint64_t T, bool wide_ok, int elem_bytes, 
 
 inline bool aligned(const void* p, uintptr_t a) { return p == nullptr || ((uintptr_t)p % a) == 0; }
 
-template <class Op, int E, int W, class A>
+template <class Op, int E, int W, class A, bool NT = false>
 hipError_t launch_cfg(const typename Op::Args& a, const Sched& s, hipStream_t stream)
 {
     void* kargs[] = {(void*)&a, (void*)&s};
-    return hipLaunchKernel((const void*)&scan_kernel<Op, E, W, A>, dim3(s.num_tiles), dim3(W * kWave),
-                           kargs, 0, stream);
+    return hipLaunchKernel((const void*)&scan_kernel<Op, E, W, A, NT>, dim3(s.num_tiles),
+                           dim3(W * kWave), kargs, 0, stream);
 }
 
 template <template <int> class Op, class A>
 hipError_t launch_any(int cfg, const typename Op<4>::Args& a, const Sched& s, hipStream_t stream)
 {
+    constexpr bool kNT = Op<4>::kStreamLoads;
     switch (cfg) {
         case 0: return launch_cfg<Op<4>, 4, 1, A>(a, s, stream);
         case 1: return launch_cfg<Op<4>, 4, 4, A>(a, s, stream);
-        case 2: return launch_cfg<Op<8>, 8, 4, A>(a, s, stream);
-        case 3: return launch_cfg<Op<4>, 4, 8, A>(a, s, stream);
+        // Non-temporal input loads on long rows: the look-back tiles (4x8,
+        // and 8x4 for 16-bit data) and the 8192-element tiles.
+        case 2:
+            return s.lookback ? launch_cfg<Op<8>, 8, 4, A, kNT>(a, s, stream)
+                              : launch_cfg<Op<8>, 8, 4, A>(a, s, stream);
+        case 3:
+            return s.lookback ? launch_cfg<Op<4>, 4, 8, A, kNT>(a, s, stream)
+                              : launch_cfg<Op<4>, 4, 8, A>(a, s, stream);
         case 4: return launch_cfg<Op<16>, 16, 4, A>(a, s, stream);
         case 5: return launch_cfg<Op<4>, 4, 16, A>(a, s, stream);
-        default: return launch_cfg<Op<8>, 8, 16, A>(a, s, stream);
+        default: return launch_cfg<Op<8>, 8, 16, A, kNT>(a, s, stream);
     }
 }
 

@@ -174,7 +174,7 @@ __device__ __forceinline__ Aff<T> row_scan(Aff<T> x)
 // every access below is an unconditional vector load or store.  Otherwise
 // (the last tile, misaligned views) each access checks the lane's count.
 
-template <int E, bool kFull, bool kTM = false>
+template <int E, bool kFull, bool kTM = false, bool kNT = false>
 struct Pos {
     uint64_t i0;     // flat index of element 0
     uint64_t n0;     // row of element 0
@@ -188,15 +188,15 @@ struct Pos {
     uint64_t stride;
 };
 
-template <int E, bool kFull, bool TM>
-__device__ __forceinline__ bool vector_ok(const Pos<E, kFull, TM>& P, bool vec)
+template <int E, bool kFull, bool TM, bool NT>
+__device__ __forceinline__ bool vector_ok(const Pos<E, kFull, TM, NT>& P, bool vec)
 {
     return !TM && (kFull || (vec && P.count == E));
 }
 
 // Flat index of a lane's element j.
-template <int E, bool kFull, bool TM>
-__device__ __forceinline__ uint64_t elem_index(const Pos<E, kFull, TM>& P, int j)
+template <int E, bool kFull, bool TM, bool NT>
+__device__ __forceinline__ uint64_t elem_index(const Pos<E, kFull, TM, NT>& P, int j)
 {
     return TM ? P.i0 + (uint64_t)j * P.stride : P.i0 + (uint64_t)j;
 }
@@ -254,28 +254,61 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi)
         return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
 }
 
-template <int E, bool kFull, bool TM, class D>
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Input vectors are read once per launch.  With NT set (long rows: look-back
+// launches and 8192-element tiles, where it measures faster) they are loaded
+// non-temporally, like the output stores; elsewhere plain loads measure
+// faster.  Both go component by component through HIP's vector structs, so
+// that the compiler can drop components a lane never reads (a lane that only
+// needs elements 1..3 issues one 12-byte load).
+template <class V, bool NT, class S>
+__device__ __forceinline__ V ld_vec(const S* p)
+{
+    if constexpr (!NT) {
+        return *reinterpret_cast<const V*>(p);
+    } else if constexpr (std::is_arithmetic<V>::value) {
+        return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+    } else {
+        using C = typename V::value_type;
+        constexpr int n = sizeof(V) / sizeof(C);
+        static_assert(n == 2 || n == 4, "two- or four-component vectors");
+        const C* q = reinterpret_cast<const C*>(p);
+        V r;
+        r.x = __builtin_nontemporal_load(q);
+        r.y = __builtin_nontemporal_load(q + 1);
+        if constexpr (n == 4) {
+            r.z = __builtin_nontemporal_load(q + 2);
+            r.w = __builtin_nontemporal_load(q + 3);
+        }
+        return r;
+    }
+}
+
+template <int E, bool kFull, bool TM, bool NT, class D>
 __device__ __forceinline__ void load_f32(float (&v)[E], const D* __restrict__ p,
-                                         const Pos<E, kFull, TM>& P, bool vec)
+                                         const Pos<E, kFull, TM, NT>& P, bool vec)
 {
     if (vector_ok(P, vec)) {
         if constexpr (std::is_same<D, float>::value) {
 #pragma unroll
             for (int k = 0; k < E / 4; ++k) {
-                const float4 q = *reinterpret_cast<const float4*>(p + P.i0 + 4 * k);
+                const float4 q = ld_vec<float4, NT>(p + P.i0 + 4 * k);
                 v[4 * k + 0] = q.x;
                 v[4 * k + 1] = q.y;
                 v[4 * k + 2] = q.z;
                 v[4 * k + 3] = q.w;
             }
         } else if constexpr (E == 4) {
-            const uint2 q = *reinterpret_cast<const uint2*>(p + P.i0);
+            const uint2 q = ld_vec<uint2, NT>(p + P.i0);
             unpack2<D>(q.x, v[0], v[1]);
             unpack2<D>(q.y, v[2], v[3]);
         } else {
 #pragma unroll
             for (int k = 0; k < E / 8; ++k) {
-                const uint4 q = *reinterpret_cast<const uint4*>(p + P.i0 + 8 * k);
+                const uint4 q = ld_vec<uint4, NT>(p + P.i0 + 8 * k);
                 unpack2<D>(q.x, v[8 * k + 0], v[8 * k + 1]);
                 unpack2<D>(q.y, v[8 * k + 2], v[8 * k + 3]);
                 unpack2<D>(q.z, v[8 * k + 4], v[8 * k + 5]);
@@ -288,18 +321,18 @@ __device__ __forceinline__ void load_f32(float (&v)[E], const D* __restrict__ p,
     }
 }
 
-template <int E, bool kFull, bool TM>
+template <int E, bool kFull, bool TM, bool NT>
 __device__ __forceinline__ void load_u32(uint32_t (&v)[E], const int32_t* __restrict__ p,
-                                         const Pos<E, kFull, TM>& P, bool vec)
+                                         const Pos<E, kFull, TM, NT>& P, bool vec)
 {
     if (vector_ok(P, vec)) {
 #pragma unroll
         for (int k = 0; k < E / 4; ++k) {
-            const int4 q = *reinterpret_cast<const int4*>(p + P.i0 + 4 * k);
-            v[4 * k + 0] = (uint32_t)q.x;
-            v[4 * k + 1] = (uint32_t)q.y;
-            v[4 * k + 2] = (uint32_t)q.z;
-            v[4 * k + 3] = (uint32_t)q.w;
+            const uint4 q = ld_vec<uint4, NT>(p + P.i0 + 4 * k);
+            v[4 * k + 0] = q.x;
+            v[4 * k + 1] = q.y;
+            v[4 * k + 2] = q.z;
+            v[4 * k + 3] = q.w;
         }
     } else {
 #pragma unroll
@@ -319,18 +352,18 @@ __device__ __forceinline__ uint32_t nonzero_bytes(uint32_t w)
 }
 
 // Bit j of the result is (mask[i0 + j] != 0); a null mask reads as all zero.
-template <int E, bool kFull, bool TM>
-__device__ __forceinline__ uint32_t load_mask(const uint8_t* __restrict__ p, const Pos<E, kFull, TM>& P,
+template <int E, bool kFull, bool TM, bool NT>
+__device__ __forceinline__ uint32_t load_mask(const uint8_t* __restrict__ p, const Pos<E, kFull, TM, NT>& P,
                                               bool vec)
 {
     static_assert(E == 4 || E == 8 || E == 16, "mask loads are 4, 8 or 16 bytes");
     if (vector_ok(P, vec)) {
-        if (E == 4) return nonzero_bytes(*reinterpret_cast<const uint32_t*>(p + P.i0));
+        if (E == 4) return nonzero_bytes(ld_vec<uint32_t, NT>(p + P.i0));
         if (E == 8) {
-            const uint2 w = *reinterpret_cast<const uint2*>(p + P.i0);
+            const uint2 w = ld_vec<uint2, NT>(p + P.i0);
             return nonzero_bytes(w.x) | (nonzero_bytes(w.y) << 4);
         }
-        const uint4 w = *reinterpret_cast<const uint4*>(p + P.i0);
+        const uint4 w = ld_vec<uint4, NT>(p + P.i0);
         return nonzero_bytes(w.x) | (nonzero_bytes(w.y) << 4) | (nonzero_bytes(w.z) << 8) |
                (nonzero_bytes(w.w) << 12);
     }
@@ -343,14 +376,10 @@ __device__ __forceinline__ uint32_t load_mask(const uint8_t* __restrict__ p, con
 
 // Outputs are written once and not read again by this launch: full-tile
 // stores are non-temporal (streamed past the caches).
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-template <int E, bool kFull, bool TM, class D>
+template <int E, bool kFull, bool TM, bool NT, class D>
 __device__ __forceinline__ void store_f32(D* __restrict__ p, const float (&v)[E],
-                                          const Pos<E, kFull, TM>& P, bool vec)
+                                          const Pos<E, kFull, TM, NT>& P, bool vec)
 {
     if (vector_ok(P, vec)) {
         if constexpr (std::is_same<D, float>::value) {
@@ -376,9 +405,9 @@ __device__ __forceinline__ void store_f32(D* __restrict__ p, const float (&v)[E]
     }
 }
 
-template <int E, bool kFull, bool TM>
+template <int E, bool kFull, bool TM, bool NT>
 __device__ __forceinline__ void store_u32(int32_t* __restrict__ p, const uint32_t (&v)[E],
-                                          const Pos<E, kFull, TM>& P, bool vec)
+                                          const Pos<E, kFull, TM, NT>& P, bool vec)
 {
     if (vector_ok(P, vec)) {
 #pragma unroll
