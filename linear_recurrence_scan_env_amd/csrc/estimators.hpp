@@ -31,6 +31,12 @@ struct Ctx {
     bool vec;        // base pointers allow vector access
 };
 
+// Tile shape of an op's look-back launches on fp32 data (measured on long
+// rows): four elements per lane in 2048-element tiles for ops with many
+// input streams; eight per lane for ops with few; four per lane in
+// 4096-element tiles for the prefix sums.
+enum LookbackTile { kLbNarrow, kLbLight, kLbWide4 };
+
 // Value of stream p at flat index i0+E (element 0 of the next chunk).  Full
 // tiles load it in every lane (same cache line as the neighbouring chunk's
 // vector load), unconditionally, so it is in flight with the lane's other
@@ -174,6 +180,7 @@ struct GaeOp {
     static constexpr int kElemBytes = sizeof(D);
     static constexpr bool kBackward = true;
     static constexpr bool kWideTiles = true;
+    static constexpr LookbackTile kLookbackTile = kLbNarrow;
     static constexpr bool kStreamLoads = true;
     struct State {
         uint32_t end;
@@ -231,6 +238,7 @@ struct LambdaOp {
     static constexpr int kElemBytes = sizeof(D);
     static constexpr bool kBackward = true;
     static constexpr bool kWideTiles = true;
+    static constexpr LookbackTile kLookbackTile = kLbLight;
     // non-temporal input loads measure slower for this op on long rows
     static constexpr bool kStreamLoads = false;
     struct State {
@@ -286,6 +294,7 @@ struct DiscOp {
     static constexpr int kElemBytes = sizeof(D);
     static constexpr bool kBackward = true;
     static constexpr bool kWideTiles = true;
+    static constexpr LookbackTile kLookbackTile = kLbLight;
     static constexpr bool kStreamLoads = true;
     struct State {
         uint32_t end;
@@ -344,6 +353,7 @@ struct VtraceOp {
     // Whole rows of 4096 or 8192 in one block (E = 8 or 16 waves) cost
     // this op occupancy: its per-element state needs more registers.
     static constexpr bool kWideTiles = false;
+    static constexpr LookbackTile kLookbackTile = kLbNarrow;
     static constexpr bool kStreamLoads = true;
     struct State {
         uint32_t end;
@@ -423,6 +433,7 @@ struct RetraceOp {
     // Whole rows of 4096 or 8192 in one block (E = 8 or 16 waves) cost
     // this op occupancy: its per-element state needs more registers.
     static constexpr bool kWideTiles = false;
+    static constexpr LookbackTile kLookbackTile = kLbNarrow;
     static constexpr bool kStreamLoads = true;
     struct State {
         uint32_t end;
@@ -524,6 +535,7 @@ struct EligOp {
     static constexpr int kElemBytes = sizeof(D);
     static constexpr bool kBackward = false;
     static constexpr bool kWideTiles = true;
+    static constexpr LookbackTile kLookbackTile = kLbLight;
     static constexpr bool kStreamLoads = true;
     struct State {
         uint32_t reset;
@@ -563,6 +575,7 @@ struct PrefixF32Op {
     static constexpr int kElemBytes = sizeof(D);
     static constexpr bool kBackward = false;
     static constexpr bool kWideTiles = true;
+    static constexpr LookbackTile kLookbackTile = kLbWide4;
     static constexpr bool kStreamLoads = true;
     struct State {
         uint32_t reset;
@@ -602,6 +615,7 @@ struct PrefixI32Op {
     static constexpr int kElemBytes = 4;
     static constexpr bool kBackward = false;
     static constexpr bool kWideTiles = true;
+    static constexpr LookbackTile kLookbackTile = kLbWide4;
     static constexpr bool kStreamLoads = true;
     struct State {
         uint32_t reset;
@@ -657,6 +671,7 @@ struct AffineOp {
     static constexpr int kElemBytes = sizeof(D);
     static constexpr bool kBackward = kRev;
     static constexpr bool kWideTiles = true;
+    static constexpr LookbackTile kLookbackTile = kLbWide4;
     static constexpr bool kStreamLoads = true;
     struct State {
         uint32_t cut;

@@ -306,6 +306,8 @@ constexpr int kAlignedCfgs[5] = {0, 1, 3, 5, 6};  // 4x1, 4x4, 4x8, 4x16, 8x16
 constexpr uint32_t kNarrowMaxTile = 2048;  // ops without kWideTiles stop at 4x8
 constexpr uint64_t kWideMinTiles = 1024;   // whole-row tiles above 2048 need this many
 constexpr int kLookbackCfg = 3;            // 4x8: 2048-element tiles
+constexpr int kLookbackCfgWide4 = 5;       // 4x16: prefix sums, maps composed in fp64
+constexpr int kLookbackCfgLight = 2;       // 8x4: kLbLight ops, below kWideMinTiles
 // 16-bit data: eight elements per lane make each data load 16 bytes
 constexpr int kLookbackCfgHalfWide = 6;    // 8x16: 8192-element tiles (ops with kWideTiles)
 constexpr int kLookbackCfgHalf = 2;        // 8x4: 2048-element tiles
@@ -351,7 +353,14 @@ inline size_t workspace_bytes_for(uint64_t total)
 // kWideTiles when at least kWideMinTiles of them fill the chip, else in
 // 2048-element tiles of four waves.  16-bit rows that divide 2048 also take
 // those 2048-element tiles when at least kWideMinTiles of them fill the chip.
-inline int choose_cfg(uint64_t total, uint64_t T, bool wide_ok, int elem_bytes, bool* lookback)
+// Long fp32 rows (measured at 64 x 131072, 256 x 65536 and 1024 x 16384)
+// follow the op's LookbackTile: kLbLight ops take eight elements per lane,
+// in 8192-element tiles when kWideMinTiles of them fill the chip, else in
+// 2048-element ones; kLbWide4 ops and maps composed in fp64 take
+// 4096-element tiles of four per lane; kLbNarrow ops 2048-element tiles of
+// four per lane.
+inline int choose_cfg(uint64_t total, uint64_t T, bool wide_ok, LookbackTile lb, bool fp64, int elem_bytes,
+                      bool* lookback)
 {
     const int forced = g_forced_cfg.load();
     const bool force_lb = g_force_lookback.load() != 0;
@@ -379,11 +388,12 @@ inline int choose_cfg(uint64_t total, uint64_t T, bool wide_ok, int elem_bytes, 
         }
     }
     *lookback = true;
-    if (elem_bytes == 2) {
-        const uint64_t wide_tiles = (total + kCfgs[kLookbackCfgHalfWide].tile() - 1) /
-                                    kCfgs[kLookbackCfgHalfWide].tile();
+    const uint64_t wide_tiles = (total + kCfgs[kLookbackCfgHalfWide].tile() - 1) /
+                                kCfgs[kLookbackCfgHalfWide].tile();
+    if (elem_bytes == 2)
         return wide_ok && wide_tiles >= kWideMinTiles ? kLookbackCfgHalfWide : kLookbackCfgHalf;
-    }
+    if (fp64 || lb == kLbWide4) return kLookbackCfgWide4;
+    if (lb == kLbLight) return wide_tiles >= kWideMinTiles ? kLookbackCfgHalfWide : kLookbackCfgLight;
     return kLookbackCfg;
 }
 
@@ -427,7 +437,13 @@ lrs_status run(const char* name, int64_t N, int64_t T, float beta_max, const typ
 {
     const uint64_t total = (uint64_t)N * (uint64_t)T;
     bool lookback = false;
-    const int cfg = choose_cfg(total, (uint64_t)T, Op<4>::kWideTiles, Op<4>::kElemBytes, &lookback);
+    // fp32 maps compose in fp64 when the call's betas may come close to 1:
+    // long near-undamped chains (sums) accumulate fp32 rounding beyond the
+    // parity bound, while damped chains forget it within ~1/(1 - beta) steps.
+    using Val = typename Op<4>::T;
+    const bool fp64 = std::is_same<Val, float>::value && beta_max > kFp32BetaMax;
+    const int cfg = choose_cfg(total, (uint64_t)T, Op<4>::kWideTiles, Op<4>::kLookbackTile, fp64,
+                               Op<4>::kElemBytes, &lookback);
     const Cfg& k = kCfgs[cfg];
     Sched s{};
     s.total = total;
@@ -463,14 +479,9 @@ lrs_status run(const char* name, int64_t N, int64_t T, float beta_max, const typ
     for (int i = 0; i < nfloats; ++i) vec = vec && aligned(floats[i], data_align);
     for (int i = 0; i < nmasks; ++i) vec = vec && aligned(masks[i], (uintptr_t)k.E);
     s.vec = vec ? 1 : 0;
-    // fp32 maps compose in fp64 when the call's betas may come close to 1:
-    // long near-undamped chains (sums) accumulate fp32 rounding beyond the
-    // parity bound, while damped chains forget it within ~1/(1 - beta) steps.
-    using Val = typename Op<4>::T;
     hipError_t e;
     if constexpr (std::is_same<Val, float>::value)
-        e = beta_max > kFp32BetaMax ? launch_any<Op, double>(cfg, a, s, stream)
-                                    : launch_any<Op, float>(cfg, a, s, stream);
+        e = fp64 ? launch_any<Op, double>(cfg, a, s, stream) : launch_any<Op, float>(cfg, a, s, stream);
     else
         e = launch_any<Op, Val>(cfg, a, s, stream);
     if (e != hipSuccess)
