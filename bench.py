@@ -97,15 +97,47 @@ def key(est, trunc, n=None, t=None):
     return k if n is None else f"{k}@{n}x{t}"
 
 
-def alg_bytes(est, trunc, n, t, width=4):
+def make_batches(name):
+    """Seeded host inputs of a workload, one batch per (num_envs, seq_len)."""
+    from linear_recurrence_scan_env_amd import workloads
+    calls = WORKLOADS[name]
+    p = workloads.WORKLOADS[BASE_WORKLOAD.get(name, name)]
+    batches = {}
+    for n, t in sorted({(n, t) for _, _, n, t in calls}):
+        if name.startswith("affine"):
+            arrs = workloads.affine_inputs(n, t, seed=0, reset_p=p["reset_p"],
+                                           beta_range=p["beta_range"])
+            batches[(n, t)] = workloads.Rollout(n, t, 1.0, 1.0, arrs)
+            continue
+        streams = {s_ for e, tr, n_, t_ in calls if (n_, t_) == (n, t) for s_ in NEEDS[e]}
+        if any(tr for e, tr, n_, t_ in calls if (n_, t_) == (n, t)):
+            streams.add("truncateds")
+        batches[(n, t)] = workloads.rollout(
+            n, t, seed=0, term_p=p["term_p"], trunc_p=p["trunc_p"], gamma=p["gamma"],
+            lambda_=p["lambda_"], done_p=p["term_p"], streams=sorted(streams))
+    return batches
+
+
+def trunc_counts(batches):
+    """Truncations per batch (the trunc_values the method reads)."""
+    out = {}
+    for s_, b in batches.items():
+        tr = b.arrays.get("truncateds")
+        out[s_] = int(np.count_nonzero(tr)) if tr is not None else 0
+    return out
+
+
+def alg_bytes(est, trunc, n, t, width=4, n_trunc=None):
     """One read of each input stream and one write of each output, with
-    `width`-byte data: STREAMS per element, plus one mask byte and one datum
-    (trunc_values) per element with truncations, plus one datum of bootstrap
-    (or carry) per env."""
+    `width`-byte data: STREAMS per element, plus one datum of bootstrap (or
+    carry) per env.  With truncations: one mask byte per element, and one
+    datum of trunc_values per truncation (n_trunc of them), the only ones
+    the method uses and the only ones the row-major kernels read; without a
+    count, one per element."""
     data, masks = STREAMS[est]
     b = (data * width + masks) * n * t
     if trunc:
-        b += (width + 1) * n * t
+        b += n * t + width * (n * t if n_trunc is None else n_trunc)
     if est in BACKWARD or est.startswith("affine"):
         b += width * n
     return b
@@ -275,6 +307,7 @@ def summarize_counters(fetch_csv, write_csv, command_fetch, command_write):
     ff = CALIBRATION_BYTES / (sum(fcal) / len(fcal))
     wf = CALIBRATION_BYTES / (sum(wcal) / len(wcal))
     n, t = 4096, 128
+    n_trunc = trunc_counts(make_batches(DEFAULT_WORKLOAD))[(n, t)]
     out = ["# HBM traffic per launch: seven estimators at 4096 x 128 (cold inputs)", "",
            "Commands (one counter per pass):", "", "```", command_fetch, command_write, "```", "",
            f"Calibration: a device copy of {CALIBRATION_BYTES >> 20} MiB reads FETCH_SIZE "
@@ -288,7 +321,7 @@ def summarize_counters(fetch_csv, write_csv, command_fetch, command_write):
         wr = sum(write[k]) / len(write[k])
         traffic = int(round(fr * ff + wr * wf))
         est, tr = k.split("+")[0], k.endswith("+trunc")
-        ab = alg_bytes(est, tr, n, t)
+        ab = alg_bytes(est, tr, n, t, 4, n_trunc)
         data[k] = traffic
         out.append(f"| {k} | {fr / 1024:.1f} | {wr / 1024:.1f} | {traffic} | {ab} | {traffic / ab:.3f} |")
     out += ["", "Machine-readable (read by bench.py; valid only for these kernel sources):", "",
@@ -413,19 +446,8 @@ def main():
     width = 2 if storage in ("bf16", "f16") else 4
     store_dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[storage]
     shapes = sorted({(n, t) for _, _, n, t in calls})
-    batches = {}
-    for n, t in shapes:
-        if name.startswith("affine"):
-            arrs = workloads.affine_inputs(n, t, seed=0, reset_p=p["reset_p"],
-                                           beta_range=p["beta_range"])
-            batches[(n, t)] = workloads.Rollout(n, t, 1.0, 1.0, arrs)
-            continue
-        streams = {s_ for e, tr, n_, t_ in calls if (n_, t_) == (n, t) for s_ in NEEDS[e]}
-        if any(tr for e, tr, n_, t_ in calls if (n_, t_) == (n, t)):
-            streams.add("truncateds")
-        batches[(n, t)] = workloads.rollout(
-            n, t, seed=0, term_p=p["term_p"], trunc_p=p["trunc_p"], gamma=p["gamma"],
-            lambda_=p["lambda_"], done_p=p["term_p"], streams=sorted(streams))
+    batches = make_batches(name)
+    n_trunc = trunc_counts(batches)
     ro0 = batches[shapes[0]]
     g, lam = ro0.gamma, ro0.lambda_
 
@@ -538,7 +560,7 @@ def main():
             ev1.record(stream)
             torch.cuda.synchronize()
             us = ev0.elapsed_time(ev1) * 1e3 / (args.roofline_reps * launches[k_])
-            b = alg_bytes(e, tr, n, t, width)
+            b = alg_bytes(e, tr, n, t, width, n_trunc[(n, t)])
             per_call[k_ if len(shapes) > 1 else key(e, tr)] = {
                 "us": round(us, 3), "alg_bytes": b, "GBps": round(b / us / 1e3, 1),
                 "Gelem/s": round(n * t / us / 1e3, 2)}

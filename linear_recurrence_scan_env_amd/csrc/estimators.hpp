@@ -97,20 +97,39 @@ struct BoundaryArgs {
     int has_boot;           // passes another input array and has_boot = 0
 };
 
+// trunc_values only matter where truncated: on row-major arrays a lane
+// reads them only when it holds a truncation (with vector access, all E at
+// once; otherwise element by element), and the others read as 0.  The
+// stream then costs HBM traffic around truncations only.  The load depends
+// on the truncation mask, so callers issue it after every other load of the
+// tile.  Time-major lanes (one scalar load per step) measure faster loading
+// them unconditionally with the other streams.
+template <int E, bool F, bool TM, bool NT, class D>
+__device__ __forceinline__ void load_trunc_values(float (&tv)[E], const D* __restrict__ p, uint32_t kap,
+                                                  const Pos<E, F, TM, NT>& P, bool vec)
+{
+    if constexpr (TM) {
+        load_f32<E>(tv, p, P, vec);
+    } else if (vector_ok(P, vec)) {
+        if (kap != 0u) {
+            load_f32<E>(tv, p, P, vec);
+        } else {
+#pragma unroll
+            for (int j = 0; j < E; ++j) tv[j] = 0.0f;
+        }
+    } else {
+        // kap has bits only for the lane's valid elements
+#pragma unroll
+        for (int j = 0; j < E; ++j) tv[j] = ((kap >> j) & 1u) ? to_f32(p[elem_index(P, j)]) : 0.0f;
+    }
+}
+
 template <int E, bool F, bool TM, bool NT, bool kTrunc, class D>
 __device__ __forceinline__ Ends<E> load_ends(const BoundaryArgs<D>& b, const Pos<E, F, TM, NT>& P,
                                              const Ctx& c)
 {
     const uint32_t tau = load_mask<E>(b.term, P, c.vec);
-    uint32_t kap = 0u;
-    float tv[E];
-    if constexpr (kTrunc) {
-        kap = load_mask<E>(b.trunc, P, c.vec);
-        load_f32<E>(tv, b.tv, P, c.vec);
-    } else {
-#pragma unroll
-        for (int j = 0; j < E; ++j) tv[j] = 0.0f;
-    }
+    const uint32_t kap = kTrunc ? load_mask<E>(b.trunc, P, c.vec) : 0u;
     // Bootstrap of each row end in the lane.  Full tiles have seq_len >= E,
     // so a lane holds at most one row end, which belongs to its first row:
     // one unconditional load.  The guarded path loads per row end.
@@ -127,6 +146,13 @@ __device__ __forceinline__ Ends<E> load_ends(const BoundaryArgs<D>& b, const Pos
             bv[j] = (last && b.has_boot) ? to_f32(b.boot[n]) : 0.0f;
             if (last) ++n;
         }
+    }
+    float tv[E];
+    if constexpr (kTrunc) {
+        load_trunc_values<E>(tv, b.tv, kap, P, c.vec);
+    } else {
+#pragma unroll
+        for (int j = 0; j < E; ++j) tv[j] = 0.0f;
     }
     Ends<E> r;
     r.end = tau | kap | P.last;
@@ -193,8 +219,8 @@ struct GaeOp {
         float r[E], v[E];
         load_f32<E>(r, a.rewards, P, c.vec);
         load_f32<E>(v, a.values, P, c.vec);
-        const Ends<E> e = load_ends<E, F, TM, NT, kTrunc>(a.b, P, c);
         const float vnx = next_elem<E>(v[0], a.values, P, c, successor_used(P));
+        const Ends<E> e = load_ends<E, F, TM, NT, kTrunc>(a.b, P, c);
 #pragma unroll
         for (int j = 0; j < E; ++j) {
             const bool end = (e.end >> j) & 1u;
@@ -252,8 +278,8 @@ struct LambdaOp {
         float r[E], v[E];
         load_f32<E>(r, a.rewards, P, c.vec);
         load_f32<E>(v, a.values, P, c.vec);
-        const Ends<E> e = load_ends<E, F, TM, NT, kTrunc>(a.b, P, c);
         const float vnx = next_elem<E>(v[0], a.values, P, c, successor_used(P));
+        const Ends<E> e = load_ends<E, F, TM, NT, kTrunc>(a.b, P, c);
 #pragma unroll
         for (int j = 0; j < E; ++j) {
             const bool end = (e.end >> j) & 1u;
@@ -368,8 +394,8 @@ struct VtraceOp {
         load_f32<E>(lr, a.log_rhos, P, c.vec);
         load_f32<E>(s.r, a.rewards, P, c.vec);
         load_f32<E>(s.v, a.values, P, c.vec);
-        const Ends<E> e = load_ends<E, F, TM, NT, kTrunc>(a.b, P, c);
         const float vnx = next_elem<E>(s.v[0], a.values, P, c, successor_used(P));
+        const Ends<E> e = load_ends<E, F, TM, NT, kTrunc>(a.b, P, c);
 #pragma unroll
         for (int j = 0; j < E; ++j) {
             const bool end = (e.end >> j) & 1u;
@@ -453,12 +479,12 @@ struct RetraceOp {
         load_f32<E>(r, a.rewards, P, c.vec);
         load_f32<E>(q, a.q_values, P, c.vec);
         load_f32<E>(v, a.values, P, c.vec);
-        const Ends<E> e = load_ends<E, F, TM, NT, kTrunc>(a.b, P, c);
         const bool used = successor_used(P);
         // successor (t+1) quantities of the lane's last element
         const float lrnx = next_elem<E>(lr[0], a.log_rhos, P, c, used);
         const float qnx = next_elem<E>(q[0], a.q_values, P, c, used);
         const float vnx = next_elem<E>(v[0], a.values, P, c, used);
+        const Ends<E> e = load_ends<E, F, TM, NT, kTrunc>(a.b, P, c);
 #pragma unroll
         for (int j = 0; j < E; ++j) cc[j] = trace(a, lr[j]);
         const float cnx = trace(a, lrnx);
