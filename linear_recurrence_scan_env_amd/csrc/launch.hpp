@@ -118,7 +118,6 @@ struct BlockShared {
     A a[W];
     A b[W];
     A carry;
-    uint32_t tag;
     uint32_t open;
 };
 
@@ -138,10 +137,16 @@ __device__ __forceinline__ void tile_body(const typename Op::Args& args, const S
     WsHeader* hdr = reinterpret_cast<WsHeader*>(s.ws);
     uint64_t* rec = reinterpret_cast<uint64_t*>(s.ws + sizeof(WsHeader));
 
-    // The neighbour's record is read first, in flight with the tile's loads.
+    // The launch tag and the neighbour's record are read first, in flight
+    // with the tile's loads.
     const bool far_most = kB ? (tile == s.num_tiles - 1u) : (tile == 0u);
     Record early{{0, 0, 0, 0}};
-    if (s.lookback && !far_most && wave == 0) early = read_adjacent<kB, A>(rec, tile);
+    uint32_t tag = 0;
+    if (s.lookback && wave == 0) {
+        tag = __builtin_amdgcn_readfirstlane(
+                  __hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) + 1u;
+        if (!far_most) early = read_adjacent<kB, A>(rec, tile);
+    }
 
     T alpha[E], beta[E];
     typename Op::State st;
@@ -181,17 +186,12 @@ __device__ __forceinline__ void tile_body(const typename Op::Args& args, const S
         // One wave per block: everything stays in registers, no barrier.
         tile_agg = readlane(inc, kWave - 1);
         if (s.lookback) {
-            const uint32_t tag = __builtin_amdgcn_readfirstlane(__hip_atomic_load(
-                                     &hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) + 1u;
             const uint32_t open = readlane(Op::far_open(st) ? 1u : 0u, 0);
             if (lane == 0) publish_aggregate<A>(rec, tile, tag, tile_agg);
             if (!far_most && open)
                 carry = lookback_carry<kB, A>(rec, tile, s.num_tiles, tag, lane, &hdr->error, early);
-            if (lane == 0) finish_launch(hdr, s.num_tiles, blockIdx.x, tag);
         }
     } else {
-        if (s.lookback && tid == 0)
-            sh.tag = __hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
         if (lane == kWave - 1) {
             sh.a[wave] = inc.a;
             sh.b[wave] = inc.b;
@@ -210,17 +210,13 @@ __device__ __forceinline__ void tile_body(const typename Op::Args& args, const S
         if (kB ? (w < W - 1) : (w > 0)) beyond = readlane(x, kB ? w + 1 : w - 1);
 
         if (s.lookback) {
-            const uint32_t tag = sh.tag;
             if (wave == 0) {
                 if (lane == 0) publish_aggregate<A>(rec, tile, tag, tile_agg);
                 A cin = A(0);
                 if (!far_most && sh.open)
                     cin = lookback_carry<kB, A>(rec, tile, s.num_tiles, tag, lane, &hdr->error,
                                                 early);
-                if (lane == 0) {
-                    sh.carry = cin;
-                    finish_launch(hdr, s.num_tiles, blockIdx.x, tag);
-                }
+                if (lane == 0) sh.carry = cin;
             }
             __syncthreads();
             carry = sh.carry;
@@ -230,6 +226,9 @@ __device__ __forceinline__ void tile_body(const typename Op::Args& args, const S
     const A wave_in = apply(beyond, carry);
     const T lane_in = T(apply(exc, wave_in));
     Op::finish(args, P, c, alpha, beta, st, lane_in);
+    // Count the block out last, after its stores are issued: the counter's
+    // round trip then delays no wave's outputs.
+    if (s.lookback && wave == 0 && lane == 0) finish_launch(hdr, s.num_tiles, blockIdx.x, tag);
 }
 
 template <class Op, int E, int W, class A, bool NT>

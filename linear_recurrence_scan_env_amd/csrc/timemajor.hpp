@@ -100,6 +100,14 @@ __device__ __forceinline__ void tile_body_tm(const typename Op::Args& args, cons
     const Pos<E, F, true> P{(uint64_t)t0 * s.N + col, col, count, last, first, s.N};
     const Ctx c{(uint64_t)s.N * s.T, s.T, lane, false};
 
+    // The launch tag is read first, in flight with the tile's loads.
+    WsHeader* hdr = reinterpret_cast<WsHeader*>(s.ws);
+    const bool carries = wave == kNear && s.time_tiles > 1;
+    uint32_t tag = 0;
+    if (carries)
+        tag = __builtin_amdgcn_readfirstlane(
+                  __hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) + 1u;
+
     T alpha[E], beta[E];
     typename Op::State st;
     Op::prepare(args, P, c, alpha, beta, st);
@@ -139,15 +147,12 @@ __device__ __forceinline__ void tile_body_tm(const typename Op::Args& args, cons
     }
 
     R carry = R(0);
-    if (wave == kNear && s.time_tiles > 1) {
-        WsHeader* hdr = reinterpret_cast<WsHeader*>(s.ws);
+    if (carries) {
         uint64_t* rec = reinterpret_cast<uint64_t*>(s.ws + sizeof(WsHeader));
         const uint64_t plane = (uint64_t)s.time_tiles * s.N;
         uint64_t* rec_a = rec;
         uint64_t* rec_b = rec + plane;
         uint64_t* rec_y = rec + 2 * plane;
-        const uint32_t tag = __builtin_amdgcn_readfirstlane(__hip_atomic_load(
-                                 &hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) + 1u;
         const Aff<A> tile_map = combine(x, beyond);
         const Aff<R> tile = {(R)tile_map.a, (R)tile_map.b};  // as published
         const bool far_most = kB ? (k == s.time_tiles - 1u) : (k == 0u);
@@ -208,7 +213,6 @@ __device__ __forceinline__ void tile_body_tm(const typename Op::Args& args, cons
             if (active && !near_most && tile.b != R(0))
                 st_agent(rec_y + own, tagged(tag, apply(tile, carry)));
         }
-        if (lane == 0) finish_launch(hdr, s.num_blocks, blockIdx.x, tag);
     }
     if constexpr (W > 1) {
         if (wave == kNear) sh.carry[lane] = carry;
@@ -218,6 +222,8 @@ __device__ __forceinline__ void tile_body_tm(const typename Op::Args& args, cons
 
     const T lane_in = T(apply(beyond, A(carry)));
     Op::finish(args, P, c, alpha, beta, st, lane_in);
+    // Count the block out last, after its stores are issued.
+    if (carries && lane == 0) finish_launch(hdr, s.num_blocks, blockIdx.x, tag);
 }
 
 template <class Op, int E, int W, class A>
