@@ -539,9 +539,11 @@ lrs_status lrs_affine_scan_tm_f16(int64_t num_envs, int64_t seq_len,
 lrs_status lrs_debug_set_schedule(int force_lookback, int elems_per_lane,
                                   int waves_per_block);
 
-/* Time-major calls: fix the waves per block (8: tiles of 64 steps, 16:
- * tiles of 128 steps; 8 steps per lane either way), or 0 for the automatic
- * choice.  Returns LRS_ERR_INVALID_ARG for any other value. */
+/* Time-major calls: fix the waves per block (2, 4, 8 or 16: tiles of 16,
+ * 32, 64 or 128 steps; 8 steps per lane), or 0 for the automatic choice.
+ * Returns LRS_ERR_INVALID_ARG for any other value.  While 2 or 4 is set,
+ * lrs_workspace_bytes reports the larger workspace such tiles need
+ * (24 bytes per env per 16 or 32 steps). */
 lrs_status lrs_debug_set_time_major_waves(int waves_per_block);
 
 #ifdef __cplusplus

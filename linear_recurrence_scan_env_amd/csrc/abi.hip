@@ -57,9 +57,9 @@ lrs_status lrs_debug_set_schedule(int force_lookback, int elems_per_lane, int wa
 
 lrs_status lrs_debug_set_time_major_waves(int waves_per_block)
 {
-    if (waves_per_block != 0 && waves_per_block != kTmWSmall && waves_per_block != kTmWLarge)
-        return fail(LRS_ERR_INVALID_ARG, "lrs_debug_set_time_major_waves: %d is not 0, %d or %d",
-                    waves_per_block, kTmWSmall, kTmWLarge);
+    if (waves_per_block != 0 && !tm_waves_supported(waves_per_block))
+        return fail(LRS_ERR_INVALID_ARG, "lrs_debug_set_time_major_waves: %d is not 0, 2, 4, 8 or 16",
+                    waves_per_block);
     g_forced_tm_waves.store(waves_per_block);
     return LRS_OK;
 }

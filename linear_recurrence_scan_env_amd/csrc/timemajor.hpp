@@ -244,23 +244,39 @@ __global__ __launch_bounds__(W * kWave) void scan_kernel_tm(const typename Op::A
 
 // ------------------------------------------------------------- host side
 constexpr int kTmE = 8;        // steps per lane
-constexpr int kTmWSmall = 8;   // waves per block: 64-step tiles, for rows of <= 64 steps
-constexpr int kTmWLarge = 16;  // 128-step tiles otherwise (measured faster from T = 128 up)
+constexpr int kTmWSmall = 8;   // waves per block: 64-step tiles
+constexpr int kTmWLarge = 16;  // 128-step tiles
+constexpr uint64_t kTmFewGroups = 16;  // below this many 64-env groups, long rows take 64-step tiles
 
 inline uint64_t tm_tiles(uint64_t T, int W) { return (T + (uint64_t)kTmE * W - 1) / ((uint64_t)kTmE * W); }
 
-inline int tm_waves(uint64_t T)
+inline bool tm_waves_supported(int W) { return W == 2 || W == 4 || W == 8 || W == 16; }
+
+// Waves per block (measured at 4096 x {32 .. 8192} and 64 x 131072): rows of
+// at most 64 steps take the smallest block that holds them whole (16-, 32-
+// or 64-step tiles: no carries, no idle waves); longer rows take 128-step
+// tiles, or 64-step ones when there are few environment groups (twice the
+// blocks along time; 5-10% faster at 64 x 131072).  Smaller tiles with
+// carries measured slower everywhere (at 4096 x 128: 4.7 us on one 128-step
+// tile, 6.1-8.1 us on 2-8 tiles).
+inline int tm_waves(uint64_t N, uint64_t T)
 {
     const int forced = g_forced_tm_waves.load();
     if (forced > 0) return forced;
-    return T <= (uint64_t)kTmE * kTmWSmall ? kTmWSmall : kTmWLarge;
+    if (T <= 2u * kTmE) return 2;
+    if (T <= 4u * kTmE) return 4;
+    if (T <= (uint64_t)kTmWSmall * kTmE) return kTmWSmall;
+    return (N + kWave - 1) / kWave < kTmFewGroups ? kTmWSmall : kTmWLarge;
 }
 
 // Workspace of a time-major call: the header and three words per
-// (64-step tile, environment).
+// (64-step tile, environment).  Only a forced smaller block (a diagnostic
+// setting) needs more, and then this reports that.
 inline size_t workspace_bytes_tm(uint64_t N, uint64_t T)
 {
-    return sizeof(WsHeader) + 8 * kPlanesTM * N * tm_tiles(T, kTmWSmall);
+    const int forced = g_forced_tm_waves.load();
+    const int w = forced > 0 && forced < kTmWSmall ? forced : kTmWSmall;
+    return sizeof(WsHeader) + 8 * kPlanesTM * N * tm_tiles(T, w);
 }
 
 template <template <int> class Op, int W, class A>
@@ -289,7 +305,7 @@ lrs_status run_tm(const char* name, int64_t N, int64_t T, float beta_max,
 {
     if (N >= (int64_t(1) << 32))
         return fail(LRS_ERR_INVALID_ARG, "%s: time-major calls need num_envs < 2^32", name);
-    const int W = tm_waves((uint64_t)T);
+    const int W = tm_waves((uint64_t)N, (uint64_t)T);
     SchedTM s{};
     s.N = (uint32_t)N;
     s.T = (uint32_t)T;
@@ -304,8 +320,13 @@ lrs_status run_tm(const char* name, int64_t N, int64_t T, float beta_max,
                         need, ws == nullptr ? (size_t)0 : ws_bytes);
         if (!aligned(ws, 16)) return fail(LRS_ERR_WORKSPACE, "%s: workspace not 16-byte aligned", name);
     }
-    const hipError_t e = W == kTmWLarge ? launch_tm_acc<Op, kTmWLarge>(beta_max, a, s, stream)
-                                        : launch_tm_acc<Op, kTmWSmall>(beta_max, a, s, stream);
+    hipError_t e;
+    switch (W) {
+        case 2: e = launch_tm_acc<Op, 2>(beta_max, a, s, stream); break;
+        case 4: e = launch_tm_acc<Op, 4>(beta_max, a, s, stream); break;
+        case 8: e = launch_tm_acc<Op, 8>(beta_max, a, s, stream); break;
+        default: e = launch_tm_acc<Op, 16>(beta_max, a, s, stream); break;
+    }
     if (e != hipSuccess)
         return fail(LRS_ERR_HIP, "%s: kernel launch failed: %s", name, hipGetErrorString(e));
     g_err[0] = '\0';

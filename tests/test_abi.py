@@ -145,10 +145,15 @@ def test_time_major_and_16bit_entry_points_reject(lib):
 
 
 def test_time_major_waves_validation(lib):
-    for w in (1, 4, 12, 32, -1):
+    for w in (1, 3, 12, 32, -1):
         assert lib.lrs_debug_set_time_major_waves(w) == 1
-    for w in (8, 16, 0):
+    for w in (2, 4, 8, 16, 0):
         assert lib.lrs_debug_set_time_major_waves(w) == 0
+    # a forced small block needs the workspace of its tiles
+    assert lib.lrs_debug_set_time_major_waves(2) == 0
+    assert lib.lrs_workspace_bytes(0, 64, 4096) == 4224 + 24 * 64 * 4096 // 16
+    assert lib.lrs_debug_set_time_major_waves(0) == 0
+    assert lib.lrs_workspace_bytes(0, 64, 4096) == documented_workspace(64, 4096)
 
 
 def test_debug_schedule_validation(lib):

@@ -32,9 +32,9 @@ def _gpu():
     lrs.set_time_major_waves(0)
 
 
-@pytest.fixture(params=[8, 16], ids=["W8", "W16"])
+@pytest.fixture(params=[2, 4, 8, 16], ids=["W2", "W4", "W8", "W16"])
 def waves(request):
-    """Both time-major tile shapes (64- and 128-step tiles)."""
+    """Every time-major tile shape (16-, 32-, 64- and 128-step tiles)."""
     lrs.set_time_major_waves(request.param)
     yield request.param
     lrs.set_time_major_waves(0)
@@ -256,7 +256,7 @@ def test_python_validation_tm():
 
 def test_time_major_waves_validation():
     with pytest.raises(Exception):
-        lrs.set_time_major_waves(4)
+        lrs.set_time_major_waves(3)
     lrs.set_time_major_waves(0)
 
 
