@@ -278,6 +278,32 @@ def test_no_leakage_exact(est):
                 assert np.array_equal(x[:, :cut + 1], y[:, :cut + 1])
 
 
+@pytest.mark.parametrize("est", sorted(TRUNCATING))
+@pytest.mark.parametrize("shape,tile", [((33, 128), None), ((3, 5000), None), ((5, 999), (4, 1)),
+                                        ((2, 9000), (4, 8)), ((7, 3001), (8, 16))],
+                         ids=lambda x: "x".join(map(str, x)) if x else "auto")
+def test_trunc_values_read_only_at_truncations(est, shape, tile):
+    """trunc_values enter only at truncated steps: NaN everywhere else leaves
+    every output bit-identical (the kernels skip those reads), on the
+    automatic schedule and on forced look-back tiles."""
+    N, T = shape
+    ro = workloads.rollout(N, T, seed=N * 7 + T, term_p=0.01, trunc_p=0.02)
+    if tile is not None:
+        lrs.set_schedule(True, *tile)
+    try:
+        base = [o.cpu().numpy() for o, _ in run_pair(est, ro)]
+        b = dict(ro.arrays)
+        b["trunc_values"] = np.where(b["truncateds"] != 0, b["trunc_values"], np.float32(np.nan))
+        ro2 = workloads.Rollout(N, T, ro.gamma, ro.lambda_, b)
+        pairs = run_pair(est, ro2)
+        new = [o.cpu().numpy() for o, _ in pairs]
+    finally:
+        lrs.set_schedule(False, 0, 0)
+    for x, y in zip(base, new):
+        assert np.array_equal(x, y)
+    check(pairs, T)
+
+
 def test_deterministic_lookback():
     ro = workloads.rollout(8, 50000, seed=12, term_p=1e-4, trunc_p=1e-4)
     outs = []

@@ -183,6 +183,21 @@ def test_deterministic(waves):
             assert np.array_equal(x, y)
 
 
+@pytest.mark.parametrize("est", ["gae", "vtrace", "retrace", "lambda_returns", "discounted_returns"])
+def test_trunc_values_only_used_at_truncations(est):
+    """NaN trunc_values wherever the step is not truncated leave every
+    output bit-identical."""
+    N, T = 130, 700
+    ro = workloads.rollout(N, T, seed=77, term_p=0.01, trunc_p=0.02)
+    base = run_tm(est, ro)
+    b = dict(ro.arrays)
+    b["trunc_values"] = np.where(b["truncateds"] != 0, b["trunc_values"], np.float32(np.nan))
+    new = run_tm(est, workloads.Rollout(N, T, ro.gamma, ro.lambda_, b))
+    for (x, _), (y, ref) in zip(base, new):
+        assert np.array_equal(x, y)
+    check(new, T)
+
+
 def test_matches_row_major_call():
     """The time-major call equals the row-major call on the transposed arrays
     within fp32 re-association; the int32 prefix sum bit for bit."""
