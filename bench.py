@@ -48,6 +48,8 @@ WORKLOADS = {
     "all7_4096x128": [(e, tr, 4096, 128) for e, tr in ALL7],
     "gae_64x512": [("gae", False, 64, 512)],
     "long_64x131072": [(e, True, 64, 131072) for e in ("gae", "vtrace", "retrace")],
+    # all seven estimators on the long rows (the 12 calls of all7_4096x128)
+    "all7_64x131072": [(e, tr, 64, 131072) for e, tr in ALL7],
     "sweep_4096xT": [(e, False, 4096, t) for t in (32, 128, 512, 2048, 8192)
                      for e in ("discounted_returns", "lambda_returns", "eligibility_traces")],
     "prefix_16384x1024": [("prefix_sum_i32", False, 16384, 1024),
@@ -67,7 +69,8 @@ WORKLOADS = {
 TIME_MAJOR = {"all7_4096x128_tm", "sweep_4096xT_tm"}
 # storage type of the floating-point streams (fp32 unless listed); arithmetic is fp32 throughout
 STORAGE = {"all7_4096x128_bf16": "bf16", "long_64x131072_bf16": "bf16", "sweep_4096xT_bf16": "bf16"}
-BASE_WORKLOAD = {"all7_4096x128_bf16": "all7_4096x128", "long_64x131072_bf16": "long_64x131072",
+BASE_WORKLOAD = {"all7_64x131072": "long_64x131072",
+                 "all7_4096x128_bf16": "all7_4096x128", "long_64x131072_bf16": "long_64x131072",
                  "sweep_4096xT_bf16": "sweep_4096xT", "all7_4096x128_tm": "all7_4096x128",
                  "sweep_4096xT_tm": "sweep_4096xT"}
 DEFAULT_WORKLOAD = "all7_4096x128"
