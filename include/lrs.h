@@ -367,7 +367,13 @@ lrs_status lrs_affine_scan_f16(int64_t num_envs, int64_t seq_len,
  * rollout buffers filled one step at a time.  Per-env arrays
  * (bootstrap_value, carry_in) stay [num_envs].  Same operation, arguments,
  * limits, precision and errors as the call of the same name (num_envs must
- * also be below 2^32); results equal that call's on the transposed arrays
+ * also be below 2^32, and the launch -- one lane per environment, padded
+ * to a multiple of 64, per 8 steps, padded to whole tiles -- must hold fewer
+ * than 2^32 work items, else LRS_ERR_INVALID_ARG; with 64 or more
+ * environments the size limit above already implies it, so it binds when
+ * fewer than 64 environments have rows of about 2^29 steps or more, where
+ * the row-major call on the same memory serves); results equal that call's
+ * on the transposed arrays
  * up to fp32 re-association, bit for bit for the int32 prefix sum.  The
  * pages fix the [num_envs, seq_len] layout (README Usage); this layout is
  * this library's extension.  A lane owns one environment (loads coalesce

@@ -396,6 +396,14 @@ inline int choose_cfg(uint64_t total, uint64_t T, bool wide_ok, LookbackTile lb,
     return kLookbackCfg;
 }
 
+// Work items of a launch over `total` elements on tiles of configuration c.
+inline uint64_t launch_items(uint64_t total, const Cfg& c)
+{
+    return (total + c.tile() - 1) / c.tile() * (uint64_t)(c.W * kWave);
+}
+constexpr uint64_t kMaxLaunchItems = 0xffffffffull;  // a dispatch's grid size is 32-bit
+constexpr int kWideCfg = 6;                          // 8x16: 8192-element tiles
+
 inline bool aligned(const void* p, uintptr_t a) { return p == nullptr || ((uintptr_t)p % a) == 0; }
 
 template <class Op, int E, int W, class A, bool NT = false>
@@ -441,8 +449,16 @@ lrs_status run(const char* name, int64_t N, int64_t T, float beta_max, const typ
     // parity bound, while damped chains forget it within ~1/(1 - beta) steps.
     using Val = typename Op<4>::T;
     const bool fp64 = std::is_same<Val, float>::value && beta_max > kFp32BetaMax;
-    const int cfg = choose_cfg(total, (uint64_t)T, Op<4>::kWideTiles, Op<4>::kLookbackTile, fp64,
-                               Op<4>::kElemBytes, &lookback);
+    int cfg = choose_cfg(total, (uint64_t)T, Op<4>::kWideTiles, Op<4>::kLookbackTile, fp64,
+                         Op<4>::kElemBytes, &lookback);
+    // A dispatch holds at most 2^32 - 1 work items.  Four elements per lane
+    // exceed that only within one tile of 2^34 elements; eight elements per
+    // lane in 8192-element tiles stay below 2^31 for every accepted size.
+    if (launch_items(total, kCfgs[cfg]) > kMaxLaunchItems) {
+        cfg = kWideCfg;
+        const uint64_t tiles = (total + kCfgs[cfg].tile() - 1) / kCfgs[cfg].tile();
+        lookback = lookback || (tiles > 1 && kCfgs[cfg].tile() % (uint64_t)T != 0);
+    }
     const Cfg& k = kCfgs[cfg];
     Sched s{};
     s.total = total;

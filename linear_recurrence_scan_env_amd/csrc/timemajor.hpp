@@ -312,6 +312,16 @@ lrs_status run_tm(const char* name, int64_t N, int64_t T, float beta_max,
     s.groups = (uint32_t)((N + kWave - 1) / kWave);
     s.time_tiles = (uint32_t)tm_tiles((uint64_t)T, W);
     s.num_blocks = s.groups * s.time_tiles;
+    // One lane per environment, padded to whole groups of 64: with few
+    // environments and very long rows the launch could exceed the 2^32 - 1
+    // work items a dispatch holds.
+    if ((uint64_t)s.num_blocks * (uint64_t)(W * kWave) > 0xffffffffull)
+        return fail(LRS_ERR_INVALID_ARG,
+                    "%s: time-major launch of %llu work items (ceil(num_envs/64)*64 lanes x "
+                    "%llu steps / 8) exceeds 2^32 - 1; use the row-major call for so few, so "
+                    "long rows",
+                    name, (unsigned long long)s.num_blocks * (unsigned long long)(W * kWave),
+                    (unsigned long long)s.time_tiles * kTmE * W);
     s.ws = static_cast<uint8_t*>(ws);
     if (s.time_tiles > 1) {
         const size_t need = sizeof(WsHeader) + 8 * kPlanesTM * (size_t)N * s.time_tiles;

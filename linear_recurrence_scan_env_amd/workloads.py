@@ -132,3 +132,32 @@ WORKLOADS = {
     # 8192: beta ~ U[0.9, 1), resets Bern(0.02), a carry per env.
     "affine_4096x8192": dict(num_envs=4096, seq_len=8192, reset_p=0.02, beta_range=(0.9, 1.0)),
 }
+
+
+def device_stream(seed, name, shape, device, *, kind, p=None, sigma=1.0, lo=-1000, hi=1000,
+                  chunk=1 << 28):
+    """Draws one stream straight into device memory, for arrays too large to
+    draw on the host (billions of elements).  torch's device generator (Philox)
+    is seeded with ``(seed << 8) | STREAM_KEY[name]`` and fills the flat array
+    in chunks of ``chunk`` elements, in order, so the values depend only on
+    (seed, name, shape).  The values are not the numpy draws of the same seed.
+
+    kind: "normal" -> float32 N(0, sigma^2); "bernoulli" -> uint8 with
+    P(1) = p; "int" -> int32 uniform on [lo, hi] inclusive.
+    """
+    import torch
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed((int(seed) << 8) | STREAM_KEY[name])
+    dtype = {"normal": torch.float32, "bernoulli": torch.uint8, "int": torch.int32}[kind]
+    out = torch.empty(shape, dtype=dtype, device=device)
+    flat = out.view(-1)
+    for s in range(0, flat.numel(), chunk):
+        n = min(chunk, flat.numel() - s)
+        if kind == "normal":
+            flat[s:s + n].normal_(0.0, sigma, generator=gen)
+        elif kind == "bernoulli":
+            flat[s:s + n] = torch.rand(n, generator=gen, device=device) < p
+        else:
+            flat[s:s + n].random_(lo, hi + 1, generator=gen)
+    return out

@@ -73,6 +73,11 @@ def test_workspace_bytes(lib):
     assert lib.lrs_workspace_bytes(0, 0, 128) == 0
     assert lib.lrs_workspace_bytes(0, 5, 0) == 0
     assert lib.lrs_workspace_bytes(0, 1 << 20, 1 << 20) == 0  # 2^40 elements: over the limit
+    # the limits themselves: seq_len < 2^31 and num_envs * seq_len < 2^34
+    assert lib.lrs_workspace_bytes(0, 8, (1 << 31) - 1) == documented_workspace(8, (1 << 31) - 1)
+    assert lib.lrs_workspace_bytes(0, 1, 1 << 31) == 0
+    assert lib.lrs_workspace_bytes(0, 16, 1 << 30) == 0  # exactly 2^34 elements
+    assert lib.lrs_workspace_bytes(0, (1 << 34) - 1, 1) == documented_workspace((1 << 34) - 1, 1)
     assert lib.lrs_workspace_bytes(42, 4, 4) == 0
     assert lib.lrs_workspace_bytes(8, 4096, 128) == lib.lrs_workspace_bytes(0, 4096, 128)
     assert lib.lrs_workspace_bytes(9, 4, 4) == 0
@@ -88,6 +93,7 @@ def gae(lib, N=4, T=8, r=FAKE, v=FAKE, term=FAKE, trunc=None, tv=None, boot=None
 
 @pytest.mark.parametrize("kwargs", [
     dict(N=0), dict(T=0), dict(N=-3), dict(T=1 << 31), dict(N=1 << 20, T=1 << 15),
+    dict(N=16, T=1 << 30), dict(N=1 << 34, T=1),
     dict(r=None), dict(v=None), dict(term=None), dict(out=None),
     dict(trunc=FAKE, tv=None),
     dict(g=1.5), dict(g=-0.1), dict(l=1.01), dict(g=math.nan), dict(l=math.nan),
@@ -142,6 +148,13 @@ def test_time_major_and_16bit_entry_points_reject(lib):
     st = lib.lrs_discounted_returns_tm_f32(4, 1000, FAKE, FAKE, None, None, None, 0.9, FAKE, None,
                                            0, None)
     assert st == 2 and b"workspace" in lib.lrs_last_error()
+    # a time-major launch pads environments to 64 lanes: one environment of
+    # 2^31 - 1 steps would need 2^34 work items, more than a dispatch holds
+    st = lib.lrs_episodic_prefix_sum_tm_i32(1, (1 << 31) - 1, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                                            None)
+    assert st == 1 and b"work items" in lib.lrs_last_error()
+    st = lib.lrs_episodic_prefix_sum_tm_i32(1, (1 << 29) - 64, FAKE, FAKE, FAKE, None, 0, None)
+    assert st == 2  # fits the launch; only the missing workspace is reported
 
 
 def test_time_major_waves_validation(lib):
