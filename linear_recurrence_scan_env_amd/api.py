@@ -166,15 +166,18 @@ def workspace_state():
     """Diagnostics: synchronize, then read the header of every cached workspace.
     Returns a list of dicts: epoch (launches that used the carry protocol),
     error (nonzero: a carry wait gave up, bit 2 = timeout), top and
-    counters_nonzero (both 0 between launches: every launch resets them)."""
+    counters_nonzero (both 0 between launches: every launch resets them), and
+    epochs_in_step (every count word carries the header's epoch)."""
     import numpy as np
     torch.cuda.synchronize()
     out = []
     for ws in _workspaces.values():
         h = ws[:4224].cpu().numpy().view(np.uint32)
-        counts = h[32::32][:32]  # one counter per 128-byte line after the first
+        counts = h[32::32][:32]  # count words, one per 128-byte line after the first:
+        epochs = h[33::32][:32]  # low half the count, high half the epoch
         out.append({"epoch": int(h[0]), "error": int(h[1]), "top": int(h[2]),
-                    "counters_nonzero": int(np.count_nonzero(counts))})
+                    "counters_nonzero": int(np.count_nonzero(counts)),
+                    "epochs_in_step": bool((epochs == h[0]).all())})
     return out
 
 

@@ -91,28 +91,6 @@ __device__ __forceinline__ void split_index32(uint32_t u, const Sched& s, uint32
     t = u - q * s.T;
 }
 
-// Called once per block (one thread) after its last look-back read.
-__device__ __forceinline__ void finish_launch(WsHeader* hdr, uint32_t num_blocks, uint32_t block,
-                                              uint32_t tag)
-{
-    const uint32_t g = block % kGroups;
-    const uint32_t members = (num_blocks - g + kGroups - 1) / kGroups;  // blocks in group g
-    const uint32_t groups = num_blocks < kGroups ? num_blocks : kGroups;
-    const uint32_t seen =
-        __hip_atomic_fetch_add(&hdr->group[g].count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (seen != members - 1u) return;
-    const uint32_t done =
-        __hip_atomic_fetch_add(&hdr->top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (done != groups - 1u) return;
-    // Last block of the launch: every block has read the epoch by now.
-    for (uint32_t i = 0; i < groups; ++i)
-        __hip_atomic_store(&hdr->group[i].count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&hdr->top, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    uint32_t next = tag;                 // = epoch + 1
-    if (next == 0xffffffffu) next = 0u;  // keep tags (epoch + 1) nonzero
-    __hip_atomic_store(&hdr->epoch, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 template <class A, int W>
 struct BlockShared {
     A a[W];
@@ -137,14 +115,14 @@ __device__ __forceinline__ void tile_body(const typename Op::Args& args, const S
     WsHeader* hdr = reinterpret_cast<WsHeader*>(s.ws);
     uint64_t* rec = reinterpret_cast<uint64_t*>(s.ws + sizeof(WsHeader));
 
-    // The launch tag and the neighbour's record are read first, in flight
-    // with the tile's loads.
+    // The block count (which returns the launch tag) and the neighbour's record
+    // are issued first, in flight with the tile's loads.
     const bool far_most = kB ? (tile == s.num_tiles - 1u) : (tile == 0u);
     Record early{{0, 0, 0, 0}};
-    uint32_t tag = 0;
+    uint64_t entry = 0;
+    uint32_t tag = 0, top_seen = ~0u;
     if (s.lookback && wave == 0) {
-        tag = __builtin_amdgcn_readfirstlane(
-                  __hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) + 1u;
+        if (lane == 0) entry = count_block(hdr, blockIdx.x);
         if (!far_most) early = read_adjacent<kB, A>(rec, tile);
     }
 
@@ -186,6 +164,8 @@ __device__ __forceinline__ void tile_body(const typename Op::Args& args, const S
         // One wave per block: everything stays in registers, no barrier.
         tile_agg = readlane(inc, kWave - 1);
         if (s.lookback) {
+            tag = launch_tag(entry);
+            if (lane == 0) top_seen = count_group(hdr, entry, s.num_tiles, blockIdx.x);
             const uint32_t open = readlane(Op::far_open(st) ? 1u : 0u, 0);
             if (lane == 0) publish_aggregate<A>(rec, tile, tag, tile_agg);
             if (!far_most && open)
@@ -211,6 +191,8 @@ __device__ __forceinline__ void tile_body(const typename Op::Args& args, const S
 
         if (s.lookback) {
             if (wave == 0) {
+                tag = launch_tag(entry);
+                if (lane == 0) top_seen = count_group(hdr, entry, s.num_tiles, blockIdx.x);
                 if (lane == 0) publish_aggregate<A>(rec, tile, tag, tile_agg);
                 A cin = A(0);
                 if (!far_most && sh.open)
@@ -226,9 +208,7 @@ __device__ __forceinline__ void tile_body(const typename Op::Args& args, const S
     const A wave_in = apply(beyond, carry);
     const T lane_in = T(apply(exc, wave_in));
     Op::finish(args, P, c, alpha, beta, st, lane_in);
-    // Count the block out last, after its stores are issued: the counter's
-    // round trip then delays no wave's outputs.
-    if (s.lookback && wave == 0 && lane == 0) finish_launch(hdr, s.num_tiles, blockIdx.x, tag);
+    if (s.lookback && wave == 0 && lane == 0) close_launch(hdr, top_seen, s.num_tiles, tag);
 }
 
 template <class Op, int E, int W, class A, bool NT>

@@ -431,14 +431,21 @@ __device__ __forceinline__ void store_u32(int32_t* __restrict__ p, const uint32_
 // word carries its own tag, so a reader that sees all four tags equal to this
 // launch's tag holds a consistent aggregate without any fence.
 //
-// Header: the launch epoch, an error word, and block-completion counters
-// spread over kGroups cache lines (block b counts itself in group b % kGroups;
-// the block completing a group counts the group in `top`).  tag = epoch + 1.
-// Every block reads the epoch before counting itself out; the block that
-// completes the last group zeroes the counters and advances the epoch, so
-// the next launch on the same stream starts clean and stale records (older
-// tags, or the zero fill) are never mistaken for fresh ones.  Spreading the
-// counters keeps same-address atomics, which serialize, to a few per line.
+// Header: the launch epoch, an error word, a group counter `top`, and
+// kGroups count words on separate cache lines, each (epoch << 32 | blocks
+// of the current launch counted so far).  Block b counts itself with one
+// atomic add on word b % kGroups.  The row-major kernel does this at the
+// block's start, in flight with the tile's loads, and takes its tag from the
+// word's old value, so the tag read and the count are one access that no
+// wave waits for until the tag is needed.  The time-major kernel reads the
+// epoch at the start and counts at the block's end.  Either way a block has
+// its tag before it is counted.  The block that counted last in its group
+// counts the group in `top`; the one that completes `top` has seen every
+// block of the launch take its tag, so it rewrites every count word as
+// (epoch + 1) << 32, zeroes `top` and advances `epoch`.  The next launch on
+// the same stream thus starts clean, and stale records (older tags, or the
+// zero fill) are never mistaken for fresh ones.  Spreading the counts keeps
+// same-address atomics, which serialize, to a few per line.
 //
 // A tile only ever waits for tiles of lower block index (the host maps
 // blocks to tiles so).  Workgroups of a dispatch are started in index order,
@@ -452,14 +459,61 @@ constexpr uint32_t kLine = 128;  // bytes between counters
 struct WsHeader {
     uint32_t epoch;
     uint32_t error;  // nonzero: a wait gave up (kErrTimeout)
-    uint32_t top;    // number of completed groups
+    uint32_t top;    // number of groups whose blocks have all counted in
     uint32_t pad0[kLine / 4 - 3];
     struct {
-        uint32_t count;
-        uint32_t pad[kLine / 4 - 1];
+        uint64_t word;  // epoch << 32 | blocks counted in (low half first in memory)
+        uint32_t pad[kLine / 4 - 2];
     } group[kGroups];
 };
 static_assert(sizeof(WsHeader) == kLine * (kGroups + 1), "header layout");
+
+__device__ __forceinline__ void st_agent_hdr(uint64_t* p, uint64_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One lane per block: count the block; the returned word holds the launch's
+// epoch.  Only launches with carries between tiles call these.
+__device__ __forceinline__ uint64_t count_block(WsHeader* hdr, uint32_t block)
+{
+    return __hip_atomic_fetch_add(&hdr->group[block % kGroups].word, 1ull, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The launch tag from a count word held by lane 0 of the calling wave
+// (wave-uniform result).
+__device__ __forceinline__ uint32_t launch_tag(uint64_t entry)
+{
+    return (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(entry >> 32), 0) + 1u;
+}
+
+// Lane 0, once its count word is in: if the block was its group's last to
+// be counted, count the group in `top` and return top's old value (the
+// launch is complete when it is groups - 1); otherwise ~0u.
+__device__ __forceinline__ uint32_t count_group(WsHeader* hdr, uint64_t entry, uint32_t num_blocks,
+                                                uint32_t block)
+{
+    const uint32_t g = block % kGroups;
+    const uint32_t members = (num_blocks - g + kGroups - 1) / kGroups;  // blocks in group g
+    if ((uint32_t)entry != members - 1u) return ~0u;
+    return __hip_atomic_fetch_add(&hdr->top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Lane 0, at the block's end, with count_group's result: the block that
+// completed `top` resets the counters and advances the epoch.  Every block
+// holds its tag by then, and none touches the header again in this launch.
+__device__ __forceinline__ void close_launch(WsHeader* hdr, uint32_t top_seen, uint32_t num_blocks,
+                                             uint32_t tag)
+{
+    const uint32_t groups = num_blocks < kGroups ? num_blocks : kGroups;
+    if (top_seen != groups - 1u) return;
+    uint32_t next = tag;                 // = epoch + 1
+    if (next == 0xffffffffu) next = 0u;  // keep tags (epoch + 1) nonzero
+    for (uint32_t i = 0; i < kGroups; ++i) st_agent_hdr(&hdr->group[i].word, (uint64_t)next << 32);
+    __hip_atomic_store(&hdr->top, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&hdr->epoch, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Upper bound on the polls of one look-back wait (about a second).
 constexpr uint32_t kMaxPolls = 1u << 20;

@@ -100,7 +100,11 @@ __device__ __forceinline__ void tile_body_tm(const typename Op::Args& args, cons
     const Pos<E, F, true> P{(uint64_t)t0 * s.N + col, col, count, last, first, s.N};
     const Ctx c{(uint64_t)s.N * s.T, s.T, lane, false};
 
-    // The launch tag is read first, in flight with the tile's loads.
+    // The launch tag is read first, in flight with the tile's loads.  These
+    // blocks count themselves in at their end instead, after their stores
+    // are issued (measured faster here than counting in at the start, as the
+    // row-major kernel does; both keep the same header state between
+    // launches).
     WsHeader* hdr = reinterpret_cast<WsHeader*>(s.ws);
     const bool carries = wave == kNear && s.time_tiles > 1;
     uint32_t tag = 0;
@@ -222,8 +226,10 @@ __device__ __forceinline__ void tile_body_tm(const typename Op::Args& args, cons
 
     const T lane_in = T(apply(beyond, A(carry)));
     Op::finish(args, P, c, alpha, beta, st, lane_in);
-    // Count the block out last, after its stores are issued.
-    if (carries && lane == 0) finish_launch(hdr, s.num_blocks, blockIdx.x, tag);
+    if (carries && lane == 0) {
+        const uint64_t entry = count_block(hdr, blockIdx.x);
+        close_launch(hdr, count_group(hdr, entry, s.num_blocks, blockIdx.x), s.num_blocks, tag);
+    }
 }
 
 template <class Op, int E, int W, class A>

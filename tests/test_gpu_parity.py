@@ -401,4 +401,4 @@ def test_zz_workspace_headers_clean():
     completion counters reset."""
     for h in lrs.workspace_state():
         assert h["error"] == 0, h
-        assert h["top"] == 0 and h["counters_nonzero"] == 0, h
+        assert h["top"] == 0 and h["counters_nonzero"] == 0 and h["epochs_in_step"], h
