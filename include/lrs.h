@@ -377,8 +377,10 @@ lrs_status lrs_affine_scan_f16(int64_t num_envs, int64_t seq_len,
  * up to fp32 re-association, bit for bit for the int32 prefix sum.  The
  * pages fix the [num_envs, seq_len] layout (README Usage); this layout is
  * this library's extension.  A lane owns one environment (loads coalesce
- * across environments) and tiles of 64 or 128 steps pass carries along time; no
- * alignment beyond the element size is needed.  The workspace from
+ * across environments) and tiles of 64 or 128 steps pass carries along time;
+ * rows of up to 128 steps on fewer than 16384 environments take blocks of 32
+ * environments that hold whole rows; no alignment beyond the element size is
+ * needed.  The workspace from
  * lrs_workspace_bytes covers both layouts.  Results are deterministic run
  * to run, as for the row-major calls.                                    */
 lrs_status lrs_gae_tm_f32(int64_t num_envs, int64_t seq_len,
@@ -546,7 +548,9 @@ lrs_status lrs_debug_set_schedule(int force_lookback, int elems_per_lane,
                                   int waves_per_block);
 
 /* Time-major calls: fix the waves per block (2, 4, 8 or 16: tiles of 16,
- * 32, 64 or 128 steps; 8 steps per lane), or 0 for the automatic choice.
+ * 32, 64 or 128 steps of 64 environments; 8 steps per lane), or 0 for the
+ * automatic choice (which may also take blocks of 32 environments holding
+ * whole rows of up to 128 steps).
  * Returns LRS_ERR_INVALID_ARG for any other value.  While 2 or 4 is set,
  * lrs_workspace_bytes reports the larger workspace such tiles need
  * (24 bytes per env per 16 or 32 steps). */

@@ -142,7 +142,8 @@ def set_schedule(force_lookback: bool = False, elems_per_lane: int = 0, waves_pe
 
 def set_time_major_waves(waves_per_block: int = 0):
     """Diagnostics: waves per block of the time-major calls (2, 4, 8 or 16: tiles of
-    16 to 128 steps; 0 = automatic)."""
+    16 to 128 steps of 64 environments; 0 = automatic, which also uses blocks of 32
+    environments for rows of up to 128 steps when there are few environments)."""
     _check(load().lrs_debug_set_time_major_waves(int(waves_per_block)), "set_time_major_waves")
 
 

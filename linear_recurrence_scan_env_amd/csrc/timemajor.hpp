@@ -248,6 +248,98 @@ __global__ __launch_bounds__(W * kWave) void scan_kernel_tm(const typename Op::A
         tile_body_tm<Op, E, W, A, false>(args, s, k, g, sh);
 }
 
+// Rows that fit one tile, on few environments: V environments per block
+// instead of 64, so that a 4096-environment batch spreads over 4096 / V
+// blocks rather than 64.  A wave holds C = 64 / V chunks of E steps of
+// its V environments (lane l: environment l mod V, chunk l / V), so each load
+// instruction reads C time rows of V consecutive environments; a block of W
+// waves covers E * W * C steps, the whole row, and needs no carry.  The chunk
+// maps combine through LDS as the wave maps of the wide kernel do.
+template <class A, int Q, int V>
+struct BlockSharedTMRows {
+    A a[Q][V];
+    A b[Q][V];
+};
+
+template <class Op, int E, int W, int V, class A, bool F>
+__device__ __forceinline__ void rows_body_tm(const typename Op::Args& args, const SchedTM& s,
+                                             uint32_t g, BlockSharedTMRows<A, W * (kWave / V), V>& sh)
+{
+    using T = typename Op::T;
+    constexpr bool kB = Op::kBackward;
+    constexpr int C = kWave / V;
+    constexpr int Q = W * C;  // chunks along time
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int v = lane % V;
+    const int q = (tid / kWave) * C + lane / V;
+    const uint32_t n = g * V + (uint32_t)v;
+    const bool active = n < s.N;
+    const uint32_t t0 = (uint32_t)q * E;
+
+    int count = 0;
+    uint32_t last = 0, first = 0;
+    if (active && t0 < s.T) {
+        count = (int)(s.T - t0 < (uint32_t)E ? s.T - t0 : E);
+        if (s.T - 1u - t0 < (uint32_t)count) last = 1u << (s.T - 1u - t0);
+        if (t0 == 0) first = 1u;
+    }
+    const uint32_t col = active ? n : 0u;  // inactive lanes touch nothing (count = 0)
+    const Pos<E, F, true> P{(uint64_t)t0 * s.N + col, col, count, last, first, s.N};
+    const Ctx c{(uint64_t)s.N * s.T, s.T, lane, false};
+
+    T alpha[E], beta[E];
+    typename Op::State st;
+    Op::prepare(args, P, c, alpha, beta, st);
+
+    Aff<A> x = identity<A>();
+    if constexpr (std::is_same<A, float>::value) {
+        float a = 0.0f;
+        double b = 1.0;
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+            const int j = kB ? E - 1 - k : k;
+            a = fmaf(beta[j], a, alpha[j]);
+            b *= (double)beta[j];
+        }
+        x = {a, (float)b};
+    } else if (kB) {
+#pragma unroll
+        for (int j = E - 1; j >= 0; --j) x = combine(Aff<A>{A(alpha[j]), A(beta[j])}, x);
+    } else {
+#pragma unroll
+        for (int j = 0; j < E; ++j) x = combine(Aff<A>{A(alpha[j]), A(beta[j])}, x);
+    }
+    sh.a[q][v] = x.a;
+    sh.b[q][v] = x.b;
+    __syncthreads();
+
+    // Chunks between this one and the row's far end, nearest first.
+    Aff<A> beyond = identity<A>();
+#pragma unroll
+    for (int d = 1; d < Q; ++d) {
+        const int w = kB ? q + d : q - d;
+        if (w >= 0 && w < Q) beyond = combine(beyond, Aff<A>{sh.a[w][v], sh.b[w][v]});
+    }
+    const T lane_in = T(apply(beyond, A(0)));
+    Op::finish(args, P, c, alpha, beta, st, lane_in);
+}
+
+template <class Op, int E, int W, int V, class A>
+__global__ __launch_bounds__(W * kWave) void scan_kernel_tm_rows(const typename Op::Args args,
+                                                                 const SchedTM s)
+{
+    constexpr uint32_t kSteps = (uint32_t)E * W * (kWave / V);
+    __shared__ BlockSharedTMRows<A, W * (kWave / V), V> sh;
+    const uint32_t g = blockIdx.x;
+    const bool full = kSteps == s.T && (uint64_t)(g + 1u) * V <= s.N;
+    if (full)
+        rows_body_tm<Op, E, W, V, A, true>(args, s, g, sh);
+    else
+        rows_body_tm<Op, E, W, V, A, false>(args, s, g, sh);
+}
+
 // ------------------------------------------------------------- host side
 constexpr int kTmE = 8;        // steps per lane
 constexpr int kTmWSmall = 8;   // waves per block: 64-step tiles
@@ -257,6 +349,25 @@ constexpr uint64_t kTmFewGroups = 16;  // below this many 64-env groups, long ro
 inline uint64_t tm_tiles(uint64_t T, int W) { return (T + (uint64_t)kTmE * W - 1) / ((uint64_t)kTmE * W); }
 
 inline bool tm_waves_supported(int W) { return W == 2 || W == 4 || W == 8 || W == 16; }
+
+// Narrow blocks for rows that fit one tile (measured at 4096 x {32, 128}):
+// when the wide kernel would have fewer than kTmRowsMaxGroups blocks of 64
+// environments, rows of at most 128 steps take blocks of kTmRowsV = 32
+// environments (twice the blocks; each load instruction reads two time rows
+// of 128 bytes for fp32): 17-21% faster at 4096 x 128, 11% at 4096 x 32; 16
+// environments per block measured slower than 32 at 128 steps.  Returns the
+// waves per narrow block (1, 2, 4 or 8: 16 to 128 steps), or 0 for the wide
+// kernel, which a forced wave count also selects.
+constexpr int kTmRowsV = 32;
+constexpr uint64_t kTmRowsMaxGroups = 256;
+inline int tm_rows_waves(uint64_t N, uint64_t T)
+{
+    if (g_forced_tm_waves.load() != 0) return 0;
+    if ((N + kWave - 1) / kWave >= kTmRowsMaxGroups) return 0;
+    for (int W = 1; W <= 8; W *= 2)
+        if ((uint64_t)kTmE * W * (kWave / kTmRowsV) >= T) return W;
+    return 0;
+}
 
 // Waves per block (measured at 4096 x {32 .. 8192} and 64 x 131072): rows of
 // at most 64 steps take the smallest block that holds them whole (16-, 32-
@@ -293,6 +404,26 @@ hipError_t launch_tm(const typename Op<kTmE>::Args& a, const SchedTM& s, hipStre
                            dim3(s.num_blocks), dim3(W * kWave), params, 0, stream);
 }
 
+template <template <int> class Op, int W, int V, class A>
+hipError_t launch_tm_rows(const typename Op<kTmE>::Args& a, const SchedTM& s, hipStream_t stream)
+{
+    void* params[] = {(void*)&a, (void*)&s};
+    return hipLaunchKernel((const void*)&scan_kernel_tm_rows<Op<kTmE>, kTmE, W, V, A>,
+                           dim3(s.num_blocks), dim3(W * kWave), params, 0, stream);
+}
+
+template <template <int> class Op, int W, int V>
+hipError_t launch_tm_rows_acc(float beta_max, const typename Op<kTmE>::Args& a, const SchedTM& s,
+                              hipStream_t stream)
+{
+    using Val = typename Op<kTmE>::T;
+    if constexpr (std::is_same<Val, float>::value)
+        return beta_max > kFp32BetaMax ? launch_tm_rows<Op, W, V, double>(a, s, stream)
+                                       : launch_tm_rows<Op, W, V, float>(a, s, stream);
+    else
+        return launch_tm_rows<Op, W, V, Val>(a, s, stream);
+}
+
 template <template <int> class Op, int W>
 hipError_t launch_tm_acc(float beta_max, const typename Op<kTmE>::Args& a, const SchedTM& s,
                          hipStream_t stream)
@@ -311,6 +442,26 @@ lrs_status run_tm(const char* name, int64_t N, int64_t T, float beta_max,
 {
     if (N >= (int64_t(1) << 32))
         return fail(LRS_ERR_INVALID_ARG, "%s: time-major calls need num_envs < 2^32", name);
+    if (const int Wr = tm_rows_waves((uint64_t)N, (uint64_t)T)) {
+        SchedTM s{};
+        s.N = (uint32_t)N;
+        s.T = (uint32_t)T;
+        s.groups = (uint32_t)((N + kTmRowsV - 1) / kTmRowsV);
+        s.time_tiles = 1;
+        s.num_blocks = s.groups;
+        s.ws = static_cast<uint8_t*>(ws);
+        hipError_t e;
+        switch (Wr) {
+            case 1: e = launch_tm_rows_acc<Op, 1, kTmRowsV>(beta_max, a, s, stream); break;
+            case 2: e = launch_tm_rows_acc<Op, 2, kTmRowsV>(beta_max, a, s, stream); break;
+            case 4: e = launch_tm_rows_acc<Op, 4, kTmRowsV>(beta_max, a, s, stream); break;
+            default: e = launch_tm_rows_acc<Op, 8, kTmRowsV>(beta_max, a, s, stream); break;
+        }
+        if (e != hipSuccess)
+            return fail(LRS_ERR_HIP, "%s: kernel launch failed: %s", name, hipGetErrorString(e));
+        g_err[0] = '\0';
+        return LRS_OK;
+    }
     const int W = tm_waves((uint64_t)N, (uint64_t)T);
     SchedTM s{};
     s.N = (uint32_t)N;

@@ -32,9 +32,11 @@ def _gpu():
     lrs.set_time_major_waves(0)
 
 
-@pytest.fixture(params=[2, 4, 8, 16], ids=["W2", "W4", "W8", "W16"])
+@pytest.fixture(params=[0, 2, 4, 8, 16], ids=["auto", "W2", "W4", "W8", "W16"])
 def waves(request):
-    """Every time-major tile shape (16-, 32-, 64- and 128-step tiles)."""
+    """Every time-major tile shape: the automatic choice (narrow 32-environment
+    blocks for rows of up to 128 steps on few environments), and the wide
+    kernel's 16-, 32-, 64- and 128-step tiles."""
     lrs.set_time_major_waves(request.param)
     yield request.param
     lrs.set_time_major_waves(0)
@@ -119,6 +121,21 @@ SHAPES = [(1, 1), (3, 5), (64, 128), (65, 129), (63, 127), (130, 300), (7, 1000)
 def test_small_shapes(shape, est, waves):
     N, T = shape
     ro = workloads.rollout(N, T, seed=N * 7 + T, term_p=0.05, trunc_p=0.03, gamma=0.97,
+                           lambda_=0.9)
+    check(run_tm(est, ro), T)
+
+
+NARROW_SHAPES = [(n, t) for n in (1, 33, 100) for t in (1, 16, 17, 64, 100, 128)]
+
+
+@pytest.mark.parametrize("est", ESTIMATORS)
+@pytest.mark.parametrize("shape", NARROW_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
+def test_narrow_whole_row_blocks(shape, est):
+    """Automatic choice on rows of up to 128 steps and few environments: the
+    narrow kernel (32 environments per block, two 8-step chunks per wave),
+    with ragged environment groups and rows shorter than the tile."""
+    N, T = shape
+    ro = workloads.rollout(N, T, seed=N * 13 + T, term_p=0.05, trunc_p=0.03, gamma=0.97,
                            lambda_=0.9)
     check(run_tm(est, ro), T)
 
