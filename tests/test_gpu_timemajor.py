@@ -243,16 +243,21 @@ def test_affine_scan(shape, reverse, waves):
 
 
 @pytest.mark.parametrize("est", ["gae", "vtrace", "eligibility_traces", "prefix_sum_f32"])
-def test_bf16_storage(est):
-    """bf16 time-major: within half a bf16 ulp plus the fp32 bound of the
-    oracle on the rounded inputs."""
-    N, T = 130, 1000
+@pytest.mark.parametrize("dtype,shape", [(torch.bfloat16, (130, 1000)), (torch.bfloat16, (70, 100)),
+                                         (torch.float16, (70, 100))],
+                         ids=["bf16-130x1000", "bf16-70x100", "f16-70x100"])
+def test_bf16_storage(est, dtype, shape):
+    """16-bit time-major, on the wide kernel (1000 steps) and on the narrow
+    whole-row blocks (100 steps): within the storage type's unit roundoff
+    plus the fp32 bound of the oracle on the rounded inputs."""
+    N, T = shape
+    u = 2.0 ** -8 if dtype == torch.bfloat16 else 2.0 ** -11
     ro = workloads.rollout(N, T, seed=78, term_p=0.02, trunc_p=0.02)
     for k, v in list(ro.arrays.items()):
         if v.dtype == np.float32:
-            ro.arrays[k] = torch.from_numpy(v).to(torch.bfloat16).float().numpy()
-    for got, ref in run_tm(est, ro, dtype=torch.bfloat16):
-        excess = np.abs(got.astype(np.float64) - ref) - (2.0 ** -8 * np.abs(ref)
+            ro.arrays[k] = torch.from_numpy(v).to(dtype).float().numpy()
+    for got, ref in run_tm(est, ro, dtype=dtype):
+        excess = np.abs(got.astype(np.float64) - ref) - (u * np.abs(ref)
                                                          + 1.01e-5 * (1 + np.abs(ref)))
         assert excess.max() <= 0.0
 
