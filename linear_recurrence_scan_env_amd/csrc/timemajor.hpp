@@ -344,7 +344,6 @@ __global__ __launch_bounds__(W * kWave) void scan_kernel_tm_rows(const typename 
 constexpr int kTmE = 8;        // steps per lane
 constexpr int kTmWSmall = 8;   // waves per block: 64-step tiles
 constexpr int kTmWLarge = 16;  // 128-step tiles
-constexpr uint64_t kTmFewGroups = 16;  // below this many 64-env groups, long rows take 64-step tiles
 
 inline uint64_t tm_tiles(uint64_t T, int W) { return (T + (uint64_t)kTmE * W - 1) / ((uint64_t)kTmE * W); }
 
@@ -369,21 +368,22 @@ inline int tm_rows_waves(uint64_t N, uint64_t T)
     return 0;
 }
 
-// Waves per block (measured at 4096 x {32 .. 8192} and 64 x 131072): rows of
-// at most 64 steps take the smallest block that holds them whole (16-, 32-
-// or 64-step tiles: no carries, no idle waves); longer rows take 128-step
-// tiles, or 64-step ones when there are few environment groups (twice the
-// blocks along time; 5-10% faster at 64 x 131072).  Smaller tiles with
-// carries measured slower everywhere (at 4096 x 128: 4.7 us on one 128-step
-// tile, 6.1-8.1 us on 2-8 tiles).
-inline int tm_waves(uint64_t N, uint64_t T)
+// Waves per block (measured at 4096 x {32 .. 8192} and at 64 to 1024
+// environments with 2^23 elements): rows of at most 64 steps take the
+// smallest block that holds them whole (16-, 32- or 64-step tiles: no
+// carries, no idle waves); longer rows take 128-step tiles, whose carries
+// run along time in half as many steps as 64-step tiles' (3-44% faster than
+// those, most with few environments: 64 x 131072 GAE 160 -> 89 us).  Smaller
+// tiles with carries measured slower everywhere (at 4096 x 128: 4.7 us on
+// one 128-step tile, 6.1-8.1 us on 2-8 tiles).
+inline int tm_waves(uint64_t T)
 {
     const int forced = g_forced_tm_waves.load();
     if (forced > 0) return forced;
     if (T <= 2u * kTmE) return 2;
     if (T <= 4u * kTmE) return 4;
     if (T <= (uint64_t)kTmWSmall * kTmE) return kTmWSmall;
-    return (N + kWave - 1) / kWave < kTmFewGroups ? kTmWSmall : kTmWLarge;
+    return kTmWLarge;
 }
 
 // Workspace of a time-major call: the header and three words per
@@ -462,7 +462,7 @@ lrs_status run_tm(const char* name, int64_t N, int64_t T, float beta_max,
         g_err[0] = '\0';
         return LRS_OK;
     }
-    const int W = tm_waves((uint64_t)N, (uint64_t)T);
+    const int W = tm_waves((uint64_t)T);
     SchedTM s{};
     s.N = (uint32_t)N;
     s.T = (uint32_t)T;

@@ -153,7 +153,7 @@ def test_time_major_and_16bit_entry_points_reject(lib):
     st = lib.lrs_episodic_prefix_sum_tm_i32(1, (1 << 31) - 1, FAKE, FAKE, FAKE, FAKE, 1 << 40,
                                             None)
     assert st == 1 and b"work items" in lib.lrs_last_error()
-    st = lib.lrs_episodic_prefix_sum_tm_i32(1, (1 << 29) - 64, FAKE, FAKE, FAKE, None, 0, None)
+    st = lib.lrs_episodic_prefix_sum_tm_i32(1, (1 << 29) - 256, FAKE, FAKE, FAKE, None, 0, None)
     assert st == 2  # fits the launch; only the missing workspace is reported
 
 
