@@ -262,6 +262,28 @@ def test_bf16_storage(est, dtype, shape):
         assert excess.max() <= 0.0
 
 
+def test_workspace_shared_with_row_major():
+    """Row-major look-back launches and time-major carry launches alternate
+    on one stream, and so on one cached workspace: both layouts count their
+    blocks in the same header, so every call stays exact and the header ends
+    clean (counts zero, every count word at the header's epoch)."""
+    import test_gpu_parity as rm
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for i in range(6):
+            ro = workloads.rollout(5, 3001, seed=300 + i, term_p=0.002, trunc_p=0.002,
+                                   done_p=0.002)
+            est = ESTIMATORS[i % len(ESTIMATORS)]
+            if i % 2 == 0:
+                rm.check(rm.run_pair(est, ro), ro.seq_len)
+            else:
+                check(run_tm(est, ro), ro.seq_len)
+        s.synchronize()
+    for h in lrs.workspace_state():
+        assert h["error"] == 0 and h["top"] == 0 and h["counters_nonzero"] == 0, h
+        assert h["epochs_in_step"], h
+
+
 def test_full_all7_128x4096():
     """The 4096-env, 128-step workload in time-major layout, every output."""
     p = workloads.WORKLOADS["all7_4096x128"]
