@@ -10,9 +10,10 @@ one of the other benchmark workloads (their steps are listed in WORKLOADS).
 Inputs sit in HBM before timing starts.  Each workload's batch is replicated
 R times (>= 1 GiB in all, four times the 256 MB Infinity Cache) and step k
 uses replica k mod R, so every call reads its inputs from HBM rather than
-from a cache ("cold"); --warm reuses one replica.  Each replica's calls are
-captured once into a HIP graph (torch.cuda.CUDAGraph), so the timed loop is
-K graph replays and host launch overhead stays off the critical path.
+from a cache ("cold"); --warm reuses one replica.  The calls are captured
+into HIP graphs (torch.cuda.CUDAGraph) of G consecutive steps each (G = 1 for
+steps of 24 or more calls, more for short steps), so the timed loop is K / G
+graph replays and host launch overhead stays off the critical path.
 
 Prints one JSON line.  value = elements processed per step / step time
 (Gelem/s).  roofline: the call with the longest average duration, its
@@ -27,6 +28,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -93,6 +95,11 @@ NEEDS = {
 STREAMS = {"gae": (3, 1), "vtrace": (5, 1), "retrace": (5, 1), "lambda_returns": (3, 1),
            "discounted_returns": (2, 1), "eligibility_traces": (2, 1), "prefix_sum_f32": (2, 1),
            "prefix_sum_i32": (2, 1), "affine_fwd": (3, 1), "affine_rev": (3, 1)}
+
+
+def steps_per_graph(calls_per_step):
+    """Steps captured per graph: enough for at least 24 calls."""
+    return max(1, -(-24 // calls_per_step))
 
 
 def key(est, trunc, n=None, t=None):
@@ -530,7 +537,22 @@ def main():
                     f()
             return gr
 
-        step_graphs = [capture(step_fns(i)) for i in range(R)]
+        # Several consecutive steps per graph when a step has few calls (at least 24
+        # calls per graph), so that host-side replay cost never paces the GPU.  Graph
+        # i holds the steps on replicas i*G, i*G+1, ... (mod R): replaying the graphs
+        # in order walks the replicas in order, so no call reuses recent inputs.
+        G = steps_per_graph(len(calls))
+        n_graphs = R // math.gcd(R, G)
+
+        def steps_graph(first, count):
+            fns = []
+            for k in range(first, first + count):
+                fns += step_fns(k % R)
+            return capture(fns)
+
+        step_graphs = [steps_graph(i * G, G) for i in range(n_graphs)]
+        full, rest = divmod(args.steps, G)
+        tail_graph = steps_graph(full * G, rest) if rest else None
         call_keys = [key(e, tr, n, t) for e, tr, n, t in calls]
         # per call: a graph of >= 64 launches cycling over that call's replicas
         launches = {k_: max(64, nrep[(n, t)]) for k_, (e, tr, n, t) in zip(call_keys, calls)}
@@ -538,15 +560,17 @@ def main():
                        for k_, (e, tr, n, t) in zip(call_keys, calls)}
         torch.cuda.synchronize()
 
-        # ---- timed steps
-        for k in range(args.warmup):
-            step_graphs[k % R].replay()
+        # ---- timed steps: exactly args.steps steps (full graphs, then the rest)
+        for k in range(-(-args.warmup // G)):
+            step_graphs[k % n_graphs].replay()
         torch.cuda.synchronize()
         t_start = torch.cuda.Event(enable_timing=True)
         t_end = torch.cuda.Event(enable_timing=True)
         t_start.record(stream)
-        for k in range(args.steps):
-            step_graphs[k % R].replay()
+        for k in range(full):
+            step_graphs[k % n_graphs].replay()
+        if tail_graph is not None:
+            tail_graph.replay()
         t_end.record(stream)
         torch.cuda.synchronize()
         ms_per_step = t_start.elapsed_time(t_end) / args.steps
@@ -576,7 +600,7 @@ def main():
     cfg = {"workload": name, "calls_per_step": len(calls),
            "cache": "warm" if args.warm else "cold",
            "replicas": {f"{n}x{t}": nrep[(n, t)] for n, t in shapes},
-           "launch": "hip graph per step", "storage": storage,
+           "launch": f"hip graphs of {G} step(s)", "storage": storage,
            "layout": "time-major [seq_len, num_envs]" if tm else "row-major [num_envs, seq_len]"}
     if len(shapes) == 1:
         cfg.update(num_envs=shapes[0][0], seq_len=shapes[0][1])
