@@ -102,6 +102,18 @@ def steps_per_graph(calls_per_step):
     return max(1, -(-24 // calls_per_step))
 
 
+def replay_plan(R, G, K):
+    """Graphs of G steps over R replicas for K timed steps: graph i holds the
+    steps on replicas i*G, ..., i*G + G - 1 (mod R), R / gcd(R, G) graphs in
+    all, replayed in order; a last graph holds the K mod G remaining steps.
+    Returns (first replica of each graph, number of full replays, first
+    replica of the remainder graph or None).  Step k of the timed loop then
+    uses replica k mod R."""
+    n_graphs = R // math.gcd(R, G)
+    full, rest = divmod(K, G)
+    return [(i * G) % R for i in range(n_graphs)], full, ((full * G) % R if rest else None)
+
+
 def key(est, trunc, n=None, t=None):
     k = est + ("+trunc" if trunc else "")
     return k if n is None else f"{k}@{n}x{t}"
@@ -542,7 +554,8 @@ def main():
         # i holds the steps on replicas i*G, i*G+1, ... (mod R): replaying the graphs
         # in order walks the replicas in order, so no call reuses recent inputs.
         G = steps_per_graph(len(calls))
-        n_graphs = R // math.gcd(R, G)
+        starts, full, tail_start = replay_plan(R, G, args.steps)
+        n_graphs = len(starts)
 
         def steps_graph(first, count):
             fns = []
@@ -550,9 +563,8 @@ def main():
                 fns += step_fns(k % R)
             return capture(fns)
 
-        step_graphs = [steps_graph(i * G, G) for i in range(n_graphs)]
-        full, rest = divmod(args.steps, G)
-        tail_graph = steps_graph(full * G, rest) if rest else None
+        step_graphs = [steps_graph(first, G) for first in starts]
+        tail_graph = steps_graph(tail_start, args.steps % G) if tail_start is not None else None
         call_keys = [key(e, tr, n, t) for e, tr, n, t in calls]
         # per call: a graph of >= 64 launches cycling over that call's replicas
         launches = {k_: max(64, nrep[(n, t)]) for k_, (e, tr, n, t) in zip(call_keys, calls)}
