@@ -371,13 +371,13 @@ lrs_status lrs_affine_scan_f16(int64_t num_envs, int64_t seq_len,
  * to a multiple of 64, per 8 steps, padded to whole tiles -- must hold fewer
  * than 2^32 work items, else LRS_ERR_INVALID_ARG; with 64 or more
  * environments the size limit above already implies it, so it binds when
- * fewer than 64 environments have rows of about 2^29 steps or more, where
+ * fewer than 64 environments have rows of about 2^30 steps or more, where
  * the row-major call on the same memory serves); results equal that call's
  * on the transposed arrays
  * up to fp32 re-association, bit for bit for the int32 prefix sum.  The
  * pages fix the [num_envs, seq_len] layout (README Usage); this layout is
  * this library's extension.  A lane owns one environment (loads coalesce
- * across environments) and tiles of 64 or 128 steps pass carries along time;
+ * across environments) and tiles of up to 256 steps pass carries along time;
  * rows of up to 128 steps on fewer than 16384 environments take blocks of 32
  * environments that hold whole rows; no alignment beyond the element size is
  * needed.  The workspace from

@@ -342,6 +342,13 @@ __global__ __launch_bounds__(W * kWave) void scan_kernel_tm_rows(const typename 
 
 // ------------------------------------------------------------- host side
 constexpr int kTmE = 8;        // steps per lane
+// Rows longer than 128 steps take 16 steps per lane in 16-wave blocks:
+// 256-step tiles, so the carries run along time in half as many tiles as
+// with 128-step ones (64 environments x 131072 steps: GAE 89 -> 58 us;
+// 256 x 32768: 13-21% faster; 4096 x 2048: 0-6%).  V-trace then spills a few
+// bytes per lane and is still faster (95 -> 70 us at 64 x 131072).
+constexpr int kTmELong = 16;
+constexpr uint64_t kTmLongRow = 128;
 constexpr int kTmWSmall = 8;   // waves per block: 64-step tiles
 constexpr int kTmWLarge = 16;  // 128-step tiles
 
@@ -396,11 +403,11 @@ inline size_t workspace_bytes_tm(uint64_t N, uint64_t T)
     return sizeof(WsHeader) + 8 * kPlanesTM * N * tm_tiles(T, w);
 }
 
-template <template <int> class Op, int W, class A>
+template <template <int> class Op, int E, int W, class A>
 hipError_t launch_tm(const typename Op<kTmE>::Args& a, const SchedTM& s, hipStream_t stream)
 {
     void* params[] = {(void*)&a, (void*)&s};
-    return hipLaunchKernel((const void*)&scan_kernel_tm<Op<kTmE>, kTmE, W, A>,
+    return hipLaunchKernel((const void*)&scan_kernel_tm<Op<E>, E, W, A>,
                            dim3(s.num_blocks), dim3(W * kWave), params, 0, stream);
 }
 
@@ -424,16 +431,16 @@ hipError_t launch_tm_rows_acc(float beta_max, const typename Op<kTmE>::Args& a, 
         return launch_tm_rows<Op, W, V, Val>(a, s, stream);
 }
 
-template <template <int> class Op, int W>
+template <template <int> class Op, int W, int E = kTmE>
 hipError_t launch_tm_acc(float beta_max, const typename Op<kTmE>::Args& a, const SchedTM& s,
                          hipStream_t stream)
 {
     using Val = typename Op<kTmE>::T;
     if constexpr (std::is_same<Val, float>::value)
-        return beta_max > kFp32BetaMax ? launch_tm<Op, W, double>(a, s, stream)
-                                       : launch_tm<Op, W, float>(a, s, stream);
+        return beta_max > kFp32BetaMax ? launch_tm<Op, E, W, double>(a, s, stream)
+                                       : launch_tm<Op, E, W, float>(a, s, stream);
     else
-        return launch_tm<Op, W, Val>(a, s, stream);
+        return launch_tm<Op, E, W, Val>(a, s, stream);
 }
 
 template <template <int> class Op>
@@ -463,11 +470,13 @@ lrs_status run_tm(const char* name, int64_t N, int64_t T, float beta_max,
         return LRS_OK;
     }
     const int W = tm_waves((uint64_t)T);
+    const bool long_rows = g_forced_tm_waves.load() == 0 && (uint64_t)T > kTmLongRow;
     SchedTM s{};
     s.N = (uint32_t)N;
     s.T = (uint32_t)T;
     s.groups = (uint32_t)((N + kWave - 1) / kWave);
-    s.time_tiles = (uint32_t)tm_tiles((uint64_t)T, W);
+    const uint64_t tile_steps = (uint64_t)(long_rows ? kTmELong : kTmE) * W;
+    s.time_tiles = (uint32_t)(((uint64_t)T + tile_steps - 1) / tile_steps);
     s.num_blocks = s.groups * s.time_tiles;
     // One lane per environment, padded to whole groups of 64: with few
     // environments and very long rows the launch could exceed the 2^32 - 1
@@ -475,10 +484,10 @@ lrs_status run_tm(const char* name, int64_t N, int64_t T, float beta_max,
     if ((uint64_t)s.num_blocks * (uint64_t)(W * kWave) > 0xffffffffull)
         return fail(LRS_ERR_INVALID_ARG,
                     "%s: time-major launch of %llu work items (ceil(num_envs/64)*64 lanes x "
-                    "%llu steps / 8) exceeds 2^32 - 1; use the row-major call for so few, so "
+                    "%llu steps / %d) exceeds 2^32 - 1; use the row-major call for so few, so "
                     "long rows",
                     name, (unsigned long long)s.num_blocks * (unsigned long long)(W * kWave),
-                    (unsigned long long)s.time_tiles * kTmE * W);
+                    (unsigned long long)(s.time_tiles * tile_steps), (int)(tile_steps / W));
     s.ws = static_cast<uint8_t*>(ws);
     if (s.time_tiles > 1) {
         const size_t need = sizeof(WsHeader) + 8 * kPlanesTM * (size_t)N * s.time_tiles;
@@ -488,7 +497,9 @@ lrs_status run_tm(const char* name, int64_t N, int64_t T, float beta_max,
         if (!aligned(ws, 16)) return fail(LRS_ERR_WORKSPACE, "%s: workspace not 16-byte aligned", name);
     }
     hipError_t e;
-    switch (W) {
+    if (long_rows) {
+        e = launch_tm_acc<Op, kTmWLarge, kTmELong>(beta_max, a, s, stream);
+    } else switch (W) {
         case 2: e = launch_tm_acc<Op, 2>(beta_max, a, s, stream); break;
         case 4: e = launch_tm_acc<Op, 4>(beta_max, a, s, stream); break;
         case 8: e = launch_tm_acc<Op, 8>(beta_max, a, s, stream); break;
