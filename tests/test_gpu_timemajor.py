@@ -128,6 +128,19 @@ def test_small_shapes(shape, est, waves):
 NARROW_SHAPES = [(n, t) for n in (1, 33, 100) for t in (1, 16, 17, 64, 100, 128)]
 
 
+@pytest.mark.parametrize("est", ["gae", "vtrace", "eligibility_traces", "prefix_sum_i32"])
+@pytest.mark.parametrize("shape", [(16383, 100), (16384, 100), (16385, 128), (70, 128), (70, 129),
+                                   (70, 256), (70, 257)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_automatic_tile_boundaries(shape, est):
+    """Both sides of every automatic choice: narrow blocks below 256 groups of
+    64 environments and 128 steps, 8 steps per lane up to 128 steps, 16 above
+    (one 256-step tile, then two)."""
+    N, T = shape
+    ro = workloads.rollout(N, T, seed=N + 3 * T, term_p=0.02, trunc_p=0.02, gamma=0.97,
+                           lambda_=0.9)
+    check(run_tm(est, ro), T)
+
+
 @pytest.mark.parametrize("est", ESTIMATORS)
 @pytest.mark.parametrize("shape", NARROW_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
 def test_narrow_whole_row_blocks(shape, est):
