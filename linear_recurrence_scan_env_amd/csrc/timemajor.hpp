@@ -12,7 +12,7 @@
 // Carries between tiles run along time, per environment: each tile publishes
 // its aggregate as soon as its own maps are composed, and its inclusive value
 // (the value at its near edge) once it has its carry.  A tile looks back over
-// up to kWindowTM earlier-in-scan tiles, to the first published inclusive
+// up to kWindowTM<W> earlier-in-scan tiles, to the first published inclusive
 // value or cut, and applies the aggregates in between from the far one to the
 // near one.  That is exactly the arithmetic by which those tiles form their
 // own inclusive values, so the result is the same bits however far a tile
@@ -43,8 +43,12 @@ struct SchedTM {
 // rebuilds y from published aggregates gets the same bits.
 constexpr uint32_t kPlanesTM = 3;
 // Aggregates a waiting tile may compose: inclusive values then propagate up
-// to 32 tiles per hop (64 environments x 131072 steps: 20% faster than 16).
-constexpr int kWindowTM = 32;
+// to that many tiles per hop.  32 for the 16-wave blocks that carry long rows
+// (64 environments x 131072 steps: 20% faster than 16); 16 for smaller
+// blocks, which carry only under a forced wave count and would otherwise
+// give up occupancy to the window's LDS.
+template <int W>
+constexpr int kWindowTM = W >= 16 ? 32 : 16;
 
 // Record payload type of a composition type: uint32 stays, fp32/fp64 -> fp32.
 template <class A>
@@ -67,8 +71,8 @@ template <class A, int W>
 struct BlockSharedTM {
     A a[W][kWave];
     A b[W][kWave];
-    RecOf<A> win_a[kWindowTM][kWave];  // aggregates gathered by the look-back
-    RecOf<A> win_b[kWindowTM][kWave];
+    RecOf<A> win_a[kWindowTM<W>][kWave];  // aggregates gathered by the look-back
+    RecOf<A> win_b[kWindowTM<W>][kWave];
     RecOf<A> carry[kWave];
 };
 
@@ -195,7 +199,7 @@ __device__ __forceinline__ void tile_body_tm(const typename Op::Args& args, cons
                     if (untag(wy, tag, y)) {
                         base = y;
                         done = true;
-                    } else if (j != last_tile && depth < kWindowTM &&
+                    } else if (j != last_tile && depth < kWindowTM<W> &&
                                untag(wa, tag, a) && untag(wb, tag, b)) {
                         moved = true;
                         // (at the far-most tile only its y is awaited, so j
