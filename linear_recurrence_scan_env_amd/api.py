@@ -150,14 +150,21 @@ def set_time_major_waves(waves_per_block: int = 0):
 # ------------------------------------------------------------ marshalling
 
 _workspaces = {}
+# Workspaces replaced by larger ones stay allocated: a HIP graph captured
+# earlier keeps the pointer it saw, and its replays still use that memory.
+_retired = []
 
 
 def workspace(device: torch.device, stream: torch.cuda.Stream, est: str, n: int, t: int):
-    """Zero-filled workspace cached per (device, stream), grown on demand."""
+    """Zero-filled workspace cached per (device, stream), grown on demand.
+    Under graph capture, run each call eagerly on the capture stream first,
+    so that capturing allocates nothing."""
     need = int(load().lrs_workspace_bytes(ESTIMATOR_ID[est], n, t))
     key = (device.index, stream.cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < need:
+        if ws is not None:
+            _retired.append(ws)
         ws = torch.zeros(max(need, 4096), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
