@@ -33,7 +33,6 @@
  *     uint8 with 0 = false, nonzero = true.  Any alignment of at least the
  *     element size is accepted; 16-byte aligned floats and 8-byte aligned
  *     masks take the vectorised fast path.
- *   - Outputs must not overlap any input or each other.
  *   - All float inputs must be finite.
  *   - Precision: coefficients and each lane's recursion are fp32; maps are
  *     composed across lanes, waves and tiles in fp32 with every lane's own
@@ -52,9 +51,16 @@
  *     NULL with workspace_bytes 0 when lrs_workspace_bytes returns 0.
  *     Its first 4224 bytes are a header the calls maintain; the 32-bit word at
  *     byte offset 4 is an error word that a call sets (bit 1, value 2) if one
- *     of its carry waits gave up after its bounded number of polls (results
- *     of that call are then wrong); it stays set until the caller clears it.
- *     Reading it after synchronising is a cheap health check.
+ *     of its carry waits gave up after its bounded number of polls (a broken
+ *     workspace, or calls sharing it concurrently).  The tile whose wait gave
+ *     up then takes a NaN carry: in floating-point calls every output of that
+ *     tile that depends on the carry is NaN; in the int32 prefix sum the tile
+ *     is summed from a carry of 0, so its sums are wrong.  The word stays set
+ *     until the caller clears it; reading it after synchronising is a cheap
+ *     health check.
+ *   - Outputs and the workspace must not share memory with any input or with
+ *     each other (checked on the host from the arrays' extents; inputs may
+ *     share memory with each other); LRS_ERR_INVALID_ARG otherwise.
  *   - stream: the HIP stream to enqueue on (NULL = the null stream).  Calls
  *     are asynchronous; the library never allocates, frees or synchronises.
  *   - Errors: argument checks run on the host before anything is enqueued
@@ -555,6 +561,47 @@ lrs_status lrs_debug_set_schedule(int force_lookback, int elems_per_lane,
  * lrs_workspace_bytes reports the larger workspace such tiles need
  * (24 bytes per env per 16 or 32 steps). */
 lrs_status lrs_debug_set_time_major_waves(int waves_per_block);
+
+/* The launch a call would make, computed on the host by the same code that
+ * plans and places the call's tiles (no GPU work, usable without a GPU).
+ * Carries between tiles rely on one ordering: every tile a block may wait for
+ * belongs to a block of lower index, which has started because a dispatch
+ * starts its workgroups in index order.  This entry lets a caller check that
+ * ordering for any shape and schedule setting. */
+typedef struct lrs_schedule_info {
+    int64_t num_blocks;       /* workgroups of the launch                          */
+    int64_t num_tiles;        /* tiles; time-major: time tiles x groups            */
+    int64_t tile_elems;       /* row-major: elements per tile                      */
+    int64_t tile_steps;       /* time-major: steps per tile                        */
+    int64_t groups;           /* time-major: environment groups (blocks per time tile) */
+    int64_t envs_per_group;   /* time-major: environments per block (64 or 32)     */
+    int32_t time_major;
+    int32_t carries;          /* tiles exchange carries (look-back / time tiles > 1) */
+    int32_t backward;         /* the scan runs from the end of each row            */
+    int32_t tiles_per_row;    /* row-major look-back in position-major order: > 1  */
+    int32_t elems_per_lane;
+    int32_t waves_per_block;
+    int32_t composition_fp64; /* maps composed in fp64 (betas may exceed 0.99)     */
+    int32_t reserved;
+} lrs_schedule_info;
+
+enum {
+    LRS_SCHED_TRUNCATED = 1,  /* backward estimators: the truncating variant; affine: reset mask */
+    LRS_SCHED_REVERSE = 2,    /* affine scan: reverse direction                      */
+    LRS_SCHED_TIME_MAJOR = 4, /* the _tm_ call                                       */
+    LRS_SCHED_16BIT = 8       /* the _bf16 / _f16 call (not for LRS_PREFIX_SUM_I32)   */
+};
+
+/* Fills *info for a call of `est` with `flags` (LRS_SCHED_*) at
+ * [num_envs, seq_len] whose betas are at most beta_max (gamma*lambda,
+ * gamma, gamma*lambda*c_bar, 1 for sums, INFINITY for the affine scan), under
+ * the current lrs_debug_set_* settings, and, when tile_of_block is not NULL
+ * and capacity >= info->num_blocks, tile_of_block[b] = the tile block b works
+ * on (time-major: time_tile * groups + group).  Returns LRS_ERR_INVALID_ARG
+ * for sizes or flags the calls reject. */
+lrs_status lrs_debug_schedule(lrs_estimator est, int flags, int64_t num_envs, int64_t seq_len,
+                              float beta_max, lrs_schedule_info* info, uint32_t* tile_of_block,
+                              int64_t capacity);
 
 #ifdef __cplusplus
 }

@@ -158,7 +158,19 @@ _retired = []
 def workspace(device: torch.device, stream: torch.cuda.Stream, est: str, n: int, t: int):
     """Zero-filled workspace cached per (device, stream), grown on demand.
     Under graph capture, run each call eagerly on the capture stream first,
-    so that capturing allocates nothing."""
+    so that capturing allocates nothing.
+
+    Calls that share a workspace must run one after another: its header
+    counts the blocks of one launch at a time.  Eager calls on one stream are
+    ordered by the stream.  A graph captured on a stream keeps that stream's
+    workspace, and replays run on the caller's current stream, so graphs
+    captured on the same stream (torch.cuda.graph uses one shared side stream
+    unless given another) must be replayed one after another, and not beside
+    eager calls issued on their capture stream.  Replaying such graphs
+    concurrently on different streams races: carry waits then give up and the
+    affected outputs are NaN, with the header's error word set (see
+    workspace_state).  To replay graphs concurrently, capture each on its own
+    stream."""
     need = int(load().lrs_workspace_bytes(ESTIMATOR_ID[est], n, t))
     key = (device.index, stream.cuda_stream)
     ws = _workspaces.get(key)

@@ -56,17 +56,31 @@ template <class D> struct AffineSel {
     template <int E> using RevN = AffineOp<E, true, false, D>;
 };
 
+// Argument checks of a GAE call (everything but the workspace's size).
 template <class D>
-lrs_status gae_entry(const char* nm, bool tm, int64_t N, int64_t T, const D* rewards,
-                     const D* values, const uint8_t* term, const uint8_t* trunc, const D* tv,
-                     const D* boot, float gamma, float lambda, D* adv, void* ws, size_t ws_bytes,
-                     hipStream_t stream)
+lrs_status gae_check(const char* nm, int64_t N, int64_t T, const D* rewards, const D* values,
+                     const uint8_t* term, const uint8_t* trunc, const D* tv, const D* boot,
+                     float gamma, float lambda, D* adv, void* ws, size_t ws_bytes)
 {
     LRS_TRY(check_common(nm, N, T));
     LRS_REQUIRE(rewards && values && adv, "%s: rewards, values and advantages are required", nm);
     LRS_TRY(check_boundary(nm, term, trunc, tv));
     LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda),
                 "%s: gamma and lambda must be in [0, 1]", nm);
+    const uint64_t nt = (uint64_t)N * (uint64_t)T, nb = nt * sizeof(D), eb = (uint64_t)N * sizeof(D);
+    const Span outs[] = {{adv, nb}, {ws, ws_bytes}};
+    const Span ins[] = {{rewards, nb}, {values, nb}, {term, nt}, {trunc, nt}, {tv, nb}, {boot, eb}};
+    return check_disjoint(nm, outs, 2, ins, 6);
+}
+
+template <class D>
+lrs_status gae_entry(const char* nm, bool tm, int64_t N, int64_t T, const D* rewards,
+                     const D* values, const uint8_t* term, const uint8_t* trunc, const D* tv,
+                     const D* boot, float gamma, float lambda, D* adv, void* ws, size_t ws_bytes,
+                     hipStream_t stream)
+{
+    LRS_TRY(gae_check<D>(nm, N, T, rewards, values, term, trunc, tv, boot, gamma, lambda, adv, ws,
+                         ws_bytes));
     GaeArgs<D> a{{term, trunc, tv, boot ? boot : rewards, boot != nullptr}, rewards, values, gamma,
                  (float)((double)gamma * (double)lambda), adv};
     const void* f[] = {rewards, values, adv, tv};
@@ -92,6 +106,11 @@ lrs_status vtrace_entry(const char* nm, bool tm, int64_t N, int64_t T, const D* 
                 "%s: gamma and lambda must be in [0, 1]", nm);
     LRS_REQUIRE(positive(rho_bar) && positive(c_bar) && positive(pg_rho_bar),
                 "%s: rho_bar, c_bar and pg_rho_bar must be > 0", nm);
+    const uint64_t nt = (uint64_t)N * (uint64_t)T, nb = nt * sizeof(D), eb = (uint64_t)N * sizeof(D);
+    const Span outs[] = {{vs, nb}, {pg_adv, nb}, {ws, ws_bytes}};
+    const Span ins[] = {{log_rhos, nb}, {rewards, nb}, {values, nb}, {term, nt},
+                        {trunc, nt},    {tv, nb},      {boot, eb}};
+    LRS_TRY(check_disjoint(nm, outs, 3, ins, 7));
     VtraceArgs<D> a{{term, trunc, tv, boot ? boot : rewards, boot != nullptr}, log_rhos, rewards,
                     values, gamma, lambda, rho_bar, c_bar, pg_rho_bar, vs, pg_adv};
     const void* f[] = {log_rhos, rewards, values, vs, pg_adv, tv};
@@ -117,6 +136,11 @@ lrs_status retrace_entry(const char* nm, bool tm, int64_t N, int64_t T, const D*
     LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda),
                 "%s: gamma and lambda must be in [0, 1]", nm);
     LRS_REQUIRE(positive(c_bar), "%s: c_bar must be > 0", nm);
+    const uint64_t nt = (uint64_t)N * (uint64_t)T, nb = nt * sizeof(D), eb = (uint64_t)N * sizeof(D);
+    const Span outs[] = {{q_ret, nb}, {ws, ws_bytes}};
+    const Span ins[] = {{log_rhos, nb}, {rewards, nb}, {q_values, nb}, {values, nb},
+                        {term, nt},     {trunc, nt},   {tv, nb},       {boot, eb}};
+    LRS_TRY(check_disjoint(nm, outs, 2, ins, 8));
     RetraceArgs<D> a{{term, trunc, tv, boot ? boot : rewards, boot != nullptr}, log_rhos, rewards,
                      q_values, values, gamma, lambda, c_bar, q_ret};
     const void* f[] = {log_rhos, rewards, q_values, values, q_ret, tv};
@@ -139,6 +163,10 @@ lrs_status lambda_returns_entry(const char* nm, bool tm, int64_t N, int64_t T, c
     LRS_TRY(check_boundary(nm, term, trunc, tv));
     LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda),
                 "%s: gamma and lambda must be in [0, 1]", nm);
+    const uint64_t nt = (uint64_t)N * (uint64_t)T, nb = nt * sizeof(D), eb = (uint64_t)N * sizeof(D);
+    const Span outs[] = {{out, nb}, {ws, ws_bytes}};
+    const Span ins[] = {{rewards, nb}, {values, nb}, {term, nt}, {trunc, nt}, {tv, nb}, {boot, eb}};
+    LRS_TRY(check_disjoint(nm, outs, 2, ins, 6));
     LambdaArgs<D> a{{term, trunc, tv, boot ? boot : rewards, boot != nullptr}, rewards, values,
                     gamma,
                     (float)((double)gamma * (double)lambda),
@@ -161,6 +189,10 @@ lrs_status discounted_returns_entry(const char* nm, bool tm, int64_t N, int64_t 
     LRS_REQUIRE(rewards && out, "%s: rewards and returns are required", nm);
     LRS_TRY(check_boundary(nm, term, trunc, tv));
     LRS_REQUIRE(unit_interval(gamma), "%s: gamma must be in [0, 1]", nm);
+    const uint64_t nt = (uint64_t)N * (uint64_t)T, nb = nt * sizeof(D), eb = (uint64_t)N * sizeof(D);
+    const Span outs[] = {{out, nb}, {ws, ws_bytes}};
+    const Span ins[] = {{rewards, nb}, {term, nt}, {trunc, nt}, {tv, nb}, {boot, eb}};
+    LRS_TRY(check_disjoint(nm, outs, 2, ins, 5));
     DiscArgs<D> a{{term, trunc, tv, boot ? boot : rewards, boot != nullptr}, rewards, gamma, out};
     const void* f[] = {rewards, out, tv};
     const void* m[] = {term, trunc};
@@ -179,6 +211,10 @@ lrs_status eligibility_traces_entry(const char* nm, bool tm, int64_t N, int64_t 
     LRS_REQUIRE(x && dones && out, "%s: x, dones and traces are required", nm);
     LRS_REQUIRE(unit_interval(gamma) && unit_interval(lambda),
                 "%s: gamma and lambda must be in [0, 1]", nm);
+    const uint64_t nt = (uint64_t)N * (uint64_t)T, nb = nt * sizeof(D);
+    const Span outs[] = {{out, nb}, {ws, ws_bytes}};
+    const Span ins[] = {{x, nb}, {dones, nt}};
+    LRS_TRY(check_disjoint(nm, outs, 2, ins, 2));
     ForwardArgs a{x, dones, (float)((double)gamma * (double)lambda), out};
     const void* f[] = {x, out};
     const void* m[] = {dones};
@@ -193,6 +229,10 @@ lrs_status prefix_sum_entry(const char* nm, bool tm, int64_t N, int64_t T, const
 {
     LRS_TRY(check_common(nm, N, T));
     LRS_REQUIRE(x && dones && out, "%s: x, dones and sums are required", nm);
+    const uint64_t nt = (uint64_t)N * (uint64_t)T, nb = nt * sizeof(D);
+    const Span outs[] = {{out, nb}, {ws, ws_bytes}};
+    const Span ins[] = {{x, nb}, {dones, nt}};
+    LRS_TRY(check_disjoint(nm, outs, 2, ins, 2));
     ForwardArgs a{x, dones, 1.0f, out};
     const void* f[] = {x, out};
     const void* m[] = {dones};
@@ -206,6 +246,10 @@ inline lrs_status prefix_sum_i32_entry(const char* nm, bool tm, int64_t N, int64
 {
     LRS_TRY(check_common(nm, N, T));
     LRS_REQUIRE(x && dones && out, "%s: x, dones and sums are required", nm);
+    const uint64_t nt = (uint64_t)N * (uint64_t)T, nb = nt * sizeof(int32_t);
+    const Span outs[] = {{out, nb}, {ws, ws_bytes}};
+    const Span ins[] = {{x, nb}, {dones, nt}};
+    LRS_TRY(check_disjoint(nm, outs, 2, ins, 2));
     ForwardArgs a{x, dones, 1.0f, out};
     const void* f[] = {x, out};
     const void* m[] = {dones};
@@ -220,6 +264,10 @@ lrs_status affine_scan_entry(const char* nm, bool tm, int64_t N, int64_t T, cons
     LRS_TRY(check_common(nm, N, T));
     LRS_REQUIRE(alpha && beta && out, "%s: alpha, beta and out are required", nm);
     LRS_REQUIRE(reverse == 0 || reverse == 1, "%s: reverse must be 0 or 1", nm);
+    const uint64_t nt = (uint64_t)N * (uint64_t)T, nb = nt * sizeof(D), eb = (uint64_t)N * sizeof(D);
+    const Span outs[] = {{out, nb}, {ws, ws_bytes}};
+    const Span ins[] = {{alpha, nb}, {beta, nb}, {reset, nt}, {carry_in, eb}};
+    LRS_TRY(check_disjoint(nm, outs, 2, ins, 4));
     AffineArgs<D> a{alpha, beta, reset, carry_in ? carry_in : alpha, carry_in != nullptr, out};
     const void* f[] = {alpha, beta, out};
     const void* m[] = {reset};

@@ -91,6 +91,30 @@ __device__ __forceinline__ void split_index32(uint32_t u, const Sched& s, uint32
     t = u - q * s.T;
 }
 
+// The tile block b works on.  Look-back launches take tiles so that every
+// tile a block may wait for belongs to a block of lower index (workgroups of
+// a dispatch start in index order, so that block is running or done):
+// position-major order (all rows' outermost tiles first, counted from the
+// row end for backward scans) when every row spans tiles_per_row > 1 whole
+// tiles, else flat order from the end of the array (backward) or its start
+// (forward).  Launches without carries take tiles in flat order.  Shared by
+// the kernel and the host's schedule diagnostics (lrs_debug_schedule).
+struct TilePlace {
+    uint32_t tile;
+    uint32_t row;  // position-major only: the tile's row and its place in it
+    uint32_t pos;
+};
+
+__host__ __device__ inline TilePlace place_tile(uint32_t b, const Sched& s, bool backward)
+{
+    if (s.lookback && s.tiles_per_row > 1) {
+        const uint32_t pos = b / s.rows, row = b % s.rows;
+        const uint32_t p = backward ? s.tiles_per_row - 1u - pos : pos;
+        return {row * s.tiles_per_row + p, row, p};
+    }
+    return {(s.lookback && backward) ? s.num_tiles - 1u - b : b, 0u, 0u};
+}
+
 template <class A, int W>
 struct BlockShared {
     A a[W];
@@ -220,19 +244,15 @@ __global__ __launch_bounds__(W * kWave) void scan_kernel(const typename Op::Args
 
     const int tid = threadIdx.x;
     // On the look-back path the tile a block depends on always belongs to a
-    // block of lower index: backward scans take tiles from the end of their
-    // row (or of the array), forward scans from the start.
-    uint32_t tile = blockIdx.x;
+    // block of lower index (place_tile).
+    const TilePlace tp = place_tile(blockIdx.x, s, kB);
+    const uint32_t tile = tp.tile;
     uint64_t tile_row;
     uint32_t tile_t;
     if (s.lookback && s.tiles_per_row > 1) {
-        const uint32_t pos = blockIdx.x / s.rows, row = blockIdx.x % s.rows;
-        const uint32_t p = kB ? s.tiles_per_row - 1u - pos : pos;
-        tile = row * s.tiles_per_row + p;
-        tile_row = row;
-        tile_t = p * kTile;
+        tile_row = tp.row;
+        tile_t = tp.pos * kTile;
     } else {
-        if (s.lookback && kB) tile = s.num_tiles - 1u - blockIdx.x;
         split_index((uint64_t)tile * kTile, s, tile_row, tile_t);
     }
     const uint64_t tile_start = (uint64_t)tile * kTile;
@@ -415,18 +435,22 @@ hipError_t launch_any(int cfg, const typename Op<4>::Args& a, const Sched& s, hi
     }
 }
 
-// Shared checks and launch.  floats/masks: every array the kernel may
-// vector-load, for the alignment decision.
+// The schedule of a row-major call: tile shape (an index into kCfgs), the
+// Sched fields that do not depend on pointers, and the composition type.
+struct Plan {
+    int cfg;
+    bool fp64;
+    Sched s;
+};
+
+// fp32 maps compose in fp64 when the call's betas may come close to 1:
+// long near-undamped chains (sums) accumulate fp32 rounding beyond the
+// parity bound, while damped chains forget it within ~1/(1 - beta) steps.
 template <template <int> class Op>
-lrs_status run(const char* name, int64_t N, int64_t T, float beta_max, const typename Op<4>::Args& a,
-               const void* const* floats, int nfloats, const void* const* masks, int nmasks,
-               void* ws, size_t ws_bytes, hipStream_t stream)
+Plan plan_row_major(int64_t N, int64_t T, float beta_max)
 {
     const uint64_t total = (uint64_t)N * (uint64_t)T;
     bool lookback = false;
-    // fp32 maps compose in fp64 when the call's betas may come close to 1:
-    // long near-undamped chains (sums) accumulate fp32 rounding beyond the
-    // parity bound, while damped chains forget it within ~1/(1 - beta) steps.
     using Val = typename Op<4>::T;
     const bool fp64 = std::is_same<Val, float>::value && beta_max > kFp32BetaMax;
     int cfg = choose_cfg(total, (uint64_t)T, Op<4>::kWideTiles, Op<4>::kLookbackTile, fp64,
@@ -460,8 +484,26 @@ lrs_status run(const char* name, int64_t N, int64_t T, float beta_max, const typ
     while ((1ull << s.log2T) < (uint64_t)T) ++s.log2T;
     s.magic = s.pow2 ? 0 : ~0ull / (uint64_t)T + 1ull;  // T >= 3 here: no overflow
     s.lane_in_row = (uint64_t)T % (uint64_t)k.E == 0 ? 1 : 0;
+    s.ws = nullptr;
+    s.vec = 0;
+    return Plan{cfg, fp64, s};
+}
+
+// Shared checks and launch.  floats/masks: every array the kernel may
+// vector-load, for the alignment decision.
+template <template <int> class Op>
+lrs_status run(const char* name, int64_t N, int64_t T, float beta_max, const typename Op<4>::Args& a,
+               const void* const* floats, int nfloats, const void* const* masks, int nmasks,
+               void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    using Val = typename Op<4>::T;
+    Plan plan = plan_row_major<Op>(N, T, beta_max);
+    const int cfg = plan.cfg;
+    const bool fp64 = plan.fp64;
+    const Cfg& k = kCfgs[cfg];
+    Sched s = plan.s;
     s.ws = static_cast<uint8_t*>(ws);
-    if (lookback) {
+    if (s.lookback) {
         const size_t need = sizeof(WsHeader) + 8 * kRecordWords * (size_t)s.num_tiles;
         if (ws == nullptr || ws_bytes < need)
             return fail(LRS_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", name,
@@ -504,6 +546,43 @@ inline lrs_status check_boundary(const char* name, const uint8_t* term, const ui
     if (term == nullptr) return fail(LRS_ERR_INVALID_ARG, "%s: terminateds is required", name);
     if (trunc != nullptr && tv == nullptr)
         return fail(LRS_ERR_INVALID_ARG, "%s: truncateds given without trunc_values", name);
+    return LRS_OK;
+}
+
+// Memory an array argument covers (a null pointer covers nothing).
+struct Span {
+    const void* p;
+    uint64_t bytes;
+};
+
+inline bool spans_overlap(const Span& x, const Span& y)
+{
+    if (x.p == nullptr || y.p == nullptr || x.bytes == 0 || y.bytes == 0) return false;
+    const uintptr_t a = (uintptr_t)x.p, b = (uintptr_t)y.p;
+    return a < b + y.bytes && b < a + x.bytes;
+}
+
+// Every array a call writes (its outputs and the workspace) must be disjoint
+// from every array it reads and from every other one it writes: a tile reads
+// its neighbours' inputs (successor values, the predecessor's done flag)
+// while other tiles store, so overlapping memory would race.
+inline lrs_status check_disjoint(const char* name, const Span* outs, int nouts, const Span* ins,
+                                 int nins)
+{
+    for (int i = 0; i < nouts; ++i) {
+        for (int j = 0; j < nins; ++j)
+            if (spans_overlap(outs[i], ins[j]))
+                return fail(LRS_ERR_INVALID_ARG,
+                            "%s: output array %d overlaps input array %d (outputs and the "
+                            "workspace must not share memory with any input)",
+                            name, i, j);
+        for (int k = i + 1; k < nouts; ++k)
+            if (spans_overlap(outs[i], outs[k]))
+                return fail(LRS_ERR_INVALID_ARG,
+                            "%s: output arrays %d and %d overlap (outputs and the workspace must "
+                            "not share memory)",
+                            name, i, k);
+    }
     return LRS_OK;
 }
 

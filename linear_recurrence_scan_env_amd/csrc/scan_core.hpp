@@ -451,7 +451,8 @@ __device__ __forceinline__ void store_u32(int32_t* __restrict__ p, const uint32_
 // blocks to tiles so).  Workgroups of a dispatch are started in index order,
 // so those blocks are running or finished and every wait ends; each wait is
 // also bounded (kMaxPolls), so a violated assumption or a corrupted
-// workspace yields a flagged error in the header instead of a hang.
+// workspace yields a flagged error in the header and NaN outputs (see
+// give_up_carry) instead of a hang.
 
 constexpr uint32_t kGroups = 32;
 constexpr uint32_t kLine = 128;  // bytes between counters
@@ -518,6 +519,19 @@ __device__ __forceinline__ void close_launch(WsHeader* hdr, uint32_t top_seen, u
 // Upper bound on the polls of one look-back wait (about a second).
 constexpr uint32_t kMaxPolls = 1u << 20;
 constexpr uint32_t kErrTimeout = 2u;
+
+// The carry a tile takes when its wait gave up: a quiet NaN for floating-point
+// maps, so that every output that depends on the missing carry is NaN rather
+// than a plausible wrong value; 0 for the integer prefix sum (its outputs in
+// that tile are then wrong, and the header's error word says so).
+template <class A>
+__device__ __forceinline__ A give_up_carry()
+{
+    if constexpr (std::is_floating_point<A>::value)
+        return __builtin_nan("");
+    else
+        return A(0);
+}
 
 __device__ __forceinline__ uint64_t ld_agent(const uint64_t* p)
 {
@@ -644,7 +658,7 @@ __device__ A lookback_carry(const uint64_t* rec, uint32_t tile, uint32_t num_til
                 if (lane == 0)
                     __hip_atomic_fetch_or(error, kErrTimeout, __ATOMIC_RELAXED,
                                           __HIP_MEMORY_SCOPE_AGENT);
-                return A(0);
+                return give_up_carry<A>();
             }
             __builtin_amdgcn_s_sleep(1);
         }
@@ -683,7 +697,7 @@ __device__ A lookback_carry(const uint64_t* rec, uint32_t tile, uint32_t num_til
                 if (lane == 0)
                     __hip_atomic_fetch_or(error, kErrTimeout, __ATOMIC_RELAXED,
                                           __HIP_MEMORY_SCOPE_AGENT);
-                return A(0);
+                return give_up_carry<A>();
             }
             __builtin_amdgcn_s_sleep(1);
         }

@@ -18,7 +18,8 @@
 // own inclusive values, so the result is the same bits however far a tile
 // had to look: deterministic.  Blocks take tiles time-tile-major from the
 // scan's far end, so every tile a block reads belongs to a block of lower
-// index, which is running or done.  Every wait is bounded (kMaxPolls).
+// index, which is running or done.  Every wait is bounded (kMaxPolls); a
+// wait that gives up flags the header and makes the tile's outputs NaN.
 #pragma once
 
 #include "launch.hpp"
@@ -65,6 +66,20 @@ __device__ __forceinline__ bool untag(uint64_t w, uint32_t tag, R& v)
     if ((uint32_t)(w >> 32) != tag) return false;
     v = __builtin_bit_cast(R, (uint32_t)w);
     return true;
+}
+
+// The tile (time tile k, environment group g) block b works on: tiles are
+// taken time-tile-major from the scan's far end, so the tile one step
+// farther in scan order, the only kind a tile waits for, belongs to block
+// b - groups.  Shared by the kernel and lrs_debug_schedule.
+struct TilePlaceTM {
+    uint32_t k, g;
+};
+
+__host__ __device__ inline TilePlaceTM place_tile_tm(uint32_t b, const SchedTM& s, bool backward)
+{
+    const uint32_t pos = b / s.groups, g = b % s.groups;
+    return {backward ? s.time_tiles - 1u - pos : pos, g};
 }
 
 template <class A, int W>
@@ -186,6 +201,7 @@ __device__ __forceinline__ void tile_body_tm(const typename Op::Args& args, cons
             bool done = !active;
             R base = R(0);
             uint32_t polls = 0;
+            bool gave_up = false;
             while (__ballot(!done) != 0) {
                 bool moved = false;
                 if (!done) {
@@ -219,6 +235,7 @@ __device__ __forceinline__ void tile_body_tm(const typename Op::Args& args, cons
                     if (lane == 0)
                         __hip_atomic_fetch_or(&hdr->error, kErrTimeout, __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_AGENT);
+                    gave_up = true;
                     break;
                 }
                 // pause only when no lane moved on
@@ -227,6 +244,9 @@ __device__ __forceinline__ void tile_body_tm(const typename Op::Args& args, cons
             carry = base;
             for (int d = depth - 1; d >= 0; --d)
                 carry = apply(Aff<R>{sh.win_a[d][lane], sh.win_b[d][lane]}, carry);
+            // a wait that gave up leaves every lane of the tile without its
+            // carry: NaN for fp32 maps (0 for the integer prefix sum)
+            if (gave_up) carry = give_up_carry<R>();
             if (active && !near_most && tile.b != R(0))
                 st_agent(rec_y + own, tagged(tag, apply(tile, carry)));
         }
@@ -251,9 +271,8 @@ __global__ __launch_bounds__(W * kWave) void scan_kernel_tm(const typename Op::A
 {
     constexpr uint32_t kSteps = (uint32_t)E * W;
     __shared__ BlockSharedTM<A, W> sh;
-    // Tiles are taken time-tile-major from the scan's far end.
-    const uint32_t pos = blockIdx.x / s.groups, g = blockIdx.x % s.groups;
-    const uint32_t k = Op::kBackward ? s.time_tiles - 1u - pos : pos;
+    const TilePlaceTM tp = place_tile_tm(blockIdx.x, s, Op::kBackward);
+    const uint32_t k = tp.k, g = tp.g;
     const bool full = (uint64_t)(k + 1u) * kSteps <= s.T && (uint64_t)(g + 1u) * kWave <= s.N;
     if (full)
         tile_body_tm<Op, E, W, A, true>(args, s, k, g, sh);
@@ -456,19 +475,51 @@ hipError_t launch_tm_acc(float beta_max, const typename Op<kTmE>::Args& a, const
         return launch_tm<Op, E, W, Val>(a, s, stream);
 }
 
+// The schedule of a time-major call: narrow whole-row blocks (rows_waves > 0
+// waves of kTmRowsV environments) or the wide kernel (waves W, 16 steps per
+// lane when long_rows), and its SchedTM without the workspace.  The launch
+// checks that the grid fits a dispatch.
+struct PlanTM {
+    int rows_waves;
+    int W;
+    bool long_rows;
+    uint64_t tile_steps;
+    SchedTM s;
+};
+
+inline PlanTM plan_time_major(int64_t N, int64_t T)
+{
+    PlanTM p{};
+    p.s.N = (uint32_t)N;
+    p.s.T = (uint32_t)T;
+    p.s.ws = nullptr;
+    p.rows_waves = tm_rows_waves((uint64_t)N, (uint64_t)T);
+    if (p.rows_waves) {
+        p.W = p.rows_waves;
+        p.tile_steps = (uint64_t)T;
+        p.s.groups = (uint32_t)((N + kTmRowsV - 1) / kTmRowsV);
+        p.s.time_tiles = 1;
+        p.s.num_blocks = p.s.groups;
+        return p;
+    }
+    p.W = tm_waves((uint64_t)T);
+    p.long_rows = g_forced_tm_waves.load() == 0 && (uint64_t)T > kTmLongRow;
+    p.s.groups = (uint32_t)((N + kWave - 1) / kWave);
+    p.tile_steps = (uint64_t)(p.long_rows ? kTmELong : kTmE) * p.W;
+    p.s.time_tiles = (uint32_t)(((uint64_t)T + p.tile_steps - 1) / p.tile_steps);
+    p.s.num_blocks = p.s.groups * p.s.time_tiles;
+    return p;
+}
+
 template <template <int> class Op>
 lrs_status run_tm(const char* name, int64_t N, int64_t T, float beta_max,
                   const typename Op<kTmE>::Args& a, void* ws, size_t ws_bytes, hipStream_t stream)
 {
     if (N >= (int64_t(1) << 32))
         return fail(LRS_ERR_INVALID_ARG, "%s: time-major calls need num_envs < 2^32", name);
-    if (const int Wr = tm_rows_waves((uint64_t)N, (uint64_t)T)) {
-        SchedTM s{};
-        s.N = (uint32_t)N;
-        s.T = (uint32_t)T;
-        s.groups = (uint32_t)((N + kTmRowsV - 1) / kTmRowsV);
-        s.time_tiles = 1;
-        s.num_blocks = s.groups;
+    const PlanTM plan = plan_time_major(N, T);
+    if (const int Wr = plan.rows_waves) {
+        SchedTM s = plan.s;
         s.ws = static_cast<uint8_t*>(ws);
         hipError_t e;
         switch (Wr) {
@@ -482,15 +533,10 @@ lrs_status run_tm(const char* name, int64_t N, int64_t T, float beta_max,
         g_err[0] = '\0';
         return LRS_OK;
     }
-    const int W = tm_waves((uint64_t)T);
-    const bool long_rows = g_forced_tm_waves.load() == 0 && (uint64_t)T > kTmLongRow;
-    SchedTM s{};
-    s.N = (uint32_t)N;
-    s.T = (uint32_t)T;
-    s.groups = (uint32_t)((N + kWave - 1) / kWave);
-    const uint64_t tile_steps = (uint64_t)(long_rows ? kTmELong : kTmE) * W;
-    s.time_tiles = (uint32_t)(((uint64_t)T + tile_steps - 1) / tile_steps);
-    s.num_blocks = s.groups * s.time_tiles;
+    const int W = plan.W;
+    const bool long_rows = plan.long_rows;
+    const uint64_t tile_steps = plan.tile_steps;
+    SchedTM s = plan.s;
     // One lane per environment, padded to whole groups of 64: with few
     // environments and very long rows the launch could exceed the 2^32 - 1
     // work items a dispatch holds.

@@ -179,7 +179,7 @@ def test_long_chains_gamma_lambda_one(est):
     for tile in [(4, 1), (8, 4)]:
         lrs.set_schedule(True, *tile)
         try:
-            check(run_pair(est, ro, trunc=False), T, tol=2e-4)
+            check(run_pair(est, ro, trunc=False), T)
         finally:
             lrs.set_schedule(False, 0, 0)
 
