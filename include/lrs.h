@@ -138,6 +138,27 @@ lrs_status lrs_gae_f32(int64_t num_envs, int64_t seq_len,
                        void* workspace, size_t workspace_bytes,
                        hipStream_t stream);
 
+/* lrs_gae_f32 for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same computation and results, without a workspace argument.  The carry
+ * records live in a static device area of 8 MiB per GPU, held until the
+ * process ends, so calls accept num_envs * seq_len <= 67075072 (the area
+ * holds 4224 + 32 * ceil(num_envs * seq_len / 256) bytes) and larger ones
+ * return LRS_ERR_INVALID_ARG.  The library allocates nothing in this call.
+ * Every call on a GPU shares that GPU's area: calls that overlap in time on
+ * one GPU race (as calls sharing a workspace do), so order them on one
+ * stream.  The first call on each device clears the area with a small kernel
+ * on `stream` and must not be made under graph capture (it returns
+ * LRS_ERR_INVALID_ARG then); later calls may be captured.  Arguments and
+ * errors otherwise as lrs_gae_f32. */
+lrs_status lrs_gae_noalloc_f32(int64_t num_envs, int64_t seq_len,
+                               const float* rewards, const float* values,
+                               const uint8_t* terminateds, const uint8_t* truncateds,
+                               const float* trunc_values, const float* bootstrap_value,
+                               float gamma, float lambda,
+                               float* advantages,
+                               hipStream_t stream);
+
 /* V-trace (README Kernels table, compute_vtrace: importance-weighted targets
  * and advantages; Espeholt et al. 2018 sec. 4.1 eq. 1 with the lambda-trace of
  * sec. 4.2).  w_t = exp(log_rhos_t) = pi/mu of the taken action:

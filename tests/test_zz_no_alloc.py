@@ -1,0 +1,127 @@
+"""lrs_gae_noalloc_f32, the GAE entry point for callers that cannot allocate,
+against lrs_gae_f32 (same kernels, caller workspace) through the C ABI.
+
+The two share every kernel and the carry protocol is deterministic, so the
+outputs must be identical bit for bit (stricter than the fp32 bound against
+the oracle, which the lrs_gae_f32 parity tests already hold).  Two calls in a
+row reuse the static scratch area, the second on a smaller input; a third
+case checks the size limit and that a rejected call leaves the area usable.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+import linear_recurrence_scan_env_amd as lrs  # noqa: E402
+from linear_recurrence_scan_env_amd import workloads  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+MAX_ELEMS = 67075072  # (8 MiB - 4224) / 32 * 256
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lib = lrs.load()
+    f = lib.lrs_gae_noalloc_f32
+    P, I64, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
+    f.argtypes = [I64, I64, P, P, P, P, P, P, F, F, P, P]
+    f.restype = ctypes.c_int
+    return lib
+
+
+def dev(a):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def ptr(x):
+    return None if x is None else x.data_ptr()
+
+
+def both(lib, ro, trunc):
+    """(noalloc output, lrs_gae_f32 output, oracle) on one rollout."""
+    a = ro.arrays
+    D = {k: dev(v) for k, v in a.items()}
+    n, t = ro.num_envs, ro.seq_len
+    tr = D["truncateds"] if trunc else None
+    tv = D["trunc_values"] if trunc else None
+    stream = torch.cuda.current_stream().cuda_stream
+    out_s = torch.full((n, t), float("nan"), device="cuda")
+    out_w = torch.full((n, t), float("nan"), device="cuda")
+    st = lib.lrs_gae_noalloc_f32(n, t, ptr(D["rewards"]), ptr(D["values"]), ptr(D["terminateds"]),
+                                 ptr(tr), ptr(tv), ptr(D["bootstrap_value"]), ro.gamma, ro.lambda_,
+                                 ptr(out_s), stream)
+    assert st == 0, lib.lrs_last_error()
+    ws = torch.zeros(lib.lrs_workspace_bytes(0, n, t), dtype=torch.uint8, device="cuda")
+    st = lib.lrs_gae_f32(n, t, ptr(D["rewards"]), ptr(D["values"]), ptr(D["terminateds"]), ptr(tr),
+                         ptr(tv), ptr(D["bootstrap_value"]), ro.gamma, ro.lambda_, ptr(out_w),
+                         ptr(ws), ws.numel(), stream)
+    assert st == 0, lib.lrs_last_error()
+    ref = oracle.gae(a["rewards"], a["values"], a["terminateds"], ro.gamma, ro.lambda_,
+                     truncateds=a["truncateds"] if trunc else None,
+                     trunc_values=a["trunc_values"] if trunc else None,
+                     bootstrap_value=a["bootstrap_value"])
+    torch.cuda.synchronize()
+    return out_s.cpu().numpy(), out_w.cpu().numpy(), ref
+
+
+def tol_for(t):
+    return 1e-5 if t <= 4096 else 1e-4
+
+
+def check(got, want, ref, t):
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), \
+        f"{np.count_nonzero(got != want)} elements differ from lrs_gae_f32"
+    err = np.abs(got.astype(np.float64) - ref) / (1.0 + np.abs(ref))
+    assert err.max() <= tol_for(t)
+
+
+def test_two_calls_in_a_row_second_smaller(lib):
+    # 64 x 131072: the look-back path over 4096 tiles (the scratch area's
+    # header and records); then 5 x 3001: look-back again, fewer tiles, with
+    # the area holding the first call's records
+    big = workloads.rollout(64, 131072, seed=11, term_p=1e-4, trunc_p=1e-4, gamma=0.99,
+                            lambda_=0.95)
+    small = workloads.rollout(5, 3001, seed=12, term_p=0.01, trunc_p=0.01, gamma=0.99,
+                              lambda_=0.95)
+    for ro in (big, small):
+        got, want, ref = both(lib, ro, trunc=True)
+        check(got, want, ref, ro.seq_len)
+
+
+def test_whole_rows_and_forced_lookback(lib):
+    ro = workloads.rollout(4096, 128, seed=13, term_p=1 / 64, trunc_p=1 / 128, gamma=0.99,
+                           lambda_=0.95)
+    got, want, ref = both(lib, ro, trunc=True)
+    check(got, want, ref, 128)
+    lrs.set_schedule(True, 4, 1)
+    try:
+        ro = workloads.rollout(7, 5000, seed=14, term_p=0.002, trunc_p=0.0, gamma=0.99,
+                               lambda_=0.95)
+        got, want, ref = both(lib, ro, trunc=False)
+        check(got, want, ref, 5000)
+    finally:
+        lrs.set_schedule(False, 0, 0)
+
+
+def test_size_limit(lib):
+    stream = torch.cuda.current_stream().cuda_stream
+    fake = ctypes.c_void_p(0x10000)
+    out = ctypes.c_void_p(0x70000000)
+    # one element over the limit: rejected on the host, nothing enqueued
+    st = lib.lrs_gae_noalloc_f32(1, MAX_ELEMS + 1, fake, fake, fake, None, None, None, 0.9, 0.9,
+                                 out, stream)
+    assert st == 1 and b"scratch" in lib.lrs_last_error()
+    st = lib.lrs_gae_noalloc_f32(2, MAX_ELEMS // 2 + 1, fake, fake, fake, None, None, None, 0.9,
+                                 0.9, out, stream)
+    assert st == 1
+    # the area still serves a call after the rejections
+    ro = workloads.rollout(3, 70001, seed=15, term_p=1e-4, trunc_p=1e-4, gamma=0.99,
+                           lambda_=0.95)
+    got, want, ref = both(lib, ro, trunc=True)
+    check(got, want, ref, 70001)
