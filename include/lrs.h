@@ -28,11 +28,34 @@
  * Conventions shared by every call
  *   - num_envs (N) >= 1, 1 <= seq_len (T) < 2^31, N*T < 2^34.
  *   - Every array pointer is DEVICE memory owned by the caller.  Arrays of
- *     shape [N, T] are row-major and contiguous (row stride T); per-env
- *     arrays have N elements.  Float inputs/outputs are fp32; masks are
+ *     shape [N, T] are row-major with unit stride along T; per-env arrays
+ *     have N elements, contiguous.  Float inputs/outputs are fp32; masks are
  *     uint8 with 0 = false, nonzero = true.  Any alignment of at least the
  *     element size is accepted; 16-byte aligned floats and 8-byte aligned
  *     masks take the vectorised fast path.
+ *   - strides: NULL (every [N, T] array contiguous, row stride T), or a HOST
+ *     array with one row stride per [N, T] array argument of the call -- the
+ *     number of elements between the starts of consecutive rows -- in the
+ *     order those arguments appear in the signature, inputs and outputs
+ *     alike (for GAE: rewards, values, terminateds, truncateds,
+ *     trunc_values, advantages).  0 means contiguous; otherwise the stride
+ *     must be >= T.  Entries of absent (NULL) arrays are ignored.  A view
+ *     such as buffer[:, :T] of a wider [N, Tmax] buffer is then read or
+ *     written in place.  The vectorised fast path also needs every strided
+ *     array's stride times its element size to be a multiple of the vector
+ *     width (16 bytes for fp32 data, the elements per lane for masks) and T
+ *     a multiple of the elements per lane; other strides take the scalar
+ *     path.  The time-major (_tm_) calls take the stride between
+ *     consecutive time steps (>= N).  The entries, call by call:
+ *       GAE, TD(lambda) returns: rewards, values, terminateds, truncateds,
+ *         trunc_values, out
+ *       discounted returns: rewards, terminateds, truncateds, trunc_values, out
+ *       V-trace: log_rhos, rewards, values, terminateds, truncateds,
+ *         trunc_values, vs, pg_advantages
+ *       Retrace: log_rhos, rewards, q_values, values, terminateds,
+ *         truncateds, trunc_values, q_ret
+ *       eligibility traces, prefix sums: x, dones, out
+ *       affine scan: alpha, beta, reset, out
  *   - All float inputs must be finite.
  *   - Precision: coefficients and each lane's recursion are fp32; maps are
  *     composed across lanes, waves and tiles in fp32 with every lane's own
@@ -135,6 +158,7 @@ lrs_status lrs_gae_f32(int64_t num_envs, int64_t seq_len,
                        const float* trunc_values, const float* bootstrap_value,
                        float gamma, float lambda,
                        float* advantages,
+                       const int64_t* strides,
                        void* workspace, size_t workspace_bytes,
                        hipStream_t stream);
 
@@ -156,7 +180,7 @@ lrs_status lrs_gae_noalloc_f32(int64_t num_envs, int64_t seq_len,
                                const uint8_t* terminateds, const uint8_t* truncateds,
                                const float* trunc_values, const float* bootstrap_value,
                                float gamma, float lambda,
-                               float* advantages,
+                               float* advantages, const int64_t* strides,
                                hipStream_t stream);
 
 /* V-trace (README Kernels table, compute_vtrace: importance-weighted targets
@@ -176,6 +200,7 @@ lrs_status lrs_vtrace_f32(int64_t num_envs, int64_t seq_len,
                           float gamma, float lambda,
                           float rho_bar, float c_bar, float pg_rho_bar,
                           float* vs, float* pg_advantages,
+                          const int64_t* strides,
                           void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
 
@@ -192,6 +217,7 @@ lrs_status lrs_retrace_f32(int64_t num_envs, int64_t seq_len,
                            const float* trunc_values, const float* bootstrap_value,
                            float gamma, float lambda, float c_bar,
                            float* q_ret,
+                           const int64_t* strides,
                            void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
@@ -205,6 +231,7 @@ lrs_status lrs_lambda_returns_f32(int64_t num_envs, int64_t seq_len,
                                   const float* trunc_values, const float* bootstrap_value,
                                   float gamma, float lambda,
                                   float* returns,
+                                  const int64_t* strides,
                                   void* workspace, size_t workspace_bytes,
                                   hipStream_t stream);
 
@@ -219,6 +246,7 @@ lrs_status lrs_discounted_returns_f32(int64_t num_envs, int64_t seq_len,
                                       const float* trunc_values, const float* bootstrap_value,
                                       float gamma,
                                       float* returns,
+                                      const int64_t* strides,
                                       void* workspace, size_t workspace_bytes,
                                       hipStream_t stream);
 
@@ -230,6 +258,7 @@ lrs_status lrs_eligibility_traces_f32(int64_t num_envs, int64_t seq_len,
                                       const float* x, const uint8_t* dones,
                                       float gamma, float lambda,
                                       float* traces,
+                                      const int64_t* strides,
                                       void* workspace, size_t workspace_bytes,
                                       hipStream_t stream);
 
@@ -242,12 +271,14 @@ lrs_status lrs_eligibility_traces_f32(int64_t num_envs, int64_t seq_len,
 lrs_status lrs_episodic_prefix_sum_i32(int64_t num_envs, int64_t seq_len,
                                        const int32_t* x, const uint8_t* dones,
                                        int32_t* sums,
+                                       const int64_t* strides,
                                        void* workspace, size_t workspace_bytes,
                                        hipStream_t stream);
 
 lrs_status lrs_episodic_prefix_sum_f32(int64_t num_envs, int64_t seq_len,
                                        const float* x, const uint8_t* dones,
                                        float* sums,
+                                       const int64_t* strides,
                                        void* workspace, size_t workspace_bytes,
                                        hipStream_t stream);
 
@@ -273,6 +304,7 @@ lrs_status lrs_affine_scan_f32(int64_t num_envs, int64_t seq_len,
                                const uint8_t* reset, const float* carry_in,
                                int reverse,
                                float* y,
+                               const int64_t* strides,
                                void* workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
@@ -295,6 +327,7 @@ lrs_status lrs_gae_bf16(int64_t num_envs, int64_t seq_len,
                         const uint8_t* terminateds, const uint8_t* truncateds,
                         const lrs_bf16* trunc_values, const lrs_bf16* bootstrap_value,
                         float gamma, float lambda, lrs_bf16* advantages,
+                        const int64_t* strides,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 lrs_status lrs_vtrace_bf16(int64_t num_envs, int64_t seq_len,
                            const lrs_bf16* log_rhos, const lrs_bf16* rewards, const lrs_bf16* values,
@@ -303,6 +336,7 @@ lrs_status lrs_vtrace_bf16(int64_t num_envs, int64_t seq_len,
                            float gamma, float lambda,
                            float rho_bar, float c_bar, float pg_rho_bar,
                            lrs_bf16* vs, lrs_bf16* pg_advantages,
+                           const int64_t* strides,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 lrs_status lrs_retrace_bf16(int64_t num_envs, int64_t seq_len,
                             const lrs_bf16* log_rhos, const lrs_bf16* rewards,
@@ -310,33 +344,39 @@ lrs_status lrs_retrace_bf16(int64_t num_envs, int64_t seq_len,
                             const uint8_t* terminateds, const uint8_t* truncateds,
                             const lrs_bf16* trunc_values, const lrs_bf16* bootstrap_value,
                             float gamma, float lambda, float c_bar, lrs_bf16* q_ret,
+                            const int64_t* strides,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 lrs_status lrs_lambda_returns_bf16(int64_t num_envs, int64_t seq_len,
                                    const lrs_bf16* rewards, const lrs_bf16* values,
                                    const uint8_t* terminateds, const uint8_t* truncateds,
                                    const lrs_bf16* trunc_values, const lrs_bf16* bootstrap_value,
                                    float gamma, float lambda, lrs_bf16* returns,
+                                   const int64_t* strides,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 lrs_status lrs_discounted_returns_bf16(int64_t num_envs, int64_t seq_len,
                                        const lrs_bf16* rewards,
                                        const uint8_t* terminateds, const uint8_t* truncateds,
                                        const lrs_bf16* trunc_values, const lrs_bf16* bootstrap_value,
                                        float gamma, lrs_bf16* returns,
+                                       const int64_t* strides,
                                        void* workspace, size_t workspace_bytes,
                                        hipStream_t stream);
 lrs_status lrs_eligibility_traces_bf16(int64_t num_envs, int64_t seq_len,
                                        const lrs_bf16* x, const uint8_t* dones,
                                        float gamma, float lambda, lrs_bf16* traces,
+                                       const int64_t* strides,
                                        void* workspace, size_t workspace_bytes,
                                        hipStream_t stream);
 lrs_status lrs_episodic_prefix_sum_bf16(int64_t num_envs, int64_t seq_len,
                                         const lrs_bf16* x, const uint8_t* dones, lrs_bf16* sums,
+                                        const int64_t* strides,
                                         void* workspace, size_t workspace_bytes,
                                         hipStream_t stream);
 lrs_status lrs_affine_scan_bf16(int64_t num_envs, int64_t seq_len,
                                 const lrs_bf16* alpha, const lrs_bf16* beta,
                                 const uint8_t* reset, const lrs_bf16* carry_in, int reverse,
                                 lrs_bf16* y,
+                                const int64_t* strides,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 lrs_status lrs_gae_f16(int64_t num_envs, int64_t seq_len,
@@ -344,6 +384,7 @@ lrs_status lrs_gae_f16(int64_t num_envs, int64_t seq_len,
                         const uint8_t* terminateds, const uint8_t* truncateds,
                         const lrs_f16* trunc_values, const lrs_f16* bootstrap_value,
                         float gamma, float lambda, lrs_f16* advantages,
+                        const int64_t* strides,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 lrs_status lrs_vtrace_f16(int64_t num_envs, int64_t seq_len,
                            const lrs_f16* log_rhos, const lrs_f16* rewards, const lrs_f16* values,
@@ -352,6 +393,7 @@ lrs_status lrs_vtrace_f16(int64_t num_envs, int64_t seq_len,
                            float gamma, float lambda,
                            float rho_bar, float c_bar, float pg_rho_bar,
                            lrs_f16* vs, lrs_f16* pg_advantages,
+                           const int64_t* strides,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 lrs_status lrs_retrace_f16(int64_t num_envs, int64_t seq_len,
                             const lrs_f16* log_rhos, const lrs_f16* rewards,
@@ -359,33 +401,39 @@ lrs_status lrs_retrace_f16(int64_t num_envs, int64_t seq_len,
                             const uint8_t* terminateds, const uint8_t* truncateds,
                             const lrs_f16* trunc_values, const lrs_f16* bootstrap_value,
                             float gamma, float lambda, float c_bar, lrs_f16* q_ret,
+                            const int64_t* strides,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 lrs_status lrs_lambda_returns_f16(int64_t num_envs, int64_t seq_len,
                                    const lrs_f16* rewards, const lrs_f16* values,
                                    const uint8_t* terminateds, const uint8_t* truncateds,
                                    const lrs_f16* trunc_values, const lrs_f16* bootstrap_value,
                                    float gamma, float lambda, lrs_f16* returns,
+                                   const int64_t* strides,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 lrs_status lrs_discounted_returns_f16(int64_t num_envs, int64_t seq_len,
                                        const lrs_f16* rewards,
                                        const uint8_t* terminateds, const uint8_t* truncateds,
                                        const lrs_f16* trunc_values, const lrs_f16* bootstrap_value,
                                        float gamma, lrs_f16* returns,
+                                       const int64_t* strides,
                                        void* workspace, size_t workspace_bytes,
                                        hipStream_t stream);
 lrs_status lrs_eligibility_traces_f16(int64_t num_envs, int64_t seq_len,
                                        const lrs_f16* x, const uint8_t* dones,
                                        float gamma, float lambda, lrs_f16* traces,
+                                       const int64_t* strides,
                                        void* workspace, size_t workspace_bytes,
                                        hipStream_t stream);
 lrs_status lrs_episodic_prefix_sum_f16(int64_t num_envs, int64_t seq_len,
                                         const lrs_f16* x, const uint8_t* dones, lrs_f16* sums,
+                                        const int64_t* strides,
                                         void* workspace, size_t workspace_bytes,
                                         hipStream_t stream);
 lrs_status lrs_affine_scan_f16(int64_t num_envs, int64_t seq_len,
                                 const lrs_f16* alpha, const lrs_f16* beta,
                                 const uint8_t* reset, const lrs_f16* carry_in, int reverse,
                                 lrs_f16* y,
+                                const int64_t* strides,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Time-major variants (_tm_): every call above, for each storage type, with
@@ -415,6 +463,7 @@ lrs_status lrs_gae_tm_f32(int64_t num_envs, int64_t seq_len,
                            const uint8_t* terminateds, const uint8_t* truncateds,
                            const float* trunc_values, const float* bootstrap_value,
                            float gamma, float lambda, float* advantages,
+                           const int64_t* strides,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 lrs_status lrs_vtrace_tm_f32(int64_t num_envs, int64_t seq_len,
                               const float* log_rhos, const float* rewards, const float* values,
@@ -423,6 +472,7 @@ lrs_status lrs_vtrace_tm_f32(int64_t num_envs, int64_t seq_len,
                               float gamma, float lambda,
                               float rho_bar, float c_bar, float pg_rho_bar,
                               float* vs, float* pg_advantages,
+                              const int64_t* strides,
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 lrs_status lrs_retrace_tm_f32(int64_t num_envs, int64_t seq_len,
                                const float* log_rhos, const float* rewards,
@@ -430,12 +480,14 @@ lrs_status lrs_retrace_tm_f32(int64_t num_envs, int64_t seq_len,
                                const uint8_t* terminateds, const uint8_t* truncateds,
                                const float* trunc_values, const float* bootstrap_value,
                                float gamma, float lambda, float c_bar, float* q_ret,
+                               const int64_t* strides,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 lrs_status lrs_lambda_returns_tm_f32(int64_t num_envs, int64_t seq_len,
                                       const float* rewards, const float* values,
                                       const uint8_t* terminateds, const uint8_t* truncateds,
                                       const float* trunc_values, const float* bootstrap_value,
                                       float gamma, float lambda, float* returns,
+                                      const int64_t* strides,
                                       void* workspace, size_t workspace_bytes,
                                       hipStream_t stream);
 lrs_status lrs_discounted_returns_tm_f32(int64_t num_envs, int64_t seq_len,
@@ -443,24 +495,29 @@ lrs_status lrs_discounted_returns_tm_f32(int64_t num_envs, int64_t seq_len,
                                           const uint8_t* terminateds, const uint8_t* truncateds,
                                           const float* trunc_values, const float* bootstrap_value,
                                           float gamma, float* returns,
+                                          const int64_t* strides,
                                           void* workspace, size_t workspace_bytes,
                                           hipStream_t stream);
 lrs_status lrs_eligibility_traces_tm_f32(int64_t num_envs, int64_t seq_len,
                                           const float* x, const uint8_t* dones,
                                           float gamma, float lambda, float* traces,
+                                          const int64_t* strides,
                                           void* workspace, size_t workspace_bytes,
                                           hipStream_t stream);
 lrs_status lrs_episodic_prefix_sum_tm_f32(int64_t num_envs, int64_t seq_len,
                                            const float* x, const uint8_t* dones, float* sums,
+                                           const int64_t* strides,
                                            void* workspace, size_t workspace_bytes,
                                            hipStream_t stream);
 lrs_status lrs_affine_scan_tm_f32(int64_t num_envs, int64_t seq_len,
                                    const float* alpha, const float* beta,
                                    const uint8_t* reset, const float* carry_in, int reverse,
                                    float* y,
+                                   const int64_t* strides,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 lrs_status lrs_episodic_prefix_sum_tm_i32(int64_t num_envs, int64_t seq_len,
                                           const int32_t* x, const uint8_t* dones, int32_t* sums,
+                                          const int64_t* strides,
                                           void* workspace, size_t workspace_bytes,
                                           hipStream_t stream);
 lrs_status lrs_gae_tm_bf16(int64_t num_envs, int64_t seq_len,
@@ -468,6 +525,7 @@ lrs_status lrs_gae_tm_bf16(int64_t num_envs, int64_t seq_len,
                            const uint8_t* terminateds, const uint8_t* truncateds,
                            const lrs_bf16* trunc_values, const lrs_bf16* bootstrap_value,
                            float gamma, float lambda, lrs_bf16* advantages,
+                           const int64_t* strides,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 lrs_status lrs_vtrace_tm_bf16(int64_t num_envs, int64_t seq_len,
                               const lrs_bf16* log_rhos, const lrs_bf16* rewards, const lrs_bf16* values,
@@ -476,6 +534,7 @@ lrs_status lrs_vtrace_tm_bf16(int64_t num_envs, int64_t seq_len,
                               float gamma, float lambda,
                               float rho_bar, float c_bar, float pg_rho_bar,
                               lrs_bf16* vs, lrs_bf16* pg_advantages,
+                              const int64_t* strides,
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 lrs_status lrs_retrace_tm_bf16(int64_t num_envs, int64_t seq_len,
                                const lrs_bf16* log_rhos, const lrs_bf16* rewards,
@@ -483,12 +542,14 @@ lrs_status lrs_retrace_tm_bf16(int64_t num_envs, int64_t seq_len,
                                const uint8_t* terminateds, const uint8_t* truncateds,
                                const lrs_bf16* trunc_values, const lrs_bf16* bootstrap_value,
                                float gamma, float lambda, float c_bar, lrs_bf16* q_ret,
+                               const int64_t* strides,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 lrs_status lrs_lambda_returns_tm_bf16(int64_t num_envs, int64_t seq_len,
                                       const lrs_bf16* rewards, const lrs_bf16* values,
                                       const uint8_t* terminateds, const uint8_t* truncateds,
                                       const lrs_bf16* trunc_values, const lrs_bf16* bootstrap_value,
                                       float gamma, float lambda, lrs_bf16* returns,
+                                      const int64_t* strides,
                                       void* workspace, size_t workspace_bytes,
                                       hipStream_t stream);
 lrs_status lrs_discounted_returns_tm_bf16(int64_t num_envs, int64_t seq_len,
@@ -496,27 +557,32 @@ lrs_status lrs_discounted_returns_tm_bf16(int64_t num_envs, int64_t seq_len,
                                           const uint8_t* terminateds, const uint8_t* truncateds,
                                           const lrs_bf16* trunc_values, const lrs_bf16* bootstrap_value,
                                           float gamma, lrs_bf16* returns,
+                                          const int64_t* strides,
                                           void* workspace, size_t workspace_bytes,
                                           hipStream_t stream);
 lrs_status lrs_eligibility_traces_tm_bf16(int64_t num_envs, int64_t seq_len,
                                           const lrs_bf16* x, const uint8_t* dones,
                                           float gamma, float lambda, lrs_bf16* traces,
+                                          const int64_t* strides,
                                           void* workspace, size_t workspace_bytes,
                                           hipStream_t stream);
 lrs_status lrs_episodic_prefix_sum_tm_bf16(int64_t num_envs, int64_t seq_len,
                                            const lrs_bf16* x, const uint8_t* dones, lrs_bf16* sums,
+                                           const int64_t* strides,
                                            void* workspace, size_t workspace_bytes,
                                            hipStream_t stream);
 lrs_status lrs_affine_scan_tm_bf16(int64_t num_envs, int64_t seq_len,
                                    const lrs_bf16* alpha, const lrs_bf16* beta,
                                    const uint8_t* reset, const lrs_bf16* carry_in, int reverse,
                                    lrs_bf16* y,
+                                   const int64_t* strides,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 lrs_status lrs_gae_tm_f16(int64_t num_envs, int64_t seq_len,
                            const lrs_f16* rewards, const lrs_f16* values,
                            const uint8_t* terminateds, const uint8_t* truncateds,
                            const lrs_f16* trunc_values, const lrs_f16* bootstrap_value,
                            float gamma, float lambda, lrs_f16* advantages,
+                           const int64_t* strides,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 lrs_status lrs_vtrace_tm_f16(int64_t num_envs, int64_t seq_len,
                               const lrs_f16* log_rhos, const lrs_f16* rewards, const lrs_f16* values,
@@ -525,6 +591,7 @@ lrs_status lrs_vtrace_tm_f16(int64_t num_envs, int64_t seq_len,
                               float gamma, float lambda,
                               float rho_bar, float c_bar, float pg_rho_bar,
                               lrs_f16* vs, lrs_f16* pg_advantages,
+                              const int64_t* strides,
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 lrs_status lrs_retrace_tm_f16(int64_t num_envs, int64_t seq_len,
                                const lrs_f16* log_rhos, const lrs_f16* rewards,
@@ -532,12 +599,14 @@ lrs_status lrs_retrace_tm_f16(int64_t num_envs, int64_t seq_len,
                                const uint8_t* terminateds, const uint8_t* truncateds,
                                const lrs_f16* trunc_values, const lrs_f16* bootstrap_value,
                                float gamma, float lambda, float c_bar, lrs_f16* q_ret,
+                               const int64_t* strides,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 lrs_status lrs_lambda_returns_tm_f16(int64_t num_envs, int64_t seq_len,
                                       const lrs_f16* rewards, const lrs_f16* values,
                                       const uint8_t* terminateds, const uint8_t* truncateds,
                                       const lrs_f16* trunc_values, const lrs_f16* bootstrap_value,
                                       float gamma, float lambda, lrs_f16* returns,
+                                      const int64_t* strides,
                                       void* workspace, size_t workspace_bytes,
                                       hipStream_t stream);
 lrs_status lrs_discounted_returns_tm_f16(int64_t num_envs, int64_t seq_len,
@@ -545,21 +614,25 @@ lrs_status lrs_discounted_returns_tm_f16(int64_t num_envs, int64_t seq_len,
                                           const uint8_t* terminateds, const uint8_t* truncateds,
                                           const lrs_f16* trunc_values, const lrs_f16* bootstrap_value,
                                           float gamma, lrs_f16* returns,
+                                          const int64_t* strides,
                                           void* workspace, size_t workspace_bytes,
                                           hipStream_t stream);
 lrs_status lrs_eligibility_traces_tm_f16(int64_t num_envs, int64_t seq_len,
                                           const lrs_f16* x, const uint8_t* dones,
                                           float gamma, float lambda, lrs_f16* traces,
+                                          const int64_t* strides,
                                           void* workspace, size_t workspace_bytes,
                                           hipStream_t stream);
 lrs_status lrs_episodic_prefix_sum_tm_f16(int64_t num_envs, int64_t seq_len,
                                            const lrs_f16* x, const uint8_t* dones, lrs_f16* sums,
+                                           const int64_t* strides,
                                            void* workspace, size_t workspace_bytes,
                                            hipStream_t stream);
 lrs_status lrs_affine_scan_tm_f16(int64_t num_envs, int64_t seq_len,
                                    const lrs_f16* alpha, const lrs_f16* beta,
                                    const uint8_t* reset, const lrs_f16* carry_in, int reverse,
                                    lrs_f16* y,
+                                   const int64_t* strides,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Diagnostics and tuning (process-wide; not for concurrent use).

@@ -10,6 +10,14 @@ kernels behind the C ABI (include/lrs.h).  torch supplies device memory and
 the current stream.  There is no CPU path: calling any compute_* function
 without the built library, or on tensors that are not on a GPU, raises.
 
+Strided views.  A per-step tensor whose last dimension has unit stride and
+whose rows do not overlap (for example buffer[:, :T] of a wider rollout
+buffer, or a column slice of a time-major buffer) is passed in place with its
+own row stride: no copy is made.  Any other layout (a transposed view, a
+stride along the last dimension other than 1) is first copied with
+.contiguous(), which costs one extra read and write of that tensor in HBM
+outside the kernel.  out= tensors must already have unit inner stride.
+
 Names and keyword arguments follow the rl-triton README (Kernels table and
 Usage section): compute_gae(rewards, values, terminateds, gamma, lambda_).
 """
@@ -29,17 +37,18 @@ _I64 = ctypes.c_int64
 _F = ctypes.c_float
 _SZ = ctypes.c_size_t
 
+# every call ends with (strides, workspace, workspace_bytes, stream)
+_TAIL = [_P, _P, _SZ, _P]
 _BASE_SIGS = {
-    "lrs_gae_f32": [_I64, _I64, _P, _P, _P, _P, _P, _P, _F, _F, _P, _P, _SZ, _P],
-    "lrs_vtrace_f32": [_I64, _I64, _P, _P, _P, _P, _P, _P, _P, _F, _F, _F, _F, _F, _P, _P, _P, _SZ,
-                       _P],
-    "lrs_retrace_f32": [_I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _F, _F, _F, _P, _P, _SZ, _P],
-    "lrs_lambda_returns_f32": [_I64, _I64, _P, _P, _P, _P, _P, _P, _F, _F, _P, _P, _SZ, _P],
-    "lrs_discounted_returns_f32": [_I64, _I64, _P, _P, _P, _P, _P, _F, _P, _P, _SZ, _P],
-    "lrs_eligibility_traces_f32": [_I64, _I64, _P, _P, _F, _F, _P, _P, _SZ, _P],
-    "lrs_episodic_prefix_sum_i32": [_I64, _I64, _P, _P, _P, _P, _SZ, _P],
-    "lrs_episodic_prefix_sum_f32": [_I64, _I64, _P, _P, _P, _P, _SZ, _P],
-    "lrs_affine_scan_f32": [_I64, _I64, _P, _P, _P, _P, ctypes.c_int, _P, _P, _SZ, _P],
+    "lrs_gae_f32": [_I64, _I64, _P, _P, _P, _P, _P, _P, _F, _F, _P] + _TAIL,
+    "lrs_vtrace_f32": [_I64, _I64, _P, _P, _P, _P, _P, _P, _P, _F, _F, _F, _F, _F, _P, _P] + _TAIL,
+    "lrs_retrace_f32": [_I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _F, _F, _F, _P] + _TAIL,
+    "lrs_lambda_returns_f32": [_I64, _I64, _P, _P, _P, _P, _P, _P, _F, _F, _P] + _TAIL,
+    "lrs_discounted_returns_f32": [_I64, _I64, _P, _P, _P, _P, _P, _F, _P] + _TAIL,
+    "lrs_eligibility_traces_f32": [_I64, _I64, _P, _P, _F, _F, _P] + _TAIL,
+    "lrs_episodic_prefix_sum_i32": [_I64, _I64, _P, _P, _P] + _TAIL,
+    "lrs_episodic_prefix_sum_f32": [_I64, _I64, _P, _P, _P] + _TAIL,
+    "lrs_affine_scan_f32": [_I64, _I64, _P, _P, _P, _P, ctypes.c_int, _P] + _TAIL,
 }
 # the 16-bit variants take the same arguments (pointers to 16-bit data), and
 # so do the time-major (_tm_) variants of every call
@@ -201,7 +210,7 @@ def workspace_state():
     return out
 
 
-def _dev_tensor(x, name, dtype, shape, device):
+def _checked(x, name, dtype, shape, device):
     if not isinstance(x, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if x.device.type != "cuda":
@@ -212,11 +221,57 @@ def _dev_tensor(x, name, dtype, shape, device):
         raise TypeError(f"{name} must be {dtype}, got {x.dtype}")
     if shape is not None and tuple(x.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(x.shape)}")
-    return x.contiguous()
+    return x
+
+
+def _dev_tensor(x, name, dtype, shape, device):
+    """A per-env tensor (contiguous, copied if it is not)."""
+    return _checked(x, name, dtype, shape, device).contiguous()
+
+
+def _row_stride(x):
+    """Row stride of a 2-D tensor the kernels can read in place (unit stride
+    along the last dimension, rows that do not overlap), else None."""
+    rows, cols = x.shape
+    if cols > 1 and x.stride(1) != 1:
+        return None
+    if rows == 1:
+        return cols
+    return x.stride(0) if x.stride(0) >= cols else None
+
+
+class _Step:
+    """A per-step [rows, cols] tensor as passed to a call: the tensor (a view
+    of the caller's memory, or a contiguous copy when its layout cannot be
+    read in place) and its row stride."""
+    __slots__ = ("t", "ld")
+
+    def __init__(self, t, ld):
+        self.t, self.ld = t, ld
+
+
+def _step(x, name, dtype, shape, device):
+    x = _checked(x, name, dtype, shape, device)
+    ld = _row_stride(x)
+    if ld is None:
+        x = x.contiguous()
+        ld = x.shape[1]
+    return _Step(x, ld)
+
+
+def _strides(*arrays):
+    """The strides argument of a call: None when every array is contiguous,
+    else a host int64 array in signature order (0 for absent arrays)."""
+    vals = [0 if a is None else a.ld for a in arrays]
+    cols = next(a.t.shape[1] for a in arrays if a is not None)
+    if all(v in (0, cols) for v in vals):
+        return None
+    return (ctypes.c_int64 * len(vals))(*vals)
 
 
 def _mask(x, name, shape, device):
-    """bool/uint8 masks pass through; other dtypes become (x != 0) first."""
+    """bool/uint8 masks pass through (strided views in place); other dtypes
+    become (x != 0) first."""
     if x is None:
         return None
     if not isinstance(x, torch.Tensor):
@@ -225,11 +280,13 @@ def _mask(x, name, shape, device):
         x = x.view(torch.uint8)
     elif x.dtype != torch.uint8:
         x = (x != 0).view(torch.uint8)
-    return _dev_tensor(x, name, torch.uint8, shape, device)
+    return _step(x, name, torch.uint8, shape, device)
 
 
 def _ptr(x):
-    return None if x is None else x.data_ptr()
+    if x is None:
+        return None
+    return x.t.data_ptr() if isinstance(x, _Step) else x.data_ptr()
 
 
 def _rows(x, name, time_major=False):
@@ -256,7 +313,7 @@ def _prep_boundary(shape, n, device, dtype, terminateds, truncateds, trunc_value
     if trunc is not None:
         if trunc_values is None:
             raise ValueError("truncateds given without trunc_values")
-        tv = _dev_tensor(trunc_values, "trunc_values", dtype, shape, device)
+        tv = _step(trunc_values, "trunc_values", dtype, shape, device)
     boot = None
     if bootstrap_value is not None:
         boot = _dev_tensor(bootstrap_value, "bootstrap_value", dtype, (n,), device)
@@ -264,12 +321,17 @@ def _prep_boundary(shape, n, device, dtype, terminateds, truncateds, trunc_value
 
 
 def _out(out, like, name):
+    """The output: a new contiguous tensor, or the caller's out= tensor in
+    place (unit stride along its last dimension, rows not overlapping)."""
     if out is None:
-        return torch.empty_like(like)
-    o = _dev_tensor(out, name, like.dtype, like.shape, like.device)
-    if o.data_ptr() != out.data_ptr():
-        raise ValueError(f"{name} must be contiguous")
-    return o
+        return _Step(torch.empty(like.t.shape, dtype=like.t.dtype, device=like.t.device),
+                     like.t.shape[1])
+    o = _checked(out, name, like.t.dtype, like.t.shape, like.t.device)
+    ld = _row_stride(o)
+    if ld is None:
+        raise ValueError(f"{name} must have unit stride along its last dimension and "
+                         "non-overlapping rows")
+    return _Step(o, ld)
 
 
 def _launch_ctx(device, est, n, t):
@@ -285,17 +347,18 @@ def compute_gae(rewards, values, terminateds, gamma=0.99, lambda_=0.95, *, trunc
     rewards (float32, bfloat16 or float16; every float input must match)."""
     n, t, shape = _rows(rewards, "rewards", time_major)
     dev, sfx, dt = rewards.device, _suffix(rewards, "rewards"), rewards.dtype
-    r = _dev_tensor(rewards, "rewards", dt, shape, None)
-    v = _dev_tensor(values, "values", dt, shape, dev)
+    r = _step(rewards, "rewards", dt, shape, None)
+    v = _step(values, "values", dt, shape, dev)
     term, trunc, tv, boot = _prep_boundary(shape, n, dev, dt, terminateds, truncateds,
                                            trunc_values, bootstrap_value)
     adv = _out(out, r, "out")
     ws, wsb, st = _launch_ctx(dev, "gae", n, t)
     fn = _entry("lrs_gae", sfx, time_major)
     _check(fn(n, t, _ptr(r), _ptr(v), _ptr(term), _ptr(trunc), _ptr(tv),
-              _ptr(boot), gamma, lambda_, _ptr(adv), _ptr(ws), wsb, st),
+              _ptr(boot), gamma, lambda_, _ptr(adv), _strides(r, v, term, trunc, tv, adv),
+              _ptr(ws), wsb, st),
            "compute_gae")
-    return adv
+    return adv.t
 
 
 def compute_vtrace(log_rhos, rewards, values, terminateds, gamma=0.99, lambda_=1.0, *,
@@ -304,9 +367,9 @@ def compute_vtrace(log_rhos, rewards, values, terminateds, gamma=0.99, lambda_=1
     """V-trace targets and policy-gradient advantages: returns (vs, pg_advantages)."""
     n, t, shape = _rows(rewards, "rewards", time_major)
     dev, sfx, dt = rewards.device, _suffix(rewards, "rewards"), rewards.dtype
-    r = _dev_tensor(rewards, "rewards", dt, shape, None)
-    lr = _dev_tensor(log_rhos, "log_rhos", dt, shape, dev)
-    v = _dev_tensor(values, "values", dt, shape, dev)
+    r = _step(rewards, "rewards", dt, shape, None)
+    lr = _step(log_rhos, "log_rhos", dt, shape, dev)
+    v = _step(values, "values", dt, shape, dev)
     term, trunc, tv, boot = _prep_boundary(shape, n, dev, dt, terminateds, truncateds,
                                            trunc_values, bootstrap_value)
     vs = _out(None if out is None else out[0], r, "out[0]")
@@ -317,21 +380,22 @@ def compute_vtrace(log_rhos, rewards, values, terminateds, gamma=0.99, lambda_=1
     fn = _entry("lrs_vtrace", sfx, time_major)
     _check(fn(n, t, _ptr(lr), _ptr(r), _ptr(v), _ptr(term), _ptr(trunc),
               _ptr(tv), _ptr(boot), gamma, lambda_, _inf(rho_bar), _inf(c_bar),
-              _inf(pg_rho_bar), _ptr(vs), _ptr(pg), _ptr(ws), wsb, st),
+              _inf(pg_rho_bar), _ptr(vs), _ptr(pg), _strides(lr, r, v, term, trunc, tv, vs, pg),
+              _ptr(ws), wsb, st),
            "compute_vtrace")
-    return vs, pg
+    return vs.t, pg.t
 
 
 def compute_retrace(log_rhos, rewards, q_values, values, terminateds, gamma=0.99, lambda_=0.95, *,
                     c_bar=1.0, truncateds=None, trunc_values=None, bootstrap_value=None, out=None,
-                time_major=False):
+                    time_major=False):
     """Retrace(lambda) targets for Q(s_t, a_t); values = E_pi Q(s_t, .)."""
     n, t, shape = _rows(rewards, "rewards", time_major)
     dev, sfx, dt = rewards.device, _suffix(rewards, "rewards"), rewards.dtype
-    r = _dev_tensor(rewards, "rewards", dt, shape, None)
-    lr = _dev_tensor(log_rhos, "log_rhos", dt, shape, dev)
-    q = _dev_tensor(q_values, "q_values", dt, shape, dev)
-    v = _dev_tensor(values, "values", dt, shape, dev)
+    r = _step(rewards, "rewards", dt, shape, None)
+    lr = _step(log_rhos, "log_rhos", dt, shape, dev)
+    q = _step(q_values, "q_values", dt, shape, dev)
+    v = _step(values, "values", dt, shape, dev)
     term, trunc, tv, boot = _prep_boundary(shape, n, dev, dt, terminateds, truncateds,
                                            trunc_values, bootstrap_value)
     g = _out(out, r, "out")
@@ -339,45 +403,47 @@ def compute_retrace(log_rhos, rewards, q_values, values, terminateds, gamma=0.99
     fn = _entry("lrs_retrace", sfx, time_major)
     _check(fn(n, t, _ptr(lr), _ptr(r), _ptr(q), _ptr(v), _ptr(term),
               _ptr(trunc), _ptr(tv), _ptr(boot), gamma, lambda_, _inf(c_bar),
-              _ptr(g), _ptr(ws), wsb, st), "compute_retrace")
-    return g
+              _ptr(g), _strides(lr, r, q, v, term, trunc, tv, g), _ptr(ws), wsb, st),
+           "compute_retrace")
+    return g.t
 
 
 def compute_lambda_returns(rewards, values, terminateds, gamma=0.99, lambda_=0.95, *,
                            truncateds=None, trunc_values=None, bootstrap_value=None, out=None,
-                time_major=False):
+                           time_major=False):
     """TD(lambda) returns."""
     n, t, shape = _rows(rewards, "rewards", time_major)
     dev, sfx, dt = rewards.device, _suffix(rewards, "rewards"), rewards.dtype
-    r = _dev_tensor(rewards, "rewards", dt, shape, None)
-    v = _dev_tensor(values, "values", dt, shape, dev)
+    r = _step(rewards, "rewards", dt, shape, None)
+    v = _step(values, "values", dt, shape, dev)
     term, trunc, tv, boot = _prep_boundary(shape, n, dev, dt, terminateds, truncateds,
                                            trunc_values, bootstrap_value)
     g = _out(out, r, "out")
     ws, wsb, st = _launch_ctx(dev, "lambda_returns", n, t)
     fn = _entry("lrs_lambda_returns", sfx, time_major)
     _check(fn(n, t, _ptr(r), _ptr(v), _ptr(term), _ptr(trunc),
-              _ptr(tv), _ptr(boot), gamma, lambda_, _ptr(g), _ptr(ws),
-              wsb, st), "compute_lambda_returns")
-    return g
+              _ptr(tv), _ptr(boot), gamma, lambda_, _ptr(g),
+              _strides(r, v, term, trunc, tv, g), _ptr(ws), wsb, st),
+           "compute_lambda_returns")
+    return g.t
 
 
 def compute_discounted_returns(rewards, terminateds, gamma=0.99, *, truncateds=None,
                                trunc_values=None, bootstrap_value=None, out=None,
-                time_major=False):
+                               time_major=False):
     """Discounted reward-to-go."""
     n, t, shape = _rows(rewards, "rewards", time_major)
     dev, sfx, dt = rewards.device, _suffix(rewards, "rewards"), rewards.dtype
-    r = _dev_tensor(rewards, "rewards", dt, shape, None)
+    r = _step(rewards, "rewards", dt, shape, None)
     term, trunc, tv, boot = _prep_boundary(shape, n, dev, dt, terminateds, truncateds,
                                            trunc_values, bootstrap_value)
     g = _out(out, r, "out")
     ws, wsb, st = _launch_ctx(dev, "discounted_returns", n, t)
     fn = _entry("lrs_discounted_returns", sfx, time_major)
     _check(fn(n, t, _ptr(r), _ptr(term), _ptr(trunc), _ptr(tv),
-              _ptr(boot), gamma, _ptr(g), _ptr(ws), wsb, st),
+              _ptr(boot), gamma, _ptr(g), _strides(r, term, trunc, tv, g), _ptr(ws), wsb, st),
            "compute_discounted_returns")
-    return g
+    return g.t
 
 
 def compute_eligibility_traces(x, dones, gamma=0.99, lambda_=0.95, *, out=None,
@@ -385,16 +451,16 @@ def compute_eligibility_traces(x, dones, gamma=0.99, lambda_=0.95, *, out=None,
     """Accumulating eligibility traces, forward in time (dtype of x)."""
     n, t, shape = _rows(x, "x", time_major)
     dev, sfx = x.device, _suffix(x, "x")
-    xs = _dev_tensor(x, "x", x.dtype, shape, None)
+    xs = _step(x, "x", x.dtype, shape, None)
     d = _mask(dones, "dones", shape, dev)
     if d is None:
         raise ValueError("dones is required")
     e = _out(out, xs, "out")
     ws, wsb, st = _launch_ctx(dev, "eligibility_traces", n, t)
     fn = _entry("lrs_eligibility_traces", sfx, time_major)
-    _check(fn(n, t, _ptr(xs), _ptr(d), gamma, lambda_, _ptr(e),
+    _check(fn(n, t, _ptr(xs), _ptr(d), gamma, lambda_, _ptr(e), _strides(xs, d, e),
               _ptr(ws), wsb, st), "compute_eligibility_traces")
-    return e
+    return e.t
 
 
 def compute_episodic_prefix_sum(x, dones, *, out=None, time_major=False):
@@ -403,19 +469,20 @@ def compute_episodic_prefix_sum(x, dones, *, out=None, time_major=False):
     n, t, shape = _rows(x, "x", time_major)
     dev = x.device
     if isinstance(x, torch.Tensor) and x.dtype == torch.int32:
-        xs = _dev_tensor(x, "x", torch.int32, shape, None)
+        xs = _step(x, "x", torch.int32, shape, None)
         fn, est = _entry("lrs_episodic_prefix_sum", "i32", time_major), "prefix_sum_i32"
     else:
         sfx = _suffix(x, "x")
-        xs = _dev_tensor(x, "x", x.dtype, shape, None)
+        xs = _step(x, "x", x.dtype, shape, None)
         fn, est = _entry("lrs_episodic_prefix_sum", sfx, time_major), "prefix_sum_f32"
     d = _mask(dones, "dones", shape, dev)
     if d is None:
         raise ValueError("dones is required")
     s = _out(out, xs, "out")
     ws, wsb, st = _launch_ctx(dev, est, n, t)
-    _check(fn(n, t, _ptr(xs), _ptr(d), _ptr(s), _ptr(ws), wsb, st), "compute_episodic_prefix_sum")
-    return s
+    _check(fn(n, t, _ptr(xs), _ptr(d), _ptr(s), _strides(xs, d, s), _ptr(ws), wsb, st),
+           "compute_episodic_prefix_sum")
+    return s.t
 
 
 def compute_affine_scan(alpha, beta, *, reset=None, carry_in=None, reverse=False, out=None,
@@ -426,16 +493,17 @@ def compute_affine_scan(alpha, beta, *, reset=None, carry_in=None, reverse=False
     in scan order (0 if None); where reset is set, y_t = alpha_t."""
     n, t, shape = _rows(alpha, "alpha", time_major)
     dev, sfx, dt = alpha.device, _suffix(alpha, "alpha"), alpha.dtype
-    a = _dev_tensor(alpha, "alpha", dt, shape, None)
-    b = _dev_tensor(beta, "beta", dt, shape, dev)
+    a = _step(alpha, "alpha", dt, shape, None)
+    b = _step(beta, "beta", dt, shape, dev)
     rs = _mask(reset, "reset", shape, dev)
     c = None if carry_in is None else _dev_tensor(carry_in, "carry_in", dt, (n,), dev)
     y = _out(out, a, "out")
     ws, wsb, st = _launch_ctx(dev, "affine_scan", n, t)
     _check(_entry("lrs_affine_scan", sfx, time_major)(n, t, _ptr(a), _ptr(b), _ptr(rs), _ptr(c),
-                                      1 if reverse else 0, _ptr(y), _ptr(ws), wsb, st),
+                                                      1 if reverse else 0, _ptr(y),
+                                                      _strides(a, b, rs, y), _ptr(ws), wsb, st),
            "compute_affine_scan")
-    return y
+    return y.t
 
 
 def _inf(x):

@@ -8,21 +8,21 @@ extern "C" {
 
 lrs_status lrs_affine_scan_f16(int64_t N, int64_t T, const lrs_f16* alpha, const lrs_f16* beta,
                                const uint8_t* reset, const lrs_f16* carry_in, int reverse,
-                               lrs_f16* out, void* ws, size_t ws_bytes, hipStream_t stream)
+                               lrs_f16* out, const int64_t* strides, void* ws, size_t ws_bytes, hipStream_t stream)
 {
     return affine_scan_entry<f16_t>("lrs_affine_scan_f16", false, N, T,
         reinterpret_cast<const f16_t*>(alpha), reinterpret_cast<const f16_t*>(beta), reset,
-        reinterpret_cast<const f16_t*>(carry_in), reverse, reinterpret_cast<f16_t*>(out), ws,
+        reinterpret_cast<const f16_t*>(carry_in), reverse, reinterpret_cast<f16_t*>(out), strides, ws,
         ws_bytes, stream);
 }
 
 lrs_status lrs_affine_scan_tm_f16(int64_t N, int64_t T, const lrs_f16* alpha, const lrs_f16* beta,
                                   const uint8_t* reset, const lrs_f16* carry_in, int reverse,
-                                  lrs_f16* out, void* ws, size_t ws_bytes, hipStream_t stream)
+                                  lrs_f16* out, const int64_t* strides, void* ws, size_t ws_bytes, hipStream_t stream)
 {
     return affine_scan_entry<f16_t>("lrs_affine_scan_tm_f16", true, N, T,
         reinterpret_cast<const f16_t*>(alpha), reinterpret_cast<const f16_t*>(beta), reset,
-        reinterpret_cast<const f16_t*>(carry_in), reverse, reinterpret_cast<f16_t*>(out), ws,
+        reinterpret_cast<const f16_t*>(carry_in), reverse, reinterpret_cast<f16_t*>(out), strides, ws,
         ws_bytes, stream);
 }
 

@@ -46,26 +46,29 @@ enum LookbackTile { kLbNarrow, kLbLight, kLbWide4 };
 // wave's last chunk.  `used` (the lane's last element is not a row end)
 // guarantees i0+E < N*T.
 template <int E, bool F, bool TM, bool NT, class D>
-__device__ __forceinline__ float next_elem(float my0, const D* __restrict__ p,
+__device__ __forceinline__ float next_elem(float my0, Strided<const D> a,
                                            const Pos<E, F, TM, NT>& P, const Ctx& c, bool used)
 {
+    const D* __restrict__ p = a.p;
     if constexpr (TM) {
         // time-major: the successor is the same row's next step, E rows on
         // (it exists whenever `used`); full lanes load unconditionally (their
         // own first element when unused)
         if constexpr (F) {
-            const float v = to_f32(p[used ? P.i0 + (uint64_t)E * P.stride : P.i0]);
+            const float v = to_f32(p[used ? elem_offset(P, E, a.gap) : elem_offset(P, 0, a.gap)]);
             return used ? v : 0.0f;
         }
-        return used ? to_f32(p[P.i0 + (uint64_t)E * P.stride]) : 0.0f;
+        return used ? to_f32(p[elem_offset(P, E, a.gap)]) : 0.0f;
     } else if constexpr (F) {
         // unused: re-read the lane's own first element (a line already
-        // fetched) rather than touch the next tile
-        const float v = to_f32(p[used ? P.i0 + E : P.i0]);
+        // fetched) rather than touch the next tile.  Full tiles of a strided
+        // array never straddle a row end, so element E is in row o0.
+        const uint64_t b = base_offset(P, a.gap);
+        const float v = to_f32(p[used ? b + E : b]);
         return used ? v : 0.0f;
     } else {
         float v = lane_prev(my0, 0.0f);
-        if (c.lane == 0) v = used ? to_f32(p[P.i0 + E]) : 0.0f;
+        if (c.lane == 0) v = used ? to_f32(p[elem_offset(P, E, a.gap)]) : 0.0f;
         return v;
     }
 }
@@ -90,11 +93,11 @@ struct Ends {
 
 template <class D>
 struct BoundaryArgs {
-    const uint8_t* term;
-    const uint8_t* trunc;   // used iff the kernel is the truncating variant
-    const D* tv;            // idem
-    const D* boot;          // never null: without bootstrap values the host
-    int has_boot;           // passes another input array and has_boot = 0
+    Strided<const uint8_t> term;
+    Strided<const uint8_t> trunc;  // used iff the kernel is the truncating variant
+    Strided<const D> tv;           // idem
+    const D* boot;                 // [N]; never null: without bootstrap values the
+    int has_boot;                  // host passes another input array and has_boot = 0
 };
 
 // trunc_values only matter where truncated: on row-major arrays a lane
@@ -105,7 +108,7 @@ struct BoundaryArgs {
 // tile.  Time-major lanes (one scalar load per step) measure faster loading
 // them unconditionally with the other streams.
 template <int E, bool F, bool TM, bool NT, class D>
-__device__ __forceinline__ void load_trunc_values(float (&tv)[E], const D* __restrict__ p, uint32_t kap,
+__device__ __forceinline__ void load_trunc_values(float (&tv)[E], Strided<const D> p, uint32_t kap,
                                                   const Pos<E, F, TM, NT>& P, bool vec)
 {
     if constexpr (TM) {
@@ -120,7 +123,8 @@ __device__ __forceinline__ void load_trunc_values(float (&tv)[E], const D* __res
     } else {
         // kap has bits only for the lane's valid elements
 #pragma unroll
-        for (int j = 0; j < E; ++j) tv[j] = ((kap >> j) & 1u) ? to_f32(p[elem_index(P, j)]) : 0.0f;
+        for (int j = 0; j < E; ++j)
+            tv[j] = ((kap >> j) & 1u) ? to_f32(p.p[elem_offset(P, j, p.gap)]) : 0.0f;
     }
 }
 
@@ -193,10 +197,10 @@ __device__ __forceinline__ void backward_pass(float (&out)[E], const float (&alp
 template <class D>
 struct GaeArgs {
     BoundaryArgs<D> b;
-    const D* rewards;
-    const D* values;
+    Strided<const D> rewards;
+    Strided<const D> values;
     float gamma, gl;  // gl = fp32(gamma*lambda)
-    D* adv;
+    Strided<D> adv;
 };
 
 template <int E, bool kTrunc, class D = float>
@@ -251,10 +255,10 @@ struct GaeOp {
 template <class D>
 struct LambdaArgs {
     BoundaryArgs<D> b;
-    const D* rewards;
-    const D* values;
+    Strided<const D> rewards;
+    Strided<const D> values;
     float gamma, gl, g1l;  // gl = fp32(gamma*lambda), g1l = fp32(gamma*(1-lambda))
-    D* out;
+    Strided<D> out;
 };
 
 template <int E, bool kTrunc, class D = float>
@@ -308,9 +312,9 @@ struct LambdaOp {
 template <class D>
 struct DiscArgs {
     BoundaryArgs<D> b;
-    const D* rewards;
+    Strided<const D> rewards;
     float gamma;
-    D* out;
+    Strided<D> out;
 };
 
 template <int E, bool kTrunc, class D = float>
@@ -362,12 +366,12 @@ struct DiscOp {
 template <class D>
 struct VtraceArgs {
     BoundaryArgs<D> b;
-    const D* log_rhos;
-    const D* rewards;
-    const D* values;
+    Strided<const D> log_rhos;
+    Strided<const D> rewards;
+    Strided<const D> values;
     float gamma, lambda, rho_bar, c_bar, pg_rho_bar;
-    D* vs;
-    D* pg;
+    Strided<D> vs;
+    Strided<D> pg;
 };
 
 template <int E, bool kTrunc, class D = float>
@@ -442,12 +446,12 @@ struct VtraceOp {
 template <class D>
 struct RetraceArgs {
     BoundaryArgs<D> b;
-    const D* log_rhos;
-    const D* rewards;
-    const D* q_values;
-    const D* values;
+    Strided<const D> log_rhos;
+    Strided<const D> rewards;
+    Strided<const D> q_values;
+    Strided<const D> values;
     float gamma, lambda, c_bar;
-    D* out;
+    Strided<D> out;
 };
 
 template <int E, bool kTrunc, class D = float>
@@ -517,40 +521,57 @@ struct RetraceOp {
 // lane comes from the neighbouring lane (lane 0 of a wave reads it, except
 // at a row start where it is not needed).
 template <int E, bool F, bool TM, bool NT>
-__device__ __forceinline__ uint32_t load_resets(const uint8_t* __restrict__ dones,
+__device__ __forceinline__ uint32_t load_resets(Strided<const uint8_t> dn,
                                                 const Pos<E, F, TM, NT>& P, const Ctx& c)
 {
-    const uint32_t d = load_mask<E>(dones, P, c.vec);
+    const uint8_t* __restrict__ dones = dn.p;
+    const uint32_t d = load_mask<E>(dn, P, c.vec);
+    // The predecessor of element 0 is in the same row whenever it is used
+    // (element 0 is not a row start): base offset - 1 (row-major) or one
+    // time step back (time-major).
     uint32_t dprev;
     if constexpr (TM) {
         // time-major: the predecessor is the same row's previous step
         const bool used = P.count > 0 && !(P.first & 1u);
+        const uint64_t own = elem_offset(P, 0, dn.gap);
         if constexpr (F) {
-            const uint32_t w = dones[used ? P.i0 - P.stride : P.i0] != 0 ? 1u : 0u;
+            const uint32_t w = dones[used ? own - P.stride - dn.gap : own] != 0 ? 1u : 0u;
             dprev = used ? w : 0u;
         } else {
-            dprev = used ? (dones[P.i0 - P.stride] != 0 ? 1u : 0u) : 0u;
+            dprev = used ? (dones[own - P.stride - dn.gap] != 0 ? 1u : 0u) : 0u;
         }
     } else if constexpr (F) {
         // every lane loads its predecessor's flag unconditionally, in flight
         // with the other loads (its own first flag where none is needed)
         const bool used = P.i0 > 0 && !(P.first & 1u);
-        const uint32_t w = dones[used ? P.i0 - 1 : P.i0] != 0 ? 1u : 0u;
+        const uint64_t b = base_offset(P, dn.gap);
+        const uint32_t w = dones[used ? b - 1 : b] != 0 ? 1u : 0u;
         dprev = used ? w : 0u;
     } else {
         dprev = lane_prev((d >> (E - 1)) & 1u, 0u);
         if (c.lane == 0 && !(P.first & 1u) && P.count > 0 && P.i0 > 0)
-            dprev = dones[P.i0 - 1] != 0 ? 1u : 0u;
+            dprev = dones[base_offset(P, dn.gap) - 1] != 0 ? 1u : 0u;
     }
     return P.first | (d << 1) | dprev;  // bit j: reset at element j
 }
 
 struct ForwardArgs {
-    const void* x;
-    const uint8_t* dones;
+    Strided<const void> x;  // D (the storage type) or int32 elements
+    Strided<const uint8_t> dones;
     float gl;  // eligibility traces: fp32(gamma*lambda)
-    void* out;
+    Strided<void> out;
 };
+
+template <class D>
+__device__ __forceinline__ Strided<const D> typed(Strided<const void> a)
+{
+    return {static_cast<const D*>(a.p), a.gap};
+}
+template <class D>
+__device__ __forceinline__ Strided<D> typed(Strided<void> a)
+{
+    return {static_cast<D*>(a.p), a.gap};
+}
 
 // README Kernels table (compute_eligibility_traces):
 // e_t = x_t + gamma*lambda*(1 - d_{t-1})*e_{t-1}.
@@ -570,7 +591,7 @@ struct EligOp {
     __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
-        load_f32<E>(alpha, (const D*)a.x, P, c.vec);
+        load_f32<E>(alpha, typed<D>(a.x), P, c.vec);
         s.reset = load_resets<E>(a.dones, P, c);
 #pragma unroll
         for (int j = 0; j < E; ++j) beta[j] = ((s.reset >> j) & 1u) ? 0.0f : a.gl;
@@ -589,7 +610,7 @@ struct EligOp {
             e = fmaf(beta[j], e, alpha[j]);
             out[j] = e;
         }
-        store_f32<E>((D*)a.out, out, P, c.vec);
+        store_f32<E>(typed<D>(a.out), out, P, c.vec);
     }
 };
 
@@ -610,7 +631,7 @@ struct PrefixF32Op {
     __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
-        load_f32<E>(alpha, (const D*)a.x, P, c.vec);
+        load_f32<E>(alpha, typed<D>(a.x), P, c.vec);
         s.reset = load_resets<E>(a.dones, P, c);
 #pragma unroll
         for (int j = 0; j < E; ++j) beta[j] = ((s.reset >> j) & 1u) ? 0.0f : 1.0f;
@@ -630,7 +651,7 @@ struct PrefixF32Op {
             out[j] = e;
         }
         (void)beta;
-        store_f32<E>((D*)a.out, out, P, c.vec);
+        store_f32<E>(typed<D>(a.out), out, P, c.vec);
     }
 };
 
@@ -650,7 +671,7 @@ struct PrefixI32Op {
     __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
                                    uint32_t (&alpha)[E], uint32_t (&beta)[E], State& s)
     {
-        load_u32<E>(alpha, (const int32_t*)a.x, P, c.vec);
+        load_u32<E>(alpha, typed<int32_t>(a.x), P, c.vec);
         s.reset = load_resets<E>(a.dones, P, c);
 #pragma unroll
         for (int j = 0; j < E; ++j) beta[j] = ((s.reset >> j) & 1u) ? 0u : 1u;
@@ -670,7 +691,7 @@ struct PrefixI32Op {
             out[j] = e;
         }
         (void)beta;
-        store_u32<E>((int32_t*)a.out, out, P, c.vec);
+        store_u32<E>(typed<int32_t>(a.out), out, P, c.vec);
     }
 };
 
@@ -682,12 +703,12 @@ struct PrefixI32Op {
 // is carry[n] (0 without carries).  A set reset[t] drops beta_t * y_prev.
 template <class D>
 struct AffineArgs {
-    const D* alpha;
-    const D* beta;
-    const uint8_t* reset;  // used iff the kernel is the resetting variant
-    const D* carry;        // never null: without carries the host passes
-    int has_carry;         // alpha and has_carry = 0
-    D* out;
+    Strided<const D> alpha;
+    Strided<const D> beta;
+    Strided<const uint8_t> reset;  // used iff the kernel is the resetting variant
+    const D* carry;                // [N]; never null: without carries the host
+    int has_carry;                 // passes another input array and has_carry = 0
+    Strided<D> out;
 };
 
 template <int E, bool kRev, bool kReset, class D = float>

@@ -7,39 +7,39 @@ using namespace lrs;
 extern "C" {
 
 lrs_status lrs_eligibility_traces_f16(int64_t N, int64_t T, const lrs_f16* x, const uint8_t* dones,
-                                      float gamma, float lambda, lrs_f16* out, void* ws,
+                                      float gamma, float lambda, lrs_f16* out, const int64_t* strides, void* ws,
                                       size_t ws_bytes, hipStream_t stream)
 {
     return eligibility_traces_entry<f16_t>("lrs_eligibility_traces_f16", false, N, T,
-        reinterpret_cast<const f16_t*>(x), dones, gamma, lambda, reinterpret_cast<f16_t*>(out), ws,
+        reinterpret_cast<const f16_t*>(x), dones, gamma, lambda, reinterpret_cast<f16_t*>(out), strides, ws,
         ws_bytes, stream);
 }
 
 lrs_status lrs_eligibility_traces_tm_f16(int64_t N, int64_t T, const lrs_f16* x,
                                          const uint8_t* dones, float gamma, float lambda,
-                                         lrs_f16* out, void* ws, size_t ws_bytes,
+                                         lrs_f16* out, const int64_t* strides, void* ws, size_t ws_bytes,
                                          hipStream_t stream)
 {
     return eligibility_traces_entry<f16_t>("lrs_eligibility_traces_tm_f16", true, N, T,
-        reinterpret_cast<const f16_t*>(x), dones, gamma, lambda, reinterpret_cast<f16_t*>(out), ws,
+        reinterpret_cast<const f16_t*>(x), dones, gamma, lambda, reinterpret_cast<f16_t*>(out), strides, ws,
         ws_bytes, stream);
 }
 
 lrs_status lrs_episodic_prefix_sum_f16(int64_t N, int64_t T, const lrs_f16* x,
-                                       const uint8_t* dones, lrs_f16* out, void* ws,
+                                       const uint8_t* dones, lrs_f16* out, const int64_t* strides, void* ws,
                                        size_t ws_bytes, hipStream_t stream)
 {
     return prefix_sum_entry<f16_t>("lrs_episodic_prefix_sum_f16", false, N, T,
-        reinterpret_cast<const f16_t*>(x), dones, reinterpret_cast<f16_t*>(out), ws, ws_bytes,
+        reinterpret_cast<const f16_t*>(x), dones, reinterpret_cast<f16_t*>(out), strides, ws, ws_bytes,
         stream);
 }
 
 lrs_status lrs_episodic_prefix_sum_tm_f16(int64_t N, int64_t T, const lrs_f16* x,
-                                          const uint8_t* dones, lrs_f16* out, void* ws,
+                                          const uint8_t* dones, lrs_f16* out, const int64_t* strides, void* ws,
                                           size_t ws_bytes, hipStream_t stream)
 {
     return prefix_sum_entry<f16_t>("lrs_episodic_prefix_sum_tm_f16", true, N, T,
-        reinterpret_cast<const f16_t*>(x), dones, reinterpret_cast<f16_t*>(out), ws, ws_bytes,
+        reinterpret_cast<const f16_t*>(x), dones, reinterpret_cast<f16_t*>(out), strides, ws, ws_bytes,
         stream);
 }
 

@@ -282,11 +282,11 @@ __global__ __launch_bounds__(W * kWave) void scan_kernel(const typename Op::Args
     const Ctx c{s.total, s.T, tid & (kWave - 1), s.vec != 0};
 
     if (s.vec && tile_start + kTile <= s.total && s.T >= (uint32_t)E) {
-        const Pos<E, true, false, NT> P{i0, n0, E, last, first};
+        const Pos<E, true, false, NT> P{i0, n0, E, last, first, 0, n0};
         tile_body<Op, E, W, A, true, NT>(args, s, tile, P, c, sh);
     } else {
         const uint32_t valid = (count >= 32) ? ~0u : ((1u << count) - 1u);
-        const Pos<E, false, false, NT> P{i0, n0, count, last & valid, first & valid};
+        const Pos<E, false, false, NT> P{i0, n0, count, last & valid, first & valid, 0, n0};
         tile_body<Op, E, W, A, false, NT>(args, s, tile, P, c, sh);
     }
 }
@@ -489,12 +489,18 @@ Plan plan_row_major(int64_t N, int64_t T, float beta_max)
     return Plan{cfg, fp64, s};
 }
 
-// Shared checks and launch.  floats/masks: every array the kernel may
-// vector-load, for the alignment decision.
+// An [N, T] array argument as the vector-access decision sees it.
+struct ArrayRef {
+    const void* p;
+    uint64_t gap;    // row stride - seq_len, in elements
+    int elem_bytes;  // 1 (masks), 2 or 4
+};
+
+// Shared checks and launch.  arrays: every [N, T] array the kernel may
+// vector-load or -store, for the alignment decision.
 template <template <int> class Op>
 lrs_status run(const char* name, int64_t N, int64_t T, float beta_max, const typename Op<4>::Args& a,
-               const void* const* floats, int nfloats, const void* const* masks, int nmasks,
-               void* ws, size_t ws_bytes, hipStream_t stream)
+               const ArrayRef* arrays, int narrays, void* ws, size_t ws_bytes, hipStream_t stream)
 {
     using Val = typename Op<4>::T;
     Plan plan = plan_row_major<Op>(N, T, beta_max);
@@ -510,11 +516,18 @@ lrs_status run(const char* name, int64_t N, int64_t T, float beta_max, const typ
                         need, ws == nullptr ? (size_t)0 : ws_bytes);
         if (!aligned(ws, 16)) return fail(LRS_ERR_WORKSPACE, "%s: workspace not 16-byte aligned", name);
     }
+    // One vector access per lane covers its E elements, at most 16 bytes: every
+    // array's base must be aligned to it, and a strided array's rows too, with
+    // no lane straddling a row end (seq_len a multiple of E), so that a lane's
+    // elements stay contiguous.
     bool vec = true;
-    // data streams: one vector access per lane covers E elements, at most 16 bytes
-    const uintptr_t data_align = (uintptr_t)(k.E * Op<4>::kElemBytes < 16 ? k.E * Op<4>::kElemBytes : 16);
-    for (int i = 0; i < nfloats; ++i) vec = vec && aligned(floats[i], data_align);
-    for (int i = 0; i < nmasks; ++i) vec = vec && aligned(masks[i], (uintptr_t)k.E);
+    for (int i = 0; i < narrays; ++i) {
+        const ArrayRef& r = arrays[i];
+        if (r.p == nullptr) continue;
+        const uint64_t align = (uint64_t)k.E * r.elem_bytes < 16 ? (uint64_t)k.E * r.elem_bytes : 16;
+        vec = vec && aligned(r.p, (uintptr_t)align);
+        if (r.gap != 0) vec = vec && s.lane_in_row && (r.gap * (uint64_t)r.elem_bytes) % align == 0;
+    }
     s.vec = vec ? 1 : 0;
     hipError_t e;
     if constexpr (std::is_same<Val, float>::value)

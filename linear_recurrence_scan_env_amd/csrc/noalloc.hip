@@ -94,13 +94,14 @@ extern "C" lrs_status lrs_gae_noalloc_f32(int64_t N, int64_t T, const float* rew
                                           const float* values, const uint8_t* term,
                                           const uint8_t* trunc, const float* tv, const float* boot,
                                           float gamma, float lambda, float* adv,
-                                          hipStream_t stream)
+                                          const int64_t* strides, hipStream_t stream)
 {
     const char* nm = "lrs_gae_noalloc_f32";
     // every argument is checked before anything (the first use's clear
     // included) is enqueued
-    LRS_TRY(gae_check<float>(nm, N, T, rewards, values, term, trunc, tv, boot, gamma, lambda, adv,
-                             nullptr, 0));
+    uint64_t gaps[6];
+    LRS_TRY(gae_check<float>(nm, Layout{false, N, T, strides}, rewards, values, term, trunc, tv,
+                             boot, gamma, lambda, adv, nullptr, 0, gaps));
     const size_t need = workspace_bytes_for((uint64_t)N * (uint64_t)T);
     if (need > kScratchBytes)
         return fail(LRS_ERR_INVALID_ARG,
@@ -113,5 +114,5 @@ extern "C" lrs_status lrs_gae_noalloc_f32(int64_t N, int64_t T, const float* rew
     void* ws = device_scratch(nm, stream, &st);
     if (ws == nullptr) return st;
     return gae_entry<float>(nm, false, N, T, rewards, values, term, trunc, tv, boot, gamma, lambda,
-                            adv, ws, kScratchBytes, stream);
+                            adv, strides, ws, kScratchBytes, stream);
 }

@@ -9,55 +9,55 @@ lrs_status lrs_vtrace_bf16(int64_t N, int64_t T, const lrs_bf16* log_rhos, const
                            const lrs_bf16* values, const uint8_t* term, const uint8_t* trunc,
                            const lrs_bf16* tv, const lrs_bf16* boot, float gamma, float lambda,
                            float rho_bar, float c_bar, float pg_rho_bar, lrs_bf16* vs,
-                           lrs_bf16* pg_adv, void* ws, size_t ws_bytes, hipStream_t stream)
+                           lrs_bf16* pg_adv, const int64_t* strides, void* ws, size_t ws_bytes, hipStream_t stream)
 {
     return vtrace_entry<bf16_t>("lrs_vtrace_bf16", false, N, T,
         reinterpret_cast<const bf16_t*>(log_rhos), reinterpret_cast<const bf16_t*>(rewards),
         reinterpret_cast<const bf16_t*>(values), term, trunc, reinterpret_cast<const bf16_t*>(tv),
         reinterpret_cast<const bf16_t*>(boot), gamma, lambda, rho_bar, c_bar, pg_rho_bar,
-        reinterpret_cast<bf16_t*>(vs), reinterpret_cast<bf16_t*>(pg_adv), ws, ws_bytes, stream);
+        reinterpret_cast<bf16_t*>(vs), reinterpret_cast<bf16_t*>(pg_adv), strides, ws, ws_bytes, stream);
 }
 
 lrs_status lrs_vtrace_tm_bf16(int64_t N, int64_t T, const lrs_bf16* log_rhos,
                               const lrs_bf16* rewards, const lrs_bf16* values, const uint8_t* term,
                               const uint8_t* trunc, const lrs_bf16* tv, const lrs_bf16* boot,
                               float gamma, float lambda, float rho_bar, float c_bar,
-                              float pg_rho_bar, lrs_bf16* vs, lrs_bf16* pg_adv, void* ws,
+                              float pg_rho_bar, lrs_bf16* vs, lrs_bf16* pg_adv, const int64_t* strides, void* ws,
                               size_t ws_bytes, hipStream_t stream)
 {
     return vtrace_entry<bf16_t>("lrs_vtrace_tm_bf16", true, N, T,
         reinterpret_cast<const bf16_t*>(log_rhos), reinterpret_cast<const bf16_t*>(rewards),
         reinterpret_cast<const bf16_t*>(values), term, trunc, reinterpret_cast<const bf16_t*>(tv),
         reinterpret_cast<const bf16_t*>(boot), gamma, lambda, rho_bar, c_bar, pg_rho_bar,
-        reinterpret_cast<bf16_t*>(vs), reinterpret_cast<bf16_t*>(pg_adv), ws, ws_bytes, stream);
+        reinterpret_cast<bf16_t*>(vs), reinterpret_cast<bf16_t*>(pg_adv), strides, ws, ws_bytes, stream);
 }
 
 lrs_status lrs_retrace_bf16(int64_t N, int64_t T, const lrs_bf16* log_rhos,
                             const lrs_bf16* rewards, const lrs_bf16* q_values,
                             const lrs_bf16* values, const uint8_t* term, const uint8_t* trunc,
                             const lrs_bf16* tv, const lrs_bf16* boot, float gamma, float lambda,
-                            float c_bar, lrs_bf16* q_ret, void* ws, size_t ws_bytes,
+                            float c_bar, lrs_bf16* q_ret, const int64_t* strides, void* ws, size_t ws_bytes,
                             hipStream_t stream)
 {
     return retrace_entry<bf16_t>("lrs_retrace_bf16", false, N, T,
         reinterpret_cast<const bf16_t*>(log_rhos), reinterpret_cast<const bf16_t*>(rewards),
         reinterpret_cast<const bf16_t*>(q_values), reinterpret_cast<const bf16_t*>(values), term,
         trunc, reinterpret_cast<const bf16_t*>(tv), reinterpret_cast<const bf16_t*>(boot), gamma,
-        lambda, c_bar, reinterpret_cast<bf16_t*>(q_ret), ws, ws_bytes, stream);
+        lambda, c_bar, reinterpret_cast<bf16_t*>(q_ret), strides, ws, ws_bytes, stream);
 }
 
 lrs_status lrs_retrace_tm_bf16(int64_t N, int64_t T, const lrs_bf16* log_rhos,
                                const lrs_bf16* rewards, const lrs_bf16* q_values,
                                const lrs_bf16* values, const uint8_t* term, const uint8_t* trunc,
                                const lrs_bf16* tv, const lrs_bf16* boot, float gamma, float lambda,
-                               float c_bar, lrs_bf16* q_ret, void* ws, size_t ws_bytes,
+                               float c_bar, lrs_bf16* q_ret, const int64_t* strides, void* ws, size_t ws_bytes,
                                hipStream_t stream)
 {
     return retrace_entry<bf16_t>("lrs_retrace_tm_bf16", true, N, T,
         reinterpret_cast<const bf16_t*>(log_rhos), reinterpret_cast<const bf16_t*>(rewards),
         reinterpret_cast<const bf16_t*>(q_values), reinterpret_cast<const bf16_t*>(values), term,
         trunc, reinterpret_cast<const bf16_t*>(tv), reinterpret_cast<const bf16_t*>(boot), gamma,
-        lambda, c_bar, reinterpret_cast<bf16_t*>(q_ret), ws, ws_bytes, stream);
+        lambda, c_bar, reinterpret_cast<bf16_t*>(q_ret), strides, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

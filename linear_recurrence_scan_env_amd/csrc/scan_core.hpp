@@ -177,16 +177,36 @@ __device__ __forceinline__ Aff<T> row_scan(Aff<T> x)
 template <int E, bool kFull, bool kTM = false, bool kNT = false>
 struct Pos {
     uint64_t i0;     // flat index of element 0
-    uint64_t n0;     // row of element 0
+    uint64_t n0;     // row (environment) of element 0
     int count;       // valid elements (E except at the end of the array)
     uint32_t last;   // bit j: element j is the last step of its row
     uint32_t first;  // bit j: element j is the first step of its row
-    // Time-major ([T, N]) lanes: element j sits at i0 + j * stride (stride =
-    // N) and all E elements are steps of row n0; every access is a scalar
-    // access, coalesced across the lanes of a wave, and unconditional when
-    // kFull (the lane's E steps all exist).
+    // Time-major ([T, N]) lanes: element j sits at flat index i0 + j * stride
+    // (stride = N) and all E elements are steps of row n0; every access is a
+    // scalar access, coalesced across the lanes of a wave, and unconditional
+    // when kFull (the lane's E steps all exist).
     uint64_t stride;
+    // Outer index of element 0: its row (row-major) or its time step
+    // (time-major).  A strided array places the element at flat index i and
+    // outer index o at p[i + o * gap] (see Strided).
+    uint64_t o0;
 };
+
+// An [N, T] array (or [T, N] for time-major calls) whose rows (time steps)
+// start ld elements apart, ld >= T (>= N): element (n, t) at n * ld + t, so at
+// flat index i = n * T + t plus n * gap, gap = ld - T.  gap = 0 for a
+// contiguous array.
+template <class D>
+struct Strided {
+    D* p;
+    uint64_t gap;
+};
+
+template <class D>
+__device__ __forceinline__ Strided<const D> as_const(Strided<D> s)
+{
+    return {s.p, s.gap};
+}
 
 template <int E, bool kFull, bool TM, bool NT>
 __device__ __forceinline__ bool vector_ok(const Pos<E, kFull, TM, NT>& P, bool vec)
@@ -194,11 +214,23 @@ __device__ __forceinline__ bool vector_ok(const Pos<E, kFull, TM, NT>& P, bool v
     return !TM && (kFull || (vec && P.count == E));
 }
 
-// Flat index of a lane's element j.
+// Offset of a lane's element j (0 <= j <= E) in an array with the given gap.
+// Row-major: element j lies in row o0 plus the number of row ends among the
+// lane's elements before it.  Time-major: element j is time step o0 + j.
 template <int E, bool kFull, bool TM, bool NT>
-__device__ __forceinline__ uint64_t elem_index(const Pos<E, kFull, TM, NT>& P, int j)
+__device__ __forceinline__ uint64_t elem_offset(const Pos<E, kFull, TM, NT>& P, int j, uint64_t gap)
 {
-    return TM ? P.i0 + (uint64_t)j * P.stride : P.i0 + (uint64_t)j;
+    if constexpr (TM) return P.i0 + (uint64_t)j * P.stride + (P.o0 + (uint64_t)j) * gap;
+    const uint32_t before = P.last & ((1u << j) - 1u);
+    return P.i0 + (uint64_t)j + (P.o0 + (uint64_t)__builtin_popcount(before)) * gap;
+}
+
+// Offset of element 0, where a lane's vector accesses start: the host allows
+// vector access to a strided array only when no lane straddles a row end.
+template <int E, bool kFull, bool TM, bool NT>
+__device__ __forceinline__ uint64_t base_offset(const Pos<E, kFull, TM, NT>& P, uint64_t gap)
+{
+    return P.i0 + P.o0 * gap;
 }
 
 // ------------------------------------------------------- element storage
@@ -288,27 +320,29 @@ __device__ __forceinline__ V ld_vec(const S* p)
 }
 
 template <int E, bool kFull, bool TM, bool NT, class D>
-__device__ __forceinline__ void load_f32(float (&v)[E], const D* __restrict__ p,
+__device__ __forceinline__ void load_f32(float (&v)[E], Strided<const D> a,
                                          const Pos<E, kFull, TM, NT>& P, bool vec)
 {
+    const D* __restrict__ p = a.p;
     if (vector_ok(P, vec)) {
+        const uint64_t b = base_offset(P, a.gap);
         if constexpr (std::is_same<D, float>::value) {
 #pragma unroll
             for (int k = 0; k < E / 4; ++k) {
-                const float4 q = ld_vec<float4, NT>(p + P.i0 + 4 * k);
+                const float4 q = ld_vec<float4, NT>(p + b + 4 * k);
                 v[4 * k + 0] = q.x;
                 v[4 * k + 1] = q.y;
                 v[4 * k + 2] = q.z;
                 v[4 * k + 3] = q.w;
             }
         } else if constexpr (E == 4) {
-            const uint2 q = ld_vec<uint2, NT>(p + P.i0);
+            const uint2 q = ld_vec<uint2, NT>(p + b);
             unpack2<D>(q.x, v[0], v[1]);
             unpack2<D>(q.y, v[2], v[3]);
         } else {
 #pragma unroll
             for (int k = 0; k < E / 8; ++k) {
-                const uint4 q = ld_vec<uint4, NT>(p + P.i0 + 8 * k);
+                const uint4 q = ld_vec<uint4, NT>(p + b + 8 * k);
                 unpack2<D>(q.x, v[8 * k + 0], v[8 * k + 1]);
                 unpack2<D>(q.y, v[8 * k + 2], v[8 * k + 3]);
                 unpack2<D>(q.z, v[8 * k + 4], v[8 * k + 5]);
@@ -317,18 +351,21 @@ __device__ __forceinline__ void load_f32(float (&v)[E], const D* __restrict__ p,
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < E; ++j) v[j] = (kFull || j < P.count) ? to_f32(p[elem_index(P, j)]) : 0.0f;
+        for (int j = 0; j < E; ++j)
+            v[j] = (kFull || j < P.count) ? to_f32(p[elem_offset(P, j, a.gap)]) : 0.0f;
     }
 }
 
 template <int E, bool kFull, bool TM, bool NT>
-__device__ __forceinline__ void load_u32(uint32_t (&v)[E], const int32_t* __restrict__ p,
+__device__ __forceinline__ void load_u32(uint32_t (&v)[E], Strided<const int32_t> a,
                                          const Pos<E, kFull, TM, NT>& P, bool vec)
 {
+    const int32_t* __restrict__ p = a.p;
     if (vector_ok(P, vec)) {
+        const uint64_t b = base_offset(P, a.gap);
 #pragma unroll
         for (int k = 0; k < E / 4; ++k) {
-            const uint4 q = ld_vec<uint4, NT>(p + P.i0 + 4 * k);
+            const uint4 q = ld_vec<uint4, NT>(p + b + 4 * k);
             v[4 * k + 0] = q.x;
             v[4 * k + 1] = q.y;
             v[4 * k + 2] = q.z;
@@ -336,7 +373,8 @@ __device__ __forceinline__ void load_u32(uint32_t (&v)[E], const int32_t* __rest
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < E; ++j) v[j] = (kFull || j < P.count) ? (uint32_t)p[elem_index(P, j)] : 0u;
+        for (int j = 0; j < E; ++j)
+            v[j] = (kFull || j < P.count) ? (uint32_t)p[elem_offset(P, j, a.gap)] : 0u;
     }
 }
 
@@ -353,24 +391,26 @@ __device__ __forceinline__ uint32_t nonzero_bytes(uint32_t w)
 
 // Bit j of the result is (mask[i0 + j] != 0); a null mask reads as all zero.
 template <int E, bool kFull, bool TM, bool NT>
-__device__ __forceinline__ uint32_t load_mask(const uint8_t* __restrict__ p, const Pos<E, kFull, TM, NT>& P,
+__device__ __forceinline__ uint32_t load_mask(Strided<const uint8_t> a, const Pos<E, kFull, TM, NT>& P,
                                               bool vec)
 {
     static_assert(E == 4 || E == 8 || E == 16, "mask loads are 4, 8 or 16 bytes");
+    const uint8_t* __restrict__ p = a.p;
     if (vector_ok(P, vec)) {
-        if (E == 4) return nonzero_bytes(ld_vec<uint32_t, NT>(p + P.i0));
+        const uint64_t b = base_offset(P, a.gap);
+        if (E == 4) return nonzero_bytes(ld_vec<uint32_t, NT>(p + b));
         if (E == 8) {
-            const uint2 w = ld_vec<uint2, NT>(p + P.i0);
+            const uint2 w = ld_vec<uint2, NT>(p + b);
             return nonzero_bytes(w.x) | (nonzero_bytes(w.y) << 4);
         }
-        const uint4 w = ld_vec<uint4, NT>(p + P.i0);
+        const uint4 w = ld_vec<uint4, NT>(p + b);
         return nonzero_bytes(w.x) | (nonzero_bytes(w.y) << 4) | (nonzero_bytes(w.z) << 8) |
                (nonzero_bytes(w.w) << 12);
     }
     uint32_t bits = 0;
 #pragma unroll
     for (int j = 0; j < E; ++j)
-        if ((kFull || j < P.count) && p[elem_index(P, j)] != 0) bits |= 1u << j;
+        if ((kFull || j < P.count) && p[elem_offset(P, j, a.gap)] != 0) bits |= 1u << j;
     return bits;
 }
 
@@ -378,46 +418,50 @@ __device__ __forceinline__ uint32_t load_mask(const uint8_t* __restrict__ p, con
 // stores are non-temporal (streamed past the caches).
 
 template <int E, bool kFull, bool TM, bool NT, class D>
-__device__ __forceinline__ void store_f32(D* __restrict__ p, const float (&v)[E],
+__device__ __forceinline__ void store_f32(Strided<D> a, const float (&v)[E],
                                           const Pos<E, kFull, TM, NT>& P, bool vec)
 {
+    D* __restrict__ p = a.p;
     if (vector_ok(P, vec)) {
+        const uint64_t b = base_offset(P, a.gap);
         if constexpr (std::is_same<D, float>::value) {
 #pragma unroll
             for (int k = 0; k < E / 4; ++k)
                 __builtin_nontemporal_store(f32x4{v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]},
-                                            reinterpret_cast<f32x4*>(p + P.i0 + 4 * k));
+                                            reinterpret_cast<f32x4*>(p + b + 4 * k));
         } else if constexpr (E == 4) {
             __builtin_nontemporal_store(u32x2{pack2<D>(v[0], v[1]), pack2<D>(v[2], v[3])},
-                                        reinterpret_cast<u32x2*>(p + P.i0));
+                                        reinterpret_cast<u32x2*>(p + b));
         } else {
 #pragma unroll
             for (int k = 0; k < E / 8; ++k)
                 __builtin_nontemporal_store(
                     u32x4{pack2<D>(v[8 * k + 0], v[8 * k + 1]), pack2<D>(v[8 * k + 2], v[8 * k + 3]),
                           pack2<D>(v[8 * k + 4], v[8 * k + 5]), pack2<D>(v[8 * k + 6], v[8 * k + 7])},
-                    reinterpret_cast<u32x4*>(p + P.i0 + 8 * k));
+                    reinterpret_cast<u32x4*>(p + b + 8 * k));
         }
     } else {
 #pragma unroll
         for (int j = 0; j < E; ++j)
-            if (kFull || j < P.count) p[elem_index(P, j)] = from_f32<D>(v[j]);
+            if (kFull || j < P.count) p[elem_offset(P, j, a.gap)] = from_f32<D>(v[j]);
     }
 }
 
 template <int E, bool kFull, bool TM, bool NT>
-__device__ __forceinline__ void store_u32(int32_t* __restrict__ p, const uint32_t (&v)[E],
+__device__ __forceinline__ void store_u32(Strided<int32_t> a, const uint32_t (&v)[E],
                                           const Pos<E, kFull, TM, NT>& P, bool vec)
 {
+    int32_t* __restrict__ p = a.p;
     if (vector_ok(P, vec)) {
+        const uint64_t b = base_offset(P, a.gap);
 #pragma unroll
         for (int k = 0; k < E / 4; ++k)
             __builtin_nontemporal_store(u32x4{v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]},
-                                        reinterpret_cast<u32x4*>(p + P.i0 + 4 * k));
+                                        reinterpret_cast<u32x4*>(p + b + 4 * k));
     } else {
 #pragma unroll
         for (int j = 0; j < E; ++j)
-            if (kFull || j < P.count) p[elem_index(P, j)] = (int32_t)v[j];
+            if (kFull || j < P.count) p[elem_offset(P, j, a.gap)] = (int32_t)v[j];
     }
 }
 

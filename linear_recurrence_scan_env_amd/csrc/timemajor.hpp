@@ -118,7 +118,7 @@ __device__ __forceinline__ void tile_body_tm(const typename Op::Args& args, cons
         if (t0 == 0) first = 1u;
     }
     const uint32_t col = active ? n : 0u;  // inactive lanes touch nothing (count = 0)
-    const Pos<E, F, true> P{(uint64_t)t0 * s.N + col, col, count, last, first, s.N};
+    const Pos<E, F, true> P{(uint64_t)t0 * s.N + col, col, count, last, first, s.N, t0};
     const Ctx c{(uint64_t)s.N * s.T, s.T, lane, false};
 
     // The launch tag is read first, in flight with the tile's loads.  These
@@ -318,7 +318,7 @@ __device__ __forceinline__ void rows_body_tm(const typename Op::Args& args, cons
         if (t0 == 0) first = 1u;
     }
     const uint32_t col = active ? n : 0u;  // inactive lanes touch nothing (count = 0)
-    const Pos<E, F, true> P{(uint64_t)t0 * s.N + col, col, count, last, first, s.N};
+    const Pos<E, F, true> P{(uint64_t)t0 * s.N + col, col, count, last, first, s.N, t0};
     const Ctx c{(uint64_t)s.N * s.T, s.T, lane, false};
 
     T alpha[E], beta[E];

@@ -91,7 +91,7 @@ OUT2 = ctypes.c_void_p(0x78000000)
 
 def gae(lib, N=4, T=8, r=FAKE, v=FAKE, term=FAKE, trunc=None, tv=None, boot=None, g=0.99, l=0.95,
         out=OUT):
-    return lib.lrs_gae_f32(N, T, r, v, term, trunc, tv, boot, g, l, out, None, 0, None)
+    return lib.lrs_gae_f32(N, T, r, v, term, trunc, tv, boot, g, l, out, None, None, 0, None)
 
 
 @pytest.mark.parametrize("kwargs", [
@@ -109,30 +109,30 @@ def test_gae_rejects(lib, kwargs):
 def test_vtrace_rejects_bad_clips(lib):
     for rb, cb, pb in [(0.0, 1.0, 1.0), (1.0, -1.0, 1.0), (1.0, 1.0, math.nan)]:
         st = lib.lrs_vtrace_f32(4, 8, FAKE, FAKE, FAKE, FAKE, None, None, None, 0.99, 0.95, rb,
-                                cb, pb, OUT, OUT2, None, 0, None)
+                                cb, pb, OUT, OUT2, None, None, 0, None)
         assert st == 1
     st = lib.lrs_vtrace_f32(4, 8, FAKE, FAKE, FAKE, FAKE, None, None, None, 0.99, 0.95, 1.0,
-                            1.0, 1.0, OUT, None, None, 0, None)
+                            1.0, 1.0, OUT, None, None, None, 0, None)
     assert st == 1  # pg_advantages is required
 
 
 def test_other_estimators_reject(lib):
     assert lib.lrs_retrace_f32(4, 8, FAKE, FAKE, None, FAKE, FAKE, None, None, None, 0.9, 0.9,
-                               1.0, OUT, None, 0, None) == 1
+                               1.0, OUT, None, None, 0, None) == 1
     assert lib.lrs_retrace_f32(4, 8, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 0.9, 0.9,
-                               0.0, OUT, None, 0, None) == 1
-    assert lib.lrs_lambda_returns_f32(4, 8, FAKE, FAKE, FAKE, None, None, None, 2.0, 0.9, OUT,
+                               0.0, OUT, None, None, 0, None) == 1
+    assert lib.lrs_lambda_returns_f32(4, 8, FAKE, FAKE, FAKE, None, None, None, 2.0, 0.9, OUT, None,
                                       None, 0, None) == 1
-    assert lib.lrs_discounted_returns_f32(4, 8, FAKE, None, None, None, None, 0.9, OUT, None, 0,
+    assert lib.lrs_discounted_returns_f32(4, 8, FAKE, None, None, None, None, 0.9, OUT, None, None, 0,
                                           None) == 1
-    assert lib.lrs_eligibility_traces_f32(4, 8, FAKE, None, 0.9, 0.9, OUT, None, 0, None) == 1
-    assert lib.lrs_episodic_prefix_sum_i32(4, 0, FAKE, FAKE, OUT, None, 0, None) == 1
-    assert lib.lrs_episodic_prefix_sum_f32(4, 8, FAKE, FAKE, None, None, 0, None) == 1
+    assert lib.lrs_eligibility_traces_f32(4, 8, FAKE, None, 0.9, 0.9, OUT, None, None, 0, None) == 1
+    assert lib.lrs_episodic_prefix_sum_i32(4, 0, FAKE, FAKE, OUT, None, None, 0, None) == 1
+    assert lib.lrs_episodic_prefix_sum_f32(4, 8, FAKE, FAKE, None, None, None, 0, None) == 1
 
 
 def test_affine_scan_rejects(lib):
     def call(N=4, T=8, a=FAKE, b=FAKE, reverse=0, y=OUT):
-        return lib.lrs_affine_scan_f32(N, T, a, b, None, None, reverse, y, None, 0, None)
+        return lib.lrs_affine_scan_f32(N, T, a, b, None, None, reverse, y, None, None, 0, None)
     for kw in [dict(N=0), dict(T=-1), dict(a=None), dict(b=None), dict(y=None), dict(reverse=2),
                dict(reverse=-1)]:
         assert call(**kw) == 1
@@ -142,23 +142,23 @@ def test_affine_scan_rejects(lib):
 def test_time_major_and_16bit_entry_points_reject(lib):
     for name in ["lrs_gae_tm_f32", "lrs_gae_bf16", "lrs_gae_tm_f16"]:
         fn = getattr(lib, name)
-        assert fn(0, 8, FAKE, FAKE, FAKE, None, None, None, 0.9, 0.9, OUT, None, 0, None) == 1
-        assert fn(4, 8, FAKE, FAKE, None, None, None, None, 0.9, 0.9, OUT, None, 0, None) == 1
+        assert fn(0, 8, FAKE, FAKE, FAKE, None, None, None, 0.9, 0.9, OUT, None, None, 0, None) == 1
+        assert fn(4, 8, FAKE, FAKE, None, None, None, None, 0.9, 0.9, OUT, None, None, 0, None) == 1
         assert lib.lrs_last_error().startswith(name.encode())
-    assert lib.lrs_episodic_prefix_sum_tm_i32(4, 8, FAKE, None, OUT, None, 0, None) == 1
-    assert lib.lrs_affine_scan_tm_bf16(4, 8, FAKE, FAKE, None, None, 3, OUT, None, 0, None) == 1
+    assert lib.lrs_episodic_prefix_sum_tm_i32(4, 8, FAKE, None, OUT, None, None, 0, None) == 1
+    assert lib.lrs_affine_scan_tm_bf16(4, 8, FAKE, FAKE, None, None, 3, OUT, None, None, 0, None) == 1
     # time-major calls with more than one tile need the workspace
-    st = lib.lrs_discounted_returns_tm_f32(4, 1000, FAKE, FAKE, None, None, None, 0.9, OUT, None,
+    st = lib.lrs_discounted_returns_tm_f32(4, 1000, FAKE, FAKE, None, None, None, 0.9, OUT, None, None,
                                            0, None)
     assert st == 2 and b"workspace" in lib.lrs_last_error()
     # a time-major launch pads environments to 64 lanes: one environment of
     # 2^31 - 1 steps would need 2^34 work items, more than a dispatch holds
     st = lib.lrs_episodic_prefix_sum_tm_i32(1, (1 << 31) - 1, ctypes.c_void_p(1 << 40), FAKE,
-                                            ctypes.c_void_p(2 << 40), ctypes.c_void_p(3 << 40),
+                                            ctypes.c_void_p(2 << 40), None, ctypes.c_void_p(3 << 40),
                                             1 << 40, None)
     assert st == 1 and b"work items" in lib.lrs_last_error()
     st = lib.lrs_episodic_prefix_sum_tm_i32(1, (1 << 29) - 256, ctypes.c_void_p(1 << 40), FAKE,
-                                            ctypes.c_void_p(2 << 40), None, 0, None)
+                                            ctypes.c_void_p(2 << 40), None, None, 0, None)
     assert st == 2  # fits the launch; only the missing workspace is reported
 
 
@@ -171,7 +171,7 @@ def test_outputs_must_not_overlap(lib):
     nb = N * T * 4
 
     def g(r=a, v=b, term=c, out=OUT, trunc=None, tv=None, boot=None, ws=None, wsb=0):
-        return lib.lrs_gae_f32(N, T, r, v, term, trunc, tv, boot, 0.9, 0.9, out, ws, wsb, None)
+        return lib.lrs_gae_f32(N, T, r, v, term, trunc, tv, boot, 0.9, 0.9, out, None, ws, wsb, None)
     # the same pointer, a partial overlap from either side, the mask and the
     # bootstrap array, the truncation values, and the workspace
     for kw in [dict(out=a), dict(out=ctypes.c_void_p(0x100000 + nb - 4)),
@@ -188,19 +188,49 @@ def test_outputs_must_not_overlap(lib):
     # workspace its 1000-step time-major tiles need (a call that passes every
     # check would be enqueued, which needs a GPU)
     st = lib.lrs_gae_tm_f32(N, 1000, a, a, c, c, a, ctypes.c_void_p(0x100000 + N * 1000 * 4),
-                            0.9, 0.9, ctypes.c_void_p(0x100000 + N * 1000 * 4 + N * 4), None, 0,
+                            0.9, 0.9, ctypes.c_void_p(0x100000 + N * 1000 * 4 + N * 4), None, None, 0,
                             None)
     assert st == 2 and b"workspace" in lib.lrs_last_error()
     assert lib.lrs_vtrace_f32(N, T, a, b, d, c, None, None, None, 0.9, 0.9, 1.0, 1.0, 1.0, OUT,
-                              OUT, None, 0, None) == 1
+                              OUT, None, None, 0, None) == 1
     assert b"overlap" in lib.lrs_last_error()
     assert lib.lrs_vtrace_f32(N, T, a, b, d, c, None, None, None, 0.9, 0.9, 1.0, 1.0, 1.0, OUT,
-                              ctypes.c_void_p(0x70000000 + nb - 4), None, 0, None) == 1
-    assert lib.lrs_episodic_prefix_sum_i32(N, T, a, b, a, None, 0, None) == 1
-    assert lib.lrs_affine_scan_f32(N, T, a, b, None, ctypes.c_void_p(0x70000000 + 4), 0, OUT,
+                              ctypes.c_void_p(0x70000000 + nb - 4), None, None, 0, None) == 1
+    assert lib.lrs_episodic_prefix_sum_i32(N, T, a, b, a, None, None, 0, None) == 1
+    assert lib.lrs_affine_scan_f32(N, T, a, b, None, ctypes.c_void_p(0x70000000 + 4), 0, OUT, None,
                                    None, 0, None) == 1
-    assert lib.lrs_eligibility_traces_tm_f32(N, T, a, b, 0.9, 0.9, b, None, 0, None) == 1
+    assert lib.lrs_eligibility_traces_tm_f32(N, T, a, b, 0.9, 0.9, b, None, None, 0, None) == 1
     assert b"overlap" in lib.lrs_last_error()
+
+
+def test_row_strides_validation(lib):
+    """strides: one per [N, T] array argument in signature order; 0 means
+    contiguous, anything else must be at least seq_len (num_envs for
+    time-major calls); the extents of strided arrays enter the overlap check."""
+    N, T = 4, 8
+    a, b, c = (ctypes.c_void_p(x) for x in (0x100000, 0x200000, 0x300000))
+
+    def st(*vals):
+        return (ctypes.c_int64 * len(vals))(*vals)
+
+    def g(strides, out=OUT, n=N, t=T, fn=None):
+        fn = fn or lib.lrs_gae_f32
+        return fn(n, t, a, b, c, None, None, None, 0.9, 0.9, out, strides, None, 0, None)
+    assert g(st(7, 0, 0, 0, 0, 0)) == 1 and b"row stride 7 of array argument 0" in lib.lrs_last_error()
+    assert g(st(0, 0, 0, 0, 0, -8)) == 1 and b"array argument 5" in lib.lrs_last_error()
+    assert g(st(0, 0, 1 << 62, 0, 0, 0)) == 1 and b"too large" in lib.lrs_last_error()
+    # a row stride of 2T puts rewards' rows over [a, a + (3 * 16 + 8) * 4): an
+    # output starting inside that extent is rejected (the check compares
+    # extents, not the interleaved elements)
+    assert g(st(2 * T, 0, 0, 0, 0, 0), out=ctypes.c_void_p(0x100000 + T * 4)) == 1
+    assert b"overlap" in lib.lrs_last_error()
+    # time-major strides are >= num_envs; strides of absent arrays
+    # (truncateds, trunc_values here) are ignored: this call fails only for
+    # want of the workspace
+    fn = lib.lrs_gae_tm_f32
+    assert g(st(N + 1, 3 * N, N, 1, 1, 0), n=N, t=1000, fn=fn) == 2
+    assert g(st(N - 1, 0, 0, 0, 0, 0), n=N, t=1000, fn=fn) == 1
+    assert b"num_envs" in lib.lrs_last_error()
 
 
 def test_time_major_waves_validation(lib):

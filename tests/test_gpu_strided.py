@@ -1,0 +1,305 @@
+"""Strided views through the C ABI: per-step inputs and outputs that are
+slices of wider buffers (buffer[:, off:off + T] of an [N, T + pad] rollout
+buffer; time-major: buffer[:, off:off + N] of a [T, N + pad] buffer), each
+array with its own row stride, read and written in place.
+
+Every element is compared with the oracle on the same values (contiguous
+copies on the host), at the parity bounds of the contiguous calls.  The
+padding around each view holds sentinels (NaN for floats, 1 for masks, a
+fixed pattern for int32): a kernel that read outside its view would pull a
+NaN or a spurious episode end into the results, and one that wrote outside
+would change the sentinels, which are checked after every call.  Row strides
+cover the vector path (a multiple of the vector width) and the scalar path
+(odd strides), rows that straddle lanes (seq_len not a multiple of the
+elements per lane) and the look-back and whole-row schedules.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+import linear_recurrence_scan_env_amd as lrs  # noqa: E402
+from linear_recurrence_scan_env_amd import api, workloads  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+ESTIMATORS = ["gae", "vtrace", "retrace", "lambda_returns", "discounted_returns",
+              "eligibility_traces", "prefix_sum_f32", "prefix_sum_i32"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lrs.load()
+    yield
+    lrs.set_schedule(False, 0, 0)
+
+
+def tol_for(T):
+    return 1e-5 if T <= 4096 else 1e-4
+
+
+class Views:
+    """Device views of host arrays inside wider sentinel-filled buffers."""
+
+    def __init__(self, time_major, dtype=torch.float32):
+        self.tm = time_major
+        self.dtype = dtype
+        self.bufs = []  # (buffer, sentinel copy, view slice)
+
+    def _sentinel(self, dt):
+        if dt == torch.uint8:
+            return 1
+        if dt == torch.int32:
+            return -123456789
+        return float("nan")
+
+    def put(self, a, pad, off):
+        """a: host [N, T] array -> device view with row stride inner + pad."""
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        if t.dtype == torch.float32:
+            t = t.to(self.dtype)
+        if self.tm:
+            t = t.t()
+        rows, cols = t.shape
+        buf = torch.full((rows, cols + pad), self._sentinel(t.dtype), dtype=t.dtype, device="cuda")
+        view = buf[:, off:off + cols]
+        view.copy_(t.cuda())
+        self.bufs.append((buf, view))
+        return view
+
+    def empty(self, like, pad, off):
+        """An output view (sentinel-filled buffer) shaped like `like`."""
+        rows, cols = like.shape
+        buf = torch.full((rows, cols + pad), self._sentinel(like.dtype), dtype=like.dtype,
+                         device="cuda")
+        view = buf[:, off:off + cols]
+        self.bufs.append((buf, view))
+        return view
+
+    def snapshot(self):
+        self.before = [b.clone() for b, _ in self.bufs]
+
+    def check_padding(self):
+        """Nothing outside the views changed."""
+        for (buf, view), old in zip(self.bufs, self.before):
+            mask = torch.ones_like(buf, dtype=torch.bool)
+            off = view.data_ptr() - buf.data_ptr()
+            off //= buf.element_size()
+            mask[:, off:off + view.shape[1]] = False
+            a, b = buf[mask], old[mask]
+            if a.dtype.is_floating_point:
+                same = (a == b) | (torch.isnan(a) & torch.isnan(b))
+            else:
+                same = a == b
+            assert bool(same.all()), "a kernel wrote outside its view"
+
+
+def host(x):
+    x = x.float() if x.dtype in (torch.bfloat16, torch.float16) else x
+    return x.cpu().numpy()
+
+
+def run_strided(est, ro, pads, time_major=False, dtype=torch.float32, trunc=True):
+    """pads: row padding (elements) of each array, cycled; offsets vary too."""
+    a = ro.arrays
+    V = Views(time_major, dtype)
+    k = [0]
+
+    def nxt():
+        p = pads[k[0] % len(pads)]
+        k[0] += 1
+        return p, (k[0] % 3) * (1 if p else 0) if p >= 2 else 0
+
+    def put(name):
+        p, o = nxt()
+        return V.put(a[name], p, min(o, p))
+
+    g, lam = ro.gamma, ro.lambda_
+    shape_dev = (ro.seq_len, ro.num_envs) if time_major else (ro.num_envs, ro.seq_len)
+    ref_host = {}
+
+    def to_dt(x):  # the oracle sees the values the device holds
+        return x if dtype == torch.float32 else host(torch.from_numpy(x).to(dtype))
+
+    def out_view(dt):
+        p, o = nxt()
+        return V.empty(torch.empty(shape_dev, dtype=dt), p, min(o, p))
+
+    fdt = dtype
+    kw = dict(time_major=time_major)
+    okw = {}
+    if est in ("gae", "vtrace", "retrace", "lambda_returns", "discounted_returns"):
+        D = {n: put(n) for n in ("rewards", "values", "q_values", "log_rhos", "terminateds")}
+        if trunc:
+            D["truncateds"] = put("truncateds")
+            D["trunc_values"] = put("trunc_values")
+            kw.update(truncateds=D["truncateds"], trunc_values=D["trunc_values"])
+            okw.update(truncateds=a["truncateds"], trunc_values=to_dt(a["trunc_values"]))
+        boot = torch.from_numpy(a["bootstrap_value"]).to(fdt).cuda()
+        kw["bootstrap_value"] = boot
+        okw["bootstrap_value"] = to_dt(a["bootstrap_value"])
+        for n in ("rewards", "values", "q_values", "log_rhos"):
+            ref_host[n] = to_dt(a[n])
+    else:
+        xn = "x_int" if est == "prefix_sum_i32" else "x"
+        D = {"x": put(xn), "dones": put("dones")}
+        ref_host["x"] = a[xn] if est == "prefix_sum_i32" else to_dt(a[xn])
+    V.snapshot()
+    out_dt = torch.int32 if est == "prefix_sum_i32" else fdt
+    o1 = out_view(out_dt)
+    V.before.append(V.bufs[-1][0].clone())
+    if est == "vtrace":
+        o2 = out_view(fdt)
+        V.before.append(V.bufs[-1][0].clone())
+    R = ref_host
+    if est == "gae":
+        got = [lrs.compute_gae(D["rewards"], D["values"], D["terminateds"], g, lam, out=o1, **kw)]
+        ref = [oracle.gae(R["rewards"], R["values"], a["terminateds"], g, lam, **okw)]
+    elif est == "vtrace":
+        got = list(lrs.compute_vtrace(D["log_rhos"], D["rewards"], D["values"], D["terminateds"],
+                                      g, lam, rho_bar=1.3, c_bar=0.9, out=(o1, o2), **kw))
+        ref = list(oracle.vtrace(R["log_rhos"], R["rewards"], R["values"], a["terminateds"], g,
+                                 lam, rho_bar=1.3, c_bar=0.9, pg_rho_bar=1.3, **okw))
+    elif est == "retrace":
+        got = [lrs.compute_retrace(D["log_rhos"], D["rewards"], D["q_values"], D["values"],
+                                   D["terminateds"], g, lam, c_bar=0.9, out=o1, **kw)]
+        ref = [oracle.retrace(R["log_rhos"], R["rewards"], R["q_values"], R["values"],
+                              a["terminateds"], g, lam, c_bar=0.9, **okw)]
+    elif est == "lambda_returns":
+        got = [lrs.compute_lambda_returns(D["rewards"], D["values"], D["terminateds"], g, lam,
+                                          out=o1, **kw)]
+        ref = [oracle.lambda_returns(R["rewards"], R["values"], a["terminateds"], g, lam, **okw)]
+    elif est == "discounted_returns":
+        got = [lrs.compute_discounted_returns(D["rewards"], D["terminateds"], g, out=o1, **kw)]
+        ref = [oracle.discounted_returns(R["rewards"], a["terminateds"], g, **okw)]
+    elif est == "eligibility_traces":
+        got = [lrs.compute_eligibility_traces(D["x"], D["dones"], g, lam, out=o1, **kw)]
+        ref = [oracle.eligibility_traces(R["x"], a["dones"], g, lam)]
+    else:
+        got = [lrs.compute_episodic_prefix_sum(D["x"], D["dones"], out=o1, **kw)]
+        ref = [oracle.prefix_sum(R["x"], a["dones"])]
+    torch.cuda.synchronize()
+    # the results are the caller's views themselves: nothing was copied
+    assert got[0].data_ptr() == o1.data_ptr()
+    V.check_padding()
+    return [(host(x).T if time_major else host(x), r) for x, r in zip(got, ref)]
+
+
+def check(pairs, T, dtype=torch.float32):
+    u = {torch.float32: 0.0, torch.bfloat16: 2.0 ** -8, torch.float16: 2.0 ** -11}[dtype]
+    for got, ref in pairs:
+        if ref.dtype == np.int32:
+            assert np.array_equal(got, ref)
+            continue
+        assert np.isfinite(got).all(), "NaN from a sentinel: a read outside the view"
+        err = np.abs(got.astype(np.float64) - ref) - u * np.abs(ref)
+        bound = 1.01 * tol_for(T) * (1.0 + np.abs(ref)) if u else tol_for(T) * (1.0 + np.abs(ref))
+        worst = (err / bound).max()
+        assert worst <= 1.0, f"error {worst:.3f} x the bound"
+
+
+def rollout(n, t, seed, p=0.01):
+    return workloads.rollout(n, t, seed=seed, term_p=p, trunc_p=p / 2, gamma=0.99, lambda_=0.95,
+                             done_p=p)
+
+
+# pads: 4 / 8 keep fp32 rows 16-byte aligned (vector path), odd pads force
+# the scalar path; 0 with an offset gives a contiguous view at a shifted base.
+PADS = {"vector": [4, 8, 12, 4], "odd": [1, 3, 5, 7], "mixed": [0, 4, 1, 8, 3]}
+
+
+@pytest.mark.parametrize("est", ESTIMATORS)
+@pytest.mark.parametrize("pads", sorted(PADS), ids=str)
+@pytest.mark.parametrize("shape", [(33, 128), (5, 3001), (7, 1000), (2, 4097), (300, 64)],
+                         ids=lambda s: f"{s[0]}x{s[1]}")
+def test_row_major_views(est, pads, shape):
+    n, t = shape
+    check(run_strided(est, rollout(n, t, seed=n * 31 + t), PADS[pads]), t)
+
+
+@pytest.mark.parametrize("est", ESTIMATORS)
+@pytest.mark.parametrize("tile", [(4, 1), (8, 4), (4, 16)], ids=lambda t: f"E{t[0]}W{t[1]}")
+def test_row_major_views_forced_lookback(est, tile):
+    """Carries across tiles with strided rows that straddle lanes (3001 is
+    not a multiple of the elements per lane)."""
+    lrs.set_schedule(True, *tile)
+    try:
+        check(run_strided(est, rollout(5, 3001, seed=77, p=0.002), PADS["mixed"]), 3001)
+        check(run_strided(est, rollout(3, 4096, seed=78, p=0.002), PADS["vector"]), 4096)
+    finally:
+        lrs.set_schedule(False, 0, 0)
+
+
+@pytest.mark.parametrize("est", ESTIMATORS)
+@pytest.mark.parametrize("pads", ["vector", "odd"])
+@pytest.mark.parametrize("shape", [(100, 1000), (4099, 33), (64, 300)],
+                         ids=lambda s: f"{s[0]}x{s[1]}")
+def test_time_major_views(est, pads, shape):
+    n, t = shape
+    check(run_strided(est, rollout(n, t, seed=n + 7 * t), PADS[pads], time_major=True), t)
+
+
+@pytest.mark.parametrize("est", ["gae", "vtrace", "eligibility_traces", "prefix_sum_f32"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=str)
+def test_16bit_views(est, dtype):
+    check(run_strided(est, rollout(9, 1000, seed=5), [8, 16, 3], dtype=dtype), 1000, dtype)
+    check(run_strided(est, rollout(64, 300, seed=6), [8, 1], dtype=dtype, time_major=True), 300,
+          dtype)
+
+
+@pytest.mark.parametrize("est", ESTIMATORS)
+def test_full_size_4096x128_views(est):
+    """The headline shape with every array a slice of a wider buffer."""
+    ro = workloads.rollout(4096, 128, seed=0, term_p=1 / 64, trunc_p=1 / 128, gamma=0.99,
+                           lambda_=0.95, done_p=1 / 64)
+    check(run_strided(est, ro, [4, 8]), 128)
+    check(run_strided(est, ro, [64, 1], time_major=True), 128)
+
+
+@pytest.mark.parametrize("est", ["gae", "vtrace", "retrace"])
+def test_full_size_64x131072_views(est):
+    """The long rows of the chunked path, strided, row-major and time-major."""
+    ro = workloads.rollout(64, 131072, seed=0, term_p=1e-4, trunc_p=1e-4, gamma=0.99,
+                           lambda_=0.95)
+    check(run_strided(est, ro, [64, 4]), 131072)
+    check(run_strided(est, ro, [8, 3], time_major=True), 131072)
+
+
+def test_affine_scan_views():
+    n, t = 6, 2500
+    arrs = workloads.affine_inputs(n, t, seed=3, reset_p=0.01, beta_range=(0.9, 1.0))
+    for tm in (False, True):
+        V = Views(tm)
+        al, be, rs = V.put(arrs["alpha"], 4, 2), V.put(arrs["beta"], 3, 1), V.put(arrs["reset"], 5, 0)
+        carry = torch.from_numpy(arrs["carry_in"]).cuda()
+        V.snapshot()
+        shape = (t, n) if tm else (n, t)
+        out = V.empty(torch.empty(shape), 7, 3)
+        V.before.append(V.bufs[-1][0].clone())
+        for rev in (False, True):
+            y = lrs.compute_affine_scan(al, be, reset=rs, carry_in=carry, reverse=rev, out=out,
+                                        time_major=tm)
+            torch.cuda.synchronize()
+            assert y.data_ptr() == out.data_ptr()
+            ref = oracle.affine_scan(arrs["alpha"], arrs["beta"], reset=arrs["reset"],
+                                     carry_in=arrs["carry_in"], reverse=rev)
+            check([(host(y).T if tm else host(y), ref)], t)
+        V.check_padding()
+
+
+def test_views_are_passed_in_place():
+    """The binding passes unit-inner-stride views with their own row stride
+    and copies only layouts the kernels cannot read in place."""
+    buf = torch.zeros(8, 40, device="cuda")
+    v = buf[:, 3:35]
+    s = api._step(v, "x", torch.float32, (8, 32), None)
+    assert s.t.data_ptr() == v.data_ptr() and s.ld == 40
+    tr = torch.zeros(32, 8, device="cuda").t()  # unit stride along rows, not along columns
+    s = api._step(tr, "x", torch.float32, (8, 32), None)
+    assert s.t.is_contiguous() and s.ld == 32 and s.t.data_ptr() != tr.data_ptr()
+    with pytest.raises(ValueError, match="unit stride"):
+        lrs.compute_discounted_returns(v, torch.zeros(8, 32, dtype=torch.bool, device="cuda"),
+                                       out=torch.empty(32, 8, device="cuda").t())

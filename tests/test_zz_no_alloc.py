@@ -30,7 +30,7 @@ def lib():
     lib = lrs.load()
     f = lib.lrs_gae_noalloc_f32
     P, I64, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
-    f.argtypes = [I64, I64, P, P, P, P, P, P, F, F, P, P]
+    f.argtypes = [I64, I64, P, P, P, P, P, P, F, F, P, P, P]
     f.restype = ctypes.c_int
     return lib
 
@@ -55,12 +55,12 @@ def both(lib, ro, trunc):
     out_w = torch.full((n, t), float("nan"), device="cuda")
     st = lib.lrs_gae_noalloc_f32(n, t, ptr(D["rewards"]), ptr(D["values"]), ptr(D["terminateds"]),
                                  ptr(tr), ptr(tv), ptr(D["bootstrap_value"]), ro.gamma, ro.lambda_,
-                                 ptr(out_s), stream)
+                                 ptr(out_s), None, stream)
     assert st == 0, lib.lrs_last_error()
     ws = torch.zeros(lib.lrs_workspace_bytes(0, n, t), dtype=torch.uint8, device="cuda")
     st = lib.lrs_gae_f32(n, t, ptr(D["rewards"]), ptr(D["values"]), ptr(D["terminateds"]), ptr(tr),
                          ptr(tv), ptr(D["bootstrap_value"]), ro.gamma, ro.lambda_, ptr(out_w),
-                         ptr(ws), ws.numel(), stream)
+                         None, ptr(ws), ws.numel(), stream)
     assert st == 0, lib.lrs_last_error()
     ref = oracle.gae(a["rewards"], a["values"], a["terminateds"], ro.gamma, ro.lambda_,
                      truncateds=a["truncateds"] if trunc else None,
@@ -115,10 +115,10 @@ def test_size_limit(lib):
     out = ctypes.c_void_p(0x70000000)
     # one element over the limit: rejected on the host, nothing enqueued
     st = lib.lrs_gae_noalloc_f32(1, MAX_ELEMS + 1, fake, fake, fake, None, None, None, 0.9, 0.9,
-                                 out, stream)
+                                 out, None, stream)
     assert st == 1 and b"scratch" in lib.lrs_last_error()
     st = lib.lrs_gae_noalloc_f32(2, MAX_ELEMS // 2 + 1, fake, fake, fake, None, None, None, 0.9,
-                                 0.9, out, stream)
+                                 0.9, out, None, stream)
     assert st == 1
     # the area still serves a call after the rejections
     ro = workloads.rollout(3, 70001, seed=15, term_p=1e-4, trunc_p=1e-4, gamma=0.99,
