@@ -7,26 +7,34 @@ fp32) and the five truncating estimators once more with truncations: 12
 library calls, each one pass over its [4096, 128] inputs.  --workload picks
 one of the other benchmark workloads (their steps are listed in WORKLOADS).
 
-Inputs sit in HBM before timing starts.  Each workload's batch is replicated
-R times (>= 1 GiB in all, four times the 256 MB Infinity Cache) and step k
-uses replica k mod R, so every call reads its inputs from HBM rather than
-from a cache ("cold"); --warm reuses one replica.  The calls are captured
-into HIP graphs (torch.cuda.CUDAGraph) of G consecutive steps each (G = 1 for
-steps of 24 or more calls, more for short steps), so the timed loop is K / G
-graph replays and host launch overhead stays off the critical path.
+Inputs sit in HBM before timing starts.  Each shape's batch is replicated R
+times and step k uses replica k mod R, so every call reads its inputs from HBM
+rather than from a cache ("cold"): R is chosen so that every single call
+cycles over at least 1 GiB of its own inputs and outputs, four times the
+256 MB Infinity Cache; --warm reuses one replica.  The calls are captured into
+HIP graphs (torch.cuda.CUDAGraph) of G consecutive steps each (G = 1 for steps
+of 24 or more calls, more for short steps), so the timed loop is K / G graph
+replays and host launch overhead stays off the critical path; it starts at the
+graph after the last one warm-up replayed.
 
 Prints one JSON line.  value = elements processed per step / step time
-(Gelem/s).  roofline: the call with the longest average duration, its
-algorithmic bytes (one read of every input stream, one write of every
-output) over its average duration, measured with HIP events around a graph
-of >= 64 back-to-back launches of that call (cycling over its replicas) on
-the launch stream; copy_same_bytes times a plain device copy of the same
-bytes the same way, for context.  cpu_baseline:
-the fp64 oracle on the host cores, whole steps on the same batch.
+(Gelem/s).  per_call: each call's average launch duration from HIP events
+around graphs of >= 64 back-to-back launches of that call (cycling over its
+replicas) on the launch stream, the inter-launch gap included.  roofline: the
+call with the longest average duration, its algorithmic bytes (one read of
+every input stream, one write of every output) over that duration; beside it
+the same fraction from the committed rocprofv3 kernel trace of this command
+(kernel time alone, no gap) while the kernel sources match; floor: an empty
+kernel and a streaming kernel that moves the call's bytes on the call's own
+grid, timed the same way; copy_same_bytes: a plain device copy of the bytes.
+With the default workload, long_path reports the chunked-path calls (GAE,
+V-trace and Retrace with truncations at 64 x 131072) the same way.
+cpu_baseline: the fp64 oracle on the host cores, whole steps on the same batch.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import math
 import os
@@ -40,41 +48,49 @@ sys.path.insert(0, ROOT)
 
 METRIC = "Gelem/s + HBM GB/s (% peak), 7 estimators, 4096 envs×T=128..131072"
 HBM_PEAK_GBPS = 8000.0
+MIN_CYCLE_BYTES = 1 << 30  # every timed call cycles over at least this much of its own data
 BACKWARD = ("gae", "vtrace", "retrace", "lambda_returns", "discounted_returns")
 ALL7 = [("gae", False), ("vtrace", False), ("retrace", False), ("lambda_returns", False),
         ("discounted_returns", False), ("eligibility_traces", False), ("prefix_sum_f32", False),
         ("gae", True), ("vtrace", True), ("retrace", True), ("lambda_returns", True),
         ("discounted_returns", True)]
+LONG3 = [(e, True, 64, 131072) for e in ("gae", "vtrace", "retrace")]
+SWEEP = [(e, False, 4096, t) for t in (32, 128, 512, 2048, 8192)
+         for e in ("discounted_returns", "lambda_returns", "eligibility_traces")]
 # workload -> the calls of one step: (estimator, with truncations, num_envs, seq_len)
 WORKLOADS = {
     "all7_4096x128": [(e, tr, 4096, 128) for e, tr in ALL7],
     "gae_64x512": [("gae", False, 64, 512)],
-    "long_64x131072": [(e, True, 64, 131072) for e in ("gae", "vtrace", "retrace")],
+    "long_64x131072": LONG3,
     # all seven estimators on the long rows (the 12 calls of all7_4096x128)
     "all7_64x131072": [(e, tr, 64, 131072) for e, tr in ALL7],
-    "sweep_4096xT": [(e, False, 4096, t) for t in (32, 128, 512, 2048, 8192)
-                     for e in ("discounted_returns", "lambda_returns", "eligibility_traces")],
+    "sweep_4096xT": SWEEP,
     "prefix_16384x1024": [("prefix_sum_i32", False, 16384, 1024),
                           ("prefix_sum_f32", False, 16384, 1024)],
     "affine_4096x8192": [("affine_fwd", False, 4096, 8192), ("affine_rev", False, 4096, 8192)],
     # the same calls with bfloat16 storage of every floating-point stream
     "all7_4096x128_bf16": [(e, tr, 4096, 128) for e, tr in ALL7],
-    "long_64x131072_bf16": [(e, True, 64, 131072) for e in ("gae", "vtrace", "retrace")],
-    "sweep_4096xT_bf16": [(e, False, 4096, t) for t in (32, 128, 512, 2048, 8192)
-                          for e in ("discounted_returns", "lambda_returns", "eligibility_traces")],
+    "long_64x131072_bf16": LONG3,
+    "sweep_4096xT_bf16": SWEEP,
     # the same calls on time-major [seq_len, num_envs] arrays
     "all7_4096x128_tm": [(e, tr, 4096, 128) for e, tr in ALL7],
-    "sweep_4096xT_tm": [(e, False, 4096, t) for t in (32, 128, 512, 2048, 8192)
-                        for e in ("discounted_returns", "lambda_returns", "eligibility_traces")],
+    "sweep_4096xT_tm": SWEEP,
+    # the same calls on views of wider buffers: every per-step array a slice
+    # [:, :T] of an [N, T + pad] buffer (its own row stride), read in place
+    "all7_4096x128_strided": [(e, tr, 4096, 128) for e, tr in ALL7],
+    "long_64x131072_strided": LONG3,
 }
 # workloads on time-major arrays
 TIME_MAJOR = {"all7_4096x128_tm", "sweep_4096xT_tm"}
 # storage type of the floating-point streams (fp32 unless listed); arithmetic is fp32 throughout
 STORAGE = {"all7_4096x128_bf16": "bf16", "long_64x131072_bf16": "bf16", "sweep_4096xT_bf16": "bf16"}
+# row padding (elements) of the strided workloads: rows stay 16-byte aligned
+STRIDE_PAD = {"all7_4096x128_strided": 4, "long_64x131072_strided": 64}
 BASE_WORKLOAD = {"all7_64x131072": "long_64x131072",
                  "all7_4096x128_bf16": "all7_4096x128", "long_64x131072_bf16": "long_64x131072",
                  "sweep_4096xT_bf16": "sweep_4096xT", "all7_4096x128_tm": "all7_4096x128",
-                 "sweep_4096xT_tm": "sweep_4096xT"}
+                 "sweep_4096xT_tm": "sweep_4096xT", "all7_4096x128_strided": "all7_4096x128",
+                 "long_64x131072_strided": "long_64x131072"}
 DEFAULT_WORKLOAD = "all7_4096x128"
 # input streams each estimator reads
 NEEDS = {
@@ -89,12 +105,17 @@ NEEDS = {
     "affine_fwd": ("alpha", "beta", "reset", "carry_in"),
     "affine_rev": ("alpha", "beta", "reset", "carry_in"),
 }
-# dense per-element streams of each call: (data streams read or written, uint8 masks read).
-# With 4-byte data: GAE and TD(lambda) 13 B/elem, V-trace and Retrace 21, the others 9,
-# the affine scan 13.
-STREAMS = {"gae": (3, 1), "vtrace": (5, 1), "retrace": (5, 1), "lambda_returns": (3, 1),
-           "discounted_returns": (2, 1), "eligibility_traces": (2, 1), "prefix_sum_f32": (2, 1),
-           "prefix_sum_i32": (2, 1), "affine_fwd": (3, 1), "affine_rev": (3, 1)}
+# dense per-element streams of each call: (data streams read, data streams
+# written, uint8 masks read).  With 4-byte data: GAE and TD(lambda) 13 B/elem,
+# V-trace and Retrace 21, the others 9, the affine scan 13.
+STREAMS = {"gae": (2, 1, 1), "vtrace": (3, 2, 1), "retrace": (4, 1, 1),
+           "lambda_returns": (2, 1, 1), "discounted_returns": (1, 1, 1),
+           "eligibility_traces": (1, 1, 1), "prefix_sum_f32": (1, 1, 1),
+           "prefix_sum_i32": (1, 1, 1), "affine_fwd": (2, 1, 1), "affine_rev": (2, 1, 1)}
+# estimator id of lrs_debug_schedule and flags
+EST_ID = {"gae": 0, "vtrace": 1, "retrace": 2, "lambda_returns": 3, "discounted_returns": 4,
+          "eligibility_traces": 5, "prefix_sum_i32": 6, "prefix_sum_f32": 7, "affine_fwd": 8,
+          "affine_rev": 8}
 
 
 def steps_per_graph(calls_per_step):
@@ -102,16 +123,26 @@ def steps_per_graph(calls_per_step):
     return max(1, -(-24 // calls_per_step))
 
 
-def replay_plan(R, G, K):
+def replay_plan(R, G, K, first_graph=0):
     """Graphs of G steps over R replicas for K timed steps: graph i holds the
     steps on replicas i*G, ..., i*G + G - 1 (mod R), R / gcd(R, G) graphs in
-    all, replayed in order; a last graph holds the K mod G remaining steps.
-    Returns (first replica of each graph, number of full replays, first
-    replica of the remainder graph or None).  Step k of the timed loop then
-    uses replica k mod R."""
+    all, replayed in order from graph `first_graph`; a last graph holds the
+    K mod G remaining steps.  Returns (first replica of each graph, number of
+    full replays, first replica of the remainder graph or None).  Step k of
+    the timed loop then uses replica (first_graph * G + k) mod R."""
     n_graphs = R // math.gcd(R, G)
     full, rest = divmod(K, G)
-    return [(i * G) % R for i in range(n_graphs)], full, ((full * G) % R if rest else None)
+    starts = [(i * G) % R for i in range(n_graphs)]
+    tail = ((first_graph + full) * G) % R if rest else None
+    return starts, full, tail
+
+
+def replicas_for(call_bytes, min_bytes=MIN_CYCLE_BYTES, multiple=1):
+    """Replicas of a shape's batch so that each call cycles over at least
+    min_bytes of its own data: the largest need among its calls, >= 2, rounded
+    up to a multiple of the steps per graph."""
+    r = max([2] + [-(-min_bytes // b) for b in call_bytes])
+    return -(-r // multiple) * multiple
 
 
 def key(est, trunc, n=None, t=None):
@@ -119,10 +150,10 @@ def key(est, trunc, n=None, t=None):
     return k if n is None else f"{k}@{n}x{t}"
 
 
-def make_batches(name):
+def make_batches(name, calls=None):
     """Seeded host inputs of a workload, one batch per (num_envs, seq_len)."""
     from linear_recurrence_scan_env_amd import workloads
-    calls = WORKLOADS[name]
+    calls = WORKLOADS[name] if calls is None else calls
     p = workloads.WORKLOADS[BASE_WORKLOAD.get(name, name)]
     batches = {}
     for n, t in sorted({(n, t) for _, _, n, t in calls}):
@@ -149,20 +180,62 @@ def trunc_counts(batches):
     return out
 
 
-def alg_bytes(est, trunc, n, t, width=4, n_trunc=None):
-    """One read of each input stream and one write of each output, with
-    `width`-byte data: STREAMS per element, plus one datum of bootstrap (or
-    carry) per env.  With truncations: one mask byte per element, and one
-    datum of trunc_values per truncation (n_trunc of them), the only ones
-    the method uses and the only ones the row-major kernels read; without a
-    count, one per element."""
-    data, masks = STREAMS[est]
-    b = (data * width + masks) * n * t
+def alg_bytes_rw(est, trunc, n, t, width=4, n_trunc=None):
+    """(bytes read, bytes written) of one call: one read of each input stream
+    and one write of each output, with `width`-byte data, plus one datum of
+    bootstrap (or carry) per env.  With truncations: one mask byte per
+    element, and one datum of trunc_values per truncation (n_trunc of them),
+    the only ones the method uses and the only ones the row-major kernels
+    read; without a count, one per element."""
+    rd, wr, masks = STREAMS[est]
+    r = (rd * width + masks) * n * t
     if trunc:
-        b += n * t + width * (n * t if n_trunc is None else n_trunc)
+        r += n * t + width * (n * t if n_trunc is None else n_trunc)
     if est in BACKWARD or est.startswith("affine"):
-        b += width * n
-    return b
+        r += width * n
+    return r, wr * width * n * t
+
+
+def alg_bytes(est, trunc, n, t, width=4, n_trunc=None):
+    return sum(alg_bytes_rw(est, trunc, n, t, width, n_trunc))
+
+
+def beta_max(est, g, lam, c_bar=1.0):
+    """The largest beta a call's maps hold, as the library derives it."""
+    if est in ("gae", "lambda_returns", "eligibility_traces"):
+        return g * lam
+    if est == "discounted_returns":
+        return g
+    if est in ("vtrace", "retrace"):
+        return g * lam * c_bar
+    if est.startswith("prefix"):
+        return 1.0
+    return float("inf")
+
+
+class SchedInfo(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int64), ("num_tiles", ctypes.c_int64),
+                ("tile_elems", ctypes.c_int64), ("tile_steps", ctypes.c_int64),
+                ("groups", ctypes.c_int64), ("envs_per_group", ctypes.c_int64),
+                ("time_major", ctypes.c_int32), ("carries", ctypes.c_int32),
+                ("backward", ctypes.c_int32), ("tiles_per_row", ctypes.c_int32),
+                ("elems_per_lane", ctypes.c_int32), ("waves_per_block", ctypes.c_int32),
+                ("composition_fp64", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+def launch_grid(lib, est, trunc, n, t, g, lam, tm=False, half=False):
+    """(blocks, threads per block) of a call, from the library's own plan."""
+    flags = (1 if trunc else 0) | (2 if est == "affine_rev" else 0) | (4 if tm else 0) | \
+        (8 if half else 0)
+    info = SchedInfo()
+    fn = lib.lrs_debug_schedule
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+                   ctypes.POINTER(SchedInfo), ctypes.c_void_p, ctypes.c_int64]
+    st = fn(EST_ID[est], flags, n, t, beta_max(est, g, lam), ctypes.byref(info), None, 0)
+    if st != 0:
+        raise RuntimeError(lib.lrs_last_error().decode())
+    return int(info.num_blocks), int(info.waves_per_block) * 64
 
 
 def make_call(lrs, est, trunc, D, O, g, lam, tm=False):
@@ -258,12 +331,15 @@ def cpu_baseline(name, batches, seconds):
                       f"fp64 sequential recursion, OpenMP over envs"}
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_all7_4096x128.md")
+# ------------------------------------------------------------ profiles
+
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_PROFILE = os.path.join(PROFILES, "hbm_traffic_all7_4096x128.md")
 CALIBRATION_BYTES = 64 << 20  # one --calibrate-copy dispatch reads and writes this much
 
 
 def source_hash():
-    """sha256 of the kernel sources (csrc/): counters taken on other sources are stale."""
+    """sha256 of the kernel sources (csrc/): figures taken on other sources are stale."""
     import hashlib
     h = hashlib.sha256()
     pkg = os.path.join(ROOT, "linear_recurrence_scan_env_amd", "csrc")
@@ -277,6 +353,10 @@ def source_hash():
 def call_of_kernel(name):
     """Map a demangled kernel name (scan_kernel<Op<E, ...>, E, W, Acc>) to a bench call key."""
     import re
+    if "floor_empty" in name:
+        return "floor:empty"
+    if "floor_stream" in name:
+        return "floor:stream"
     ops = {"GaeOp": "gae", "VtraceOp": "vtrace", "RetraceOp": "retrace",
            "LambdaOp": "lambda_returns", "DiscOp": "discounted_returns",
            "EligOp": "eligibility_traces", "PrefixF32Op": "prefix_sum_f32",
@@ -293,17 +373,70 @@ def call_of_kernel(name):
     return None
 
 
-def summarize_stats(csv_path, command, title="seven estimators at 4096 x 128"):
+def profile_path(workload):
+    return os.path.join(PROFILES, f"kernel_stats_{workload}.md")
+
+
+def summarize_trace(trace_csv, command, workload, title):
+    """Markdown summary of a rocprofv3 kernel trace of `bench.py --workload
+    workload`: per-kernel statistics, then each call's average duration
+    (dispatches matched to calls by kernel and grid), and a machine-readable
+    block that bench.py reads while the kernel sources are unchanged."""
     import csv
-    rows = list(csv.DictReader(open(csv_path)))
+    import collections
+    import linear_recurrence_scan_env_amd as lrs
+    lib = lrs.load()
+    calls = list(WORKLOADS[workload]) + (LONG3 if workload == DEFAULT_WORKLOAD else [])
+    p = make_batches(workload).popitem()[1]
+    tm, half = workload in TIME_MAJOR, workload in STORAGE
+    grids = {}
+    for e, tr, n, t in calls:
+        b, th = launch_grid(lib, e, tr, n, t, p.gamma, p.lambda_, tm, half)
+        grids.setdefault((key(e, tr), b * th), key(e, tr, n, t))
+    per_kernel = collections.defaultdict(list)
+    per_call = collections.defaultdict(list)
+    for r in csv.DictReader(open(trace_csv)):
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        name = r["Kernel_Name"]
+        per_kernel[name].append(us)
+        c = call_of_kernel(name)
+        grid = int(r.get("Grid_Size_X") or r.get("Grid_Size") or 0)
+        if c and c.startswith("floor:"):
+            per_call[c].append(us)
+        elif c and (c, grid) in grids:
+            per_call[grids[(c, grid)]].append(us)
     out = [f"# rocprofv3 kernel statistics: {title}", "",
            "Command:", "", "```", command, "```", "",
            "| kernel | call | dispatches | avg us | min us | max us |", "|---|---|---|---|---|---|"]
-    for r in rows:
-        out.append(f"| `{r['Name'].split('(')[0]}` | {call_of_kernel(r['Name']) or '-'} | "
-                   f"{r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
-                   f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} |")
+    for name, v in sorted(per_kernel.items(), key=lambda kv: -sum(kv[1])):
+        out.append(f"| `{name.split('(')[0]}` | {call_of_kernel(name) or '-'} | {len(v)} | "
+                   f"{sum(v) / len(v):.3f} | {min(v):.3f} | {max(v):.3f} |")
+    out += ["", "Average duration per call (dispatches matched by kernel and grid size):", "",
+            "| call | dispatches | avg us |", "|---|---|---|"]
+    avg = {}
+    for c in sorted(per_call):
+        v = per_call[c]
+        avg[c] = round(sum(v) / len(v), 3)
+        out.append(f"| {c} | {len(v)} | {avg[c]:.3f} |")
+    out += ["", "Machine-readable (read by bench.py; valid only for these kernel sources):", "",
+            f"source_sha256: {source_hash()}", "kernel_avg_us: " + json.dumps(avg, sort_keys=True)]
     print("\n".join(out))
+
+
+def committed_profile(workload):
+    """Per-call average kernel durations (us) from the committed rocprofv3
+    summary of this workload, or None when missing or taken on other sources."""
+    try:
+        text = open(profile_path(workload)).read()
+    except OSError:
+        return None
+    sha = avg = None
+    for line in text.splitlines():
+        if line.startswith("source_sha256:"):
+            sha = line.split(":", 1)[1].strip()
+        if line.startswith("kernel_avg_us:"):
+            avg = json.loads(line.split(":", 1)[1])
+    return avg if sha == source_hash() and avg else None
 
 
 def summarize_counters(fetch_csv, write_csv, command_fetch, command_write):
@@ -318,7 +451,7 @@ def summarize_counters(fetch_csv, write_csv, command_fetch, command_write):
         for r in csv.DictReader(open(path)):
             v = float(r["Counter_Value"]) * 1024.0
             k = call_of_kernel(r["Kernel_Name"])
-            if k:
+            if k and not k.startswith("floor:"):
                 per[k].append(v)
             elif "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) == CALIBRATION_BYTES // 512:
                 calib.append(v)
@@ -370,6 +503,32 @@ def committed_traffic(call):
     return traffic.get(call)
 
 
+# ------------------------------------------------------------ timing
+
+def time_graph(gr, stream, reps, launches):
+    """Average time per launch of a graph of `launches` launches, from HIP
+    events around `reps` replays on `stream` (after one untimed replay)."""
+    import torch
+    gr.replay()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(reps):
+        gr.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) * 1e3 / (reps * launches)
+
+
+def capture(fns, stream):
+    import torch
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr, stream=stream):
+        for f in fns:
+            f()
+    return gr
+
+
 def copy_reference(alg_bytes, stream, reps):
     """A plain device copy moving the dominant call's algorithmic bytes (half
     read, half written), timed like the calls: cold buffers (>= 1 GiB of
@@ -378,7 +537,7 @@ def copy_reference(alg_bytes, stream, reps):
     context beside the roofline fraction."""
     import torch
     half = max(4, alg_bytes // 2) // 4  # fp32 elements per side
-    pairs = max(8, -(-(1 << 30) // (8 * half)))
+    pairs = max(8, -(-MIN_CYCLE_BYTES // (8 * half)))
     bufs = [(torch.empty(half, device=stream.device), torch.empty(half, device=stream.device))
             for _ in range(pairs)]
     launches = max(64, pairs)
@@ -386,31 +545,147 @@ def copy_reference(alg_bytes, stream, reps):
         for src, dst in bufs[:2]:
             dst.copy_(src)
         stream.synchronize()
-        gr = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gr, stream=stream):
-            for i in range(launches):
-                src, dst = bufs[i % pairs]
-                dst.copy_(src)
-        gr.replay()
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
-        ev0.record(stream)
-        for _ in range(reps):
-            gr.replay()
-        ev1.record(stream)
-        torch.cuda.synchronize()
-    us = ev0.elapsed_time(ev1) * 1e3 / (reps * launches)
+        gr = capture([(lambda s=src, d=dst: d.copy_(s)) for src, dst in
+                      (bufs[i % pairs] for i in range(launches))], stream)
+        us = time_graph(gr, stream, reps, launches)
     del bufs
     return {"us": round(us, 3), "GBps": round(8 * half / us / 1e3, 1)}
 
 
-def run_eager(args, steps_fns, stream):
+def floor_reference(lib, grid, rw_bytes, stream, reps):
+    """The dominant call's grid with no work (an empty kernel) and with only
+    its bytes (lrs_debug_floor's streaming kernel reading and writing the
+    call's byte counts, cold buffers cycled over >= 1 GiB), each in a graph of
+    >= 64 back-to-back launches timed like the calls.  call - empty is the
+    call's own time beyond a launch of its grid; stream - empty is what the
+    bytes alone cost on that grid."""
+    import torch
+    blocks, threads = grid
+    rd = -(-rw_bytes[0] // 16) * 16
+    wr = -(-rw_bytes[1] // 16) * 16
+    fn = lib.lrs_debug_floor
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+                   ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    pairs = max(8, -(-MIN_CYCLE_BYTES // (rd + wr)))
+    bufs = [(torch.empty(rd, dtype=torch.uint8, device=stream.device),
+             torch.empty(wr, dtype=torch.uint8, device=stream.device)) for _ in range(pairs)]
+    launches = max(64, pairs)
+    sid = stream.cuda_stream
+
+    def empty():
+        if fn(0, blocks, threads, None, 0, None, 0, sid) != 0:
+            raise RuntimeError(lib.lrs_last_error().decode())
+
+    def streamer(s, d):
+        def f():
+            if fn(1, blocks, threads, s.data_ptr(), rd, d.data_ptr(), wr, sid) != 0:
+                raise RuntimeError(lib.lrs_last_error().decode())
+        return f
+
+    with torch.cuda.stream(stream):
+        empty()
+        streamer(*bufs[0])()
+        stream.synchronize()
+        ge = capture([empty] * 64, stream)
+        gs = capture([streamer(*bufs[i % pairs]) for i in range(launches)], stream)
+        e_us = time_graph(ge, stream, reps, 64)
+        s_us = time_graph(gs, stream, reps, launches)
+    del bufs
+    return {"grid": [blocks, threads], "empty_us": round(e_us, 3), "stream_us": round(s_us, 3),
+            "stream_bytes": rd + wr, "stream_GBps": round((rd + wr) / s_us / 1e3, 1)}
+
+
+class Store:
+    """Device replicas of a workload's batches and its calls' outputs."""
+
+    def __init__(self, lrs, name, calls, batches, dev, storage, tm, pad, nrep_fn):
+        import torch
+        self.calls, self.tm = calls, tm
+        width = 2 if storage in ("bf16", "f16") else 4
+        store_dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[storage]
+        shapes = sorted({(n, t) for _, _, n, t in calls})
+        hosts = {s_: {k: torch.from_numpy(v) for k, v in b.arrays.items() if v is not None}
+                 for s_, b in batches.items() if s_ in shapes}
+        for h in hosts.values():
+            for k, v in list(h.items()):
+                if v.dtype == torch.float32 and storage != "f32":
+                    v = v.to(store_dt)
+                if tm and v.dim() == 2:  # per-step arrays as [seq_len, num_envs]
+                    v = v.t().contiguous()
+                h[k] = v
+        self.nrep = {}
+        self.data = {}  # (shape, replica) -> (inputs, outputs)
+
+        def place(v0):
+            """A copy of device tensor v0; per-step arrays as views of
+            [rows, cols + pad] buffers when pad > 0."""
+            if pad and v0.dim() == 2:
+                rows, cols = v0.shape
+                buf = torch.empty((rows, cols + pad), dtype=v0.dtype, device=dev)
+                view = buf[:, :cols]
+                view.copy_(v0)
+                return view
+            return v0.clone()
+
+        for s_ in shapes:
+            ntr = int(np.count_nonzero(batches[s_].arrays.get("truncateds"))) \
+                if batches[s_].arrays.get("truncateds") is not None else 0
+            cb = [alg_bytes(e, tr, n, t, width, ntr) for e, tr, n, t in calls if (n, t) == s_]
+            R = nrep_fn(cb)
+            self.nrep[s_] = R
+            first = {k: v.to(dev) for k, v in hosts[s_].items()}
+            for i in range(R):
+                D = {k: place(v) for k, v in first.items()}
+                O = {}
+                for e, tr, n, t in calls:
+                    if (n, t) != s_:
+                        continue
+                    dt = torch.int32 if e == "prefix_sum_i32" else store_dt
+                    oshape = (t, n) if tm else (n, t)
+                    k = key(e, tr)
+                    O[k] = place(torch.empty(oshape, device=dev, dtype=dt))
+                    if e == "vtrace":
+                        O[k + "/pg"] = place(torch.empty(oshape, device=dev, dtype=dt))
+                D["_O"] = O
+                self.data[(s_, i)] = D
+            del first
+        self.lrs = lrs
+        self.g, self.lam = batches[shapes[0]].gamma, batches[shapes[0]].lambda_
+
+    def fn(self, e, tr, n, t, i):
+        D = self.data[((n, t), i % self.nrep[(n, t)])]
+        return make_call(self.lrs, e, tr, D, D["_O"], self.g, self.lam, self.tm)
+
+    def step_fns(self, i):
+        return [self.fn(e, tr, n, t, i) for e, tr, n, t in self.calls]
+
+
+def time_per_call(st, stream, reps, width, n_trunc, shapes_in_key):
+    """Each call's average launch duration: a graph of max(64, R) launches
+    cycling over the call's R replicas (>= 1 GiB of its own data)."""
+    per_call = {}
+    for e, tr, n, t in st.calls:
+        R = st.nrep[(n, t)]
+        launches = max(64, R)
+        gr = capture([st.fn(e, tr, n, t, i) for i in range(launches)], stream)
+        us = time_graph(gr, stream, reps, launches)
+        del gr
+        b = alg_bytes(e, tr, n, t, width, n_trunc[(n, t)])
+        per_call[key(e, tr, n, t) if shapes_in_key else key(e, tr)] = {
+            "us": round(us, 3), "alg_bytes": b, "GBps": round(b / us / 1e3, 1),
+            "frac": round(b / us / 1e3 / HBM_PEAK_GBPS, 4), "Gelem/s": round(n * t / us / 1e3, 2),
+            "cycle_bytes": b * R}
+    return per_call
+
+
+def run_eager(args, st, stream):
     """Counter-collection mode: the same calls, launched one by one."""
     import torch
-    R = len(steps_fns)
+    R = max(st.nrep.values())
     with torch.cuda.stream(stream):
         for k in range(args.warmup + args.steps):
-            for f in steps_fns[k % R]:
+            for f in st.step_fns(k % R):
                 f()
         torch.cuda.synchronize()
     print(json.dumps({"mode": "eager", "steps": args.steps, "warmup": args.warmup,
@@ -423,10 +698,13 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--replicas", type=int, default=0, help="0: enough for >= 1 GiB")
+    ap.add_argument("--replicas", type=int, default=0,
+                    help="0: enough for >= 1 GiB of every call's own data")
     ap.add_argument("--warm", action="store_true", help="one replica: cache-resident inputs")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-long-path", action="store_true",
+                    help="default workload: skip the 64 x 131072 chunked-path calls")
     ap.add_argument("--roofline-reps", type=int, default=20)
     ap.add_argument("--eager", action="store_true",
                     help="launch calls one by one instead of replaying HIP graphs "
@@ -434,15 +712,17 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run 5 device copies of a 64 MiB tensor: a kernel of known "
                          "HBM traffic for scaling FETCH_SIZE / WRITE_SIZE counters")
-    ap.add_argument("--summarize-stats", nargs="+", metavar="CSV COMMAND [TITLE]",
-                    help="print a markdown summary of a rocprofv3 kernel_stats.csv")
+    ap.add_argument("--summarize-trace", nargs=4,
+                    metavar=("TRACE_CSV", "COMMAND", "WORKLOAD", "TITLE"),
+                    help="print the markdown summary of a rocprofv3 kernel_trace.csv of a run "
+                         "of WORKLOAD")
     ap.add_argument("--summarize-counters", nargs=4,
                     metavar=("FETCH_CSV", "WRITE_CSV", "FETCH_COMMAND", "WRITE_COMMAND"),
                     help="print the HBM-traffic summary of two rocprofv3 --pmc runs")
     args = ap.parse_args()
 
-    if args.summarize_stats:
-        return summarize_stats(*args.summarize_stats)
+    if args.summarize_trace:
+        return summarize_trace(*args.summarize_trace)
     if args.summarize_counters:
         return summarize_counters(*args.summarize_counters)
 
@@ -454,75 +734,32 @@ def main():
 
     import torch
     import linear_recurrence_scan_env_amd as lrs
-    from linear_recurrence_scan_env_amd import workloads
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    lrs.load()
+    lib = lrs.load()
 
     name = args.workload
     calls = WORKLOADS[name]
-    p = workloads.WORKLOADS[BASE_WORKLOAD.get(name, name)]
     storage = STORAGE.get(name, "f32")
     width = 2 if storage in ("bf16", "f16") else 4
-    store_dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[storage]
+    tm = name in TIME_MAJOR
+    pad = STRIDE_PAD.get(name, 0)
     shapes = sorted({(n, t) for _, _, n, t in calls})
     batches = make_batches(name)
     n_trunc = trunc_counts(batches)
-    ro0 = batches[shapes[0]]
-    g, lam = ro0.gamma, ro0.lambda_
+    G = steps_per_graph(len(calls))
 
-    hosts = {s_: {k: torch.from_numpy(v) for k, v in b.arrays.items() if v is not None}
-             for s_, b in batches.items()}
-    if storage != "f32":
-        for h in hosts.values():
-            for k, v in h.items():
-                if v.dtype == torch.float32:
-                    h[k] = v.to(store_dt)
-    tm = name in TIME_MAJOR
-    if tm:  # per-step arrays as [seq_len, num_envs]
-        for h in hosts.values():
-            for k, v in h.items():
-                if v.dim() == 2:
-                    h[k] = v.t().contiguous()
+    def nrep_fn(call_bytes):
+        if args.warm:
+            return 1
+        if args.replicas:
+            return args.replicas
+        return replicas_for(call_bytes, MIN_CYCLE_BYTES, G)
 
-    # Replicas per shape: enough copies of that shape's inputs and outputs
-    # for >= 1 GiB, so that each call reads cold data however small it is.
-    def shape_bytes(s_):
-        b = sum(v.numel() * v.element_size() for v in hosts[s_].values())
-        return b + sum((2 if e == "vtrace" else 1) * n * t * width for e, _, n, t in calls
-                       if (n, t) == s_)
-
-    if args.warm:
-        nrep = {s_: 1 for s_ in shapes}
-    elif args.replicas:
-        nrep = {s_: args.replicas for s_ in shapes}
-    else:
-        nrep = {s_: max(2, -(-(1 << 30) // shape_bytes(s_))) for s_ in shapes}
-    R = max(nrep.values())
-    store = {}  # (shape, replica) -> (inputs, outputs)
-    for s_ in shapes:
-        for i in range(nrep[s_]):
-            D = {k: v.to(dev) for k, v in hosts[s_].items()}
-            O = {}
-            for e, tr, n, t in calls:
-                if (n, t) != s_:
-                    continue
-                dt = torch.int32 if e == "prefix_sum_i32" else store_dt
-                oshape = (t, n) if tm else (n, t)
-                O[key(e, tr)] = torch.empty(oshape, device=dev, dtype=dt)
-                if e == "vtrace":
-                    O[key(e, tr) + "/pg"] = torch.empty(oshape, device=dev, dtype=dt)
-            store[(s_, i)] = (D, O)
-
-    def fn(e, tr, n, t, i):
-        D, O = store[((n, t), i % nrep[(n, t)])]
-        return make_call(lrs, e, tr, D, O, g, lam, tm)
-
-    def step_fns(i):
-        return [fn(e, tr, n, t, i) for e, tr, n, t in calls]
-
+    st = Store(lrs, name, calls, batches, dev, storage, tm, pad, nrep_fn)
+    R = max(st.nrep.values())
     stream = torch.cuda.Stream(dev)
     if args.calibrate_copy:
         src = torch.ones(CALIBRATION_BYTES // 4, device=dev)
@@ -533,87 +770,82 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     if args.eager:
-        return run_eager(args, [step_fns(i) for i in range(R)], stream)
+        return run_eager(args, st, stream)
 
     with torch.cuda.stream(stream):
         # Eager warm-up on the capture stream (allocates its workspace outside capture).
         for i in range(min(R, 2)):
-            for f in step_fns(i):
+            for f in st.step_fns(i):
                 f()
         stream.synchronize()
-
-        def capture(fns):
-            gr = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gr, stream=stream):
-                for f in fns:
-                    f()
-            return gr
 
         # Several consecutive steps per graph when a step has few calls (at least 24
         # calls per graph), so that host-side replay cost never paces the GPU.  Graph
         # i holds the steps on replicas i*G, i*G+1, ... (mod R): replaying the graphs
         # in order walks the replicas in order, so no call reuses recent inputs.
-        G = steps_per_graph(len(calls))
+        warm_graphs = -(-args.warmup // G)
         starts, full, tail_start = replay_plan(R, G, args.steps)
         n_graphs = len(starts)
+        first_graph = warm_graphs % n_graphs
+        _, full, tail_start = replay_plan(R, G, args.steps, first_graph)
 
         def steps_graph(first, count):
             fns = []
             for k in range(first, first + count):
-                fns += step_fns(k % R)
-            return capture(fns)
+                fns += st.step_fns(k % R)
+            return capture(fns, stream)
 
         step_graphs = [steps_graph(first, G) for first in starts]
         tail_graph = steps_graph(tail_start, args.steps % G) if tail_start is not None else None
-        call_keys = [key(e, tr, n, t) for e, tr, n, t in calls]
-        # per call: a graph of >= 64 launches cycling over that call's replicas
-        launches = {k_: max(64, nrep[(n, t)]) for k_, (e, tr, n, t) in zip(call_keys, calls)}
-        call_graphs = {k_: capture([fn(e, tr, n, t, i) for i in range(launches[k_])])
-                       for k_, (e, tr, n, t) in zip(call_keys, calls)}
         torch.cuda.synchronize()
 
-        # ---- timed steps: exactly args.steps steps (full graphs, then the rest)
-        for k in range(-(-args.warmup // G)):
+        # ---- timed steps: exactly args.steps steps (full graphs, then the rest),
+        # starting at the graph after the last one the warm-up replayed
+        for k in range(warm_graphs):
             step_graphs[k % n_graphs].replay()
         torch.cuda.synchronize()
         t_start = torch.cuda.Event(enable_timing=True)
         t_end = torch.cuda.Event(enable_timing=True)
         t_start.record(stream)
         for k in range(full):
-            step_graphs[k % n_graphs].replay()
+            step_graphs[(first_graph + k) % n_graphs].replay()
         if tail_graph is not None:
             tail_graph.replay()
         t_end.record(stream)
         torch.cuda.synchronize()
         ms_per_step = t_start.elapsed_time(t_end) / args.steps
+        del step_graphs, tail_graph
 
-        # ---- per-call average launch duration (graph of R launches, events around it)
-        per_call = {}
-        for (e, tr, n, t), k_ in zip(calls, call_keys):
-            call_graphs[k_].replay()
-            ev0 = torch.cuda.Event(enable_timing=True)
-            ev1 = torch.cuda.Event(enable_timing=True)
-            ev0.record(stream)
-            for _ in range(args.roofline_reps):
-                call_graphs[k_].replay()
-            ev1.record(stream)
-            torch.cuda.synchronize()
-            us = ev0.elapsed_time(ev1) * 1e3 / (args.roofline_reps * launches[k_])
-            b = alg_bytes(e, tr, n, t, width, n_trunc[(n, t)])
-            per_call[k_ if len(shapes) > 1 else key(e, tr)] = {
-                "us": round(us, 3), "alg_bytes": b, "GBps": round(b / us / 1e3, 1),
-                "Gelem/s": round(n * t / us / 1e3, 2)}
+        # ---- per-call average launch duration
+        per_call = time_per_call(st, stream, args.roofline_reps, width, n_trunc, len(shapes) > 1)
 
     elems_per_step = sum(n * t for _, _, n, t in calls)
     value = elems_per_step / (ms_per_step * 1e-3) / 1e9
     dom = max(per_call, key=lambda k_: per_call[k_]["us"])
+    dom_call = next(c for c in calls if key(c[0], c[1], c[2], c[3]) == dom or
+                    key(c[0], c[1]) == dom)
+    e_d, tr_d, n_d, t_d = dom_call
     achieved = per_call[dom]["GBps"]
+    rw = alg_bytes_rw(e_d, tr_d, n_d, t_d, width, n_trunc[(n_d, t_d)])
+    grid = launch_grid(lib, e_d, tr_d, n_d, t_d, st.g, st.lam, tm, width == 2)
+    floor = floor_reference(lib, grid, rw, stream, args.roofline_reps)
+    floor["call_minus_empty_us"] = round(per_call[dom]["us"] - floor["empty_us"], 3)
+    floor["stream_minus_empty_us"] = round(floor["stream_us"] - floor["empty_us"], 3)
     copy_ref = copy_reference(per_call[dom]["alg_bytes"], stream, args.roofline_reps)
+    prof = committed_profile(name)
+    dom_full = key(e_d, tr_d, n_d, t_d)
+    rocprof = None
+    if prof and dom_full in prof:
+        us = prof[dom_full]
+        rocprof = {"us": us, "frac": round(per_call[dom]["alg_bytes"] / us / 1e3 / HBM_PEAK_GBPS, 4),
+                   "profile": os.path.relpath(profile_path(name), ROOT),
+                   "source": "rocprofv3 kernel trace of this command: kernel time alone"}
     cfg = {"workload": name, "calls_per_step": len(calls),
            "cache": "warm" if args.warm else "cold",
-           "replicas": {f"{n}x{t}": nrep[(n, t)] for n, t in shapes},
+           "replicas": {f"{n}x{t}": st.nrep[(n, t)] for n, t in shapes},
            "launch": f"hip graphs of {G} step(s)", "storage": storage,
-           "layout": "time-major [seq_len, num_envs]" if tm else "row-major [num_envs, seq_len]"}
+           "layout": ("time-major [seq_len, num_envs]" if tm else "row-major [num_envs, seq_len]") +
+                     (f", views of [rows, cols + {pad}] buffers" if pad else "")}
     if len(shapes) == 1:
         cfg.update(num_envs=shapes[0][0], seq_len=shapes[0][1])
     else:
@@ -634,14 +866,43 @@ def main():
         "config": cfg,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": committed_traffic(dom) if name == DEFAULT_WORKLOAD else None,
+                     "traffic": committed_traffic(key(e_d, tr_d)) if name == DEFAULT_WORKLOAD
+                     else None,
                      "alg_bytes": per_call[dom]["alg_bytes"],
-                     "copy_same_bytes": copy_ref},
+                     "duration_source": "HIP events around graphs of back-to-back launches of "
+                                        "the call on its stream (inter-launch gap included)",
+                     "rocprof": rocprof, "floor": floor, "copy_same_bytes": copy_ref},
         "per_call": per_call,
     }
+    if name == DEFAULT_WORKLOAD and not args.no_long_path:
+        out["long_path"] = long_path(lrs, lib, dev, stream, args)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(name, batches, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def long_path(lrs, lib, dev, stream, args):
+    """The chunked path's calls (GAE, V-trace and Retrace with truncations at
+    64 x 131072: multi-block carries along 131072-step rows), each timed like
+    the per-call figures above, with the rocprof kernel time of the committed
+    default-workload profile beside it."""
+    import torch
+    batches = make_batches("long_64x131072")
+    st = Store(lrs, "long_64x131072", LONG3, batches, dev, "f32", False, 0,
+               lambda cb: replicas_for(cb, MIN_CYCLE_BYTES, 1))
+    with torch.cuda.stream(stream):
+        for f in st.step_fns(0):
+            f()
+        stream.synchronize()
+        per = time_per_call(st, stream, max(4, args.roofline_reps // 4), 4,
+                            trunc_counts(batches), True)
+    prof = committed_profile(DEFAULT_WORKLOAD) or {}
+    for k, v in per.items():
+        if k in prof:
+            v["rocprof_us"] = prof[k]
+            v["rocprof_frac"] = round(v["alg_bytes"] / prof[k] / 1e3 / HBM_PEAK_GBPS, 4)
+    del st
+    return per
 
 
 if __name__ == "__main__":

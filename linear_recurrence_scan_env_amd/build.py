@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 # One translation unit per group of entry points, compiled in parallel.
-SOURCES = [os.path.join(CSRC, "abi.hip"), os.path.join(CSRC, "noalloc.hip")] + [
+SOURCES = [os.path.join(CSRC, f) for f in ("abi.hip", "noalloc.hip", "floor.hip")] + [
     os.path.join(CSRC, f"{group}{sfx}.hip")
     for group in ("returns", "offpolicy", "forward", "affine") for sfx in ("", "_bf16", "_f16")]
 HEADERS = [os.path.join(CSRC, f)

@@ -20,7 +20,11 @@ lrs_status run_layout(bool tm, const char* nm, int64_t N, int64_t T, float beta_
                       const typename Op<4>::Args& a, const ArrayRef* arrays, int narrays, void* ws,
                       size_t ws_bytes, hipStream_t stream)
 {
-    if (tm) return run_tm<Op>(nm, N, T, beta_max, a, ws, ws_bytes, stream);
+    if (tm) {
+        bool strided = false;
+        for (int i = 0; i < narrays; ++i) strided = strided || (arrays[i].p && arrays[i].gap != 0);
+        return run_tm<Op>(nm, N, T, beta_max, a, strided, ws, ws_bytes, stream);
+    }
     return run<Op>(nm, N, T, beta_max, a, arrays, narrays, ws, ws_bytes, stream);
 }
 
@@ -358,11 +362,14 @@ lrs_status prefix_sum_entry(const char* nm, bool tm, int64_t N, int64_t T, const
                                                       stream);
 }
 
-inline lrs_status prefix_sum_i32_entry(const char* nm, bool tm, int64_t N, int64_t T,
-                                       const int32_t* x, const uint8_t* dones, int32_t* out,
-                                       const int64_t* strides, void* ws, size_t ws_bytes,
-                                       hipStream_t stream)
+// A template only so that the kernels it launches are compiled in the one
+// translation unit that calls it (I = int32_t).
+template <class I>
+lrs_status prefix_sum_int_entry(const char* nm, bool tm, int64_t N, int64_t T, const I* x,
+                                const uint8_t* dones, I* out, const int64_t* strides, void* ws,
+                                size_t ws_bytes, hipStream_t stream)
 {
+    static_assert(std::is_same<I, int32_t>::value, "int32 sums only");
     LRS_TRY(check_common(nm, N, T));
     LRS_REQUIRE(x && dones && out, "%s: x, dones and sums are required", nm);
     ForwardArgs a{};

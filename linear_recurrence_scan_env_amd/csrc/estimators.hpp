@@ -31,6 +31,16 @@ struct Ctx {
     bool vec;        // base pointers allow vector access
 };
 
+// e^x on the hardware base-2 exponential (v_exp_f32, correct to about one
+// unit in the last place): e^x = 2^(x * log2(e)).  Rounding x * log2(e) to
+// fp32 adds a relative error of about |x| * 2^-24 to the result, so for
+// log-ratios of moderate size the result stays within a few units in the last
+// place, far inside the parity bound of the estimators that take it.
+__device__ __forceinline__ float exp_e(float x)
+{
+    return __builtin_amdgcn_exp2f(x * 1.44269504088896341f);
+}
+
 // Tile shape of an op's look-back launches on fp32 data (measured on long
 // rows): four elements per lane in 2048-element tiles for ops with many
 // input streams; eight per lane for ops with few; four per lane in
@@ -40,14 +50,16 @@ enum LookbackTile { kLbNarrow, kLbLight, kLbWide4 };
 // Value of stream p at flat index i0+E (element 0 of the next chunk).  Full
 // tiles load it in every lane (same cache line as the neighbouring chunk's
 // vector load), unconditionally, so it is in flight with the lane's other
-// loads; it is discarded where unused.  The guarded path takes it from the
-// lane holding the next chunk (backward estimators hold chunks in reversed
-// lane order: lane L-1) and reads memory only in lane 0, which holds the
-// wave's last chunk.  `used` (the lane's last element is not a row end)
-// guarantees i0+E < N*T.
-template <int E, bool F, bool TM, bool NT, class D>
+// loads; it is discarded where unused.  (Taking it from the neighbouring lane
+// instead, with a DPP shift after the vector load, measured 3-12% slower at
+// 4096 x 128: the wave then waits for that load before issuing the rest.)
+// The guarded path takes it from the lane holding the next chunk (backward
+// estimators hold chunks in reversed lane order: lane L-1) and reads memory
+// only in lane 0, which holds the wave's last chunk.  `used` (the lane's last
+// element is not a row end) guarantees i0+E < N*T.
+template <int E, bool F, bool TM, bool NT, bool S, class D>
 __device__ __forceinline__ float next_elem(float my0, Strided<const D> a,
-                                           const Pos<E, F, TM, NT>& P, const Ctx& c, bool used)
+                                           const Pos<E, F, TM, NT, S>& P, const Ctx& c, bool used)
 {
     const D* __restrict__ p = a.p;
     if constexpr (TM) {
@@ -75,8 +87,8 @@ __device__ __forceinline__ float next_elem(float my0, Strided<const D> a,
 
 // The successor of the lane's last element is read only when that element
 // is not the last of its row.
-template <int E, bool F, bool TM, bool NT>
-__device__ __forceinline__ bool successor_used(const Pos<E, F, TM, NT>& P)
+template <int E, bool F, bool TM, bool NT, bool S>
+__device__ __forceinline__ bool successor_used(const Pos<E, F, TM, NT, S>& P)
 {
     return P.count == E && !((P.last >> (E - 1)) & 1u);
 }
@@ -106,10 +118,12 @@ struct BoundaryArgs {
 // stream then costs HBM traffic around truncations only.  The load depends
 // on the truncation mask, so callers issue it after every other load of the
 // tile.  Time-major lanes (one scalar load per step) measure faster loading
-// them unconditionally with the other streams.
-template <int E, bool F, bool TM, bool NT, class D>
+// them unconditionally with the other streams.  On row-major calls of
+// 4096 x 128, where most waves hold a truncation and so wait for the mask, a
+// dense load issued with the others measured no faster (-1.5% to +1.3%).
+template <int E, bool F, bool TM, bool NT, bool S, class D>
 __device__ __forceinline__ void load_trunc_values(float (&tv)[E], Strided<const D> p, uint32_t kap,
-                                                  const Pos<E, F, TM, NT>& P, bool vec)
+                                                  const Pos<E, F, TM, NT, S>& P, bool vec)
 {
     if constexpr (TM) {
         load_f32<E>(tv, p, P, vec);
@@ -128,8 +142,8 @@ __device__ __forceinline__ void load_trunc_values(float (&tv)[E], Strided<const 
     }
 }
 
-template <int E, bool F, bool TM, bool NT, bool kTrunc, class D>
-__device__ __forceinline__ Ends<E> load_ends(const BoundaryArgs<D>& b, const Pos<E, F, TM, NT>& P,
+template <int E, bool F, bool TM, bool NT, bool S, bool kTrunc, class D>
+__device__ __forceinline__ Ends<E> load_ends(const BoundaryArgs<D>& b, const Pos<E, F, TM, NT, S>& P,
                                              const Ctx& c)
 {
     const uint32_t tau = load_mask<E>(b.term, P, c.vec);
@@ -167,8 +181,8 @@ __device__ __forceinline__ Ends<E> load_ends(const BoundaryArgs<D>& b, const Pos
 }
 
 // Elements past the end of the array are identities.
-template <int E, bool F, bool TM, bool NT, class T>
-__device__ __forceinline__ void clear_tail(T (&alpha)[E], T (&beta)[E], const Pos<E, F, TM, NT>& P)
+template <int E, bool F, bool TM, bool NT, bool S, class T>
+__device__ __forceinline__ void clear_tail(T (&alpha)[E], T (&beta)[E], const Pos<E, F, TM, NT, S>& P)
 {
     if (F) return;
 #pragma unroll
@@ -216,15 +230,15 @@ struct GaeOp {
         uint32_t end;
     };
 
-    template <bool F, bool TM, bool NT>
-    __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT, bool S>
+    __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT, S>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
         float r[E], v[E];
         load_f32<E>(r, a.rewards, P, c.vec);
         load_f32<E>(v, a.values, P, c.vec);
         const float vnx = next_elem<E>(v[0], a.values, P, c, successor_used(P));
-        const Ends<E> e = load_ends<E, F, TM, NT, kTrunc>(a.b, P, c);
+        const Ends<E> e = load_ends<E, F, TM, NT, S, kTrunc>(a.b, P, c);
 #pragma unroll
         for (int j = 0; j < E; ++j) {
             const bool end = (e.end >> j) & 1u;
@@ -237,8 +251,8 @@ struct GaeOp {
         s.end = e.end;
     }
     __device__ static bool far_open(const State& s) { return !((s.end >> (E - 1)) & 1u); }
-    template <bool F, bool TM, bool NT>
-    __device__ static void finish(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT, bool S>
+    __device__ static void finish(const Args& a, const Pos<E, F, TM, NT, S>& P, const Ctx& c,
                                   const float (&alpha)[E], const float (&beta)[E], const State&,
                                   float carry)
     {
@@ -275,15 +289,15 @@ struct LambdaOp {
         uint32_t end;
     };
 
-    template <bool F, bool TM, bool NT>
-    __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT, bool S>
+    __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT, S>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
         float r[E], v[E];
         load_f32<E>(r, a.rewards, P, c.vec);
         load_f32<E>(v, a.values, P, c.vec);
         const float vnx = next_elem<E>(v[0], a.values, P, c, successor_used(P));
-        const Ends<E> e = load_ends<E, F, TM, NT, kTrunc>(a.b, P, c);
+        const Ends<E> e = load_ends<E, F, TM, NT, S, kTrunc>(a.b, P, c);
 #pragma unroll
         for (int j = 0; j < E; ++j) {
             const bool end = (e.end >> j) & 1u;
@@ -295,8 +309,8 @@ struct LambdaOp {
         s.end = e.end;
     }
     __device__ static bool far_open(const State& s) { return !((s.end >> (E - 1)) & 1u); }
-    template <bool F, bool TM, bool NT>
-    __device__ static void finish(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT, bool S>
+    __device__ static void finish(const Args& a, const Pos<E, F, TM, NT, S>& P, const Ctx& c,
                                   const float (&alpha)[E], const float (&beta)[E], const State&,
                                   float carry)
     {
@@ -330,13 +344,13 @@ struct DiscOp {
         uint32_t end;
     };
 
-    template <bool F, bool TM, bool NT>
-    __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT, bool S>
+    __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT, S>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
         float r[E];
         load_f32<E>(r, a.rewards, P, c.vec);
-        const Ends<E> e = load_ends<E, F, TM, NT, kTrunc>(a.b, P, c);
+        const Ends<E> e = load_ends<E, F, TM, NT, S, kTrunc>(a.b, P, c);
 #pragma unroll
         for (int j = 0; j < E; ++j) {
             const bool end = (e.end >> j) & 1u;
@@ -347,8 +361,8 @@ struct DiscOp {
         s.end = e.end;
     }
     __device__ static bool far_open(const State& s) { return !((s.end >> (E - 1)) & 1u); }
-    template <bool F, bool TM, bool NT>
-    __device__ static void finish(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT, bool S>
+    __device__ static void finish(const Args& a, const Pos<E, F, TM, NT, S>& P, const Ctx& c,
                                   const float (&alpha)[E], const float (&beta)[E], const State&,
                                   float carry)
     {
@@ -390,8 +404,8 @@ struct VtraceOp {
         float r[E], v[E], tgt[E], rho_pg[E];  // tgt: Vnext at ends, V_{t+1} elsewhere
     };
 
-    template <bool F, bool TM, bool NT>
-    __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT, bool S>
+    __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT, S>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
         float lr[E];
@@ -399,11 +413,11 @@ struct VtraceOp {
         load_f32<E>(s.r, a.rewards, P, c.vec);
         load_f32<E>(s.v, a.values, P, c.vec);
         const float vnx = next_elem<E>(s.v[0], a.values, P, c, successor_used(P));
-        const Ends<E> e = load_ends<E, F, TM, NT, kTrunc>(a.b, P, c);
+        const Ends<E> e = load_ends<E, F, TM, NT, S, kTrunc>(a.b, P, c);
 #pragma unroll
         for (int j = 0; j < E; ++j) {
             const bool end = (e.end >> j) & 1u;
-            const float w = expf(lr[j]);
+            const float w = exp_e(lr[j]);
             const float rho = fminf(a.rho_bar, w);
             const float cc = a.lambda * fminf(a.c_bar, w);
             const float v1 = (j + 1 < E) ? s.v[(j + 1) % E] : vnx;
@@ -417,8 +431,8 @@ struct VtraceOp {
         s.end = e.end;
     }
     __device__ static bool far_open(const State& s) { return !((s.end >> (E - 1)) & 1u); }
-    template <bool F, bool TM, bool NT>
-    __device__ static void finish(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT, bool S>
+    __device__ static void finish(const Args& a, const Pos<E, F, TM, NT, S>& P, const Ctx& c,
                                   const float (&alpha)[E], const float (&beta)[E], const State& s,
                                   float carry)
     {
@@ -471,11 +485,11 @@ struct RetraceOp {
 
     __device__ static float trace(const Args& a, float lr)
     {
-        return a.lambda * fminf(a.c_bar, expf(lr));
+        return a.lambda * fminf(a.c_bar, exp_e(lr));
     }
 
-    template <bool F, bool TM, bool NT>
-    __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT, bool S>
+    __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT, S>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
         float lr[E], r[E], q[E], v[E], cc[E];
@@ -488,7 +502,7 @@ struct RetraceOp {
         const float lrnx = next_elem<E>(lr[0], a.log_rhos, P, c, used);
         const float qnx = next_elem<E>(q[0], a.q_values, P, c, used);
         const float vnx = next_elem<E>(v[0], a.values, P, c, used);
-        const Ends<E> e = load_ends<E, F, TM, NT, kTrunc>(a.b, P, c);
+        const Ends<E> e = load_ends<E, F, TM, NT, S, kTrunc>(a.b, P, c);
 #pragma unroll
         for (int j = 0; j < E; ++j) cc[j] = trace(a, lr[j]);
         const float cnx = trace(a, lrnx);
@@ -505,8 +519,8 @@ struct RetraceOp {
         s.end = e.end;
     }
     __device__ static bool far_open(const State& s) { return !((s.end >> (E - 1)) & 1u); }
-    template <bool F, bool TM, bool NT>
-    __device__ static void finish(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT, bool S>
+    __device__ static void finish(const Args& a, const Pos<E, F, TM, NT, S>& P, const Ctx& c,
                                   const float (&alpha)[E], const float (&beta)[E], const State&,
                                   float carry)
     {
@@ -520,9 +534,9 @@ struct RetraceOp {
 // reset_j = first-in-row_j | dones_{j-1}.  dones of the element before the
 // lane comes from the neighbouring lane (lane 0 of a wave reads it, except
 // at a row start where it is not needed).
-template <int E, bool F, bool TM, bool NT>
+template <int E, bool F, bool TM, bool NT, bool S>
 __device__ __forceinline__ uint32_t load_resets(Strided<const uint8_t> dn,
-                                                const Pos<E, F, TM, NT>& P, const Ctx& c)
+                                                const Pos<E, F, TM, NT, S>& P, const Ctx& c)
 {
     const uint8_t* __restrict__ dones = dn.p;
     const uint32_t d = load_mask<E>(dn, P, c.vec);
@@ -587,8 +601,8 @@ struct EligOp {
     struct State {
         uint32_t reset;
     };
-    template <bool F, bool TM, bool NT>
-    __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT, bool S>
+    __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT, S>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
         load_f32<E>(alpha, typed<D>(a.x), P, c.vec);
@@ -598,8 +612,8 @@ struct EligOp {
         clear_tail(alpha, beta, P);
     }
     __device__ static bool far_open(const State& s) { return !(s.reset & 1u); }
-    template <bool F, bool TM, bool NT>
-    __device__ static void finish(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT, bool S>
+    __device__ static void finish(const Args& a, const Pos<E, F, TM, NT, S>& P, const Ctx& c,
                                   const float (&alpha)[E], const float (&beta)[E], const State&,
                                   float carry)
     {
@@ -627,8 +641,8 @@ struct PrefixF32Op {
     struct State {
         uint32_t reset;
     };
-    template <bool F, bool TM, bool NT>
-    __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT, bool S>
+    __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT, S>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
         load_f32<E>(alpha, typed<D>(a.x), P, c.vec);
@@ -638,8 +652,8 @@ struct PrefixF32Op {
         clear_tail(alpha, beta, P);
     }
     __device__ static bool far_open(const State& s) { return !(s.reset & 1u); }
-    template <bool F, bool TM, bool NT>
-    __device__ static void finish(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT, bool S>
+    __device__ static void finish(const Args& a, const Pos<E, F, TM, NT, S>& P, const Ctx& c,
                                   const float (&alpha)[E], const float (&beta)[E], const State& s,
                                   float carry)
     {
@@ -667,8 +681,8 @@ struct PrefixI32Op {
     struct State {
         uint32_t reset;
     };
-    template <bool F, bool TM, bool NT>
-    __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT, bool S>
+    __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT, S>& P, const Ctx& c,
                                    uint32_t (&alpha)[E], uint32_t (&beta)[E], State& s)
     {
         load_u32<E>(alpha, typed<int32_t>(a.x), P, c.vec);
@@ -678,8 +692,8 @@ struct PrefixI32Op {
         clear_tail(alpha, beta, P);
     }
     __device__ static bool far_open(const State& s) { return !(s.reset & 1u); }
-    template <bool F, bool TM, bool NT>
-    __device__ static void finish(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT, bool S>
+    __device__ static void finish(const Args& a, const Pos<E, F, TM, NT, S>& P, const Ctx& c,
                                   const uint32_t (&alpha)[E], const uint32_t (&beta)[E],
                                   const State& s, uint32_t carry)
     {
@@ -724,8 +738,8 @@ struct AffineOp {
         uint32_t cut;
     };
 
-    template <bool F, bool TM, bool NT>
-    __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT, bool S>
+    __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT, S>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
         load_f32<E>(alpha, a.alpha, P, c.vec);
@@ -766,8 +780,8 @@ struct AffineOp {
     {
         return kRev ? !((s.cut >> (E - 1)) & 1u) : !(s.cut & 1u);
     }
-    template <bool F, bool TM, bool NT>
-    __device__ static void finish(const Args& a, const Pos<E, F, TM, NT>& P, const Ctx& c,
+    template <bool F, bool TM, bool NT, bool S>
+    __device__ static void finish(const Args& a, const Pos<E, F, TM, NT, S>& P, const Ctx& c,
                                   const float (&alpha)[E], const float (&beta)[E], const State&,
                                   float carry)
     {

@@ -42,7 +42,7 @@ lrs_status lrs_episodic_prefix_sum_i32(int64_t N, int64_t T, const int32_t* x,
                                        const uint8_t* dones, int32_t* out, const int64_t* strides, void* ws,
                                        size_t ws_bytes, hipStream_t stream)
 {
-    return prefix_sum_i32_entry("lrs_episodic_prefix_sum_i32", false, N, T, x, dones, out, strides, ws,
+    return prefix_sum_int_entry<int32_t>("lrs_episodic_prefix_sum_i32", false, N, T, x, dones, out, strides, ws,
                                 ws_bytes, stream);
 }
 
@@ -50,7 +50,7 @@ lrs_status lrs_episodic_prefix_sum_tm_i32(int64_t N, int64_t T, const int32_t* x
                                           const uint8_t* dones, int32_t* out, const int64_t* strides, void* ws,
                                           size_t ws_bytes, hipStream_t stream)
 {
-    return prefix_sum_i32_entry("lrs_episodic_prefix_sum_tm_i32", true, N, T, x, dones, out, strides, ws,
+    return prefix_sum_int_entry<int32_t>("lrs_episodic_prefix_sum_tm_i32", true, N, T, x, dones, out, strides, ws,
                                 ws_bytes, stream);
 }
 

@@ -126,9 +126,9 @@ struct BlockShared {
 // Everything after the positions are known.  F: the tile lies wholly inside
 // the array and the base pointers are vector aligned (straight-line vector
 // loads and stores); otherwise every access is guarded by the lane's count.
-template <class Op, int E, int W, class A, bool F, bool NT>
+template <class Op, int E, int W, class A, bool F, bool NT, bool S>
 __device__ __forceinline__ void tile_body(const typename Op::Args& args, const Sched& s,
-                                          uint32_t tile, const Pos<E, F, false, NT>& P, const Ctx& c,
+                                          uint32_t tile, const Pos<E, F, false, NT, S>& P, const Ctx& c,
                                           BlockShared<A, W>& sh)
 {
     using T = typename Op::T;  // A: the composition type (fp32 or fp64 for fp32 maps)
@@ -235,7 +235,7 @@ __device__ __forceinline__ void tile_body(const typename Op::Args& args, const S
     if (s.lookback && wave == 0 && lane == 0) close_launch(hdr, top_seen, s.num_tiles, tag);
 }
 
-template <class Op, int E, int W, class A, bool NT>
+template <class Op, int E, int W, class A, bool NT, bool S>
 __global__ __launch_bounds__(W * kWave) void scan_kernel(const typename Op::Args args, const Sched s)
 {
     constexpr bool kB = Op::kBackward;
@@ -282,12 +282,12 @@ __global__ __launch_bounds__(W * kWave) void scan_kernel(const typename Op::Args
     const Ctx c{s.total, s.T, tid & (kWave - 1), s.vec != 0};
 
     if (s.vec && tile_start + kTile <= s.total && s.T >= (uint32_t)E) {
-        const Pos<E, true, false, NT> P{i0, n0, E, last, first, 0, n0};
-        tile_body<Op, E, W, A, true, NT>(args, s, tile, P, c, sh);
+        const Pos<E, true, false, NT, S> P{i0, n0, E, last, first, 0, n0};
+        tile_body<Op, E, W, A, true, NT, S>(args, s, tile, P, c, sh);
     } else {
         const uint32_t valid = (count >= 32) ? ~0u : ((1u << count) - 1u);
-        const Pos<E, false, false, NT> P{i0, n0, count, last & valid, first & valid, 0, n0};
-        tile_body<Op, E, W, A, false, NT>(args, s, tile, P, c, sh);
+        const Pos<E, false, false, NT, S> P{i0, n0, count, last & valid, first & valid, 0, n0};
+        tile_body<Op, E, W, A, false, NT, S>(args, s, tile, P, c, sh);
     }
 }
 
@@ -406,33 +406,42 @@ constexpr int kWideCfg = 6;                          // 8x16: 8192-element tiles
 
 inline bool aligned(const void* p, uintptr_t a) { return p == nullptr || ((uintptr_t)p % a) == 0; }
 
-template <class Op, int E, int W, class A, bool NT = false>
+template <class Op, int E, int W, class A, bool S, bool NT = false>
 hipError_t launch_cfg(const typename Op::Args& a, const Sched& s, hipStream_t stream)
 {
     void* kargs[] = {(void*)&a, (void*)&s};
-    return hipLaunchKernel((const void*)&scan_kernel<Op, E, W, A, NT>, dim3(s.num_tiles),
+    return hipLaunchKernel((const void*)&scan_kernel<Op, E, W, A, NT, S>, dim3(s.num_tiles),
                            dim3(W * kWave), kargs, 0, stream);
 }
 
-template <template <int> class Op, class A>
+// S: some array of the call has a row stride other than its row length.
+template <template <int> class Op, class A, bool S>
 hipError_t launch_any(int cfg, const typename Op<4>::Args& a, const Sched& s, hipStream_t stream)
 {
     constexpr bool kNT = Op<4>::kStreamLoads;
     switch (cfg) {
-        case 0: return launch_cfg<Op<4>, 4, 1, A>(a, s, stream);
-        case 1: return launch_cfg<Op<4>, 4, 4, A>(a, s, stream);
+        case 0: return launch_cfg<Op<4>, 4, 1, A, S>(a, s, stream);
+        case 1: return launch_cfg<Op<4>, 4, 4, A, S>(a, s, stream);
         // Non-temporal input loads on long rows: the look-back tiles (4x8,
         // and 8x4 for 16-bit data) and the 8192-element tiles.
         case 2:
-            return s.lookback ? launch_cfg<Op<8>, 8, 4, A, kNT>(a, s, stream)
-                              : launch_cfg<Op<8>, 8, 4, A>(a, s, stream);
+            return s.lookback ? launch_cfg<Op<8>, 8, 4, A, S, kNT>(a, s, stream)
+                              : launch_cfg<Op<8>, 8, 4, A, S>(a, s, stream);
         case 3:
-            return s.lookback ? launch_cfg<Op<4>, 4, 8, A, kNT>(a, s, stream)
-                              : launch_cfg<Op<4>, 4, 8, A>(a, s, stream);
-        case 4: return launch_cfg<Op<16>, 16, 4, A>(a, s, stream);
-        case 5: return launch_cfg<Op<4>, 4, 16, A>(a, s, stream);
-        default: return launch_cfg<Op<8>, 8, 16, A, kNT>(a, s, stream);
+            return s.lookback ? launch_cfg<Op<4>, 4, 8, A, S, kNT>(a, s, stream)
+                              : launch_cfg<Op<4>, 4, 8, A, S>(a, s, stream);
+        case 4: return launch_cfg<Op<16>, 16, 4, A, S>(a, s, stream);
+        case 5: return launch_cfg<Op<4>, 4, 16, A, S>(a, s, stream);
+        default: return launch_cfg<Op<8>, 8, 16, A, S, kNT>(a, s, stream);
     }
+}
+
+template <template <int> class Op, class A>
+hipError_t launch_any(bool strided, int cfg, const typename Op<4>::Args& a, const Sched& s,
+                      hipStream_t stream)
+{
+    return strided ? launch_any<Op, A, true>(cfg, a, s, stream)
+                   : launch_any<Op, A, false>(cfg, a, s, stream);
 }
 
 // The schedule of a row-major call: tile shape (an index into kCfgs), the
@@ -520,10 +529,11 @@ lrs_status run(const char* name, int64_t N, int64_t T, float beta_max, const typ
     // array's base must be aligned to it, and a strided array's rows too, with
     // no lane straddling a row end (seq_len a multiple of E), so that a lane's
     // elements stay contiguous.
-    bool vec = true;
+    bool vec = true, strided = false;
     for (int i = 0; i < narrays; ++i) {
         const ArrayRef& r = arrays[i];
         if (r.p == nullptr) continue;
+        strided = strided || r.gap != 0;
         const uint64_t align = (uint64_t)k.E * r.elem_bytes < 16 ? (uint64_t)k.E * r.elem_bytes : 16;
         vec = vec && aligned(r.p, (uintptr_t)align);
         if (r.gap != 0) vec = vec && s.lane_in_row && (r.gap * (uint64_t)r.elem_bytes) % align == 0;
@@ -531,9 +541,10 @@ lrs_status run(const char* name, int64_t N, int64_t T, float beta_max, const typ
     s.vec = vec ? 1 : 0;
     hipError_t e;
     if constexpr (std::is_same<Val, float>::value)
-        e = fp64 ? launch_any<Op, double>(cfg, a, s, stream) : launch_any<Op, float>(cfg, a, s, stream);
+        e = fp64 ? launch_any<Op, double>(strided, cfg, a, s, stream)
+                 : launch_any<Op, float>(strided, cfg, a, s, stream);
     else
-        e = launch_any<Op, Val>(cfg, a, s, stream);
+        e = launch_any<Op, Val>(strided, cfg, a, s, stream);
     if (e != hipSuccess)
         return fail(LRS_ERR_HIP, "%s: kernel launch failed: %s", name, hipGetErrorString(e));
     g_err[0] = '\0';

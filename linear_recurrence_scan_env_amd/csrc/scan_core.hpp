@@ -174,7 +174,7 @@ __device__ __forceinline__ Aff<T> row_scan(Aff<T> x)
 // every access below is an unconditional vector load or store.  Otherwise
 // (the last tile, misaligned views) each access checks the lane's count.
 
-template <int E, bool kFull, bool kTM = false, bool kNT = false>
+template <int E, bool kFull, bool kTM = false, bool kNT = false, bool kStrided = false>
 struct Pos {
     uint64_t i0;     // flat index of element 0
     uint64_t n0;     // row (environment) of element 0
@@ -208,8 +208,8 @@ __device__ __forceinline__ Strided<const D> as_const(Strided<D> s)
     return {s.p, s.gap};
 }
 
-template <int E, bool kFull, bool TM, bool NT>
-__device__ __forceinline__ bool vector_ok(const Pos<E, kFull, TM, NT>& P, bool vec)
+template <int E, bool kFull, bool TM, bool NT, bool S>
+__device__ __forceinline__ bool vector_ok(const Pos<E, kFull, TM, NT, S>& P, bool vec)
 {
     return !TM && (kFull || (vec && P.count == E));
 }
@@ -217,19 +217,24 @@ __device__ __forceinline__ bool vector_ok(const Pos<E, kFull, TM, NT>& P, bool v
 // Offset of a lane's element j (0 <= j <= E) in an array with the given gap.
 // Row-major: element j lies in row o0 plus the number of row ends among the
 // lane's elements before it.  Time-major: element j is time step o0 + j.
-template <int E, bool kFull, bool TM, bool NT>
-__device__ __forceinline__ uint64_t elem_offset(const Pos<E, kFull, TM, NT>& P, int j, uint64_t gap)
+// Launches whose arrays are all contiguous (S = false) ignore the gaps, which
+// are then 0, and keep their address arithmetic to the flat index.
+template <int E, bool kFull, bool TM, bool NT, bool S>
+__device__ __forceinline__ uint64_t elem_offset(const Pos<E, kFull, TM, NT, S>& P, int j, uint64_t gap)
 {
-    if constexpr (TM) return P.i0 + (uint64_t)j * P.stride + (P.o0 + (uint64_t)j) * gap;
+    const uint64_t flat = TM ? P.i0 + (uint64_t)j * P.stride : P.i0 + (uint64_t)j;
+    if constexpr (!S) return flat;
+    if constexpr (TM) return flat + (P.o0 + (uint64_t)j) * gap;
     const uint32_t before = P.last & ((1u << j) - 1u);
-    return P.i0 + (uint64_t)j + (P.o0 + (uint64_t)__builtin_popcount(before)) * gap;
+    return flat + (P.o0 + (uint64_t)__builtin_popcount(before)) * gap;
 }
 
 // Offset of element 0, where a lane's vector accesses start: the host allows
 // vector access to a strided array only when no lane straddles a row end.
-template <int E, bool kFull, bool TM, bool NT>
-__device__ __forceinline__ uint64_t base_offset(const Pos<E, kFull, TM, NT>& P, uint64_t gap)
+template <int E, bool kFull, bool TM, bool NT, bool S>
+__device__ __forceinline__ uint64_t base_offset(const Pos<E, kFull, TM, NT, S>& P, uint64_t gap)
 {
+    if constexpr (!S) return P.i0;
     return P.i0 + P.o0 * gap;
 }
 
@@ -319,9 +324,9 @@ __device__ __forceinline__ V ld_vec(const S* p)
     }
 }
 
-template <int E, bool kFull, bool TM, bool NT, class D>
+template <int E, bool kFull, bool TM, bool NT, bool S, class D>
 __device__ __forceinline__ void load_f32(float (&v)[E], Strided<const D> a,
-                                         const Pos<E, kFull, TM, NT>& P, bool vec)
+                                         const Pos<E, kFull, TM, NT, S>& P, bool vec)
 {
     const D* __restrict__ p = a.p;
     if (vector_ok(P, vec)) {
@@ -356,9 +361,9 @@ __device__ __forceinline__ void load_f32(float (&v)[E], Strided<const D> a,
     }
 }
 
-template <int E, bool kFull, bool TM, bool NT>
+template <int E, bool kFull, bool TM, bool NT, bool S>
 __device__ __forceinline__ void load_u32(uint32_t (&v)[E], Strided<const int32_t> a,
-                                         const Pos<E, kFull, TM, NT>& P, bool vec)
+                                         const Pos<E, kFull, TM, NT, S>& P, bool vec)
 {
     const int32_t* __restrict__ p = a.p;
     if (vector_ok(P, vec)) {
@@ -390,8 +395,8 @@ __device__ __forceinline__ uint32_t nonzero_bytes(uint32_t w)
 }
 
 // Bit j of the result is (mask[i0 + j] != 0); a null mask reads as all zero.
-template <int E, bool kFull, bool TM, bool NT>
-__device__ __forceinline__ uint32_t load_mask(Strided<const uint8_t> a, const Pos<E, kFull, TM, NT>& P,
+template <int E, bool kFull, bool TM, bool NT, bool S>
+__device__ __forceinline__ uint32_t load_mask(Strided<const uint8_t> a, const Pos<E, kFull, TM, NT, S>& P,
                                               bool vec)
 {
     static_assert(E == 4 || E == 8 || E == 16, "mask loads are 4, 8 or 16 bytes");
@@ -417,9 +422,9 @@ __device__ __forceinline__ uint32_t load_mask(Strided<const uint8_t> a, const Po
 // Outputs are written once and not read again by this launch: full-tile
 // stores are non-temporal (streamed past the caches).
 
-template <int E, bool kFull, bool TM, bool NT, class D>
+template <int E, bool kFull, bool TM, bool NT, bool S, class D>
 __device__ __forceinline__ void store_f32(Strided<D> a, const float (&v)[E],
-                                          const Pos<E, kFull, TM, NT>& P, bool vec)
+                                          const Pos<E, kFull, TM, NT, S>& P, bool vec)
 {
     D* __restrict__ p = a.p;
     if (vector_ok(P, vec)) {
@@ -447,9 +452,9 @@ __device__ __forceinline__ void store_f32(Strided<D> a, const float (&v)[E],
     }
 }
 
-template <int E, bool kFull, bool TM, bool NT>
+template <int E, bool kFull, bool TM, bool NT, bool S>
 __device__ __forceinline__ void store_u32(Strided<int32_t> a, const uint32_t (&v)[E],
-                                          const Pos<E, kFull, TM, NT>& P, bool vec)
+                                          const Pos<E, kFull, TM, NT, S>& P, bool vec)
 {
     int32_t* __restrict__ p = a.p;
     if (vector_ok(P, vec)) {

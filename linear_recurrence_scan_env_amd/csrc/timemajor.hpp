@@ -93,7 +93,7 @@ struct BlockSharedTM {
 
 // One tile.  F: every lane of the block is an environment and every one of
 // its steps exists (unconditional accesses); otherwise accesses are guarded.
-template <class Op, int E, int W, class A, bool F>
+template <class Op, int E, int W, class A, bool F, bool S>
 __device__ __forceinline__ void tile_body_tm(const typename Op::Args& args, const SchedTM& s,
                                              uint32_t k, uint32_t g, BlockSharedTM<A, W>& sh)
 {
@@ -118,7 +118,7 @@ __device__ __forceinline__ void tile_body_tm(const typename Op::Args& args, cons
         if (t0 == 0) first = 1u;
     }
     const uint32_t col = active ? n : 0u;  // inactive lanes touch nothing (count = 0)
-    const Pos<E, F, true> P{(uint64_t)t0 * s.N + col, col, count, last, first, s.N, t0};
+    const Pos<E, F, true, false, S> P{(uint64_t)t0 * s.N + col, col, count, last, first, s.N, t0};
     const Ctx c{(uint64_t)s.N * s.T, s.T, lane, false};
 
     // The launch tag is read first, in flight with the tile's loads.  These
@@ -265,7 +265,7 @@ __device__ __forceinline__ void tile_body_tm(const typename Op::Args& args, cons
     }
 }
 
-template <class Op, int E, int W, class A>
+template <class Op, int E, int W, class A, bool S>
 __global__ __launch_bounds__(W * kWave) void scan_kernel_tm(const typename Op::Args args,
                                                             const SchedTM s)
 {
@@ -275,9 +275,9 @@ __global__ __launch_bounds__(W * kWave) void scan_kernel_tm(const typename Op::A
     const uint32_t k = tp.k, g = tp.g;
     const bool full = (uint64_t)(k + 1u) * kSteps <= s.T && (uint64_t)(g + 1u) * kWave <= s.N;
     if (full)
-        tile_body_tm<Op, E, W, A, true>(args, s, k, g, sh);
+        tile_body_tm<Op, E, W, A, true, S>(args, s, k, g, sh);
     else
-        tile_body_tm<Op, E, W, A, false>(args, s, k, g, sh);
+        tile_body_tm<Op, E, W, A, false, S>(args, s, k, g, sh);
 }
 
 // Rows that fit one tile, on few environments: V environments per block
@@ -293,7 +293,7 @@ struct BlockSharedTMRows {
     A b[Q][V];
 };
 
-template <class Op, int E, int W, int V, class A, bool F>
+template <class Op, int E, int W, int V, class A, bool F, bool S>
 __device__ __forceinline__ void rows_body_tm(const typename Op::Args& args, const SchedTM& s,
                                              uint32_t g, BlockSharedTMRows<A, W * (kWave / V), V>& sh)
 {
@@ -318,7 +318,7 @@ __device__ __forceinline__ void rows_body_tm(const typename Op::Args& args, cons
         if (t0 == 0) first = 1u;
     }
     const uint32_t col = active ? n : 0u;  // inactive lanes touch nothing (count = 0)
-    const Pos<E, F, true> P{(uint64_t)t0 * s.N + col, col, count, last, first, s.N, t0};
+    const Pos<E, F, true, false, S> P{(uint64_t)t0 * s.N + col, col, count, last, first, s.N, t0};
     const Ctx c{(uint64_t)s.N * s.T, s.T, lane, false};
 
     T alpha[E], beta[E];
@@ -358,7 +358,7 @@ __device__ __forceinline__ void rows_body_tm(const typename Op::Args& args, cons
     Op::finish(args, P, c, alpha, beta, st, lane_in);
 }
 
-template <class Op, int E, int W, int V, class A>
+template <class Op, int E, int W, int V, class A, bool S>
 __global__ __launch_bounds__(W * kWave) void scan_kernel_tm_rows(const typename Op::Args args,
                                                                  const SchedTM s)
 {
@@ -367,9 +367,9 @@ __global__ __launch_bounds__(W * kWave) void scan_kernel_tm_rows(const typename 
     const uint32_t g = blockIdx.x;
     const bool full = kSteps == s.T && (uint64_t)(g + 1u) * V <= s.N;
     if (full)
-        rows_body_tm<Op, E, W, V, A, true>(args, s, g, sh);
+        rows_body_tm<Op, E, W, V, A, true, S>(args, s, g, sh);
     else
-        rows_body_tm<Op, E, W, V, A, false>(args, s, g, sh);
+        rows_body_tm<Op, E, W, V, A, false, S>(args, s, g, sh);
 }
 
 // ------------------------------------------------------------- host side
@@ -436,43 +436,47 @@ inline size_t workspace_bytes_tm(uint64_t N, uint64_t T)
 }
 
 template <template <int> class Op, int E, int W, class A>
-hipError_t launch_tm(const typename Op<kTmE>::Args& a, const SchedTM& s, hipStream_t stream)
+hipError_t launch_tm(bool strided, const typename Op<kTmE>::Args& a, const SchedTM& s,
+                     hipStream_t stream)
 {
     void* params[] = {(void*)&a, (void*)&s};
-    return hipLaunchKernel((const void*)&scan_kernel_tm<Op<E>, E, W, A>,
-                           dim3(s.num_blocks), dim3(W * kWave), params, 0, stream);
+    const void* k = strided ? (const void*)&scan_kernel_tm<Op<E>, E, W, A, true>
+                            : (const void*)&scan_kernel_tm<Op<E>, E, W, A, false>;
+    return hipLaunchKernel(k, dim3(s.num_blocks), dim3(W * kWave), params, 0, stream);
 }
 
 template <template <int> class Op, int W, int V, class A>
-hipError_t launch_tm_rows(const typename Op<kTmE>::Args& a, const SchedTM& s, hipStream_t stream)
+hipError_t launch_tm_rows(bool strided, const typename Op<kTmE>::Args& a, const SchedTM& s,
+                          hipStream_t stream)
 {
     void* params[] = {(void*)&a, (void*)&s};
-    return hipLaunchKernel((const void*)&scan_kernel_tm_rows<Op<kTmE>, kTmE, W, V, A>,
-                           dim3(s.num_blocks), dim3(W * kWave), params, 0, stream);
+    const void* k = strided ? (const void*)&scan_kernel_tm_rows<Op<kTmE>, kTmE, W, V, A, true>
+                            : (const void*)&scan_kernel_tm_rows<Op<kTmE>, kTmE, W, V, A, false>;
+    return hipLaunchKernel(k, dim3(s.num_blocks), dim3(W * kWave), params, 0, stream);
 }
 
 template <template <int> class Op, int W, int V>
-hipError_t launch_tm_rows_acc(float beta_max, const typename Op<kTmE>::Args& a, const SchedTM& s,
-                              hipStream_t stream)
+hipError_t launch_tm_rows_acc(float beta_max, bool strided, const typename Op<kTmE>::Args& a,
+                              const SchedTM& s, hipStream_t stream)
 {
     using Val = typename Op<kTmE>::T;
     if constexpr (std::is_same<Val, float>::value)
-        return beta_max > kFp32BetaMax ? launch_tm_rows<Op, W, V, double>(a, s, stream)
-                                       : launch_tm_rows<Op, W, V, float>(a, s, stream);
+        return beta_max > kFp32BetaMax ? launch_tm_rows<Op, W, V, double>(strided, a, s, stream)
+                                       : launch_tm_rows<Op, W, V, float>(strided, a, s, stream);
     else
-        return launch_tm_rows<Op, W, V, Val>(a, s, stream);
+        return launch_tm_rows<Op, W, V, Val>(strided, a, s, stream);
 }
 
 template <template <int> class Op, int W, int E = kTmE>
-hipError_t launch_tm_acc(float beta_max, const typename Op<kTmE>::Args& a, const SchedTM& s,
-                         hipStream_t stream)
+hipError_t launch_tm_acc(float beta_max, bool strided, const typename Op<kTmE>::Args& a,
+                         const SchedTM& s, hipStream_t stream)
 {
     using Val = typename Op<kTmE>::T;
     if constexpr (std::is_same<Val, float>::value)
-        return beta_max > kFp32BetaMax ? launch_tm<Op, E, W, double>(a, s, stream)
-                                       : launch_tm<Op, E, W, float>(a, s, stream);
+        return beta_max > kFp32BetaMax ? launch_tm<Op, E, W, double>(strided, a, s, stream)
+                                       : launch_tm<Op, E, W, float>(strided, a, s, stream);
     else
-        return launch_tm<Op, E, W, Val>(a, s, stream);
+        return launch_tm<Op, E, W, Val>(strided, a, s, stream);
 }
 
 // The schedule of a time-major call: narrow whole-row blocks (rows_waves > 0
@@ -513,7 +517,8 @@ inline PlanTM plan_time_major(int64_t N, int64_t T)
 
 template <template <int> class Op>
 lrs_status run_tm(const char* name, int64_t N, int64_t T, float beta_max,
-                  const typename Op<kTmE>::Args& a, void* ws, size_t ws_bytes, hipStream_t stream)
+                  const typename Op<kTmE>::Args& a, bool strided, void* ws, size_t ws_bytes,
+                  hipStream_t stream)
 {
     if (N >= (int64_t(1) << 32))
         return fail(LRS_ERR_INVALID_ARG, "%s: time-major calls need num_envs < 2^32", name);
@@ -523,10 +528,10 @@ lrs_status run_tm(const char* name, int64_t N, int64_t T, float beta_max,
         s.ws = static_cast<uint8_t*>(ws);
         hipError_t e;
         switch (Wr) {
-            case 1: e = launch_tm_rows_acc<Op, 1, kTmRowsV>(beta_max, a, s, stream); break;
-            case 2: e = launch_tm_rows_acc<Op, 2, kTmRowsV>(beta_max, a, s, stream); break;
-            case 4: e = launch_tm_rows_acc<Op, 4, kTmRowsV>(beta_max, a, s, stream); break;
-            default: e = launch_tm_rows_acc<Op, 8, kTmRowsV>(beta_max, a, s, stream); break;
+            case 1: e = launch_tm_rows_acc<Op, 1, kTmRowsV>(beta_max, strided, a, s, stream); break;
+            case 2: e = launch_tm_rows_acc<Op, 2, kTmRowsV>(beta_max, strided, a, s, stream); break;
+            case 4: e = launch_tm_rows_acc<Op, 4, kTmRowsV>(beta_max, strided, a, s, stream); break;
+            default: e = launch_tm_rows_acc<Op, 8, kTmRowsV>(beta_max, strided, a, s, stream); break;
         }
         if (e != hipSuccess)
             return fail(LRS_ERR_HIP, "%s: kernel launch failed: %s", name, hipGetErrorString(e));
@@ -557,12 +562,12 @@ lrs_status run_tm(const char* name, int64_t N, int64_t T, float beta_max,
     }
     hipError_t e;
     if (long_rows) {
-        e = launch_tm_acc<Op, kTmWLarge, kTmELong>(beta_max, a, s, stream);
+        e = launch_tm_acc<Op, kTmWLarge, kTmELong>(beta_max, strided, a, s, stream);
     } else switch (W) {
-        case 2: e = launch_tm_acc<Op, 2>(beta_max, a, s, stream); break;
-        case 4: e = launch_tm_acc<Op, 4>(beta_max, a, s, stream); break;
-        case 8: e = launch_tm_acc<Op, 8>(beta_max, a, s, stream); break;
-        default: e = launch_tm_acc<Op, 16>(beta_max, a, s, stream); break;
+        case 2: e = launch_tm_acc<Op, 2>(beta_max, strided, a, s, stream); break;
+        case 4: e = launch_tm_acc<Op, 4>(beta_max, strided, a, s, stream); break;
+        case 8: e = launch_tm_acc<Op, 8>(beta_max, strided, a, s, stream); break;
+        default: e = launch_tm_acc<Op, 16>(beta_max, strided, a, s, stream); break;
     }
     if (e != hipSuccess)
         return fail(LRS_ERR_HIP, "%s: kernel launch failed: %s", name, hipGetErrorString(e));
