@@ -42,9 +42,12 @@ __device__ __forceinline__ float exp_e(float x)
 }
 
 // Tile shape of an op's look-back launches on fp32 data (measured on long
-// rows): four elements per lane in 2048-element tiles for ops with many
-// input streams; eight per lane for ops with few; four per lane in
-// 4096-element tiles for the prefix sums.
+// rows): four elements per lane in 2048-element tiles for GAE and V-trace;
+// four per lane in 4096-element tiles for Retrace (its four input streams
+// and shifted traces; 1-2% faster than 2048 at 64 x 131072, 12% with
+// truncations at 1024 x 16384) and the affine scan; eight per lane for the
+// ops with few streams, the prefix sums included (int32: 12-21% faster
+// than four per lane in 4096-element tiles).
 enum LookbackTile { kLbNarrow, kLbLight, kLbWide4 };
 
 // Value of stream p at flat index i0+E (element 0 of the next chunk).  Full
@@ -477,7 +480,7 @@ struct RetraceOp {
     // Whole rows of 4096 or 8192 in one block (E = 8 or 16 waves) cost
     // this op occupancy: its per-element state needs more registers.
     static constexpr bool kWideTiles = false;
-    static constexpr LookbackTile kLookbackTile = kLbNarrow;
+    static constexpr LookbackTile kLookbackTile = kLbWide4;
     static constexpr bool kStreamLoads = true;
     struct State {
         uint32_t end;
@@ -636,7 +639,7 @@ struct PrefixF32Op {
     static constexpr int kElemBytes = sizeof(D);
     static constexpr bool kBackward = false;
     static constexpr bool kWideTiles = true;
-    static constexpr LookbackTile kLookbackTile = kLbWide4;
+    static constexpr LookbackTile kLookbackTile = kLbLight;
     static constexpr bool kStreamLoads = true;
     struct State {
         uint32_t reset;
@@ -676,7 +679,7 @@ struct PrefixI32Op {
     static constexpr int kElemBytes = 4;
     static constexpr bool kBackward = false;
     static constexpr bool kWideTiles = true;
-    static constexpr LookbackTile kLookbackTile = kLbWide4;
+    static constexpr LookbackTile kLookbackTile = kLbLight;
     static constexpr bool kStreamLoads = true;
     struct State {
         uint32_t reset;

@@ -140,7 +140,11 @@ __device__ __forceinline__ void tile_body(const typename Op::Args& args, const S
     uint64_t* rec = reinterpret_cast<uint64_t*>(s.ws + sizeof(WsHeader));
 
     // The block count (which returns the launch tag) and the neighbour's record
-    // are issued first, in flight with the tile's loads.
+    // are issued first, in flight with the tile's loads.  (Publishing one
+    // record per wave instead, so that a waiting neighbour needs only the
+    // waves nearest to it, measured 15-90% slower on long rows: every wave
+    // then needs the launch tag before the block's barrier, and the reads of
+    // the one header word that carries it serialize.)
     const bool far_most = kB ? (tile == s.num_tiles - 1u) : (tile == 0u);
     Record early{{0, 0, 0, 0}};
     uint64_t entry = 0;
@@ -352,12 +356,12 @@ inline size_t workspace_bytes_for(uint64_t total)
 // kWideTiles when at least kWideMinTiles of them fill the chip, else in
 // 2048-element tiles of four waves.  16-bit rows that divide 2048 also take
 // those 2048-element tiles when at least kWideMinTiles of them fill the chip.
-// Long fp32 rows (measured at 64 x 131072, 256 x 65536 and 1024 x 16384)
-// follow the op's LookbackTile: kLbLight ops take eight elements per lane,
-// in 8192-element tiles when kWideMinTiles of them fill the chip, else in
-// 2048-element ones; kLbWide4 ops and maps composed in fp64 take
-// 4096-element tiles of four per lane; kLbNarrow ops 2048-element tiles of
-// four per lane.
+// Long fp32 rows (measured at 64 x 131072 and 1024 x 16384 on inputs
+// cycled over >= 1 GiB) follow the op's LookbackTile: kLbLight ops take
+// eight elements per lane, in 8192-element tiles when kWideMinTiles of them
+// fill the chip, else in 2048-element ones (also when composed in fp64);
+// kLbWide4 ops, and kLbNarrow ops composed in fp64, 4096-element tiles of
+// four per lane; kLbNarrow ops 2048-element tiles of four per lane.
 inline int choose_cfg(uint64_t total, uint64_t T, bool wide_ok, LookbackTile lb, bool fp64, int elem_bytes,
                       bool* lookback)
 {
@@ -391,7 +395,7 @@ inline int choose_cfg(uint64_t total, uint64_t T, bool wide_ok, LookbackTile lb,
                                 kCfgs[kLookbackCfgHalfWide].tile();
     if (elem_bytes == 2)
         return wide_ok && wide_tiles >= kWideMinTiles ? kLookbackCfgHalfWide : kLookbackCfgHalf;
-    if (fp64 || lb == kLbWide4) return kLookbackCfgWide4;
+    if (lb == kLbWide4 || (fp64 && lb == kLbNarrow)) return kLookbackCfgWide4;
     if (lb == kLbLight) return wide_tiles >= kWideMinTiles ? kLookbackCfgHalfWide : kLookbackCfgLight;
     return kLookbackCfg;
 }

@@ -187,7 +187,7 @@ def test_schedule_info_matches_plan(lib):
     info, _ = schedule(lib, GAE, 0, 1024, 16384, 0.9405)
     assert info.carries == 1 and info.tiles_per_row == 16384 // info.tile_elems  # position-major
     info, _ = schedule(lib, PREFIX_F32, 0, 64, 131072, 1.0)
-    assert info.composition_fp64 == 1 and info.elems_per_lane == 4 and info.waves_per_block == 16
+    assert info.composition_fp64 == 1 and info.elems_per_lane == 8 and info.waves_per_block == 16
     info, _ = schedule(lib, GAE, 0, 64, 131072, 0.9405)
     assert info.composition_fp64 == 0
     info, _ = schedule(lib, GAE, TIME_MAJOR, 4096, 128, 0.9)
