@@ -336,6 +336,9 @@ def cpu_baseline(name, batches, seconds):
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_PROFILE = os.path.join(PROFILES, "hbm_traffic_all7_4096x128.md")
 CALIBRATION_BYTES = 64 << 20  # one --calibrate-copy dispatch reads and writes this much
+# grid of the calibration dispatch (lrs_debug_floor's streaming kernel, eight
+# 16-byte vectors per lane): unique among the dispatches of a counter run
+CALIBRATION_GRID = (CALIBRATION_BYTES // 16 // 8 // 256, 256)
 
 
 def source_hash():
@@ -441,7 +444,8 @@ def committed_profile(workload):
 
 def summarize_counters(fetch_csv, write_csv, command_fetch, command_write):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by what the same
-    counters read for the calibration copy of CALIBRATION_BYTES."""
+    counters read for the calibration dispatch: the streaming kernel reading
+    and writing CALIBRATION_BYTES (matched by kernel name and grid size)."""
     import csv
     import collections
 
@@ -453,7 +457,7 @@ def summarize_counters(fetch_csv, write_csv, command_fetch, command_write):
             k = call_of_kernel(r["Kernel_Name"])
             if k and not k.startswith("floor:"):
                 per[k].append(v)
-            elif "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) == CALIBRATION_BYTES // 512:
+            elif k == "floor:stream" and int(r["Grid_Size"]) == CALIBRATION_GRID[0] * CALIBRATION_GRID[1]:
                 calib.append(v)
         return per, calib
 
@@ -465,7 +469,8 @@ def summarize_counters(fetch_csv, write_csv, command_fetch, command_write):
     n_trunc = trunc_counts(make_batches(DEFAULT_WORKLOAD))[(n, t)]
     out = ["# HBM traffic per launch: seven estimators at 4096 x 128 (cold inputs)", "",
            "Commands (one counter per pass):", "", "```", command_fetch, command_write, "```", "",
-           f"Calibration: a device copy of {CALIBRATION_BYTES >> 20} MiB reads FETCH_SIZE "
+           f"Calibration: the streaming kernel reading and writing {CALIBRATION_BYTES >> 20} MiB "
+           f"(grid {CALIBRATION_GRID[0]} x {CALIBRATION_GRID[1]}) reads FETCH_SIZE "
            f"{sum(fcal) / len(fcal) / 1024:.1f} KiB and WRITE_SIZE {sum(wcal) / len(wcal) / 1024:.1f} KiB "
            f"per dispatch, so the scale factors are fetch x{ff:.4f}, write x{wf:.4f}.", "",
            "| call | FETCH KiB (raw) | WRITE KiB (raw) | traffic bytes (scaled) | algorithmic bytes | traffic / algorithmic |",
@@ -710,8 +715,8 @@ def main():
                     help="launch calls one by one instead of replaying HIP graphs "
                          "(for counter collection)")
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="first run 5 device copies of a 64 MiB tensor: a kernel of known "
-                         "HBM traffic for scaling FETCH_SIZE / WRITE_SIZE counters")
+                    help="first run the streaming kernel 5 times over 64 MiB in and 64 MiB out: a "
+                         "kernel of known HBM traffic for scaling FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--summarize-trace", nargs=4,
                     metavar=("TRACE_CSV", "COMMAND", "WORKLOAD", "TITLE"),
                     help="print the markdown summary of a rocprofv3 kernel_trace.csv of a run "
@@ -764,9 +769,14 @@ def main():
     if args.calibrate_copy:
         src = torch.ones(CALIBRATION_BYTES // 4, device=dev)
         dst = torch.empty_like(src)
-        with torch.cuda.stream(stream):
-            for _ in range(5):
-                dst.copy_(src)
+        fl = lib.lrs_debug_floor
+        fl.restype = ctypes.c_int
+        fl.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+                       ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        for _ in range(5):
+            if fl(1, CALIBRATION_GRID[0], CALIBRATION_GRID[1], src.data_ptr(), CALIBRATION_BYTES,
+                  dst.data_ptr(), CALIBRATION_BYTES, stream.cuda_stream) != 0:
+                raise RuntimeError(lib.lrs_last_error().decode())
         torch.cuda.synchronize()
         del src, dst
     if args.eager:

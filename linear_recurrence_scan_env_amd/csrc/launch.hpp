@@ -242,6 +242,7 @@ __device__ __forceinline__ void tile_body(const typename Op::Args& args, const S
 template <class Op, int E, int W, class A, bool NT, bool S>
 __global__ __launch_bounds__(W * kWave) void scan_kernel(const typename Op::Args args, const Sched s)
 {
+    warm_kernargs<kernarg_bytes<typename Op::Args, Sched>()>();
     constexpr bool kB = Op::kBackward;
     constexpr uint32_t kTile = (uint32_t)E * kWave * W;
     __shared__ BlockShared<A, W> sh;

@@ -167,6 +167,33 @@ __device__ __forceinline__ Aff<T> row_scan(Aff<T> x)
     return x;
 }
 
+// ------------------------------------------------------- kernel arguments
+// A kernel's arguments are read through the scalar cache, which starts each
+// dispatch cold.  Left alone, the compiler loads each argument where it is
+// first used: the schedule fields that pick the branch first, then the
+// array pointers inside it, so a wave waits for several dependent cache
+// misses before its first data load (at 4096 x 128 about 1 us of a 3-5 us
+// call).  Reading one word of every 64-byte line of the argument block at
+// entry, and consuming their xor in an empty asm statement, issues all those
+// misses together; the later loads of the same lines then hit.
+template <int kBytes>
+__device__ __forceinline__ void warm_kernargs()
+{
+    typedef __attribute__((address_space(4))) const uint32_t kword;
+    const kword* k = (const kword*)__builtin_amdgcn_kernarg_segment_ptr();
+    uint32_t x = 0u;
+#pragma unroll
+    for (int off = 0; off < kBytes; off += 64) x ^= k[off / 4];
+    asm volatile("" ::"s"(x));
+}
+
+// Bytes of the explicit arguments (args, sched) of a scan kernel.
+template <class Args, class Sch>
+constexpr int kernarg_bytes()
+{
+    return (int)((sizeof(Args) + alignof(Sch) - 1) / alignof(Sch) * alignof(Sch) + sizeof(Sch));
+}
+
 // ----------------------------------------------------------------- loads
 // A lane owns E consecutive elements starting at flat index i0 (a multiple
 // of E).  Pos<E, kFull> says where they are; kFull marks a tile that lies

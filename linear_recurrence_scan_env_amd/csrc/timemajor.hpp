@@ -269,6 +269,7 @@ template <class Op, int E, int W, class A, bool S>
 __global__ __launch_bounds__(W * kWave) void scan_kernel_tm(const typename Op::Args args,
                                                             const SchedTM s)
 {
+    warm_kernargs<kernarg_bytes<typename Op::Args, SchedTM>()>();
     constexpr uint32_t kSteps = (uint32_t)E * W;
     __shared__ BlockSharedTM<A, W> sh;
     const TilePlaceTM tp = place_tile_tm(blockIdx.x, s, Op::kBackward);
@@ -362,6 +363,7 @@ template <class Op, int E, int W, int V, class A, bool S>
 __global__ __launch_bounds__(W * kWave) void scan_kernel_tm_rows(const typename Op::Args args,
                                                                  const SchedTM s)
 {
+    warm_kernargs<kernarg_bytes<typename Op::Args, SchedTM>()>();
     constexpr uint32_t kSteps = (uint32_t)E * W * (kWave / V);
     __shared__ BlockSharedTMRows<A, W * (kWave / V), V> sh;
     const uint32_t g = blockIdx.x;
