@@ -3,7 +3,11 @@
     python -m linear_recurrence_scan_env_amd.build [--resource-usage]
 
 Flags: gfx950 only; packed-fp32 instruction selection disabled; -O3; no
-fast-math (the kernels rely on IEEE fma/min semantics).
+fast-math (the kernels rely on IEEE fma/min semantics); the compiler's
+atomic optimizer off.  Every atomic here is already issued by one lane; the
+optimizer would still rewrite a returning one into a wave-wide form whose
+result is broadcast at once, which waits for the atomic's round trip right
+after it (a block's look-back count then held back its data loads).
 """
 from __future__ import annotations
 
@@ -39,6 +43,7 @@ def hipcc() -> str:
 def flags(resource_usage: bool = False):
     f = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
          "-Wall", "-Wno-unused-command-line-argument",
          "-I", os.path.join(ROOT, "include")]
     if resource_usage:
