@@ -50,6 +50,15 @@ __device__ __forceinline__ float exp_e(float x)
 // than four per lane in 4096-element tiles).
 enum LookbackTile { kLbNarrow, kLbLight, kLbWide4 };
 
+// kLeanSgprs: the op's look-back launches (four or more waves per block) use
+// a kernel built with a cap on scalar registers.  A block of W waves needs W / 4 wave
+// slots on each SIMD, and on gfx950 a kernel measured to need at most about 72
+// SGPRs for eight waves per SIMD (more cost it blocks per CU, whatever the
+// compiler's occupancy estimate says).  V-trace's kernels hold 83-100; capped,
+// they spill a few to vector lanes and run 2-3% faster on long rows.  Maps
+// composed in fp64 are capped for every op (the fp32 prefix sum at 64 x 131072:
+// one block per CU instead of two, 22.9 -> 19.0 us).
+
 // Value of stream p at flat index i0+E (element 0 of the next chunk).  Full
 // tiles load it in every lane (same cache line as the neighbouring chunk's
 // vector load), unconditionally, so it is in flight with the lane's other
@@ -229,6 +238,7 @@ struct GaeOp {
     static constexpr bool kWideTiles = true;
     static constexpr LookbackTile kLookbackTile = kLbNarrow;
     static constexpr bool kStreamLoads = true;
+    static constexpr bool kLeanSgprs = false;
     struct State {
         uint32_t end;
     };
@@ -288,6 +298,7 @@ struct LambdaOp {
     static constexpr LookbackTile kLookbackTile = kLbLight;
     // non-temporal input loads measure slower for this op on long rows
     static constexpr bool kStreamLoads = false;
+    static constexpr bool kLeanSgprs = false;
     struct State {
         uint32_t end;
     };
@@ -343,6 +354,7 @@ struct DiscOp {
     static constexpr bool kWideTiles = true;
     static constexpr LookbackTile kLookbackTile = kLbLight;
     static constexpr bool kStreamLoads = true;
+    static constexpr bool kLeanSgprs = false;
     struct State {
         uint32_t end;
     };
@@ -402,6 +414,7 @@ struct VtraceOp {
     static constexpr bool kWideTiles = false;
     static constexpr LookbackTile kLookbackTile = kLbNarrow;
     static constexpr bool kStreamLoads = true;
+    static constexpr bool kLeanSgprs = true;
     struct State {
         uint32_t end;
         float r[E], v[E], tgt[E], rho_pg[E];  // tgt: Vnext at ends, V_{t+1} elsewhere
@@ -482,6 +495,7 @@ struct RetraceOp {
     static constexpr bool kWideTiles = false;
     static constexpr LookbackTile kLookbackTile = kLbWide4;
     static constexpr bool kStreamLoads = true;
+    static constexpr bool kLeanSgprs = false;
     struct State {
         uint32_t end;
     };
@@ -601,6 +615,7 @@ struct EligOp {
     static constexpr bool kWideTiles = true;
     static constexpr LookbackTile kLookbackTile = kLbLight;
     static constexpr bool kStreamLoads = true;
+    static constexpr bool kLeanSgprs = false;
     struct State {
         uint32_t reset;
     };
@@ -641,6 +656,7 @@ struct PrefixF32Op {
     static constexpr bool kWideTiles = true;
     static constexpr LookbackTile kLookbackTile = kLbLight;
     static constexpr bool kStreamLoads = true;
+    static constexpr bool kLeanSgprs = false;
     struct State {
         uint32_t reset;
     };
@@ -681,6 +697,7 @@ struct PrefixI32Op {
     static constexpr bool kWideTiles = true;
     static constexpr LookbackTile kLookbackTile = kLbLight;
     static constexpr bool kStreamLoads = true;
+    static constexpr bool kLeanSgprs = false;
     struct State {
         uint32_t reset;
     };
@@ -737,6 +754,7 @@ struct AffineOp {
     static constexpr bool kWideTiles = true;
     static constexpr LookbackTile kLookbackTile = kLbWide4;
     static constexpr bool kStreamLoads = true;
+    static constexpr bool kLeanSgprs = false;
     struct State {
         uint32_t cut;
     };

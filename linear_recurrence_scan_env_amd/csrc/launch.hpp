@@ -240,7 +240,7 @@ __device__ __forceinline__ void tile_body(const typename Op::Args& args, const S
 }
 
 template <class Op, int E, int W, class A, bool NT, bool S>
-__global__ __launch_bounds__(W * kWave) void scan_kernel(const typename Op::Args args, const Sched s)
+__device__ __forceinline__ void scan_body(const typename Op::Args& args, const Sched& s)
 {
     warm_kernargs<kernarg_bytes<typename Op::Args, Sched>()>();
     constexpr bool kB = Op::kBackward;
@@ -294,6 +294,37 @@ __global__ __launch_bounds__(W * kWave) void scan_kernel(const typename Op::Args
         const Pos<E, false, false, NT, S> P{i0, n0, count, last & valid, first & valid, 0, n0};
         tile_body<Op, E, W, A, false, NT, S>(args, s, tile, P, c, sh);
     }
+}
+
+template <class Op, int E, int W, class A, bool NT, bool S>
+__global__ __launch_bounds__(W * kWave) void scan_kernel(const typename Op::Args args, const Sched s)
+{
+    scan_body<Op, E, W, A, NT, S>(args, s);
+}
+
+// The same kernel with its scalar registers capped at 72: a gfx950 SIMD held
+// eight waves of a kernel only while it needed at most about that many
+// (measured from per-block timestamps: kernels of 68-72 SGPRs ran eight waves
+// per SIMD, one of 87 six, ones of 77 and 88 could not fit a second 16-wave
+// block per CU), although the compiler estimates full occupancy up to about
+// 100.  The excess spills to vector lanes.
+template <class Op, int E, int W, class A, bool NT, bool S>
+__global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_num_sgpr(72))) void scan_kernel_lean(
+    const typename Op::Args args, const Sched s)
+{
+    scan_body<Op, E, W, A, NT, S>(args, s);
+}
+
+// Look-back launches with four or more waves per block take the capped
+// kernel for maps composed in fp64 and for ops that ask for it (kLeanSgprs):
+// there a block waiting for its carry holds its slot, and more resident
+// blocks keep loads in flight.  Launches without carries keep the uncapped
+// kernel (the capped one measured 1-3% slower there: the spills cost and the
+// loads already saturate).
+template <class Op, int W, class A>
+constexpr bool lean_sgprs()
+{
+    return W >= 4 && (std::is_same<A, double>::value || Op::kLeanSgprs);
 }
 
 // ------------------------------------------------------------ host side
@@ -415,8 +446,10 @@ template <class Op, int E, int W, class A, bool S, bool NT = false>
 hipError_t launch_cfg(const typename Op::Args& a, const Sched& s, hipStream_t stream)
 {
     void* kargs[] = {(void*)&a, (void*)&s};
-    return hipLaunchKernel((const void*)&scan_kernel<Op, E, W, A, NT, S>, dim3(s.num_tiles),
-                           dim3(W * kWave), kargs, 0, stream);
+    const void* k = (const void*)&scan_kernel<Op, E, W, A, NT, S>;
+    if constexpr (lean_sgprs<Op, W, A>())
+        if (s.lookback) k = (const void*)&scan_kernel_lean<Op, E, W, A, NT, S>;
+    return hipLaunchKernel(k, dim3(s.num_tiles), dim3(W * kWave), kargs, 0, stream);
 }
 
 // S: some array of the call has a row stride other than its row length.
