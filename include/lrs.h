@@ -701,7 +701,7 @@ lrs_status lrs_debug_schedule(lrs_estimator est, int flags, int64_t num_envs, in
  * of `blocks` workgroups of `threads` lanes (64..1024, a multiple of 64): the
  * fixed cost of a launch of that grid.  kind 1: the same grid reading
  * read_bytes from src and then writing write_bytes to dst (device memory,
- * 16-byte aligned, multiples of 16 bytes, at most 128 bytes read per lane),
+ * 16-byte aligned, multiples of 16 bytes, at most 256 bytes read per lane),
  * each lane's stores waiting for its loads: the cost of a call's bytes on its
  * grid without the recurrence.  Asynchronous on `stream`. */
 lrs_status lrs_debug_floor(int kind, int64_t blocks, int threads, const void* src,

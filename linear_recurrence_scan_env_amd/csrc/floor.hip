@@ -4,6 +4,9 @@
 // on the same grid, with no recurrence).  Timed beside a call, they split its
 // duration into the launch floor, the memory traffic and the rest.  Not part
 // of any estimator.
+#include <array>
+#include <utility>
+
 #include "launch.hpp"
 
 namespace lrs {
@@ -46,6 +49,19 @@ hipError_t launch_stream(uint32_t blocks, uint32_t threads, const u32x4* src, ui
                            stream);
 }
 
+// Up to 16 vectors per lane (the time-major grids are small: 64 blocks for
+// 4096 environments of 128 steps).
+constexpr int kMaxVectorsPerLane = 16;
+using StreamLauncher = hipError_t (*)(uint32_t, uint32_t, const u32x4*, uint64_t, u32x4*, uint64_t,
+                                      hipStream_t);
+template <int... I>
+constexpr auto stream_launchers(std::integer_sequence<int, I...>)
+{
+    return std::array<StreamLauncher, sizeof...(I)>{&launch_stream<I + 1>...};
+}
+constexpr auto kStreamLaunchers =
+    stream_launchers(std::make_integer_sequence<int, kMaxVectorsPerLane>{});
+
 }  // namespace
 }  // namespace lrs
 
@@ -76,20 +92,10 @@ extern "C" lrs_status lrs_debug_floor(int kind, int64_t blocks, int threads, con
         const u32x4* s = static_cast<const u32x4*>(src);
         u32x4* d = static_cast<u32x4*>(dst);
         const uint32_t b = (uint32_t)blocks, t = (uint32_t)threads;
-        switch (per_lane) {
-            case 0:
-            case 1: e = launch_stream<1>(b, t, s, n_in, d, n_out, stream); break;
-            case 2: e = launch_stream<2>(b, t, s, n_in, d, n_out, stream); break;
-            case 3: e = launch_stream<3>(b, t, s, n_in, d, n_out, stream); break;
-            case 4: e = launch_stream<4>(b, t, s, n_in, d, n_out, stream); break;
-            case 5: e = launch_stream<5>(b, t, s, n_in, d, n_out, stream); break;
-            case 6: e = launch_stream<6>(b, t, s, n_in, d, n_out, stream); break;
-            case 7: e = launch_stream<7>(b, t, s, n_in, d, n_out, stream); break;
-            case 8: e = launch_stream<8>(b, t, s, n_in, d, n_out, stream); break;
-            default:
-                return fail(LRS_ERR_INVALID_ARG, "%s: at most 8 vectors of 16 bytes read per lane "
-                            "(%llu asked)", nm, (unsigned long long)per_lane);
-        }
+        if (per_lane > (uint64_t)kMaxVectorsPerLane)
+            return fail(LRS_ERR_INVALID_ARG, "%s: at most %d vectors of 16 bytes read per lane "
+                        "(%llu asked)", nm, kMaxVectorsPerLane, (unsigned long long)per_lane);
+        e = kStreamLaunchers[per_lane == 0 ? 0 : per_lane - 1](b, t, s, n_in, d, n_out, stream);
     } else {
         return fail(LRS_ERR_INVALID_ARG, "%s: kind must be 0 (empty) or 1 (stream)", nm);
     }

@@ -252,6 +252,22 @@ def test_debug_schedule_validation(lib):
     assert lib.lrs_debug_set_schedule(0, 0, 0) == 0
 
 
+def test_debug_floor_validation(lib):
+    f = lib.lrs_debug_floor
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    assert f(2, 64, 64, None, 0, None, 0, None) == 1                   # no such kind
+    assert f(0, 0, 64, None, 0, None, 0, None) == 1                    # no blocks
+    assert f(0, 64, 65, None, 0, None, 0, None) == 1                   # not whole waves
+    assert f(0, 64, 2048, None, 0, None, 0, None) == 1                 # block too large
+    assert f(1, 64, 64, FAKE, 24, FAKE, 0, None) == 1                  # not a multiple of 16
+    assert f(1, 64, 64, ctypes.c_void_p(0x10004), 16, FAKE, 0, None) == 1  # misaligned
+    # 64 x 64 lanes read at most 16 vectors of 16 bytes each
+    assert f(1, 64, 64, FAKE, 64 * 64 * 16 * 17, FAKE, 0, None) == 1
+    assert "at most 16 vectors" in lib.lrs_last_error().decode()
+
+
 def test_python_api_has_no_cpu_path():
     import torch
     x = torch.zeros(4, 8)
