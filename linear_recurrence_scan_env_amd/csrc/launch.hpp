@@ -316,15 +316,18 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_num_sgpr(72))) voi
 }
 
 // Look-back launches with four or more waves per block take the capped
-// kernel for maps composed in fp64 and for ops that ask for it (kLeanSgprs):
-// there a block waiting for its carry holds its slot, and more resident
-// blocks keep loads in flight.  Launches without carries keep the uncapped
-// kernel (the capped one measured 1-3% slower there: the spills cost and the
-// loads already saturate).
-template <class Op, int W, class A>
+// kernel for maps composed in fp64, for strided arrays (each array's row gap
+// adds scalar registers: GAE+trunc 72 -> 84, Retrace+trunc 77 -> 93; capped,
+// strided Retrace+trunc at 64 x 131072 went 48.1 -> 37.7 us, GAE+trunc
+// 27.0 -> 25.0, level with contiguous arrays) and for ops that ask for it
+// (kLeanSgprs): there a block waiting for its carry holds its slot, and more
+// resident blocks keep loads in flight.  Launches without carries keep the
+// uncapped kernel (the capped one measured 1-3% slower there: the spills cost
+// and the loads already saturate).
+template <class Op, int W, class A, bool S>
 constexpr bool lean_sgprs()
 {
-    return W >= 4 && (std::is_same<A, double>::value || Op::kLeanSgprs);
+    return W >= 4 && (std::is_same<A, double>::value || Op::kLeanSgprs || S);
 }
 
 // ------------------------------------------------------------ host side
@@ -447,7 +450,7 @@ hipError_t launch_cfg(const typename Op::Args& a, const Sched& s, hipStream_t st
 {
     void* kargs[] = {(void*)&a, (void*)&s};
     const void* k = (const void*)&scan_kernel<Op, E, W, A, NT, S>;
-    if constexpr (lean_sgprs<Op, W, A>())
+    if constexpr (lean_sgprs<Op, W, A, S>())
         if (s.lookback) k = (const void*)&scan_kernel_lean<Op, E, W, A, NT, S>;
     return hipLaunchKernel(k, dim3(s.num_tiles), dim3(W * kWave), kargs, 0, stream);
 }
