@@ -58,6 +58,15 @@ enum LookbackTile { kLbNarrow, kLbLight, kLbWide4 };
 // they spill a few to vector lanes and run 2-3% faster on long rows.  Maps
 // composed in fp64 are capped for every op (the fp32 prefix sum at 64 x 131072:
 // one block per CU instead of two, 22.9 -> 19.0 us).
+// kLeanTm: the op's time-major kernels with 16 steps per lane take a twin
+// capped for eight waves per SIMD (64 VGPRs and 72 SGPRs) on grids larger
+// than the CU count, for contiguous arrays.  Only where they fit without
+// spills: discounted returns and traces with maps composed in fp32
+// (kLeanTmFp32), the prefix sums with either composition (kLeanTmAny).  At
+// 4096 x 2048: discounted 21.5 -> 19.0 us, traces 21.5 -> 19.5, fp32 prefix
+// sum 22.1 -> 19.3.  GAE, TD(lambda), V-trace and Retrace spill under the
+// caps and ran 7% to 2.3x slower.
+enum LeanTm { kLeanTmNo, kLeanTmFp32, kLeanTmAny };
 
 // Value of stream p at flat index i0+E (element 0 of the next chunk).  Full
 // tiles load it in every lane (same cache line as the neighbouring chunk's
@@ -239,6 +248,7 @@ struct GaeOp {
     static constexpr LookbackTile kLookbackTile = kLbNarrow;
     static constexpr bool kStreamLoads = true;
     static constexpr bool kLeanSgprs = false;
+    static constexpr LeanTm kLeanTm = kLeanTmNo;
     struct State {
         uint32_t end;
     };
@@ -299,6 +309,7 @@ struct LambdaOp {
     // non-temporal input loads measure slower for this op on long rows
     static constexpr bool kStreamLoads = false;
     static constexpr bool kLeanSgprs = false;
+    static constexpr LeanTm kLeanTm = kLeanTmNo;
     struct State {
         uint32_t end;
     };
@@ -355,6 +366,7 @@ struct DiscOp {
     static constexpr LookbackTile kLookbackTile = kLbLight;
     static constexpr bool kStreamLoads = true;
     static constexpr bool kLeanSgprs = false;
+    static constexpr LeanTm kLeanTm = kLeanTmFp32;
     struct State {
         uint32_t end;
     };
@@ -415,6 +427,7 @@ struct VtraceOp {
     static constexpr LookbackTile kLookbackTile = kLbNarrow;
     static constexpr bool kStreamLoads = true;
     static constexpr bool kLeanSgprs = true;
+    static constexpr LeanTm kLeanTm = kLeanTmNo;
     struct State {
         uint32_t end;
         float r[E], v[E], tgt[E], rho_pg[E];  // tgt: Vnext at ends, V_{t+1} elsewhere
@@ -496,6 +509,7 @@ struct RetraceOp {
     static constexpr LookbackTile kLookbackTile = kLbWide4;
     static constexpr bool kStreamLoads = true;
     static constexpr bool kLeanSgprs = false;
+    static constexpr LeanTm kLeanTm = kLeanTmNo;
     struct State {
         uint32_t end;
     };
@@ -616,6 +630,7 @@ struct EligOp {
     static constexpr LookbackTile kLookbackTile = kLbLight;
     static constexpr bool kStreamLoads = true;
     static constexpr bool kLeanSgprs = false;
+    static constexpr LeanTm kLeanTm = kLeanTmFp32;
     struct State {
         uint32_t reset;
     };
@@ -657,6 +672,7 @@ struct PrefixF32Op {
     static constexpr LookbackTile kLookbackTile = kLbLight;
     static constexpr bool kStreamLoads = true;
     static constexpr bool kLeanSgprs = false;
+    static constexpr LeanTm kLeanTm = kLeanTmAny;
     struct State {
         uint32_t reset;
     };
@@ -698,6 +714,7 @@ struct PrefixI32Op {
     static constexpr LookbackTile kLookbackTile = kLbLight;
     static constexpr bool kStreamLoads = true;
     static constexpr bool kLeanSgprs = false;
+    static constexpr LeanTm kLeanTm = kLeanTmAny;
     struct State {
         uint32_t reset;
     };
@@ -755,6 +772,7 @@ struct AffineOp {
     static constexpr LookbackTile kLookbackTile = kLbWide4;
     static constexpr bool kStreamLoads = true;
     static constexpr bool kLeanSgprs = false;
+    static constexpr LeanTm kLeanTm = kLeanTmNo;
     struct State {
         uint32_t cut;
     };

@@ -445,6 +445,25 @@ constexpr int kWideCfg = 6;                          // 8x16: 8192-element tiles
 
 inline bool aligned(const void* p, uintptr_t a) { return p == nullptr || ((uintptr_t)p % a) == 0; }
 
+// Compute units of the device that `stream` belongs to, queried once per
+// device (256 on MI355X; also the answer if the query fails).
+inline uint32_t device_cus(hipStream_t stream)
+{
+    constexpr int kMaxDevices = 64;
+    static std::atomic<uint32_t> cache[kMaxDevices];
+    int dev = 0;
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    uint32_t n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            v = 256;
+        n = (uint32_t)v;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 template <class Op, int E, int W, class A, bool S, bool NT = false>
 hipError_t launch_cfg(const typename Op::Args& a, const Sched& s, hipStream_t stream)
 {

@@ -266,8 +266,7 @@ __device__ __forceinline__ void tile_body_tm(const typename Op::Args& args, cons
 }
 
 template <class Op, int E, int W, class A, bool S>
-__global__ __launch_bounds__(W * kWave) void scan_kernel_tm(const typename Op::Args args,
-                                                            const SchedTM s)
+__device__ __forceinline__ void scan_body_tm(const typename Op::Args& args, const SchedTM& s)
 {
     warm_kernargs<kernarg_bytes<typename Op::Args, SchedTM>()>();
     constexpr uint32_t kSteps = (uint32_t)E * W;
@@ -359,6 +358,26 @@ __device__ __forceinline__ void rows_body_tm(const typename Op::Args& args, cons
     Op::finish(args, P, c, alpha, beta, st, lane_in);
 }
 
+template <class Op, int E, int W, class A, bool S>
+__global__ __launch_bounds__(W * kWave) void scan_kernel_tm(const typename Op::Args args,
+                                                            const SchedTM s)
+{
+    scan_body_tm<Op, E, W, A, S>(args, s);
+}
+
+// The same kernel capped for eight waves per SIMD (64 VGPRs, 72 SGPRs): two
+// 16-wave blocks per CU instead of one.  The uncapped 16-step kernels hold
+// 64-74 VGPRs and 95-106 SGPRs; calls that fit the caps without spilling
+// take this twin on grids larger than the CU count (kLeanTm).
+template <class Op, int E, int W, class A, bool S>
+__global__ __launch_bounds__(W * kWave)
+__attribute__((amdgpu_num_sgpr(72), amdgpu_waves_per_eu(8, 8))) void scan_kernel_tm_lean(
+    const typename Op::Args args, const SchedTM s)
+{
+    scan_body_tm<Op, E, W, A, S>(args, s);
+}
+
+
 template <class Op, int E, int W, int V, class A, bool S>
 __global__ __launch_bounds__(W * kWave) void scan_kernel_tm_rows(const typename Op::Args args,
                                                                  const SchedTM s)
@@ -444,6 +463,13 @@ hipError_t launch_tm(bool strided, const typename Op<kTmE>::Args& a, const Sched
     void* params[] = {(void*)&a, (void*)&s};
     const void* k = strided ? (const void*)&scan_kernel_tm<Op<E>, E, W, A, true>
                             : (const void*)&scan_kernel_tm<Op<E>, E, W, A, false>;
+    constexpr LeanTm kLean = Op<E>::kLeanTm;
+    constexpr bool kLeanOk = kLean == kLeanTmAny ||
+                             (kLean == kLeanTmFp32 && !std::is_same<A, double>::value);
+    if constexpr (kLeanOk && E == kTmELong && W == 16) {
+        if (!strided && s.num_blocks > device_cus(stream))
+            k = (const void*)&scan_kernel_tm_lean<Op<E>, E, W, A, false>;
+    }
     return hipLaunchKernel(k, dim3(s.num_blocks), dim3(W * kWave), params, 0, stream);
 }
 
