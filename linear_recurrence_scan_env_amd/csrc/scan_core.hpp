@@ -447,7 +447,23 @@ __device__ __forceinline__ uint32_t load_mask(Strided<const uint8_t> a, const Po
 }
 
 // Outputs are written once and not read again by this launch: full-tile
-// stores are non-temporal (streamed past the caches).
+// stores are non-temporal (streamed past the caches), and so are the
+// element-wise stores of time-major tiles, whose wave stores cover 64
+// consecutive environments of one time step (4096 environments x 2048 steps:
+// a plain load/store kernel of that tiling took 17.4 us with plain stores,
+// 15.8 with non-temporal ones).
+template <bool NTS, class D>
+__device__ __forceinline__ void put(D* p, D v)
+{
+    if constexpr (!NTS) {
+        *p = v;
+    } else if constexpr (std::is_arithmetic<D>::value) {
+        __builtin_nontemporal_store(v, p);
+    } else {
+        static_assert(sizeof(D) == 2, "16-bit storage types");
+        __builtin_nontemporal_store(v.bits, reinterpret_cast<uint16_t*>(p));
+    }
+}
 
 template <int E, bool kFull, bool TM, bool NT, bool S, class D>
 __device__ __forceinline__ void store_f32(Strided<D> a, const float (&v)[E],
@@ -475,7 +491,7 @@ __device__ __forceinline__ void store_f32(Strided<D> a, const float (&v)[E],
     } else {
 #pragma unroll
         for (int j = 0; j < E; ++j)
-            if (kFull || j < P.count) p[elem_offset(P, j, a.gap)] = from_f32<D>(v[j]);
+            if (kFull || j < P.count) put<TM>(p + elem_offset(P, j, a.gap), from_f32<D>(v[j]));
     }
 }
 
@@ -493,7 +509,7 @@ __device__ __forceinline__ void store_u32(Strided<int32_t> a, const uint32_t (&v
     } else {
 #pragma unroll
         for (int j = 0; j < E; ++j)
-            if (kFull || j < P.count) p[elem_offset(P, j, a.gap)] = (int32_t)v[j];
+            if (kFull || j < P.count) put<TM>(p + elem_offset(P, j, a.gap), (int32_t)v[j]);
     }
 }
 
