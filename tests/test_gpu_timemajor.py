@@ -111,9 +111,10 @@ def check(pairs, T, tol=None):
 
 
 # (num_envs, seq_len): ragged env groups (not multiples of 64) and ragged
-# 128-step tiles, one and many tiles along time
+# 128-step tiles, one and many tiles along time; a last group of 2 (130) or
+# 1 (257) environments on rows of several 256-step tiles
 SHAPES = [(1, 1), (3, 5), (64, 128), (65, 129), (63, 127), (130, 300), (7, 1000), (200, 257),
-          (1, 2048), (33, 4097)]
+          (257, 1000), (1, 2048), (33, 4097)]
 
 
 @pytest.mark.parametrize("est", ESTIMATORS)
