@@ -668,7 +668,7 @@ typedef struct lrs_schedule_info {
     int64_t tile_elems;       /* row-major: elements per tile                      */
     int64_t tile_steps;       /* time-major: steps per tile                        */
     int64_t groups;           /* time-major: environment groups (blocks per time tile) */
-    int64_t envs_per_group;   /* time-major: environments per block (64 or 32)     */
+    int64_t envs_per_group;   /* time-major: environments per block (128, 64 or 32) */
     int32_t time_major;
     int32_t carries;          /* tiles exchange carries (look-back / time tiles > 1) */
     int32_t backward;         /* the scan runs from the end of each row            */

@@ -101,7 +101,7 @@ lrs_status describe(bool tm, int64_t N, int64_t T, float beta_max, lrs_schedule_
     info->num_tiles = (int64_t)p.s.time_tiles * p.s.groups;
     info->tile_steps = (int64_t)p.tile_steps;
     info->groups = p.s.groups;
-    info->envs_per_group = p.rows_waves ? kTmRowsV : kWave;
+    info->envs_per_group = p.rows_waves ? kTmRowsV : kWave * p.G;
     info->carries = p.s.time_tiles > 1 ? 1 : 0;
     info->elems_per_lane = p.rows_waves ? kTmE : (p.long_rows ? kTmELong : kTmE);
     info->waves_per_block = p.W;

@@ -351,6 +351,20 @@ __device__ __forceinline__ V ld_vec(const S* p)
     }
 }
 
+// One element; non-temporal for time-major tiles with NT set.
+template <bool NTL, class D>
+__device__ __forceinline__ D get(const D* p)
+{
+    if constexpr (!NTL) {
+        return *p;
+    } else if constexpr (std::is_arithmetic<D>::value) {
+        return __builtin_nontemporal_load(p);
+    } else {
+        static_assert(sizeof(D) == 2, "16-bit storage types");
+        return D{__builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p))};
+    }
+}
+
 template <int E, bool kFull, bool TM, bool NT, bool S, class D>
 __device__ __forceinline__ void load_f32(float (&v)[E], Strided<const D> a,
                                          const Pos<E, kFull, TM, NT, S>& P, bool vec)
@@ -384,7 +398,7 @@ __device__ __forceinline__ void load_f32(float (&v)[E], Strided<const D> a,
     } else {
 #pragma unroll
         for (int j = 0; j < E; ++j)
-            v[j] = (kFull || j < P.count) ? to_f32(p[elem_offset(P, j, a.gap)]) : 0.0f;
+            v[j] = (kFull || j < P.count) ? to_f32(get<TM && NT>(p + elem_offset(P, j, a.gap))) : 0.0f;
     }
 }
 
@@ -406,7 +420,7 @@ __device__ __forceinline__ void load_u32(uint32_t (&v)[E], Strided<const int32_t
     } else {
 #pragma unroll
         for (int j = 0; j < E; ++j)
-            v[j] = (kFull || j < P.count) ? (uint32_t)p[elem_offset(P, j, a.gap)] : 0u;
+            v[j] = (kFull || j < P.count) ? (uint32_t)get<TM && NT>(p + elem_offset(P, j, a.gap)) : 0u;
     }
 }
 
@@ -442,7 +456,7 @@ __device__ __forceinline__ uint32_t load_mask(Strided<const uint8_t> a, const Po
     uint32_t bits = 0;
 #pragma unroll
     for (int j = 0; j < E; ++j)
-        if ((kFull || j < P.count) && p[elem_offset(P, j, a.gap)] != 0) bits |= 1u << j;
+        if ((kFull || j < P.count) && get<TM && NT>(p + elem_offset(P, j, a.gap)) != 0) bits |= 1u << j;
     return bits;
 }
 

@@ -82,33 +82,44 @@ __host__ __device__ inline TilePlaceTM place_tile_tm(uint32_t b, const SchedTM& 
     return {backward ? s.time_tiles - 1u - pos : pos, g};
 }
 
-template <class A, int W>
+// G groups of 64 environments per block; per group W / G waves along time.
+// Environment (group q, lane l) at column q * 64 + l.
+template <class A, int W, int G>
 struct BlockSharedTM {
-    A a[W][kWave];
-    A b[W][kWave];
-    RecOf<A> win_a[kWindowTM<W>][kWave];  // aggregates gathered by the look-back
-    RecOf<A> win_b[kWindowTM<W>][kWave];
-    RecOf<A> carry[kWave];
+    A a[W / G][kWave * G];
+    A b[W / G][kWave * G];
+    RecOf<A> win_a[kWindowTM<W>][kWave * G];  // aggregates gathered by the look-back
+    RecOf<A> win_b[kWindowTM<W>][kWave * G];
+    RecOf<A> carry[kWave * G];
 };
 
-// One tile.  F: every lane of the block is an environment and every one of
-// its steps exists (unconditional accesses); otherwise accesses are guarded.
-template <class Op, int E, int W, class A, bool F, bool S>
+// One tile: 64 G environments x E W / G steps.  Wave w works on environment
+// group w % G and on the E steps w / G of the tile, so the G waves of a time
+// step read G adjacent 256-byte runs of each time row together (4096 x 2048:
+// a load/store kernel on 128 x 128-step tiles of two groups took 14.3 us,
+// on 64 x 256-step tiles of one group 15.9).  F: every environment of the
+// block and every step of the tile exist (unconditional accesses); otherwise
+// accesses are guarded.
+template <class Op, int E, int W, int G, class A, bool F, bool S>
 __device__ __forceinline__ void tile_body_tm(const typename Op::Args& args, const SchedTM& s,
-                                             uint32_t k, uint32_t g, BlockSharedTM<A, W>& sh)
+                                             uint32_t k, uint32_t g, BlockSharedTM<A, W, G>& sh)
 {
     using T = typename Op::T;
     using R = RecOf<A>;
     constexpr bool kB = Op::kBackward;
-    constexpr uint32_t kSteps = (uint32_t)E * W;
-    constexpr int kNear = kB ? 0 : W - 1;  // the wave holding the tile's near edge
+    constexpr int kWavesT = W / G;  // waves along time
+    constexpr uint32_t kSteps = (uint32_t)E * kWavesT;
+    constexpr int kNear = kB ? 0 : kWavesT - 1;  // the time wave holding the tile's near edge
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    const uint32_t n = g * kWave + lane;
+    const int grp = wave % G;
+    const int tw = wave / G;
+    const int col_l = grp * kWave + lane;  // the environment's column in the shared arrays
+    const uint32_t n = (g * G + (uint32_t)grp) * kWave + lane;
     const bool active = n < s.N;
-    const uint32_t t0 = k * kSteps + (uint32_t)wave * E;
+    const uint32_t t0 = k * kSteps + (uint32_t)tw * E;
 
     int count = 0;
     uint32_t last = 0, first = 0;
@@ -118,7 +129,9 @@ __device__ __forceinline__ void tile_body_tm(const typename Op::Args& args, cons
         if (t0 == 0) first = 1u;
     }
     const uint32_t col = active ? n : 0u;  // inactive lanes touch nothing (count = 0)
-    const Pos<E, F, true, false, S> P{(uint64_t)t0 * s.N + col, col, count, last, first, s.N, t0};
+    // Several groups per block read non-temporally (measured faster there,
+    // slower with one group).
+    const Pos<E, F, true, (G > 1), S> P{(uint64_t)t0 * s.N + col, col, count, last, first, s.N, t0};
     const Ctx c{(uint64_t)s.N * s.T, s.T, lane, false};
 
     // The launch tag is read first, in flight with the tile's loads.  These
@@ -127,7 +140,7 @@ __device__ __forceinline__ void tile_body_tm(const typename Op::Args& args, cons
     // row-major kernel does; both keep the same header state between
     // launches).
     WsHeader* hdr = reinterpret_cast<WsHeader*>(s.ws);
-    const bool carries = wave == kNear && s.time_tiles > 1;
+    const bool carries = tw == kNear && s.time_tiles > 1;
     uint32_t tag = 0;
     if (carries)
         tag = __builtin_amdgcn_readfirstlane(
@@ -158,17 +171,18 @@ __device__ __forceinline__ void tile_body_tm(const typename Op::Args& args, cons
         for (int j = 0; j < E; ++j) x = combine(Aff<A>{A(alpha[j]), A(beta[j])}, x);
     }
     if constexpr (W > 1) {
-        sh.a[wave][lane] = x.a;
-        sh.b[wave][lane] = x.b;
+        sh.a[tw][col_l] = x.a;
+        sh.b[tw][col_l] = x.b;
         __syncthreads();
     }
 
-    // Waves between this one and the tile's far edge, nearest first.
+    // The group's waves between this one and the tile's far edge, nearest
+    // first.
     Aff<A> beyond = identity<A>();
 #pragma unroll
-    for (int d = 1; d < W; ++d) {
-        const int w = kB ? wave + d : wave - d;
-        if (w >= 0 && w < W) beyond = combine(beyond, Aff<A>{sh.a[w][lane], sh.b[w][lane]});
+    for (int d = 1; d < kWavesT; ++d) {
+        const int w = kB ? tw + d : tw - d;
+        if (w >= 0 && w < kWavesT) beyond = combine(beyond, Aff<A>{sh.a[w][col_l], sh.b[w][col_l]});
     }
 
     R carry = R(0);
@@ -224,8 +238,8 @@ __device__ __forceinline__ void tile_body_tm(const typename Op::Args& args, cons
                             base = a;
                             done = true;
                         } else {
-                            sh.win_a[depth][lane] = a;
-                            sh.win_b[depth][lane] = b;
+                            sh.win_a[depth][col_l] = a;
+                            sh.win_b[depth][col_l] = b;
                             ++depth;
                             j += step;
                         }
@@ -243,7 +257,7 @@ __device__ __forceinline__ void tile_body_tm(const typename Op::Args& args, cons
             }
             carry = base;
             for (int d = depth - 1; d >= 0; --d)
-                carry = apply(Aff<R>{sh.win_a[d][lane], sh.win_b[d][lane]}, carry);
+                carry = apply(Aff<R>{sh.win_a[d][col_l], sh.win_b[d][col_l]}, carry);
             // a wait that gave up leaves every lane of the tile without its
             // carry: NaN for fp32 maps (0 for the integer prefix sum)
             if (gave_up) carry = give_up_carry<R>();
@@ -252,32 +266,34 @@ __device__ __forceinline__ void tile_body_tm(const typename Op::Args& args, cons
         }
     }
     if constexpr (W > 1) {
-        if (wave == kNear) sh.carry[lane] = carry;
+        if (tw == kNear) sh.carry[col_l] = carry;
         __syncthreads();
-        carry = sh.carry[lane];
+        carry = sh.carry[col_l];
     }
 
     const T lane_in = T(apply(beyond, A(carry)));
     Op::finish(args, P, c, alpha, beta, st, lane_in);
-    if (carries && lane == 0) {
+    // One wave counts the block, after the barrier above, which every wave
+    // reaches after reading its tag.
+    if (carries && grp == 0 && lane == 0) {
         const uint64_t entry = count_block(hdr, blockIdx.x);
         close_launch(hdr, count_group(hdr, entry, s.num_blocks, blockIdx.x), s.num_blocks, tag);
     }
 }
 
-template <class Op, int E, int W, class A, bool S>
+template <class Op, int E, int W, int G, class A, bool S>
 __device__ __forceinline__ void scan_body_tm(const typename Op::Args& args, const SchedTM& s)
 {
     warm_kernargs<kernarg_bytes<typename Op::Args, SchedTM>()>();
-    constexpr uint32_t kSteps = (uint32_t)E * W;
-    __shared__ BlockSharedTM<A, W> sh;
+    constexpr uint32_t kSteps = (uint32_t)E * (W / G);
+    __shared__ BlockSharedTM<A, W, G> sh;
     const TilePlaceTM tp = place_tile_tm(blockIdx.x, s, Op::kBackward);
     const uint32_t k = tp.k, g = tp.g;
-    const bool full = (uint64_t)(k + 1u) * kSteps <= s.T && (uint64_t)(g + 1u) * kWave <= s.N;
+    const bool full = (uint64_t)(k + 1u) * kSteps <= s.T && (uint64_t)(g + 1u) * kWave * G <= s.N;
     if (full)
-        tile_body_tm<Op, E, W, A, true, S>(args, s, k, g, sh);
+        tile_body_tm<Op, E, W, G, A, true, S>(args, s, k, g, sh);
     else
-        tile_body_tm<Op, E, W, A, false, S>(args, s, k, g, sh);
+        tile_body_tm<Op, E, W, G, A, false, S>(args, s, k, g, sh);
 }
 
 // Rows that fit one tile, on few environments: V environments per block
@@ -358,23 +374,23 @@ __device__ __forceinline__ void rows_body_tm(const typename Op::Args& args, cons
     Op::finish(args, P, c, alpha, beta, st, lane_in);
 }
 
-template <class Op, int E, int W, class A, bool S>
+template <class Op, int E, int W, int G, class A, bool S>
 __global__ __launch_bounds__(W * kWave) void scan_kernel_tm(const typename Op::Args args,
                                                             const SchedTM s)
 {
-    scan_body_tm<Op, E, W, A, S>(args, s);
+    scan_body_tm<Op, E, W, G, A, S>(args, s);
 }
 
 // The same kernel capped for eight waves per SIMD (64 VGPRs, 72 SGPRs): two
 // 16-wave blocks per CU instead of one.  The uncapped 16-step kernels hold
 // 64-74 VGPRs and 95-106 SGPRs; calls that fit the caps without spilling
 // take this twin on grids larger than the CU count (kLeanTm).
-template <class Op, int E, int W, class A, bool S>
+template <class Op, int E, int W, int G, class A, bool S>
 __global__ __launch_bounds__(W * kWave)
 __attribute__((amdgpu_num_sgpr(72), amdgpu_waves_per_eu(8, 8))) void scan_kernel_tm_lean(
     const typename Op::Args args, const SchedTM s)
 {
-    scan_body_tm<Op, E, W, A, S>(args, s);
+    scan_body_tm<Op, E, W, G, A, S>(args, s);
 }
 
 
@@ -403,6 +419,18 @@ constexpr int kTmE = 8;        // steps per lane
 constexpr int kTmELong = 16;
 constexpr uint64_t kTmLongRow = 128;
 constexpr int kTmWSmall = 8;   // waves per block: 64-step tiles
+// Long rows on many environments take two groups of 64 per block (128
+// environments x 128 steps: twice the time tiles of one group's 256-step
+// tiles, and adjacent 256-byte runs per row read together).  Measured against
+// one group: 1-13% faster at 4096 x 1024, 4096 x 2048, 8192 x 1024,
+// 8192 x 2048 and 16384 x 512; at 4096 x 8192 5-11% faster for the calls of
+// three or more streams, the others within 1%; slower with fewer
+// environments (2048 x 2048: +2-11%, 256 x 32768: +11-23%) and on rows of
+// 256 steps (4096 x 256: +7-22%), which one group holds in a single tile.
+inline bool tm_two_groups(uint64_t N, uint64_t T)
+{
+    return (N >= 4096 && T >= 1024) || (N >= 8192 && T >= 512);
+}
 constexpr int kTmWLarge = 16;  // 128-step tiles
 
 inline uint64_t tm_tiles(uint64_t T, int W) { return (T + (uint64_t)kTmE * W - 1) / ((uint64_t)kTmE * W); }
@@ -456,19 +484,19 @@ inline size_t workspace_bytes_tm(uint64_t N, uint64_t T)
     return sizeof(WsHeader) + 8 * kPlanesTM * N * tm_tiles(T, w);
 }
 
-template <template <int> class Op, int E, int W, class A>
+template <template <int> class Op, int E, int W, int G, class A>
 hipError_t launch_tm(bool strided, const typename Op<kTmE>::Args& a, const SchedTM& s,
                      hipStream_t stream)
 {
     void* params[] = {(void*)&a, (void*)&s};
-    const void* k = strided ? (const void*)&scan_kernel_tm<Op<E>, E, W, A, true>
-                            : (const void*)&scan_kernel_tm<Op<E>, E, W, A, false>;
+    const void* k = strided ? (const void*)&scan_kernel_tm<Op<E>, E, W, G, A, true>
+                            : (const void*)&scan_kernel_tm<Op<E>, E, W, G, A, false>;
     constexpr LeanTm kLean = Op<E>::kLeanTm;
     constexpr bool kLeanOk = kLean == kLeanTmAny ||
                              (kLean == kLeanTmFp32 && !std::is_same<A, double>::value);
     if constexpr (kLeanOk && E == kTmELong && W == 16) {
         if (!strided && s.num_blocks > device_cus(stream))
-            k = (const void*)&scan_kernel_tm_lean<Op<E>, E, W, A, false>;
+            k = (const void*)&scan_kernel_tm_lean<Op<E>, E, W, G, A, false>;
     }
     return hipLaunchKernel(k, dim3(s.num_blocks), dim3(W * kWave), params, 0, stream);
 }
@@ -495,16 +523,16 @@ hipError_t launch_tm_rows_acc(float beta_max, bool strided, const typename Op<kT
         return launch_tm_rows<Op, W, V, Val>(strided, a, s, stream);
 }
 
-template <template <int> class Op, int W, int E = kTmE>
+template <template <int> class Op, int W, int E = kTmE, int G = 1>
 hipError_t launch_tm_acc(float beta_max, bool strided, const typename Op<kTmE>::Args& a,
                          const SchedTM& s, hipStream_t stream)
 {
     using Val = typename Op<kTmE>::T;
     if constexpr (std::is_same<Val, float>::value)
-        return beta_max > kFp32BetaMax ? launch_tm<Op, E, W, double>(strided, a, s, stream)
-                                       : launch_tm<Op, E, W, float>(strided, a, s, stream);
+        return beta_max > kFp32BetaMax ? launch_tm<Op, E, W, G, double>(strided, a, s, stream)
+                                       : launch_tm<Op, E, W, G, float>(strided, a, s, stream);
     else
-        return launch_tm<Op, E, W, Val>(strided, a, s, stream);
+        return launch_tm<Op, E, W, G, Val>(strided, a, s, stream);
 }
 
 // The schedule of a time-major call: narrow whole-row blocks (rows_waves > 0
@@ -515,6 +543,7 @@ struct PlanTM {
     int rows_waves;
     int W;
     bool long_rows;
+    int G;  // environment groups of 64 per block of the wide kernel
     uint64_t tile_steps;
     SchedTM s;
 };
@@ -526,6 +555,7 @@ inline PlanTM plan_time_major(int64_t N, int64_t T)
     p.s.T = (uint32_t)T;
     p.s.ws = nullptr;
     p.rows_waves = tm_rows_waves((uint64_t)N, (uint64_t)T);
+    p.G = 1;
     if (p.rows_waves) {
         p.W = p.rows_waves;
         p.tile_steps = (uint64_t)T;
@@ -536,8 +566,9 @@ inline PlanTM plan_time_major(int64_t N, int64_t T)
     }
     p.W = tm_waves((uint64_t)T);
     p.long_rows = g_forced_tm_waves.load() == 0 && (uint64_t)T > kTmLongRow;
-    p.s.groups = (uint32_t)((N + kWave - 1) / kWave);
-    p.tile_steps = (uint64_t)(p.long_rows ? kTmELong : kTmE) * p.W;
+    if (p.long_rows && tm_two_groups((uint64_t)N, (uint64_t)T)) p.G = 2;
+    p.s.groups = (uint32_t)((N + (int64_t)kWave * p.G - 1) / ((int64_t)kWave * p.G));
+    p.tile_steps = (uint64_t)(p.long_rows ? kTmELong : kTmE) * (uint64_t)(p.W / p.G);
     p.s.time_tiles = (uint32_t)(((uint64_t)T + p.tile_steps - 1) / p.tile_steps);
     p.s.num_blocks = p.s.groups * p.s.time_tiles;
     return p;
@@ -589,7 +620,9 @@ lrs_status run_tm(const char* name, int64_t N, int64_t T, float beta_max,
         if (!aligned(ws, 16)) return fail(LRS_ERR_WORKSPACE, "%s: workspace not 16-byte aligned", name);
     }
     hipError_t e;
-    if (long_rows) {
+    if (long_rows && plan.G == 2) {
+        e = launch_tm_acc<Op, kTmWLarge, kTmELong, 2>(beta_max, strided, a, s, stream);
+    } else if (long_rows) {
         e = launch_tm_acc<Op, kTmWLarge, kTmELong>(beta_max, strided, a, s, stream);
     } else switch (W) {
         case 2: e = launch_tm_acc<Op, 2>(beta_max, strided, a, s, stream); break;

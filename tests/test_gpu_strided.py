@@ -235,7 +235,7 @@ def test_row_major_views_forced_lookback(est, tile):
 
 @pytest.mark.parametrize("est", ESTIMATORS)
 @pytest.mark.parametrize("pads", ["vector", "odd"])
-@pytest.mark.parametrize("shape", [(100, 1000), (4099, 33), (64, 300)],
+@pytest.mark.parametrize("shape", [(100, 1000), (4099, 33), (64, 300), (4100, 1030)],
                          ids=lambda s: f"{s[0]}x{s[1]}")
 def test_time_major_views(est, pads, shape):
     n, t = shape

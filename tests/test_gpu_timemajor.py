@@ -143,6 +143,19 @@ def test_automatic_tile_boundaries(shape, est):
 
 
 @pytest.mark.parametrize("est", ESTIMATORS)
+@pytest.mark.parametrize("shape", [(4096, 1024), (4100, 1030), (8200, 520)],
+                         ids=lambda s: f"{s[0]}x{s[1]}")
+def test_two_groups_per_block(shape, est):
+    """Long rows on many environments: blocks of two 64-environment groups
+    on 128-step tiles, exact (4096 x 1024) and with a last block of 4
+    environments and a ragged last tile (4100 x 1030, 8200 x 520)."""
+    N, T = shape
+    ro = workloads.rollout(N, T, seed=N + 5 * T, term_p=0.01, trunc_p=0.01, gamma=0.97,
+                           lambda_=0.9)
+    check(run_tm(est, ro), T)
+
+
+@pytest.mark.parametrize("est", ESTIMATORS)
 @pytest.mark.parametrize("shape", NARROW_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
 def test_narrow_whole_row_blocks(shape, est):
     """Automatic choice on rows of up to 128 steps and few environments: the

@@ -168,7 +168,7 @@ def test_time_major_schedules(lib, waves):
         any_carry = False
         for est, flags in CALLS:
             for n, t in [(1, 1), (64, 131072), (4096, 128), (4096, 2048), (100, 1000), (4099, 33),
-                         (7, 300000)]:
+                         (7, 300000), (8200, 1030)]:
                 info, waits = check_call(lib, est, flags | TIME_MAJOR, n, t, 0.95)
                 any_carry = any_carry or bool(info.carries and waits)
         assert any_carry
@@ -194,6 +194,14 @@ def test_schedule_info_matches_plan(lib):
     assert (info.carries, info.envs_per_group, info.groups) == (0, 32, 128)
     info, _ = schedule(lib, GAE, TIME_MAJOR, 64, 131072, 0.9)
     assert (info.carries, info.tile_steps, info.groups) == (1, 256, 1)
+    # many environments: two groups of 64 per block, 128-step tiles
+    info, _ = schedule(lib, GAE, TIME_MAJOR, 4096, 2048, 0.9)
+    assert (info.envs_per_group, info.tile_steps, info.groups, info.waves_per_block) == (128, 128, 32, 16)
+    info, _ = schedule(lib, GAE, TIME_MAJOR, 8192, 512, 0.9)
+    assert (info.envs_per_group, info.tile_steps) == (128, 128)
+    for n, t in [(4096, 512), (2048, 8192), (4096, 256)]:
+        info, _ = schedule(lib, GAE, TIME_MAJOR, n, t, 0.9)
+        assert (info.envs_per_group, info.tile_steps) == (64, 256), (n, t)
     assert lib.lrs_debug_schedule(99, 0, 4, 4, 0.5, ctypes.byref(info), None, 0) == 1
     assert lib.lrs_debug_schedule(GAE, REVERSE, 4, 4, 0.5, ctypes.byref(info), None, 0) == 1
     assert lib.lrs_debug_schedule(PREFIX_I32, HALF, 4, 4, 0.5, ctypes.byref(info), None, 0) == 1
