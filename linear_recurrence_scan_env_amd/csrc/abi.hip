@@ -95,7 +95,7 @@ lrs_status describe(bool tm, int64_t N, int64_t T, float beta_max, lrs_schedule_
     }
     if (N >= (int64_t(1) << 32))
         return fail(LRS_ERR_INVALID_ARG, "lrs_debug_schedule: time-major calls need num_envs < 2^32");
-    const PlanTM p = plan_time_major(N, T);
+    const PlanTM p = plan_time_major(N, T, tm_lean_capable<Op>(beta_max));
     using Val = typename Op<4>::T;
     info->num_blocks = p.s.num_blocks;
     info->num_tiles = (int64_t)p.s.time_tiles * p.s.groups;

@@ -548,7 +548,31 @@ struct PlanTM {
     SchedTM s;
 };
 
-inline PlanTM plan_time_major(int64_t N, int64_t T)
+// Calls whose kernels fit the capped twin (kLeanTm, with maps composed in
+// fp32 where that matters).  The others hold 71-128 VGPRs: one block per CU.
+template <template <int> class Op>
+inline bool tm_lean_capable(float beta_max)
+{
+    constexpr LeanTm kLean = Op<kTmE>::kLeanTm;
+    using Val = typename Op<kTmE>::T;
+    const bool fp64 = std::is_same<Val, float>::value && beta_max > kFp32BetaMax;
+    return kLean == kLeanTmAny || (kLean == kLeanTmFp32 && !fp64);
+}
+
+// Long rows whose 256-step tiles would make fewer blocks than the device's
+// 256 CUs.  The calls that run one block per CU then take 128-step tiles
+// (8 steps per lane): twice the blocks (V-trace, Retrace and GAE with
+// truncations 5-23% faster at 4096 x 256, 4096 x 512, 2048 x 512 and
+// 1024 x 1024; GAE and TD(lambda) within 2% or faster).  The others keep
+// 256-step tiles (up to 19% faster than 128-step ones there).
+constexpr uint64_t kTmFewBlocks = 256;
+inline bool tm_few_blocks(uint64_t N, uint64_t T)
+{
+    const uint64_t tiles = (T + (uint64_t)kTmELong * kTmWLarge - 1) / ((uint64_t)kTmELong * kTmWLarge);
+    return (N + kWave - 1) / kWave * tiles < kTmFewBlocks;
+}
+
+inline PlanTM plan_time_major(int64_t N, int64_t T, bool lean_capable)
 {
     PlanTM p{};
     p.s.N = (uint32_t)N;
@@ -566,7 +590,10 @@ inline PlanTM plan_time_major(int64_t N, int64_t T)
     }
     p.W = tm_waves((uint64_t)T);
     p.long_rows = g_forced_tm_waves.load() == 0 && (uint64_t)T > kTmLongRow;
-    if (p.long_rows && tm_two_groups((uint64_t)N, (uint64_t)T)) p.G = 2;
+    if (p.long_rows && tm_two_groups((uint64_t)N, (uint64_t)T))
+        p.G = 2;
+    else if (p.long_rows && !lean_capable && tm_few_blocks((uint64_t)N, (uint64_t)T))
+        p.long_rows = false;
     p.s.groups = (uint32_t)((N + (int64_t)kWave * p.G - 1) / ((int64_t)kWave * p.G));
     p.tile_steps = (uint64_t)(p.long_rows ? kTmELong : kTmE) * (uint64_t)(p.W / p.G);
     p.s.time_tiles = (uint32_t)(((uint64_t)T + p.tile_steps - 1) / p.tile_steps);
@@ -581,7 +608,7 @@ lrs_status run_tm(const char* name, int64_t N, int64_t T, float beta_max,
 {
     if (N >= (int64_t(1) << 32))
         return fail(LRS_ERR_INVALID_ARG, "%s: time-major calls need num_envs < 2^32", name);
-    const PlanTM plan = plan_time_major(N, T);
+    const PlanTM plan = plan_time_major(N, T, tm_lean_capable<Op>(beta_max));
     if (const int Wr = plan.rows_waves) {
         SchedTM s = plan.s;
         s.ws = static_cast<uint8_t*>(ws);

@@ -131,11 +131,14 @@ NARROW_SHAPES = [(n, t) for n in (1, 33, 100) for t in (1, 16, 17, 64, 100, 128)
 
 @pytest.mark.parametrize("est", ["gae", "vtrace", "eligibility_traces", "prefix_sum_i32"])
 @pytest.mark.parametrize("shape", [(16383, 100), (16384, 100), (16385, 128), (70, 128), (70, 129),
-                                   (70, 256), (70, 257)], ids=lambda s: f"{s[0]}x{s[1]}")
+                                   (70, 256), (70, 257), (300, 14000)],
+                         ids=lambda s: f"{s[0]}x{s[1]}")
 def test_automatic_tile_boundaries(shape, est):
     """Both sides of every automatic choice: narrow blocks below 256 groups of
     64 environments and 128 steps, 8 steps per lane up to 128 steps, 16 above
-    (one 256-step tile, then two)."""
+    (one 256-step tile, then two); calls that run one block per CU keep 8
+    steps per lane while 256-step tiles would make fewer than 256 blocks
+    (70 x 257) and take 16 beyond (300 x 14000: 5 x 55 blocks)."""
     N, T = shape
     ro = workloads.rollout(N, T, seed=N + 3 * T, term_p=0.02, trunc_p=0.02, gamma=0.97,
                            lambda_=0.9)

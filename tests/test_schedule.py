@@ -200,8 +200,18 @@ def test_schedule_info_matches_plan(lib):
     info, _ = schedule(lib, GAE, TIME_MAJOR, 8192, 512, 0.9)
     assert (info.envs_per_group, info.tile_steps) == (128, 128)
     for n, t in [(4096, 512), (2048, 8192), (4096, 256)]:
-        info, _ = schedule(lib, GAE, TIME_MAJOR, n, t, 0.9)
+        info, _ = schedule(lib, DISC, TIME_MAJOR, n, t, 0.9)
         assert (info.envs_per_group, info.tile_steps) == (64, 256), (n, t)
+    # one block per CU and 256-step tiles would leave CUs idle: 128-step tiles
+    # (fewer than 256 blocks of 256 steps), for the calls the capped kernel
+    # cannot take, including discounted returns with maps composed in fp64
+    for est, bm in [(GAE, 0.9), (VTRACE, 0.9), (RETRACE, 0.9), (DISC, 0.995)]:
+        info, _ = schedule(lib, est, TIME_MAJOR, 4096, 512, bm)
+        assert (info.tile_steps, info.elems_per_lane, info.groups) == (128, 8, 64), est
+    info, _ = schedule(lib, GAE, TIME_MAJOR, 4096, 769, 0.9)  # 64 x 4 blocks: enough
+    assert info.tile_steps == 256
+    info, _ = schedule(lib, GAE, TIME_MAJOR, 4096, 768, 0.9)  # 64 x 3 blocks: few
+    assert info.tile_steps == 128
     assert lib.lrs_debug_schedule(99, 0, 4, 4, 0.5, ctypes.byref(info), None, 0) == 1
     assert lib.lrs_debug_schedule(GAE, REVERSE, 4, 4, 0.5, ctypes.byref(info), None, 0) == 1
     assert lib.lrs_debug_schedule(PREFIX_I32, HALF, 4, 4, 0.5, ctypes.byref(info), None, 0) == 1
