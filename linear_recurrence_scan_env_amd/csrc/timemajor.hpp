@@ -4,10 +4,12 @@
 //
 // A lane owns one environment, so each load instruction of a wave reads 64
 // consecutive columns of one time row (coalesced).  A wave holds E
-// consecutive steps of its 64 environments; a block stacks W waves along
-// time, so a tile is 64 environments x E*W steps.  The estimator functors are
-// the row-major ones, fed a time-major Pos (strided, guarded accesses; all
-// of a lane's steps belong to one environment).
+// consecutive steps of its 64 environments; a block holds G groups of 64
+// environments (1, or 2 on long rows with many environments) and stacks
+// W / G waves along time per group, so a tile is 64 G environments x E W / G
+// steps.  The estimator functors are the row-major ones, fed a time-major Pos
+// (strided, guarded accesses; all of a lane's steps belong to one
+// environment).
 //
 // Carries between tiles run along time, per environment: each tile publishes
 // its aggregate as soon as its own maps are composed, and its inclusive value
