@@ -274,12 +274,15 @@ def test_affine_scan(shape, reverse, waves):
 
 @pytest.mark.parametrize("est", ["gae", "vtrace", "eligibility_traces", "prefix_sum_f32"])
 @pytest.mark.parametrize("dtype,shape", [(torch.bfloat16, (130, 1000)), (torch.bfloat16, (70, 100)),
-                                         (torch.float16, (70, 100))],
-                         ids=["bf16-130x1000", "bf16-70x100", "f16-70x100"])
+                                         (torch.float16, (70, 100)), (torch.bfloat16, (4100, 1030)),
+                                         (torch.float16, (4100, 1030))],
+                         ids=["bf16-130x1000", "bf16-70x100", "f16-70x100", "bf16-4100x1030",
+                              "f16-4100x1030"])
 def test_bf16_storage(est, dtype, shape):
-    """16-bit time-major, on the wide kernel (1000 steps) and on the narrow
-    whole-row blocks (100 steps): within the storage type's unit roundoff
-    plus the fp32 bound of the oracle on the rounded inputs."""
+    """16-bit time-major, on the wide kernel (1000 steps; 1030 steps of 4100
+    environments: two groups per block, non-temporal 16-bit loads) and on the
+    narrow whole-row blocks (100 steps): within the storage type's unit
+    roundoff plus the fp32 bound of the oracle on the rounded inputs."""
     N, T = shape
     u = 2.0 ** -8 if dtype == torch.bfloat16 else 2.0 ** -11
     ro = workloads.rollout(N, T, seed=78, term_p=0.02, trunc_p=0.02)
