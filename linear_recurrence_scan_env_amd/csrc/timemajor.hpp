@@ -115,7 +115,11 @@ __device__ __forceinline__ void tile_body_tm(const typename Op::Args& args, cons
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
+    // The wave index is uniform across the wave; saying so lets the compiler
+    // keep time-row bases in scalar registers (4096 x 2048: 4-12 fewer VGPRs
+    // per kernel, discounted returns with truncations 23% faster, the other
+    // calls 0-3%; the same change in the row-major kernel made it slower).
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int grp = wave % G;
     const int tw = wave / G;
     const int col_l = grp * kWave + lane;  // the environment's column in the shared arrays
@@ -323,7 +327,7 @@ __device__ __forceinline__ void rows_body_tm(const typename Op::Args& args, cons
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int v = lane % V;
-    const int q = (tid / kWave) * C + lane / V;
+    const int q = __builtin_amdgcn_readfirstlane(tid / kWave) * C + lane / V;
     const uint32_t n = g * V + (uint32_t)v;
     const bool active = n < s.N;
     const uint32_t t0 = (uint32_t)q * E;
