@@ -397,8 +397,17 @@ __device__ __forceinline__ void load_f32(float (&v)[E], Strided<const D> a,
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < E; ++j)
-            v[j] = (kFull || j < P.count) ? to_f32(get<TM && NT>(p + elem_offset(P, j, a.gap))) : 0.0f;
+        for (int j = 0; j < E; ++j) {
+            const bool in = kFull || j < P.count;
+            if constexpr (TM) {
+                // as in load_mask: every element loaded (element 0 of the array
+                // for those past the count), then masked
+                const float x = to_f32(get<NT>(p + (in ? elem_offset(P, j, a.gap) : 0)));
+                v[j] = in ? x : 0.0f;
+            } else {
+                v[j] = in ? to_f32(p[elem_offset(P, j, a.gap)]) : 0.0f;
+            }
+        }
     }
 }
 
@@ -419,8 +428,15 @@ __device__ __forceinline__ void load_u32(uint32_t (&v)[E], Strided<const int32_t
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < E; ++j)
-            v[j] = (kFull || j < P.count) ? (uint32_t)get<TM && NT>(p + elem_offset(P, j, a.gap)) : 0u;
+        for (int j = 0; j < E; ++j) {
+            const bool in = kFull || j < P.count;
+            if constexpr (TM) {
+                const uint32_t x = (uint32_t)get<NT>(p + (in ? elem_offset(P, j, a.gap) : 0));
+                v[j] = in ? x : 0u;
+            } else {
+                v[j] = in ? (uint32_t)p[elem_offset(P, j, a.gap)] : 0u;
+            }
+        }
     }
 }
 
@@ -454,9 +470,25 @@ __device__ __forceinline__ uint32_t load_mask(Strided<const uint8_t> a, const Po
                (nonzero_bytes(w.w) << 12);
     }
     uint32_t bits = 0;
+    if constexpr (TM) {
+        // Time-major lanes take this path for every partial tile.  Every
+        // element is loaded, those past the lane's count from element 0 of the
+        // array (which exists), and masked after: no load sits under a branch
+        // or is overwritten while in flight, so the lane's loads are all
+        // issued before the first wait instead of one round trip each
+        // (4096 x 100: 37-58% faster; row-major tiles, which come here only
+        // for a tail lane, measured 0-7% slower with it).
 #pragma unroll
-    for (int j = 0; j < E; ++j)
-        if ((kFull || j < P.count) && get<TM && NT>(p + elem_offset(P, j, a.gap)) != 0) bits |= 1u << j;
+        for (int j = 0; j < E; ++j) {
+            const bool in = kFull || j < P.count;
+            const uint8_t m = get<NT>(p + (in ? elem_offset(P, j, a.gap) : 0));
+            bits |= (uint32_t)(in && m != 0) << j;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            if ((kFull || j < P.count) && p[elem_offset(P, j, a.gap)] != 0) bits |= 1u << j;
+    }
     return bits;
 }
 
