@@ -91,7 +91,10 @@ __device__ __forceinline__ float next_elem(float my0, Strided<const D> a,
             const float v = to_f32(p[used ? elem_offset(P, E, a.gap) : elem_offset(P, 0, a.gap)]);
             return used ? v : 0.0f;
         }
-        return used ? to_f32(p[elem_offset(P, E, a.gap)]) : 0.0f;
+        // partial tiles: element 0 of the array when unused (as the guarded
+        // loads do), so no wait follows the load
+        const float v = to_f32(p[used ? elem_offset(P, E, a.gap) : 0]);
+        return used ? v : 0.0f;
     } else if constexpr (F) {
         // unused: re-read the lane's own first element (a line already
         // fetched) rather than touch the next tile.  Full tiles of a strided
