@@ -180,6 +180,11 @@ def test_schedule_info_matches_plan(lib):
     """Spot checks of the plans the tuning notes describe."""
     info, _ = schedule(lib, RETRACE, TRUNC, 4096, 128, 0.9405)
     assert (info.carries, info.tile_elems) == (0, 256)          # whole rows, 4 x 1 tiles
+    # look-back on 4096-element tiles, or 2048 when fewer than 128 of those
+    info, _ = schedule(lib, RETRACE, 0, 4096, 100, 0.9405)       # 100 tiles of 4096
+    assert (info.carries, info.tile_elems) == (1, 2048)
+    info, _ = schedule(lib, AFFINE, 0, 2048, 300, float("inf"))  # 150 tiles of 4096
+    assert (info.carries, info.tile_elems) == (1, 4096)
     info, _ = schedule(lib, GAE, TRUNC, 64, 131072, 0.9405)
     assert (info.carries, info.tile_elems, info.tiles_per_row) == (1, 2048, 0)  # flat look-back
     info, _ = schedule(lib, GAE, 0, 2048, 8192, 0.9405)
