@@ -166,12 +166,22 @@ __device__ __forceinline__ void load_trunc_values(float (&tv)[E], Strided<const 
     }
 }
 
+// The truncation mask of the lane's elements (0 for the non-truncating
+// variants).  Estimators read it before their other streams: the
+// trunc_values read waits for it, and so leaves while those are in flight.
+template <int E, bool F, bool TM, bool NT, bool S, bool kTrunc, class D>
+__device__ __forceinline__ uint32_t trunc_mask(const BoundaryArgs<D>& b, const Pos<E, F, TM, NT, S>& P,
+                                               const Ctx& c)
+{
+    return kTrunc ? load_mask<E>(b.trunc, P, c.vec) : 0u;
+}
+
+// kap: trunc_mask's result.
 template <int E, bool F, bool TM, bool NT, bool S, bool kTrunc, class D>
 __device__ __forceinline__ Ends<E> load_ends(const BoundaryArgs<D>& b, const Pos<E, F, TM, NT, S>& P,
-                                             const Ctx& c)
+                                             const Ctx& c, uint32_t kap)
 {
     const uint32_t tau = load_mask<E>(b.term, P, c.vec);
-    const uint32_t kap = kTrunc ? load_mask<E>(b.trunc, P, c.vec) : 0u;
     // Bootstrap of each row end in the lane.  Full tiles have seq_len >= E,
     // so a lane holds at most one row end, which belongs to its first row:
     // one unconditional load.  The guarded path loads per row end.
@@ -260,11 +270,12 @@ struct GaeOp {
     __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT, S>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
+        const uint32_t kap = trunc_mask<E, F, TM, NT, S, kTrunc>(a.b, P, c);  // first: see trunc_mask
         float r[E], v[E];
         load_f32<E>(r, a.rewards, P, c.vec);
         load_f32<E>(v, a.values, P, c.vec);
         const float vnx = next_elem<E>(v[0], a.values, P, c, successor_used(P));
-        const Ends<E> e = load_ends<E, F, TM, NT, S, kTrunc>(a.b, P, c);
+        const Ends<E> e = load_ends<E, F, TM, NT, S, kTrunc>(a.b, P, c, kap);
 #pragma unroll
         for (int j = 0; j < E; ++j) {
             const bool end = (e.end >> j) & 1u;
@@ -321,11 +332,12 @@ struct LambdaOp {
     __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT, S>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
+        const uint32_t kap = trunc_mask<E, F, TM, NT, S, kTrunc>(a.b, P, c);  // first: see trunc_mask
         float r[E], v[E];
         load_f32<E>(r, a.rewards, P, c.vec);
         load_f32<E>(v, a.values, P, c.vec);
         const float vnx = next_elem<E>(v[0], a.values, P, c, successor_used(P));
-        const Ends<E> e = load_ends<E, F, TM, NT, S, kTrunc>(a.b, P, c);
+        const Ends<E> e = load_ends<E, F, TM, NT, S, kTrunc>(a.b, P, c, kap);
 #pragma unroll
         for (int j = 0; j < E; ++j) {
             const bool end = (e.end >> j) & 1u;
@@ -378,9 +390,10 @@ struct DiscOp {
     __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT, S>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
+        const uint32_t kap = trunc_mask<E, F, TM, NT, S, kTrunc>(a.b, P, c);  // first: see trunc_mask
         float r[E];
         load_f32<E>(r, a.rewards, P, c.vec);
-        const Ends<E> e = load_ends<E, F, TM, NT, S, kTrunc>(a.b, P, c);
+        const Ends<E> e = load_ends<E, F, TM, NT, S, kTrunc>(a.b, P, c, kap);
 #pragma unroll
         for (int j = 0; j < E; ++j) {
             const bool end = (e.end >> j) & 1u;
@@ -440,12 +453,13 @@ struct VtraceOp {
     __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT, S>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
+        const uint32_t kap = trunc_mask<E, F, TM, NT, S, kTrunc>(a.b, P, c);  // first: see trunc_mask
         float lr[E];
         load_f32<E>(lr, a.log_rhos, P, c.vec);
         load_f32<E>(s.r, a.rewards, P, c.vec);
         load_f32<E>(s.v, a.values, P, c.vec);
         const float vnx = next_elem<E>(s.v[0], a.values, P, c, successor_used(P));
-        const Ends<E> e = load_ends<E, F, TM, NT, S, kTrunc>(a.b, P, c);
+        const Ends<E> e = load_ends<E, F, TM, NT, S, kTrunc>(a.b, P, c, kap);
 #pragma unroll
         for (int j = 0; j < E; ++j) {
             const bool end = (e.end >> j) & 1u;
@@ -526,6 +540,7 @@ struct RetraceOp {
     __device__ static void prepare(const Args& a, const Pos<E, F, TM, NT, S>& P, const Ctx& c,
                                    float (&alpha)[E], float (&beta)[E], State& s)
     {
+        const uint32_t kap = trunc_mask<E, F, TM, NT, S, kTrunc>(a.b, P, c);  // first: see trunc_mask
         float lr[E], r[E], q[E], v[E], cc[E];
         load_f32<E>(lr, a.log_rhos, P, c.vec);
         load_f32<E>(r, a.rewards, P, c.vec);
@@ -536,7 +551,7 @@ struct RetraceOp {
         const float lrnx = next_elem<E>(lr[0], a.log_rhos, P, c, used);
         const float qnx = next_elem<E>(q[0], a.q_values, P, c, used);
         const float vnx = next_elem<E>(v[0], a.values, P, c, used);
-        const Ends<E> e = load_ends<E, F, TM, NT, S, kTrunc>(a.b, P, c);
+        const Ends<E> e = load_ends<E, F, TM, NT, S, kTrunc>(a.b, P, c, kap);
 #pragma unroll
         for (int j = 0; j < E; ++j) cc[j] = trace(a, lr[j]);
         const float cnx = trace(a, lrnx);
