@@ -345,7 +345,7 @@ constexpr uint32_t kNarrowMaxTile = 2048;  // ops without kWideTiles stop at 4x8
 constexpr uint64_t kWideMinTiles = 1024;   // whole-row tiles above 2048 need this many
 constexpr int kLookbackCfg = 3;            // 4x8: 2048-element tiles
 constexpr int kLookbackCfgWide4 = 5;       // 4x16: prefix sums, maps composed in fp64
-constexpr uint64_t kFewWide4Tiles = 128;    // fewer 4x16 look-back tiles than this: 4x8
+constexpr uint64_t kFewWide4Tiles = 128;   // fewer 4x16 look-back tiles than this: 4x8
 constexpr int kLookbackCfgLight = 2;       // 8x4: kLbLight ops, below kWideMinTiles
 // 16-bit data: eight elements per lane make each data load 16 bytes
 constexpr int kLookbackCfgHalfWide = 6;    // 8x16: 8192-element tiles (ops with kWideTiles)
@@ -397,7 +397,8 @@ inline size_t workspace_bytes_for(uint64_t total)
 // eight elements per lane, in 8192-element tiles when kWideMinTiles of them
 // fill the chip, else in 2048-element ones (also when composed in fp64);
 // kLbWide4 ops, and kLbNarrow ops composed in fp64, 4096-element tiles of
-// four per lane; kLbNarrow ops 2048-element tiles of four per lane.
+// four per lane (kLbWide4 ops on fewer than kFewWide4Tiles of them: 2048);
+// kLbNarrow ops 2048-element tiles of four per lane.
 inline int choose_cfg(uint64_t total, uint64_t T, bool wide_ok, LookbackTile lb, bool fp64, int elem_bytes,
                       bool* lookback)
 {

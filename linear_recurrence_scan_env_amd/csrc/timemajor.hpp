@@ -279,8 +279,8 @@ __device__ __forceinline__ void tile_body_tm(const typename Op::Args& args, cons
 
     const T lane_in = T(apply(beyond, A(carry)));
     Op::finish(args, P, c, alpha, beta, st, lane_in);
-    // One wave counts the block, after the barrier above, which every wave
-    // reaches after reading its tag.
+    // One wave counts the block, after the barrier above: each group's near
+    // wave, the only ones that read the launch tag, has it by then.
     if (carries && grp == 0 && lane == 0) {
         const uint64_t entry = count_block(hdr, blockIdx.x);
         close_launch(hdr, count_group(hdr, entry, s.num_blocks, blockIdx.x), s.num_blocks, tag);
@@ -555,7 +555,7 @@ struct PlanTM {
 };
 
 // Calls whose kernels fit the capped twin (kLeanTm, with maps composed in
-// fp32 where that matters).  The others hold 71-128 VGPRs: one block per CU.
+// fp32 where that matters).  The others hold 69-128 VGPRs: one block per CU.
 template <template <int> class Op>
 inline bool tm_lean_capable(float beta_max)
 {
