@@ -340,6 +340,8 @@ __device__ __forceinline__ void rows_body_tm(const typename Op::Args& args, cons
         if (t0 == 0) first = 1u;
     }
     const uint32_t col = active ? n : 0u;  // inactive lanes touch nothing (count = 0)
+    // Plain loads: non-temporal ones measured up to 13% slower on these short
+    // rows (4096 x 32, 4096 x 100, 4096 x 128).
     const Pos<E, F, true, false, S> P{(uint64_t)t0 * s.N + col, col, count, last, first, s.N, t0};
     const Ctx c{(uint64_t)s.N * s.T, s.T, lane, false};
 
